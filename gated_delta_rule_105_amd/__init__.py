@@ -1,0 +1,147 @@
+"""MI355X-native Kimi Delta Attention (KDA): chunked prefill and decode step.
+
+Thin PyTorch-facing layer over the C ABI of ``libkda.so`` (include/kda.h).
+PyTorch supplies device memory and the current HIP stream; all arithmetic
+runs in the library's HIP kernels.  There is no CPU fallback: calling into a
+missing library raises.
+
+    o, ht = chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None)
+    o = decode_step(q, k, v, g, beta, state)          # state updated in place
+
+KDA is the gated delta rule with a channel-wise forget gate,
+S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+o_t = S_t^T q_t, alpha_t = exp(max(g_t, g_floor)) ("Kimi K3 深度拆解"
+(chenxutan.com), 4.2 "线性注意力与 Delta Rule"; "Kimi K3 技術報告"
+(akiraxclaw.com), "長度：KDA 為什麼還要搭配 Gated MLA？").
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+from ._lib import (KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_OK, ChunkDesc, KdaError, status_string,
+                   version)
+from . import _lib
+
+__all__ = ["chunk_forward", "decode_step", "workspace_bytes", "make_desc", "KdaError",
+           "status_string", "version"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t}; KDA takes bfloat16 or float32")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def make_desc(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
+              g_floor: float = -0.125) -> ChunkDesc:
+    return ChunkDesc(B=B, T=T, H=H, d_k=d, d_v=d, chunk=chunk, n_seqs=n_seqs,
+                     dtype=_dtype_code(dtype), g_floor=g_floor)
+
+
+def workspace_bytes(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
+                    g_floor: float = -0.125) -> int:
+    """Device workspace one chunk_forward call of this shape needs."""
+    return _lib.workspace_size(make_desc(B, T, H, d, dtype, n_seqs, chunk, g_floor))
+
+
+def check_cu_seqlens(cu, T: int) -> None:
+    """Host-side check of packed-sequence offsets (the library trusts them)."""
+    c = [int(x) for x in (cu.tolist() if hasattr(cu, "tolist") else cu)]
+    if len(c) < 2 or c[0] != 0 or c[-1] != T or any(b < a for a, b in zip(c, c[1:])):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+
+
+def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
+                  g_floor: float = -0.125, *, o=None, ht=None, workspace=None,
+                  output_final_state: bool = True, validate_cu: bool = True,
+                  stream=None) -> Tuple[object, object]:
+    """Chunked KDA forward over whole sequences.
+
+    q, k, g: [B, T, H, d]; v: [B, T, H, d] (bf16 or fp32); beta: [B, T, H] fp32.
+    cu_seqlens: int32 device tensor [n+1] for n packed sequences (B == 1).
+    h0: fp32 [S, H, d, d] or None.  Returns (o [B, T, H, d], ht [S, H, d, d]
+    fp32, or None when output_final_state is False).
+    """
+    torch = _torch()
+    B, T, H, d = q.shape
+    dt = q.dtype
+    _check_dev("q", q, dt)
+    for name, t in (("k", k), ("g", g), ("v", v)):
+        _check_dev(name, t, dt, (B, T, H, d))
+    _check_dev("beta", beta, torch.float32, (B, T, H))
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        if validate_cu:
+            check_cu_seqlens(cu_seqlens.cpu(), T)
+    S = n_seqs if n_seqs else B
+    _check_dev("h0", h0, torch.float32, (S, H, d, d))
+    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor)
+    ws_bytes = _lib.workspace_size(desc)
+    if o is None:
+        o = torch.empty((B, T, H, d), dtype=dt, device=q.device)
+    _check_dev("o", o, dt, (B, T, H, d))
+    if ht is None and output_final_state:
+        ht = torch.empty((S, H, d, d), dtype=torch.float32, device=q.device)
+    _check_dev("ht", ht, torch.float32, (S, H, d, d))
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.chunk_forward_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), stream)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_forward")
+    return o, ht
+
+
+def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, stream=None):
+    """One decode step for N sequences; ``state`` [N, H, d, d] fp32 is updated
+    in place.  q, k, v, g: [N, H, d]; beta: [N, H] fp32.  Returns o [N, H, d]."""
+    torch = _torch()
+    N, H, d = q.shape
+    dt = q.dtype
+    _check_dev("q", q, dt)
+    for name, t in (("k", k), ("g", g), ("v", v)):
+        _check_dev(name, t, dt, (N, H, d))
+    _check_dev("beta", beta, torch.float32, (N, H))
+    _check_dev("state", state, torch.float32, (N, H, d, d))
+    if o is None:
+        o = torch.empty((N, H, d), dtype=dt, device=q.device)
+    _check_dev("o", o, dt, (N, H, d))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.decode_step_raw(N, H, d, d, _dtype_code(dt), g_floor, _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(g), _ptr(beta), _ptr(state), _ptr(o), stream)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_step")
+    return o

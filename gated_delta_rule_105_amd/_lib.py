@@ -1,0 +1,96 @@
+"""ctypes binding of ``libkda.so`` (the C ABI declared in include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Loading fails loudly when the library is missing;
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE_TOO_SMALL = 3
+KDA_ERR_HIP = 4
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+
+# Every symbol include/kda.h declares.
+EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
+           "kda_chunk_forward", "kda_decode_step")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class ChunkDesc(ctypes.Structure):
+    """Mirror of kda_chunk_desc_t."""
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("n_seqs", ctypes.c_int), ("dtype", ctypes.c_int), ("g_floor", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it first with `python -m gated_delta_rule_105_amd.build` "
+            "(the KDA path has no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_chunk_forward_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(sz)]
+    lib.kda_chunk_forward_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_forward.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.kda_chunk_forward.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().kda_version())
+
+
+def workspace_size(desc: ChunkDesc) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().kda_chunk_forward_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_forward_workspace_size")
+    return int(out.value)
+
+
+def chunk_forward_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, ws, ws_bytes, stream) -> int:
+    """Call kda_chunk_forward with raw integer addresses; returns the status."""
+    return int(load().kda_chunk_forward(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, ws,
+                                        ctypes.c_size_t(ws_bytes), stream))
+
+
+def decode_step_raw(N, H, d_k, d_v, dtype, g_floor, q, k, v, g, beta, state, o, stream) -> int:
+    """Call kda_decode_step with raw integer addresses; returns the status."""
+    return int(load().kda_decode_step(N, H, d_k, d_v, dtype, ctypes.c_float(g_floor), q, k, v, g,
+                                      beta, state, o, stream))

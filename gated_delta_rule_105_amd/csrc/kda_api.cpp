@@ -1,0 +1,184 @@
+// C-ABI front end of the KDA library: argument validation and dispatch.
+//
+// Plain C++: nothing here touches HIP, so every argument error is reported
+// before any GPU call (and can be exercised on a machine without a GPU).
+// The entry points and their contracts are declared in include/kda.h.
+#include "kda.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 16;
+constexpr size_t kWsAlign = 256;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Multiply non-negative sizes, flagging overflow of size_t.
+bool mul(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+size_t elem_size(kda_dtype_t t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
+
+struct Sizes {
+  size_t tokens;      // B * T
+  size_t n_states;    // sequences
+  size_t x_bytes;     // one of q, k, v, g, o
+  size_t beta_bytes;
+  size_t state_bytes; // h0 or ht
+  size_t n_chunks;    // upper bound of chunks over all sequences
+  size_t ws_bytes;
+};
+
+int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
+  if (!d) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->B < 1 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1 || d->n_seqs < 0)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->n_seqs > 0 && d->B != 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (!(d->g_floor >= -1.0f && d->g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;  // NaN fails too
+  if ((double)d->chunk * -(double)d->g_floor > 16.0) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->d_k != d->d_v) return KDA_ERR_UNSUPPORTED;
+  if (d->d_k != 64 && d->d_k != 128) return KDA_ERR_UNSUPPORTED;
+  if (d->chunk != 64) return KDA_ERR_UNSUPPORTED;
+  const size_t per = kda::chunk_bytes(d->dtype == KDA_DTYPE_BF16, d->d_k);
+  if (per == 0) return KDA_ERR_UNSUPPORTED;  // fp32 with d = 128
+
+  const size_t B = (size_t)d->B, T = (size_t)d->T, H = (size_t)d->H, D = (size_t)d->d_k;
+  s->n_states = d->n_seqs > 0 ? (size_t)d->n_seqs : B;
+  if (!mul(B, T, &s->tokens)) return KDA_ERR_INVALID_ARGUMENT;
+  size_t th, x;
+  if (!mul(s->tokens, H, &th) || !mul(th, D, &x) || !mul(x, elem_size(d->dtype), &s->x_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!mul(th, 4, &s->beta_bytes)) return KDA_ERR_INVALID_ARGUMENT;
+  size_t sh, sd;
+  if (!mul(s->n_states, H, &sh) || !mul(sh, D * D, &sd) || !mul(sd, 4, &s->state_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (d->n_seqs > 0)
+    s->n_chunks = (T + 63) / 64 + (size_t)d->n_seqs;
+  else
+    s->n_chunks = B * ((T + 63) / 64);
+  if (s->n_chunks > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  size_t ch;
+  if (!mul(s->n_chunks, H, &ch) || !mul(ch, per, &s->ws_bytes)) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->tokens > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    default: return "KDA_ERR_UNKNOWN";
+  }
+}
+
+int kda_version(void) { return KDA_VERSION; }
+
+int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
+  if (!bytes) return KDA_ERR_INVALID_ARGUMENT;
+  Sizes s;
+  const int st = check_desc(d, &s);
+  if (st != KDA_OK) return st;
+  *bytes = s.ws_bytes;
+  return KDA_OK;
+}
+
+int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                      const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                      void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+  Sizes s;
+  const int st = check_desc(d, &s);
+  if (st != KDA_OK) return st;
+  const bool has_tokens = s.tokens > 0;
+  if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  if ((d->n_seqs > 0) != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
+  if (s.ws_bytes > 0) {
+    if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < s.ws_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (has_tokens) {
+    const Range ro = range(o, s.x_bytes);
+    const Range ins[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes),
+                         range(g, s.x_bytes), range(beta, s.beta_bytes), range(h0, s.state_bytes)};
+    for (const Range& r : ins)
+      if (overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  if (ht) {
+    const Range rh = range(ht, s.state_bytes);
+    const Range others[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes),
+                            range(g, s.x_bytes), range(beta, s.beta_bytes), range(o, s.x_bytes)};
+    for (const Range& r : others)
+      if (overlap(rh, r)) return KDA_ERR_INVALID_ARGUMENT;
+    if (h0 && h0 != ht && overlap(rh, range(h0, s.state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace && s.ws_bytes > 0) {
+    const Range rw = range(workspace, s.ws_bytes);
+    const Range all[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes), range(g, s.x_bytes),
+                         range(beta, s.beta_bytes), range(o, s.x_bytes), range(h0, s.state_bytes),
+                         range(ht, s.state_bytes)};
+    for (const Range& r : all)
+      if (overlap(rw, r)) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  if (!ht && s.tokens == 0) return KDA_OK;  // nothing to write
+  const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
+  const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H,
+                                          (int64_t)(has_tokens ? s.n_chunks : 0), d->g_floor, q, k, v, g,
+                                          beta, h0, cu_seqlens, o, ht, workspace, stream);
+  return e == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor, const void* q,
+                    const void* k, const void* v, const void* g, const float* beta, float* state, void* o,
+                    void* stream) {
+  if (N < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (!(g_floor >= -1.0f && g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, g, beta, state, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
+  size_t nh, x, xb, sb, bb;
+  if (!mul((size_t)N, (size_t)H, &nh) || !mul(nh, (size_t)d_k, &x) || !mul(x, elem_size(dtype), &xb) ||
+      !mul(x, (size_t)d_k * 4, &sb) || !mul(nh, 4, &bb))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (nh > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const Range rs = range(state, sb), ro = range(o, xb);
+  const Range ins[] = {range(q, xb), range(k, xb), range(v, xb), range(g, xb), range(beta, bb)};
+  for (const Range& r : ins)
+    if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
+  if (overlap(rs, ro)) return KDA_ERR_INVALID_ARGUMENT;
+  const int e = kda::launch_decode_step(dtype == KDA_DTYPE_BF16, d_k, N, H, g_floor, q, k, v, g, beta,
+                                        state, o, stream);
+  return e == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4).
+//
+// MFMA operand convention used throughout (checked against the hardware):
+// for a 16x16 output tile and a k-block of KB indices, lane l = 16*g + i
+// (i = l % 16, g = l / 16) supplies
+//     A-fragment: row i of A,    k = 16*(e/4) + 4*g + e%4  for element e
+//     B-fragment: column i of B, the same k for element e
+// and receives D[4*g + r][i] in accumulator register r (r = 0..3).
+//   bf16: v_mfma_f32_16x16x32_bf16, KB = 32, 8 elements (16 bytes) per lane.
+//   fp32: v_mfma_f32_16x16x4f32 issued 4 times (element e in issue e),
+//         KB = 16, 4 elements (16 bytes) per lane.
+// The hardware's own order of k inside a lane is a permutation of the one
+// above; a sum over k is invariant under any permutation applied to both
+// operands, so the convention only has to be the same for A and B.
+// Its payoff: an accumulator tile (rows 4g..4g+3 of column i in lane l) is
+// already a B-fragment whose k runs over the tile's rows, so an output can
+// feed the next product without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef uint16_t bf16_t;  // storage type of bf16 tensors in memory
+
+// ---- scalar conversions -------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+    return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Element-type traits: storage type, fragment type, k-block of one MMA step.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int KB = 16;
+  typedef f32x4 frag;
+  __device__ static __forceinline__ float load(const float* p) { return *p; }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ float from_f32(float x) { return x; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int KB = 32;
+  typedef bf16x8 frag;
+  __device__ static __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+  __device__ static __forceinline__ bf16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// ---- MMA on one 16x16 tile over one k-block ----------------------------
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const f32x4& a, const f32x4& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+  return c;
+}
+
+// ---- fragments ----------------------------------------------------------
+// A- or B-fragment from a row-major array X[row][k] (k contiguous, row
+// stride `ld` elements): this lane's row, k-block starting at k0.
+__device__ __forceinline__ f32x4 frag_rows(const float* X, int ld, int row, int k0, int g) {
+  const float* p = X + row * ld + k0 + 4 * g;
+  return *(const f32x4*)p;
+}
+__device__ __forceinline__ bf16x8 frag_rows(const bf16_t* X, int ld, int row, int k0, int g) {
+  const bf16_t* p = X + row * ld + k0 + 4 * g;
+  bf16x4 lo = *(const bf16x4*)p;
+  bf16x4 hi = *(const bf16x4*)(p + 16);
+  return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// bf16 fragment read from an fp32 row-major array (rounded on the fly)
+__device__ __forceinline__ bf16x8 frag_rows_f32_to_bf16(const float* X, int ld, int row, int k0, int g) {
+  const float* p = X + row * ld + k0 + 4 * g;
+  f32x4 lo = *(const f32x4*)p;
+  f32x4 hi = *(const f32x4*)(p + 16);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = __builtin_bit_cast(__bf16, f32_to_bf16(lo[e]));
+    r[e + 4] = __builtin_bit_cast(__bf16, f32_to_bf16(hi[e]));
+  }
+  return r;
+}
+
+// B-fragment from accumulator tiles whose rows run over k.
+__device__ __forceinline__ f32x4 frag_from_acc(const f32x4& t0) { return t0; }
+__device__ __forceinline__ bf16x8 frag_from_acc(const f32x4& t0, const f32x4& t1) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = __builtin_bit_cast(__bf16, f32_to_bf16(t0[e]));
+    r[e + 4] = __builtin_bit_cast(__bf16, f32_to_bf16(t1[e]));
+  }
+  return r;
+}
+
+// Uniform view over the two element types for kernels templated on T.
+template <typename T> struct Frag;
+template <> struct Frag<float> {
+  typedef f32x4 type;
+  // fragment over k-block kb from accumulator tiles acc[], where tile j
+  // covers k = 16 j .. 16 j + 15
+  __device__ static __forceinline__ f32x4 from_acc(const f32x4* acc, int kb) { return acc[kb]; }
+  __device__ static __forceinline__ f32x4 from_f32_rows(const float* X, int ld, int row, int k0, int g) {
+    return frag_rows(X, ld, row, k0, g);
+  }
+};
+template <> struct Frag<bf16_t> {
+  typedef bf16x8 type;
+  __device__ static __forceinline__ bf16x8 from_acc(const f32x4* acc, int kb) {
+    return frag_from_acc(acc[2 * kb], acc[2 * kb + 1]);
+  }
+  __device__ static __forceinline__ bf16x8 from_f32_rows(const float* X, int ld, int row, int k0, int g) {
+    return frag_rows_f32_to_bf16(X, ld, row, k0, g);
+  }
+};
+
+// ---- workspace layout of one (chunk, head) ------------------------------
+// All operand blocks are stored as whole fragments: [fragment][lane][16 B],
+// so that a wave loads one fragment with one 16-byte load per lane.
+template <typename T, int D> struct ChunkLayout {
+  static constexpr int C = 64;                   // tokens per chunk
+  static constexpr int KB = Elem<T>::KB;
+  static constexpr int FRAG = 64 * 16;           // bytes per fragment
+  static constexpr int NKD = D / KB;             // k-blocks over channels
+  static constexpr int NKC = C / KB;             // k-blocks over tokens
+  static constexpr size_t WK = 0;                              // [4][NKD]
+  static constexpr size_t QT = WK + 4 * NKD * FRAG;            // [4][NKD]
+  static constexpr size_t P = QT + 4 * NKD * FRAG;             // [4][NKC]
+  static constexpr size_t KBT = P + 4 * NKC * FRAG;            // [D/16][NKC]
+  static constexpr size_t WV = KBT + (D / 16) * NKC * FRAG;    // [D/16][4] acc tiles
+  static constexpr size_t WV_TILE = 64 * 4 * sizeof(T);        // bytes per tile
+  static constexpr size_t GL = WV + (D / 16) * 4 * WV_TILE;    // [D] fp32
+  static constexpr size_t BYTES = ((GL + D * 4 + 255) / 256) * 256;
+};
+
+// Chunk bookkeeping: sequence n owns tokens [cu[n], cu[n+1]) and chunks
+// [chunk_base(n), chunk_base(n) + ceil(len/64)).
+struct SeqInfo {
+  int64_t tok0;
+  int len;
+  int64_t chunk0;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const int32_t* cu, int n, int T) {
+  SeqInfo s;
+  if (cu) {
+    int64_t base = 0;
+    for (int m = 0; m < n; ++m) base += (cu[m + 1] - cu[m] + 63) / 64;
+    s.tok0 = cu[n];
+    s.len = cu[n + 1] - cu[n];
+    s.chunk0 = base;
+  } else {
+    s.tok0 = (int64_t)n * T;
+    s.len = T;
+    s.chunk0 = (int64_t)n * ((T + 63) / 64);
+  }
+  return s;
+}
+
+}  // namespace kda

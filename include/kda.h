@@ -1,0 +1,141 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * KDA is the gated delta rule with a channel-wise forget gate and one
+ * fixed-size state matrix S (d_k x d_v, fp32) per (sequence, head):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,           alpha_t = exp(max(g_t, g_floor))
+ *
+ * Sources (page title, section):
+ *   - delta-rule update (erase along k, then write), output read from the
+ *     updated state, state of size [d, d_v]: "Kimi K3 深度拆解" (chenxutan.com),
+ *     4.2 "线性注意力与 Delta Rule";
+ *   - one forget rate per key channel rather than per head: "Kimi K3 技術報告：
+ *     三個架構改動一次看懂" (akiraxclaw.com), "長度：KDA 為什麼還要搭配 Gated MLA？";
+ *   - fixed-size recurrent state, chunk-parallel computation: "3 分钟看懂
+ *     Kimi K3" (landx.limxdynamics.com), "第一条主线";
+ *   - lower bound on the log-decay so that every causal chunk, the diagonal
+ *     block included, is a dense matrix product: same page, Figure 3; and
+ *     "Kimi K3 发布 47 页技术报告" (163.com), section 01;
+ *   - decode cost and state size independent of context length: "Kimi K3：
+ *     预训练规模与推理算力，必须一起扩展" (studioglobal.ai), "KDA 与 Gated MLA".
+ * The pages leave the position of the gate relative to the erase open; this
+ * library decays first, as in the formula above.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *     16-byte aligned.  The caller owns every buffer; the library allocates
+ *     nothing, never synchronises, keeps no global state and is reentrant.
+ *   - Arguments are validated on the host before any HIP call, so argument
+ *     errors come back as status codes even on a machine without a GPU.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and is asynchronous: results are valid once the caller synchronises.
+ *   - A failed launch returns KDA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Log-decays g must be <= 0 (alpha in (0, 1]); the library applies
+ *     max(g, g_floor) itself, which is a no-op on inputs already floored.
+ *   - NaN or Inf inputs propagate into the outputs; they never fault or hang.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, bad size, misalignment, overlap */
+  KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k = 96)   */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+  KDA_ERR_HIP = 4               /* the HIP runtime reported an error          */
+} kda_status_t;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+/* Shape of one chunked forward call. */
+typedef struct {
+  int B;            /* batch; must be 1 when n_seqs > 0                      */
+  int T;            /* tokens per batch row (packed total when n_seqs > 0)   */
+  int H;            /* heads                                                 */
+  int d_k;          /* key/query channels: 64 or 128                         */
+  int d_v;          /* value channels: must equal d_k                        */
+  int chunk;        /* tokens per chunk: 64                                  */
+  int n_seqs;       /* 0: B sequences of T tokens; > 0: packed sequences     */
+  kda_dtype_t dtype;/* dtype of q, k, v, g and o                             */
+  float g_floor;    /* per-step log-decay floor, in [-1, 0), |chunk*floor|<=16 */
+} kda_chunk_desc_t;
+
+/* Static, human-readable name of a status code; never NULL. */
+const char* kda_status_string(int status);
+
+/* KDA_VERSION of the built library. */
+int kda_version(void);
+
+/*
+ * Bytes of device workspace that kda_chunk_forward needs for `d`
+ * (host-only query, no HIP call).  Returns KDA_OK or KDA_ERR_* for an
+ * invalid or unsupported descriptor.
+ */
+int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
+
+/*
+ * Chunked forward ("prefill") over whole sequences.
+ *
+ * Computes, for every sequence and head, the recurrence above over the
+ * sequence's tokens, starting from h0 (or zeros), writing o for every token
+ * and the final state to ht.  Internally the sequence is cut into chunks of
+ * `chunk` tokens (restarting at every sequence start; the last chunk may be
+ * short): the chunk-local work is dense bf16/fp32 matrix products and a
+ * triangular inverse, then the state is carried from chunk to chunk.  The
+ * result equals the token-by-token recurrence up to rounding.
+ *
+ *   q, k, g : [B, T, H, d_k]  dtype
+ *   v       : [B, T, H, d_v]  dtype
+ *   beta    : [B, T, H]       fp32, write strengths in [0, 1]
+ *   h0      : [S, H, d_k, d_v] fp32 or NULL (= zero state); S = n_seqs or B
+ *   cu_seqlens: device int32 [n_seqs + 1], cu[0] = 0, non-decreasing,
+ *             cu[n_seqs] = T; NULL when n_seqs == 0.  Contents are trusted
+ *             (they live on the device); callers validate them beforehand.
+ *   o       : [B, T, H, d_v]  dtype, written
+ *   ht      : [S, H, d_k, d_v] fp32, written, or NULL; may alias h0 exactly
+ *   workspace: device buffer of at least kda_chunk_forward_workspace_size()
+ *             bytes, 256-byte aligned; its contents are scratch.
+ * o must not overlap any input; ht must not overlap q, k, v, g, beta or o.
+ */
+int kda_chunk_forward(const kda_chunk_desc_t* d,
+                      const void* q, const void* k, const void* v, const void* g,
+                      const float* beta, const float* h0,
+                      const int32_t* cu_seqlens,
+                      void* o, float* ht,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * One decode step: one new token for each of N sequences, state resident
+ * in device memory and updated IN PLACE.  For every (n, h):
+ *     S' = diag(alpha) S;  u = beta (v - S'^T k);  S <- S' + k u^T;
+ *     o  = S^T q
+ * (the recurrence above for a single token; decode cost and state size do
+ * not depend on how many tokens came before).
+ *
+ *   q, k, g : [N, H, d_k] dtype      v: [N, H, d_v] dtype
+ *   beta    : [N, H] fp32            o: [N, H, d_v] dtype, written
+ *   state   : [N, H, d_k, d_v] fp32, read and overwritten
+ * d_k = d_v in {64, 128}.  state must not overlap any other argument and o
+ * must not overlap any input.
+ */
+int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor,
+                    const void* q, const void* k, const void* v, const void* g,
+                    const float* beta, float* state, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

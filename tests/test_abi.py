@@ -1,0 +1,170 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before any HIP call.  Every call below carries at least one invalid argument,
+so none of them reaches a kernel launch (the pointers are fake addresses)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_105_amd import _lib
+from gated_delta_rule_105_amd._lib import (KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_ERR_INVALID_ARGUMENT,
+                                           KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_OK,
+                                           ChunkDesc)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kda.h")
+GB = 1 << 30
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define KDA_VERSION (\d+)", open(HEADER).read())
+    assert lib.kda_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for st in range(-2, 8):
+        s = lib.kda_status_string(st)
+        assert s is not None and s.startswith(b"KDA_")
+    assert _lib.status_string(KDA_ERR_WORKSPACE_TOO_SMALL) == "KDA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def desc(**kw):
+    base = dict(B=1, T=4096, H=16, d_k=128, d_v=128, chunk=64, n_seqs=0, dtype=KDA_DTYPE_BF16,
+                g_floor=-0.125)
+    base.update(kw)
+    return ChunkDesc(**base)
+
+
+def ws_status(lib, d):
+    out = ctypes.c_size_t(0)
+    st = lib.kda_chunk_forward_workspace_size(None if d is None else ctypes.byref(d), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_valid(lib):
+    st, n = ws_status(lib, desc())
+    assert st == KDA_OK and n > 0 and n % 256 == 0
+    st2, n2 = ws_status(lib, desc(T=8192))
+    assert st2 == KDA_OK and n2 == 2 * n
+    st3, n3 = ws_status(lib, desc(T=0))
+    assert st3 == KDA_OK and n3 == 0
+    st4, _ = ws_status(lib, desc(d_k=64, d_v=64, dtype=KDA_DTYPE_F32))
+    assert st4 == KDA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_k=96, d_v=96), KDA_ERR_UNSUPPORTED),
+    (dict(d_k=128, d_v=64), KDA_ERR_UNSUPPORTED),
+    (dict(chunk=32), KDA_ERR_UNSUPPORTED),
+    (dict(dtype=KDA_DTYPE_F32), KDA_ERR_UNSUPPORTED),          # fp32 is d = 64 only
+    (dict(B=2, n_seqs=3), KDA_ERR_INVALID_ARGUMENT),
+    (dict(g_floor=0.0), KDA_ERR_INVALID_ARGUMENT),
+    (dict(g_floor=-2.0), KDA_ERR_INVALID_ARGUMENT),
+    (dict(g_floor=math.nan), KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), KDA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), KDA_ERR_INVALID_ARGUMENT),
+    (dict(n_seqs=-1), KDA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), KDA_ERR_INVALID_ARGUMENT),
+    (dict(d_k=0, d_v=0), KDA_ERR_INVALID_ARGUMENT),
+])
+def test_workspace_size_rejects(lib, kw, code):
+    assert ws_status(lib, desc(**kw))[0] == code
+
+
+def test_workspace_size_null(lib):
+    assert ws_status(lib, None)[0] == KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_chunk_forward_workspace_size(ctypes.byref(desc()), None) == KDA_ERR_INVALID_ARGUMENT
+
+
+def fake_args(lib, d):
+    """Valid-looking, non-overlapping fake device addresses for every buffer."""
+    st, ws = ws_status(lib, d)
+    assert st == KDA_OK
+    a = {name: (i + 1) * 64 * GB for i, name in enumerate(
+        ["q", "k", "v", "g", "beta", "h0", "cu", "o", "ht", "ws"])}
+    a["ws_bytes"] = ws
+    if d.n_seqs == 0:
+        a["cu"] = None
+    return a
+
+
+def call(lib, d, a):
+    return _lib.chunk_forward_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["o"],
+                                  a["ht"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: a.update(q=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(beta=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(o=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(k=a["k"] + 8), KDA_ERR_INVALID_ARGUMENT),          # misaligned
+    (lambda a: a.update(ws=a["ws"] + 64), KDA_ERR_INVALID_ARGUMENT),       # workspace alignment
+    (lambda a: a.update(ws=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(ws_bytes=a["ws_bytes"] - 1), KDA_ERR_WORKSPACE_TOO_SMALL),
+    (lambda a: a.update(o=a["q"] + 1024), KDA_ERR_INVALID_ARGUMENT),       # o overlaps q
+    (lambda a: a.update(o=a["h0"]), KDA_ERR_INVALID_ARGUMENT),             # o overlaps h0
+    (lambda a: a.update(ht=a["o"] + 4096), KDA_ERR_INVALID_ARGUMENT),      # ht overlaps o
+    (lambda a: a.update(ht=a["h0"] + 4096), KDA_ERR_INVALID_ARGUMENT),     # partial alias of h0
+    (lambda a: a.update(ws=a["v"]), KDA_ERR_INVALID_ARGUMENT),             # workspace overlaps v
+    (lambda a: a.update(cu=7 * 64 * GB), KDA_ERR_INVALID_ARGUMENT),        # cu without n_seqs
+])
+def test_chunk_forward_rejects(lib, mutate, code):
+    d = desc()
+    a = fake_args(lib, d)
+    mutate(a)
+    assert call(lib, d, a) == code
+
+
+def test_chunk_forward_rejects_bad_desc(lib):
+    a = fake_args(lib, desc())
+    assert call(lib, desc(d_k=96, d_v=96), a) == KDA_ERR_UNSUPPORTED
+    assert call(lib, desc(g_floor=-0.5), a) == KDA_ERR_INVALID_ARGUMENT  # 64 * 0.5 > 16
+    dv = desc(T=300, n_seqs=4)
+    av = fake_args(lib, dv)
+    av["cu"] = None
+    assert call(lib, dv, av) == KDA_ERR_INVALID_ARGUMENT                 # n_seqs without cu
+    av = fake_args(lib, dv)
+    av["cu"] += 2
+    assert call(lib, dv, av) == KDA_ERR_INVALID_ARGUMENT                 # misaligned cu
+
+
+def dec(lib, N=256, H=32, d=128, dtype=KDA_DTYPE_BF16, g_floor=-0.125, **ptrs):
+    p = {name: (i + 1) * 64 * GB for i, name in enumerate(["q", "k", "v", "g", "beta", "state", "o"])}
+    p.update(ptrs)
+    return _lib.decode_step_raw(N, H, d, d, dtype, g_floor, p["q"], p["k"], p["v"], p["g"], p["beta"],
+                                p["state"], p["o"], None)
+
+
+def test_decode_rejects(lib):
+    assert dec(lib, N=-1) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, H=0) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, d=96) == KDA_ERR_UNSUPPORTED
+    assert dec(lib, dtype=5) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, g_floor=0.5) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, q=None) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, state=None) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, o=64 * GB + 4) == KDA_ERR_INVALID_ARGUMENT              # misaligned
+    assert dec(lib, state=64 * GB + 1024) == KDA_ERR_INVALID_ARGUMENT       # state overlaps q
+    assert dec(lib, o=2 * 64 * GB) == KDA_ERR_INVALID_ARGUMENT              # o overlaps k
+    assert dec(lib, N=0) == KDA_OK                                          # nothing to do

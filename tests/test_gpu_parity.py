@@ -1,0 +1,172 @@
+"""HIP path vs the CPU oracle, element by element, on seeded inputs.
+
+Tolerance: max|x - x_ref| / max|x_ref| <= 1e-4 for the fp32 path and <= 1e-2
+for the bf16 path, on the outputs o and on the final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_105_amd as kda
+import oracle
+import synth
+from gpu_util import TOL, f64, gpu_forward, note, oracle_forward, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, T, H, d, dtype, h0=True, lengths=None, g_mode="floored", wid=100, sigma_g=1.0):
+    inp = synth.prefill_inputs(B, T, H, d, d, dtype, wid=wid, sigma_g=sigma_g, h0=h0, lengths=lengths)
+    if g_mode == "weak":
+        inp["g"] = torch.full_like(inp["g"], -1e-3)
+    elif g_mode == "zero":
+        inp["g"] = torch.zeros_like(inp["g"])
+    return inp
+
+
+SMALL = {
+    "cfg0-f32-d64-T256": lambda: synth.workload_inputs(synth.WORKLOADS[0]),
+    "f32-d64-B2-T130": lambda: _case(2, 130, 3, 64, "f32", wid=101),
+    "f32-d64-T1": lambda: _case(1, 1, 2, 64, "f32", wid=102),
+    "f32-d64-T63": lambda: _case(1, 63, 2, 64, "f32", wid=103),
+    "f32-d64-T64-noh0": lambda: _case(1, 64, 2, 64, "f32", h0=False, wid=104),
+    "bf16-d128-T200": lambda: _case(1, 200, 3, 128, "bf16", wid=105),
+    "bf16-d128-B3-T65": lambda: _case(3, 65, 2, 128, "bf16", wid=106),
+    "bf16-d64-B2-T129": lambda: _case(2, 129, 2, 64, "bf16", wid=107),
+    "bf16-d128-varlen": lambda: _case(1, 0, 2, 128, "bf16", lengths=[1, 64, 65, 0, 100, 37], wid=108),
+    "f32-d64-varlen": lambda: _case(1, 0, 2, 64, "f32", lengths=[5, 0, 128, 70], wid=109),
+    "bf16-d128-weak-decay": lambda: _case(1, 300, 2, 128, "bf16", g_mode="weak", wid=110),
+    "f32-d64-weak-decay": lambda: _case(1, 300, 2, 64, "f32", g_mode="weak", wid=111),
+    "f32-d64-no-decay": lambda: _case(1, 256, 2, 64, "f32", g_mode="zero", wid=112),
+    "bf16-d128-no-decay": lambda: _case(1, 256, 2, 128, "bf16", g_mode="zero", wid=113),
+    "bf16-d128-sigma2": lambda: _case(1, 333, 4, 128, "bf16", sigma_g=2.0, wid=114),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_chunk_forward_small(name):
+    inp = SMALL[name]()
+    dtype = "bf16" if inp["q"].dtype == torch.bfloat16 else "f32"
+    note(f"chunk_forward {name} q{tuple(inp['q'].shape)} {dtype}")
+    o, ht = gpu_forward(inp)
+    ro, rht = oracle_forward(inp)
+    eo, eh = rel_err(f64(o), ro), rel_err(f64(ht), rht)
+    print(f"{name}: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
+
+
+def test_config1_full():
+    """B=1, H=16, T=4096, d=128, bf16, nonzero initial state: every output."""
+    inp = synth.workload_inputs(synth.WORKLOADS[1])
+    note("chunk_forward workload 1 full")
+    o, ht = gpu_forward(inp)
+    ro, rht = oracle_forward(inp)
+    eo, eh = rel_err(f64(o), ro), rel_err(f64(ht), rht)
+    print(f"workload1: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_config2_full_sampled_heads():
+    """8 packed sequences, L ~ U[1024, 8192], H=32: every output of 4 heads."""
+    w = synth.WORKLOADS[2]
+    inp = synth.workload_inputs(w)
+    note(f"chunk_forward workload 2 full, lengths {np.diff(inp['cu_seqlens'].numpy()).tolist()}")
+    o, ht = gpu_forward(inp)
+    heads = [0, 7, 19, 31]
+    sub = {key: (val[:, :, heads].contiguous() if key in ("q", "k", "v", "g", "beta") else val)
+           for key, val in inp.items()}
+    ro, rht = oracle_forward(sub)
+    eo = rel_err(f64(o[:, :, heads]), ro)
+    eh = rel_err(f64(ht[:, heads]), rht)
+    print(f"workload2: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_config3_full_sampled():
+    """T = 1,048,576, H=16: final state and o at 96 seeded positions of one
+    head (64 uniform positions plus 32 at chunk offsets 0..7)."""
+    w = synth.WORKLOADS[3]
+    note("chunk_forward workload 3 full (inputs generated on the GPU)")
+    inp = synth.workload_inputs(w, device="cuda")
+    o, ht = kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"])
+    torch.cuda.synchronize()
+    h = 5
+    sub = {key: inp[key][:, :, h:h + 1].cpu() for key in ("q", "k", "v", "g", "beta")}
+    sub["h0"] = inp["h0"][:, h:h + 1].cpu()
+    pos = synth.sample_positions(w.wid, w.T, 64)
+    rng = np.random.default_rng(3)
+    pos += sorted(int(64 * c + off) for c, off in zip(rng.integers(0, w.T // 64, 32), np.arange(32) % 8))
+    o_s = f64(o[0, pos, h])
+    ht_s = f64(ht[:, h])
+    del o, ht, inp
+    torch.cuda.empty_cache()
+    ro, rht = oracle_forward(sub)
+    eo = rel_err(o_s, ro[0, pos, 0])
+    eh = rel_err(ht_s, rht[:, 0])
+    print(f"workload3 head {h}: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("d,dtype", [(64, "f32"), (128, "f32"), (64, "bf16"), (128, "bf16")])
+def test_decode_small(d, dtype):
+    N, H, steps = 5, 3, 6
+    inp = synth.decode_inputs(N, H, d, d, steps, dtype, wid=120 + d)
+    note(f"decode N{N} H{H} d{d} {dtype} x{steps}")
+    state = inp["state"].cuda()
+    ref_state = inp["state"].double().numpy()
+    for s in range(steps):
+        args = [inp[key][s].cuda() for key in ("q", "k", "v", "g", "beta")]
+        o = kda.decode_step(*args, state)
+        torch.cuda.synchronize()
+        ro, ref_state = oracle.decode_step(*(inp[key][s] for key in ("q", "k", "v", "g", "beta")),
+                                           ref_state)
+        eo = rel_err(f64(o), ro)
+        assert eo <= TOL[dtype], (s, eo)
+    es = rel_err(f64(state), ref_state)
+    print(f"decode d{d} {dtype}: last err_o={eo:.3e} err_state={es:.3e}")
+    assert es <= TOL[dtype]
+
+
+def test_decode_config4_1000_steps():
+    """N=256, H=32, d=128, 1000 steps from a 0.02 N(0,1) state.  The oracle
+    follows 16 seeded (sequence, head) pairs through every step; o is compared
+    at steps 1, 2, 3, 10, 100, 500, 999, 1000 and 8 seeded others, and the
+    final state of those pairs; the whole state is compared after step 1."""
+    w = synth.WORKLOADS[4]
+    note("decode workload 4, 1000 steps (inputs generated on the GPU)")
+    inp = synth.decode_inputs(w.N, w.H, w.dk, w.dv, w.steps, w.dtype, wid=w.wid, device="cuda")
+    state = inp["state"].clone()
+    rng = np.random.default_rng(4)
+    check = sorted({1, 2, 3, 10, 100, 500, 999, 1000} | set(int(x) for x in rng.integers(4, 999, 8)))
+    pairs_n = rng.integers(0, w.N, 16)
+    pairs_h = rng.integers(0, w.H, 16)
+    outs = {}
+    state1 = None
+    for s in range(1, w.steps + 1):
+        o = kda.decode_step(inp["q"][s - 1], inp["k"][s - 1], inp["v"][s - 1], inp["g"][s - 1],
+                            inp["beta"][s - 1], state)
+        if s in check:
+            outs[s] = o[pairs_n, pairs_h].cpu()
+        if s == 1:
+            state1 = state.cpu()
+    torch.cuda.synchronize()
+    # whole state after one step
+    r1o, r1 = oracle.decode_step(*(inp[key][0].cpu() for key in ("q", "k", "v", "g", "beta")),
+                                 inp["state"].cpu())
+    e1 = rel_err(state1.double().numpy(), r1)
+    assert e1 <= TOL["bf16"], e1
+    # 16 pairs through all steps
+    sub = {key: inp[key][:, pairs_n, pairs_h].unsqueeze(2).cpu() for key in ("q", "k", "v", "g", "beta")}
+    ref_state = inp["state"][pairs_n, pairs_h].unsqueeze(1).cpu().double().numpy()
+    worst = 0.0
+    for s in range(1, w.steps + 1):
+        ro, ref_state = oracle.decode_step(*(sub[key][s - 1] for key in ("q", "k", "v", "g", "beta")),
+                                           ref_state)
+        if s in outs:
+            e = rel_err(outs[s].double().numpy(), ro[:, 0])
+            worst = max(worst, e)
+            assert e <= TOL["bf16"], (s, e)
+    es = rel_err(state[pairs_n, pairs_h].cpu().double().numpy(), ref_state[:, 0])
+    print(f"workload4: step1 state err={e1:.3e} worst o err={worst:.3e} final state err={es:.3e}")
+    assert es <= TOL["bf16"]
