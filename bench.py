@@ -1,0 +1,273 @@
+"""Throughput of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one ``kda_chunk_forward`` over the prefill workload B=1, H=16,
+T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v/g/o, fp32 beta and state, nonzero
+initial state (the workload the headline tokens/s figure is quoted on).  The
+decode leg then times ``kda_decode_step`` on 256 sequences x 32 heads,
+d=128, fp32 state [256, 32, 128, 128] updated in place, over consecutive steps
+with fresh pre-staged inputs per step.  Inputs are seeded synthetic tensors
+(package ``synth``) already resident in device memory when timing starts.
+
+The prefill inputs are replicated over enough distinct buffer sets that their
+total exceeds the 256 MB last-level cache several times; consecutive steps
+cycle through them, so each step reads its inputs from HBM, not from cache.
+
+Prints ONE JSON line.  ``roofline`` describes the dominant kernel work, the
+chunked forward call, against HBM: algorithmic bytes per call divided by the
+call's mean duration from HIP events recorded on the launch stream.
+``cpu_baseline`` times the fp64 CPU oracle on the host cores (a baseline, not
+a target).  Other legs: ``--copy-calib MiB`` runs only a device copy of known
+size (for scaling the HBM byte counters), ``--only prefill|decode`` runs one
+leg, ``--no-cpu`` skips the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+LLC_BYTES = 256 << 20          # MI355X last-level (infinity) cache
+
+# Algorithmic work and compulsory traffic of the chunked forward per (token,
+# head) at d_k = d_v = 128, chunk 64 (multiply-adds counted over the needed
+# triangles only, FLOP = 2 MAC):
+#   3 d^2                     state products Wk S, Qt S, Kb^T U
+#   d (C - 1) / 2             strict-lower key Gram
+#   4 d (C + 1) / 2           Wk, Wv, P, P U (lower triangles incl. diagonal)
+#   (C - 1)(C - 2) / 6        triangular inverse
+FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 128 * 63 // 2 + 4 * 128 * 65 // 2 + 63 * 62 // 6)
+# bf16 q, k, v, g read + bf16 o written (2 B x 128 each) + fp32 beta
+BYTES_PER_TOKEN_HEAD = 5 * 2 * 128 + 4
+STATE_BYTES = 128 * 128 * 4    # one fp32 state matrix (h0 read, ht written)
+
+PREFILL = dict(B=1, T=4096, H=16, d=128, wid=1)
+DECODE = dict(N=256, H=32, d=128, wid=4)
+CPU_SAMPLE_SECONDS = 10.0
+
+PREFILL_SOURCES = ("kda_chunk.hip", "kda_device.h", "kda_api.cpp")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_105_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, digest: str):
+    """HBM bytes per call from a committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, _, val = line.partition("=")
+            vals[key.strip()] = val.strip()
+    if vals.get("source_digest") != digest or "hbm_bytes_per_call" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_call"])
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed prefill calls")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=1000, help="timed decode steps")
+    ap.add_argument("--only", choices=("prefill", "decode", "both"), default="both")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
+                    help="only run device copies of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calib(mib: int) -> None:
+    import torch
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n, "dispatches": 5}))
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    B, T, H, d, wid = (PREFILL[k] for k in ("B", "T", "H", "d", "wid"))
+    log(f"prefill inputs B={B} T={T} H={H} d={d} bf16 (generated on the GPU)")
+    base = synth.prefill_inputs(B, T, H, d, d, "bf16", wid=wid, h0=True, device="cuda")
+    set_bytes = 4 * base["q"].numel() * 2 + base["beta"].numel() * 4 + base["q"].numel() * 2
+    n_sets = max(2, math.ceil(3 * LLC_BYTES / set_bytes))
+    sets = []
+    for i in range(n_sets):
+        s = {key: base[key].clone() for key in ("q", "k", "v", "g", "beta", "h0")}
+        s["o"] = torch.empty_like(base["q"])
+        s["ht"] = torch.empty_like(base["h0"])
+        sets.append(s)
+    del base
+    ws = torch.empty(kda.workspace_bytes(B, T, H, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(s):
+        kda.chunk_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], h0=s["h0"], o=s["o"], ht=s["ht"],
+                          workspace=ws)
+
+    log(f"prefill warmup {warmup} over {n_sets} buffer sets of {set_bytes / 1e6:.1f} MB")
+    for i in range(warmup):
+        call(sets[i % n_sets])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(sets[i % n_sets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    mean_call = sum(durs) / len(durs)
+    log(f"prefill {steps} calls: wall {wall * 1e3:.3f} ms, mean call {mean_call * 1e6:.2f} us")
+    token_heads = B * T * H
+    bytes_call = token_heads * BYTES_PER_TOKEN_HEAD + 2 * B * H * STATE_BYTES
+    flop_call = token_heads * FLOP_PER_TOKEN_HEAD
+    return dict(wall=wall, mean_call=mean_call, min_call=min(durs), tokens=B * T,
+                bytes_call=bytes_call, flop_call=flop_call, n_sets=n_sets)
+
+
+def bench_decode(steps: int, warmup: int):
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    N, H, d, wid = (DECODE[k] for k in ("N", "H", "d", "wid"))
+    n_in = steps + warmup
+    log(f"decode inputs N={N} H={H} d={d} bf16, {n_in} pre-staged steps (generated on the GPU)")
+    inp = synth.decode_inputs(N, H, d, d, n_in, "bf16", wid=wid, device="cuda")
+    state = inp["state"]
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        kda.decode_step(inp["q"][i], inp["k"][i], inp["v"][i], inp["g"][i], inp["beta"][i], state, o=o)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    mean_step = sum(durs) / len(durs)
+    log(f"decode {steps} steps: wall {wall * 1e3:.3f} ms, mean step {mean_step * 1e6:.2f} us")
+    state_b = N * H * d * d * 4
+    bytes_step = 2 * state_b + N * H * (5 * d * 2 + 4)
+    return dict(wall=wall, mean_step=mean_step, steps=steps, bytes_step=bytes_step)
+
+
+def cpu_baseline():
+    import oracle
+    import synth
+
+    B, T, H, d, wid = (PREFILL[k] for k in ("B", "T", "H", "d", "wid"))
+    inp = synth.prefill_inputs(B, T, H, d, d, "bf16", wid=wid, h0=True)
+    orc = oracle.default()
+    threads = min(orc.max_threads(), B * H)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= CPU_SAMPLE_SECONDS:
+            break
+    log(f"cpu oracle: {reps} full passes in {el:.2f} s on {threads} threads")
+    return {"value": reps * B * T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full passes of the prefill workload (B=1, H=16, T=4096, d=128), fp64 "
+                      f"token-by-token recurrence, OpenMP over the 16 heads, {el:.1f} s"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the KDA path shards by sequence and head with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calib:
+        copy_calib(args.copy_calib)
+        return 0
+    out = {"metric": "KDA prefill tokens/s/GPU + % MFMA peak; decode steps/s + % HBM peak",
+           "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                                    "beta sigmoid(N(0,1)), g max(-softplus(N(0,1)), -0.125))",
+           "config": {"workload": "kda-prefill-bf16-B1-H16-T4096-d128-chunk64", "B": 1, "T": 4096,
+                      "H": 16, "d_k": 128, "d_v": 128, "chunk": 64, "h0": "0.02 N(0,1)"}}
+    if args.only in ("prefill", "both"):
+        p = bench_prefill(args.steps, args.warmup)
+        out["ms_per_step"] = p["wall"] / args.steps * 1e3
+        out["value"] = p["tokens"] * args.steps / p["wall"]
+        gbs = p["bytes_call"] / p["mean_call"] / 1e9
+        traffic = read_traffic("kda_chunk_forward_prefill_T4096_H16_traffic.txt",
+                               source_digest(PREFILL_SOURCES))
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
+                           "kernel": "kda_chunk_forward call (kda_chunk_local + kda_state_pass)",
+                           "algorithmic_bytes": p["bytes_call"], "mean_call_us": p["mean_call"] * 1e6}
+        tf = p["flop_call"] / p["mean_call"] / 1e12
+        out["mfma"] = {"achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop": p["flop_call"]}
+        out["config"]["buffer_sets"] = p["n_sets"]
+    if args.only in ("decode", "both"):
+        dd = bench_decode(args.decode_steps, max(1, args.warmup))
+        gbs = dd["bytes_step"] / dd["mean_step"] / 1e9
+        out["decode"] = {"workload": "kda-decode-bf16-N256-H32-d128-fp32-state-in-place",
+                         "value": dd["steps"] / dd["wall"], "unit": "steps/s",
+                         "mean_step_us": dd["mean_step"] * 1e6,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gbs / PEAK_HBM_GBS, "kernel": "kda_decode",
+                                      "algorithmic_bytes": dd["bytes_step"],
+                                      "traffic": read_traffic("kda_decode_N256_H32_traffic.txt",
+                                                              source_digest(("kda_decode.hip",
+                                                                             "kda_device.h")))}}
+        if out["value"] is None:
+            out["value"] = None
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
