@@ -56,7 +56,7 @@ PREFILL = dict(B=1, T=4096, H=16, d=128, wid=1)
 DECODE = dict(N=256, H=32, d=128, wid=4)
 CPU_SAMPLE_SECONDS = 10.0
 
-PREFILL_SOURCES = ("kda_chunk.hip", "kda_device.h", "kda_api.cpp")
+PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
 
 
 def log(msg: str) -> None:

@@ -41,8 +41,7 @@ struct Sizes {
   size_t x_bytes;     // one of q, k, v, g, o
   size_t beta_bytes;
   size_t state_bytes; // h0 or ht
-  size_t n_chunks;    // upper bound of chunks over all sequences
-  size_t ws_bytes;
+  kda::SegPlan plan;  // segments and workspace
 };
 
 int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
@@ -55,9 +54,8 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   if ((double)d->chunk * -(double)d->g_floor > 16.0) return KDA_ERR_INVALID_ARGUMENT;
   if (d->d_k != d->d_v) return KDA_ERR_UNSUPPORTED;
   if (d->d_k != 64 && d->d_k != 128) return KDA_ERR_UNSUPPORTED;
-  if (d->chunk != 64) return KDA_ERR_UNSUPPORTED;
-  const size_t per = kda::chunk_bytes(d->dtype == KDA_DTYPE_BF16, d->d_k);
-  if (per == 0) return KDA_ERR_UNSUPPORTED;  // fp32 with d = 128
+  if (d->chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if (d->dtype == KDA_DTYPE_F32 && d->d_k != 64) return KDA_ERR_UNSUPPORTED;  // fp32 tiles fit LDS at d = 64
 
   const size_t B = (size_t)d->B, T = (size_t)d->T, H = (size_t)d->H, D = (size_t)d->d_k;
   s->n_states = d->n_seqs > 0 ? (size_t)d->n_seqs : B;
@@ -69,14 +67,11 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   size_t sh, sd;
   if (!mul(s->n_states, H, &sh) || !mul(sh, D * D, &sd) || !mul(sd, 4, &s->state_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
-  if (d->n_seqs > 0)
-    s->n_chunks = (T + 63) / 64 + (size_t)d->n_seqs;
-  else
-    s->n_chunks = B * ((T + 63) / 64);
-  if (s->n_chunks > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  size_t ch;
-  if (!mul(s->n_chunks, H, &ch) || !mul(ch, per, &s->ws_bytes)) return KDA_ERR_INVALID_ARGUMENT;
   if (s->tokens > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
+  if (!kda::plan_segments(d->d_k, rows, (int64_t)d->T, d->H, d->n_seqs > 0, &s->plan))
+    return KDA_ERR_UNSUPPORTED;
+  if (s->plan.n_seg_bound > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 
@@ -102,7 +97,7 @@ int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
   Sizes s;
   const int st = check_desc(d, &s);
   if (st != KDA_OK) return st;
-  *bytes = s.ws_bytes;
+  *bytes = s.plan.ws_bytes;
   return KDA_OK;
 }
 
@@ -119,9 +114,10 @@ int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, c
   for (const void* p : ptrs)
     if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
-  if (s.ws_bytes > 0) {
+  const size_t ws_need = s.plan.ws_bytes;
+  if (ws_need > 0) {
     if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < s.ws_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   }
   if (has_tokens) {
     const Range ro = range(o, s.x_bytes);
@@ -138,8 +134,8 @@ int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, c
       if (overlap(rh, r)) return KDA_ERR_INVALID_ARGUMENT;
     if (h0 && h0 != ht && overlap(rh, range(h0, s.state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
   }
-  if (workspace && s.ws_bytes > 0) {
-    const Range rw = range(workspace, s.ws_bytes);
+  if (workspace && ws_need > 0) {
+    const Range rw = range(workspace, ws_need);
     const Range all[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes), range(g, s.x_bytes),
                          range(beta, s.beta_bytes), range(o, s.x_bytes), range(h0, s.state_bytes),
                          range(ht, s.state_bytes)};
@@ -148,9 +144,9 @@ int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, c
   }
   if (!ht && s.tokens == 0) return KDA_OK;  // nothing to write
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
-  const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H,
-                                          (int64_t)(has_tokens ? s.n_chunks : 0), d->g_floor, q, k, v, g,
-                                          beta, h0, cu_seqlens, o, ht, workspace, stream);
+  const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
+                                          d->g_floor, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace,
+                                          stream);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -31,13 +31,17 @@ typedef uint16_t bf16_t;  // storage type of bf16 tensors in memory
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
-// round to nearest even; NaN stays NaN
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats to two bf16 in one instruction (v_cvt_pk_bf16_f32: round to
+// nearest even, NaN stays NaN); a in the low half
+__device__ __forceinline__ bf16x2 f32x2_to_bf16x2(float a, float b) {
+  return __builtin_convertvector((f32x2){a, b}, bf16x2);
+}
+// Single halves are read from the packed 32-bit word: bit-casting one lane
+// of a bf16 vector to an integer returned the other lane with this compiler.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
-    return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return (bf16_t)__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(f, 0.f));
 }
 
 // Element-type traits: storage type, fragment type, k-block of one MMA step.
@@ -84,27 +88,19 @@ __device__ __forceinline__ bf16x8 frag_rows(const bf16_t* X, int ld, int row, in
 // bf16 fragment read from an fp32 row-major array (rounded on the fly)
 __device__ __forceinline__ bf16x8 frag_rows_f32_to_bf16(const float* X, int ld, int row, int k0, int g) {
   const float* p = X + row * ld + k0 + 4 * g;
-  f32x4 lo = *(const f32x4*)p;
-  f32x4 hi = *(const f32x4*)(p + 16);
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = __builtin_bit_cast(__bf16, f32_to_bf16(lo[e]));
-    r[e + 4] = __builtin_bit_cast(__bf16, f32_to_bf16(hi[e]));
-  }
-  return r;
+  const f32x4 lo = *(const f32x4*)p;
+  const f32x4 hi = *(const f32x4*)(p + 16);
+  const bf16x2 a = f32x2_to_bf16x2(lo[0], lo[1]), b = f32x2_to_bf16x2(lo[2], lo[3]);
+  const bf16x2 c = f32x2_to_bf16x2(hi[0], hi[1]), d = f32x2_to_bf16x2(hi[2], hi[3]);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // B-fragment from accumulator tiles whose rows run over k.
 __device__ __forceinline__ f32x4 frag_from_acc(const f32x4& t0) { return t0; }
 __device__ __forceinline__ bf16x8 frag_from_acc(const f32x4& t0, const f32x4& t1) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = __builtin_bit_cast(__bf16, f32_to_bf16(t0[e]));
-    r[e + 4] = __builtin_bit_cast(__bf16, f32_to_bf16(t1[e]));
-  }
-  return r;
+  const bf16x2 a = f32x2_to_bf16x2(t0[0], t0[1]), b = f32x2_to_bf16x2(t0[2], t0[3]);
+  const bf16x2 c = f32x2_to_bf16x2(t1[0], t1[1]), d = f32x2_to_bf16x2(t1[2], t1[3]);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Uniform view over the two element types for kernels templated on T.
@@ -127,48 +123,5 @@ template <> struct Frag<bf16_t> {
     return frag_rows_f32_to_bf16(X, ld, row, k0, g);
   }
 };
-
-// ---- workspace layout of one (chunk, head) ------------------------------
-// All operand blocks are stored as whole fragments: [fragment][lane][16 B],
-// so that a wave loads one fragment with one 16-byte load per lane.
-template <typename T, int D> struct ChunkLayout {
-  static constexpr int C = 64;                   // tokens per chunk
-  static constexpr int KB = Elem<T>::KB;
-  static constexpr int FRAG = 64 * 16;           // bytes per fragment
-  static constexpr int NKD = D / KB;             // k-blocks over channels
-  static constexpr int NKC = C / KB;             // k-blocks over tokens
-  static constexpr size_t WK = 0;                              // [4][NKD]
-  static constexpr size_t QT = WK + 4 * NKD * FRAG;            // [4][NKD]
-  static constexpr size_t P = QT + 4 * NKD * FRAG;             // [4][NKC]
-  static constexpr size_t KBT = P + 4 * NKC * FRAG;            // [D/16][NKC]
-  static constexpr size_t WV = KBT + (D / 16) * NKC * FRAG;    // [D/16][4] acc tiles
-  static constexpr size_t WV_TILE = 64 * 4 * sizeof(T);        // bytes per tile
-  static constexpr size_t GL = WV + (D / 16) * 4 * WV_TILE;    // [D] fp32
-  static constexpr size_t BYTES = ((GL + D * 4 + 255) / 256) * 256;
-};
-
-// Chunk bookkeeping: sequence n owns tokens [cu[n], cu[n+1]) and chunks
-// [chunk_base(n), chunk_base(n) + ceil(len/64)).
-struct SeqInfo {
-  int64_t tok0;
-  int len;
-  int64_t chunk0;
-};
-
-__device__ __forceinline__ SeqInfo seq_info(const int32_t* cu, int n, int T) {
-  SeqInfo s;
-  if (cu) {
-    int64_t base = 0;
-    for (int m = 0; m < n; ++m) base += (cu[m + 1] - cu[m] + 63) / 64;
-    s.tok0 = cu[n];
-    s.len = cu[n + 1] - cu[n];
-    s.chunk0 = base;
-  } else {
-    s.tok0 = (int64_t)n * T;
-    s.len = T;
-    s.chunk0 = (int64_t)n * ((T + 63) / 64);
-  }
-  return s;
-}
 
 }  // namespace kda

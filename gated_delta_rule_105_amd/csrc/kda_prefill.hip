@@ -1,0 +1,841 @@
+// Chunked KDA forward for gfx950: two chunk passes around a segment scan.
+//
+// Chunk algebra (per sequence and head; chunk rows r = 0..63, S the state
+// entering the chunk, g floored, G = running sum of g over the chunk's rows,
+// G_L its last row, gamma = e^{G_L} per key channel):
+//   Qt = Q e^{G},  Kt = K e^{G},  Kh = K e^{-G}
+//   A  = diag(beta) strict_lower(Kt Kh^T),   T = (I + A)^{-1}
+//   Wk = T diag(beta) Kt,   Wv = T diag(beta) V,   P = lower_incl(Qt Kh^T)
+//   U  = Wv - Wk S,   O = Qt S + P U,   S <- diag(gamma) (S + Kh^T U)
+// which is the recurrence S_t = (I - b k k^T) diag(a) S_{t-1} + b k v^T,
+// o_t = S_t^T q_t unrolled over one chunk (K e^{G_L - G} = diag(gamma) Kh
+// folds the chunk-end decay into one row scaling).  Sources: chunk-parallel
+// computation with an inter-chunk recurrence built from blocked matrix
+// products, "Kimi K3 深度拆解" (chenxutan.com), 4.2; the lower bound on the
+// log-decay, which keeps e^{-G} finite so that the diagonal block is a dense
+// product too, "3 分钟看懂 Kimi K3" (landx.limxdynamics.com), "第一条主线",
+// Figure 3, and "Kimi K3 发布 47 页技术报告" (163.com), 01.
+//
+// One chunk maps the state affinely, S -> M_j S + B_j.  Every sequence is cut
+// into segments of L chunks; the composition of a segment's maps is again
+// affine, S_out = M S_in + B.  Three launches:
+//   1. kda_seg_summary (one workgroup per (segment, head), all in parallel):
+//      runs the segment's chunks on the augmented state [B | M], started from
+//      [0 | I], with the value part of U switched off for the M columns, and
+//      writes B and M.  The last segment of a sequence is skipped: no later
+//      segment needs its map.
+//   2. kda_seg_scan (one workgroup per (sequence, head, 16 state columns)):
+//      S_0 = h0, S_{s+1} = M_s S_s + B_s, writing every segment's incoming
+//      state.  M S is done as three bf16 products of a hi/lo split of both
+//      factors (about fp32 accuracy).
+//   3. kda_seg_forward (one workgroup per (segment, head), all in parallel):
+//      the full chunk recurrence from the segment's incoming state, writing o
+//      and, for the last segment, the final state.
+// The chunk-local part (decay prefix sums, the Gram blocks, the triangular
+// inverse, Wk and Wv) is recomputed in both chunk passes from the inputs;
+// nothing per chunk goes through device memory.  Within a workgroup, wave w
+// owns 16 value columns of S (32 columns of [B | M] in pass 1): columns of
+// U, O and S never mix, so the state products need no exchange.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = kChunk;
+
+// ---- LDS layout of the chunk engine -------------------------------------
+template <typename T, int D> struct Lds {
+  static constexpr int PADT = 16 / (int)sizeof(T);
+  static constexpr int LDT = D + PADT;  // token-major arrays [64][LDT]
+  static constexpr int LDC = C + PADT;  // channel-major arrays [D][LDC]; P [64][LDC]
+  static constexpr int LDF = C + 4;     // fp32 [64][LDF]
+  static constexpr int ROW_T = C * LDT * (int)sizeof(T);
+  static constexpr int ROW_F = C * LDF * 4;
+  static constexpr int ROW = ((ROW_T > ROW_F ? ROW_T : ROW_F) + 15) / 16 * 16;
+  static constexpr int COL = (D * LDC * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int PSZ = (C * LDC * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int Q = 0;              // q, then Qt
+  static constexpr int K = ROW;            // k, then Kt, then Wk
+  static constexpr int G = 2 * ROW;        // g, then Kh, then T (fp32)
+  static constexpr int V = 3 * ROW;        // v, then A (fp32)
+  static constexpr int KT = 4 * ROW;       // Kt^T
+  static constexpr int KH = KT + COL;      // Kh^T
+  static constexpr int VT = KH + COL;      // V^T
+  static constexpr int P = VT + COL;       // P
+  static constexpr int BETA = P + PSZ;     // fp32 [64]
+  static constexpr int PART = BETA + C * 4;  // fp32 [4][D] partial sums of g
+  static constexpr int GL = PART + 4 * D * 4;  // fp32 [D] gamma
+  static constexpr int BYTES = GL + D * 4;
+};
+
+// ---- sequences and segments ---------------------------------------------
+__device__ __forceinline__ int n_segments(int len, int L) { return ((len + C - 1) / C + L - 1) / L; }
+
+struct Seg {
+  int64_t tok0;  // first packed token of the sequence
+  int len;       // tokens of the sequence
+  int n;         // sequence
+  int s;         // segment within the sequence
+  int nseg;      // segments of the sequence
+};
+
+// Global segment gs -> its sequence.  false when gs is past the last one.
+__device__ __forceinline__ bool locate(const int32_t* cu, int n_rows, int T, int L, int64_t gs, Seg& r) {
+  if (!cu) {
+    const int per = n_segments(T, L);
+    if (per == 0) return false;
+    const int64_t n = gs / per;
+    if (n >= n_rows) return false;
+    r.n = (int)n;
+    r.s = (int)(gs % per);
+    r.nseg = per;
+    r.tok0 = n * (int64_t)T;
+    r.len = T;
+    return true;
+  }
+  int64_t base = 0;
+  for (int n = 0; n < n_rows; ++n) {
+    const int len = cu[n + 1] - cu[n];
+    const int ns = n_segments(len, L);
+    if (gs < base + ns) {
+      r.n = n;
+      r.s = (int)(gs - base);
+      r.nseg = ns;
+      r.tok0 = cu[n];
+      r.len = len;
+      return true;
+    }
+    base += ns;
+  }
+  return false;
+}
+
+// ---- raw chunk inputs: global -> registers (prefetch) -> LDS -------------
+template <typename T, int D, int NT, bool WITH_Q> struct Raw {
+  typedef Lds<T, D> M;
+  static constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  static constexpr int VPR = D / EPV;              // vectors per token row
+  static constexpr int PER = C * VPR / NT;         // vectors per thread per tensor
+  static_assert(PER * NT == C * VPR, "thread count must divide the chunk");
+  uint4 q[WITH_Q ? PER : 1], k[PER], v[PER], g[PER];
+  float beta;
+
+  __device__ __forceinline__ void load(const T* Q, const T* K, const T* V, const T* G, const float* B,
+                                       int64_t tok0, int clen, int H, int h, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
+      const uint4 z = {0u, 0u, 0u, 0u};
+      if (t < clen) {
+        const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;
+        if (WITH_Q) q[j] = *(const uint4*)(Q + off);
+        k[j] = *(const uint4*)(K + off);
+        v[j] = *(const uint4*)(V + off);
+        g[j] = *(const uint4*)(G + off);
+      } else {
+        if (WITH_Q) q[j] = z;
+        k[j] = z;
+        v[j] = z;
+        g[j] = z;
+      }
+    }
+    beta = (tid < clen) ? B[(size_t)(tok0 + tid) * H + h] : 0.f;
+  }
+
+  __device__ __forceinline__ void store(unsigned char* smem, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
+      const int off = t * M::LDT * (int)sizeof(T) + cv * 16;
+      if (WITH_Q) *(uint4*)(smem + M::Q + off) = q[j];
+      *(uint4*)(smem + M::K + off) = k[j];
+      *(uint4*)(smem + M::V + off) = v[j];
+      *(uint4*)(smem + M::G + off) = g[j];
+    }
+    if (tid < C) ((float*)(smem + M::BETA))[tid] = beta;
+  }
+
+  // Chunk output [64][LDT] staged in LDS -> o rows tok0 .. tok0 + clen - 1.
+  __device__ __forceinline__ static void store_out(const unsigned char* stage, T* o, int64_t tok0, int clen, int H,
+                                                   int h, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
+      if (t < clen)
+        *(uint4*)(o + ((size_t)(tok0 + t) * H + h) * D + cv * EPV) =
+            *(const uint4*)(stage + t * M::LDT * (int)sizeof(T) + cv * 16);
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) { return Elem<T>::to_f32(x); }
+
+// ---- element-wise stage: prefix sums of the floored log-decay and the
+// decay-scaled operands.  Thread (channel c, quarter tq) owns 16 rows.
+template <typename T, int D, bool WITH_Q>
+__device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, int tid) {
+  typedef Lds<T, D> M;
+  constexpr int LDT = M::LDT, LDC = M::LDC;
+  T* sQ = (T*)(smem + M::Q);
+  T* sK = (T*)(smem + M::K);
+  T* sG = (T*)(smem + M::G);
+  const T* sV = (const T*)(smem + M::V);
+  T* sKT = (T*)(smem + M::KT);
+  T* sKH = (T*)(smem + M::KH);
+  T* sVT = (T*)(smem + M::VT);
+  float* sPart = (float*)(smem + M::PART);
+  float* sGL = (float*)(smem + M::GL);
+  const int c = tid % D, tq = tid / D, t0 = 16 * tq;
+
+  float gf[16];
+  float part = 0.f;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    float x = to_f32(sG[(t0 + s) * LDT + c]);
+    x = x < g_floor ? g_floor : x;  // NaN stays NaN
+    gf[s] = x;
+    part += x;
+  }
+  sPart[tq * D + c] = part;
+  __syncthreads();
+  float off = 0.f, gl = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float x = sPart[p * D + c];
+    off += p < tq ? x : 0.f;
+    gl += x;
+  }
+  if (tq == 0) sGL[c] = __expf(gl);
+
+  float gam = off;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t kt[8], kh[8], vt[8];
+#pragma unroll
+    for (int s = 0; s < 16; s += 2) {
+      float e[2], ei[2], kv[2], qv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        gam += gf[s + u];
+        e[u] = __expf(gam);
+        ei[u] = __expf(-gam);
+        kv[u] = to_f32(sK[(t0 + s + u) * LDT + c]);
+        if (WITH_Q) qv[u] = to_f32(sQ[(t0 + s + u) * LDT + c]);
+      }
+      const bf16x2 a = f32x2_to_bf16x2(kv[0] * e[0], kv[1] * e[1]);
+      const bf16x2 b = f32x2_to_bf16x2(kv[0] * ei[0], kv[1] * ei[1]);
+      // halves are taken from the packed word: bit-casting a single lane of
+      // a bf16 vector is not reliable with this compiler
+      kt[s / 2] = __builtin_bit_cast(uint32_t, a);
+      kh[s / 2] = __builtin_bit_cast(uint32_t, b);
+      vt[s / 2] = (uint32_t)sV[(t0 + s) * LDT + c] | ((uint32_t)sV[(t0 + s + 1) * LDT + c] << 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        sK[(t0 + s + u) * LDT + c] = (bf16_t)(kt[s / 2] >> (16 * u));
+        sG[(t0 + s + u) * LDT + c] = (bf16_t)(kh[s / 2] >> (16 * u));
+      }
+      if (WITH_Q) {
+        const uint32_t qq = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(qv[0] * e[0], qv[1] * e[1]));
+        sQ[(t0 + s) * LDT + c] = (bf16_t)qq;
+        sQ[(t0 + s + 1) * LDT + c] = (bf16_t)(qq >> 16);
+      }
+    }
+    uint4* dkt = (uint4*)(sKT + c * LDC + t0);
+    uint4* dkh = (uint4*)(sKH + c * LDC + t0);
+    uint4* dvt = (uint4*)(sVT + c * LDC + t0);
+    dkt[0] = (uint4){kt[0], kt[1], kt[2], kt[3]};
+    dkt[1] = (uint4){kt[4], kt[5], kt[6], kt[7]};
+    dkh[0] = (uint4){kh[0], kh[1], kh[2], kh[3]};
+    dkh[1] = (uint4){kh[4], kh[5], kh[6], kh[7]};
+    dvt[0] = (uint4){vt[0], vt[1], vt[2], vt[3]};
+    dvt[1] = (uint4){vt[4], vt[5], vt[6], vt[7]};
+  } else {
+    float kt[16], kh[16], vt[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int t = t0 + s;
+      gam += gf[s];
+      const float e = __expf(gam), ei = __expf(-gam);
+      const float kv = sK[t * LDT + c];
+      if (WITH_Q) sQ[t * LDT + c] = sQ[t * LDT + c] * e;
+      kt[s] = kv * e;
+      kh[s] = kv * ei;
+      vt[s] = sV[t * LDT + c];
+      sK[t * LDT + c] = kt[s];
+      sG[t * LDT + c] = kh[s];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *(f32x4*)((float*)sKT + c * LDC + t0 + 4 * u) = (f32x4){kt[4 * u], kt[4 * u + 1], kt[4 * u + 2], kt[4 * u + 3]};
+      *(f32x4*)((float*)sKH + c * LDC + t0 + 4 * u) = (f32x4){kh[4 * u], kh[4 * u + 1], kh[4 * u + 2], kh[4 * u + 3]};
+      *(f32x4*)((float*)sVT + c * LDC + t0 + 4 * u) = (f32x4){vt[4 * u], vt[4 * u + 1], vt[4 * u + 2], vt[4 * u + 3]};
+    }
+  }
+  __syncthreads();
+}
+
+// ---- Gram blocks: A = diag(beta) strict_lower(Kt Kh^T) (fp32) and
+// P = lower_incl(Qt Kh^T) (operand type), as 16 x 16 tiles.  Only tiles on
+// or below the diagonal are computed; of the upper tiles only the P tiles
+// that share a 32-wide k-block with a needed one are read, and those are
+// zeroed (bf16 path).
+__device__ __forceinline__ void tile_of(int j, int& rt, int& ct) {
+  const uint64_t R = 0x3333222110ull, K = 0x3210210100ull;  // lower tiles in row order
+  rt = (int)((R >> (4 * j)) & 15);
+  ct = (int)((K >> (4 * j)) & 15);
+}
+
+template <typename T, int D, int NW, bool WITH_P>
+__device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
+  typedef Lds<T, D> M;
+  constexpr int KB = Elem<T>::KB, NKD = D / KB, LDT = M::LDT, LDC = M::LDC, LDF = M::LDF;
+  const T* sQ = (const T*)(smem + M::Q);
+  const T* sK = (const T*)(smem + M::K);
+  const T* sG = (const T*)(smem + M::G);
+  float* sA = (float*)(smem + M::V);
+  T* sP = (T*)(smem + M::P);
+  const float* sBeta = (const float*)(smem + M::BETA);
+  const int idx = lane & 15, gq = lane >> 4;
+  constexpr int NJ = WITH_P ? 20 : 10;  // A tiles 0..9, then P tiles
+#pragma unroll
+  for (int n = 0; n < (NJ + NW - 1) / NW; ++n) {
+    const int j = wave + n * NW;  // wave-uniform
+    if (j < NJ) {
+      const bool isP = j >= 10;
+      int rt, ct;
+      tile_of(isP ? j - 10 : j, rt, ct);
+      const T* X = isP ? sQ : sK;
+      typename Frag<T>::type fa[NKD], fb[NKD];
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) {
+        fa[kb] = frag_rows(X, LDT, 16 * rt + idx, kb * KB, gq);
+        fb[kb] = frag_rows(sG, LDT, 16 * ct + idx, kb * KB, gq);
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) acc = mma(fa[kb], fb[kb], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * gq + i, s = 16 * ct + idx;
+        if (isP)
+          sP[r * LDC + s] = Elem<T>::from_f32(s <= r ? acc[i] : 0.f);
+        else
+          sA[r * LDF + s] = s < r ? sBeta[r] * acc[i] : 0.f;
+      }
+    }
+  }
+  if (WITH_P && KB == 32 && wave == NW - 1) {
+    // P tiles (0, 1) and (2, 3)
+#pragma unroll
+    for (int z = 0; z < 2; ++z)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sP[(32 * z + 4 * gq + i) * LDC + 32 * z + 16 + idx] = Elem<T>::from_f32(0.f);
+  }
+  __syncthreads();
+}
+
+// ---- T = (I + A)^{-1}: blocked 4 x 4 over 16 x 16 blocks (fp32) ----------
+// Diagonal blocks by forward substitution (lane idx solves column idx), then
+// T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj by sub-diagonal, with fp32 MFMA.
+template <int LDF>
+__device__ __forceinline__ void tri_inverse(const float* sA, float* sT, int wave, int lane) {
+  const int idx = lane & 15, gq = lane >> 4;
+  if (wave < 4) {
+    const int b0 = 16 * wave;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == idx) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) acc -= sA[(b0 + r) * LDF + b0 + m] * x[m];
+      x[r] = acc;
+    }
+    if (gq == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDF + b0 + idx] = x[r];
+    }
+    const int w = 48 - b0;  // columns right of the diagonal block
+    for (int e = lane; e < 16 * w; e += 64) sT[(b0 + e / w) * LDF + b0 + 16 + e % w] = 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    const int j = wave, i = wave + d;
+    if (i < 4) {
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+      for (int m = j; m < i; ++m) {
+        const f32x4 a = frag_rows(sA, LDF, 16 * i + idx, 16 * m, gq);
+        f32x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = sT[(16 * m + 4 * gq + e) * LDF + 16 * j + idx];
+        X = mma(a, b, X);
+      }
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+      Y = mma(frag_rows(sT, LDF, 16 * i + idx, 16 * i, gq), X, Y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * gq + r) * LDF + 16 * j + idx] = -Y[r];
+    }
+    __syncthreads();
+  }
+}
+
+// A-fragment of T diag(beta) (rows and k both over the chunk's tokens).
+template <typename T, int LDF> struct TbFrag;
+template <int LDF> struct TbFrag<bf16_t, LDF> {
+  __device__ static __forceinline__ bf16x8 get(const float* sT, const float* sBeta, int row, int k0, int g) {
+    const float* p = sT + row * LDF + k0 + 4 * g;
+    const f32x4 lo = *(const f32x4*)p, hi = *(const f32x4*)(p + 16);
+    const f32x4 blo = *(const f32x4*)(sBeta + k0 + 4 * g), bhi = *(const f32x4*)(sBeta + k0 + 16 + 4 * g);
+    const bf16x2 a = f32x2_to_bf16x2(lo[0] * blo[0], lo[1] * blo[1]);
+    const bf16x2 b = f32x2_to_bf16x2(lo[2] * blo[2], lo[3] * blo[3]);
+    const bf16x2 c = f32x2_to_bf16x2(hi[0] * bhi[0], hi[1] * bhi[1]);
+    const bf16x2 d = f32x2_to_bf16x2(hi[2] * bhi[2], hi[3] * bhi[3]);
+    return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+};
+template <int LDF> struct TbFrag<float, LDF> {
+  __device__ static __forceinline__ f32x4 get(const float* sT, const float* sBeta, int row, int k0, int g) {
+    const f32x4 t = *(const f32x4*)(sT + row * LDF + k0 + 4 * g);
+    const f32x4 b = *(const f32x4*)(sBeta + k0 + 4 * g);
+    return (f32x4){t[0] * b[0], t[1] * b[1], t[2] * b[2], t[3] * b[3]};
+  }
+};
+
+// Fragments of T diag(beta) for the four row tiles of the chunk.  Tile rt
+// only needs k-blocks that reach row 16 rt + 15 (T is lower triangular).
+template <typename T, int D> struct WyOps {
+  typedef Lds<T, D> M;
+  typedef typename Frag<T>::type FragT;
+  static constexpr int KB = Elem<T>::KB, NKC = C / KB;
+  FragT a[4][NKC];
+
+  __device__ __forceinline__ void load(const unsigned char* smem, int lane) {
+    const float* sT = (const float*)(smem + M::G);
+    const float* sBeta = (const float*)(smem + M::BETA);
+    const int idx = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+        if (kb * KB <= 16 * rt + 15) a[rt][kb] = TbFrag<T, M::LDF>::get(sT, sBeta, 16 * rt + idx, kb * KB, gq);
+  }
+  // out[rt] = (T diag(beta) X)[16 rt.., 16 ct..] with X^T stored channel-major
+  __device__ __forceinline__ void product(const T* XT, int ct, int lane, f32x4 out[4]) const {
+    const int idx = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+        if (kb * KB <= 16 * rt + 15) acc = mma(a[rt][kb], frag_rows(XT, M::LDC, 16 * ct + idx, kb * KB, gq), acc);
+      out[rt] = acc;
+    }
+  }
+};
+
+// Wk tile (all 64 rows, 16 channels from 16 ct) into LDS, token-major.
+template <typename T, int D>
+__device__ __forceinline__ void store_wk(unsigned char* smem, const WyOps<T, D>& wy, int ct, int lane) {
+  typedef Lds<T, D> M;
+  f32x4 w[4];
+  wy.product((const T*)(smem + M::KT), ct, lane, w);
+  T* sW = (T*)(smem + M::K);
+  const int idx = lane & 15, gq = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * gq + i) * M::LDT + 16 * ct + idx] = Elem<T>::from_f32(w[rt][i]);
+}
+
+// One column tile of the state (rows = D key channels) through one chunk:
+// U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
+// O = Qt S + P U, returned in O[4].  `wv` holds Wv's tiles for this column.
+template <typename T, int D, bool WITH_O>
+__device__ __forceinline__ void state_step(const unsigned char* smem, f32x4 (&S)[D / 16], const f32x4 (&wv)[4],
+                                           f32x4 (&O)[4], int lane) {
+  typedef Lds<T, D> M;
+  typedef typename Frag<T>::type FragT;
+  constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, LDT = M::LDT, LDC = M::LDC;
+  const T* sQ = (const T*)(smem + M::Q);
+  const T* sW = (const T*)(smem + M::K);
+  const T* sP = (const T*)(smem + M::P);
+  const T* sKH = (const T*)(smem + M::KH);
+  const float* sGL = (const float*)(smem + M::GL);
+  const int idx = lane & 15, gq = lane >> 4;
+
+  FragT SB[NKD];
+#pragma unroll
+  for (int kb = 0; kb < NKD; ++kb) SB[kb] = Frag<T>::from_acc(S, kb);
+  f32x4 U[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 ws = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      ws = mma(frag_rows(sW, LDT, 16 * rt + idx, kb * KB, gq), SB[kb], ws);
+      if (WITH_O) qs = mma(frag_rows(sQ, LDT, 16 * rt + idx, kb * KB, gq), SB[kb], qs);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) U[rt][i] = wv[rt][i] - ws[i];
+    O[rt] = qs;
+  }
+  FragT UB[NKC];
+#pragma unroll
+  for (int kb = 0; kb < NKC; ++kb) UB[kb] = Frag<T>::from_acc(U, kb);
+  if (WITH_O) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+        if (kb * KB <= 16 * rt + 15) O[rt] = mma(frag_rows(sP, LDC, 16 * rt + idx, kb * KB, gq), UB[kb], O[rt]);
+  }
+#pragma unroll
+  for (int rr = 0; rr < D / 16; ++rr) {
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) S[rr] = mma(frag_rows(sKH, LDC, 16 * rr + idx, kb * KB, gq), UB[kb], S[rr]);
+    const f32x4 gm = *(const f32x4*)(sGL + 16 * rr + 4 * gq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[rr][i] *= gm[i];
+  }
+}
+
+// ---- pass 1: affine map [B | M] of every segment but the last ------------
+template <typename T, int D>
+__global__ void __launch_bounds__(4 * D)
+kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
+                const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_rows, int T_per,
+                int H, int L, float g_floor, float* __restrict__ ws) {
+  typedef Lds<T, D> M;
+  constexpr int NW = D / 16, NT = 64 * NW, NR = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
+  Seg sg;
+  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
+  if (sg.s == sg.nseg - 1) return;  // nothing downstream needs the last map
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
+  const int idx = lane & 15, gq = lane >> 4;
+  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
+
+  // wave owns columns 32 wave .. 32 wave + 31 of [B | M] (2 tiles)
+  f32x4 X[2][NR];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rr + 4 * gq + i, col = 32 * wave + 16 * cc + idx;
+        X[cc][rr][i] = (col >= D && row == col - D) ? 1.f : 0.f;
+      }
+
+  Raw<T, D, NT, false> raw;
+  raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
+  raw.store(smem, tid);
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) {
+    if (j + 1 < j1) raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
+    elementwise<T, D, false>(smem, g_floor, tid);
+    gram<T, D, NW, false>(smem, wave, lane);
+    tri_inverse<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
+    WyOps<T, D> wy;
+    wy.load(smem, lane);
+    store_wk<T, D>(smem, wy, wave, lane);
+    f32x4 wv[2][4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      if (wave < NW / 2) {
+        wy.product((const T*)(smem + M::VT), 2 * wave + cc, lane, wv[cc]);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) wv[cc][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    __syncthreads();  // Wk complete
+    f32x4 unused[4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) state_step<T, D, false>(smem, X[cc], wv[cc], unused, lane);
+    __syncthreads();  // done with this chunk's LDS
+    if (j + 1 < j1) {
+      raw.store(smem, tid);
+      __syncthreads();
+    }
+  }
+
+  float* rec = ws + ((size_t)(blockIdx.x) * H + h) * (3 * D * D);
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rr + 4 * gq + i, col = 32 * wave + 16 * cc + idx;
+        rec[row * D + col + (col >= D ? D * D - D : 0)] = X[cc][rr][i];
+      }
+}
+
+// ---- pass 3: outputs from every segment's incoming state -----------------
+template <typename T, int D>
+__global__ void __launch_bounds__(4 * D)
+kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                int n_rows, int T_per, int H, int L, float g_floor, const float* __restrict__ ws,
+                T* __restrict__ o, float* ht) {
+  typedef Lds<T, D> M;
+  constexpr int NW = D / 16, NT = 64 * NW, NR = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
+  Seg sg;
+  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
+  const int idx = lane & 15, gq = lane >> 4, vcol = 16 * wave + idx;
+  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
+
+  const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * (3 * D * D) + 2 * D * D;
+  f32x4 S[NR];
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[rr][i] = sin[(16 * rr + 4 * gq + i) * D + vcol];
+
+  Raw<T, D, NT, true> raw;
+  raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
+  raw.store(smem, tid);
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) {
+    const int clen = min(C, sg.len - C * j);
+    const int64_t tokc = sg.tok0 + (int64_t)C * j;
+    if (j + 1 < j1) raw.load(q, k, v, g, beta, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid);
+    elementwise<T, D, true>(smem, g_floor, tid);
+    gram<T, D, NW, true>(smem, wave, lane);
+    tri_inverse<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
+    WyOps<T, D> wy;
+    wy.load(smem, lane);
+    store_wk<T, D>(smem, wy, wave, lane);
+    f32x4 wv[4];
+    wy.product((const T*)(smem + M::VT), wave, lane, wv);
+    __syncthreads();  // Wk complete
+    f32x4 O[4];
+    state_step<T, D, true>(smem, S, wv, O, lane);
+    // O goes through LDS (the Kt^T area, dead since the W products) so that
+    // the global stores are whole 16-byte rows pieces
+    T* sO = (T*)(smem + M::KT);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sO[(16 * rt + 4 * gq + i) * M::LDT + vcol] = Elem<T>::from_f32(O[rt][i]);
+    __syncthreads();
+    raw.store_out(smem + M::KT, o, tokc, clen, H, h, tid);
+    if (j + 1 < j1) raw.store(smem, tid);
+    __syncthreads();
+  }
+  if (ht && sg.s == sg.nseg - 1) {
+    float* dst = ht + ((size_t)sg.n * H + h) * D * D;
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * rr + 4 * gq + i) * D + vcol] = S[rr][i];
+  }
+}
+
+// ---- pass 2: segment scan S_{s+1} = M_s S_s + B_s ------------------------
+// Workgroup = (sequence, head, 16 state columns); wave w owns the k-block w
+// (rows KB w .. KB w + KB - 1 of S), forms the partial products of all row
+// tiles over its k-block, and the partials are summed through LDS.
+template <typename T, int D> struct ScanOps;
+template <int D> struct ScanOps<bf16_t, D> {
+  static constexpr int KB = 32;
+  // hi/lo bf16 split of the state rows held by this wave (two acc tiles)
+  struct SFrag { bf16x8 hi, lo; };
+  __device__ static __forceinline__ SFrag state_frag(const f32x4* Sk) {
+    SFrag r;
+    r.hi = frag_from_acc(Sk[0], Sk[1]);
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = Sk[0][e] - (float)r.hi[e];
+      b[e] = Sk[1][e] - (float)r.hi[e + 4];
+    }
+    r.lo = frag_from_acc(a, b);
+    return r;
+  }
+  struct MRaw { f32x4 lo, hi; };
+  __device__ static __forceinline__ MRaw load_m(const float* Mm, int row, int k0, int g) {
+    const float* p = Mm + (size_t)row * D + k0 + 4 * g;
+    MRaw m;
+    m.lo = *(const f32x4*)p;
+    m.hi = *(const f32x4*)(p + 16);
+    return m;
+  }
+  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s) {
+    const bf16x8 mh = frag_from_acc(m.lo, m.hi);
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = m.lo[e] - (float)mh[e];
+      b[e] = m.hi[e] - (float)mh[e + 4];
+    }
+    const bf16x8 ml = frag_from_acc(a, b);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma(mh, s.hi, acc);
+    acc = mma(mh, s.lo, acc);
+    acc = mma(ml, s.hi, acc);
+    return acc;
+  }
+};
+template <int D> struct ScanOps<float, D> {
+  static constexpr int KB = 16;
+  struct SFrag { f32x4 s; };
+  __device__ static __forceinline__ SFrag state_frag(const f32x4* Sk) { return SFrag{Sk[0]}; }
+  struct MRaw { f32x4 m; };
+  __device__ static __forceinline__ MRaw load_m(const float* Mm, int row, int k0, int g) {
+    return MRaw{*(const f32x4*)(Mm + (size_t)row * D + k0 + 4 * g)};
+  }
+  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    return mma(m.m, s.s, acc);
+  }
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64 * (D / ScanOps<T, D>::KB))
+kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* __restrict__ cu, int n_rows,
+             int T_per, int H, int L) {
+  typedef ScanOps<T, D> Ops;
+  constexpr int KB = Ops::KB, NWS = D / KB, RT = KB / 16, NRT = D / 16, WPP = D / 16;
+  __shared__ f32x4 sRed[NWS][NRT][64];
+  const int n_pairs = n_rows * H;
+  // XCD-aware order: the WPP workgroups of one (sequence, head) get ids with
+  // the same residue mod 8, so they share one XCD's L2 for M and B.
+  const int id = blockIdx.x, xcd = id & 7, jj = id >> 3;
+  const int p = (jj / WPP) * 8 + xcd, ct = jj % WPP;
+  if (p >= n_pairs) return;
+  const int n = p / H, h = p % H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, idx = lane & 15, gq = lane >> 4;
+  const int col = 16 * ct + idx;
+
+  int64_t base = 0;
+  int len;
+  if (cu) {
+    for (int m = 0; m < n; ++m) base += n_segments(cu[m + 1] - cu[m], L);
+    len = cu[n + 1] - cu[n];
+  } else {
+    base = (int64_t)n * n_segments(T_per, L);
+    len = T_per;
+  }
+  const int nseg = n_segments(len, L);
+
+  f32x4 Sk[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (RT * wave + t) + 4 * gq + i;
+      Sk[t][i] = h0 ? h0[((size_t)p * D + row) * D + col] : 0.f;
+    }
+  auto rec = [&](int s) -> float* { return ws + ((size_t)(base + s) * H + h) * (3 * D * D); };
+  auto put = [&](float* dst) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * (RT * wave + t) + 4 * gq + i) * D + col] = Sk[t][i];
+  };
+  if (nseg == 0) {
+    if (ht) put(ht + (size_t)p * D * D);
+    return;
+  }
+  put(rec(0) + 2 * D * D);
+  typename Ops::MRaw mr[NRT];
+  f32x4 bt[RT];
+  auto load_b = [&](int s, f32x4* dst) {
+    const float* Bm = rec(s);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[t][i] = Bm[(16 * (RT * wave + t) + 4 * gq + i) * D + col];
+  };
+  if (nseg > 1) {
+#pragma unroll
+    for (int rr = 0; rr < NRT; ++rr) mr[rr] = Ops::load_m(rec(0) + D * D, 16 * rr + idx, KB * wave, gq);
+    load_b(0, bt);
+  }
+  for (int s = 0; s + 1 < nseg; ++s) {
+    // the next step's M and B do not depend on the state: load them now
+    typename Ops::MRaw mn[NRT];
+    f32x4 bn[RT];
+    if (s + 2 < nseg) {
+#pragma unroll
+      for (int rr = 0; rr < NRT; ++rr) mn[rr] = Ops::load_m(rec(s + 1) + D * D, 16 * rr + idx, KB * wave, gq);
+      load_b(s + 1, bn);
+    }
+    const typename Ops::SFrag sf = Ops::state_frag(Sk);
+#pragma unroll
+    for (int rr = 0; rr < NRT; ++rr) sRed[wave][rr][lane] = Ops::product(mr[rr], sf);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      f32x4 acc = bt[t];
+#pragma unroll
+      for (int w = 0; w < NWS; ++w) {
+        const f32x4 x = sRed[w][RT * wave + t][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += x[i];
+      }
+      Sk[t] = acc;
+    }
+    put(rec(s + 1) + 2 * D * D);
+    __syncthreads();
+    if (s + 2 < nseg) {
+#pragma unroll
+      for (int rr = 0; rr < NRT; ++rr) mr[rr] = mn[rr];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) bt[t] = bn[t];
+    }
+  }
+}
+
+template <typename T, int D>
+int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
+                 const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
+                 float* ht, void* ws, hipStream_t stream) {
+  const int L = plan.seg_chunks;
+  float* wsf = (float*)ws;
+  const bool has_segments = plan.n_seg_bound > 0;
+  if (has_segments) {
+    hipLaunchKernelGGL((kda_seg_summary<T, D>), dim3((unsigned)plan.n_seg_bound, H), dim3(4 * D), 0, stream,
+                       (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor, wsf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  const int64_t pairs = (int64_t)n_rows * H;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * (D / 16);
+  hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / ScanOps<T, D>::KB)), 0, stream,
+                     h0, ht, wsf, cu, n_rows, T_per, H, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  if (has_segments) {
+    hipLaunchKernelGGL((kda_seg_forward<T, D>), dim3((unsigned)plan.n_seg_bound, H), dim3(4 * D), 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor,
+                       (const float*)wsf, (T*)o, ht);
+    e = hipGetLastError();
+  }
+  return (int)e;
+}
+
+}  // namespace
+
+int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan, float g_floor,
+                         const void* q, const void* k, const void* v, const void* g, const float* beta,
+                         const float* h0, const int32_t* cu, void* o, float* ht, void* ws, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (is_bf16 && d == 64)
+    return launch_typed<bf16_t, 64>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+  if (is_bf16 && d == 128)
+    return launch_typed<bf16_t, 128>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+  if (!is_bf16 && d == 64)
+    return launch_typed<float, 64>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace kda

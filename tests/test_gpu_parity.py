@@ -40,6 +40,14 @@ SMALL = {
     "f32-d64-no-decay": lambda: _case(1, 256, 2, 64, "f32", g_mode="zero", wid=112),
     "bf16-d128-no-decay": lambda: _case(1, 256, 2, 128, "bf16", g_mode="zero", wid=113),
     "bf16-d128-sigma2": lambda: _case(1, 333, 4, 128, "bf16", sigma_g=2.0, wid=114),
+    # long sequences: many segments, so the segment scan carries the state
+    # across tens of segment boundaries; weak and no decay keep it alive
+    "bf16-d128-T16384-weak-decay": lambda: _case(1, 16384, 2, 128, "bf16", g_mode="weak", wid=115),
+    "bf16-d128-T16384-no-decay": lambda: _case(1, 16384, 2, 128, "bf16", g_mode="zero", wid=116),
+    "bf16-d64-T8192-weak-decay": lambda: _case(1, 8192, 2, 64, "bf16", g_mode="weak", wid=117),
+    "f32-d64-T4096-weak-decay": lambda: _case(1, 4096, 2, 64, "f32", g_mode="weak", wid=118),
+    "bf16-d128-varlen-long-weak": lambda: _case(1, 0, 2, 128, "bf16", g_mode="weak",
+                                                lengths=[3000, 1, 4096, 0, 777], wid=119),
 }
 
 
@@ -170,3 +178,28 @@ def test_decode_config4_1000_steps():
     es = rel_err(state[pairs_n, pairs_h].cpu().double().numpy(), ref_state[:, 0])
     print(f"workload4: step1 state err={e1:.3e} worst o err={worst:.3e} final state err={es:.3e}")
     assert es <= TOL["bf16"]
+
+
+def test_chunk_forward_in_place_state():
+    """ht may alias h0: the final state overwrites the initial one, with the
+    sequence spread over many segments."""
+    inp = _case(1, 3000, 3, 128, "bf16", wid=130)
+    note("chunk_forward in-place h0/ht T=3000 H=3 d=128 bf16")
+    d = {key: (val.cuda() if isinstance(val, torch.Tensor) else val) for key, val in inp.items()}
+    state = d["h0"].clone()
+    o, ht = kda.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=state, ht=state)
+    torch.cuda.synchronize()
+    assert ht.data_ptr() == state.data_ptr()
+    ro, rht = oracle_forward(inp)
+    eo, eh = rel_err(f64(o), ro), rel_err(f64(state), rht)
+    print(f"in-place: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_chunk_forward_deterministic():
+    """No atomics anywhere: two calls give bitwise-identical o and ht."""
+    inp = _case(1, 2500, 4, 128, "bf16", wid=131)
+    note("chunk_forward determinism T=2500 H=4 d=128 bf16")
+    o1, h1 = gpu_forward(inp)
+    o2, h2 = gpu_forward(inp)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
