@@ -64,8 +64,8 @@ template <typename T, int D> struct Lds {
   static constexpr int VT = KH + COL;      // V^T
   static constexpr int P = VT + COL;       // P
   static constexpr int BETA = P + PSZ;     // fp32 [64]
-  static constexpr int PART = BETA + C * 4;  // fp32 [4][D] partial sums of g
-  static constexpr int GL = PART + 4 * D * 4;  // fp32 [D] gamma
+  static constexpr int PART = BETA + C * 4;  // fp32 [8][D] partial sums of g
+  static constexpr int GL = PART + 8 * D * 4;  // fp32 [D] gamma
   static constexpr int BYTES = GL + D * 4;
 };
 
@@ -173,104 +173,115 @@ template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return Elem<T>::to_f32(x); }
 
 // ---- element-wise stage: prefix sums of the floored log-decay and the
-// decay-scaled operands.  Thread (channel c, quarter tq) owns 16 rows.
-template <typename T, int D, bool WITH_Q>
+// decay-scaled operands.  Thread (channel pair c, c + 1; part p) owns TPP
+// consecutive rows of its two channels; the parts exchange their sums through
+// LDS.  Rows are processed in blocks of 8 whose LDS reads are issued together.
+template <typename T> struct Pair;
+template <> struct Pair<bf16_t> {
+  typedef uint32_t word;  // two bf16 channels
+  __device__ static __forceinline__ float lo(word w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(word w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ word pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(a, b));
+  }
+};
+template <> struct Pair<float> {
+  typedef f32x2 word;
+  __device__ static __forceinline__ float lo(word w) { return w[0]; }
+  __device__ static __forceinline__ float hi(word w) { return w[1]; }
+  __device__ static __forceinline__ word pack(float a, float b) { return (f32x2){a, b}; }
+};
+
+// Channel-major store of 8 consecutive rows of a channel pair, given the 8
+// token-major pair words: channel c gets the low halves, c + 1 the high ones.
+__device__ __forceinline__ void store_cols8(bf16_t* dst, int ldc, const uint32_t (&w)[8]) {
+  uint32_t a[4], b[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    a[u] = (w[2 * u] & 0xffffu) | (w[2 * u + 1] << 16);
+    b[u] = (w[2 * u] >> 16) | (w[2 * u + 1] & 0xffff0000u);
+  }
+  *(uint4*)dst = (uint4){a[0], a[1], a[2], a[3]};
+  *(uint4*)(dst + ldc) = (uint4){b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void store_cols8(float* dst, int ldc, const f32x2 (&w)[8]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    *(f32x4*)(dst + 4 * u) = (f32x4){w[4 * u][0], w[4 * u + 1][0], w[4 * u + 2][0], w[4 * u + 3][0]};
+    *(f32x4*)(dst + ldc + 4 * u) = (f32x4){w[4 * u][1], w[4 * u + 1][1], w[4 * u + 2][1], w[4 * u + 3][1]};
+  }
+}
+
+template <typename T, int D, int NW, bool WITH_Q>
 __device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, int tid) {
   typedef Lds<T, D> M;
+  typedef Pair<T> PW;
+  typedef typename PW::word word;
   constexpr int LDT = M::LDT, LDC = M::LDC;
-  T* sQ = (T*)(smem + M::Q);
-  T* sK = (T*)(smem + M::K);
-  T* sG = (T*)(smem + M::G);
-  const T* sV = (const T*)(smem + M::V);
+  constexpr int NT = 64 * NW, NPR = D / 2, NP = NT / NPR, TPP = C / NP;
+  static_assert(NP * NPR == NT && NP * TPP == C && NP <= 8 && TPP % 8 == 0, "thread layout");
+  word* sQ = (word*)(smem + M::Q);
+  word* sK = (word*)(smem + M::K);
+  word* sG = (word*)(smem + M::G);
+  const word* sV = (const word*)(smem + M::V);
   T* sKT = (T*)(smem + M::KT);
   T* sKH = (T*)(smem + M::KH);
   T* sVT = (T*)(smem + M::VT);
   float* sPart = (float*)(smem + M::PART);
   float* sGL = (float*)(smem + M::GL);
-  const int c = tid % D, tq = tid / D, t0 = 16 * tq;
+  const int cp = tid % NPR, c = 2 * cp, part = tid / NPR, t0 = TPP * part;
+  auto at = [&](int t) { return t * (LDT / 2) + cp; };  // pair index of (row t, channel c)
 
-  float gf[16];
-  float part = 0.f;
+  float g0[TPP], g1[TPP];
+  float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    float x = to_f32(sG[(t0 + s) * LDT + c]);
-    x = x < g_floor ? g_floor : x;  // NaN stays NaN
-    gf[s] = x;
-    part += x;
+  for (int s = 0; s < TPP; ++s) {
+    const word w = sG[at(t0 + s)];
+    const float x0 = PW::lo(w), x1 = PW::hi(w);
+    g0[s] = x0 < g_floor ? g_floor : x0;  // NaN stays NaN
+    g1[s] = x1 < g_floor ? g_floor : x1;
+    p0 += g0[s];
+    p1 += g1[s];
   }
-  sPart[tq * D + c] = part;
+  *(f32x2*)(sPart + part * D + c) = (f32x2){p0, p1};
   __syncthreads();
-  float off = 0.f, gl = 0.f;
+  float gam0 = 0.f, gam1 = 0.f, gl0 = 0.f, gl1 = 0.f;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float x = sPart[p * D + c];
-    off += p < tq ? x : 0.f;
-    gl += x;
+  for (int p = 0; p < NP; ++p) {
+    const f32x2 x = *(const f32x2*)(sPart + p * D + c);
+    gam0 += p < part ? x[0] : 0.f;
+    gam1 += p < part ? x[1] : 0.f;
+    gl0 += x[0];
+    gl1 += x[1];
   }
-  if (tq == 0) sGL[c] = __expf(gl);
+  if (part == 0) *(f32x2*)(sGL + c) = (f32x2){__expf(gl0), __expf(gl1)};
 
-  float gam = off;
-  if constexpr (sizeof(T) == 2) {
-    uint32_t kt[8], kh[8], vt[8];
 #pragma unroll
-    for (int s = 0; s < 16; s += 2) {
-      float e[2], ei[2], kv[2], qv[2];
+  for (int b0 = 0; b0 < TPP; b0 += 8) {
+    const int tb = t0 + b0;
+    word kw[8], qw[8], vw[8];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        gam += gf[s + u];
-        e[u] = __expf(gam);
-        ei[u] = __expf(-gam);
-        kv[u] = to_f32(sK[(t0 + s + u) * LDT + c]);
-        if (WITH_Q) qv[u] = to_f32(sQ[(t0 + s + u) * LDT + c]);
-      }
-      const bf16x2 a = f32x2_to_bf16x2(kv[0] * e[0], kv[1] * e[1]);
-      const bf16x2 b = f32x2_to_bf16x2(kv[0] * ei[0], kv[1] * ei[1]);
-      // halves are taken from the packed word: bit-casting a single lane of
-      // a bf16 vector is not reliable with this compiler
-      kt[s / 2] = __builtin_bit_cast(uint32_t, a);
-      kh[s / 2] = __builtin_bit_cast(uint32_t, b);
-      vt[s / 2] = (uint32_t)sV[(t0 + s) * LDT + c] | ((uint32_t)sV[(t0 + s + 1) * LDT + c] << 16);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        sK[(t0 + s + u) * LDT + c] = (bf16_t)(kt[s / 2] >> (16 * u));
-        sG[(t0 + s + u) * LDT + c] = (bf16_t)(kh[s / 2] >> (16 * u));
-      }
-      if (WITH_Q) {
-        const uint32_t qq = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(qv[0] * e[0], qv[1] * e[1]));
-        sQ[(t0 + s) * LDT + c] = (bf16_t)qq;
-        sQ[(t0 + s + 1) * LDT + c] = (bf16_t)(qq >> 16);
-      }
+    for (int s = 0; s < 8; ++s) {
+      kw[s] = sK[at(tb + s)];
+      vw[s] = sV[at(tb + s)];
+      if (WITH_Q) qw[s] = sQ[at(tb + s)];
     }
-    uint4* dkt = (uint4*)(sKT + c * LDC + t0);
-    uint4* dkh = (uint4*)(sKH + c * LDC + t0);
-    uint4* dvt = (uint4*)(sVT + c * LDC + t0);
-    dkt[0] = (uint4){kt[0], kt[1], kt[2], kt[3]};
-    dkt[1] = (uint4){kt[4], kt[5], kt[6], kt[7]};
-    dkh[0] = (uint4){kh[0], kh[1], kh[2], kh[3]};
-    dkh[1] = (uint4){kh[4], kh[5], kh[6], kh[7]};
-    dvt[0] = (uint4){vt[0], vt[1], vt[2], vt[3]};
-    dvt[1] = (uint4){vt[4], vt[5], vt[6], vt[7]};
-  } else {
-    float kt[16], kh[16], vt[16];
+    word kt[8], kh[8];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int t = t0 + s;
-      gam += gf[s];
-      const float e = __expf(gam), ei = __expf(-gam);
-      const float kv = sK[t * LDT + c];
-      if (WITH_Q) sQ[t * LDT + c] = sQ[t * LDT + c] * e;
-      kt[s] = kv * e;
-      kh[s] = kv * ei;
-      vt[s] = sV[t * LDT + c];
-      sK[t * LDT + c] = kt[s];
-      sG[t * LDT + c] = kh[s];
+    for (int s = 0; s < 8; ++s) {
+      gam0 += g0[b0 + s];
+      gam1 += g1[b0 + s];
+      const float e0 = __expf(gam0), e1 = __expf(gam1), ei0 = __expf(-gam0), ei1 = __expf(-gam1);
+      const float k0 = PW::lo(kw[s]), k1 = PW::hi(kw[s]);
+      kt[s] = PW::pack(k0 * e0, k1 * e1);
+      kh[s] = PW::pack(k0 * ei0, k1 * ei1);
+      sK[at(tb + s)] = kt[s];
+      sG[at(tb + s)] = kh[s];
+      if (WITH_Q) sQ[at(tb + s)] = PW::pack(PW::lo(qw[s]) * e0, PW::hi(qw[s]) * e1);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *(f32x4*)((float*)sKT + c * LDC + t0 + 4 * u) = (f32x4){kt[4 * u], kt[4 * u + 1], kt[4 * u + 2], kt[4 * u + 3]};
-      *(f32x4*)((float*)sKH + c * LDC + t0 + 4 * u) = (f32x4){kh[4 * u], kh[4 * u + 1], kh[4 * u + 2], kh[4 * u + 3]};
-      *(f32x4*)((float*)sVT + c * LDC + t0 + 4 * u) = (f32x4){vt[4 * u], vt[4 * u + 1], vt[4 * u + 2], vt[4 * u + 3]};
-    }
+    store_cols8(sKT + c * LDC + tb, LDC, kt);
+    store_cols8(sKH + c * LDC + tb, LDC, kh);
+    store_cols8(sVT + c * LDC + tb, LDC, vw);
   }
   __syncthreads();
 }
@@ -448,12 +459,13 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const WyOps<T, D>&
     for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * gq + i) * M::LDT + 16 * ct + idx] = Elem<T>::from_f32(w[rt][i]);
 }
 
-// One column tile of the state (rows = D key channels) through one chunk:
+// CT column tiles of the state (rows = D key channels) through one chunk:
 // U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
-// O = Qt S + P U, returned in O[4].  `wv` holds Wv's tiles for this column.
-template <typename T, int D, bool WITH_O>
-__device__ __forceinline__ void state_step(const unsigned char* smem, f32x4 (&S)[D / 16], const f32x4 (&wv)[4],
-                                           f32x4 (&O)[4], int lane) {
+// O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  Every A-operand
+// fragment read from LDS feeds the CT tiles.
+template <typename T, int D, int CT, bool WITH_O>
+__device__ __forceinline__ void state_step(const unsigned char* smem, f32x4 (&S)[CT][D / 16],
+                                           const f32x4 (&wv)[CT][4], f32x4 (&O)[CT][4], int lane) {
   typedef Lds<T, D> M;
   typedef typename Frag<T>::type FragT;
   constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, LDT = M::LDT, LDC = M::LDC;
@@ -464,50 +476,78 @@ __device__ __forceinline__ void state_step(const unsigned char* smem, f32x4 (&S)
   const float* sGL = (const float*)(smem + M::GL);
   const int idx = lane & 15, gq = lane >> 4;
 
-  FragT SB[NKD];
+  FragT SB[CT][NKD];
 #pragma unroll
-  for (int kb = 0; kb < NKD; ++kb) SB[kb] = Frag<T>::from_acc(S, kb);
-  f32x4 U[4];
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) SB[c][kb] = Frag<T>::from_acc(S[c], kb);
+  f32x4 U[CT][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    f32x4 ws = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+    f32x4 ws[CT], qs[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) ws[c] = qs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) {
-      ws = mma(frag_rows(sW, LDT, 16 * rt + idx, kb * KB, gq), SB[kb], ws);
-      if (WITH_O) qs = mma(frag_rows(sQ, LDT, 16 * rt + idx, kb * KB, gq), SB[kb], qs);
+      const FragT aw = frag_rows(sW, LDT, 16 * rt + idx, kb * KB, gq);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) ws[c] = mma(aw, SB[c][kb], ws[c]);
+      if (WITH_O) {
+        const FragT aq = frag_rows(sQ, LDT, 16 * rt + idx, kb * KB, gq);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) qs[c] = mma(aq, SB[c][kb], qs[c]);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) U[rt][i] = wv[rt][i] - ws[i];
-    O[rt] = qs;
-  }
-  FragT UB[NKC];
+    for (int c = 0; c < CT; ++c) {
 #pragma unroll
-  for (int kb = 0; kb < NKC; ++kb) UB[kb] = Frag<T>::from_acc(U, kb);
+      for (int i = 0; i < 4; ++i) U[c][rt][i] = wv[c][rt][i] - ws[c][i];
+      O[c][rt] = qs[c];
+    }
+  }
+  FragT UB[CT][NKC];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) UB[c][kb] = Frag<T>::from_acc(U[c], kb);
   if (WITH_O) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
-        if (kb * KB <= 16 * rt + 15) O[rt] = mma(frag_rows(sP, LDC, 16 * rt + idx, kb * KB, gq), UB[kb], O[rt]);
+        if (kb * KB <= 16 * rt + 15) {
+          const FragT ap = frag_rows(sP, LDC, 16 * rt + idx, kb * KB, gq);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) O[c][rt] = mma(ap, UB[c][kb], O[c][rt]);
+        }
   }
 #pragma unroll
   for (int rr = 0; rr < D / 16; ++rr) {
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) S[rr] = mma(frag_rows(sKH, LDC, 16 * rr + idx, kb * KB, gq), UB[kb], S[rr]);
+    for (int kb = 0; kb < NKC; ++kb) {
+      const FragT ak = frag_rows(sKH, LDC, 16 * rr + idx, kb * KB, gq);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) S[c][rr] = mma(ak, UB[c][kb], S[c][rr]);
+    }
     const f32x4 gm = *(const f32x4*)(sGL + 16 * rr + 4 * gq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[rr][i] *= gm[i];
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[c][rr][i] *= gm[i];
   }
 }
 
 // ---- pass 1: affine map [B | M] of every segment but the last ------------
-template <typename T, int D>
-__global__ void __launch_bounds__(4 * D)
+// Wave w owns the 2 D / 16 / NW column tiles w + NW x of [B | M] (tiles below
+// D / 16 are value columns), processed two at a time.
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(64 * NW)
 kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
                 const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_rows, int T_per,
                 int H, int L, float g_floor, float* __restrict__ ws) {
   typedef Lds<T, D> M;
-  constexpr int NW = D / 16, NT = 64 * NW, NR = D / 16;
+  constexpr int NT = 64 * NW, NR = D / 16, NX = 2 * NR / NW, NPAIR = NX / 2;
+  static_assert(NX >= 2 && NX % 2 == 0, "each wave owns pairs of column tiles");
   __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
@@ -517,17 +557,18 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
   const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
 
-  // wave owns columns 32 wave .. 32 wave + 31 of [B | M] (2 tiles)
-  f32x4 X[2][NR];
+  f32x4 X[NPAIR][2][NR];
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+  for (int p = 0; p < NPAIR; ++p)
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * rr + 4 * gq + i, col = 32 * wave + 16 * cc + idx;
-        X[cc][rr][i] = (col >= D && row == col - D) ? 1.f : 0.f;
-      }
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rr + 4 * gq + i, col = 16 * (wave + NW * (2 * p + c)) + idx;
+          X[p][c][rr][i] = (col >= D && row == col - D) ? 1.f : 0.f;
+        }
 
   Raw<T, D, NT, false> raw;
   raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
@@ -535,26 +576,30 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
   __syncthreads();
   for (int j = j0; j < j1; ++j) {
     if (j + 1 < j1) raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
-    elementwise<T, D, false>(smem, g_floor, tid);
+    elementwise<T, D, NW, false>(smem, g_floor, tid);
     gram<T, D, NW, false>(smem, wave, lane);
     tri_inverse<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
     WyOps<T, D> wy;
     wy.load(smem, lane);
-    store_wk<T, D>(smem, wy, wave, lane);
-    f32x4 wv[2][4];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      if (wave < NW / 2) {
-        wy.product((const T*)(smem + M::VT), 2 * wave + cc, lane, wv[cc]);
-      } else {
+    for (int c = 0; c < NR / NW; ++c) store_wk<T, D>(smem, wy, wave + NW * c, lane);
+    // tile wave + NW x is a value tile exactly when x < NX / 2 (wave < NW)
+    f32x4 wv[NPAIR][2][4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wv[cc][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NPAIR; ++p)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (2 * p + c < NX / 2) {
+          wy.product((const T*)(smem + M::VT), wave + NW * (2 * p + c), lane, wv[p][c]);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) wv[p][c][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
       }
-    }
     __syncthreads();  // Wk complete
-    f32x4 unused[4];
+    f32x4 unused[2][4];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) state_step<T, D, false>(smem, X[cc], wv[cc], unused, lane);
+    for (int p = 0; p < NPAIR; ++p) state_step<T, D, 2, false>(smem, X[p], wv[p], unused, lane);
     __syncthreads();  // done with this chunk's LDS
     if (j + 1 < j1) {
       raw.store(smem, tid);
@@ -564,39 +609,45 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 
   float* rec = ws + ((size_t)(blockIdx.x) * H + h) * (3 * D * D);
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+  for (int p = 0; p < NPAIR; ++p)
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * rr + 4 * gq + i, col = 32 * wave + 16 * cc + idx;
-        rec[row * D + col + (col >= D ? D * D - D : 0)] = X[cc][rr][i];
-      }
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rr + 4 * gq + i, col = 16 * (wave + NW * (2 * p + c)) + idx;
+          rec[row * D + col + (col >= D ? D * D - D : 0)] = X[p][c][rr][i];
+        }
 }
 
 // ---- pass 3: outputs from every segment's incoming state -----------------
-template <typename T, int D>
-__global__ void __launch_bounds__(4 * D)
+// Wave w owns the D / 16 / NW value-column tiles w + NW x.
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(64 * NW)
 kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                 const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
                 int n_rows, int T_per, int H, int L, float g_floor, const float* __restrict__ ws,
                 T* __restrict__ o, float* ht) {
   typedef Lds<T, D> M;
-  constexpr int NW = D / 16, NT = 64 * NW, NR = D / 16;
+  constexpr int NT = 64 * NW, NR = D / 16, CT = NR / NW;
+  static_assert(CT >= 1 && CT * NW == NR, "waves must split the value columns");
   __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
-  const int idx = lane & 15, gq = lane >> 4, vcol = 16 * wave + idx;
+  const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
 
   const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * (3 * D * D) + 2 * D * D;
-  f32x4 S[NR];
+  f32x4 S[CT][NR];
 #pragma unroll
-  for (int rr = 0; rr < NR; ++rr)
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[rr][i] = sin[(16 * rr + 4 * gq + i) * D + vcol];
+    for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[c][rr][i] = sin[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx];
 
   Raw<T, D, NT, true> raw;
   raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
@@ -606,24 +657,30 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     const int clen = min(C, sg.len - C * j);
     const int64_t tokc = sg.tok0 + (int64_t)C * j;
     if (j + 1 < j1) raw.load(q, k, v, g, beta, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid);
-    elementwise<T, D, true>(smem, g_floor, tid);
+    elementwise<T, D, NW, true>(smem, g_floor, tid);
     gram<T, D, NW, true>(smem, wave, lane);
     tri_inverse<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
     WyOps<T, D> wy;
     wy.load(smem, lane);
-    store_wk<T, D>(smem, wy, wave, lane);
-    f32x4 wv[4];
-    wy.product((const T*)(smem + M::VT), wave, lane, wv);
+    f32x4 wv[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      store_wk<T, D>(smem, wy, wave + NW * c, lane);
+      wy.product((const T*)(smem + M::VT), wave + NW * c, lane, wv[c]);
+    }
     __syncthreads();  // Wk complete
-    f32x4 O[4];
-    state_step<T, D, true>(smem, S, wv, O, lane);
+    f32x4 O[CT][4];
+    state_step<T, D, CT, true>(smem, S, wv, O, lane);
     // O goes through LDS (the Kt^T area, dead since the W products) so that
-    // the global stores are whole 16-byte rows pieces
+    // the global stores are whole 16-byte pieces of rows
     T* sO = (T*)(smem + M::KT);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sO[(16 * rt + 4 * gq + i) * M::LDT + vcol] = Elem<T>::from_f32(O[rt][i]);
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sO[(16 * rt + 4 * gq + i) * M::LDT + 16 * (wave + NW * c) + idx] = Elem<T>::from_f32(O[c][rt][i]);
     __syncthreads();
     raw.store_out(smem + M::KT, o, tokc, clen, H, h, tid);
     if (j + 1 < j1) raw.store(smem, tid);
@@ -632,9 +689,11 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   if (ht && sg.s == sg.nseg - 1) {
     float* dst = ht + ((size_t)sg.n * H + h) * D * D;
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * rr + 4 * gq + i) * D + vcol] = S[rr][i];
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx] = S[c][rr][i];
   }
 }
 
@@ -746,36 +805,30 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
     return;
   }
   put(rec(0) + 2 * D * D);
-  typename Ops::MRaw mr[NRT];
-  f32x4 bt[RT];
-  auto load_b = [&](int s, f32x4* dst) {
-    const float* Bm = rec(s);
+  // M_s and B_s do not depend on the state: they are fetched two steps ahead
+  // into a ring of three register stages (the loop is unrolled by three so
+  // that the stages never move between registers).
+  struct Stage {
+    typename Ops::MRaw m[NRT];
+    f32x4 b[RT];
+  };
+  auto fetch = [&](int s, Stage& st) {
+    const float* r = rec(s);
+#pragma unroll
+    for (int rr = 0; rr < NRT; ++rr) st.m[rr] = Ops::load_m(r + D * D, 16 * rr + idx, KB * wave, gq);
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[t][i] = Bm[(16 * (RT * wave + t) + 4 * gq + i) * D + col];
+      for (int i = 0; i < 4; ++i) st.b[t][i] = r[(16 * (RT * wave + t) + 4 * gq + i) * D + col];
   };
-  if (nseg > 1) {
-#pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) mr[rr] = Ops::load_m(rec(0) + D * D, 16 * rr + idx, KB * wave, gq);
-    load_b(0, bt);
-  }
-  for (int s = 0; s + 1 < nseg; ++s) {
-    // the next step's M and B do not depend on the state: load them now
-    typename Ops::MRaw mn[NRT];
-    f32x4 bn[RT];
-    if (s + 2 < nseg) {
-#pragma unroll
-      for (int rr = 0; rr < NRT; ++rr) mn[rr] = Ops::load_m(rec(s + 1) + D * D, 16 * rr + idx, KB * wave, gq);
-      load_b(s + 1, bn);
-    }
+  auto step = [&](int s, const Stage& st) {
     const typename Ops::SFrag sf = Ops::state_frag(Sk);
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) sRed[wave][rr][lane] = Ops::product(mr[rr], sf);
+    for (int rr = 0; rr < NRT; ++rr) sRed[wave][rr][lane] = Ops::product(st.m[rr], sf);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      f32x4 acc = bt[t];
+      f32x4 acc = st.b[t];
 #pragma unroll
       for (int w = 0; w < NWS; ++w) {
         const f32x4 x = sRed[w][RT * wave + t][lane];
@@ -786,16 +839,24 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
     }
     put(rec(s + 1) + 2 * D * D);
     __syncthreads();
-    if (s + 2 < nseg) {
-#pragma unroll
-      for (int rr = 0; rr < NRT; ++rr) mr[rr] = mn[rr];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) bt[t] = bn[t];
-    }
+  };
+  const int nsteps = nseg - 1;
+  Stage b0, b1, b2;
+  if (nsteps > 0) fetch(0, b0);
+  if (nsteps > 1) fetch(1, b1);
+  for (int s = 0; s < nsteps; s += 3) {
+    if (s + 2 < nsteps) fetch(s + 2, b2);
+    step(s, b0);
+    if (s + 1 >= nsteps) break;
+    if (s + 3 < nsteps) fetch(s + 3, b0);
+    step(s + 1, b1);
+    if (s + 2 >= nsteps) break;
+    if (s + 4 < nsteps) fetch(s + 4, b1);
+    step(s + 2, b2);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
                  const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
                  float* ht, void* ws, hipStream_t stream) {
@@ -803,7 +864,7 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   float* wsf = (float*)ws;
   const bool has_segments = plan.n_seg_bound > 0;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_summary<T, D>), dim3((unsigned)plan.n_seg_bound, H), dim3(4 * D), 0, stream,
+    hipLaunchKernelGGL((kda_seg_summary<T, D, NW>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0, stream,
                        (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor, wsf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
@@ -815,7 +876,7 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_forward<T, D>), dim3((unsigned)plan.n_seg_bound, H), dim3(4 * D), 0, stream,
+    hipLaunchKernelGGL((kda_seg_forward<T, D, NW>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor,
                        (const float*)wsf, (T*)o, ht);
     e = hipGetLastError();
@@ -830,11 +891,11 @@ int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const Seg
                          const float* h0, const int32_t* cu, void* o, float* ht, void* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<bf16_t, 64, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
   if (is_bf16 && d == 128)
-    return launch_typed<bf16_t, 128>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<bf16_t, 128, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<float, 64, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
   return (int)hipErrorInvalidValue;
 }
 
