@@ -111,6 +111,26 @@ __device__ __forceinline__ bool locate(const int32_t* cu, int n_rows, int T, int
   return false;
 }
 
+// ---- workspace record of one (segment, head): three d x d blocks of fp32 size
+//   B    : [d/16 row tiles][d/16 column tiles][64 lanes][4] fp32, accumulator
+//          tile order (lane 16 g + i holds rows 4 g .. 4 g + 3 of column i)
+//   M    : A-operand fragments of M for the scan, [d/16 row tiles][k-blocks]
+//          [64 lanes][16 bytes]; bf16 keeps a hi and a lo fragment per slot
+//          (M = hi + lo to about 2^-17), fp32 keeps M itself
+//   S_in : incoming state of the segment, accumulator tile order like B
+template <typename T, int D> struct Rec {
+  static constexpr int NRT = D / 16, KB = Elem<T>::KB, NKB = D / KB;
+  static constexpr size_t B = 0, M = (size_t)D * D, SIN = 2 * (size_t)D * D, FLOATS = 3 * (size_t)D * D;
+  // float offset of accumulator tile (rr, ct) in a tile-ordered block
+  __device__ static __forceinline__ size_t tile(int rr, int ct, int lane) {
+    return (((size_t)rr * NRT + ct) * 64 + lane) * 4;
+  }
+  // byte offset of the (rr, kb) fragment (part 0 = hi, 1 = lo for bf16)
+  __device__ static __forceinline__ size_t frag(int rr, int kb, int part, int lane) {
+    return ((((size_t)rr * NKB + kb) * (sizeof(T) == 2 ? 2 : 1) + part) * 64 + lane) * 16;
+  }
+};
+
 // ---- raw chunk inputs: global -> registers (prefetch) -> LDS -------------
 template <typename T, int D, int NT, bool WITH_Q> struct Raw {
   typedef Lds<T, D> M;
@@ -607,18 +627,47 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     }
   }
 
-  float* rec = ws + ((size_t)(blockIdx.x) * H + h) * (3 * D * D);
+  // B tiles straight from the accumulators; M through LDS into the scan's
+  // A-operand fragments
+  typedef Rec<T, D> R;
+  float* rec = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS;
+  constexpr int LDM = D + 4;
+  float* sM = (float*)smem;  // [D][LDM] fp32, free after the last chunk
 #pragma unroll
   for (int p = 0; p < NPAIR; ++p)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c) {
+      const int tile = wave + NW * (2 * p + c);
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
+      for (int rr = 0; rr < NR; ++rr) {
+        if (2 * p + c < NX / 2) {
+          *(f32x4*)(rec + R::B + R::tile(rr, tile, lane)) = X[p][c][rr];
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * rr + 4 * gq + i, col = 16 * (wave + NW * (2 * p + c)) + idx;
-          rec[row * D + col + (col >= D ? D * D - D : 0)] = X[p][c][rr][i];
+          for (int i = 0; i < 4; ++i) sM[(16 * rr + 4 * gq + i) * LDM + 16 * (tile - NR) + idx] = X[p][c][rr][i];
         }
+      }
+    }
+  __syncthreads();
+  unsigned char* mf = (unsigned char*)(rec + R::M);
+  for (int f = wave; f < NR * R::NKB; f += NW) {
+    const int rr = f / R::NKB, kb = f % R::NKB;
+    const float* src = sM + (16 * rr + idx) * LDM + R::KB * kb + 4 * gq;
+    if constexpr (sizeof(T) == 2) {
+      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 16);
+      const bf16x8 mh = frag_from_acc(lo, hi);
+      f32x4 rl, rh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rl[e] = lo[e] - (float)mh[e];
+        rh[e] = hi[e] - (float)mh[e + 4];
+      }
+      *(bf16x8*)(mf + R::frag(rr, kb, 0, lane)) = mh;
+      *(bf16x8*)(mf + R::frag(rr, kb, 1, lane)) = frag_from_acc(rl, rh);
+    } else {
+      *(f32x4*)(mf + R::frag(rr, kb, 0, lane)) = *(const f32x4*)src;
+    }
+  }
 }
 
 // ---- pass 3: outputs from every segment's incoming state -----------------
@@ -640,14 +689,13 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
 
-  const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * (3 * D * D) + 2 * D * D;
+  typedef Rec<T, D> R;
+  const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS + R::SIN;
   f32x4 S[CT][NR];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[c][rr][i] = sin[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx];
+    for (int rr = 0; rr < NR; ++rr) S[c][rr] = *(const f32x4*)(sin + R::tile(rr, wave + NW * c, lane));
 
   Raw<T, D, NT, true> raw;
   raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
@@ -718,27 +766,19 @@ template <int D> struct ScanOps<bf16_t, D> {
     r.lo = frag_from_acc(a, b);
     return r;
   }
-  struct MRaw { f32x4 lo, hi; };
-  __device__ static __forceinline__ MRaw load_m(const float* Mm, int row, int k0, int g) {
-    const float* p = Mm + (size_t)row * D + k0 + 4 * g;
+  struct MRaw { bf16x8 hi, lo; };
+  __device__ static __forceinline__ MRaw load_m(const unsigned char* mf, int rr, int kb, int lane) {
+    typedef Rec<bf16_t, D> R;
     MRaw m;
-    m.lo = *(const f32x4*)p;
-    m.hi = *(const f32x4*)(p + 16);
+    m.hi = *(const bf16x8*)(mf + R::frag(rr, kb, 0, lane));
+    m.lo = *(const bf16x8*)(mf + R::frag(rr, kb, 1, lane));
     return m;
   }
   __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s) {
-    const bf16x8 mh = frag_from_acc(m.lo, m.hi);
-    f32x4 a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = m.lo[e] - (float)mh[e];
-      b[e] = m.hi[e] - (float)mh[e + 4];
-    }
-    const bf16x8 ml = frag_from_acc(a, b);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mma(mh, s.hi, acc);
-    acc = mma(mh, s.lo, acc);
-    acc = mma(ml, s.hi, acc);
+    acc = mma(m.hi, s.hi, acc);
+    acc = mma(m.hi, s.lo, acc);
+    acc = mma(m.lo, s.hi, acc);
     return acc;
   }
 };
@@ -747,8 +787,8 @@ template <int D> struct ScanOps<float, D> {
   struct SFrag { f32x4 s; };
   __device__ static __forceinline__ SFrag state_frag(const f32x4* Sk) { return SFrag{Sk[0]}; }
   struct MRaw { f32x4 m; };
-  __device__ static __forceinline__ MRaw load_m(const float* Mm, int row, int k0, int g) {
-    return MRaw{*(const f32x4*)(Mm + (size_t)row * D + k0 + 4 * g)};
+  __device__ static __forceinline__ MRaw load_m(const unsigned char* mf, int rr, int kb, int lane) {
+    return MRaw{*(const f32x4*)(mf + Rec<float, D>::frag(rr, kb, 0, lane))};
   }
   __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -793,18 +833,23 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
       const int row = 16 * (RT * wave + t) + 4 * gq + i;
       Sk[t][i] = h0 ? h0[((size_t)p * D + row) * D + col] : 0.f;
     }
-  auto rec = [&](int s) -> float* { return ws + ((size_t)(base + s) * H + h) * (3 * D * D); };
-  auto put = [&](float* dst) {
+  typedef Rec<T, D> R;
+  auto rec = [&](int s) -> float* { return ws + ((size_t)(base + s) * H + h) * R::FLOATS; };
+  auto put = [&](float* dst) {  // incoming state, accumulator tile order
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * (RT * wave + t) + 4 * gq + i) * D + col] = Sk[t][i];
+    for (int t = 0; t < RT; ++t) *(f32x4*)(dst + R::tile(RT * wave + t, ct, lane)) = Sk[t];
   };
   if (nseg == 0) {
-    if (ht) put(ht + (size_t)p * D * D);
+    if (ht) {
+      float* dst = ht + (size_t)p * D * D;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * (RT * wave + t) + 4 * gq + i) * D + col] = Sk[t][i];
+    }
     return;
   }
-  put(rec(0) + 2 * D * D);
+  put(rec(0) + R::SIN);
   // M_s and B_s do not depend on the state: they are fetched two steps ahead
   // into a ring of three register stages (the loop is unrolled by three so
   // that the stages never move between registers).
@@ -815,11 +860,9 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   auto fetch = [&](int s, Stage& st) {
     const float* r = rec(s);
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) st.m[rr] = Ops::load_m(r + D * D, 16 * rr + idx, KB * wave, gq);
+    for (int rr = 0; rr < NRT; ++rr) st.m[rr] = Ops::load_m((const unsigned char*)(r + R::M), rr, wave, lane);
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.b[t][i] = r[(16 * (RT * wave + t) + 4 * gq + i) * D + col];
+    for (int t = 0; t < RT; ++t) st.b[t] = *(const f32x4*)(r + R::B + R::tile(RT * wave + t, ct, lane));
   };
   auto step = [&](int s, const Stage& st) {
     const typename Ops::SFrag sf = Ops::state_frag(Sk);
@@ -837,7 +880,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
       }
       Sk[t] = acc;
     }
-    put(rec(s + 1) + 2 * D * D);
+    put(rec(s + 1) + R::SIN);
     __syncthreads();
   };
   const int nsteps = nseg - 1;
