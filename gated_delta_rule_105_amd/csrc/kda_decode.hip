@@ -12,12 +12,15 @@
 //
 // The step is bound by HBM: the state is read once and written once
 // (2 * 4 d^2 bytes per (n, h)); everything else is a few hundred bytes.
-// One 256-thread workgroup owns one (n, h) tile, so the in-place write needs
-// no synchronisation beyond the block.  Each thread holds a 4-column strip of
-// d/ (256 / (d/4)) rows in registers, loaded with 16-byte loads that are all
-// issued before any arithmetic, reduces its partial sums over rows with
-// cross-lane shuffles inside the wave and through LDS across waves, and
-// writes its strip back.
+// One workgroup owns one (n, h) tile, so the in-place write needs no
+// synchronisation beyond the workgroup.  At d = 128 the workgroup has 1024
+// threads, each holding a 4-column strip of 4 rows (16-byte non-temporal
+// loads, all issued before any arithmetic): the most bytes in flight per CU
+// of the launch shapes measured (256 to 1024 threads, one or two tiles per
+// workgroup), and non-temporal loads and stores keep the stream out of the
+// caches, which held up best when the state is larger than the last-level
+// cache.  Column sums over rows are reduced by cross-lane shuffles inside a
+// wave and through LDS across waves.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -30,17 +33,23 @@ __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float ldf<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 
+template <int D> struct DecodeShape {
+  static constexpr int NTH = D == 128 ? 1024 : 256;  // threads per tile
+};
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(DecodeShape<D>::NTH)
 kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
            const T* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
            T* __restrict__ o, float g_floor) {
+  constexpr int NTH = DecodeShape<D>::NTH;
   constexpr int CPR = D / 4;         // float4 columns per row
-  constexpr int RP = 256 / CPR;      // rows per pass (row groups)
+  constexpr int RP = NTH / CPR;      // rows per pass (row groups)
   constexpr int NI = D / RP;         // passes
-  constexpr int WRG = 64 / CPR;      // row groups per wave
+  constexpr int NWV = NTH / 64;      // waves
+  static_assert(RP * CPR == NTH && NI * RP == D && CPR <= 64, "tile layout");
   __shared__ float sA[D], sK[D], sQ[D];
-  __shared__ f32x4 sW[4][CPR], sZ[4][CPR];
+  __shared__ f32x4 sW[NWV][CPR], sZ[NWV][CPR];
   __shared__ float sQK;
 
   const size_t nh = blockIdx.x;
@@ -48,14 +57,16 @@ kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   const int cg = tid % CPR, rg = tid / CPR;
   f32x4* S = (f32x4*)(state + nh * D * D);
 
-  // issue the whole strip's loads first
+  // issue the whole strip's loads first; then the gate, key and query into
+  // LDS, q.k in wave 0, and this thread's v and beta (that order measured
+  // fastest: vector-memory waits retire in issue order)
   f32x4 s[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) s[i] = __builtin_nontemporal_load(&S[(rg + RP * i) * CPR + cg]);
 
   if (tid < D) {
     float gg = ldf(g + nh * D + tid);
-    gg = gg < g_floor ? g_floor : gg;
+    gg = gg < g_floor ? g_floor : gg;  // NaN stays NaN
     sA[tid] = __expf(gg);
     sK[tid] = ldf(k + nh * D + tid);
     sQ[tid] = ldf(q + nh * D + tid);
@@ -73,6 +84,7 @@ kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   for (int e = 0; e < 4; ++e) vv[e] = ldf(v + nh * D + 4 * cg + e);
   __syncthreads();
 
+  // w = S'^T k and z = S'^T q with S' = diag(a) S, partial over this strip
   f32x4 w = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -98,12 +110,14 @@ kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     sZ[wave][cg] = z;
   }
   __syncthreads();
+  // u and o for this thread's 4 columns (each thread sums the NWV partials
+  // itself: no further barrier)
   f32x4 u, oz;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float ww = 0.f, zz = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) {
+    for (int wv = 0; wv < NWV; ++wv) {
       ww += sW[wv][cg][e];
       zz += sZ[wv][cg][e];
     }
@@ -117,11 +131,11 @@ kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     for (int e = 0; e < 4; ++e) s[i][e] += kc * u[e];
     __builtin_nontemporal_store(s[i], &S[(rg + RP * i) * CPR + cg]);
   }
+  // o after the state stores (measured faster than before them)
   if (rg == 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[nh * D + 4 * cg + e] = Elem<T>::from_f32(oz[e]);
   }
-  (void)WRG;
 }
 
 template <typename T, int D>
@@ -129,7 +143,7 @@ static int launch_typed(int N, int H, float g_floor, const void* q, const void* 
                         const void* g, const float* beta, float* state, void* o, hipStream_t s) {
   const size_t blocks = (size_t)N * H;
   if (blocks == 0) return 0;
-  hipLaunchKernelGGL((kda_decode<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, (const T*)q, (const T*)k,
+  hipLaunchKernelGGL((kda_decode<T, D>), dim3((unsigned)blocks), dim3(DecodeShape<D>::NTH), 0, s, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)g, beta, state, (T*)o, g_floor);
   return (int)hipGetLastError();
 }
