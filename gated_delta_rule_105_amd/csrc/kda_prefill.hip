@@ -307,19 +307,17 @@ __device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, 
 }
 
 // ---- Gram blocks: A = diag(beta) strict_lower(Kt Kh^T) (fp32) and
-// P = lower_incl(Qt Kh^T) (operand type), as 16 x 16 tiles.  Only tiles on
-// or below the diagonal are computed; of the upper tiles only the P tiles
-// that share a 32-wide k-block with a needed one are read, and those are
-// zeroed (bf16 path).
-__device__ __forceinline__ void tile_of(int j, int& rt, int& ct) {
-  const uint64_t R = 0x3333222110ull, K = 0x3210210100ull;  // lower tiles in row order
-  rt = (int)((R >> (4 * j)) & 15);
-  ct = (int)((K >> (4 * j)) & 15);
-}
-
+// P = lower_incl(Qt Kh^T) (operand type), as 16 x 16 tiles on and below the
+// diagonal.  Wave w computes row tile w of A and row tile 3 - w of P (five
+// tiles each); every Kh fragment it loads serves the A and the P tile of its
+// column.  Of the upper P tiles only (0, 1) and (2, 3) share a 32-wide
+// k-block with needed ones; they are zeroed (bf16 path).  A's upper tiles are
+// never read.
 template <typename T, int D, int NW, bool WITH_P>
 __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
   typedef Lds<T, D> M;
+  typedef typename Frag<T>::type FragT;
+  static_assert(NW == 4, "one row tile of A per wave");
   constexpr int KB = Elem<T>::KB, NKD = D / KB, LDT = M::LDT, LDC = M::LDC, LDF = M::LDF;
   const T* sQ = (const T*)(smem + M::Q);
   const T* sK = (const T*)(smem + M::K);
@@ -328,50 +326,66 @@ __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
   T* sP = (T*)(smem + M::P);
   const float* sBeta = (const float*)(smem + M::BETA);
   const int idx = lane & 15, gq = lane >> 4;
-  constexpr int NJ = WITH_P ? 20 : 10;  // A tiles 0..9, then P tiles
+  const int rA = wave, rP = 3 - wave;  // wave-uniform
+  FragT fa[NKD], fq[NKD];
 #pragma unroll
-  for (int n = 0; n < (NJ + NW - 1) / NW; ++n) {
-    const int j = wave + n * NW;  // wave-uniform
-    if (j < NJ) {
-      const bool isP = j >= 10;
-      int rt, ct;
-      tile_of(isP ? j - 10 : j, rt, ct);
-      const T* X = isP ? sQ : sK;
-      typename Frag<T>::type fa[NKD], fb[NKD];
+  for (int kb = 0; kb < NKD; ++kb) {
+    fa[kb] = frag_rows(sK, LDT, 16 * rA + idx, kb * KB, gq);
+    if (WITH_P) fq[kb] = frag_rows(sQ, LDT, 16 * rP + idx, kb * KB, gq);
+  }
+  float br[4];
 #pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) {
-        fa[kb] = frag_rows(X, LDT, 16 * rt + idx, kb * KB, gq);
-        fb[kb] = frag_rows(sG, LDT, 16 * ct + idx, kb * KB, gq);
+  for (int i = 0; i < 4; ++i) br[i] = sBeta[16 * rA + 4 * gq + i];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const bool doA = ct <= rA, doP = WITH_P && ct <= rP;
+    if (doA || doP) {
+      FragT fb[NKD];
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) fb[kb] = frag_rows(sG, LDT, 16 * ct + idx, kb * KB, gq);
+      const int s = 16 * ct + idx;
+      if (doA) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) acc = mma(fa[kb], fb[kb], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rA + 4 * gq + i;
+          sA[r * LDF + s] = s < r ? br[i] * acc[i] : 0.f;
+        }
       }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (doP) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) acc = mma(fa[kb], fb[kb], acc);
+        for (int kb = 0; kb < NKD; ++kb) acc = mma(fq[kb], fb[kb], acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * gq + i, s = 16 * ct + idx;
-        if (isP)
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rP + 4 * gq + i;
           sP[r * LDC + s] = Elem<T>::from_f32(s <= r ? acc[i] : 0.f);
-        else
-          sA[r * LDF + s] = s < r ? sBeta[r] * acc[i] : 0.f;
+        }
       }
     }
   }
-  if (WITH_P && KB == 32 && wave == NW - 1) {
-    // P tiles (0, 1) and (2, 3)
+  if (WITH_P && KB == 32 && (rP == 0 || rP == 2)) {
+    // P tile (0, 1) from the wave with rP = 0, tile (2, 3) from rP = 2
 #pragma unroll
-    for (int z = 0; z < 2; ++z)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sP[(32 * z + 4 * gq + i) * LDC + 32 * z + 16 + idx] = Elem<T>::from_f32(0.f);
+    for (int i = 0; i < 4; ++i) sP[(16 * rP + 4 * gq + i) * LDC + 16 * rP + 16 + idx] = Elem<T>::from_f32(0.f);
   }
   __syncthreads();
 }
 
-// ---- T = (I + A)^{-1}: blocked 4 x 4 over 16 x 16 blocks (fp32) ----------
-// Diagonal blocks by forward substitution (lane idx solves column idx), then
-// T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj by sub-diagonal, with fp32 MFMA.
+// ---- WY products: Wk = (I + A)^{-1} diag(beta) Kt, Wv = (I + A)^{-1} diag(beta) V
+// by block forward substitution over the four 16-row blocks of the chunk:
+//   R_i = diag(beta_i) X_i - sum_{m<i} A_im W_m,   W_i = (I + A_ii)^{-1} R_i.
+// The four diagonal inverses are the only shared step (fp32, forward
+// substitution, one block per wave, lane idx solving column idx); after one
+// barrier every wave solves its own column tiles with no further exchange.
+// The 16 x 16 x 16 products take A_im and (I + A_ii)^{-1} rounded to bf16 and
+// the right-hand operands W_m and R_i as a hi/lo bf16 pair (fp32 path:
+// fp32 MFMA), accumulating in fp32.
 template <int LDF>
-__device__ __forceinline__ void tri_inverse(const float* sA, float* sT, int wave, int lane) {
-  const int idx = lane & 15, gq = lane >> 4;
+__device__ __forceinline__ void diag_inverses(const float* sA, float* sT, int wave, int lane) {
+  const int idx = lane & 15;
   if (wave < 4) {
     const int b0 = 16 * wave;
     float x[16];
@@ -382,95 +396,116 @@ __device__ __forceinline__ void tri_inverse(const float* sA, float* sT, int wave
       for (int m = 0; m < r; ++m) acc -= sA[(b0 + r) * LDF + b0 + m] * x[m];
       x[r] = acc;
     }
-    if (gq == 0) {
+    if (lane < 16) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDF + b0 + idx] = x[r];
     }
-    const int w = 48 - b0;  // columns right of the diagonal block
-    for (int e = lane; e < 16 * w; e += 64) sT[(b0 + e / w) * LDF + b0 + 16 + e % w] = 0.f;
   }
   __syncthreads();
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
-    const int j = wave, i = wave + d;
-    if (i < 4) {
-      f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      for (int m = j; m < i; ++m) {
-        const f32x4 a = frag_rows(sA, LDF, 16 * i + idx, 16 * m, gq);
-        f32x4 b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = sT[(16 * m + 4 * gq + e) * LDF + 16 * j + idx];
-        X = mma(a, b, X);
-      }
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      Y = mma(frag_rows(sT, LDF, 16 * i + idx, 16 * i, gq), X, Y);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * gq + r) * LDF + 16 * j + idx] = -Y[r];
-    }
-    __syncthreads();
-  }
 }
 
-// A-fragment of T diag(beta) (rows and k both over the chunk's tokens).
-template <typename T, int LDF> struct TbFrag;
-template <int LDF> struct TbFrag<bf16_t, LDF> {
-  __device__ static __forceinline__ bf16x8 get(const float* sT, const float* sBeta, int row, int k0, int g) {
-    const float* p = sT + row * LDF + k0 + 4 * g;
-    const f32x4 lo = *(const f32x4*)p, hi = *(const f32x4*)(p + 16);
-    const f32x4 blo = *(const f32x4*)(sBeta + k0 + 4 * g), bhi = *(const f32x4*)(sBeta + k0 + 16 + 4 * g);
-    const bf16x2 a = f32x2_to_bf16x2(lo[0] * blo[0], lo[1] * blo[1]);
-    const bf16x2 b = f32x2_to_bf16x2(lo[2] * blo[2], lo[3] * blo[3]);
-    const bf16x2 c = f32x2_to_bf16x2(hi[0] * bhi[0], hi[1] * bhi[1]);
-    const bf16x2 d = f32x2_to_bf16x2(hi[2] * bhi[2], hi[3] * bhi[3]);
-    return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 to_bf16x4(const f32x4& x) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1]));
+  const uint32_t b = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3]));
+  return __builtin_bit_cast(s16x4, (uint2){a, b});
+}
+__device__ __forceinline__ f32x4 from_bf16x4(const s16x4& h) {
+  const uint2 w = __builtin_bit_cast(uint2, h);
+  return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xffff0000u)};
+}
+
+// c + a b over k = 16 for one 16 x 16 tile: a is a coefficient fragment (row
+// idx, k = 4 g .. 4 g + 3), b an accumulator tile whose rows run over k,
+// prepared once as an operand (Opnd) and used by every product it enters.
+template <typename T> struct Sub;
+template <> struct Sub<bf16_t> {
+  typedef s16x4 Coef;
+  struct Opnd { s16x4 hi, lo; };
+  __device__ static __forceinline__ Coef coef(const float* p, bool neg) {
+    const f32x4 v = *(const f32x4*)p;
+    return to_bf16x4(neg ? -v : v);
+  }
+  __device__ static __forceinline__ Opnd opnd(const f32x4& b) {
+    Opnd o;
+    o.hi = to_bf16x4(b);
+    o.lo = to_bf16x4(b - from_bf16x4(o.hi));
+    return o;
+  }
+  __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, c, 0, 0, 0);
+  }
+  // rows 4 g .. 4 g + 3 of column `col` of X, from X^T stored channel-major
+  __device__ static __forceinline__ f32x4 rhs(const bf16_t* XT, int ldc, int col, int row0) {
+    const uint2 w = *(const uint2*)(XT + col * ldc + row0);
+    return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                   __uint_as_float(w.y & 0xffff0000u)};
   }
 };
-template <int LDF> struct TbFrag<float, LDF> {
-  __device__ static __forceinline__ f32x4 get(const float* sT, const float* sBeta, int row, int k0, int g) {
-    const f32x4 t = *(const f32x4*)(sT + row * LDF + k0 + 4 * g);
-    const f32x4 b = *(const f32x4*)(sBeta + k0 + 4 * g);
-    return (f32x4){t[0] * b[0], t[1] * b[1], t[2] * b[2], t[3] * b[3]};
+template <> struct Sub<float> {
+  typedef f32x4 Coef;
+  typedef f32x4 Opnd;
+  __device__ static __forceinline__ Coef coef(const float* p, bool neg) {
+    const f32x4 v = *(const f32x4*)p;
+    return neg ? -v : v;
+  }
+  __device__ static __forceinline__ Opnd opnd(const f32x4& b) { return b; }
+  __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) { return mma(a, b, c); }
+  __device__ static __forceinline__ f32x4 rhs(const float* XT, int ldc, int col, int row0) {
+    return *(const f32x4*)(XT + col * ldc + row0);
   }
 };
 
-// Fragments of T diag(beta) for the four row tiles of the chunk.  Tile rt
-// only needs k-blocks that reach row 16 rt + 15 (T is lower triangular).
-template <typename T, int D> struct WyOps {
+template <typename T, int D> struct Wy {
   typedef Lds<T, D> M;
-  typedef typename Frag<T>::type FragT;
-  static constexpr int KB = Elem<T>::KB, NKC = C / KB;
-  FragT a[4][NKC];
+  typedef Sub<T> S;
+  typename S::Coef tinv[4], a[4][3];  // (I + A_ii)^{-1}; -A_im for m < i
 
   __device__ __forceinline__ void load(const unsigned char* smem, int lane) {
+    const float* sA = (const float*)(smem + M::V);
     const float* sT = (const float*)(smem + M::G);
+    const int idx = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tinv[i] = S::coef(sT + (16 * i + idx) * M::LDF + 16 * i + 4 * gq, false);
+#pragma unroll
+      for (int m = 0; m < i; ++m) a[i][m] = S::coef(sA + (16 * i + idx) * M::LDF + 16 * m + 4 * gq, true);
+    }
+  }
+  // W = (I + A)^{-1} diag(beta) X for NX column tiles at once (column tile
+  // ct[t] of the channel-major X^T array xt[t]); the tiles' substitution
+  // chains are independent and interleaved.
+  template <int NX>
+  __device__ __forceinline__ void solve(const unsigned char* smem, const T* const (&xt)[NX], const int (&ct)[NX],
+                                        int lane, f32x4 (&w)[NX][4]) const {
     const float* sBeta = (const float*)(smem + M::BETA);
     const int idx = lane & 15, gq = lane >> 4;
+    typename S::Opnd wo[NX][3];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 b = *(const f32x4*)(sBeta + 16 * i + 4 * gq);
+      f32x4 r[NX];
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb)
-        if (kb * KB <= 16 * rt + 15) a[rt][kb] = TbFrag<T, M::LDF>::get(sT, sBeta, 16 * rt + idx, kb * KB, gq);
-  }
-  // out[rt] = (T diag(beta) X)[16 rt.., 16 ct..] with X^T stored channel-major
-  __device__ __forceinline__ void product(const T* XT, int ct, int lane, f32x4 out[4]) const {
-    const int idx = lane & 15, gq = lane >> 4;
+      for (int t = 0; t < NX; ++t) r[t] = S::rhs(xt[t], M::LDC, 16 * ct[t] + idx, 16 * i + 4 * gq) * b;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < i; ++m)
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb)
-        if (kb * KB <= 16 * rt + 15) acc = mma(a[rt][kb], frag_rows(XT, M::LDC, 16 * ct + idx, kb * KB, gq), acc);
-      out[rt] = acc;
+        for (int t = 0; t < NX; ++t) r[t] = S::apply(a[i][m], wo[t][m], r[t]);
+#pragma unroll
+      for (int t = 0; t < NX; ++t) {
+        w[t][i] = S::apply(tinv[i], S::opnd(r[t]), (f32x4){0.f, 0.f, 0.f, 0.f});
+        if (i < 3) wo[t][i] = S::opnd(w[t][i]);
+      }
     }
   }
 };
 
-// Wk tile (all 64 rows, 16 channels from 16 ct) into LDS, token-major.
+// Wk tile (all 64 rows, 16 channels from 16 ct) into LDS, token-major (K region).
 template <typename T, int D>
-__device__ __forceinline__ void store_wk(unsigned char* smem, const WyOps<T, D>& wy, int ct, int lane) {
+__device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4], int ct, int lane) {
   typedef Lds<T, D> M;
-  f32x4 w[4];
-  wy.product((const T*)(smem + M::KT), ct, lane, w);
   T* sW = (T*)(smem + M::K);
   const int idx = lane & 15, gq = lane >> 4;
 #pragma unroll
@@ -598,23 +633,32 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     if (j + 1 < j1) raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
     elementwise<T, D, NW, false>(smem, g_floor, tid);
     gram<T, D, NW, false>(smem, wave, lane);
-    tri_inverse<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
-    WyOps<T, D> wy;
+    diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
+    Wy<T, D> wy;
     wy.load(smem, lane);
-#pragma unroll
-    for (int c = 0; c < NR / NW; ++c) store_wk<T, D>(smem, wy, wave + NW * c, lane);
     // tile wave + NW x is a value tile exactly when x < NX / 2 (wave < NW)
+    // value tiles wave + NW x, x < NV: Wk and Wv of each, solved together
+    constexpr int NV = NX / 2;
+    const T* xt[2 * NV];
+    int cts[2 * NV];
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      xt[x] = (const T*)(smem + M::KT);
+      xt[NV + x] = (const T*)(smem + M::VT);
+      cts[x] = cts[NV + x] = wave + NW * x;
+    }
+    f32x4 wsol[2 * NV][4];
+    wy.template solve<2 * NV>(smem, xt, cts, lane, wsol);
+#pragma unroll
+    for (int x = 0; x < NV; ++x) store_wk<T, D>(smem, wsol[x], wave + NW * x, lane);
     f32x4 wv[NPAIR][2][4];
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (2 * p + c < NX / 2) {
-          wy.product((const T*)(smem + M::VT), wave + NW * (2 * p + c), lane, wv[p][c]);
-        } else {
+        const int x = 2 * p + c;
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) wv[p][c][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
+        for (int rt = 0; rt < 4; ++rt) wv[p][c][rt] = x < NV ? wsol[NV + x][rt] : (f32x4){0.f, 0.f, 0.f, 0.f};
       }
     __syncthreads();  // Wk complete
     f32x4 unused[2][4];
@@ -707,14 +751,25 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     if (j + 1 < j1) raw.load(q, k, v, g, beta, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid);
     elementwise<T, D, NW, true>(smem, g_floor, tid);
     gram<T, D, NW, true>(smem, wave, lane);
-    tri_inverse<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
-    WyOps<T, D> wy;
+    diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
+    Wy<T, D> wy;
     wy.load(smem, lane);
+    const T* xt[2 * CT];
+    int cts[2 * CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      xt[c] = (const T*)(smem + M::KT);
+      xt[CT + c] = (const T*)(smem + M::VT);
+      cts[c] = cts[CT + c] = wave + NW * c;
+    }
+    f32x4 wsol[2 * CT][4];
+    wy.template solve<2 * CT>(smem, xt, cts, lane, wsol);
     f32x4 wv[CT][4];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      store_wk<T, D>(smem, wy, wave + NW * c, lane);
-      wy.product((const T*)(smem + M::VT), wave + NW * c, lane, wv[c]);
+      store_wk<T, D>(smem, wsol[c], wave + NW * c, lane);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wsol[CT + c][rt];
     }
     __syncthreads();  // Wk complete
     f32x4 O[CT][4];
