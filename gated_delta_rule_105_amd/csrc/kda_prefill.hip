@@ -141,13 +141,16 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
   uint4 q[WITH_Q ? PER : 1], k[PER], v[PER], g[PER];
   float beta;
 
+  // Rows past the chunk's end (a sequence's last chunk) are loaded as zeros
+  // (beta and g of such rows must be 0; their q, k and v then reach no
+  // output).  The buffer is scoped to one chunk iteration.
   __device__ __forceinline__ void load(const T* Q, const T* K, const T* V, const T* G, const float* B,
-                                       int64_t tok0, int clen, int H, int h, int tid) {
+                                       int64_t tok0, int len, int H, int h, int tid) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
       const uint4 z = {0u, 0u, 0u, 0u};
-      if (t < clen) {
+      if (t < len) {
         const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;
         if (WITH_Q) q[j] = *(const uint4*)(Q + off);
         k[j] = *(const uint4*)(K + off);
@@ -160,7 +163,7 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
         g[j] = z;
       }
     }
-    beta = (tid < clen) ? B[(size_t)(tok0 + tid) * H + h] : 0.f;
+    beta = (tid < len) ? B[(size_t)(tok0 + tid) * H + h] : 0.f;
   }
 
   __device__ __forceinline__ void store(unsigned char* smem, int tid) const {
@@ -252,14 +255,16 @@ __device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, 
   const int cp = tid % NPR, c = 2 * cp, part = tid / NPR, t0 = TPP * part;
   auto at = [&](int t) { return t * (LDT / 2) + cp; };  // pair index of (row t, channel c)
 
+  // decays in log2 units, so that every factor is one v_exp_f32 (exp2)
+  constexpr float kLog2e = 1.4426950408889634f;
   float g0[TPP], g1[TPP];
   float p0 = 0.f, p1 = 0.f;
 #pragma unroll
   for (int s = 0; s < TPP; ++s) {
     const word w = sG[at(t0 + s)];
     const float x0 = PW::lo(w), x1 = PW::hi(w);
-    g0[s] = x0 < g_floor ? g_floor : x0;  // NaN stays NaN
-    g1[s] = x1 < g_floor ? g_floor : x1;
+    g0[s] = (x0 < g_floor ? g_floor : x0) * kLog2e;  // NaN stays NaN
+    g1[s] = (x1 < g_floor ? g_floor : x1) * kLog2e;
     p0 += g0[s];
     p1 += g1[s];
   }
@@ -274,7 +279,7 @@ __device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, 
     gl0 += x[0];
     gl1 += x[1];
   }
-  if (part == 0) *(f32x2*)(sGL + c) = (f32x2){__expf(gl0), __expf(gl1)};
+  if (part == 0) *(f32x2*)(sGL + c) = (f32x2){__builtin_amdgcn_exp2f(gl0), __builtin_amdgcn_exp2f(gl1)};
 
 #pragma unroll
   for (int b0 = 0; b0 < TPP; b0 += 8) {
@@ -291,7 +296,8 @@ __device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, 
     for (int s = 0; s < 8; ++s) {
       gam0 += g0[b0 + s];
       gam1 += g1[b0 + s];
-      const float e0 = __expf(gam0), e1 = __expf(gam1), ei0 = __expf(-gam0), ei1 = __expf(-gam1);
+      const float e0 = __builtin_amdgcn_exp2f(gam0), e1 = __builtin_amdgcn_exp2f(gam1);
+      const float ei0 = __builtin_amdgcn_exp2f(-gam0), ei1 = __builtin_amdgcn_exp2f(-gam1);
       const float k0 = PW::lo(kw[s]), k1 = PW::hi(kw[s]);
       kt[s] = PW::pack(k0 * e0, k1 * e1);
       kh[s] = PW::pack(k0 * ei0, k1 * ei1);
@@ -625,13 +631,17 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
           X[p][c][rr][i] = (col >= D && row == col - D) ? 1.f : 0.f;
         }
 
-  Raw<T, D, NT, false> raw;
-  raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
-  raw.store(smem, tid);
+  {
+    Raw<T, D, NT, false> first;
+    first.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
+    first.store(smem, tid);
+  }
   __syncthreads();
   for (int j = j0; j < j1; ++j) {
-    if (j + 1 < j1) raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
     elementwise<T, D, NW, false>(smem, g_floor, tid);
+    // the next chunk's inputs are fetched now and land in LDS at the end
+    Raw<T, D, NT, false> raw;
+    if (j + 1 < j1) raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
     gram<T, D, NW, false>(smem, wave, lane);
     diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
     Wy<T, D> wy;
@@ -741,15 +751,19 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) S[c][rr] = *(const f32x4*)(sin + R::tile(rr, wave + NW * c, lane));
 
-  Raw<T, D, NT, true> raw;
-  raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
-  raw.store(smem, tid);
+  {
+    Raw<T, D, NT, true> first;
+    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
+    first.store(smem, tid);
+  }
   __syncthreads();
   for (int j = j0; j < j1; ++j) {
     const int clen = min(C, sg.len - C * j);
     const int64_t tokc = sg.tok0 + (int64_t)C * j;
-    if (j + 1 < j1) raw.load(q, k, v, g, beta, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid);
     elementwise<T, D, NW, true>(smem, g_floor, tid);
+    // the next chunk's inputs are fetched now and land in LDS at the end
+    Raw<T, D, NT, true> raw;
+    if (j + 1 < j1) raw.load(q, k, v, g, beta, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid);
     gram<T, D, NW, true>(smem, wave, lane);
     diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
     Wy<T, D> wy;
@@ -785,7 +799,7 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         for (int i = 0; i < 4; ++i)
           sO[(16 * rt + 4 * gq + i) * M::LDT + 16 * (wave + NW * c) + idx] = Elem<T>::from_f32(O[c][rt][i]);
     __syncthreads();
-    raw.store_out(smem + M::KT, o, tokc, clen, H, h, tid);
+    Raw<T, D, NT, true>::store_out(smem + M::KT, o, tokc, clen, H, h, tid);
     if (j + 1 < j1) raw.store(smem, tid);
     __syncthreads();
   }
