@@ -203,3 +203,90 @@ def test_chunk_forward_deterministic():
     o1, h1 = gpu_forward(inp)
     o2, h2 = gpu_forward(inp)
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+# ------------------------------------------------ cross-checks on the GPU
+def _dev(inp):
+    return {key: (val.cuda() if isinstance(val, torch.Tensor) else val) for key, val in inp.items()}
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+def test_decode_steps_equal_chunk_forward(d, dtype):
+    """T decode steps from h0 reproduce o and ht of one chunked forward."""
+    B, T, H = 3, 150, 2
+    inp = _case(B, T, H, d, dtype, wid=140 + d)
+    note(f"decode x{T} vs chunk_forward B{B} H{H} d{d} {dtype}")
+    dv = _dev(inp)
+    o, ht = kda.chunk_forward(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], h0=dv["h0"])
+    state = dv["h0"].clone()
+    od = torch.empty_like(o)
+    for t in range(T):
+        od[:, t] = kda.decode_step(dv["q"][:, t].contiguous(), dv["k"][:, t].contiguous(), dv["v"][:, t].contiguous(),
+                                   dv["g"][:, t].contiguous(), dv["beta"][:, t].contiguous(), state)
+    torch.cuda.synchronize()
+    ro, rht = oracle_forward(inp)
+    for name, x, ref in (("o chunk", o, ro), ("o decode", od, ro), ("ht chunk", ht, rht), ("ht decode", state, rht)):
+        e = rel_err(f64(x), ref)
+        print(f"{name}: {e:.3e}")
+        assert e <= TOL[dtype], name
+    e = rel_err(f64(od), f64(o))
+    print(f"decode vs chunk o: {e:.3e}")
+    assert e <= 2 * TOL[dtype]
+
+
+@pytest.mark.parametrize("split", [64, 100, 1000])
+def test_split_resume(split):
+    """run(T) equals run(T1) followed by run(T - T1, h0 = ht), split on and
+    off chunk and segment boundaries."""
+    T, H, d = 2000, 2, 128
+    inp = _case(1, T, H, d, "bf16", wid=150)
+    note(f"split/resume T={T} at {split}")
+    dv = _dev(inp)
+    o, ht = kda.chunk_forward(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], h0=dv["h0"])
+    a = {key: dv[key][:, :split].contiguous() for key in ("q", "k", "v", "g", "beta")}
+    b = {key: dv[key][:, split:].contiguous() for key in ("q", "k", "v", "g", "beta")}
+    o1, h1 = kda.chunk_forward(a["q"], a["k"], a["v"], a["g"], a["beta"], h0=dv["h0"])
+    o2, h2 = kda.chunk_forward(b["q"], b["k"], b["v"], b["g"], b["beta"], h0=h1)
+    torch.cuda.synchronize()
+    ro, rht = oracle_forward(inp)
+    e_o = rel_err(f64(torch.cat([o1, o2], dim=1)), ro)
+    e_h = rel_err(f64(h2), rht)
+    e_self = rel_err(f64(torch.cat([o1, o2], dim=1)), f64(o))
+    print(f"split {split}: err_o={e_o:.3e} err_ht={e_h:.3e} vs whole={e_self:.3e}")
+    assert e_o <= TOL["bf16"] and e_h <= TOL["bf16"] and e_self <= 2 * TOL["bf16"]
+
+
+def test_linearity_fp32():
+    """(v, h0) -> (o, ht) is linear for fixed q, k, g, beta (fp32 path)."""
+    T, H, d = 300, 2, 64
+    inp = _case(1, T, H, d, "f32", wid=160)
+    note("linearity fp32 T=300 d=64")
+    dv = _dev(inp)
+    gen = torch.Generator(device="cpu").manual_seed(161)
+    v2 = torch.randn(dv["v"].shape, generator=gen).cuda()
+    h2 = 0.02 * torch.randn(dv["h0"].shape, generator=gen).cuda()
+    a, b = 0.7, -1.3
+    run = lambda v, h: kda.chunk_forward(dv["q"], dv["k"], v.contiguous(), dv["g"], dv["beta"], h0=h.contiguous())
+    o1, s1 = run(dv["v"], dv["h0"])
+    o2, s2 = run(v2, h2)
+    o3, s3 = run(a * dv["v"] + b * v2, a * dv["h0"] + b * h2)
+    torch.cuda.synchronize()
+    e_o = rel_err(f64(o3), f64(a * o1 + b * o2))
+    e_s = rel_err(f64(s3), f64(a * s1 + b * s2))
+    print(f"linearity: o {e_o:.3e} ht {e_s:.3e}")
+    assert e_o <= 1e-4 and e_s <= 1e-4
+
+
+def test_value_column_independence():
+    """Permuting v's columns (and h0's) permutes o and ht the same way: the
+    value columns of the state never mix."""
+    T, H, d = 500, 2, 128
+    inp = _case(1, T, H, d, "bf16", wid=170)
+    note("value-column permutation T=500 d=128")
+    dv = _dev(inp)
+    perm = torch.randperm(d, generator=torch.Generator().manual_seed(171)).cuda()
+    o, ht = kda.chunk_forward(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], h0=dv["h0"])
+    op, htp = kda.chunk_forward(dv["q"], dv["k"], dv["v"][..., perm].contiguous(), dv["g"], dv["beta"],
+                                h0=dv["h0"][..., perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(op, o[..., perm]) and torch.equal(htp, ht[..., perm])
