@@ -18,7 +18,8 @@ Prints ONE JSON line.  ``roofline`` describes the dominant kernel work, the
 chunked forward call, against HBM: algorithmic bytes per call divided by the
 call's mean duration from HIP events recorded on the launch stream.
 ``cpu_baseline`` times the fp64 CPU oracle on the host cores (a baseline, not
-a target).  Other legs: ``--copy-calib MiB`` runs only a device copy of known
+a target).  ``other_workloads`` times the packed 8-sequence batch and the
+1,048,576-token context.  Other legs: ``--copy-calib MiB`` runs only a device copy of known
 size (for scaling the HBM byte counters), ``--only prefill|decode`` runs one
 leg, ``--no-cpu`` skips the oracle.
 """
@@ -95,6 +96,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1000, help="timed decode steps")
     ap.add_argument("--only", choices=("prefill", "decode", "both"), default="both")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the packed and long-context workloads")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="only run device copies of this size (counter calibration)")
     return ap.parse_args()
@@ -155,6 +157,45 @@ def bench_prefill(steps: int, warmup: int):
     flop_call = token_heads * FLOP_PER_TOKEN_HEAD
     return dict(wall=wall, mean_call=mean_call, min_call=min(durs), tokens=B * T,
                 bytes_call=bytes_call, flop_call=flop_call, n_sets=n_sets)
+
+
+def bench_workload(wid: int, calls: int):
+    """Secondary prefill workloads (packed batch, long context): tokens/s."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[wid]
+    log(f"workload {w.name}: inputs generated on the GPU")
+    inp = synth.workload_inputs(w, device="cuda")
+    T = inp["q"].shape[1]
+    n_seqs = 0 if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    ws = torch.empty(kda.workspace_bytes(1, T, w.H, w.dk, torch.bfloat16, n_seqs), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["q"])
+    ht = torch.empty((n_seqs or 1, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+    def call():
+        kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"],
+                          cu_seqlens=inp["cu_seqlens"], o=o, ht=ht, workspace=ws, validate_cu=False)
+
+    call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    mean = sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+    token_heads = T * w.H
+    bytes_call = token_heads * BYTES_PER_TOKEN_HEAD + 2 * (n_seqs or 1) * w.H * STATE_BYTES
+    log(f"workload {w.name}: {calls} calls, mean {mean * 1e6:.1f} us")
+    del inp, o, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "tokens": T, "heads": w.H, "mean_call_us": mean * 1e6,
+            "value": T / mean, "unit": "tokens/s", "hbm_frac": bytes_call / mean / 1e9 / PEAK_HBM_GBS,
+            "mfma_frac": token_heads * FLOP_PER_TOKEN_HEAD / mean / 1e12 / PEAK_BF16_TFLOPS}
 
 
 def bench_decode(steps: int, warmup: int):
@@ -249,6 +290,10 @@ def main() -> int:
         out["mfma"] = {"achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop": p["flop_call"]}
         out["config"]["buffer_sets"] = p["n_sets"]
+    if args.only in ("prefill", "both") and not args.no_extra:
+        # the packed 8-sequence batch and the million-token context, timed the
+        # same way (secondary lines: the headline value is the workload above)
+        out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3)]
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

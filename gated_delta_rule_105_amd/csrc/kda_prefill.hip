@@ -39,6 +39,13 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
+#ifndef KDA_NW128
+#define KDA_NW128 4
+#endif
+#ifndef KDA_NW128_FWD
+#define KDA_NW128_FWD 4
+#endif
+
 namespace kda {
 namespace {
 
@@ -323,7 +330,7 @@ template <typename T, int D, int NW, bool WITH_P>
 __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
   typedef Lds<T, D> M;
   typedef typename Frag<T>::type FragT;
-  static_assert(NW == 4, "one row tile of A per wave");
+  static_assert(NW == 4 || NW == 8, "row tiles of A and P over four or eight waves");
   constexpr int KB = Elem<T>::KB, NKD = D / KB, LDT = M::LDT, LDC = M::LDC, LDF = M::LDF;
   const T* sQ = (const T*)(smem + M::Q);
   const T* sK = (const T*)(smem + M::K);
@@ -332,16 +339,18 @@ __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
   T* sP = (T*)(smem + M::P);
   const float* sBeta = (const float*)(smem + M::BETA);
   const int idx = lane & 15, gq = lane >> 4;
-  const int rA = wave, rP = 3 - wave;  // wave-uniform
+  // four waves: row tile w of A and 3 - w of P; eight: A on waves 0-3, P on 4-7
+  const int rA = NW == 4 ? wave : (wave < 4 ? wave : -1);
+  const int rP = NW == 4 ? 3 - wave : (wave >= 4 ? 7 - wave : -1);  // wave-uniform
   FragT fa[NKD], fq[NKD];
 #pragma unroll
   for (int kb = 0; kb < NKD; ++kb) {
-    fa[kb] = frag_rows(sK, LDT, 16 * rA + idx, kb * KB, gq);
-    if (WITH_P) fq[kb] = frag_rows(sQ, LDT, 16 * rP + idx, kb * KB, gq);
+    if (rA >= 0) fa[kb] = frag_rows(sK, LDT, 16 * rA + idx, kb * KB, gq);
+    if (WITH_P && rP >= 0) fq[kb] = frag_rows(sQ, LDT, 16 * rP + idx, kb * KB, gq);
   }
   float br[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) br[i] = sBeta[16 * rA + 4 * gq + i];
+  for (int i = 0; i < 4; ++i) br[i] = rA >= 0 ? sBeta[16 * rA + 4 * gq + i] : 0.f;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const bool doA = ct <= rA, doP = WITH_P && ct <= rP;
@@ -968,7 +977,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NW2>
 int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
                  const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
                  float* ht, void* ws, hipStream_t stream) {
@@ -988,7 +997,7 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_forward<T, D, NW>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0, stream,
+    hipLaunchKernelGGL((kda_seg_forward<T, D, NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor,
                        (const float*)wsf, (T*)o, ht);
     e = hipGetLastError();
@@ -1003,11 +1012,11 @@ int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const Seg
                          const float* h0, const int32_t* cu, void* o, float* ht, void* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
   if (is_bf16 && d == 128)
-    return launch_typed<bf16_t, 128, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
   return (int)hipErrorInvalidValue;
 }
 
