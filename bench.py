@@ -284,7 +284,7 @@ def main() -> int:
                                source_digest(PREFILL_SOURCES))
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
-                           "kernel": "kda_chunk_forward call (kda_chunk_local + kda_state_pass)",
+                           "kernel": "kda_chunk_forward call (kda_chunk_prep, kda_seg_maps, kda_seg_scan, kda_seg_forward)",
                            "algorithmic_bytes": p["bytes_call"], "mean_call_us": p["mean_call"] * 1e6}
         tf = p["flop_call"] / p["mean_call"] / 1e12
         out["mfma"] = {"achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

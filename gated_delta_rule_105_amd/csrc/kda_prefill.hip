@@ -18,29 +18,34 @@
 //
 // One chunk maps the state affinely, S -> M_j S + B_j.  Every sequence is cut
 // into segments of L chunks; the composition of a segment's maps is again
-// affine, S_out = M S_in + B.  Three launches:
-//   1. kda_seg_summary (one workgroup per (segment, head), all in parallel):
-//      runs the segment's chunks on the augmented state [B | M], started from
-//      [0 | I], with the value part of U switched off for the M columns, and
-//      writes B and M.  The last segment of a sequence is skipped: no later
-//      segment needs its map.
-//   2. kda_seg_scan (one workgroup per (sequence, head, 16 state columns)):
+// affine, S_out = M S_in + B.  Four launches:
+//   1. kda_chunk_prep (one workgroup per (segment, head), all in parallel):
+//      the chunk-local part of each chunk (decay prefix sums, Gram blocks,
+//      the inverse (I + A)^{-1}, Wk and Wv) from the inputs, written to a
+//      per-chunk record: Qt, Wk, Kh^T, P and gamma as an image of the state
+//      passes' LDS, and Wv.
+//   2. kda_seg_maps (one workgroup per (segment, head), all in parallel):
+//      runs the segment's chunk records on the state started from 0 (giving
+//      B, half of the waves) and from I with the value part of U switched off
+//      (giving M, the other half).  The
+//      last segment of a sequence is skipped: no later segment needs its map.
+//   3. kda_seg_scan (one workgroup per (sequence, head, 16 state columns)):
 //      S_0 = h0, S_{s+1} = M_s S_s + B_s, writing every segment's incoming
 //      state.  M S is done as three bf16 products of a hi/lo split of both
 //      factors (about fp32 accuracy).
-//   3. kda_seg_forward (one workgroup per (segment, head), all in parallel):
-//      the full chunk recurrence from the segment's incoming state, writing o
-//      and, for the last segment, the final state.
-// The chunk-local part (decay prefix sums, the Gram blocks, the triangular
-// inverse, Wk and Wv) is recomputed in both chunk passes from the inputs;
-// nothing per chunk goes through device memory.  Within a workgroup, wave w
-// owns 16 value columns of S (32 columns of [B | M] in pass 1): columns of
+//   4. kda_seg_forward (one workgroup per (segment, head), all in parallel):
+//      the state recurrence from the segment's incoming state over its chunk
+//      records, writing o and, for the last segment, the final state.
+// Launches 2 and 4 keep two record images in LDS (about 62 KiB each at
+// d = 128): the next chunk's image lands by direct global-to-LDS loads while
+// the current one is used.
+// Within a workgroup, wave w owns 16 value columns of the state: columns of
 // U, O and S never mix, so the state products need no exchange.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 #ifndef KDA_NW128
-#define KDA_NW128 4
+#define KDA_NW128 8
 #endif
 #ifndef KDA_NW128_FWD
 #define KDA_NW128_FWD 4
@@ -389,15 +394,18 @@ __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
   __syncthreads();
 }
 
-// ---- WY products: Wk = (I + A)^{-1} diag(beta) Kt, Wv = (I + A)^{-1} diag(beta) V
-// by block forward substitution over the four 16-row blocks of the chunk:
-//   R_i = diag(beta_i) X_i - sum_{m<i} A_im W_m,   W_i = (I + A_ii)^{-1} R_i.
-// The four diagonal inverses are the only shared step (fp32, forward
-// substitution, one block per wave, lane idx solving column idx); after one
-// barrier every wave solves its own column tiles with no further exchange.
-// The 16 x 16 x 16 products take A_im and (I + A_ii)^{-1} rounded to bf16 and
-// the right-hand operands W_m and R_i as a hi/lo bf16 pair (fp32 path:
-// fp32 MFMA), accumulating in fp32.
+// ---- the inverse (I + A)^{-1} and the WY products -----------------------
+// Tp = (I + A)^{-1} diag(beta) (64 x 64, lower triangular) is formed once per
+// chunk, by 16-column blocks: wave j < 4 takes column block j,
+//   Tp_jj = T_jj diag(beta_j),   Tp_ij = -T_ii sum_{m=j}^{i-1} A_im Tp_mj  (i > j),
+// with the diagonal inverses T_ii = (I + A_ii)^{-1} from fp32 forward
+// substitution.  The 16 x 16 x 16 products take A_im and T_ii rounded to bf16
+// and Tp_mj as a hi/lo bf16 pair (fp32 path: fp32 MFMA), accumulating in
+// fp32.  Tp goes to LDS as a hi and a lo bf16 array (fp32 path: one fp32
+// array), zeros above the diagonal.  Then
+//   Wk = Tp Kt,   Wv = Tp V
+// are plain MFMA products whose right-hand operands are the chunk operands
+// themselves (exact in bf16): only Tp needs the two-term split.
 template <int LDF>
 __device__ __forceinline__ void diag_inverses(const float* sA, float* sT, int wave, int lane) {
   const int idx = lane & 15;
@@ -452,12 +460,6 @@ template <> struct Sub<bf16_t> {
     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, c, 0, 0, 0);
   }
-  // rows 4 g .. 4 g + 3 of column `col` of X, from X^T stored channel-major
-  __device__ static __forceinline__ f32x4 rhs(const bf16_t* XT, int ldc, int col, int row0) {
-    const uint2 w = *(const uint2*)(XT + col * ldc + row0);
-    return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-                   __uint_as_float(w.y & 0xffff0000u)};
-  }
 };
 template <> struct Sub<float> {
   typedef f32x4 Coef;
@@ -468,60 +470,117 @@ template <> struct Sub<float> {
   }
   __device__ static __forceinline__ Opnd opnd(const f32x4& b) { return b; }
   __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) { return mma(a, b, c); }
-  __device__ static __forceinline__ f32x4 rhs(const float* XT, int ldc, int col, int row0) {
-    return *(const f32x4*)(XT + col * ldc + row0);
-  }
 };
 
-template <typename T, int D> struct Wy {
+// Tp in the K area (free after the Gram blocks): rows of LD elements; bf16
+// keeps Tp = hi + lo in two arrays.
+template <typename T, int D> struct TpArea {
+  static constexpr int LD = C + 4;
+  static constexpr int HI = Lds<T, D>::K;
+  static constexpr int LO = HI + C * LD * (int)sizeof(T);
+  static_assert((sizeof(T) == 2 ? 2 : 1) * C * LD * sizeof(T) <= (size_t)Lds<T, D>::ROW, "Tp fits the K area");
+};
+
+// tile (i, j) of Tp (accumulator layout) into the Tp area
+template <typename T, int D>
+__device__ __forceinline__ void store_tp(unsigned char* smem, const f32x4& w, int i, int j, int lane) {
+  typedef TpArea<T, D> TP;
+  const int idx = lane & 15, gq = lane >> 4;
+  const int off = (16 * i + 4 * gq) * TP::LD + 16 * j + idx;
+  if constexpr (sizeof(T) == 2) {
+    const s16x4 hi = to_bf16x4(w);
+    const uint2 h = __builtin_bit_cast(uint2, hi);
+    const uint2 l = __builtin_bit_cast(uint2, to_bf16x4(w - from_bf16x4(hi)));
+    bf16_t* ph = (bf16_t*)(smem + TP::HI) + off;
+    bf16_t* pl = (bf16_t*)(smem + TP::LO) + off;
+    ph[0] = (bf16_t)(h.x & 0xffffu);
+    ph[TP::LD] = (bf16_t)(h.x >> 16);
+    ph[2 * TP::LD] = (bf16_t)(h.y & 0xffffu);
+    ph[3 * TP::LD] = (bf16_t)(h.y >> 16);
+    pl[0] = (bf16_t)(l.x & 0xffffu);
+    pl[TP::LD] = (bf16_t)(l.x >> 16);
+    pl[2 * TP::LD] = (bf16_t)(l.y & 0xffffu);
+    pl[3 * TP::LD] = (bf16_t)(l.y >> 16);
+  } else {
+    float* p = (float*)(smem + TP::HI) + off;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e * TP::LD] = w[e];
+  }
+}
+
+// Column block j = wave (< 4) of Tp into the Tp area.  Reads A (V area) and
+// the diagonal inverses (G area).
+template <typename T, int D>
+__device__ __forceinline__ void inverse_cols(unsigned char* smem, int wave, int lane) {
   typedef Lds<T, D> M;
   typedef Sub<T> S;
-  typename S::Coef tinv[4], a[4][3];  // (I + A_ii)^{-1}; -A_im for m < i
-
-  __device__ __forceinline__ void load(const unsigned char* smem, int lane) {
-    const float* sA = (const float*)(smem + M::V);
-    const float* sT = (const float*)(smem + M::G);
-    const int idx = lane & 15, gq = lane >> 4;
+  const float* sA = (const float*)(smem + M::V);
+  const float* sT = (const float*)(smem + M::G);
+  const float* sBeta = (const float*)(smem + M::BETA);
+  const int idx = lane & 15, gq = lane >> 4, j = wave;
+  typename S::Opnd wo[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tinv[i] = S::coef(sT + (16 * i + idx) * M::LDF + 16 * i + 4 * gq, false);
+  for (int i = 0; i < 4; ++i) {
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+    if (i == j) {
+      const float b = sBeta[16 * i + idx];
 #pragma unroll
-      for (int m = 0; m < i; ++m) a[i][m] = S::coef(sA + (16 * i + idx) * M::LDF + 16 * m + 4 * gq, true);
-    }
-  }
-  // W = (I + A)^{-1} diag(beta) X for NX column tiles at once (column tile
-  // ct[t] of the channel-major X^T array xt[t]); the tiles' substitution
-  // chains are independent and interleaved.
-  template <int NX>
-  __device__ __forceinline__ void solve(const unsigned char* smem, const T* const (&xt)[NX], const int (&ct)[NX],
-                                        int lane, f32x4 (&w)[NX][4]) const {
-    const float* sBeta = (const float*)(smem + M::BETA);
-    const int idx = lane & 15, gq = lane >> 4;
-    typename S::Opnd wo[NX][3];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 b = *(const f32x4*)(sBeta + 16 * i + 4 * gq);
-      f32x4 r[NX];
-#pragma unroll
-      for (int t = 0; t < NX; ++t) r[t] = S::rhs(xt[t], M::LDC, 16 * ct[t] + idx, 16 * i + 4 * gq) * b;
+      for (int e = 0; e < 4; ++e) w[e] = sT[(16 * i + 4 * gq + e) * M::LDF + 16 * i + idx] * b;
+    } else if (i > j) {
+      f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < i; ++m)
+        if (m >= j) r = S::apply(S::coef(sA + (16 * i + idx) * M::LDF + 16 * m + 4 * gq, true), wo[m], r);
+      w = S::apply(S::coef(sT + (16 * i + idx) * M::LDF + 16 * i + 4 * gq, false), S::opnd(r),
+                   (f32x4){0.f, 0.f, 0.f, 0.f});
+    }
+    if (i < 3 && i >= j) wo[i] = S::opnd(w);
+    store_tp<T, D>(smem, w, i, j, lane);
+  }
+}
+
+// W = Tp X for NX column tiles: tile ct[t] of the channel-major X^T array
+// xt[t]; w[t][rb] is row tile rb.  Tp's zero blocks above the diagonal are
+// skipped where a whole k-block is zero.
+template <typename T, int D, int NX>
+__device__ __forceinline__ void w_products(const unsigned char* smem, const T* const (&xt)[NX], const int (&ct)[NX],
+                                           int lane, f32x4 (&w)[NX][4]) {
+  typedef Lds<T, D> M;
+  typedef TpArea<T, D> TP;
+  typedef typename Frag<T>::type FragT;
+  constexpr int KB = Elem<T>::KB, NKC = C / KB;
+  const int idx = lane & 15, gq = lane >> 4;
+  const T* tph = (const T*)(smem + TP::HI);
+  const T* tpl = (const T*)(smem + TP::LO);
+  FragT xb[NX][NKC];
 #pragma unroll
-        for (int t = 0; t < NX; ++t) r[t] = S::apply(a[i][m], wo[t][m], r[t]);
+  for (int t = 0; t < NX; ++t)
 #pragma unroll
-      for (int t = 0; t < NX; ++t) {
-        w[t][i] = S::apply(tinv[i], S::opnd(r[t]), (f32x4){0.f, 0.f, 0.f, 0.f});
-        if (i < 3) wo[t][i] = S::opnd(w[t][i]);
+    for (int kb = 0; kb < NKC; ++kb) xb[t][kb] = frag_rows(xt[t], M::LDC, 16 * ct[t] + idx, kb * KB, gq);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+    for (int t = 0; t < NX; ++t) w[t][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) {
+      if (kb * KB > 16 * rb + 15) continue;
+      const FragT ah = frag_rows(tph, TP::LD, 16 * rb + idx, kb * KB, gq);
+#pragma unroll
+      for (int t = 0; t < NX; ++t) w[t][rb] = mma(ah, xb[t][kb], w[t][rb]);
+      if constexpr (sizeof(T) == 2) {
+        const FragT al = frag_rows(tpl, TP::LD, 16 * rb + idx, kb * KB, gq);
+#pragma unroll
+        for (int t = 0; t < NX; ++t) w[t][rb] = mma(al, xb[t][kb], w[t][rb]);
       }
     }
   }
-};
+}
 
-// Wk tile (all 64 rows, 16 channels from 16 ct) into LDS, token-major (K region).
-template <typename T, int D>
+// Wk tile (all 64 rows, 16 channels from 16 ct) into LDS area AREA, token-major.
+template <typename T, int D, int AREA>
 __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4], int ct, int lane) {
   typedef Lds<T, D> M;
-  T* sW = (T*)(smem + M::K);
+  T* sW = (T*)(smem + AREA);
   const int idx = lane & 15, gq = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -529,21 +588,86 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
     for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * gq + i) * M::LDT + 16 * ct + idx] = Elem<T>::from_f32(w[rt][i]);
 }
 
+// ---- chunk record: what the chunk pass leaves for the two state passes,
+// per (chunk slot, head), in device memory.  It starts with an image of the
+// state passes' LDS (Img), copied linearly in 16-byte pieces:
+//   QT  [64][LDT]  Qt rows              (operand type)
+//   WK  [64][LDT]  Wk rows              (operand type)
+//   KH  [D][LDC]   Kh^T, channel-major  (operand type)
+//   P   [64][LDC]  P                    (operand type)
+//   GAM [D]        gamma                (fp32)
+// padded to a multiple of 1 KiB, then
+//   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv (fp32), accumulator order.
+// Chunk c of global segment gs has slot gs * L + c.
+template <typename T, int D> struct Img {
+  typedef Lds<T, D> M;
+  static constexpr int QT = 0, WK = QT + M::ROW_T, KH = WK + M::ROW_T, P = KH + D * M::LDC * (int)sizeof(T),
+                       GAM = P + C * M::LDC * (int)sizeof(T), END = GAM + D * 4, BYTES = (END + 1023) / 1024 * 1024;
+};
+template <typename T, int D> struct CRec {
+  static constexpr size_t WV = Img<T, D>::BYTES, BYTES = WV + (size_t)C * D * 4;
+  __device__ static __forceinline__ size_t wv(int ct, int rt, int lane) {
+    return WV + (((size_t)ct * 4 + rt) * 64 + lane) * 16;
+  }
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS [src, src + bytes) -> device memory, 16-byte pieces over NT threads
+template <int NT, int BYTES>
+__device__ __forceinline__ void copy_out(const unsigned char* src, unsigned char* dst, int tid) {
+  static_assert(BYTES % 16 == 0, "16-byte pieces");
+#pragma unroll
+  for (int i = tid; i < BYTES / 16; i += NT) *(u32x4*)(dst + 16 * i) = *(const u32x4*)(src + 16 * i);
+}
+
+// The chunk's record from the chunk pass's LDS (Qt in Q, Wk in WKA, Kh^T in
+// KH, P in P, gamma in GL) and Wv tiles held by the waves.
+template <typename T, int D, int NT, int WKA>
+__device__ __forceinline__ void save_record(const unsigned char* smem, unsigned char* rec, int tid) {
+  typedef Lds<T, D> M;
+  typedef Img<T, D> I;
+  copy_out<NT, I::WK - I::QT>(smem + M::Q, rec + I::QT, tid);
+  copy_out<NT, I::KH - I::WK>(smem + WKA, rec + I::WK, tid);
+  copy_out<NT, I::P - I::KH>(smem + M::KH, rec + I::KH, tid);
+  copy_out<NT, I::GAM - I::P>(smem + M::P, rec + I::P, tid);
+  copy_out<NT, I::END - I::GAM>(smem + M::GL, rec + I::GAM, tid);
+}
+
+// Record image -> LDS `dst` by direct global-to-LDS loads (lane i of a wave
+// fills bytes 16 i .. 16 i + 15 of a 1 KiB block; no registers held).  The
+// loads are only issued: vmcnt_wait_all() and a barrier make them visible.
+template <typename T, int D, int NW>
+__device__ __forceinline__ void issue_image(unsigned char* dst, const unsigned char* rec, int wave, int lane) {
+  constexpr int NB = Img<T, D>::BYTES / 1024;
+  for (int b = wave; b < NB; b += NW)
+    __builtin_amdgcn_global_load_lds((const void*)(rec + 1024 * b + 16 * lane),
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16, 0, 0);
+}
+__device__ __forceinline__ void vmcnt_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Workgroup barrier that orders LDS reads and writes only: it waits for this
+// wave's LDS operations but not for its global loads, so direct-to-LDS loads
+// into the other image buffer stay in flight (__syncthreads() would wait for
+// them as pending LDS writes).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // CT column tiles of the state (rows = D key channels) through one chunk:
 // U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
-// O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  Every A-operand
-// fragment read from LDS feeds the CT tiles.
+// O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  The operands are
+// read from a record image in LDS at `img`.  Every A-operand fragment feeds the CT
+// tiles.
 template <typename T, int D, int CT, bool WITH_O>
-__device__ __forceinline__ void state_step(const unsigned char* smem, f32x4 (&S)[CT][D / 16],
+__device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[CT][D / 16],
                                            const f32x4 (&wv)[CT][4], f32x4 (&O)[CT][4], int lane) {
   typedef Lds<T, D> M;
+  typedef Img<T, D> I;
   typedef typename Frag<T>::type FragT;
   constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, LDT = M::LDT, LDC = M::LDC;
-  const T* sQ = (const T*)(smem + M::Q);
-  const T* sW = (const T*)(smem + M::K);
-  const T* sP = (const T*)(smem + M::P);
-  const T* sKH = (const T*)(smem + M::KH);
-  const float* sGL = (const float*)(smem + M::GL);
+  const T* sQ = (const T*)(img + I::QT);
+  const T* sW = (const T*)(img + I::WK);
+  const T* sP = (const T*)(img + I::P);
+  const T* sKH = (const T*)(img + I::KH);
+  const float* sGL = (const float*)(img + I::GAM);
   const int idx = lane & 15, gq = lane >> 4;
 
   FragT SB[CT][NKD];
@@ -607,112 +731,160 @@ __device__ __forceinline__ void state_step(const unsigned char* smem, f32x4 (&S)
   }
 }
 
-// ---- pass 1: affine map [B | M] of every segment but the last ------------
-// Wave w owns the 2 D / 16 / NW column tiles w + NW x of [B | M] (tiles below
-// D / 16 are value columns), processed two at a time.
+// ---- pass 1: the chunk-local part of every chunk -> its record -----------
+// One workgroup per (segment, head) walks the segment's chunks; the inputs
+// of the next chunk are fetched while the current one is finished.  Wave w
+// forms Wk and Wv for the value-column tiles w + NW x.
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
-kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
-                const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_rows, int T_per,
-                int H, int L, float g_floor, float* __restrict__ ws) {
+kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+               const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+               int n_rows, int T_per, int H, int L, float g_floor, unsigned char* __restrict__ crec) {
   typedef Lds<T, D> M;
-  constexpr int NT = 64 * NW, NR = D / 16, NX = 2 * NR / NW, NPAIR = NX / 2;
-  static_assert(NX >= 2 && NX % 2 == 0, "each wave owns pairs of column tiles");
+  typedef CRec<T, D> CR;
+  constexpr int NT = 64 * NW, NR = D / 16, NV = NR / NW;
+  static_assert(NV >= 1 && NV * NW == NR, "waves must split the value columns");
   __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
-  if (sg.s == sg.nseg - 1) return;  // nothing downstream needs the last map
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
-  const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
 
-  f32x4 X[NPAIR][2][NR];
-#pragma unroll
-  for (int p = 0; p < NPAIR; ++p)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * rr + 4 * gq + i, col = 16 * (wave + NW * (2 * p + c)) + idx;
-          X[p][c][rr][i] = (col >= D && row == col - D) ? 1.f : 0.f;
-        }
-
   {
-    Raw<T, D, NT, false> first;
-    first.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
+    Raw<T, D, NT, true> first;
+    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
     first.store(smem, tid);
   }
   __syncthreads();
   for (int j = j0; j < j1; ++j) {
-    elementwise<T, D, NW, false>(smem, g_floor, tid);
+    elementwise<T, D, NW, true>(smem, g_floor, tid);
     // the next chunk's inputs are fetched now and land in LDS at the end
-    Raw<T, D, NT, false> raw;
-    if (j + 1 < j1) raw.load(nullptr, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
-    gram<T, D, NW, false>(smem, wave, lane);
+    Raw<T, D, NT, true> raw;
+    if (j + 1 < j1)
+      raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
+    gram<T, D, NW, true>(smem, wave, lane);
     diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
-    Wy<T, D> wy;
-    wy.load(smem, lane);
-    // tile wave + NW x is a value tile exactly when x < NX / 2 (wave < NW)
-    // value tiles wave + NW x, x < NV: Wk and Wv of each, solved together
-    constexpr int NV = NX / 2;
-    const T* xt[2 * NV];
-    int cts[2 * NV];
+    if (wave < 4) inverse_cols<T, D>(smem, wave, lane);
+    __syncthreads();  // Tp complete; A and the diagonal inverses are dead
+    const T* xk[NV];
+    const T* xv[NV];
+    int cts[NV];
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
-      xt[x] = (const T*)(smem + M::KT);
-      xt[NV + x] = (const T*)(smem + M::VT);
-      cts[x] = cts[NV + x] = wave + NW * x;
+      xk[x] = (const T*)(smem + M::KT);
+      xv[x] = (const T*)(smem + M::VT);
+      cts[x] = wave + NW * x;
     }
-    f32x4 wsol[2 * NV][4];
-    wy.template solve<2 * NV>(smem, xt, cts, lane, wsol);
+    {
+      f32x4 wk[NV][4];
+      w_products<T, D, NV>(smem, xk, cts, lane, wk);
 #pragma unroll
-    for (int x = 0; x < NV; ++x) store_wk<T, D>(smem, wsol[x], wave + NW * x, lane);
-    f32x4 wv[NPAIR][2][4];
-#pragma unroll
-    for (int p = 0; p < NPAIR; ++p)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int x = 2 * p + c;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wv[p][c][rt] = x < NV ? wsol[NV + x][rt] : (f32x4){0.f, 0.f, 0.f, 0.f};
-      }
+      for (int x = 0; x < NV; ++x) store_wk<T, D, M::V>(smem, wk[x], cts[x], lane);
+    }
+    f32x4 wvt[NV][4];
+    w_products<T, D, NV>(smem, xv, cts, lane, wvt);
     __syncthreads();  // Wk complete
-    f32x4 unused[2][4];
+    unsigned char* cr = crec + ((size_t)blockIdx.x * L + (j - j0)) * H * CR::BYTES + (size_t)h * CR::BYTES;
+    save_record<T, D, NT, M::V>(smem, cr, tid);
 #pragma unroll
-    for (int p = 0; p < NPAIR; ++p) state_step<T, D, 2, false>(smem, X[p], wv[p], unused, lane);
+    for (int x = 0; x < NV; ++x)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) *(f32x4*)(cr + CR::wv(cts[x], rt, lane)) = wvt[x][rt];
     __syncthreads();  // done with this chunk's LDS
     if (j + 1 < j1) {
       raw.store(smem, tid);
       __syncthreads();
     }
   }
+}
 
-  // B tiles straight from the accumulators; M through LDS into the scan's
-  // A-operand fragments
-  typedef Rec<T, D> R;
-  float* rec = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS;
-  constexpr int LDM = D + 4;
-  float* sM = (float*)smem;  // [D][LDM] fp32, free after the last chunk
+// ---- pass 2: the affine map of every segment but the last ----------------
+// Waves 0 .. NH - 1 carry B (the state from zero, value part of U on), waves
+// NH .. 2 NH - 1 carry M (the state from I, value part off); within a half,
+// wave w owns the column tiles w + NH x.  Record images are double-buffered:
+// the next chunk's lands while the current one is used.
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(64 * NW)
+kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
+             const unsigned char* __restrict__ crec, float* __restrict__ ws) {
+  typedef CRec<T, D> CR;
+  typedef Img<T, D> I;
+  constexpr int NH = NW / 2, NR = D / 16, CT = NR / NH, LDM = D + 4;
+  static_assert(NW % 2 == 0 && CT >= 1 && CT * NH == NR, "each half of the waves splits the columns");
+  static_assert(D * LDM * 4 <= 2 * I::BYTES, "M staging fits the image buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
+  Seg sg;
+  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
+  if (sg.s == sg.nseg - 1) return;  // nothing downstream needs the last map
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
+  const bool is_m = wave >= NH;
+  const int hw = is_m ? wave - NH : wave;
+  const int idx = lane & 15, gq = lane >> 4;
+  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
+  auto rec = [&](int j) -> const unsigned char* {
+    return crec + ((size_t)blockIdx.x * L + (j - j0)) * H * CR::BYTES + (size_t)h * CR::BYTES;
+  };
+
+  f32x4 X[CT][NR];
 #pragma unroll
-  for (int p = 0; p < NPAIR; ++p)
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int tile = wave + NW * (2 * p + c);
+    for (int rr = 0; rr < NR; ++rr)
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr) {
-        if (2 * p + c < NX / 2) {
-          *(f32x4*)(rec + R::B + R::tile(rr, tile, lane)) = X[p][c][rr];
-        } else {
+      for (int i = 0; i < 4; ++i)
+        X[c][rr][i] = (is_m && 16 * rr + 4 * gq + i == 16 * (hw + NH * c) + idx) ? 1.f : 0.f;
+  auto load_wv = [&](int j, f32x4 (&w)[CT][4]) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sM[(16 * rr + 4 * gq + i) * LDM + 16 * (tile - NR) + idx] = X[p][c][rr][i];
-        }
-      }
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        w[c][rt] = is_m ? (f32x4){0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(rec(j) + CR::wv(hw + NH * c, rt, lane));
+  };
+
+  f32x4 wv[CT][4];
+  issue_image<T, D, NW>(smem, rec(j0), wave, lane);
+  load_wv(j0, wv);
+  for (int j = j0; j < j1; ++j) {
+    unsigned char* cur = smem + ((j - j0) & 1) * I::BYTES;
+    vmcnt_wait_all();
+    __syncthreads();  // image j in LDS; every wave is done with the other buffer
+    f32x4 wvn[CT][4];
+    if (j + 1 < j1) {
+      issue_image<T, D, NW>(smem + ((j + 1 - j0) & 1) * I::BYTES, rec(j + 1), wave, lane);
+      load_wv(j + 1, wvn);
     }
+    f32x4 unused[CT][4];
+    state_step<T, D, CT, false>(cur, X, wv, unused, lane);
+    if (j + 1 < j1) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wvn[c][rt];
+    }
+  }
+  __syncthreads();  // every wave is done with the images
+
+  typedef Rec<T, D> R;
+  float* recs = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS;
+  float* sM = (float*)smem;  // [D][LDM] fp32
+  if (!is_m) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) *(f32x4*)(recs + R::B + R::tile(rr, hw + NH * c, lane)) = X[c][rr];
+  } else {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sM[(16 * rr + 4 * gq + i) * LDM + 16 * (hw + NH * c) + idx] = X[c][rr][i];
+  }
   __syncthreads();
-  unsigned char* mf = (unsigned char*)(rec + R::M);
+  // M into the scan's A-operand fragments
+  unsigned char* mf = (unsigned char*)(recs + R::M);
   for (int f = wave; f < NR * R::NKB; f += NW) {
     const int rr = f / R::NKB, kb = f % R::NKB;
     const float* src = sM + (16 * rr + idx) * LDM + R::KB * kb + 4 * gq;
@@ -733,25 +905,42 @@ kda_seg_summary(const T* __restrict__ k, const T* __restrict__ v, const T* __res
   }
 }
 
-// ---- pass 3: outputs from every segment's incoming state -----------------
-// Wave w owns the D / 16 / NW value-column tiles w + NW x.
+// ---- pass 4: outputs from every segment's incoming state -----------------
+// Reads the chunk records, double-buffered like pass 2; wave w owns the
+// D / 16 / NW value-column tiles w + NW x.  O is staged in the current
+// image's Qt area (dead after the products) so that the global stores are
+// whole 16-byte pieces of rows.
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
-kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-                int n_rows, int T_per, int H, int L, float g_floor, const float* __restrict__ ws,
-                T* __restrict__ o, float* ht) {
+kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
+                const float* __restrict__ ws, const unsigned char* __restrict__ crec, T* __restrict__ o,
+                float* ht) {
   typedef Lds<T, D> M;
+  typedef CRec<T, D> CR;
+  typedef Img<T, D> I;
   constexpr int NT = 64 * NW, NR = D / 16, CT = NR / NW;
   static_assert(CT >= 1 && CT * NW == NR, "waves must split the value columns");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
+  static_assert(M::ROW_T <= I::WK, "O staging fits the Qt area");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
   const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
+  auto rec = [&](int j) -> const unsigned char* {
+    return crec + ((size_t)blockIdx.x * L + (j - j0)) * H * CR::BYTES + (size_t)h * CR::BYTES;
+  };
+  auto load_wv = [&](int j, f32x4 (&w)[CT][4]) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) w[c][rt] = *(const f32x4*)(rec(j) + CR::wv(wave + NW * c, rt, lane));
+  };
 
+  issue_image<T, D, NW>(smem, rec(j0), wave, lane);
+  f32x4 wv[CT][4];
+  load_wv(j0, wv);
   typedef Rec<T, D> R;
   const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS + R::SIN;
   f32x4 S[CT][NR];
@@ -760,46 +949,21 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) S[c][rr] = *(const f32x4*)(sin + R::tile(rr, wave + NW * c, lane));
 
-  {
-    Raw<T, D, NT, true> first;
-    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
-    first.store(smem, tid);
-  }
-  __syncthreads();
   for (int j = j0; j < j1; ++j) {
     const int clen = min(C, sg.len - C * j);
     const int64_t tokc = sg.tok0 + (int64_t)C * j;
-    elementwise<T, D, NW, true>(smem, g_floor, tid);
-    // the next chunk's inputs are fetched now and land in LDS at the end
-    Raw<T, D, NT, true> raw;
-    if (j + 1 < j1) raw.load(q, k, v, g, beta, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid);
-    gram<T, D, NW, true>(smem, wave, lane);
-    diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
-    Wy<T, D> wy;
-    wy.load(smem, lane);
-    const T* xt[2 * CT];
-    int cts[2 * CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      xt[c] = (const T*)(smem + M::KT);
-      xt[CT + c] = (const T*)(smem + M::VT);
-      cts[c] = cts[CT + c] = wave + NW * c;
+    unsigned char* cur = smem + ((j - j0) & 1) * I::BYTES;
+    vmcnt_wait_all();
+    __syncthreads();  // image j in LDS; every wave is done with the other buffer
+    f32x4 wvn[CT][4];
+    if (j + 1 < j1) {
+      issue_image<T, D, NW>(smem + ((j + 1 - j0) & 1) * I::BYTES, rec(j + 1), wave, lane);
+      load_wv(j + 1, wvn);
     }
-    f32x4 wsol[2 * CT][4];
-    wy.template solve<2 * CT>(smem, xt, cts, lane, wsol);
-    f32x4 wv[CT][4];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      store_wk<T, D>(smem, wsol[c], wave + NW * c, lane);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wsol[CT + c][rt];
-    }
-    __syncthreads();  // Wk complete
     f32x4 O[CT][4];
-    state_step<T, D, CT, true>(smem, S, wv, O, lane);
-    // O goes through LDS (the Kt^T area, dead since the W products) so that
-    // the global stores are whole 16-byte pieces of rows
-    T* sO = (T*)(smem + M::KT);
+    state_step<T, D, CT, true>(cur, S, wv, O, lane);
+    lds_barrier();  // every wave is done with Qt
+    T* sO = (T*)(cur + I::QT);
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -807,10 +971,14 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sO[(16 * rt + 4 * gq + i) * M::LDT + 16 * (wave + NW * c) + idx] = Elem<T>::from_f32(O[c][rt][i]);
-    __syncthreads();
-    Raw<T, D, NT, true>::store_out(smem + M::KT, o, tokc, clen, H, h, tid);
-    if (j + 1 < j1) raw.store(smem, tid);
-    __syncthreads();
+    lds_barrier();
+    Raw<T, D, NT, true>::store_out(cur + I::QT, o, tokc, clen, H, h, tid);
+    if (j + 1 < j1) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wvn[c][rt];
+    }
   }
   if (ht && sg.s == sg.nseg - 1) {
     float* dst = ht + ((size_t)sg.n * H + h) * D * D;
@@ -823,7 +991,7 @@ kda_seg_forward(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   }
 }
 
-// ---- pass 2: segment scan S_{s+1} = M_s S_s + B_s ------------------------
+// ---- pass 3: segment scan S_{s+1} = M_s S_s + B_s ------------------------
 // Workgroup = (sequence, head, 16 state columns); wave w owns the k-block w
 // (rows KB w .. KB w + KB - 1 of S), forms the partial products of all row
 // tiles over its k-block, and the partials are summed through LDS.
@@ -983,23 +1151,27 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
                  float* ht, void* ws, hipStream_t stream) {
   const int L = plan.seg_chunks;
   float* wsf = (float*)ws;
+  unsigned char* crec = (unsigned char*)ws + plan.crec_off;
+  if (plan.crec_bytes != CRec<T, D>::BYTES) return (int)hipErrorInvalidValue;
   const bool has_segments = plan.n_seg_bound > 0;
+  const dim3 segs((unsigned)plan.n_seg_bound, H);
+  hipError_t e;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_summary<T, D, NW>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0, stream,
-                       (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor, wsf);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW>), segs, dim3(64 * NW), 0, stream, (const T*)q, (const T*)k,
+                       (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor, crec);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    hipLaunchKernelGGL((kda_seg_maps<T, D, 2 * NW2>), segs, dim3(128 * NW2), 0, stream, cu, n_rows, T_per, H, L,
+                       (const unsigned char*)crec, wsf);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   const int64_t pairs = (int64_t)n_rows * H;
   const int64_t blocks = (pairs + 7) / 8 * 8 * (D / 16);
   hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / ScanOps<T, D>::KB)), 0, stream,
                      h0, ht, wsf, cu, n_rows, T_per, H, L);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_forward<T, D, NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2), 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor,
-                       (const float*)wsf, (T*)o, ht);
+    hipLaunchKernelGGL((kda_seg_forward<T, D, NW2>), segs, dim3(64 * NW2), 0, stream, cu, n_rows, T_per, H, L,
+                       (const float*)wsf, (const unsigned char*)crec, (T*)o, ht);
     e = hipGetLastError();
   }
   return (int)e;
