@@ -71,7 +71,7 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   if (!kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, &s->plan))
     return KDA_ERR_UNSUPPORTED;
-  if (s->plan.n_seg_bound > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (s->plan.n_seg_bound > (int64_t)INT32_MAX || s->plan.n_prep_bound > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 

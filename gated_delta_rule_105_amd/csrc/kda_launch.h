@@ -9,23 +9,29 @@ namespace kda {
 
 constexpr int kChunk = 64;  // tokens per chunk
 
-// How a chunked forward is cut for the GPU.  Every sequence is split into
-// segments of `seg_chunks` consecutive chunks.  The workspace holds
-//  - one record per (segment, head): three d x d fp32 matrices, the segment's
-//    affine state map S_out = M S_in + B (M and B) and its incoming state S_in;
-//  - one record per (chunk slot, head) with the chunk's operands for the
-//    output pass (slot = segment * seg_chunks + chunk within the segment).
+// How a chunked forward is cut for the GPU.
+//  - The chunk pass takes groups of `prep_chunks` consecutive chunks of a
+//    sequence, one workgroup per (group, head), and writes one record per
+//    (chunk, head) with the chunk's operands for the state passes.
+//  - The state passes cut every sequence into segments of `seg_chunks`
+//    chunks.  One record per (segment, head) holds three d x d fp32 matrices:
+//    the segment's affine state map S_out = M S_in + B (M and B) and its
+//    incoming state S_in.
+// Workspace: the segment records, then the chunk records.
 struct SegPlan {
-  int seg_chunks;        // chunks per segment
+  int prep_chunks;       // chunks per chunk-pass workgroup
+  int seg_chunks;        // chunks per segment of the state passes
+  int64_t n_prep_bound;  // upper bound of chunk-pass groups over all sequences
   int64_t n_seg_bound;   // upper bound of segments over all sequences
+  int64_t n_slots;       // upper bound of chunks over all sequences
   size_t rec_bytes;      // bytes of one (segment, head) record
-  size_t crec_bytes;     // bytes of one (chunk slot, head) record
+  size_t crec_bytes;     // bytes of one (chunk, head) record
   size_t crec_off;       // byte offset of the chunk records
-  size_t ws_bytes;       // crec_off + n_seg_bound * seg_chunks * H * crec_bytes
+  size_t ws_bytes;       // crec_off + n_slots * H * crec_bytes
 };
 
 // Bytes of one chunk record for key/value width d and operand size esz.  The
-// record starts with an image of the output pass's LDS: Qt and Wk as 64 rows
+// record starts with an image of the state passes' LDS: Qt and Wk as 64 rows
 // of d + 16 / esz elements, Kh^T as d rows and P as 64 rows of 64 + 16 / esz
 // elements (operand type), gamma (d fp32), padded to a multiple of 1 KiB;
 // then Wv, 64 x d fp32.
@@ -38,46 +44,61 @@ inline size_t chunk_record_bytes(int d, int esz) {
   return chunk_image_bytes(d, esz) + (size_t)kChunk * d * 4;
 }
 
-// Chooses the segment length from a cost model of the three launches:
-// longer segments mean fewer workgroups in the two chunk passes, shorter ones
-// a longer sequential chain in the segment scan.  Host-only, deterministic in
-// its arguments.  `packed`: n_rows sequences share T tokens (lengths unknown
-// on the host), else n_rows rows of T tokens each.  esz: operand bytes (2 for
-// bf16, 4 for fp32).  Returns false on overflow.
+// Upper bound of groups of g chunks over the sequences: n_rows rows of T
+// tokens, or (packed) n_rows sequences sharing T tokens.
+inline int64_t group_bound(int64_t T, int n_rows, bool packed, int64_t g) {
+  const int64_t chunks = (T + kChunk - 1) / kChunk;
+  if (T == 0) return 0;
+  if (packed) return (chunks + n_rows + g - 1) / g + n_rows;
+  return (int64_t)n_rows * ((chunks + g - 1) / g);
+}
+
+// Chooses the cut from a cost model of the launches (one workgroup per CU
+// in every pass; times per chunk and per scan step measured on the target):
+// longer segments mean fewer workgroups in the segment-map and output passes,
+// shorter ones a longer chain in the segment scan.  Host-only, deterministic
+// in its arguments.  `packed`: n_rows sequences share T tokens (lengths
+// unknown on the host; the mean length is used), else n_rows rows of T
+// tokens each.  esz: operand bytes (2 bf16, 4 fp32).  Returns false on
+// overflow.
 inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool packed, SegPlan* p) {
-  const double t_chunk = 3.0;   // us per chunk per workgroup (one workgroup per CU)
-  const double t_step = 0.5;    // us per step of the segment scan
+  const double t_map = 3.0, t_scan = 1.4, t_fwd = 4.7;  // us
   const int64_t n_cu = 256;
   const int64_t chunks_total = (T + kChunk - 1) / kChunk;
-  int64_t per_seq = packed ? (chunks_total + n_rows - 1) / (n_rows > 0 ? n_rows : 1) : chunks_total;
+  const int rows = n_rows > 0 ? n_rows : 1;
+  int64_t per_seq = packed ? (chunks_total + rows - 1) / rows : chunks_total;
   if (per_seq < 1) per_seq = 1;
   const int64_t pairs = (int64_t)n_rows * H;
+  auto rounds = [&](int64_t wg) { return (double)((wg + n_cu - 1) / n_cu); };
   double best = 1e300;
   int best_l = 1;
-  for (int L = 1; L <= 64; L *= 2) {
-    const int64_t segs = (per_seq + L - 1) / L;
-    const int64_t wg2 = pairs * segs, wg1 = pairs * (segs - 1);
-    const double t = (double)((wg1 + n_cu - 1) / n_cu + (wg2 + n_cu - 1) / n_cu) * L * t_chunk +
-                     (double)(segs - 1) * t_step;
-    if (t <= best) {
+  for (int64_t L = 1;; L *= 2) {
+    const int64_t Lc = L < per_seq ? L : per_seq;
+    const int64_t segs = (per_seq + Lc - 1) / Lc;
+    const double t = rounds(pairs * (segs - 1)) * Lc * t_map + (double)(segs - 1) * t_scan +
+                     rounds(pairs * segs) * Lc * t_fwd;
+    if (t < best) {
       best = t;
-      best_l = L;
+      best_l = (int)Lc;
     }
     if (L >= per_seq) break;
   }
-  p->seg_chunks = best_l;
-  if (T == 0) {
-    p->n_seg_bound = 0;
-  } else if (packed) {
-    p->n_seg_bound = (chunks_total + n_rows + best_l - 1) / best_l + n_rows;
-  } else {
-    p->n_seg_bound = (int64_t)n_rows * ((chunks_total + best_l - 1) / best_l);
-  }
+  // A packed batch cut into whole sequences (one segment each) needs the
+  // longest sequence to fit: use the bound of all chunks then.
+  p->seg_chunks = (packed && best_l >= per_seq) ? (int)(chunks_total > 0 ? chunks_total : 1) : best_l;
+  // chunk-pass groups: about one round of workgroups, 1 .. 64 chunks each
+  int64_t pg = 1;
+  while (pg < 64 && pairs * ((per_seq + 2 * pg - 1) / (2 * pg)) >= n_cu) pg *= 2;
+  p->prep_chunks = (int)pg;
+  p->n_prep_bound = group_bound(T, n_rows, packed, pg);
+  p->n_seg_bound = group_bound(T, n_rows, packed, p->seg_chunks);
+  p->n_slots = T == 0 ? 0 : (packed ? chunks_total + n_rows : (int64_t)n_rows * chunks_total);
   p->rec_bytes = (size_t)3 * d * d * sizeof(float);
   p->crec_bytes = chunk_record_bytes(d, esz);
-  if (p->n_seg_bound > ((int64_t)1 << 36) / (H > 0 ? H : 1)) return false;
+  const int64_t hh = H > 0 ? H : 1;
+  if (p->n_seg_bound > ((int64_t)1 << 36) / hh || p->n_slots > ((int64_t)1 << 36) / hh) return false;
   p->crec_off = (size_t)p->n_seg_bound * (size_t)H * p->rec_bytes;
-  p->ws_bytes = p->crec_off + (size_t)p->n_seg_bound * (size_t)best_l * (size_t)H * p->crec_bytes;
+  p->ws_bytes = p->crec_off + (size_t)p->n_slots * (size_t)H * p->crec_bytes;
   return true;
 }
 

@@ -85,11 +85,12 @@ template <typename T, int D> struct Lds {
 __device__ __forceinline__ int n_segments(int len, int L) { return ((len + C - 1) / C + L - 1) / L; }
 
 struct Seg {
-  int64_t tok0;  // first packed token of the sequence
-  int len;       // tokens of the sequence
-  int n;         // sequence
-  int s;         // segment within the sequence
-  int nseg;      // segments of the sequence
+  int64_t tok0;    // first packed token of the sequence
+  int64_t chunk0;  // chunks of all earlier sequences (first chunk-record slot)
+  int len;         // tokens of the sequence
+  int n;           // sequence
+  int s;           // segment within the sequence
+  int nseg;        // segments of the sequence
 };
 
 // Global segment gs -> its sequence.  false when gs is past the last one.
@@ -103,10 +104,11 @@ __device__ __forceinline__ bool locate(const int32_t* cu, int n_rows, int T, int
     r.s = (int)(gs % per);
     r.nseg = per;
     r.tok0 = n * (int64_t)T;
+    r.chunk0 = n * (int64_t)((T + C - 1) / C);
     r.len = T;
     return true;
   }
-  int64_t base = 0;
+  int64_t base = 0, chunks = 0;
   for (int n = 0; n < n_rows; ++n) {
     const int len = cu[n + 1] - cu[n];
     const int ns = n_segments(len, L);
@@ -115,10 +117,12 @@ __device__ __forceinline__ bool locate(const int32_t* cu, int n_rows, int T, int
       r.s = (int)(gs - base);
       r.nseg = ns;
       r.tok0 = cu[n];
+      r.chunk0 = chunks;
       r.len = len;
       return true;
     }
     base += ns;
+    chunks += (len + C - 1) / C;
   }
   return false;
 }
@@ -598,7 +602,7 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
 //   GAM [D]        gamma                (fp32)
 // padded to a multiple of 1 KiB, then
 //   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv (fp32), accumulator order.
-// Chunk c of global segment gs has slot gs * L + c.
+// Chunk j of sequence n has slot (chunks of sequences 0 .. n - 1) + j.
 template <typename T, int D> struct Img {
   typedef Lds<T, D> M;
   static constexpr int QT = 0, WK = QT + M::ROW_T, KH = WK + M::ROW_T, P = KH + D * M::LDC * (int)sizeof(T),
@@ -732,8 +736,10 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
 }
 
 // ---- pass 1: the chunk-local part of every chunk -> its record -----------
-// One workgroup per (segment, head) walks the segment's chunks; the inputs
-// of the next chunk are fetched while the current one is finished.  Wave w
+// One workgroup per (group of L consecutive chunks of a sequence, head)
+// walks its chunks; the inputs of the next chunk are fetched while the
+// current one is finished.  (L here is the chunk pass's own group length,
+// independent of the state passes' segments.)  Wave w
 // forms Wk and Wv for the value-column tiles w + NW x.
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
@@ -785,7 +791,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     f32x4 wvt[NV][4];
     w_products<T, D, NV>(smem, xv, cts, lane, wvt);
     __syncthreads();  // Wk complete
-    unsigned char* cr = crec + ((size_t)blockIdx.x * L + (j - j0)) * H * CR::BYTES + (size_t)h * CR::BYTES;
+    unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
     save_record<T, D, NT, M::V>(smem, cr, tid);
 #pragma unroll
     for (int x = 0; x < NV; ++x)
@@ -823,9 +829,7 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
   const int hw = is_m ? wave - NH : wave;
   const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
-  auto rec = [&](int j) -> const unsigned char* {
-    return crec + ((size_t)blockIdx.x * L + (j - j0)) * H * CR::BYTES + (size_t)h * CR::BYTES;
-  };
+  auto rec = [&](int j) -> const unsigned char* { return crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES; };
 
   f32x4 X[CT][NR];
 #pragma unroll
@@ -907,10 +911,10 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
 
 // ---- pass 4: outputs from every segment's incoming state -----------------
 // Reads the chunk records, double-buffered like pass 2; wave w owns the
-// D / 16 / NW value-column tiles w + NW x.  O is staged in the current
-// image's Qt area (dead after the products) so that the global stores are
-// whole 16-byte pieces of rows.
-template <typename T, int D, int NW>
+// value-column tiles w + NW x, x < CT.  O is staged in the current image's Qt
+// area (dead after the products) so that the global stores are whole 16-byte
+// pieces of rows.
+template <typename T, int D, int NW, int CT>
 __global__ void __launch_bounds__(64 * NW)
 kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
                 const float* __restrict__ ws, const unsigned char* __restrict__ crec, T* __restrict__ o,
@@ -918,8 +922,8 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
   typedef Lds<T, D> M;
   typedef CRec<T, D> CR;
   typedef Img<T, D> I;
-  constexpr int NT = 64 * NW, NR = D / 16, CT = NR / NW;
-  static_assert(CT >= 1 && CT * NW == NR, "waves must split the value columns");
+  constexpr int NT = 64 * NW, NR = D / 16;
+  static_assert(NW * CT == NR, "waves must split the value columns");
   static_assert(M::ROW_T <= I::WK, "O staging fits the Qt area");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
   Seg sg;
@@ -928,9 +932,7 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
   const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
-  auto rec = [&](int j) -> const unsigned char* {
-    return crec + ((size_t)blockIdx.x * L + (j - j0)) * H * CR::BYTES + (size_t)h * CR::BYTES;
-  };
+  auto rec = [&](int j) -> const unsigned char* { return crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES; };
   auto load_wv = [&](int j, f32x4 (&w)[CT][4]) {
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -987,7 +989,8 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx] = S[c][rr][i];
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx] = S[c][rr][i];
   }
 }
 
@@ -1149,19 +1152,20 @@ template <typename T, int D, int NW, int NW2>
 int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
                  const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
                  float* ht, void* ws, hipStream_t stream) {
+  constexpr int NR = D / 16;
   const int L = plan.seg_chunks;
   float* wsf = (float*)ws;
   unsigned char* crec = (unsigned char*)ws + plan.crec_off;
   if (plan.crec_bytes != CRec<T, D>::BYTES) return (int)hipErrorInvalidValue;
   const bool has_segments = plan.n_seg_bound > 0;
-  const dim3 segs((unsigned)plan.n_seg_bound, H);
   hipError_t e;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW>), segs, dim3(64 * NW), 0, stream, (const T*)q, (const T*)k,
-                       (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L, g_floor, crec);
+    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW>), dim3((unsigned)plan.n_prep_bound, H), dim3(64 * NW), 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H,
+                       plan.prep_chunks, g_floor, crec);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-    hipLaunchKernelGGL((kda_seg_maps<T, D, 2 * NW2>), segs, dim3(128 * NW2), 0, stream, cu, n_rows, T_per, H, L,
-                       (const unsigned char*)crec, wsf);
+    hipLaunchKernelGGL((kda_seg_maps<T, D, 2 * NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(128 * NW2), 0,
+                       stream, cu, n_rows, T_per, H, L, (const unsigned char*)crec, wsf);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   const int64_t pairs = (int64_t)n_rows * H;
@@ -1170,8 +1174,8 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
                      h0, ht, wsf, cu, n_rows, T_per, H, L);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_forward<T, D, NW2>), segs, dim3(64 * NW2), 0, stream, cu, n_rows, T_per, H, L,
-                       (const float*)wsf, (const unsigned char*)crec, (T*)o, ht);
+    hipLaunchKernelGGL((kda_seg_forward<T, D, NW2, NR / NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2),
+                       0, stream, cu, n_rows, T_per, H, L, (const float*)wsf, (const unsigned char*)crec, (T*)o, ht);
     e = hipGetLastError();
   }
   return (int)e;
