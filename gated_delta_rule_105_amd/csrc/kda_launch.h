@@ -31,14 +31,15 @@ struct SegPlan {
 };
 
 // Bytes of one chunk record for key/value width d and operand size esz.  The
-// record starts with an image of the state passes' LDS: Qt and Wk as 64 rows
-// of d + 16 / esz elements, Kh^T as d rows and P as 64 rows of 64 + 16 / esz
-// elements (operand type), gamma (d fp32), padded to a multiple of 1 KiB;
-// then Wv, 64 x d fp32.
+// record starts with an image of the state passes' LDS: the MFMA A-operand
+// fragments (1 KiB each, k-blocks of KB = 32 for bf16 and 16 for fp32) of
+// Qt and Wk (4 row tiles x d / KB), Kh^T (d / 16 row tiles x 64 / KB) and P
+// (4 x 64 / KB), then gamma (d fp32), padded to a multiple of 1 KiB; then
+// Wv, 64 x d fp32.
 inline size_t chunk_image_bytes(int d, int esz) {
-  const size_t ldt = (size_t)d + 16 / esz, ldc = (size_t)kChunk + 16 / esz;
-  const size_t img = (2 * kChunk * ldt + (size_t)d * ldc + kChunk * ldc) * esz + (size_t)d * 4;
-  return (img + 1023) / 1024 * 1024;
+  const size_t kb = esz == 2 ? 32 : 16;
+  const size_t frags = 8 * (d / kb) + (size_t)(d / 16) * (kChunk / kb) + 4 * (kChunk / kb);
+  return (frags * 1024 + (size_t)d * 4 + 1023) / 1024 * 1024;
 }
 inline size_t chunk_record_bytes(int d, int esz) {
   return chunk_image_bytes(d, esz) + (size_t)kChunk * d * 4;

@@ -593,20 +593,26 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
 }
 
 // ---- chunk record: what the chunk pass leaves for the two state passes,
-// per (chunk slot, head), in device memory.  It starts with an image of the
-// state passes' LDS (Img), copied linearly in 16-byte pieces:
-//   QT  [64][LDT]  Qt rows              (operand type)
-//   WK  [64][LDT]  Wk rows              (operand type)
-//   KH  [D][LDC]   Kh^T, channel-major  (operand type)
-//   P   [64][LDC]  P                    (operand type)
-//   GAM [D]        gamma                (fp32)
+// per (chunk, head), in device memory.  It starts with an image of the state
+// passes' LDS (Img), copied linearly: the A-operand fragments of the state
+// products, each 64 lanes x 16 bytes in lane order (one 16-byte LDS read per
+// lane and fragment):
+//   QF  Qt rows       [4 row tiles][D / KB k-blocks]
+//   WF  Wk rows       [4 row tiles][D / KB k-blocks]
+//   KF  Kh^T rows     [D / 16 row tiles][64 / KB k-blocks]
+//   PF  P rows        [4 row tiles][64 / KB k-blocks]
+//   GAM gamma         [D] fp32
 // padded to a multiple of 1 KiB, then
 //   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv (fp32), accumulator order.
 // Chunk j of sequence n has slot (chunks of sequences 0 .. n - 1) + j.
 template <typename T, int D> struct Img {
-  typedef Lds<T, D> M;
-  static constexpr int QT = 0, WK = QT + M::ROW_T, KH = WK + M::ROW_T, P = KH + D * M::LDC * (int)sizeof(T),
-                       GAM = P + C * M::LDC * (int)sizeof(T), END = GAM + D * 4, BYTES = (END + 1023) / 1024 * 1024;
+  static constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
+  static constexpr int QF = 0, WF = QF + 4 * NKD * 1024, KF = WF + 4 * NKD * 1024, PF = KF + NR * NKC * 1024,
+                       GAM = PF + 4 * NKC * 1024, END = GAM + D * 4, BYTES = (END + 1023) / 1024 * 1024;
+  __device__ static __forceinline__ int q(int rt, int kb, int lane) { return QF + ((rt * NKD + kb) * 64 + lane) * 16; }
+  __device__ static __forceinline__ int w(int rt, int kb, int lane) { return WF + ((rt * NKD + kb) * 64 + lane) * 16; }
+  __device__ static __forceinline__ int k(int rr, int kb, int lane) { return KF + ((rr * NKC + kb) * 64 + lane) * 16; }
+  __device__ static __forceinline__ int p(int rt, int kb, int lane) { return PF + ((rt * NKC + kb) * 64 + lane) * 16; }
 };
 template <typename T, int D> struct CRec {
   static constexpr size_t WV = Img<T, D>::BYTES, BYTES = WV + (size_t)C * D * 4;
@@ -615,27 +621,42 @@ template <typename T, int D> struct CRec {
   }
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// LDS [src, src + bytes) -> device memory, 16-byte pieces over NT threads
-template <int NT, int BYTES>
-__device__ __forceinline__ void copy_out(const unsigned char* src, unsigned char* dst, int tid) {
-  static_assert(BYTES % 16 == 0, "16-byte pieces");
-#pragma unroll
-  for (int i = tid; i < BYTES / 16; i += NT) *(u32x4*)(dst + 16 * i) = *(const u32x4*)(src + 16 * i);
-}
-
 // The chunk's record from the chunk pass's LDS (Qt in Q, Wk in WKA, Kh^T in
-// KH, P in P, gamma in GL) and Wv tiles held by the waves.
-template <typename T, int D, int NT, int WKA>
-__device__ __forceinline__ void save_record(const unsigned char* smem, unsigned char* rec, int tid) {
+// KH, P in P, gamma in GL): wave w writes the fragments w, w + NW, ...
+template <typename T, int D, int NW, int WKA>
+__device__ __forceinline__ void save_record(const unsigned char* smem, unsigned char* rec, int wave, int lane) {
   typedef Lds<T, D> M;
   typedef Img<T, D> I;
-  copy_out<NT, I::WK - I::QT>(smem + M::Q, rec + I::QT, tid);
-  copy_out<NT, I::KH - I::WK>(smem + WKA, rec + I::WK, tid);
-  copy_out<NT, I::P - I::KH>(smem + M::KH, rec + I::KH, tid);
-  copy_out<NT, I::GAM - I::P>(smem + M::P, rec + I::P, tid);
-  copy_out<NT, I::END - I::GAM>(smem + M::GL, rec + I::GAM, tid);
+  typedef typename Frag<T>::type FragT;
+  constexpr int KB = I::KB, NQ = 4 * I::NKD, NK = I::NR * I::NKC, NP = 4 * I::NKC, NF = 2 * NQ + NK + NP;
+  const int idx = lane & 15, gq = lane >> 4;
+  const T* sQ = (const T*)(smem + M::Q);
+  const T* sW = (const T*)(smem + WKA);
+  const T* sKH = (const T*)(smem + M::KH);
+  const T* sP = (const T*)(smem + M::P);
+  for (int f = wave; f < NF; f += NW) {
+    FragT x;
+    int off;
+    if (f < NQ) {
+      const int rt = f / I::NKD, kb = f % I::NKD;
+      x = frag_rows(sQ, M::LDT, 16 * rt + idx, kb * KB, gq);
+      off = I::q(rt, kb, lane);
+    } else if (f < 2 * NQ) {
+      const int rt = (f - NQ) / I::NKD, kb = (f - NQ) % I::NKD;
+      x = frag_rows(sW, M::LDT, 16 * rt + idx, kb * KB, gq);
+      off = I::w(rt, kb, lane);
+    } else if (f < 2 * NQ + NK) {
+      const int rr = (f - 2 * NQ) / I::NKC, kb = (f - 2 * NQ) % I::NKC;
+      x = frag_rows(sKH, M::LDC, 16 * rr + idx, kb * KB, gq);
+      off = I::k(rr, kb, lane);
+    } else {
+      const int rt = (f - 2 * NQ - NK) / I::NKC, kb = (f - 2 * NQ - NK) % I::NKC;
+      x = frag_rows(sP, M::LDC, 16 * rt + idx, kb * KB, gq);
+      off = I::p(rt, kb, lane);
+    }
+    *(FragT*)(rec + off) = x;
+  }
+  if (wave == 0 && lane < D / 4) *(f32x4*)(rec + I::GAM + 16 * lane) = *(const f32x4*)(smem + M::GL + 16 * lane);
 }
 
 // Record image -> LDS `dst` by direct global-to-LDS loads (lane i of a wave
@@ -657,45 +678,43 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // CT column tiles of the state (rows = D key channels) through one chunk:
 // U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
-// O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  The operands are
-// read from a record image in LDS at `img`.  Every A-operand fragment feeds the CT
-// tiles.
+// O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  The A operands
+// are fragments of a record image in LDS at `img`, each loaded once per
+// phase and fed to the CT tiles.
 template <typename T, int D, int CT, bool WITH_O>
 __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[CT][D / 16],
                                            const f32x4 (&wv)[CT][4], f32x4 (&O)[CT][4], int lane) {
-  typedef Lds<T, D> M;
   typedef Img<T, D> I;
   typedef typename Frag<T>::type FragT;
-  constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, LDT = M::LDT, LDC = M::LDC;
-  const T* sQ = (const T*)(img + I::QT);
-  const T* sW = (const T*)(img + I::WK);
-  const T* sP = (const T*)(img + I::P);
-  const T* sKH = (const T*)(img + I::KH);
-  const float* sGL = (const float*)(img + I::GAM);
-  const int idx = lane & 15, gq = lane >> 4;
+  constexpr int KB = I::KB, NKD = I::NKD, NKC = I::NKC, NR = I::NR;
+  const int gq = lane >> 4;
+  auto frag = [&](int off) { return *(const FragT*)(img + off); };
 
   FragT SB[CT][NKD];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) SB[c][kb] = Frag<T>::from_acc(S[c], kb);
+  // U and Qt S
   f32x4 U[CT][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
+    FragT aw[NKD], aq[NKD];
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      aw[kb] = frag(I::w(rt, kb, lane));
+      if (WITH_O) aq[kb] = frag(I::q(rt, kb, lane));
+    }
     f32x4 ws[CT], qs[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) ws[c] = qs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-      const FragT aw = frag_rows(sW, LDT, 16 * rt + idx, kb * KB, gq);
+    for (int kb = 0; kb < NKD; ++kb)
 #pragma unroll
-      for (int c = 0; c < CT; ++c) ws[c] = mma(aw, SB[c][kb], ws[c]);
-      if (WITH_O) {
-        const FragT aq = frag_rows(sQ, LDT, 16 * rt + idx, kb * KB, gq);
-#pragma unroll
-        for (int c = 0; c < CT; ++c) qs[c] = mma(aq, SB[c][kb], qs[c]);
+      for (int c = 0; c < CT; ++c) {
+        ws[c] = mma(aw[kb], SB[c][kb], ws[c]);
+        if (WITH_O) qs[c] = mma(aq[kb], SB[c][kb], qs[c]);
       }
-    }
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
 #pragma unroll
@@ -710,24 +729,30 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
     for (int kb = 0; kb < NKC; ++kb) UB[c][kb] = Frag<T>::from_acc(U[c], kb);
   if (WITH_O) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+      FragT ap[NKC];
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb)
+        if (kb * KB <= 16 * rt + 15) ap[kb] = frag(I::p(rt, kb, lane));
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
         if (kb * KB <= 16 * rt + 15) {
-          const FragT ap = frag_rows(sP, LDC, 16 * rt + idx, kb * KB, gq);
 #pragma unroll
-          for (int c = 0; c < CT; ++c) O[c][rt] = mma(ap, UB[c][kb], O[c][rt]);
+          for (int c = 0; c < CT; ++c) O[c][rt] = mma(ap[kb], UB[c][kb], O[c][rt]);
         }
-  }
-#pragma unroll
-  for (int rr = 0; rr < D / 16; ++rr) {
-#pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      const FragT ak = frag_rows(sKH, LDC, 16 * rr + idx, kb * KB, gq);
-#pragma unroll
-      for (int c = 0; c < CT; ++c) S[c][rr] = mma(ak, UB[c][kb], S[c][rr]);
     }
+  }
+  const float* sGL = (const float*)(img + I::GAM);
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    FragT ak[NKC];
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) ak[kb] = frag(I::k(rr, kb, lane));
     const f32x4 gm = *(const f32x4*)(sGL + 16 * rr + 4 * gq);
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) S[c][rr] = mma(ak[kb], UB[c][kb], S[c][rr]);
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -792,7 +817,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     w_products<T, D, NV>(smem, xv, cts, lane, wvt);
     __syncthreads();  // Wk complete
     unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
-    save_record<T, D, NT, M::V>(smem, cr, tid);
+    save_record<T, D, NW, M::V>(smem, cr, wave, lane);
 #pragma unroll
     for (int x = 0; x < NV; ++x)
 #pragma unroll
@@ -911,9 +936,9 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
 
 // ---- pass 4: outputs from every segment's incoming state -----------------
 // Reads the chunk records, double-buffered like pass 2; wave w owns the
-// value-column tiles w + NW x, x < CT.  O is staged in the current image's Qt
-// area (dead after the products) so that the global stores are whole 16-byte
-// pieces of rows.
+// value-column tiles w + NW x, x < CT.  O is staged at the start of the
+// current image (Qt and Wk fragments, dead after the products) so that the
+// global stores are whole 16-byte pieces of rows.
 template <typename T, int D, int NW, int CT>
 __global__ void __launch_bounds__(64 * NW)
 kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
@@ -924,7 +949,7 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
   typedef Img<T, D> I;
   constexpr int NT = 64 * NW, NR = D / 16;
   static_assert(NW * CT == NR, "waves must split the value columns");
-  static_assert(M::ROW_T <= I::WK, "O staging fits the Qt area");
+  static_assert(M::ROW_T <= I::KF, "O staging fits the Qt and Wk fragments");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
@@ -964,8 +989,8 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
     }
     f32x4 O[CT][4];
     state_step<T, D, CT, true>(cur, S, wv, O, lane);
-    lds_barrier();  // every wave is done with Qt
-    T* sO = (T*)(cur + I::QT);
+    lds_barrier();  // every wave is done with the Qt and Wk fragments
+    T* sO = (T*)cur;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -974,7 +999,7 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
         for (int i = 0; i < 4; ++i)
           sO[(16 * rt + 4 * gq + i) * M::LDT + 16 * (wave + NW * c) + idx] = Elem<T>::from_f32(O[c][rt][i]);
     lds_barrier();
-    Raw<T, D, NT, true>::store_out(cur + I::QT, o, tokc, clen, H, h, tid);
+    Raw<T, D, NT, true>::store_out(cur, o, tokc, clen, H, h, tid);
     if (j + 1 < j1) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
