@@ -597,18 +597,19 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
 // passes' LDS (Img), copied linearly: the A-operand fragments of the state
 // products, each 64 lanes x 16 bytes in lane order (one 16-byte LDS read per
 // lane and fragment):
-//   QF  Qt rows       [4 row tiles][D / KB k-blocks]
 //   WF  Wk rows       [4 row tiles][D / KB k-blocks]
 //   KF  Kh^T rows     [D / 16 row tiles][64 / KB k-blocks]
+//   GAM gamma         [D] fp32, padded to 1 KiB
+//   QF  Qt rows       [4 row tiles][D / KB k-blocks]
 //   PF  P rows        [4 row tiles][64 / KB k-blocks]
-//   GAM gamma         [D] fp32
-// padded to a multiple of 1 KiB, then
+// (the segment-map pass needs only the part before QF), then
 //   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv (fp32), accumulator order.
 // Chunk j of sequence n has slot (chunks of sequences 0 .. n - 1) + j.
 template <typename T, int D> struct Img {
   static constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
-  static constexpr int QF = 0, WF = QF + 4 * NKD * 1024, KF = WF + 4 * NKD * 1024, PF = KF + NR * NKC * 1024,
-                       GAM = PF + 4 * NKC * 1024, END = GAM + D * 4, BYTES = (END + 1023) / 1024 * 1024;
+  static constexpr int WF = 0, KF = WF + 4 * NKD * 1024, GAM = KF + NR * NKC * 1024,
+                       QF = GAM + (D * 4 + 1023) / 1024 * 1024, PF = QF + 4 * NKD * 1024, BYTES = PF + 4 * NKC * 1024,
+                       MAP_BYTES = QF;
   __device__ static __forceinline__ int q(int rt, int kb, int lane) { return QF + ((rt * NKD + kb) * 64 + lane) * 16; }
   __device__ static __forceinline__ int w(int rt, int kb, int lane) { return WF + ((rt * NKD + kb) * 64 + lane) * 16; }
   __device__ static __forceinline__ int k(int rr, int kb, int lane) { return KF + ((rr * NKC + kb) * 64 + lane) * 16; }
@@ -659,15 +660,23 @@ __device__ __forceinline__ void save_record(const unsigned char* smem, unsigned 
   if (wave == 0 && lane < D / 4) *(f32x4*)(rec + I::GAM + 16 * lane) = *(const f32x4*)(smem + M::GL + 16 * lane);
 }
 
-// Record image -> LDS `dst` by direct global-to-LDS loads (lane i of a wave
-// fills bytes 16 i .. 16 i + 15 of a 1 KiB block; no registers held).  The
-// loads are only issued: vmcnt_wait_all() and a barrier make them visible.
-template <typename T, int D, int NW>
-__device__ __forceinline__ void issue_image(unsigned char* dst, const unsigned char* rec, int wave, int lane) {
-  constexpr int NB = Img<T, D>::BYTES / 1024;
-  for (int b = wave; b < NB; b += NW)
+// Record image bytes [0, NBYTES) -> LDS `dst` by direct global-to-LDS loads
+// (lane i of a wave fills bytes 16 i .. 16 i + 15 of a 1 KiB block; no
+// registers held).  Wave w takes blocks w, w + NW, ...; part k of NPARTS
+// issues the k-th slice of them, so that the issue can be spread over other
+// work.  The loads are only issued: vmcnt_wait_all() and a barrier make them
+// visible.
+template <int NW, int NBYTES, int NPARTS>
+__device__ __forceinline__ void issue_image(unsigned char* dst, const unsigned char* rec, int wave, int lane, int k) {
+  constexpr int NB = NBYTES / 1024;
+  static_assert(NBYTES % 1024 == 0, "whole blocks");
+  const int nbw = (NB - wave + NW - 1) / NW;  // blocks of this wave
+  const int i0 = k * nbw / NPARTS, i1 = (k + 1) * nbw / NPARTS;
+  for (int i = i0; i < i1; ++i) {
+    const int b = wave + NW * i;
     __builtin_amdgcn_global_load_lds((const void*)(rec + 1024 * b + 16 * lane),
                                      (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16, 0, 0);
+  }
 }
 __device__ __forceinline__ void vmcnt_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 // Workgroup barrier that orders LDS reads and writes only: it waits for this
@@ -680,10 +689,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
 // O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  The A operands
 // are fragments of a record image in LDS at `img`, each loaded once per
-// phase and fed to the CT tiles.
-template <typename T, int D, int CT, bool WITH_O>
+// phase and fed to the CT tiles.  hook(k), k = 0 .. 4 + D / 16 - 1, is called
+// between the row blocks (the callers spread the next image's loads there).
+template <typename T, int D, int CT, bool WITH_O, typename Hook>
 __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[CT][D / 16],
-                                           const f32x4 (&wv)[CT][4], f32x4 (&O)[CT][4], int lane) {
+                                           const f32x4 (&wv)[CT][4], f32x4 (&O)[CT][4], int lane, Hook&& hook) {
   typedef Img<T, D> I;
   typedef typename Frag<T>::type FragT;
   constexpr int KB = I::KB, NKD = I::NKD, NKC = I::NKC, NR = I::NR;
@@ -721,6 +731,7 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
       for (int i = 0; i < 4; ++i) U[c][rt][i] = wv[c][rt][i] - ws[c][i];
       O[c][rt] = qs[c];
     }
+    hook(rt);
   }
   FragT UB[CT][NKC];
 #pragma unroll
@@ -757,6 +768,7 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[c][rr][i] *= gm[i];
+    hook(4 + rr);
   }
 }
 
@@ -833,8 +845,9 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
 // ---- pass 2: the affine map of every segment but the last ----------------
 // Waves 0 .. NH - 1 carry B (the state from zero, value part of U on), waves
 // NH .. 2 NH - 1 carry M (the state from I, value part off); within a half,
-// wave w owns the column tiles w + NH x.  Record images are double-buffered:
-// the next chunk's lands while the current one is used.
+// wave w owns the column tiles w + NH x.  The part of the record images this
+// pass needs (Wk, Kh^T, gamma) is double-buffered: the next chunk's is issued
+// piecewise between the row blocks of the state step.
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
 kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
@@ -843,8 +856,8 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
   typedef Img<T, D> I;
   constexpr int NH = NW / 2, NR = D / 16, CT = NR / NH, LDM = D + 4;
   static_assert(NW % 2 == 0 && CT >= 1 && CT * NH == NR, "each half of the waves splits the columns");
-  static_assert(D * LDM * 4 <= 2 * I::BYTES, "M staging fits the image buffers");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
+  static_assert(D * LDM * 4 <= 2 * I::MAP_BYTES, "M staging fits the image buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::MAP_BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
   if (sg.s == sg.nseg - 1) return;  // nothing downstream needs the last map
@@ -872,20 +885,22 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
         w[c][rt] = is_m ? (f32x4){0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(rec(j) + CR::wv(hw + NH * c, rt, lane));
   };
 
+  constexpr int NP = 4 + NR, IB = I::MAP_BYTES;  // hook points of a state step; bytes of the image used here
   f32x4 wv[CT][4];
-  issue_image<T, D, NW>(smem, rec(j0), wave, lane);
+  for (int k = 0; k < NP; ++k) issue_image<NW, IB, NP>(smem, rec(j0), wave, lane, k);
   load_wv(j0, wv);
   for (int j = j0; j < j1; ++j) {
-    unsigned char* cur = smem + ((j - j0) & 1) * I::BYTES;
+    unsigned char* cur = smem + ((j - j0) & 1) * IB;
+    unsigned char* nxt = smem + ((j + 1 - j0) & 1) * IB;
     vmcnt_wait_all();
     __syncthreads();  // image j in LDS; every wave is done with the other buffer
     f32x4 wvn[CT][4];
-    if (j + 1 < j1) {
-      issue_image<T, D, NW>(smem + ((j + 1 - j0) & 1) * I::BYTES, rec(j + 1), wave, lane);
-      load_wv(j + 1, wvn);
-    }
+    const bool more = j + 1 < j1;
+    if (more) load_wv(j + 1, wvn);
     f32x4 unused[CT][4];
-    state_step<T, D, CT, false>(cur, X, wv, unused, lane);
+    state_step<T, D, CT, false>(cur, X, wv, unused, lane, [&](int k) {
+      if (more) issue_image<NW, IB, NP>(nxt, rec(j + 1), wave, lane, k);
+    });
     if (j + 1 < j1) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
@@ -937,8 +952,9 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
 // ---- pass 4: outputs from every segment's incoming state -----------------
 // Reads the chunk records, double-buffered like pass 2; wave w owns the
 // value-column tiles w + NW x, x < CT.  O is staged at the start of the
-// current image (Qt and Wk fragments, dead after the products) so that the
-// global stores are whole 16-byte pieces of rows.
+// current image (Wk and Kh^T fragments, dead after the products) so that the
+// global stores are whole 16-byte pieces of rows.  The next chunk's image is
+// issued piecewise between the row blocks of the state step.
 template <typename T, int D, int NW, int CT>
 __global__ void __launch_bounds__(64 * NW)
 kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
@@ -949,7 +965,7 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
   typedef Img<T, D> I;
   constexpr int NT = 64 * NW, NR = D / 16;
   static_assert(NW * CT == NR, "waves must split the value columns");
-  static_assert(M::ROW_T <= I::KF, "O staging fits the Qt and Wk fragments");
+  static_assert(M::ROW_T <= I::GAM, "O staging fits the Wk and Kh^T fragments");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
   Seg sg;
   if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
@@ -965,7 +981,8 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
       for (int rt = 0; rt < 4; ++rt) w[c][rt] = *(const f32x4*)(rec(j) + CR::wv(wave + NW * c, rt, lane));
   };
 
-  issue_image<T, D, NW>(smem, rec(j0), wave, lane);
+  constexpr int NP = 4 + NR;  // hook points of a state step
+  for (int k = 0; k < NP; ++k) issue_image<NW, I::BYTES, NP>(smem, rec(j0), wave, lane, k);
   f32x4 wv[CT][4];
   load_wv(j0, wv);
   typedef Rec<T, D> R;
@@ -980,16 +997,17 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
     const int clen = min(C, sg.len - C * j);
     const int64_t tokc = sg.tok0 + (int64_t)C * j;
     unsigned char* cur = smem + ((j - j0) & 1) * I::BYTES;
+    unsigned char* nxt = smem + ((j + 1 - j0) & 1) * I::BYTES;
     vmcnt_wait_all();
     __syncthreads();  // image j in LDS; every wave is done with the other buffer
     f32x4 wvn[CT][4];
-    if (j + 1 < j1) {
-      issue_image<T, D, NW>(smem + ((j + 1 - j0) & 1) * I::BYTES, rec(j + 1), wave, lane);
-      load_wv(j + 1, wvn);
-    }
+    const bool more = j + 1 < j1;
+    if (more) load_wv(j + 1, wvn);
     f32x4 O[CT][4];
-    state_step<T, D, CT, true>(cur, S, wv, O, lane);
-    lds_barrier();  // every wave is done with the Qt and Wk fragments
+    state_step<T, D, CT, true>(cur, S, wv, O, lane, [&](int k) {
+      if (more) issue_image<NW, I::BYTES, NP>(nxt, rec(j + 1), wave, lane, k);
+    });
+    lds_barrier();  // every wave is done with the Wk and Kh^T fragments
     T* sO = (T*)cur;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -1158,17 +1176,22 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
     __syncthreads();
   };
   const int nsteps = nseg - 1;
+  if (nsteps == 0) return;
+  // Fetches past the last step re-read the last step's record (in bounds,
+  // unused): unconditional loads keep the wait counts exact, so a step waits
+  // only for its own stage and never for the fetches issued after it.
+  auto clamp = [&](int s) { return s < nsteps ? s : nsteps - 1; };
   Stage b0, b1, b2;
-  if (nsteps > 0) fetch(0, b0);
-  if (nsteps > 1) fetch(1, b1);
+  fetch(0, b0);
+  fetch(clamp(1), b1);
   for (int s = 0; s < nsteps; s += 3) {
-    if (s + 2 < nsteps) fetch(s + 2, b2);
+    fetch(clamp(s + 2), b2);
     step(s, b0);
     if (s + 1 >= nsteps) break;
-    if (s + 3 < nsteps) fetch(s + 3, b0);
+    fetch(clamp(s + 3), b0);
     step(s + 1, b1);
     if (s + 2 >= nsteps) break;
-    if (s + 4 < nsteps) fetch(s + 4, b1);
+    fetch(clamp(s + 4), b1);
     step(s + 2, b2);
   }
 }
