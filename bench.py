@@ -14,9 +14,11 @@ The prefill inputs are replicated over enough distinct buffer sets that their
 total exceeds the 256 MB last-level cache several times; consecutive steps
 cycle through them, so each step reads its inputs from HBM, not from cache.
 
-Prints ONE JSON line.  ``roofline`` describes the dominant kernel work, the
-chunked forward call, against HBM: algorithmic bytes per call divided by the
-call's mean duration from HIP events recorded on the launch stream.
+Prints ONE JSON line.  ``roofline`` describes the dominant launch of the
+chunked forward (the one with the largest mean duration, from HIP events
+recorded on the launch stream between the call's launches): its share of the
+algorithmic bytes (``LAUNCH_WORK``) divided by its mean duration, against HBM;
+``call_roofline`` and ``mfma`` do the same for the whole call.
 ``cpu_baseline`` times the fp64 CPU oracle on the host cores (a baseline, not
 a target).  ``other_workloads`` times the packed 8-sequence batch and the
 1,048,576-token context.  Other legs: ``--copy-calib MiB`` runs only a device copy of known
@@ -52,6 +54,20 @@ FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 128 * 63 // 2 + 4 * 128 * 65 // 2 + 6
 # bf16 q, k, v, g read + bf16 o written (2 B x 128 each) + fp32 beta
 BYTES_PER_TOKEN_HEAD = 5 * 2 * 128 + 4
 STATE_BYTES = 128 * 128 * 4    # one fp32 state matrix (h0 read, ht written)
+
+# The same work split over the call's launches (per token and head).  The
+# chunk pass reads every input and does the chunk-local products (key Gram,
+# P, Wk, Wv, the inverse); the output pass does the state products and P U
+# and writes o (plus h0 read / ht written per sequence and head).  The
+# segment maps and the scan are extra work of the segment decomposition, with
+# no share of the algorithmic figures.
+LAUNCH_WORK = {
+    "kda_chunk_prep": dict(bytes=4 * 2 * 128 + 4,
+                           flop=2 * (128 * 63 // 2 + 3 * 128 * 65 // 2 + 63 * 62 // 6)),
+    "kda_seg_maps": dict(bytes=0, flop=0),
+    "kda_seg_scan": dict(bytes=0, flop=0),
+    "kda_seg_forward": dict(bytes=2 * 128, flop=2 * (3 * 128 * 128 + 128 * 65 // 2)),
+}
 
 PREFILL = dict(B=1, T=4096, H=16, d=128, wid=1)
 DECODE = dict(N=256, H=32, d=128, wid=4)
@@ -133,14 +149,15 @@ def bench_prefill(steps: int, warmup: int):
     ws = torch.empty(kda.workspace_bytes(B, T, H, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def call(s):
+    def call(s, events=None):
         kda.chunk_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], h0=s["h0"], o=s["o"], ht=s["ht"],
-                          workspace=ws)
+                          workspace=ws, events=events)
 
     log(f"prefill warmup {warmup} over {n_sets} buffer sets of {set_bytes / 1e6:.1f} MB")
     for i in range(warmup):
         call(sets[i % n_sets])
     torch.cuda.synchronize()
+    # timed region 1: plain calls, an event pair around each (throughput)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -151,12 +168,28 @@ def bench_prefill(steps: int, warmup: int):
     wall = time.perf_counter() - t0
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
     mean_call = sum(durs) / len(durs)
-    log(f"prefill {steps} calls: wall {wall * 1e3:.3f} ms, mean call {mean_call * 1e6:.2f} us")
+    # timed region 2: the same calls through kda_chunk_forward_timed, which
+    # records HIP events on the launch stream before each launch and after
+    # the last (per-launch durations; the events add a little to each)
+    n_ev = len(kda.CHUNK_LAUNCHES) + 1
+    evl = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for row in evl:
+        for e in row:
+            e.record(stream)  # creates the event
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in evl]
+    for i in range(steps):
+        call(sets[i % n_sets], handles[i])
+    torch.cuda.synchronize()
+    launch = {name: sum(row[j].elapsed_time(row[j + 1]) for row in evl) / steps * 1e-3
+              for j, name in enumerate(kda.CHUNK_LAUNCHES)}
+    log(f"prefill {steps} calls: wall {wall * 1e3:.3f} ms, mean call {mean_call * 1e6:.2f} us; per launch "
+        + ", ".join(f"{n} {t * 1e6:.2f} us" for n, t in launch.items()))
     token_heads = B * T * H
     bytes_call = token_heads * BYTES_PER_TOKEN_HEAD + 2 * B * H * STATE_BYTES
     flop_call = token_heads * FLOP_PER_TOKEN_HEAD
-    return dict(wall=wall, mean_call=mean_call, min_call=min(durs), tokens=B * T,
-                bytes_call=bytes_call, flop_call=flop_call, n_sets=n_sets)
+    return dict(wall=wall, mean_call=mean_call, min_call=min(durs), tokens=B * T, token_heads=token_heads,
+                bytes_call=bytes_call, flop_call=flop_call, n_sets=n_sets, launch=launch)
 
 
 def bench_workload(wid: int, calls: int):
@@ -279,13 +312,26 @@ def main() -> int:
         p = bench_prefill(args.steps, args.warmup)
         out["ms_per_step"] = p["wall"] / args.steps * 1e3
         out["value"] = p["tokens"] * args.steps / p["wall"]
-        gbs = p["bytes_call"] / p["mean_call"] / 1e9
-        traffic = read_traffic("kda_chunk_forward_prefill_T4096_H16_traffic.txt",
-                               source_digest(PREFILL_SOURCES))
+        # roofline of the dominant launch: its share of the algorithmic work
+        # (LAUNCH_WORK x token-heads) over its mean duration from the events
+        dom = max(p["launch"], key=p["launch"].get)
+        t_dom = p["launch"][dom]
+        work = LAUNCH_WORK[dom]
+        dom_bytes = work["bytes"] * p["token_heads"] + (2 * PREFILL["B"] * PREFILL["H"] * STATE_BYTES
+                                                         if dom == "kda_seg_forward" else 0)
+        dom_flop = work["flop"] * p["token_heads"]
+        gbs = dom_bytes / t_dom / 1e9
+        traffic = read_traffic(f"{dom}_prefill_T4096_H16_traffic.txt", source_digest(PREFILL_SOURCES))
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
-                           "kernel": "kda_chunk_forward call (kda_chunk_prep, kda_seg_maps, kda_seg_scan, kda_seg_forward)",
-                           "algorithmic_bytes": p["bytes_call"], "mean_call_us": p["mean_call"] * 1e6}
+                           "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": dom,
+                           "algorithmic_bytes": dom_bytes, "algorithmic_flop": dom_flop,
+                           "mfma_frac": dom_flop / t_dom / 1e12 / PEAK_BF16_TFLOPS,
+                           "mean_launch_us": t_dom * 1e6,
+                           "launch_us": {n: t * 1e6 for n, t in p["launch"].items()}}
+        call_gbs = p["bytes_call"] / p["mean_call"] / 1e9
+        out["call_roofline"] = {"bound": "hbm", "achieved": call_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": call_gbs / PEAK_HBM_GBS, "algorithmic_bytes": p["bytes_call"],
+                                "mean_call_us": p["mean_call"] * 1e6}
         tf = p["flop_call"] / p["mean_call"] / 1e12
         out["mfma"] = {"achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop": p["flop_call"]}

@@ -18,12 +18,12 @@ from __future__ import annotations
 
 from typing import Optional, Tuple
 
-from ._lib import (KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_OK, ChunkDesc, KdaError, status_string,
-                   version)
+from ._lib import (CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_OK, ChunkDesc, KdaError,
+                   status_string, version)
 from . import _lib
 
 __all__ = ["chunk_forward", "decode_step", "workspace_bytes", "make_desc", "KdaError",
-           "status_string", "version"]
+           "status_string", "version", "CHUNK_LAUNCHES"]
 
 
 def _torch():
@@ -79,13 +79,15 @@ def check_cu_seqlens(cu, T: int) -> None:
 def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
                   g_floor: float = -0.125, *, o=None, ht=None, workspace=None,
                   output_final_state: bool = True, validate_cu: bool = True,
-                  stream=None) -> Tuple[object, object]:
+                  stream=None, events=None) -> Tuple[object, object]:
     """Chunked KDA forward over whole sequences.
 
     q, k, g: [B, T, H, d]; v: [B, T, H, d] (bf16 or fp32); beta: [B, T, H] fp32.
     cu_seqlens: int32 device tensor [n+1] for n packed sequences (B == 1).
     h0: fp32 [S, H, d, d] or None.  Returns (o [B, T, H, d], ht [S, H, d, d]
     fp32, or None when output_final_state is False).
+    events: optional len(CHUNK_LAUNCHES) + 1 raw hipEvent_t handles recorded
+    around the call's launches (kda_chunk_forward_timed), for measurement.
     """
     torch = _torch()
     B, T, H, d = q.shape
@@ -116,11 +118,14 @@ def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = _lib.chunk_forward_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
-                                _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), stream)
+    args = (desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
+            _ptr(ht), _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    if events is None:
+        st = _lib.chunk_forward_raw(*args)
+    else:
+        st = _lib.chunk_forward_timed_raw(*args, events)
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_forward")
+        raise KdaError(st, "kda_chunk_forward" if events is None else "kda_chunk_forward_timed")
     return o, ht
 
 

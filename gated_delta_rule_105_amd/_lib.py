@@ -22,7 +22,10 @@ KDA_DTYPE_BF16 = 1
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
-           "kda_chunk_forward", "kda_decode_step")
+           "kda_chunk_forward", "kda_chunk_forward_timed", "kda_decode_step")
+
+# Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed).
+CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_maps", "kda_seg_scan", "kda_seg_forward")
 
 
 class KdaError(RuntimeError):
@@ -61,6 +64,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_forward.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
     lib.kda_chunk_forward.restype = ctypes.c_int
+    lib.kda_chunk_forward_timed.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp, ctypes.POINTER(vp)]
+    lib.kda_chunk_forward_timed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -88,6 +94,14 @@ def chunk_forward_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, ws, ws_b
     """Call kda_chunk_forward with raw integer addresses; returns the status."""
     return int(load().kda_chunk_forward(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, ws,
                                         ctypes.c_size_t(ws_bytes), stream))
+
+
+def chunk_forward_timed_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, ws, ws_bytes, stream,
+                            events) -> int:
+    """Call kda_chunk_forward_timed; `events` are len(CHUNK_LAUNCHES) + 1 raw hipEvent_t handles."""
+    arr = (ctypes.c_void_p * (len(CHUNK_LAUNCHES) + 1))(*events)
+    return int(load().kda_chunk_forward_timed(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, ws,
+                                              ctypes.c_size_t(ws_bytes), stream, arr))
 
 
 def decode_step_raw(N, H, d_k, d_v, dtype, g_floor, q, k, v, g, beta, state, o, stream) -> int:

@@ -101,9 +101,9 @@ int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
   return KDA_OK;
 }
 
-int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
-                      const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
-                      void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+                         const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
+                         void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
   Sizes s;
   const int st = check_desc(d, &s);
   if (st != KDA_OK) return st;
@@ -142,12 +142,26 @@ int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, c
     for (const Range& r : all)
       if (overlap(rw, r)) return KDA_ERR_INVALID_ARGUMENT;
   }
-  if (!ht && s.tokens == 0) return KDA_OK;  // nothing to write
+  if (!ht && s.tokens == 0 && !events) return KDA_OK;  // nothing to write
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
                                           d->g_floor, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace,
-                                          stream);
+                                          stream, events);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                      const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                      void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, workspace_bytes, stream, nullptr);
+}
+
+int kda_chunk_forward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                            const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                            void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events) {
+  if (!events) return KDA_ERR_INVALID_ARGUMENT;
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, workspace_bytes, stream, events);
 }
 
 int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor, const void* q,

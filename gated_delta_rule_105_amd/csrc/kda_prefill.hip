@@ -1199,7 +1199,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
 template <typename T, int D, int NW, int NW2>
 int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
                  const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
-                 float* ht, void* ws, hipStream_t stream) {
+                 float* ht, void* ws, hipStream_t stream, void* const* events) {
   constexpr int NR = D / 16;
   const int L = plan.seg_chunks;
   float* wsf = (float*)ws;
@@ -1207,40 +1207,53 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   if (plan.crec_bytes != CRec<T, D>::BYTES) return (int)hipErrorInvalidValue;
   const bool has_segments = plan.n_seg_bound > 0;
   hipError_t e;
+  auto mark = [&](int i) -> hipError_t {
+    return (events && events[i]) ? hipEventRecord((hipEvent_t)events[i], stream) : hipSuccess;
+  };
+  if ((e = mark(0)) != hipSuccess) return (int)e;
   if (has_segments) {
     hipLaunchKernelGGL((kda_chunk_prep<T, D, NW>), dim3((unsigned)plan.n_prep_bound, H), dim3(64 * NW), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H,
                        plan.prep_chunks, g_floor, crec);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
+  if ((e = mark(1)) != hipSuccess) return (int)e;
+  if (has_segments) {
     hipLaunchKernelGGL((kda_seg_maps<T, D, 2 * NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(128 * NW2), 0,
                        stream, cu, n_rows, T_per, H, L, (const unsigned char*)crec, wsf);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
+  if ((e = mark(2)) != hipSuccess) return (int)e;
   const int64_t pairs = (int64_t)n_rows * H;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * (D / 16);
+  const int64_t blocks = (pairs + 7) / 8 * 8 * NR;
   hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / ScanOps<T, D>::KB)), 0, stream,
                      h0, ht, wsf, cu, n_rows, T_per, H, L);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if ((e = mark(3)) != hipSuccess) return (int)e;
   if (has_segments) {
     hipLaunchKernelGGL((kda_seg_forward<T, D, NW2, NR / NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2),
                        0, stream, cu, n_rows, T_per, H, L, (const float*)wsf, (const unsigned char*)crec, (T*)o, ht);
-    e = hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  return (int)e;
+  return (int)mark(4);
 }
 
 }  // namespace
 
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan, float g_floor,
                          const void* q, const void* k, const void* v, const void* g, const float* beta,
-                         const float* h0, const int32_t* cu, void* o, float* ht, void* ws, void* stream) {
+                         const float* h0, const int32_t* cu, void* o, float* ht, void* ws, void* stream,
+                         void* const* events) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s,
+                                          events);
   if (is_bf16 && d == 128)
-    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0,
+                                                               cu, o, ht, ws, s, events);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s);
+    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s,
+                                         events);
   return (int)hipErrorInvalidValue;
 }
 

@@ -173,3 +173,17 @@ def test_decode_rejects(lib):
     assert dec(lib, state=64 * GB + 1024) == KDA_ERR_INVALID_ARGUMENT       # state overlaps q
     assert dec(lib, o=2 * 64 * GB) == KDA_ERR_INVALID_ARGUMENT              # o overlaps k
     assert dec(lib, N=0) == KDA_OK                                          # nothing to do
+
+
+def test_chunk_forward_timed_needs_events(lib):
+    # the measurement twin validates like kda_chunk_forward and also needs the
+    # event array (checked before any HIP call)
+    d = desc()
+    a = fake_args(lib, d)
+    st = lib.kda_chunk_forward_timed(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+                                     a["cu"], a["o"], a["ht"], a["ws"], ctypes.c_size_t(a["ws_bytes"]), None,
+                                     None)
+    assert st == KDA_ERR_INVALID_ARGUMENT
+    assert _lib.chunk_forward_timed_raw(desc(d_k=96, d_v=96), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+                                        a["cu"], a["o"], a["ht"], a["ws"], a["ws_bytes"], None,
+                                        [None] * 5) == KDA_ERR_UNSUPPORTED

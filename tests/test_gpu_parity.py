@@ -290,3 +290,24 @@ def test_value_column_independence():
                                 h0=dv["h0"][..., perm].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(op, o[..., perm]) and torch.equal(htp, ht[..., perm])
+
+
+@pytest.mark.gpu
+def test_chunk_forward_timed_matches_and_times():
+    # the measurement entry point runs the same launches: identical outputs,
+    # and events that bracket each launch in stream order
+    inp = synth.prefill_inputs(1, 1000, 4, 128, 128, "bf16", wid=1, h0=True, device="cuda")
+    note("chunk_forward_timed B=1 T=1000 H=4 d=128 bf16")
+    o1, h1 = kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(kda.CHUNK_LAUNCHES) + 1)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    o2, h2 = kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"],
+                               events=[e.cuda_event for e in ev])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    parts = [ev[j].elapsed_time(ev[j + 1]) for j in range(len(kda.CHUNK_LAUNCHES))]
+    total = ev[0].elapsed_time(ev[-1])
+    assert all(t >= 0 for t in parts) and total > 0
+    assert abs(sum(parts) - total) <= 1e-3 + 1e-3 * total
