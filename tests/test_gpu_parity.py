@@ -311,3 +311,34 @@ def test_chunk_forward_timed_matches_and_times():
     total = ev[0].elapsed_time(ev[-1])
     assert all(t >= 0 for t in parts) and total > 0
     assert abs(sum(parts) - total) <= 1e-3 + 1e-3 * total
+
+
+@pytest.mark.parametrize("g_mode", ["floored", "weak"])
+def test_write_then_read_chunk_forward(g_mode):
+    # With beta = 1 and |k_t| = 1 the write is exact: S_t^T k_t = v_t for any
+    # decay and any history, so with q = k the output is v itself.  A property
+    # of the recurrence, checked on the GPU path without the oracle (fp32,
+    # several chunks and a ragged tail, nonzero initial state).
+    inp = _case(2, 300, 3, 64, "f32", g_mode=g_mode, wid=130)
+    inp["beta"] = torch.ones_like(inp["beta"])
+    inp["q"] = inp["k"].clone()
+    note(f"write-then-read chunk_forward f32 d64 B2 T300 H3 g={g_mode}")
+    o, _ = gpu_forward(inp)
+    e = rel_err(f64(o), f64(inp["v"]))
+    print(f"write-then-read chunk_forward {g_mode}: max|o - v| / max|v| = {e:.3e}")
+    assert e <= TOL["f32"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_write_then_read_decode(d):
+    N, H, steps = 4, 3, 5
+    inp = synth.decode_inputs(N, H, d, d, steps, "f32", wid=131)
+    note(f"write-then-read decode f32 d{d}")
+    state = inp["state"].cuda()
+    for s in range(steps):
+        k = inp["k"][s].cuda()
+        o = kda.decode_step(k, k, inp["v"][s].cuda(), inp["g"][s].cuda(),
+                            torch.ones_like(inp["beta"][s]).cuda(), state)
+        torch.cuda.synchronize()
+        e = rel_err(f64(o), f64(inp["v"][s]))
+        assert e <= TOL["f32"], (s, e)
