@@ -78,7 +78,8 @@ template <typename T, int D> struct Lds {
   static constexpr int BETA = P + PSZ;     // fp32 [64]
   static constexpr int PART = BETA + C * 4;  // fp32 [8][D] partial sums of g
   static constexpr int GL = PART + 8 * D * 4;  // fp32 [D] gamma
-  static constexpr int BYTES = GL + D * 4;
+  static constexpr int TII = GL + D * 4;       // fp32 [4][16][16] diagonal-block inverses
+  static constexpr int BYTES = TII + 4 * 16 * 16 * 4;
 };
 
 // ---- sequences and segments ---------------------------------------------
@@ -328,6 +329,27 @@ __device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, 
   __syncthreads();
 }
 
+// (I + A_bb)^{-1} for diagonal block b (16 x 16, unit lower triangular) by
+// fp32 forward substitution, lane idx solving column idx; written to
+// sTii[b][16][16].  Called by the wave that has just written row tile b of A
+// (its own LDS writes are visible to its later reads).
+template <int LDF>
+__device__ __forceinline__ void diag_inverse(const float* sA, float* sTii, int b, int lane) {
+  const int idx = lane & 15, b0 = 16 * b;
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float acc = (r == idx) ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 0; m < r; ++m) acc -= sA[(b0 + r) * LDF + b0 + m] * x[m];
+    x[r] = acc;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sTii[(b * 16 + r) * 16 + idx] = x[r];
+  }
+}
+
 // ---- Gram blocks: A = diag(beta) strict_lower(Kt Kh^T) (fp32) and
 // P = lower_incl(Qt Kh^T) (operand type), as 16 x 16 tiles on and below the
 // diagonal.  Wave w computes row tile w of A and row tile 3 - w of P (five
@@ -395,6 +417,8 @@ __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sP[(16 * rP + 4 * gq + i) * LDC + 16 * rP + 16 + idx] = Elem<T>::from_f32(0.f);
   }
+  // the diagonal block of the A row tile just written, by the same wave
+  if (rA >= 0) diag_inverse<LDF>(sA, (float*)(smem + M::TII), rA, lane);
   __syncthreads();
 }
 
@@ -410,27 +434,6 @@ __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
 //   Wk = Tp Kt,   Wv = Tp V
 // are plain MFMA products whose right-hand operands are the chunk operands
 // themselves (exact in bf16): only Tp needs the two-term split.
-template <int LDF>
-__device__ __forceinline__ void diag_inverses(const float* sA, float* sT, int wave, int lane) {
-  const int idx = lane & 15;
-  if (wave < 4) {
-    const int b0 = 16 * wave;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == idx) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) acc -= sA[(b0 + r) * LDF + b0 + m] * x[m];
-      x[r] = acc;
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDF + b0 + idx] = x[r];
-    }
-  }
-  __syncthreads();
-}
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 to_bf16x4(const f32x4& x) {
   const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1]));
@@ -513,13 +516,13 @@ __device__ __forceinline__ void store_tp(unsigned char* smem, const f32x4& w, in
 }
 
 // Column block j = wave (< 4) of Tp into the Tp area.  Reads A (V area) and
-// the diagonal inverses (G area).
+// the diagonal inverses (TII area).
 template <typename T, int D>
 __device__ __forceinline__ void inverse_cols(unsigned char* smem, int wave, int lane) {
   typedef Lds<T, D> M;
   typedef Sub<T> S;
   const float* sA = (const float*)(smem + M::V);
-  const float* sT = (const float*)(smem + M::G);
+  const float* sTii = (const float*)(smem + M::TII);  // [4][16][16]
   const float* sBeta = (const float*)(smem + M::BETA);
   const int idx = lane & 15, gq = lane >> 4, j = wave;
   typename S::Opnd wo[3];
@@ -529,13 +532,13 @@ __device__ __forceinline__ void inverse_cols(unsigned char* smem, int wave, int 
     if (i == j) {
       const float b = sBeta[16 * i + idx];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = sT[(16 * i + 4 * gq + e) * M::LDF + 16 * i + idx] * b;
+      for (int e = 0; e < 4; ++e) w[e] = sTii[(16 * i + 4 * gq + e) * 16 + idx] * b;
     } else if (i > j) {
       f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < i; ++m)
         if (m >= j) r = S::apply(S::coef(sA + (16 * i + idx) * M::LDF + 16 * m + 4 * gq, true), wo[m], r);
-      w = S::apply(S::coef(sT + (16 * i + idx) * M::LDF + 16 * i + 4 * gq, false), S::opnd(r),
+      w = S::apply(S::coef(sTii + (16 * i + idx) * 16 + 4 * gq, false), S::opnd(r),
                    (f32x4){0.f, 0.f, 0.f, 0.f});
     }
     if (i < 3 && i >= j) wo[i] = S::opnd(w);
@@ -806,8 +809,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     Raw<T, D, NT, true> raw;
     if (j + 1 < j1)
       raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
-    gram<T, D, NW, true>(smem, wave, lane);
-    diag_inverses<M::LDF>((const float*)(smem + M::V), (float*)(smem + M::G), wave, lane);
+    gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
     if (wave < 4) inverse_cols<T, D>(smem, wave, lane);
     __syncthreads();  // Tp complete; A and the diagonal inverses are dead
     const T* xk[NV];
