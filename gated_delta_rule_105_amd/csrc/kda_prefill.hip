@@ -625,42 +625,53 @@ template <typename T, int D> struct CRec {
   }
 };
 
-// The chunk's record from the chunk pass's LDS (Qt in Q, Wk in WKA, Kh^T in
-// KH, P in P, gamma in GL): wave w writes the fragments w, w + NW, ...
-template <typename T, int D, int NW, int WKA>
-__device__ __forceinline__ void save_record(const unsigned char* smem, unsigned char* rec, int wave, int lane) {
+// The chunk's record from the chunk pass's LDS, in two parts:
+//   save_early: Qt (Q area), Kh^T (KH), P (P) fragments and gamma (GL), ready
+//               once the Gram blocks are done;
+//   save_wk:    Wk fragments (area WKA), ready after the W products.
+// Waves w0 .. w0 + nw - 1 take the fragments w - w0, w - w0 + nw, ...
+template <typename T, int D>
+__device__ __forceinline__ void save_early(const unsigned char* smem, unsigned char* rec, int w, int nw, int lane) {
   typedef Lds<T, D> M;
   typedef Img<T, D> I;
   typedef typename Frag<T>::type FragT;
-  constexpr int KB = I::KB, NQ = 4 * I::NKD, NK = I::NR * I::NKC, NP = 4 * I::NKC, NF = 2 * NQ + NK + NP;
+  constexpr int KB = I::KB, NQ = 4 * I::NKD, NK = I::NR * I::NKC, NP = 4 * I::NKC, NF = NQ + NK + NP;
   const int idx = lane & 15, gq = lane >> 4;
   const T* sQ = (const T*)(smem + M::Q);
-  const T* sW = (const T*)(smem + WKA);
   const T* sKH = (const T*)(smem + M::KH);
   const T* sP = (const T*)(smem + M::P);
-  for (int f = wave; f < NF; f += NW) {
+  for (int f = w; f < NF; f += nw) {
     FragT x;
     int off;
     if (f < NQ) {
       const int rt = f / I::NKD, kb = f % I::NKD;
       x = frag_rows(sQ, M::LDT, 16 * rt + idx, kb * KB, gq);
       off = I::q(rt, kb, lane);
-    } else if (f < 2 * NQ) {
-      const int rt = (f - NQ) / I::NKD, kb = (f - NQ) % I::NKD;
-      x = frag_rows(sW, M::LDT, 16 * rt + idx, kb * KB, gq);
-      off = I::w(rt, kb, lane);
-    } else if (f < 2 * NQ + NK) {
-      const int rr = (f - 2 * NQ) / I::NKC, kb = (f - 2 * NQ) % I::NKC;
+    } else if (f < NQ + NK) {
+      const int rr = (f - NQ) / I::NKC, kb = (f - NQ) % I::NKC;
       x = frag_rows(sKH, M::LDC, 16 * rr + idx, kb * KB, gq);
       off = I::k(rr, kb, lane);
     } else {
-      const int rt = (f - 2 * NQ - NK) / I::NKC, kb = (f - 2 * NQ - NK) % I::NKC;
+      const int rt = (f - NQ - NK) / I::NKC, kb = (f - NQ - NK) % I::NKC;
       x = frag_rows(sP, M::LDC, 16 * rt + idx, kb * KB, gq);
       off = I::p(rt, kb, lane);
     }
     *(FragT*)(rec + off) = x;
   }
-  if (wave == 0 && lane < D / 4) *(f32x4*)(rec + I::GAM + 16 * lane) = *(const f32x4*)(smem + M::GL + 16 * lane);
+  if (w == 0 && lane < D / 4) *(f32x4*)(rec + I::GAM + 16 * lane) = *(const f32x4*)(smem + M::GL + 16 * lane);
+}
+template <typename T, int D, int WKA>
+__device__ __forceinline__ void save_wk(const unsigned char* smem, unsigned char* rec, int w, int nw, int lane) {
+  typedef Lds<T, D> M;
+  typedef Img<T, D> I;
+  typedef typename Frag<T>::type FragT;
+  constexpr int KB = I::KB, NQ = 4 * I::NKD;
+  const int idx = lane & 15, gq = lane >> 4;
+  const T* sW = (const T*)(smem + WKA);
+  for (int f = w; f < NQ; f += nw) {
+    const int rt = f / I::NKD, kb = f % I::NKD;
+    *(FragT*)(rec + I::w(rt, kb, lane)) = frag_rows(sW, M::LDT, 16 * rt + idx, kb * KB, gq);
+  }
 }
 
 // Record image bytes [0, NBYTES) -> LDS `dst` by direct global-to-LDS loads
@@ -810,7 +821,12 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     if (j + 1 < j1)
       raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
     gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
+    unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
+    // waves 0-3 form Tp; with eight waves the other four meanwhile write the
+    // record parts that are already final
     if (wave < 4) inverse_cols<T, D>(smem, wave, lane);
+    if (NW > 4 && wave >= 4) save_early<T, D>(smem, cr, wave - 4, NW - 4, lane);
+    if (NW <= 4) save_early<T, D>(smem, cr, wave, NW, lane);
     __syncthreads();  // Tp complete; A and the diagonal inverses are dead
     const T* xk[NV];
     const T* xv[NV];
@@ -830,8 +846,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     f32x4 wvt[NV][4];
     w_products<T, D, NV>(smem, xv, cts, lane, wvt);
     __syncthreads();  // Wk complete
-    unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
-    save_record<T, D, NW, M::V>(smem, cr, wave, lane);
+    save_wk<T, D, M::V>(smem, cr, wave, NW, lane);
 #pragma unroll
     for (int x = 0; x < NV; ++x)
 #pragma unroll
