@@ -1055,9 +1055,11 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
 }
 
 // ---- pass 3: segment scan S_{s+1} = M_s S_s + B_s ------------------------
-// Workgroup = (sequence, head, 16 state columns); wave w owns the k-block w
-// (rows KB w .. KB w + KB - 1 of S), forms the partial products of all row
-// tiles over its k-block, and the partials are summed through LDS.
+// Workgroup = (sequence, head, 16 state columns).  Wave w owns the KB rows
+// KB w .. KB w + KB - 1 of S: it publishes them as B-operand fragments (the
+// k-block w of every product) through a double-buffered LDS area, and forms
+// the same rows of the next state from all k-blocks, so one barrier per step
+// orders the exchange.
 template <typename T, int D> struct ScanOps;
 template <int D> struct ScanOps<bf16_t, D> {
   static constexpr int KB = 32;
@@ -1083,12 +1085,10 @@ template <int D> struct ScanOps<bf16_t, D> {
     m.lo = *(const bf16x8*)(mf + R::frag(rr, kb, 1, lane));
     return m;
   }
-  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) {
     acc = mma(m.hi, s.hi, acc);
     acc = mma(m.hi, s.lo, acc);
-    acc = mma(m.lo, s.hi, acc);
-    return acc;
+    return mma(m.lo, s.hi, acc);
   }
 };
 template <int D> struct ScanOps<float, D> {
@@ -1099,8 +1099,7 @@ template <int D> struct ScanOps<float, D> {
   __device__ static __forceinline__ MRaw load_m(const unsigned char* mf, int rr, int kb, int lane) {
     return MRaw{*(const f32x4*)(mf + Rec<float, D>::frag(rr, kb, 0, lane))};
   }
-  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) {
     return mma(m.m, s.s, acc);
   }
 };
@@ -1110,8 +1109,8 @@ __global__ void __launch_bounds__(64 * (D / ScanOps<T, D>::KB))
 kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* __restrict__ cu, int n_rows,
              int T_per, int H, int L) {
   typedef ScanOps<T, D> Ops;
-  constexpr int KB = Ops::KB, NWS = D / KB, RT = KB / 16, NRT = D / 16, WPP = D / 16;
-  __shared__ f32x4 sRed[NWS][NRT][64];
+  constexpr int KB = Ops::KB, NWS = D / KB, RT = KB / 16, WPP = D / 16;
+  __shared__ typename Ops::SFrag sS[2][NWS][64];  // published k-blocks, double-buffered
   const int n_pairs = n_rows * H;
   // XCD-aware order: the WPP workgroups of one (sequence, head) get ids with
   // the same residue mod 8, so they share one XCD's L2 for M and B.
@@ -1134,7 +1133,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   }
   const int nseg = n_segments(len, L);
 
-  f32x4 Sk[RT];
+  f32x4 Sk[RT];  // rows of row tiles RT wave + t
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -1163,34 +1162,39 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   // into a ring of three register stages (the loop is unrolled by three so
   // that the stages never move between registers).
   struct Stage {
-    typename Ops::MRaw m[NRT];
+    typename Ops::MRaw m[RT][NWS];
     f32x4 b[RT];
   };
   auto fetch = [&](int s, Stage& st) {
     const float* r = rec(s);
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) st.m[rr] = Ops::load_m((const unsigned char*)(r + R::M), rr, wave, lane);
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int kb = 0; kb < NWS; ++kb)
+        st.m[t][kb] = Ops::load_m((const unsigned char*)(r + R::M), RT * wave + t, kb, lane);
 #pragma unroll
     for (int t = 0; t < RT; ++t) st.b[t] = *(const f32x4*)(r + R::B + R::tile(RT * wave + t, ct, lane));
   };
   auto step = [&](int s, const Stage& st) {
-    const typename Ops::SFrag sf = Ops::state_frag(Sk);
-#pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) sRed[wave][rr][lane] = Ops::product(st.m[rr], sf);
+    sS[s & 1][wave][lane] = Ops::state_frag(Sk);
     __syncthreads();
+    // two accumulators per row tile (even and odd k-blocks) keep the MFMA
+    // chains short
+    f32x4 acc[RT][2];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      f32x4 acc = st.b[t];
-#pragma unroll
-      for (int w = 0; w < NWS; ++w) {
-        const f32x4 x = sRed[w][RT * wave + t][lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += x[i];
-      }
-      Sk[t] = acc;
+      acc[t][0] = st.b[t];
+      acc[t][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int kb = 0; kb < NWS; ++kb) {
+      const typename Ops::SFrag sf = sS[s & 1][kb][lane];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t][kb & 1] = Ops::product(st.m[t][kb], sf, acc[t][kb & 1]);
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) Sk[t] = acc[t][0] + acc[t][1];
     put(rec(s + 1) + R::SIN);
-    __syncthreads();
   };
   const int nsteps = nseg - 1;
   if (nsteps == 0) return;
