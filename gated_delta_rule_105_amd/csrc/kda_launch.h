@@ -87,9 +87,15 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
   // A packed batch cut into whole sequences (one segment each) needs the
   // longest sequence to fit: use the bound of all chunks then.
   p->seg_chunks = (packed && best_l >= per_seq) ? (int)(chunks_total > 0 ? chunks_total : 1) : best_l;
-  // chunk-pass groups: about one round of workgroups, 1 .. 64 chunks each
+  // chunk-pass groups (one workgroup each): long enough that the prefetch of
+  // the next chunk pays (at least 4 chunks where there is work for it), short
+  // enough that the last round of workgroups stays short: at most a quarter of
+  // one CU's share of all chunks, 64 at most
+  const int64_t share = (pairs * per_seq + n_cu - 1) / n_cu;
+  int64_t cap = share / 4 > 4 ? share / 4 : 4;
+  if (cap > per_seq) cap = per_seq;
   int64_t pg = 1;
-  while (pg < 64 && pairs * ((per_seq + 2 * pg - 1) / (2 * pg)) >= n_cu) pg *= 2;
+  while (pg < 64 && 2 * pg <= cap) pg *= 2;
   p->prep_chunks = (int)pg;
   p->n_prep_bound = group_bound(T, n_rows, packed, pg);
   p->n_seg_bound = group_bound(T, n_rows, packed, p->seg_chunks);
