@@ -35,14 +35,14 @@ struct SegPlan {
 // fragments (1 KiB each, k-blocks of KB = 32 for bf16 and 16 for fp32) of
 // Qt and Wk (4 row tiles x d / KB), Kh^T (d / 16 row tiles x 64 / KB) and P
 // (4 x 64 / KB), then gamma (d fp32), padded to a multiple of 1 KiB; then
-// Wv, 64 x d fp32.
+// Wv, 64 x d in the operand type.
 inline size_t chunk_image_bytes(int d, int esz) {
   const size_t kb = esz == 2 ? 32 : 16;
   const size_t frags = 8 * (d / kb) + (size_t)(d / 16) * (kChunk / kb) + 4 * (kChunk / kb);
   return (frags * 1024 + (size_t)d * 4 + 1023) / 1024 * 1024;
 }
 inline size_t chunk_record_bytes(int d, int esz) {
-  return chunk_image_bytes(d, esz) + (size_t)kChunk * d * 4;
+  return chunk_image_bytes(d, esz) + (size_t)kChunk * d * esz;
 }
 
 // Upper bound of groups of g chunks over the sequences: n_rows rows of T

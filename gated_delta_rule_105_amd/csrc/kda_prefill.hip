@@ -41,6 +41,8 @@
 // the current one is used.
 // Within a workgroup, wave w owns 16 value columns of the state: columns of
 // U, O and S never mix, so the state products need no exchange.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -606,7 +608,9 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
 //   QF  Qt rows       [4 row tiles][D / KB k-blocks]
 //   PF  P rows        [4 row tiles][64 / KB k-blocks]
 // (the segment-map pass needs only the part before QF), then
-//   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv (fp32), accumulator order.
+//   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv in the operand type (bf16
+//       path: rounded to bf16, as U = Wv - Wk S is before every product it
+//       enters), accumulator order.
 // Chunk j of sequence n has slot (chunks of sequences 0 .. n - 1) + j.
 template <typename T, int D> struct Img {
   static constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
@@ -619,9 +623,31 @@ template <typename T, int D> struct Img {
   __device__ static __forceinline__ int p(int rt, int kb, int lane) { return PF + ((rt * NKC + kb) * 64 + lane) * 16; }
 };
 template <typename T, int D> struct CRec {
-  static constexpr size_t WV = Img<T, D>::BYTES, BYTES = WV + (size_t)C * D * 4;
+  static constexpr size_t ES = sizeof(T);
+  static constexpr size_t WV = Img<T, D>::BYTES, BYTES = WV + (size_t)C * D * ES;
   __device__ static __forceinline__ size_t wv(int ct, int rt, int lane) {
-    return WV + (((size_t)ct * 4 + rt) * 64 + lane) * 16;
+    return WV + (((size_t)ct * 4 + rt) * 64 + lane) * 4 * ES;
+  }
+  // one lane's 4 accumulator values of a Wv tile, in the operand type
+  __device__ static __forceinline__ void put_wv(unsigned char* p, const f32x4& w) {
+    if constexpr (sizeof(T) == 2) {
+      *(uint2*)p = (uint2){__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[0], w[1])),
+                           __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[2], w[3]))};
+    } else {
+      *(f32x4*)p = w;
+    }
+  }
+  // loaded as raw words (a prefetch then holds them without waiting for the
+  // load) and widened only where they are used
+  typedef typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type WvRaw;
+  __device__ static __forceinline__ WvRaw load_wv(const unsigned char* p) { return *(const WvRaw*)p; }
+  __device__ static __forceinline__ f32x4 widen(const WvRaw& u) {
+    if constexpr (sizeof(T) == 2) {
+      return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+      return u;
+    }
   }
 };
 
@@ -850,7 +876,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
 #pragma unroll
     for (int x = 0; x < NV; ++x)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) *(f32x4*)(cr + CR::wv(cts[x], rt, lane)) = wvt[x][rt];
+      for (int rt = 0; rt < 4; ++rt) CR::put_wv(cr + CR::wv(cts[x], rt, lane), wvt[x][rt]);
     __syncthreads();  // done with this chunk's LDS
     if (j + 1 < j1) {
       raw.store(smem, tid);
@@ -894,16 +920,17 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         X[c][rr][i] = (is_m && 16 * rr + 4 * gq + i == 16 * (hw + NH * c) + idx) ? 1.f : 0.f;
-  auto load_wv = [&](int j, f32x4 (&w)[CT][4]) {
+  typedef typename CR::WvRaw WvRaw;
+  auto load_wv = [&](int j, WvRaw (&w)[CT][4]) {  // M waves: the value part is off
+    if (is_m) return;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        w[c][rt] = is_m ? (f32x4){0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(rec(j) + CR::wv(hw + NH * c, rt, lane));
+      for (int rt = 0; rt < 4; ++rt) w[c][rt] = CR::load_wv(rec(j) + CR::wv(hw + NH * c, rt, lane));
   };
 
   constexpr int NP = 4 + NR, IB = I::MAP_BYTES;  // hook points of a state step; bytes of the image used here
-  f32x4 wv[CT][4];
+  WvRaw wv[CT][4] = {};
   for (int k = 0; k < NP; ++k) issue_image<NW, IB, NP>(smem, rec(j0), wave, lane, k);
   load_wv(j0, wv);
   for (int j = j0; j < j1; ++j) {
@@ -911,11 +938,16 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
     unsigned char* nxt = smem + ((j + 1 - j0) & 1) * IB;
     vmcnt_wait_all();
     __syncthreads();  // image j in LDS; every wave is done with the other buffer
-    f32x4 wvn[CT][4];
+    WvRaw wvn[CT][4] = {};
     const bool more = j + 1 < j1;
     if (more) load_wv(j + 1, wvn);
+    f32x4 wvf[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) wvf[c][rt] = is_m ? (f32x4){0.f, 0.f, 0.f, 0.f} : CR::widen(wv[c][rt]);
     f32x4 unused[CT][4];
-    state_step<T, D, CT, false>(cur, X, wv, unused, lane, [&](int k) {
+    state_step<T, D, CT, false>(cur, X, wvf, unused, lane, [&](int k) {
       if (more) issue_image<NW, IB, NP>(nxt, rec(j + 1), wave, lane, k);
     });
     if (j + 1 < j1) {
@@ -991,16 +1023,17 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
   const int idx = lane & 15, gq = lane >> 4;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
   auto rec = [&](int j) -> const unsigned char* { return crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES; };
-  auto load_wv = [&](int j, f32x4 (&w)[CT][4]) {
+  typedef typename CR::WvRaw WvRaw;
+  auto load_wv = [&](int j, WvRaw (&w)[CT][4]) {
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) w[c][rt] = *(const f32x4*)(rec(j) + CR::wv(wave + NW * c, rt, lane));
+      for (int rt = 0; rt < 4; ++rt) w[c][rt] = CR::load_wv(rec(j) + CR::wv(wave + NW * c, rt, lane));
   };
 
   constexpr int NP = 4 + NR;  // hook points of a state step
   for (int k = 0; k < NP; ++k) issue_image<NW, I::BYTES, NP>(smem, rec(j0), wave, lane, k);
-  f32x4 wv[CT][4];
+  WvRaw wv[CT][4];
   load_wv(j0, wv);
   typedef Rec<T, D> R;
   const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS + R::SIN;
@@ -1017,11 +1050,16 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
     unsigned char* nxt = smem + ((j + 1 - j0) & 1) * I::BYTES;
     vmcnt_wait_all();
     __syncthreads();  // image j in LDS; every wave is done with the other buffer
-    f32x4 wvn[CT][4];
+    WvRaw wvn[CT][4];
     const bool more = j + 1 < j1;
     if (more) load_wv(j + 1, wvn);
+    f32x4 wvf[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) wvf[c][rt] = CR::widen(wv[c][rt]);
     f32x4 O[CT][4];
-    state_step<T, D, CT, true>(cur, S, wv, O, lane, [&](int k) {
+    state_step<T, D, CT, true>(cur, S, wvf, O, lane, [&](int k) {
       if (more) issue_image<NW, I::BYTES, NP>(nxt, rec(j + 1), wave, lane, k);
     });
     lds_barrier();  // every wave is done with the Wk and Kh^T fragments

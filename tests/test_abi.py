@@ -66,10 +66,10 @@ def test_workspace_size_valid(lib):
     assert st == KDA_OK and n > 0 and n % 256 == 0
     st2, n2 = ws_status(lib, desc(T=8192))
     assert st2 == KDA_OK and n2 >= n and n2 % 256 == 0
-    # at least one record of chunk operands per (chunk, head): Qt, Wk, Kh^T
-    # (64 x 128 bf16 each), P (64 x 64 bf16), gamma (128 fp32), Wv (64 x 128 fp32)
+    # at least one record of chunk operands per (chunk, head): Qt, Wk, Kh^T, Wv
+    # (64 x 128 bf16 each), P (64 x 64 bf16), gamma (128 fp32)
     d2 = desc(T=8192)
-    per_chunk = 3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4 + 64 * 128 * 4
+    per_chunk = 4 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4
     assert n2 >= d2.B * d2.H * (8192 // 64) * per_chunk
     st3, n3 = ws_status(lib, desc(T=0))
     assert st3 == KDA_OK and n3 == 0
