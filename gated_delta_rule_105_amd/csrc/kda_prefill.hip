@@ -58,6 +58,19 @@ namespace {
 
 constexpr int C = kChunk;
 
+// Streaming accesses: the chunk inputs are read once and o is written once,
+// and the chunk records are read back once per state pass; non-temporal
+// hints keep them from displacing cached data.  (The record stores stay
+// ordinary: a short workload's records are read back from cache.)
+typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4nt*)p));
+}
+__device__ __forceinline__ void stream_store16(void* p, const uint4& x) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4nt, x), (u32x4nt*)p);
+}
+
 // ---- LDS layout of the chunk engine -------------------------------------
 template <typename T, int D> struct Lds {
   static constexpr int PADT = 16 / (int)sizeof(T);
@@ -171,10 +184,10 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
       const uint4 z = {0u, 0u, 0u, 0u};
       if (t < len) {
         const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;
-        if (WITH_Q) q[j] = *(const uint4*)(Q + off);
-        k[j] = *(const uint4*)(K + off);
-        v[j] = *(const uint4*)(V + off);
-        g[j] = *(const uint4*)(G + off);
+        if (WITH_Q) q[j] = stream_load16(Q + off);
+        k[j] = stream_load16(K + off);
+        v[j] = stream_load16(V + off);
+        g[j] = stream_load16(G + off);
       } else {
         if (WITH_Q) q[j] = z;
         k[j] = z;
@@ -205,8 +218,8 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
       if (t < clen)
-        *(uint4*)(o + ((size_t)(tok0 + t) * H + h) * D + cv * EPV) =
-            *(const uint4*)(stage + t * M::LDT * (int)sizeof(T) + cv * 16);
+        stream_store16(o + ((size_t)(tok0 + t) * H + h) * D + cv * EPV,
+                       *(const uint4*)(stage + t * M::LDT * (int)sizeof(T) + cv * 16));
     }
   }
 };
@@ -640,7 +653,10 @@ template <typename T, int D> struct CRec {
   // loaded as raw words (a prefetch then holds them without waiting for the
   // load) and widened only where they are used
   typedef typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type WvRaw;
-  __device__ static __forceinline__ WvRaw load_wv(const unsigned char* p) { return *(const WvRaw*)p; }
+  __device__ static __forceinline__ WvRaw load_wv(const unsigned char* p) {
+    if constexpr (sizeof(T) == 2) return __builtin_bit_cast(WvRaw, __builtin_nontemporal_load((const u32x2nt*)p));
+    else return __builtin_bit_cast(WvRaw, __builtin_nontemporal_load((const u32x4nt*)p));
+  }
   __device__ static __forceinline__ f32x4 widen(const WvRaw& u) {
     if constexpr (sizeof(T) == 2) {
       return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
@@ -706,6 +722,7 @@ __device__ __forceinline__ void save_wk(const unsigned char* smem, unsigned char
 // issues the k-th slice of them, so that the issue can be spread over other
 // work.  The loads are only issued: vmcnt_wait_all() and a barrier make them
 // visible.
+constexpr int kCpolNt = 2;  // cache-policy operand of the direct loads: non-temporal
 template <int NW, int NBYTES, int NPARTS>
 __device__ __forceinline__ void issue_image(unsigned char* dst, const unsigned char* rec, int wave, int lane, int k) {
   constexpr int NB = NBYTES / 1024;
@@ -715,7 +732,8 @@ __device__ __forceinline__ void issue_image(unsigned char* dst, const unsigned c
   for (int i = i0; i < i1; ++i) {
     const int b = wave + NW * i;
     __builtin_amdgcn_global_load_lds((const void*)(rec + 1024 * b + 16 * lane),
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16, 0,
+                                     kCpolNt);
   }
 }
 __device__ __forceinline__ void vmcnt_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
