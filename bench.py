@@ -59,12 +59,11 @@ STATE_BYTES = 128 * 128 * 4    # one fp32 state matrix (h0 read, ht written)
 # chunk pass reads every input and does the chunk-local products (key Gram,
 # P, Wk, Wv, the inverse); the output pass does the state products and P U
 # and writes o (plus h0 read / ht written per sequence and head).  The
-# segment maps and the scan are extra work of the segment decomposition, with
-# no share of the algorithmic figures.
+# segment maps (composed in the chunk pass) and the scan are extra work of
+# the segment decomposition, with no share of the algorithmic figures.
 LAUNCH_WORK = {
     "kda_chunk_prep": dict(bytes=4 * 2 * 128 + 4,
                            flop=2 * (128 * 63 // 2 + 3 * 128 * 65 // 2 + 63 * 62 // 6)),
-    "kda_seg_maps": dict(bytes=0, flop=0),
     "kda_seg_scan": dict(bytes=0, flop=0),
     "kda_seg_forward": dict(bytes=2 * 128, flop=2 * (3 * 128 * 128 + 128 * 65 // 2)),
 }

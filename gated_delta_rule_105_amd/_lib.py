@@ -25,7 +25,7 @@ EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size
            "kda_chunk_forward", "kda_chunk_forward_timed", "kda_decode_step")
 
 # Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed).
-CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_maps", "kda_seg_scan", "kda_seg_forward")
+CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_scan", "kda_seg_forward")
 
 
 class KdaError(RuntimeError):

@@ -10,17 +10,21 @@ namespace kda {
 constexpr int kChunk = 64;  // tokens per chunk
 
 // How a chunked forward is cut for the GPU.
-//  - The chunk pass takes groups of `prep_chunks` consecutive chunks of a
-//    sequence, one workgroup per (group, head), and writes one record per
-//    (chunk, head) with the chunk's operands for the state passes.
 //  - The state passes cut every sequence into segments of `seg_chunks`
 //    chunks.  One record per (segment, head) holds three d x d fp32 matrices:
 //    the segment's affine state map S_out = M S_in + B (M and B) and its
 //    incoming state S_in.
+//  - The chunk pass writes one record per (chunk, head) with the chunk's
+//    operands for the output pass.  With `maps_in_prep` its workgroups are
+//    the (segment, head) pairs and also compose the segment maps; otherwise
+//    every sequence is a single segment (no maps) and the chunk pass takes
+//    groups of `prep_chunks` consecutive chunks of a sequence, one workgroup
+//    per (group, head).
 // Workspace: the segment records, then the chunk records.
 struct SegPlan {
   int prep_chunks;       // chunks per chunk-pass workgroup
   int seg_chunks;        // chunks per segment of the state passes
+  bool maps_in_prep;     // chunk-pass groups are the segments, and it writes their maps
   int64_t n_prep_bound;  // upper bound of chunk-pass groups over all sequences
   int64_t n_seg_bound;   // upper bound of segments over all sequences
   int64_t n_slots;       // upper bound of chunks over all sequences
@@ -55,15 +59,17 @@ inline int64_t group_bound(int64_t T, int n_rows, bool packed, int64_t g) {
 }
 
 // Chooses the cut from a cost model of the launches (one workgroup per CU
-// in every pass; times per chunk and per scan step measured on the target):
-// longer segments mean fewer workgroups in the segment-map and output passes,
-// shorter ones a longer chain in the segment scan.  Host-only, deterministic
-// in its arguments.  `packed`: n_rows sequences share T tokens (lengths
-// unknown on the host; the mean length is used), else n_rows rows of T
-// tokens each.  esz: operand bytes (2 bf16, 4 fp32).  Returns false on
-// overflow.
+// in the chunk and output passes; times per chunk and per scan step measured
+// on the target).  Either every sequence is one segment (the chunk pass then
+// balances its groups over the CUs on its own, and the output pass walks each
+// sequence), or segments of L chunks: one workgroup per (segment, head) in
+// both passes, the chunk pass composing the maps, and a scan of
+// (segments - 1) steps between them.  Host-only, deterministic in its
+// arguments.  `packed`: n_rows sequences share T tokens (lengths unknown on
+// the host; the mean length is used), else n_rows rows of T tokens each.
+// esz: operand bytes (2 bf16, 4 fp32).  Returns false on overflow.
 inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool packed, SegPlan* p) {
-  const double t_map = 3.0, t_scan = 1.4, t_fwd = 4.7;  // us
+  const double t_prep = 9.0, t_map = 1.5, t_scan = 1.4, t_fwd = 4.7;  // us
   const int64_t n_cu = 256;
   const int64_t chunks_total = (T + kChunk - 1) / kChunk;
   const int rows = n_rows > 0 ? n_rows : 1;
@@ -71,34 +77,37 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
   if (per_seq < 1) per_seq = 1;
   const int64_t pairs = (int64_t)n_rows * H;
   auto rounds = [&](int64_t wg) { return (double)((wg + n_cu - 1) / n_cu); };
-  double best = 1e300;
-  int best_l = 1;
-  for (int64_t L = 1;; L *= 2) {
-    const int64_t Lc = L < per_seq ? L : per_seq;
-    const int64_t segs = (per_seq + Lc - 1) / Lc;
-    const double t = rounds(pairs * (segs - 1)) * Lc * t_map + (double)(segs - 1) * t_scan +
-                     rounds(pairs * segs) * Lc * t_fwd;
+  // one segment per sequence
+  const int64_t share = (pairs * per_seq + n_cu - 1) / n_cu;  // chunks per CU
+  double best = (double)share * t_prep + rounds(pairs) * (double)per_seq * t_fwd;
+  int best_l = 0;  // 0: one segment per sequence
+  for (int64_t L = 1; L < per_seq; L *= 2) {
+    const int64_t segs = (per_seq + L - 1) / L;
+    const double t = rounds(pairs * segs) * (double)L * (t_prep + t_map + t_fwd) + (double)(segs - 1) * t_scan;
     if (t < best) {
       best = t;
-      best_l = (int)Lc;
+      best_l = (int)L;
     }
-    if (L >= per_seq) break;
   }
-  // A packed batch cut into whole sequences (one segment each) needs the
-  // longest sequence to fit: use the bound of all chunks then.
-  p->seg_chunks = (packed && best_l >= per_seq) ? (int)(chunks_total > 0 ? chunks_total : 1) : best_l;
-  // chunk-pass groups (one workgroup each): long enough that the prefetch of
-  // the next chunk pays (at least 4 chunks where there is work for it), short
-  // enough that the last round of workgroups stays short: at most a quarter of
-  // one CU's share of all chunks, 64 at most
-  const int64_t share = (pairs * per_seq + n_cu - 1) / n_cu;
-  int64_t cap = share / 4 > 4 ? share / 4 : 4;
-  if (cap > per_seq) cap = per_seq;
-  int64_t pg = 1;
-  while (pg < 64 && 2 * pg <= cap) pg *= 2;
-  p->prep_chunks = (int)pg;
-  p->n_prep_bound = group_bound(T, n_rows, packed, pg);
+  p->maps_in_prep = best_l > 0;
+  if (p->maps_in_prep) {
+    p->seg_chunks = best_l;
+    p->prep_chunks = best_l;
+  } else {
+    // Whole sequences: a packed batch needs the longest sequence to fit, so
+    // the segment is the bound of all chunks.  Chunk-pass groups: long enough
+    // that the prefetch of the next chunk pays (at least 4 chunks where there
+    // is work for it), short enough that the last round of workgroups stays
+    // short: at most a quarter of one CU's share of all chunks, 64 at most.
+    p->seg_chunks = (int)(packed ? (chunks_total > 0 ? chunks_total : 1) : per_seq);
+    int64_t cap = share / 4 > 4 ? share / 4 : 4;
+    if (cap > per_seq) cap = per_seq;
+    int64_t pg = 1;
+    while (pg < 64 && 2 * pg <= cap) pg *= 2;
+    p->prep_chunks = (int)pg;
+  }
   p->n_seg_bound = group_bound(T, n_rows, packed, p->seg_chunks);
+  p->n_prep_bound = p->maps_in_prep ? p->n_seg_bound : group_bound(T, n_rows, packed, p->prep_chunks);
   p->n_slots = T == 0 ? 0 : (packed ? chunks_total + n_rows : (int64_t)n_rows * chunks_total);
   p->rec_bytes = (size_t)3 * d * d * sizeof(float);
   p->crec_bytes = chunk_record_bytes(d, esz);
@@ -110,7 +119,7 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
 }
 
 // Launches of one chunked forward, in stream order.
-constexpr int kLaunches = 4;  // chunk pass, segment maps, segment scan, output pass
+constexpr int kLaunches = 3;  // chunk pass (with the segment maps), segment scan, output pass
 
 // Enqueue the chunked forward.  All arguments were validated by the caller.
 // n_rows: number of sequences (n_seqs, or B when cu == nullptr).  events:

@@ -18,27 +18,27 @@
 //
 // One chunk maps the state affinely, S -> M_j S + B_j.  Every sequence is cut
 // into segments of L chunks; the composition of a segment's maps is again
-// affine, S_out = M S_in + B.  Four launches:
+// affine, S_out = M S_in + B.  Three launches:
 //   1. kda_chunk_prep (one workgroup per (segment, head), all in parallel):
 //      the chunk-local part of each chunk (decay prefix sums, Gram blocks,
 //      the inverse (I + A)^{-1}, Wk and Wv) from the inputs, written to a
-//      per-chunk record: Qt, Wk, Kh^T, P and gamma as an image of the state
-//      passes' LDS, and Wv.
-//   2. kda_seg_maps (one workgroup per (segment, head), all in parallel):
-//      runs the segment's chunk records on the state started from 0 (giving
-//      B, half of the waves) and from I with the value part of U switched off
-//      (giving M, the other half).  The
-//      last segment of a sequence is skipped: no later segment needs its map.
-//   3. kda_seg_scan (one workgroup per (sequence, head, 16 state columns)):
+//      per-chunk record: Qt, Wk, Kh^T, P and gamma as an image of the output
+//      pass's LDS, and Wv.  The same workgroup runs each chunk, while its
+//      operands are still in LDS, on the state started from 0 (giving B) and
+//      from I with the value part of U switched off (giving M), and writes the
+//      segment's map; the last segment of a sequence has none (no later
+//      segment needs it).  When every sequence is one segment there are no
+//      maps, and the chunks are grouped by a length of the pass's own.
+//   2. kda_seg_scan (one workgroup per (sequence, head, 16 state columns)):
 //      S_0 = h0, S_{s+1} = M_s S_s + B_s, writing every segment's incoming
 //      state.  M S is done as three bf16 products of a hi/lo split of both
 //      factors (about fp32 accuracy).
-//   4. kda_seg_forward (one workgroup per (segment, head), all in parallel):
+//   3. kda_seg_forward (one workgroup per (segment, head), all in parallel):
 //      the state recurrence from the segment's incoming state over its chunk
-//      records, writing o and, for the last segment, the final state.
-// Launches 2 and 4 keep two record images in LDS (about 62 KiB each at
-// d = 128): the next chunk's image lands by direct global-to-LDS loads while
-// the current one is used.
+//      records, writing o and, for the last segment, the final state.  It
+//      keeps two record images in LDS (about 57 KiB each at d = 128): the
+//      next chunk's image lands by direct global-to-LDS loads while the
+//      current one is used.
 // Within a workgroup, wave w owns 16 value columns of the state: columns of
 // U, O and S never mix, so the state products need no exchange.
 #include <type_traits>
@@ -175,9 +175,10 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
 
   // Rows past the chunk's end (a sequence's last chunk) are loaded as zeros
   // (beta and g of such rows must be 0; their q, k and v then reach no
-  // output).  The buffer is scoped to one chunk iteration.
-  __device__ __forceinline__ void load(const T* Q, const T* K, const T* V, const T* G, const float* B,
-                                       int64_t tok0, int len, int H, int h, int tid) {
+  // output).  The buffer is scoped to one chunk iteration.  load = load_qkg
+  // (q, k, g and beta) + load_v, which may be issued at different times.
+  __device__ __forceinline__ void load_qkg(const T* Q, const T* K, const T* G, const float* B, int64_t tok0,
+                                           int len, int H, int h, int tid) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
@@ -186,29 +187,50 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
         const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;
         if (WITH_Q) q[j] = stream_load16(Q + off);
         k[j] = stream_load16(K + off);
-        v[j] = stream_load16(V + off);
         g[j] = stream_load16(G + off);
       } else {
         if (WITH_Q) q[j] = z;
         k[j] = z;
-        v[j] = z;
         g[j] = z;
       }
     }
     beta = (tid < len) ? B[(size_t)(tok0 + tid) * H + h] : 0.f;
   }
+  __device__ __forceinline__ void load_v(const T* V, int64_t tok0, int len, int H, int h, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
+      v[j] = t < len ? stream_load16(V + ((size_t)(tok0 + t) * H + h) * D + cv * EPV) : (uint4){0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void load(const T* Q, const T* K, const T* V, const T* G, const float* B,
+                                       int64_t tok0, int len, int H, int h, int tid) {
+    load_qkg(Q, K, G, B, tok0, len, H, h, tid);
+    load_v(V, tok0, len, H, h, tid);
+  }
 
-  __device__ __forceinline__ void store(unsigned char* smem, int tid) const {
+  // into LDS: everything but v (store_qkg), v (store_v), or both (store)
+  __device__ __forceinline__ void store_qkg(unsigned char* smem, int tid) const {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
       const int off = t * M::LDT * (int)sizeof(T) + cv * 16;
       if (WITH_Q) *(uint4*)(smem + M::Q + off) = q[j];
       *(uint4*)(smem + M::K + off) = k[j];
-      *(uint4*)(smem + M::V + off) = v[j];
       *(uint4*)(smem + M::G + off) = g[j];
     }
     if (tid < C) ((float*)(smem + M::BETA))[tid] = beta;
+  }
+  __device__ __forceinline__ void store_v(unsigned char* smem, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
+      *(uint4*)(smem + M::V + t * M::LDT * (int)sizeof(T) + cv * 16) = v[j];
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* smem, int tid) const {
+    store_qkg(smem, tid);
+    store_v(smem, tid);
   }
 
   // Chunk output [64][LDT] staged in LDS -> o rows tok0 .. tok0 + clen - 1.
@@ -620,7 +642,7 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
 //   GAM gamma         [D] fp32, padded to 1 KiB
 //   QF  Qt rows       [4 row tiles][D / KB k-blocks]
 //   PF  P rows        [4 row tiles][64 / KB k-blocks]
-// (the segment-map pass needs only the part before QF), then
+// then
 //   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv in the operand type (bf16
 //       path: rounded to bf16, as U = Wv - Wk S is before every product it
 //       enters), accumulator order.
@@ -628,8 +650,7 @@ __device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4
 template <typename T, int D> struct Img {
   static constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
   static constexpr int WF = 0, KF = WF + 4 * NKD * 1024, GAM = KF + NR * NKC * 1024,
-                       QF = GAM + (D * 4 + 1023) / 1024 * 1024, PF = QF + 4 * NKD * 1024, BYTES = PF + 4 * NKC * 1024,
-                       MAP_BYTES = QF;
+                       QF = GAM + (D * 4 + 1023) / 1024 * 1024, PF = QF + 4 * NKD * 1024, BYTES = PF + 4 * NKC * 1024;
   __device__ static __forceinline__ int q(int rt, int kb, int lane) { return QF + ((rt * NKD + kb) * 64 + lane) * 16; }
   __device__ static __forceinline__ int w(int rt, int kb, int lane) { return WF + ((rt * NKD + kb) * 64 + lane) * 16; }
   __device__ static __forceinline__ int k(int rr, int kb, int lane) { return KF + ((rr * NKC + kb) * 64 + lane) * 16; }
@@ -641,18 +662,19 @@ template <typename T, int D> struct CRec {
   __device__ static __forceinline__ size_t wv(int ct, int rt, int lane) {
     return WV + (((size_t)ct * 4 + rt) * 64 + lane) * 4 * ES;
   }
+  typedef typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type WvRaw;
   // one lane's 4 accumulator values of a Wv tile, in the operand type
-  __device__ static __forceinline__ void put_wv(unsigned char* p, const f32x4& w) {
+  __device__ static __forceinline__ WvRaw pack(const f32x4& w) {
     if constexpr (sizeof(T) == 2) {
-      *(uint2*)p = (uint2){__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[0], w[1])),
-                           __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[2], w[3]))};
+      return (uint2){__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[0], w[1])),
+                     __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[2], w[3]))};
     } else {
-      *(f32x4*)p = w;
+      return w;
     }
   }
+  __device__ static __forceinline__ void put_wv(unsigned char* p, const f32x4& w) { *(WvRaw*)p = pack(w); }
   // loaded as raw words (a prefetch then holds them without waiting for the
   // load) and widened only where they are used
-  typedef typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type WvRaw;
   __device__ static __forceinline__ WvRaw load_wv(const unsigned char* p) {
     if constexpr (sizeof(T) == 2) return __builtin_bit_cast(WvRaw, __builtin_nontemporal_load((const u32x2nt*)p));
     else return __builtin_bit_cast(WvRaw, __builtin_nontemporal_load((const u32x4nt*)p));
@@ -665,6 +687,8 @@ template <typename T, int D> struct CRec {
       return u;
     }
   }
+  // w rounded as the record stores it
+  __device__ static __forceinline__ f32x4 as_stored(const f32x4& w) { return widen(pack(w)); }
 };
 
 // The chunk's record from the chunk pass's LDS, in two parts:
@@ -743,20 +767,54 @@ __device__ __forceinline__ void vmcnt_wait_all() { __builtin_amdgcn_s_waitcnt(0)
 // them as pending LDS writes).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Where a state step reads its A operands (each one 16-byte LDS read per
+// lane): a record image (ImgSrc, the state passes), or the chunk pass's own
+// arrays (LdsSrc: Qt, Kh^T, P, gamma and Wk in area WKA), from which the
+// image fragments are cut, so both give the same values.
+template <typename T, int D> struct ImgSrc {
+  typedef Img<T, D> I;
+  typedef typename Frag<T>::type FragT;
+  const unsigned char* img;
+  int lane;
+  __device__ __forceinline__ FragT at(int off) const { return *(const FragT*)(img + off); }
+  __device__ __forceinline__ FragT w(int rt, int kb) const { return at(I::w(rt, kb, lane)); }
+  __device__ __forceinline__ FragT q(int rt, int kb) const { return at(I::q(rt, kb, lane)); }
+  __device__ __forceinline__ FragT p(int rt, int kb) const { return at(I::p(rt, kb, lane)); }
+  __device__ __forceinline__ FragT k(int rr, int kb) const { return at(I::k(rr, kb, lane)); }
+  __device__ __forceinline__ f32x4 gam(int rr) const {
+    return *(const f32x4*)(img + I::GAM + 4 * (16 * rr + 4 * (lane >> 4)));
+  }
+};
+template <typename T, int D, int WKA> struct LdsSrc {
+  typedef Lds<T, D> M;
+  typedef typename Frag<T>::type FragT;
+  static constexpr int KB = Elem<T>::KB;
+  const unsigned char* smem;
+  int lane;
+  __device__ __forceinline__ FragT rows(int area, int ld, int r, int kb) const {
+    return frag_rows((const T*)(smem + area), ld, r + (lane & 15), kb * KB, lane >> 4);
+  }
+  __device__ __forceinline__ FragT w(int rt, int kb) const { return rows(WKA, M::LDT, 16 * rt, kb); }
+  __device__ __forceinline__ FragT q(int rt, int kb) const { return rows(M::Q, M::LDT, 16 * rt, kb); }
+  __device__ __forceinline__ FragT p(int rt, int kb) const { return rows(M::P, M::LDC, 16 * rt, kb); }
+  __device__ __forceinline__ FragT k(int rr, int kb) const { return rows(M::KH, M::LDC, 16 * rr, kb); }
+  __device__ __forceinline__ f32x4 gam(int rr) const {
+    return *(const f32x4*)(smem + M::GL + 4 * (16 * rr + 4 * (lane >> 4)));
+  }
+};
+
 // CT column tiles of the state (rows = D key channels) through one chunk:
 // U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
 // O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  The A operands
-// are fragments of a record image in LDS at `img`, each loaded once per
-// phase and fed to the CT tiles.  hook(k), k = 0 .. 4 + D / 16 - 1, is called
-// between the row blocks (the callers spread the next image's loads there).
-template <typename T, int D, int CT, bool WITH_O, typename Hook>
-__device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[CT][D / 16],
-                                           const f32x4 (&wv)[CT][4], f32x4 (&O)[CT][4], int lane, Hook&& hook) {
+// come from `src` (ImgSrc or LdsSrc), each loaded once per phase and fed to
+// the CT tiles.  hook(k), k = 0 .. 4 + D / 16 - 1, is called between the row
+// blocks (the callers spread the next image's loads there).
+template <typename T, int D, int CT, bool WITH_O, typename Src, typename Hook>
+__device__ __forceinline__ void state_step(const Src& src, f32x4 (&S)[CT][D / 16], const f32x4 (&wv)[CT][4],
+                                           f32x4 (&O)[CT][4], int lane, Hook&& hook) {
   typedef Img<T, D> I;
   typedef typename Frag<T>::type FragT;
   constexpr int KB = I::KB, NKD = I::NKD, NKC = I::NKC, NR = I::NR;
-  const int gq = lane >> 4;
-  auto frag = [&](int off) { return *(const FragT*)(img + off); };
 
   FragT SB[CT][NKD];
 #pragma unroll
@@ -770,8 +828,8 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
     FragT aw[NKD], aq[NKD];
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) {
-      aw[kb] = frag(I::w(rt, kb, lane));
-      if (WITH_O) aq[kb] = frag(I::q(rt, kb, lane));
+      aw[kb] = src.w(rt, kb);
+      if (WITH_O) aq[kb] = src.q(rt, kb);
     }
     f32x4 ws[CT], qs[CT];
 #pragma unroll
@@ -802,7 +860,7 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
       FragT ap[NKC];
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
-        if (kb * KB <= 16 * rt + 15) ap[kb] = frag(I::p(rt, kb, lane));
+        if (kb * KB <= 16 * rt + 15) ap[kb] = src.p(rt, kb);
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
         if (kb * KB <= 16 * rt + 15) {
@@ -811,13 +869,12 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
         }
     }
   }
-  const float* sGL = (const float*)(img + I::GAM);
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
     FragT ak[NKC];
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) ak[kb] = frag(I::k(rr, kb, lane));
-    const f32x4 gm = *(const f32x4*)(sGL + 16 * rr + 4 * gq);
+    for (int kb = 0; kb < NKC; ++kb) ak[kb] = src.k(rr, kb);
+    const f32x4 gm = src.gam(rr);
 #pragma unroll
     for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
@@ -830,171 +887,25 @@ __device__ __forceinline__ void state_step(const unsigned char* img, f32x4 (&S)[
   }
 }
 
-// ---- pass 1: the chunk-local part of every chunk -> its record -----------
-// One workgroup per (group of L consecutive chunks of a sequence, head)
-// walks its chunks; the inputs of the next chunk are fetched while the
-// current one is finished.  (L here is the chunk pass's own group length,
-// independent of the state passes' segments.)  Wave w
-// forms Wk and Wv for the value-column tiles w + NW x.
-template <typename T, int D, int NW>
-__global__ void __launch_bounds__(64 * NW)
-kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-               const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-               int n_rows, int T_per, int H, int L, float g_floor, unsigned char* __restrict__ crec) {
-  typedef Lds<T, D> M;
-  typedef CRec<T, D> CR;
-  constexpr int NT = 64 * NW, NR = D / 16, NV = NR / NW;
-  static_assert(NV >= 1 && NV * NW == NR, "waves must split the value columns");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
-  Seg sg;
-  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
-  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
-  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
-
-  {
-    Raw<T, D, NT, true> first;
-    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid);
-    first.store(smem, tid);
-  }
-  __syncthreads();
-  for (int j = j0; j < j1; ++j) {
-    elementwise<T, D, NW, true>(smem, g_floor, tid);
-    // the next chunk's inputs are fetched now and land in LDS at the end
-    Raw<T, D, NT, true> raw;
-    if (j + 1 < j1)
-      raw.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * (j + 1), min(C, sg.len - C * (j + 1)), H, h, tid);
-    gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
-    unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
-    // waves 0-3 form Tp; with eight waves the other four meanwhile write the
-    // record parts that are already final
-    if (wave < 4) inverse_cols<T, D>(smem, wave, lane);
-    if (NW > 4 && wave >= 4) save_early<T, D>(smem, cr, wave - 4, NW - 4, lane);
-    if (NW <= 4) save_early<T, D>(smem, cr, wave, NW, lane);
-    __syncthreads();  // Tp complete; A and the diagonal inverses are dead
-    const T* xk[NV];
-    const T* xv[NV];
-    int cts[NV];
-#pragma unroll
-    for (int x = 0; x < NV; ++x) {
-      xk[x] = (const T*)(smem + M::KT);
-      xv[x] = (const T*)(smem + M::VT);
-      cts[x] = wave + NW * x;
-    }
-    {
-      f32x4 wk[NV][4];
-      w_products<T, D, NV>(smem, xk, cts, lane, wk);
-#pragma unroll
-      for (int x = 0; x < NV; ++x) store_wk<T, D, M::V>(smem, wk[x], cts[x], lane);
-    }
-    f32x4 wvt[NV][4];
-    w_products<T, D, NV>(smem, xv, cts, lane, wvt);
-    __syncthreads();  // Wk complete
-    save_wk<T, D, M::V>(smem, cr, wave, NW, lane);
-#pragma unroll
-    for (int x = 0; x < NV; ++x)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) CR::put_wv(cr + CR::wv(cts[x], rt, lane), wvt[x][rt]);
-    __syncthreads();  // done with this chunk's LDS
-    if (j + 1 < j1) {
-      raw.store(smem, tid);
-      __syncthreads();
-    }
-  }
-}
-
-// ---- pass 2: the affine map of every segment but the last ----------------
-// Waves 0 .. NH - 1 carry B (the state from zero, value part of U on), waves
-// NH .. 2 NH - 1 carry M (the state from I, value part off); within a half,
-// wave w owns the column tiles w + NH x.  The part of the record images this
-// pass needs (Wk, Kh^T, gamma) is double-buffered: the next chunk's is issued
-// piecewise between the row blocks of the state step.
-template <typename T, int D, int NW>
-__global__ void __launch_bounds__(64 * NW)
-kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
-             const unsigned char* __restrict__ crec, float* __restrict__ ws) {
-  typedef CRec<T, D> CR;
-  typedef Img<T, D> I;
-  constexpr int NH = NW / 2, NR = D / 16, CT = NR / NH, LDM = D + 4;
-  static_assert(NW % 2 == 0 && CT >= 1 && CT * NH == NR, "each half of the waves splits the columns");
-  static_assert(D * LDM * 4 <= 2 * I::MAP_BYTES, "M staging fits the image buffers");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::MAP_BYTES];
-  Seg sg;
-  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
-  if (sg.s == sg.nseg - 1) return;  // nothing downstream needs the last map
-  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
-  const bool is_m = wave >= NH;
-  const int hw = is_m ? wave - NH : wave;
-  const int idx = lane & 15, gq = lane >> 4;
-  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
-  auto rec = [&](int j) -> const unsigned char* { return crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES; };
-
-  f32x4 X[CT][NR];
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        X[c][rr][i] = (is_m && 16 * rr + 4 * gq + i == 16 * (hw + NH * c) + idx) ? 1.f : 0.f;
-  typedef typename CR::WvRaw WvRaw;
-  auto load_wv = [&](int j, WvRaw (&w)[CT][4]) {  // M waves: the value part is off
-    if (is_m) return;
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) w[c][rt] = CR::load_wv(rec(j) + CR::wv(hw + NH * c, rt, lane));
-  };
-
-  constexpr int NP = 4 + NR, IB = I::MAP_BYTES;  // hook points of a state step; bytes of the image used here
-  WvRaw wv[CT][4] = {};
-  for (int k = 0; k < NP; ++k) issue_image<NW, IB, NP>(smem, rec(j0), wave, lane, k);
-  load_wv(j0, wv);
-  for (int j = j0; j < j1; ++j) {
-    unsigned char* cur = smem + ((j - j0) & 1) * IB;
-    unsigned char* nxt = smem + ((j + 1 - j0) & 1) * IB;
-    vmcnt_wait_all();
-    __syncthreads();  // image j in LDS; every wave is done with the other buffer
-    WvRaw wvn[CT][4] = {};
-    const bool more = j + 1 < j1;
-    if (more) load_wv(j + 1, wvn);
-    f32x4 wvf[CT][4];
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) wvf[c][rt] = is_m ? (f32x4){0.f, 0.f, 0.f, 0.f} : CR::widen(wv[c][rt]);
-    f32x4 unused[CT][4];
-    state_step<T, D, CT, false>(cur, X, wvf, unused, lane, [&](int k) {
-      if (more) issue_image<NW, IB, NP>(nxt, rec(j + 1), wave, lane, k);
-    });
-    if (j + 1 < j1) {
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wvn[c][rt];
-    }
-  }
-  __syncthreads();  // every wave is done with the images
-
+// The segment map in the segment record (Rec): B from each wave's accumulator
+// tiles, M through LDS (sM, [D][D + 4] fp32) into the scan's A-operand
+// fragments.  wave owns the column tiles cols[x] of B (XB[x]) and of M (XM[x]).
+template <typename T, int D, int NW, int NC>
+__device__ __forceinline__ void save_map(float* sM, float* recs, const f32x4 (&XB)[NC][D / 16],
+                                         const f32x4 (&XM)[NC][D / 16], const int (&cols)[NC], int wave,
+                                         int lane) {
   typedef Rec<T, D> R;
-  float* recs = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS;
-  float* sM = (float*)smem;  // [D][LDM] fp32
-  if (!is_m) {
+  constexpr int NR = D / 16, LDM = D + 4;
+  const int idx = lane & 15, gq = lane >> 4;
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+  for (int x = 0; x < NC; ++x)
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr) *(f32x4*)(recs + R::B + R::tile(rr, hw + NH * c, lane)) = X[c][rr];
-  } else {
+    for (int rr = 0; rr < NR; ++rr) {
+      *(f32x4*)(recs + R::B + R::tile(rr, cols[x], lane)) = XB[x][rr];
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sM[(16 * rr + 4 * gq + i) * LDM + 16 * (hw + NH * c) + idx] = X[c][rr][i];
-  }
+      for (int i = 0; i < 4; ++i) sM[(16 * rr + 4 * gq + i) * LDM + 16 * cols[x] + idx] = XM[x][rr][i];
+    }
   __syncthreads();
-  // M into the scan's A-operand fragments
   unsigned char* mf = (unsigned char*)(recs + R::M);
   for (int f = wave; f < NR * R::NKB; f += NW) {
     const int rr = f / R::NKB, kb = f % R::NKB;
@@ -1013,6 +924,150 @@ kda_seg_maps(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L
     } else {
       *(f32x4*)(mf + R::frag(rr, kb, 0, lane)) = *(const f32x4*)src;
     }
+  }
+}
+
+// ---- pass 1: the chunk-local part of every chunk -> its record -----------
+// One workgroup per (group of L consecutive chunks of a sequence, head)
+// walks its chunks; the inputs of the next chunk are fetched while the
+// current one is finished.  Wave w forms Wk and Wv for the value-column tiles
+// w + NW x.
+// With MAPS the groups are the segments of the state passes, and the
+// workgroup also composes its segment's affine map S_out = M S_in + B (not
+// for the last segment of a sequence: no later segment needs it): after each
+// chunk's W products it takes the chunk's Wk, Kh^T, gamma and Wv, still in
+// LDS and registers, through a state step on B (started from 0) and on M
+// (started from I, value part of U off), wave w on the column tiles it owns.
+// Without MAPS (every sequence is one segment) the group length is the chunk
+// pass's own.
+template <typename T, int D, int NW, bool MAPS>
+__global__ void __launch_bounds__(64 * NW)
+kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+               const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+               int n_rows, int T_per, int H, int L, float g_floor, unsigned char* __restrict__ crec,
+               float* __restrict__ ws) {
+  typedef Lds<T, D> M;
+  typedef CRec<T, D> CR;
+  constexpr int NT = 64 * NW, NR = D / 16, NV = NR / NW;
+  static_assert(NV >= 1 && NV * NW == NR, "waves must split the value columns");
+  static_assert(D * (D + 4) * 4 <= M::BYTES, "M staging fits the chunk pass's LDS");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
+  Seg sg;
+  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
+  const int h = blockIdx.y, tid0 = threadIdx.x, lane0 = tid0 & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // uniform: scalar control flow
+  const int idx = lane0 & 15, gq = lane0 >> 4;
+  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
+  const bool maps = MAPS && sg.s < sg.nseg - 1;
+  int cts[NV];
+#pragma unroll
+  for (int x = 0; x < NV; ++x) cts[x] = wave + NW * x;
+  // the segment map's column tiles cts[x]: B in X[x], M in X[NV + x]
+  f32x4 X[MAPS ? 2 * NV : 1][NR];
+  if (MAPS) {
+#pragma unroll
+    for (int x = 0; x < NV; ++x)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          X[x][rr][i] = 0.f;
+          X[NV + x][rr][i] = (16 * rr + 4 * gq + i == 16 * cts[x] + idx) ? 1.f : 0.f;
+        }
+  }
+
+  {
+    Raw<T, D, NT, true> first;
+    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0);
+    first.store(smem, tid0);
+  }
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) {
+    // With MAPS (the map's state tiles take 64 registers), thread and lane
+    // index as opaque per-chunk values: the addresses derived from them are
+    // formed inside the loop, not hoisted and held across it, which would
+    // overflow the registers.
+    int tid = tid0, lane = lane0;
+    if (MAPS) asm volatile("" : "+v"(tid), "+v"(lane));
+    elementwise<T, D, NW, true>(smem, g_floor, tid);
+    // the next chunk's inputs are fetched while this one is worked on: q, k,
+    // g and beta now (into LDS once Wk is complete), v now as well, or with
+    // MAPS (short of registers) once Wk is complete, the map's state step
+    // covering its latency (into LDS at the end of the chunk)
+    Raw<T, D, NT, true> raw;
+    const bool more = j + 1 < j1;
+    const int64_t tok_n = sg.tok0 + (int64_t)C * (j + 1);
+    const int len_n = min(C, sg.len - C * (j + 1));
+    if (more) {
+      raw.load_qkg(q, k, g, beta, tok_n, len_n, H, h, tid);
+      if (!MAPS) raw.load_v(v, tok_n, len_n, H, h, tid);
+    }
+    gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
+    unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
+    // waves 0-3 form Tp; with eight waves the other four meanwhile write the
+    // record parts that are already final
+    if (wave < 4) inverse_cols<T, D>(smem, wave, lane);
+    if (NW > 4 && wave >= 4) save_early<T, D>(smem, cr, wave - 4, NW - 4, lane);
+    if (NW <= 4) save_early<T, D>(smem, cr, wave, NW, lane);
+    __syncthreads();  // Tp complete; A and the diagonal inverses are dead
+    const T* xk[NV];
+    const T* xv[NV];
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      xk[x] = (const T*)(smem + M::KT);
+      xv[x] = (const T*)(smem + M::VT);
+    }
+    {
+      f32x4 wk[NV][4];
+      w_products<T, D, NV>(smem, xk, cts, lane, wk);
+#pragma unroll
+      for (int x = 0; x < NV; ++x) store_wk<T, D, M::V>(smem, wk[x], cts[x], lane);
+    }
+    f32x4 wvt[NV][4];
+    w_products<T, D, NV>(smem, xv, cts, lane, wvt);
+    __syncthreads();  // Wk complete; Tp, Qt, Kh and beta are dead
+    // the next chunk's q, k, g and beta go to their areas now (v's area holds
+    // Wk until the end of the chunk)
+    if (more) {
+      if (MAPS) raw.load_v(v, tok_n, len_n, H, h, tid);
+      raw.store_qkg(smem, tid);
+    }
+    save_wk<T, D, M::V>(smem, cr, wave, NW, lane);
+#pragma unroll
+    for (int x = 0; x < NV; ++x)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) CR::put_wv(cr + CR::wv(cts[x], rt, lane), wvt[x][rt]);
+    if (maps) {
+      // Wv as the record holds it, so that the map and the output pass see
+      // the same chunk
+      f32x4 wvx[MAPS ? 2 * NV : 1][4], unused[MAPS ? 2 * NV : 1][4];
+#pragma unroll
+      for (int x = 0; x < NV; ++x)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          wvx[x][rt] = CR::as_stored(wvt[x][rt]);
+          wvx[NV + x][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      state_step<T, D, MAPS ? 2 * NV : 1, false>(LdsSrc<T, D, M::V>{smem, lane}, X, wvx, unused, lane,
+                                                  [](int) {});
+    }
+    __syncthreads();  // done with this chunk's LDS
+    if (more) {
+      raw.store_v(smem, tid);
+      __syncthreads();
+    }
+  }
+  if (maps) {
+    f32x4 XB[NV][NR], XM[NV][NR];
+#pragma unroll
+    for (int x = 0; x < NV; ++x)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        XB[x][rr] = X[x][rr];
+        XM[x][rr] = X[MAPS ? NV + x : 0][rr];
+      }
+    save_map<T, D, NW, NV>((float*)smem, ws + ((size_t)blockIdx.x * H + h) * Rec<T, D>::FLOATS, XB, XM, cts,
+                           wave, lane0);
   }
 }
 
@@ -1077,7 +1132,7 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) wvf[c][rt] = CR::widen(wv[c][rt]);
     f32x4 O[CT][4];
-    state_step<T, D, CT, true>(cur, S, wvf, O, lane, [&](int k) {
+    state_step<T, D, CT, true>(ImgSrc<T, D>{cur, lane}, S, wvf, O, lane, [&](int k) {
       if (more) issue_image<NW, I::BYTES, NP>(nxt, rec(j + 1), wave, lane, k);
     });
     lds_barrier();  // every wave is done with the Wk and Kh^T fragments
@@ -1288,31 +1343,30 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
     return (events && events[i]) ? hipEventRecord((hipEvent_t)events[i], stream) : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return (int)e;
-  if (has_segments) {
-    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW>), dim3((unsigned)plan.n_prep_bound, H), dim3(64 * NW), 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H,
-                       plan.prep_chunks, g_floor, crec);
+  if (has_segments && plan.maps_in_prep) {
+    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0,
+                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L,
+                       g_floor, crec, wsf);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  } else if (has_segments) {
+    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false>), dim3((unsigned)plan.n_prep_bound, H), dim3(64 * NW), 0,
+                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H,
+                       plan.prep_chunks, g_floor, crec, wsf);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((e = mark(1)) != hipSuccess) return (int)e;
-  if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_maps<T, D, 2 * NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(128 * NW2), 0,
-                       stream, cu, n_rows, T_per, H, L, (const unsigned char*)crec, wsf);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  }
-  if ((e = mark(2)) != hipSuccess) return (int)e;
   const int64_t pairs = (int64_t)n_rows * H;
   const int64_t blocks = (pairs + 7) / 8 * 8 * NR;
   hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / ScanOps<T, D>::KB)), 0, stream,
                      h0, ht, wsf, cu, n_rows, T_per, H, L);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  if ((e = mark(3)) != hipSuccess) return (int)e;
+  if ((e = mark(2)) != hipSuccess) return (int)e;
   if (has_segments) {
     hipLaunchKernelGGL((kda_seg_forward<T, D, NW2, NR / NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2),
                        0, stream, cu, n_rows, T_per, H, L, (const float*)wsf, (const unsigned char*)crec, (T*)o, ht);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  return (int)mark(4);
+  return (int)mark(3);
 }
 
 }  // namespace

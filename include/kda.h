@@ -119,14 +119,14 @@ int kda_chunk_forward(const kda_chunk_desc_t* d,
 /*
  * Measurement twin of kda_chunk_forward: the same call, and in addition
  * hipEventRecord(events[i], stream) before each of the call's launches and
- * events[4] after the last one.  The launches, in stream order, are
- *   0: chunk pass      (chunk-local operands of every chunk, to the workspace)
- *   1: segment maps    (each segment's affine state map)
- *   2: segment scan    (every segment's incoming state)
- *   3: output pass     (o and the final state)
+ * events[3] after the last one.  The launches, in stream order, are
+ *   0: chunk pass      (chunk-local operands of every chunk, to the workspace,
+ *                       and each segment's affine state map)
+ *   1: segment scan    (every segment's incoming state)
+ *   2: output pass     (o and the final state)
  * so hipEventElapsedTime(events[i], events[i + 1]) is launch i's time.  A
  * launch with nothing to do (no tokens) is skipped, its events still
- * recorded.  events: 5 hipEvent_t handles created by the caller (any entry
+ * recorded.  events: 4 hipEvent_t handles created by the caller (any entry
  * may be NULL: not recorded); the array itself must not be NULL.  No
  * synchronisation.  Returns what kda_chunk_forward returns, or
  * KDA_ERR_HIP if recording an event fails.

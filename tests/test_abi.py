@@ -186,4 +186,4 @@ def test_chunk_forward_timed_needs_events(lib):
     assert st == KDA_ERR_INVALID_ARGUMENT
     assert _lib.chunk_forward_timed_raw(desc(d_k=96, d_v=96), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
                                         a["cu"], a["o"], a["ht"], a["ws"], a["ws_bytes"], None,
-                                        [None] * 5) == KDA_ERR_UNSUPPORTED
+                                        [None] * (len(_lib.CHUNK_LAUNCHES) + 1)) == KDA_ERR_UNSUPPORTED
