@@ -389,73 +389,133 @@ __device__ __forceinline__ void diag_inverse(const float* sA, float* sTii, int b
 
 // ---- Gram blocks: A = diag(beta) strict_lower(Kt Kh^T) (fp32) and
 // P = lower_incl(Qt Kh^T) (operand type), as 16 x 16 tiles on and below the
-// diagonal.  Wave w computes row tile w of A and row tile 3 - w of P (five
-// tiles each); every Kh fragment it loads serves the A and the P tile of its
-// column.  Of the upper P tiles only (0, 1) and (2, 3) share a 32-wide
-// k-block with needed ones; they are zeroed (bf16 path).  A's upper tiles are
-// never read.
+// diagonal, each one MMA chain over the key channels: rows from Kt (A) or Qt
+// (P), columns from Kh.  Four waves: wave w takes row tile w of A and row
+// tile 3 - w of P (five tiles each; every Kh fragment it loads serves the A
+// and the P tile of its column).  Eight waves: waves 0-3 take the diagonal
+// tiles (b, b) of A and P, waves 4-7 three of the twelve others each, in an
+// order where consecutive tiles mostly share their column.  Of the upper P
+// tiles only (0, 1) and (2, 3) share a 32-wide k-block with needed ones; they
+// are zeroed (bf16 path).  A's upper tiles are never read.
+// Eight-wave tile lists, wave w's tile t in byte w of kGram8[t]: bit 6 set for
+// a tile (clear: the list has ended), bit 4 P (else A), bits 2-3 the row
+// tile, bits 0-1 the column tile.  Immediate operands, taken apart with
+// scalar shifts (a table in memory would be read by vector loads, which wait
+// behind the prefetch of the next chunk's inputs).
+constexpr uint64_t gram_code(int p, int r, int c) { return (uint64_t)(64 | 16 * p | 4 * r | c); }
+constexpr uint64_t gram_list(const int (&x)[8][3]) {
+  uint64_t v = 0;
+  for (int w = 0; w < 8; ++w)
+    if (x[w][0] >= 0) v |= gram_code(x[w][0], x[w][1], x[w][2]) << (8 * w);
+  return v;
+}
+constexpr int kGramT0[8][3] = {{0, 0, 0}, {0, 1, 1}, {0, 2, 2}, {0, 3, 3}, {0, 1, 0}, {1, 2, 0}, {0, 2, 1}, {1, 3, 1}};
+constexpr int kGramT1[8][3] = {{1, 0, 0}, {1, 1, 1}, {1, 2, 2}, {1, 3, 3}, {1, 1, 0}, {0, 3, 0}, {1, 2, 1}, {0, 3, 2}};
+constexpr int kGramT2[8][3] = {{-1, 0, 0}, {-1, 0, 0}, {-1, 0, 0}, {-1, 0, 0},
+                               {0, 2, 0},  {1, 3, 0},  {0, 3, 1},  {1, 3, 2}};
+constexpr uint64_t kGram8[3] = {gram_list(kGramT0), gram_list(kGramT1), gram_list(kGramT2)};
+
+template <typename T, int D>
+__device__ __forceinline__ void gram_store(unsigned char* smem, bool is_p, int r, int c, const f32x4& acc,
+                                           int lane) {
+  typedef Lds<T, D> M;
+  const int idx = lane & 15, gq = lane >> 4, s = 16 * c + idx;
+  if (!is_p) {
+    float* sA = (float*)(smem + M::V);
+    const float* sBeta = (const float*)(smem + M::BETA);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * r + 4 * gq + i;
+      sA[row * M::LDF + s] = s < row ? sBeta[row] * acc[i] : 0.f;
+    }
+  } else {
+    T* sP = (T*)(smem + M::P);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * r + 4 * gq + i;
+      sP[row * M::LDC + s] = Elem<T>::from_f32(s <= row ? acc[i] : 0.f);
+    }
+  }
+}
+
 template <typename T, int D, int NW, bool WITH_P>
 __device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
   typedef Lds<T, D> M;
   typedef typename Frag<T>::type FragT;
-  static_assert(NW == 4 || NW == 8, "row tiles of A and P over four or eight waves");
+  static_assert(NW == 4 || NW == 8, "Gram tiles over four or eight waves");
+  static_assert(NW == 4 || WITH_P, "the eight-wave split includes P");
   constexpr int KB = Elem<T>::KB, NKD = D / KB, LDT = M::LDT, LDC = M::LDC, LDF = M::LDF;
   const T* sQ = (const T*)(smem + M::Q);
   const T* sK = (const T*)(smem + M::K);
   const T* sG = (const T*)(smem + M::G);
-  float* sA = (float*)(smem + M::V);
   T* sP = (T*)(smem + M::P);
-  const float* sBeta = (const float*)(smem + M::BETA);
   const int idx = lane & 15, gq = lane >> 4;
-  // four waves: row tile w of A and 3 - w of P; eight: A on waves 0-3, P on 4-7
-  const int rA = NW == 4 ? wave : (wave < 4 ? wave : -1);
-  const int rP = NW == 4 ? 3 - wave : (wave >= 4 ? 7 - wave : -1);  // wave-uniform
-  FragT fa[NKD], fq[NKD];
+  if constexpr (NW == 8) {
+    FragT fb[NKD];
+    int cprev = -1;
 #pragma unroll
-  for (int kb = 0; kb < NKD; ++kb) {
-    if (rA >= 0) fa[kb] = frag_rows(sK, LDT, 16 * rA + idx, kb * KB, gq);
-    if (WITH_P && rP >= 0) fq[kb] = frag_rows(sQ, LDT, 16 * rP + idx, kb * KB, gq);
-  }
-  float br[4];
+    for (int t = 0; t < 3; ++t) {
+      const int code = (int)(kGram8[t] >> (8 * wave)) & 0xff;  // wave-uniform
+      if (!(code & 64)) break;
+      const bool is_p = code & 16;
+      const int r = (code >> 2) & 3, c = code & 3;
+      if (c != cprev) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) br[i] = rA >= 0 ? sBeta[16 * rA + 4 * gq + i] : 0.f;
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const bool doA = ct <= rA, doP = WITH_P && ct <= rP;
-    if (doA || doP) {
-      FragT fb[NKD];
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) fb[kb] = frag_rows(sG, LDT, 16 * ct + idx, kb * KB, gq);
-      const int s = 16 * ct + idx;
-      if (doA) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) acc = mma(fa[kb], fb[kb], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rA + 4 * gq + i;
-          sA[r * LDF + s] = s < r ? br[i] * acc[i] : 0.f;
-        }
+        for (int kb = 0; kb < NKD; ++kb) fb[kb] = frag_rows(sG, LDT, 16 * c + idx, kb * KB, gq);
+        cprev = c;
       }
-      if (doP) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const T* src = is_p ? sQ : sK;
+      FragT fr[NKD];
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) acc = mma(fq[kb], fb[kb], acc);
+      for (int kb = 0; kb < NKD; ++kb) fr[kb] = frag_rows(src, LDT, 16 * r + idx, kb * KB, gq);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rP + 4 * gq + i;
-          sP[r * LDC + s] = Elem<T>::from_f32(s <= r ? acc[i] : 0.f);
+      for (int kb = 0; kb < NKD; ++kb) acc = mma(fr[kb], fb[kb], acc);
+      gram_store<T, D>(smem, is_p, r, c, acc, lane);
+    }
+    if (KB == 32 && (wave == 0 || wave == 2)) {
+      // P tile (0, 1) from wave 0, tile (2, 3) from wave 2
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sP[(16 * wave + 4 * gq + i) * LDC + 16 * wave + 16 + idx] = Elem<T>::from_f32(0.f);
+    }
+    // the diagonal block of A just written, by the same wave
+    if (wave < 4) diag_inverse<LDF>((const float*)(smem + M::V), (float*)(smem + M::TII), wave, lane);
+  } else {
+    const int rA = wave, rP = 3 - wave;  // wave-uniform
+    FragT fa[NKD], fq[NKD];
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+      fa[kb] = frag_rows(sK, LDT, 16 * rA + idx, kb * KB, gq);
+      if (WITH_P) fq[kb] = frag_rows(sQ, LDT, 16 * rP + idx, kb * KB, gq);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const bool doA = ct <= rA, doP = WITH_P && ct <= rP;
+      if (doA || doP) {
+        FragT fb[NKD];
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) fb[kb] = frag_rows(sG, LDT, 16 * ct + idx, kb * KB, gq);
+        if (doA) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < NKD; ++kb) acc = mma(fa[kb], fb[kb], acc);
+          gram_store<T, D>(smem, false, rA, ct, acc, lane);
+        }
+        if (doP) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < NKD; ++kb) acc = mma(fq[kb], fb[kb], acc);
+          gram_store<T, D>(smem, true, rP, ct, acc, lane);
         }
       }
     }
-  }
-  if (WITH_P && KB == 32 && (rP == 0 || rP == 2)) {
-    // P tile (0, 1) from the wave with rP = 0, tile (2, 3) from rP = 2
+    if (WITH_P && KB == 32 && (rP == 0 || rP == 2)) {
+      // P tile (0, 1) from the wave with rP = 0, tile (2, 3) from rP = 2
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sP[(16 * rP + 4 * gq + i) * LDC + 16 * rP + 16 + idx] = Elem<T>::from_f32(0.f);
+      for (int i = 0; i < 4; ++i) sP[(16 * rP + 4 * gq + i) * LDC + 16 * rP + 16 + idx] = Elem<T>::from_f32(0.f);
+    }
+    diag_inverse<LDF>((const float*)(smem + M::V), (float*)(smem + M::TII), rA, lane);
   }
-  // the diagonal block of the A row tile just written, by the same wave
-  if (rA >= 0) diag_inverse<LDF>(sA, (float*)(smem + M::TII), rA, lane);
   __syncthreads();
 }
 
@@ -1010,21 +1070,27 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     if (NW > 4 && wave >= 4) save_early<T, D>(smem, cr, wave - 4, NW - 4, lane);
     if (NW <= 4) save_early<T, D>(smem, cr, wave, NW, lane);
     __syncthreads();  // Tp complete; A and the diagonal inverses are dead
-    const T* xk[NV];
-    const T* xv[NV];
+    // Wk and Wv in one pass over Tp: operands x < NV are Kt^T column tiles,
+    // the others V^T tiles
+    const T* xo[2 * NV];
+    int co[2 * NV];
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
-      xk[x] = (const T*)(smem + M::KT);
-      xv[x] = (const T*)(smem + M::VT);
-    }
-    {
-      f32x4 wk[NV][4];
-      w_products<T, D, NV>(smem, xk, cts, lane, wk);
-#pragma unroll
-      for (int x = 0; x < NV; ++x) store_wk<T, D, M::V>(smem, wk[x], cts[x], lane);
+      xo[x] = (const T*)(smem + M::KT);
+      xo[NV + x] = (const T*)(smem + M::VT);
+      co[x] = co[NV + x] = cts[x];
     }
     f32x4 wvt[NV][4];
-    w_products<T, D, NV>(smem, xv, cts, lane, wvt);
+    {
+      f32x4 w[2 * NV][4];
+      w_products<T, D, 2 * NV>(smem, xo, co, lane, w);
+#pragma unroll
+      for (int x = 0; x < NV; ++x) {
+        store_wk<T, D, M::V>(smem, w[x], cts[x], lane);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) wvt[x][rt] = w[NV + x][rt];
+      }
+    }
     __syncthreads();  // Wk complete; Tp, Qt, Kh and beta are dead
     // the next chunk's q, k, g and beta go to their areas now (v's area holds
     // Wk until the end of the chunk)
@@ -1166,34 +1232,35 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
 }
 
 // ---- pass 3: segment scan S_{s+1} = M_s S_s + B_s ------------------------
-// Workgroup = (sequence, head, 16 state columns).  Wave w owns the KB rows
-// KB w .. KB w + KB - 1 of S: it publishes them as B-operand fragments (the
-// k-block w of every product) through a double-buffered LDS area, and forms
-// the same rows of the next state from all k-blocks, so one barrier per step
-// orders the exchange.
+// Workgroup = (sequence, head, 16 state columns), one wave per 16-row tile of
+// S.  Each step a wave publishes its rows as halves of B-operand fragments
+// through a double-buffered LDS area and forms the same rows of the next state
+// from all k-blocks, so one barrier per step orders the exchange.  M_s and
+// B_s do not depend on the state: each wave fetches its rows of them three
+// steps ahead.
 template <typename T, int D> struct ScanOps;
 template <int D> struct ScanOps<bf16_t, D> {
-  static constexpr int KB = 32;
-  // hi/lo bf16 split of the state rows held by this wave (two acc tiles)
+  static constexpr int KB = 32, NKB = D / KB;
+  // Published state, in B-fragment order: [hi/lo][k-block][lane] 16 bytes,
+  // row tile t filling bytes 8 (t % 2) .. 8 (t % 2) + 7 of k-block t / 2.
+  typedef uint4 PubArea[2][NKB][64];
+  __device__ static __forceinline__ void publish(PubArea& a, int t, int lane, const f32x4& x) {
+    const s16x4 h = to_bf16x4(x);
+    *((uint2*)&a[0][t >> 1][lane] + (t & 1)) = __builtin_bit_cast(uint2, h);
+    *((uint2*)&a[1][t >> 1][lane] + (t & 1)) = __builtin_bit_cast(uint2, to_bf16x4(x - from_bf16x4(h)));
+  }
   struct SFrag { bf16x8 hi, lo; };
-  __device__ static __forceinline__ SFrag state_frag(const f32x4* Sk) {
-    SFrag r;
-    r.hi = frag_from_acc(Sk[0], Sk[1]);
-    f32x4 a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = Sk[0][e] - (float)r.hi[e];
-      b[e] = Sk[1][e] - (float)r.hi[e + 4];
-    }
-    r.lo = frag_from_acc(a, b);
-    return r;
+  __device__ static __forceinline__ SFrag gather(const PubArea& a, int kb, int lane) {
+    return SFrag{__builtin_bit_cast(bf16x8, a[0][kb][lane]), __builtin_bit_cast(bf16x8, a[1][kb][lane])};
   }
   struct MRaw { bf16x8 hi, lo; };
-  __device__ static __forceinline__ MRaw load_m(const unsigned char* mf, int rr, int kb, int lane) {
+  // k-block kb of this lane's M rows; off: byte offset of its (kb = 0, hi)
+  // fragment in the segment record
+  __device__ static __forceinline__ MRaw load_m(__amdgpu_buffer_rsrc_t r, uint32_t off, int kb) {
     typedef Rec<bf16_t, D> R;
     MRaw m;
-    m.hi = *(const bf16x8*)(mf + R::frag(rr, kb, 0, lane));
-    m.lo = *(const bf16x8*)(mf + R::frag(rr, kb, 1, lane));
+    m.hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)R::frag(0, kb, 0, 0), 0, 0));
+    m.lo = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)R::frag(0, kb, 1, 0), 0, 0));
     return m;
   }
   __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) {
@@ -1203,25 +1270,26 @@ template <int D> struct ScanOps<bf16_t, D> {
   }
 };
 template <int D> struct ScanOps<float, D> {
-  static constexpr int KB = 16;
-  struct SFrag { f32x4 s; };
-  __device__ static __forceinline__ SFrag state_frag(const f32x4* Sk) { return SFrag{Sk[0]}; }
-  struct MRaw { f32x4 m; };
-  __device__ static __forceinline__ MRaw load_m(const unsigned char* mf, int rr, int kb, int lane) {
-    return MRaw{*(const f32x4*)(mf + Rec<float, D>::frag(rr, kb, 0, lane))};
+  static constexpr int KB = 16, NKB = D / KB;
+  typedef f32x4 PubArea[NKB][64];  // row tile t is k-block t
+  __device__ static __forceinline__ void publish(PubArea& a, int t, int lane, const f32x4& x) { a[t][lane] = x; }
+  typedef f32x4 SFrag;
+  __device__ static __forceinline__ SFrag gather(const PubArea& a, int kb, int lane) { return a[kb][lane]; }
+  typedef f32x4 MRaw;
+  __device__ static __forceinline__ MRaw load_m(__amdgpu_buffer_rsrc_t r, uint32_t off, int kb) {
+    return __builtin_bit_cast(f32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)Rec<float, D>::frag(0, kb, 0, 0), 0, 0));
   }
-  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) {
-    return mma(m.m, s.s, acc);
-  }
+  __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) { return mma(m, s, acc); }
 };
 
 template <typename T, int D>
-__global__ void __launch_bounds__(64 * (D / ScanOps<T, D>::KB))
+__global__ void __launch_bounds__(64 * (D / 16))
 kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* __restrict__ cu, int n_rows,
              int T_per, int H, int L) {
   typedef ScanOps<T, D> Ops;
-  constexpr int KB = Ops::KB, NWS = D / KB, RT = KB / 16, WPP = D / 16;
-  __shared__ typename Ops::SFrag sS[2][NWS][64];  // published k-blocks, double-buffered
+  constexpr int NKB = Ops::NKB, NWS = D / 16, WPP = D / 16;
+  __shared__ typename Ops::PubArea sS[2];  // published state, double-buffered
   const int n_pairs = n_rows * H;
   // XCD-aware order: the WPP workgroups of one (sequence, head) get ids with
   // the same residue mod 8, so they share one XCD's L2 for M and B.
@@ -1229,7 +1297,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   const int p = (jj / WPP) * 8 + xcd, ct = jj % WPP;
   if (p >= n_pairs) return;
   const int n = p / H, h = p % H;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's row tile
   const int lane = threadIdx.x & 63, idx = lane & 15, gq = lane >> 4;
   const int col = 16 * ct + idx;
 
@@ -1244,79 +1312,71 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   }
   const int nseg = n_segments(len, L);
 
-  f32x4 Sk[RT];  // rows of row tiles RT wave + t
+  f32x4 Sk;
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * (RT * wave + t) + 4 * gq + i;
-      Sk[t][i] = h0 ? h0[((size_t)p * D + row) * D + col] : 0.f;
-    }
+  for (int i = 0; i < 4; ++i) Sk[i] = h0 ? h0[((size_t)p * D + 16 * wave + 4 * gq + i) * D + col] : 0.f;
   typedef Rec<T, D> R;
   auto rec = [&](int s) -> float* { return ws + ((size_t)(base + s) * H + h) * R::FLOATS; };
-  auto put = [&](float* dst) {  // incoming state, accumulator tile order
-#pragma unroll
-    for (int t = 0; t < RT; ++t) *(f32x4*)(dst + R::tile(RT * wave + t, ct, lane)) = Sk[t];
-  };
+  auto put = [&](float* dst) { *(f32x4*)(dst + R::tile(wave, ct, lane)) = Sk; };  // accumulator tile order
   if (nseg == 0) {
     if (ht) {
       float* dst = ht + (size_t)p * D * D;
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * (RT * wave + t) + 4 * gq + i) * D + col] = Sk[t][i];
+      for (int i = 0; i < 4; ++i) dst[(16 * wave + 4 * gq + i) * D + col] = Sk[i];
     }
     return;
   }
   put(rec(0) + R::SIN);
-  // M_s and B_s do not depend on the state: they are fetched two steps ahead
-  // into a ring of three register stages (the loop is unrolled by three so
-  // that the stages never move between registers).
   struct Stage {
-    typename Ops::MRaw m[RT][NWS];
-    f32x4 b[RT];
+    typename Ops::MRaw m[NKB];
+    f32x4 b;
   };
+  // Buffer loads: a step's record is one scalar resource, the lanes' byte
+  // offsets into it fixed registers, so the fetches take no per-lane address
+  // registers (64-bit address temporaries were placed over registers still
+  // being loaded, which made every fetch wait for the ones in flight).
+  const uint32_t m_off = (uint32_t)(R::M * 4 + R::frag(wave, 0, 0, lane));
+  const uint32_t b_off = (uint32_t)((R::B + R::tile(wave, ct, lane)) * 4);
+  constexpr int kRecBytes = (int)(R::FLOATS * 4), kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
   auto fetch = [&](int s, Stage& st) {
-    const float* r = rec(s);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(rec(s), (short)0, kRecBytes, kRsrcWord3);
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int kb = 0; kb < NWS; ++kb)
-        st.m[t][kb] = Ops::load_m((const unsigned char*)(r + R::M), RT * wave + t, kb, lane);
-#pragma unroll
-    for (int t = 0; t < RT; ++t) st.b[t] = *(const f32x4*)(r + R::B + R::tile(RT * wave + t, ct, lane));
+    for (int kb = 0; kb < NKB; ++kb) st.m[kb] = Ops::load_m(r, m_off, kb);
+    st.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, b_off, 0, 0));
+    // issued here, before the step's own temporaries are allocated (moved
+    // below them, a load's target registers were handed out as temporaries,
+    // whose writes then wait for the load)
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto step = [&](int s, const Stage& st) {
-    sS[s & 1][wave][lane] = Ops::state_frag(Sk);
+    Ops::publish(sS[s & 1], wave, lane, Sk);
     __syncthreads();
-    // two accumulators per row tile (even and odd k-blocks) keep the MFMA
-    // chains short
-    f32x4 acc[RT][2];
+    // two accumulators (even and odd k-blocks) keep the MFMA chains short
+    f32x4 acc0 = st.b, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      acc[t][0] = st.b[t];
-      acc[t][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < NKB; ++kb) {
+      const typename Ops::SFrag sf = Ops::gather(sS[s & 1], kb, lane);
+      if (kb & 1) acc1 = Ops::product(st.m[kb], sf, acc1);
+      else acc0 = Ops::product(st.m[kb], sf, acc0);
     }
-#pragma unroll
-    for (int kb = 0; kb < NWS; ++kb) {
-      const typename Ops::SFrag sf = sS[s & 1][kb][lane];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) acc[t][kb & 1] = Ops::product(st.m[t][kb], sf, acc[t][kb & 1]);
-    }
-#pragma unroll
-    for (int t = 0; t < RT; ++t) Sk[t] = acc[t][0] + acc[t][1];
+    Sk = acc0 + acc1;
     put(rec(s + 1) + R::SIN);
   };
   const int nsteps = nseg - 1;
   if (nsteps == 0) return;
   // Fetches past the last step re-read the last step's record (in bounds,
   // unused): unconditional loads keep the wait counts exact, so a step waits
-  // only for its own stage and never for the fetches issued after it.
+  // only for its own stage and never for the fetches issued after it.  A ring
+  // of three register stages (the loop unrolled by three, so that the stages
+  // never move between registers).
   auto clamp = [&](int s) { return s < nsteps ? s : nsteps - 1; };
+  // Unrolled by six (two turns of the ring), so that the conservative wait
+  // after the loop head (where the pending loads of the two incoming paths are
+  // merged) falls on one step in six.
   Stage b0, b1, b2;
   fetch(0, b0);
   fetch(clamp(1), b1);
-  for (int s = 0; s < nsteps; s += 3) {
+  for (int s = 0; s < nsteps; s += 6) {
     fetch(clamp(s + 2), b2);
     step(s, b0);
     if (s + 1 >= nsteps) break;
@@ -1325,6 +1385,15 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
     if (s + 2 >= nsteps) break;
     fetch(clamp(s + 4), b1);
     step(s + 2, b2);
+    if (s + 3 >= nsteps) break;
+    fetch(clamp(s + 5), b2);
+    step(s + 3, b0);
+    if (s + 4 >= nsteps) break;
+    fetch(clamp(s + 6), b0);
+    step(s + 4, b1);
+    if (s + 5 >= nsteps) break;
+    fetch(clamp(s + 7), b1);
+    step(s + 5, b2);
   }
 }
 
@@ -1357,7 +1426,7 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   if ((e = mark(1)) != hipSuccess) return (int)e;
   const int64_t pairs = (int64_t)n_rows * H;
   const int64_t blocks = (pairs + 7) / 8 * 8 * NR;
-  hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / ScanOps<T, D>::KB)), 0, stream,
+  hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / 16)), 0, stream,
                      h0, ht, wsf, cu, n_rows, T_per, H, L);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if ((e = mark(2)) != hipSuccess) return (int)e;
