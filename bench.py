@@ -21,9 +21,11 @@ algorithmic bytes (``LAUNCH_WORK``) divided by its mean duration, against HBM;
 ``call_roofline`` and ``mfma`` do the same for the whole call.
 ``cpu_baseline`` times the fp64 CPU oracle on the host cores (a baseline, not
 a target).  ``other_workloads`` times the packed 8-sequence batch and the
-1,048,576-token context.  Other legs: ``--copy-calib MiB`` runs only a device copy of known
-size (for scaling the HBM byte counters), ``--only prefill|decode`` runs one
-leg, ``--no-cpu`` skips the oracle.
+1,048,576-token context; ``states_workloads`` times the headline call with
+prefix-cache states (kda_chunk_forward_states) beside plain calls.  Other
+legs: ``--copy-calib MiB`` runs only a device copy of known size (for
+scaling the HBM byte counters), ``--only prefill|decode`` runs one leg,
+``--no-cpu`` skips the oracle.
 """
 from __future__ import annotations
 
@@ -230,6 +232,52 @@ def bench_workload(wid: int, calls: int):
             "mfma_frac": token_heads * FLOP_PER_TOKEN_HEAD / mean / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_states(calls: int):
+    """Prefix-cache states (kda_chunk_forward_states) on the headline workload:
+    the same calls with a state every 16 chunks (1,024 tokens) and every
+    chunk, timed beside plain calls on the same inputs, so that the
+    difference is the cost of the emission."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[1]
+    inp = synth.workload_inputs(w, device="cuda")
+    B, T, H, d = inp["q"].shape
+    ws = torch.empty(kda.workspace_bytes(B, T, H, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["q"])
+    ht = torch.empty_like(inp["h0"])
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    stream = torch.cuda.current_stream()
+
+    def mean_of(call):
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+
+    plain = mean_of(lambda: kda.chunk_forward(*args, h0=inp["h0"], o=o, ht=ht, workspace=ws))
+    out = []
+    for every in (16, 1):
+        st = torch.empty((B * (T // (64 * every)), H, d, d), dtype=torch.float32, device="cuda")
+        t = mean_of(lambda: kda.chunk_forward_states(*args, h0=inp["h0"], states_every=every, states=st, o=o,
+                                                     ht=ht, workspace=ws))
+        log(f"states every {every} chunks: {st.shape[0]} states, mean {t * 1e6:.1f} us (plain {plain * 1e6:.1f} us)")
+        out.append({"workload": f"{w.name} + a state every {64 * every} tokens", "states_every_chunks": every,
+                    "states": st.shape[0], "state_bytes": st.numel() * 4, "mean_call_us": t * 1e6,
+                    "plain_call_us": plain * 1e6, "overhead_us": (t - plain) * 1e6, "value": T / t,
+                    "unit": "tokens/s"})
+        del st
+    del inp, o, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(steps: int, warmup: int):
     import torch
     import gated_delta_rule_105_amd as kda
@@ -339,6 +387,7 @@ def main() -> int:
         # the packed 8-sequence batch and the million-token context, timed the
         # same way (secondary lines: the headline value is the workload above)
         out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3)]
+        out["states_workloads"] = bench_states(50)
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

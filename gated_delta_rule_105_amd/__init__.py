@@ -6,6 +6,7 @@ runs in the library's HIP kernels.  There is no CPU fallback: calling into a
 missing library raises.
 
     o, ht = chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None)
+    o, ht, states = chunk_forward_states(q, k, v, g, beta, states_every=16)
     o = decode_step(q, k, v, g, beta, state)          # state updated in place
 
 KDA is the gated delta rule with a channel-wise forget gate,
@@ -22,8 +23,8 @@ from ._lib import (CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_OK, ChunkD
                    status_string, version)
 from . import _lib
 
-__all__ = ["chunk_forward", "decode_step", "workspace_bytes", "make_desc", "KdaError",
-           "status_string", "version", "CHUNK_LAUNCHES"]
+__all__ = ["chunk_forward", "chunk_forward_states", "decode_step", "workspace_bytes", "make_desc",
+           "KdaError", "status_string", "version", "CHUNK_LAUNCHES"]
 
 
 def _torch():
@@ -89,6 +90,35 @@ def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
     events: optional len(CHUNK_LAUNCHES) + 1 raw hipEvent_t handles recorded
     around the call's launches (kda_chunk_forward_timed), for measurement.
     """
+    o, ht, _ = _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
+                        output_final_state, validate_cu, stream, events, None, 0)
+    return o, ht
+
+
+def chunk_forward_states(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
+                         g_floor: float = -0.125, *, states_every: int = 1, states=None, o=None, ht=None,
+                         workspace=None, output_final_state: bool = True, validate_cu: bool = True,
+                         stream=None) -> Tuple[object, object, object]:
+    """chunk_forward that also returns the state after every `states_every`
+    full chunks of each sequence (kda_chunk_forward_states): states is fp32
+    [count, H, d, d], the slots of each sequence consecutive and in order;
+    slot m - 1 of sequence n holds the state after its first
+    m * states_every * chunk tokens.  With packed sequences, count is an
+    upper bound and the slots past the last one written are left as given
+    (zeros when allocated here)."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    count = _lib.states_count(make_desc(B, T, H, d, q.dtype, n_seqs, chunk, g_floor), states_every)
+    if states is None:
+        states = torch.zeros((count, H, d, d), dtype=torch.float32, device=q.device)
+    _check_dev("states", states, torch.float32, (count, H, d, d))
+    return _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace, output_final_state,
+                    validate_cu, stream, None, states, states_every)
+
+
+def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace, output_final_state,
+             validate_cu, stream, events, states, states_every):
     torch = _torch()
     B, T, H, d = q.shape
     dt = q.dtype
@@ -119,14 +149,21 @@ def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     args = (desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
-            _ptr(ht), _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
-    if events is None:
-        st = _lib.chunk_forward_raw(*args)
+            _ptr(ht))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    if states is not None:
+        st = _lib.chunk_forward_states_raw(*args, _ptr(states) if states.numel() else None, states_every,
+                                           *tail)
+        what = "kda_chunk_forward_states"
+    elif events is None:
+        st = _lib.chunk_forward_raw(*args, *tail)
+        what = "kda_chunk_forward"
     else:
-        st = _lib.chunk_forward_timed_raw(*args, events)
+        st = _lib.chunk_forward_timed_raw(*args, *tail, events)
+        what = "kda_chunk_forward_timed"
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_forward" if events is None else "kda_chunk_forward_timed")
-    return o, ht
+        raise KdaError(st, what)
+    return o, ht, states
 
 
 def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, stream=None):

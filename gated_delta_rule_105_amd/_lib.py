@@ -22,7 +22,8 @@ KDA_DTYPE_BF16 = 1
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
-           "kda_chunk_forward", "kda_chunk_forward_timed", "kda_decode_step")
+           "kda_chunk_forward", "kda_chunk_forward_timed", "kda_chunk_forward_states_count",
+           "kda_chunk_forward_states", "kda_decode_step")
 
 # Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed).
 CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_scan", "kda_seg_forward")
@@ -67,6 +68,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_forward_timed.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp, ctypes.POINTER(vp)]
     lib.kda_chunk_forward_timed.restype = ctypes.c_int
+    lib.kda_chunk_forward_states_count.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.c_int, ctypes.POINTER(sz)]
+    lib.kda_chunk_forward_states_count.restype = ctypes.c_int
+    lib.kda_chunk_forward_states.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_forward_states.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -102,6 +108,21 @@ def chunk_forward_timed_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, ws
     arr = (ctypes.c_void_p * (len(CHUNK_LAUNCHES) + 1))(*events)
     return int(load().kda_chunk_forward_timed(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, ws,
                                               ctypes.c_size_t(ws_bytes), stream, arr))
+
+
+def states_count(desc: ChunkDesc, states_every: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().kda_chunk_forward_states_count(ctypes.byref(desc), int(states_every), ctypes.byref(out))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_forward_states_count")
+    return int(out.value)
+
+
+def chunk_forward_states_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, states, states_every, ws,
+                             ws_bytes, stream) -> int:
+    """Call kda_chunk_forward_states with raw integer addresses; returns the status."""
+    return int(load().kda_chunk_forward_states(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, states,
+                                               int(states_every), ws, ctypes.c_size_t(ws_bytes), stream))
 
 
 def decode_step_raw(N, H, d_k, d_v, dtype, g_floor, q, k, v, g, beta, state, o, stream) -> int:

@@ -75,6 +75,16 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   return KDA_OK;
 }
 
+// Slots of kda_chunk_forward_states (see include/kda.h); false for a bad
+// states_every.
+bool state_slots(const kda_chunk_desc_t* d, int every, size_t* slots) {
+  if (every < 1) return false;
+  const int64_t per = (int64_t)every * d->chunk;
+  const int64_t each = (int64_t)d->T / per;
+  *slots = (size_t)(d->n_seqs > 0 ? each : (int64_t)d->B * each);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,12 +111,38 @@ int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
   return KDA_OK;
 }
 
-static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
-                         const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
-                         void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+int kda_chunk_forward_states_count(const kda_chunk_desc_t* d, int states_every, size_t* count) {
+  if (!count) return KDA_ERR_INVALID_ARGUMENT;
   Sizes s;
   const int st = check_desc(d, &s);
   if (st != KDA_OK) return st;
+  if (!state_slots(d, states_every, count)) return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
+
+// states: NULL (no state emission) or the kda_chunk_forward_states buffer,
+// with every >= 1.
+static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+                         const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
+                         float* states, int every, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* events) {
+  Sizes s;
+  const int st = check_desc(d, &s);
+  if (st != KDA_OK) return st;
+  size_t states_bytes = 0;
+  if (states) {
+    size_t slots, per;
+    if (!state_slots(d, every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!mul((size_t)d->H * d->d_k, (size_t)d->d_v * 4, &per) || !mul(slots, per, &states_bytes))
+      return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(states, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
+    const Range rs = range(states, states_bytes);
+    const Range all[] = {range(q, s.x_bytes),     range(k, s.x_bytes),    range(v, s.x_bytes),
+                         range(g, s.x_bytes),     range(beta, s.beta_bytes), range(o, s.x_bytes),
+                         range(h0, s.state_bytes), range(ht, s.state_bytes), range(workspace, s.plan.ws_bytes)};
+    for (const Range& r : all)
+      if (overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
+  }
   const bool has_tokens = s.tokens > 0;
   if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
   if ((d->n_seqs > 0) != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARGUMENT;
@@ -142,18 +178,20 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
     for (const Range& r : all)
       if (overlap(rw, r)) return KDA_ERR_INVALID_ARGUMENT;
   }
-  if (!ht && s.tokens == 0 && !events) return KDA_OK;  // nothing to write
+  if (!ht && s.tokens == 0 && !events) return KDA_OK;  // nothing to write (no full chunk: no states either)
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
-                                          d->g_floor, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace,
-                                          stream, events);
+                                          d->g_floor, q, k, v, g, beta, h0, cu_seqlens, o, ht,
+                                          states_bytes > 0 ? states : nullptr, every, workspace, stream,
+                                          events);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
                       const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                       void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, workspace_bytes, stream, nullptr);
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, workspace, workspace_bytes, stream,
+                       nullptr);
 }
 
 int kda_chunk_forward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
@@ -161,7 +199,22 @@ int kda_chunk_forward_timed(const kda_chunk_desc_t* d, const void* q, const void
                             void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events) {
   if (!events) return KDA_ERR_INVALID_ARGUMENT;
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, workspace_bytes, stream, events);
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, workspace, workspace_bytes, stream,
+                       events);
+}
+
+int kda_chunk_forward_states(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                             const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                             void* o, float* ht, float* states, int states_every, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Sizes s;
+  const int st = check_desc(d, &s);  // before state_slots divides by the chunk
+  if (st != KDA_OK) return st;
+  size_t slots;
+  if (!state_slots(d, states_every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!states && slots > 0) return KDA_ERR_INVALID_ARGUMENT;
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, states, states_every, workspace,
+                       workspace_bytes, stream, nullptr);
 }
 
 int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor, const void* q,

@@ -122,14 +122,16 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
 constexpr int kLaunches = 3;  // chunk pass (with the segment maps), segment scan, output pass
 
 // Enqueue the chunked forward.  All arguments were validated by the caller.
-// n_rows: number of sequences (n_seqs, or B when cu == nullptr).  events:
-// null, or kLaunches + 1 hipEvent_t handles (entries may be null) recorded
-// on the stream before each launch and after the last.  Returns a hipError_t.
+// n_rows: number of sequences (n_seqs, or B when cu == nullptr).  states:
+// null, or the state slots of kda_chunk_forward_states, one every `every`
+// chunks.  events: null, or kLaunches + 1 hipEvent_t handles (entries may be
+// null) recorded on the stream before each launch and after the last.
+// Returns a hipError_t.
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan,
                          float g_floor, const void* q, const void* k, const void* v,
                          const void* g, const float* beta, const float* h0,
-                         const int32_t* cu, void* o, float* ht, void* ws, void* stream,
-                         void* const* events);
+                         const int32_t* cu, void* o, float* ht, float* states, int every,
+                         void* ws, void* stream, void* const* events);
 
 // Enqueue one decode step.  Returns a hipError_t.
 int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor,

@@ -1137,17 +1137,19 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   }
 }
 
-// ---- pass 4: outputs from every segment's incoming state -----------------
-// Reads the chunk records, double-buffered like pass 2; wave w owns the
+// ---- pass 3: outputs from every segment's incoming state -----------------
+// Reads the chunk records into two LDS image buffers; wave w owns the
 // value-column tiles w + NW x, x < CT.  O is staged at the start of the
 // current image (Wk and Kh^T fragments, dead after the products) so that the
 // global stores are whole 16-byte pieces of rows.  The next chunk's image is
-// issued piecewise between the row blocks of the state step.
+// issued piecewise between the row blocks of the state step.  With `states`,
+// the state after every `every`-th full chunk of a sequence goes to its slot
+// (the prefix-cache states of kda_chunk_forward_states).
 template <typename T, int D, int NW, int CT>
 __global__ void __launch_bounds__(64 * NW)
 kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
                 const float* __restrict__ ws, const unsigned char* __restrict__ crec, T* __restrict__ o,
-                float* ht) {
+                float* ht, float* __restrict__ states, int every) {
   typedef Lds<T, D> M;
   typedef CRec<T, D> CR;
   typedef Img<T, D> I;
@@ -1181,6 +1183,25 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
   for (int c = 0; c < CT; ++c)
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) S[c][rr] = *(const f32x4*)(sin + R::tile(rr, wave + NW * c, lane));
+  // this wave's columns of S, row-major [D][D] at dst (ht and the states)
+  auto put_state = [&](float* dst) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx] = S[c][rr][i];
+  };
+  // first state slot of this sequence: full state periods of the earlier ones
+  const int64_t period = (int64_t)C * every;
+  int64_t slot0 = 0;
+  if (states) {
+    if (cu) {
+      for (int m = 0; m < sg.n; ++m) slot0 += (cu[m + 1] - cu[m]) / period;
+    } else {
+      slot0 = (int64_t)sg.n * (T_per / period);
+    }
+  }
 
   for (int j = j0; j < j1; ++j) {
     const int clen = min(C, sg.len - C * j);
@@ -1212,6 +1233,8 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
           sO[(16 * rt + 4 * gq + i) * M::LDT + 16 * (wave + NW * c) + idx] = Elem<T>::from_f32(O[c][rt][i]);
     lds_barrier();
     Raw<T, D, NT, true>::store_out(cur, o, tokc, clen, H, h, tid);
+    if (states && (j + 1) % every == 0 && (int64_t)(j + 1) * C <= sg.len)
+      put_state(states + ((size_t)(slot0 + (j + 1) / every - 1) * H + h) * D * D);
     if (j + 1 < j1) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
@@ -1219,19 +1242,10 @@ kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, in
         for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wvn[c][rt];
     }
   }
-  if (ht && sg.s == sg.nseg - 1) {
-    float* dst = ht + ((size_t)sg.n * H + h) * D * D;
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx] = S[c][rr][i];
-  }
+  if (ht && sg.s == sg.nseg - 1) put_state(ht + ((size_t)sg.n * H + h) * D * D);
 }
 
-// ---- pass 3: segment scan S_{s+1} = M_s S_s + B_s ------------------------
+// ---- pass 2: segment scan S_{s+1} = M_s S_s + B_s ------------------------
 // Workgroup = (sequence, head, 16 state columns), one wave per 16-row tile of
 // S.  Each step a wave publishes its rows as halves of B-operand fragments
 // through a double-buffered LDS area and forms the same rows of the next state
@@ -1400,7 +1414,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
 template <typename T, int D, int NW, int NW2>
 int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
                  const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
-                 float* ht, void* ws, hipStream_t stream, void* const* events) {
+                 float* ht, float* states, int every, void* ws, hipStream_t stream, void* const* events) {
   constexpr int NR = D / 16;
   const int L = plan.seg_chunks;
   float* wsf = (float*)ws;
@@ -1432,7 +1446,8 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   if ((e = mark(2)) != hipSuccess) return (int)e;
   if (has_segments) {
     hipLaunchKernelGGL((kda_seg_forward<T, D, NW2, NR / NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2),
-                       0, stream, cu, n_rows, T_per, H, L, (const float*)wsf, (const unsigned char*)crec, (T*)o, ht);
+                       0, stream, cu, n_rows, T_per, H, L, (const float*)wsf, (const unsigned char*)crec, (T*)o, ht,
+                       states, every);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   return (int)mark(3);
@@ -1442,18 +1457,18 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
 
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan, float g_floor,
                          const void* q, const void* k, const void* v, const void* g, const float* beta,
-                         const float* h0, const int32_t* cu, void* o, float* ht, void* ws, void* stream,
-                         void* const* events) {
+                         const float* h0, const int32_t* cu, void* o, float* ht, float* states, int every,
+                         void* ws, void* stream, void* const* events) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s,
-                                          events);
+    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, states,
+                                          every, ws, s, events);
   if (is_bf16 && d == 128)
     return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0,
-                                                               cu, o, ht, ws, s, events);
+                                                               cu, o, ht, states, every, ws, s, events);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, ws, s,
-                                         events);
+    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, states,
+                                         every, ws, s, events);
   return (int)hipErrorInvalidValue;
 }
 

@@ -140,6 +140,42 @@ int kda_chunk_forward_timed(const kda_chunk_desc_t* d,
                             void* stream, void* const* events);
 
 /*
+ * States at chunk boundaries, for prefix caching (the system side of a
+ * long-context KDA model keeps KDA states and a prefix cache: "3 分钟看懂
+ * Kimi K3" (landx.limxdynamics.com), section "第一条主线", the paragraph after
+ * Figure 3).
+ *
+ * kda_chunk_forward_states_count: host only.  *count = the number of state
+ * slots kda_chunk_forward_states may write for this descriptor and
+ * states_every (>= 1, in chunks): B * floor(T / (states_every * chunk)) for
+ * a fixed-length batch, floor(T / (states_every * chunk)) for a packed one
+ * (an upper bound there: the lengths live on the device).
+ *
+ * kda_chunk_forward_states: kda_chunk_forward, and in addition, for every
+ * sequence n in order and every m >= 1 with m * states_every * chunk <=
+ * len_n, the state after the first m * states_every * chunk tokens of the
+ * sequence (what ht would be for that prefix, so a later call can resume
+ * from it as h0) is written to
+ *   states[slot]  : [H, d_k, d_v] fp32, row-major like ht,
+ *   slot = (slots of sequences 0 .. n-1) + m - 1,
+ * i.e. states is [count, H, d_k, d_v] with the slots of each sequence
+ * consecutive; slots past the last one written are left untouched.
+ * states: device buffer of at least count * H * d_k * d_v floats, 16-byte
+ * aligned, overlapping no other buffer; it may be NULL only when count is 0.
+ * Returns what kda_chunk_forward returns, and KDA_ERR_INVALID_ARGUMENT for
+ * states_every < 1 or a states buffer that breaks the rules above.
+ */
+int kda_chunk_forward_states_count(const kda_chunk_desc_t* d, int states_every, size_t* count);
+int kda_chunk_forward_states(const kda_chunk_desc_t* d,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const float* beta, const float* h0,
+                             const int32_t* cu_seqlens,
+                             void* o, float* ht,
+                             float* states, int states_every,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * One decode step: one new token for each of N sequences, state resident
  * in device memory and updated IN PLACE.  For every (n, h):
  *     S' = diag(alpha) S;  u = beta (v - S'^T k);  S <- S' + k u^T;

@@ -187,3 +187,52 @@ def test_chunk_forward_timed_needs_events(lib):
     assert _lib.chunk_forward_timed_raw(desc(d_k=96, d_v=96), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
                                         a["cu"], a["o"], a["ht"], a["ws"], a["ws_bytes"], None,
                                         [None] * (len(_lib.CHUNK_LAUNCHES) + 1)) == KDA_ERR_UNSUPPORTED
+
+
+def states_count(lib, d, every):
+    out = ctypes.c_size_t(0)
+    st = lib.kda_chunk_forward_states_count(ctypes.byref(d), every, ctypes.byref(out))
+    return st, out.value
+
+
+def test_states_count(lib):
+    # B * floor(T / (every * 64)) for a fixed-length batch, floor(T / (every * 64)) when packed
+    assert states_count(lib, desc(B=3, T=300), 1) == (KDA_OK, 12)
+    assert states_count(lib, desc(B=3, T=300), 2) == (KDA_OK, 6)
+    assert states_count(lib, desc(B=3, T=300), 5) == (KDA_OK, 0)
+    assert states_count(lib, desc(T=1000, n_seqs=4), 3) == (KDA_OK, 5)
+    assert states_count(lib, desc(T=4096), 16) == (KDA_OK, 4)
+    assert states_count(lib, desc(), 0)[0] == KDA_ERR_INVALID_ARGUMENT
+    assert states_count(lib, desc(chunk=0), 1)[0] == KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_chunk_forward_states_count(ctypes.byref(desc()), 1, None) == KDA_ERR_INVALID_ARGUMENT
+
+
+def call_states(lib, d, a, states, every):
+    return _lib.chunk_forward_states_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["o"],
+                                         a["ht"], states, every, a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("where,every", [
+    (None, 1),        # slots to write but no buffer
+    ("misaligned", 1),
+    ("free", 0),      # states_every < 1
+    ("o", 1),         # overlaps o
+    ("ws", 1),        # overlaps the workspace
+    ("h0", 1),        # overlaps h0
+])
+def test_chunk_forward_states_rejects(lib, where, every):
+    d = desc()
+    a = fake_args(lib, d)
+    free = 11 * 64 * GB
+    states = {None: None, "misaligned": free + 8, "free": free, "o": a["o"] + 4096, "ws": a["ws"] + 4096,
+              "h0": a["h0"] - 4096}[where]
+    assert call_states(lib, d, a, states, every) == KDA_ERR_INVALID_ARGUMENT
+
+
+def test_chunk_forward_states_empty(lib):
+    # no full chunk: no slots, so no buffer is needed; nothing to launch
+    d = desc(T=0)
+    a = fake_args(lib, d)
+    a["ht"] = None
+    assert call_states(lib, d, a, None, 1) == KDA_OK
+    assert call_states(lib, desc(d_k=96, d_v=96), fake_args(lib, desc()), 11 * 64 * GB, 1) == KDA_ERR_UNSUPPORTED

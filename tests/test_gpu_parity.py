@@ -10,7 +10,7 @@ import torch
 import gated_delta_rule_105_amd as kda
 import oracle
 import synth
-from gpu_util import TOL, f64, gpu_forward, note, oracle_forward, rel_err
+from gpu_util import TOL, f64, gpu_forward, note, oracle_forward, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,84 @@ def test_config3_full_sampled():
     eh = rel_err(ht_s, rht[:, 0])
     print(f"workload3 head {h}: err_o={eo:.3e} err_ht={eh:.3e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+# ---------------------------------------- states at chunk boundaries
+def _prefix_states(inp, every):
+    """Expected emitted states from the oracle: its final state on the first
+    m * every * 64 tokens of each sequence (m = 1, 2, ...), in slot order."""
+    B, T, H, d = inp["q"].shape
+    cu = inp.get("cu_seqlens")
+    if cu is None:
+        seqs = [(n, n, 0, T) for n in range(B)]  # (sequence, row, start, length)
+    else:
+        c = cu.tolist()
+        seqs = [(n, 0, c[n], c[n + 1] - c[n]) for n in range(len(c) - 1)]
+    h0 = inp.get("h0")
+    out = []
+    for n, row, s0, ln in seqs:
+        for m in range(1, ln // (64 * every) + 1):
+            p = m * 64 * every
+            sub = {key: inp[key][row:row + 1, s0:s0 + p].contiguous() for key in ("q", "k", "v", "g", "beta")}
+            sub["h0"] = None if h0 is None else h0[n:n + 1]
+            sub["g_floor"] = inp.get("g_floor", -0.125)
+            out.append(oracle_forward(sub)[1][0])
+    return np.stack(out) if out else np.zeros((0, H, d, d))
+
+
+STATES = {
+    # fused segments of one chunk; every chunk boundary
+    "bf16-d128-B2-T300-every1": (lambda: _case(2, 300, 2, 128, "bf16", wid=160), 1),
+    # packed, one segment per sequence (no maps), empty and short sequences
+    "f32-d64-varlen-every1": (lambda: _case(1, 0, 2, 64, "f32", lengths=[5, 0, 128, 70, 200], wid=161), 1),
+    # long fused segments, a period that does not divide the segment length
+    "bf16-d64-T8192-weak-every3": (lambda: _case(1, 8192, 2, 64, "bf16", g_mode="weak", wid=162), 3),
+    # packed and fused: sequences with and without maps and states
+    "bf16-d128-varlen-long-every5": (lambda: _case(1, 0, 2, 128, "bf16", g_mode="weak",
+                                                   lengths=[3000, 1, 4096, 0, 777], wid=163), 5),
+    # the bench shape, a state every 1024 tokens
+    "bf16-d128-T4096-H16-every16": (lambda: synth.workload_inputs(synth.WORKLOADS[1]), 16),
+}
+
+
+@pytest.mark.parametrize("name", list(STATES))
+def test_chunk_forward_states(name):
+    make, every = STATES[name]
+    inp = make()
+    dtype = "bf16" if inp["q"].dtype == torch.bfloat16 else "f32"
+    note(f"chunk_forward_states {name} q{tuple(inp['q'].shape)} every {every}")
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    kw = dict(h0=d.get("h0"), cu_seqlens=d.get("cu_seqlens"))
+    o, ht, st = kda.chunk_forward_states(*args, states_every=every, **kw)
+    o2, ht2 = kda.chunk_forward(*args, **kw)
+    torch.cuda.synchronize()
+    # the emission changes nothing else
+    assert torch.equal(o, o2) and torch.equal(ht, ht2)
+    ref = _prefix_states(inp, every)
+    n = ref.shape[0]
+    assert st.shape[0] >= n
+    e = rel_err(f64(st[:n]), ref) if n else 0.0
+    print(f"{name}: {n} states, err={e:.3e}")
+    assert e <= TOL[dtype]
+    assert not st[n:].any()  # slots past the last one stay as allocated
+
+
+def test_resume_from_emitted_state():
+    """Prefix caching: a later call on the rest of the sequence, started from
+    an emitted state, gives the outputs and final state of the whole run."""
+    inp = _case(1, 1500, 3, 128, "bf16", wid=164)
+    note("chunk_forward_states resume T=1500 every 4")
+    d = to_dev(inp)
+    o, ht, st = kda.chunk_forward_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], states_every=4)
+    cut = 2 * 4 * 64  # after slot 1
+    rest = {key: d[key][:, cut:].contiguous() for key in ("q", "k", "v", "g", "beta")}
+    o2, ht2 = kda.chunk_forward(rest["q"], rest["k"], rest["v"], rest["g"], rest["beta"], h0=st[1:2].contiguous())
+    torch.cuda.synchronize()
+    ro, rht = oracle_forward(inp)
+    e_o, e_h = rel_err(f64(o2), ro[:, cut:]), rel_err(f64(ht2), rht)
+    print(f"resume at {cut}: err_o={e_o:.3e} err_ht={e_h:.3e}")
+    assert e_o <= TOL["bf16"] and e_h <= TOL["bf16"]
 
 
 # ------------------------------------------------------------------ decode
