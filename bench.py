@@ -22,7 +22,9 @@ algorithmic bytes (``LAUNCH_WORK``) divided by its mean duration, against HBM;
 ``cpu_baseline`` times the fp64 CPU oracle on the host cores (a baseline, not
 a target).  ``other_workloads`` times the packed 8-sequence batch and the
 1,048,576-token context; ``states_workloads`` times the headline call with
-prefix-cache states (kda_chunk_forward_states) beside plain calls.  Other
+prefix-cache states (kda_chunk_forward_states) beside plain calls;
+``gate_workloads`` times Gated DeltaNet and DeltaNet gates beside KDA on the
+prefill and decode workloads.  Other
 legs: ``--copy-calib MiB`` runs only a device copy of known size (for
 scaling the HBM byte counters), ``--only prefill|decode`` runs one leg,
 ``--no-cpu`` skips the oracle.
@@ -278,6 +280,59 @@ def bench_states(calls: int):
     return out
 
 
+def bench_gates(calls: int, steps: int):
+    """The gate variants beside KDA on the same inputs: Gated DeltaNet (one
+    log-decay per token and head: channel 0 of the KDA gate) and DeltaNet (no
+    decay), on the headline prefill workload and on the decode workload."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    stream = torch.cuda.current_stream()
+
+    def mean_of(call, n):
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n * 1e-3
+
+    w = synth.WORKLOADS[1]
+    inp = synth.workload_inputs(w, device="cuda")
+    B, T, H, d = inp["q"].shape
+    ws = torch.empty(kda.workspace_bytes(B, T, H, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["q"])
+    ht = torch.empty_like(inp["h0"])
+    gates = {"kda": inp["g"], "gated-deltanet": inp["g"][..., 0].contiguous(), "deltanet": None}
+    out = []
+    for name, g in gates.items():
+        t = mean_of(lambda: kda.chunk_forward(inp["q"], inp["k"], inp["v"], g, inp["beta"], h0=inp["h0"], o=o,
+                                              ht=ht, workspace=ws), calls)
+        log(f"prefill gate {name}: mean {t * 1e6:.1f} us")
+        out.append({"workload": f"{w.name} gate={name}", "mean_call_us": t * 1e6, "value": T / t,
+                    "unit": "tokens/s"})
+    del inp, o, ws, gates
+    N, H, d, wid = (DECODE[k] for k in ("N", "H", "d", "wid"))
+    dec = synth.decode_inputs(N, H, d, d, 1, "bf16", wid=wid, device="cuda")
+    state = dec["state"]
+    od = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda")
+    gates = {"kda": dec["g"][0], "gated-deltanet": dec["g"][0][..., 0].contiguous(), "deltanet": None}
+    for name, g in gates.items():
+        t = mean_of(lambda: kda.decode_step(dec["q"][0], dec["k"][0], dec["v"][0], g, dec["beta"][0], state, o=od),
+                    steps)
+        bytes_step = 2 * N * H * d * d * 4
+        log(f"decode gate {name}: mean step {t * 1e6:.1f} us")
+        out.append({"workload": f"kda-decode-bf16-N{N}-H{H}-d{d} gate={name}", "mean_step_us": t * 1e6,
+                    "value": 1.0 / t, "unit": "steps/s", "hbm_frac": bytes_step / t / 1e9 / PEAK_HBM_GBS})
+    del dec, state
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(steps: int, warmup: int):
     import torch
     import gated_delta_rule_105_amd as kda
@@ -388,6 +443,7 @@ def main() -> int:
         # same way (secondary lines: the headline value is the workload above)
         out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3)]
         out["states_workloads"] = bench_states(50)
+        out["gate_workloads"] = bench_gates(50, 100)
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

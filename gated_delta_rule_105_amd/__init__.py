@@ -9,6 +9,9 @@ missing library raises.
     o, ht, states = chunk_forward_states(q, k, v, g, beta, states_every=16)
     o = decode_step(q, k, v, g, beta, state)          # state updated in place
 
+g selects the gate: [.., H, d] one log-decay per key channel (KDA), [.., H]
+one per head (Gated DeltaNet), None no decay (DeltaNet).
+
 KDA is the gated delta rule with a channel-wise forget gate,
 S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
 o_t = S_t^T q_t, alpha_t = exp(max(g_t, g_floor)) ("Kimi K3 深度拆解"
@@ -19,8 +22,8 @@ from __future__ import annotations
 
 from typing import Optional, Tuple
 
-from ._lib import (CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_OK, ChunkDesc, KdaError,
-                   status_string, version)
+from ._lib import (CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,
+                   KDA_GATE_NONE, KDA_OK, ChunkDesc, KdaError, status_string, version)
 from . import _lib
 
 __all__ = ["chunk_forward", "chunk_forward_states", "decode_step", "workspace_bytes", "make_desc",
@@ -59,9 +62,20 @@ def _check_dev(name, t, dtype=None, shape=None):
 
 
 def make_desc(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
-              g_floor: float = -0.125) -> ChunkDesc:
+              g_floor: float = -0.125, gate: int = KDA_GATE_CHANNEL) -> ChunkDesc:
     return ChunkDesc(B=B, T=T, H=H, d_k=d, d_v=d, chunk=chunk, n_seqs=n_seqs,
-                     dtype=_dtype_code(dtype), g_floor=g_floor)
+                     dtype=_dtype_code(dtype), g_floor=g_floor, gate=gate)
+
+
+def _gate_of(g, full_dims: int) -> int:
+    """Gate layout from g: per channel (full_dims dims), per head (one fewer), none."""
+    if g is None:
+        return KDA_GATE_NONE
+    if g.dim() == full_dims:
+        return KDA_GATE_CHANNEL
+    if g.dim() == full_dims - 1:
+        return KDA_GATE_HEAD
+    raise ValueError(f"g must have {full_dims} (per channel) or {full_dims - 1} (per head) dims, or be None")
 
 
 def workspace_bytes(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
@@ -83,7 +97,8 @@ def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
                   stream=None, events=None) -> Tuple[object, object]:
     """Chunked KDA forward over whole sequences.
 
-    q, k, g: [B, T, H, d]; v: [B, T, H, d] (bf16 or fp32); beta: [B, T, H] fp32.
+    q, k: [B, T, H, d]; v: [B, T, H, d] (bf16 or fp32); beta: [B, T, H] fp32.
+    g: [B, T, H, d] (KDA), [B, T, H] (Gated DeltaNet) or None (DeltaNet).
     cu_seqlens: int32 device tensor [n+1] for n packed sequences (B == 1).
     h0: fp32 [S, H, d, d] or None.  Returns (o [B, T, H, d], ht [S, H, d, d]
     fp32, or None when output_final_state is False).
@@ -123,8 +138,10 @@ def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
     B, T, H, d = q.shape
     dt = q.dtype
     _check_dev("q", q, dt)
-    for name, t in (("k", k), ("g", g), ("v", v)):
+    for name, t in (("k", k), ("v", v)):
         _check_dev(name, t, dt, (B, T, H, d))
+    gate = _gate_of(g, 4)
+    _check_dev("g", g, dt, (B, T, H, d) if gate == KDA_GATE_CHANNEL else (B, T, H))
     _check_dev("beta", beta, torch.float32, (B, T, H))
     n_seqs = 0
     if cu_seqlens is not None:
@@ -136,7 +153,7 @@ def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
             check_cu_seqlens(cu_seqlens.cpu(), T)
     S = n_seqs if n_seqs else B
     _check_dev("h0", h0, torch.float32, (S, H, d, d))
-    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor)
+    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor, gate)
     ws_bytes = _lib.workspace_size(desc)
     if o is None:
         o = torch.empty((B, T, H, d), dtype=dt, device=q.device)
@@ -168,13 +185,16 @@ def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
 
 def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, stream=None):
     """One decode step for N sequences; ``state`` [N, H, d, d] fp32 is updated
-    in place.  q, k, v, g: [N, H, d]; beta: [N, H] fp32.  Returns o [N, H, d]."""
+    in place.  q, k, v: [N, H, d]; g: [N, H, d] (KDA), [N, H] (Gated
+    DeltaNet) or None (DeltaNet); beta: [N, H] fp32.  Returns o [N, H, d]."""
     torch = _torch()
     N, H, d = q.shape
     dt = q.dtype
     _check_dev("q", q, dt)
-    for name, t in (("k", k), ("g", g), ("v", v)):
+    for name, t in (("k", k), ("v", v)):
         _check_dev(name, t, dt, (N, H, d))
+    gate = _gate_of(g, 3)
+    _check_dev("g", g, dt, (N, H, d) if gate == KDA_GATE_CHANNEL else (N, H))
     _check_dev("beta", beta, torch.float32, (N, H))
     _check_dev("state", state, torch.float32, (N, H, d, d))
     if o is None:
@@ -182,7 +202,7 @@ def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, str
     _check_dev("o", o, dt, (N, H, d))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = _lib.decode_step_raw(N, H, d, d, _dtype_code(dt), g_floor, _ptr(q), _ptr(k), _ptr(v),
+    st = _lib.decode_step_raw(N, H, d, d, _dtype_code(dt), gate, g_floor, _ptr(q), _ptr(k), _ptr(v),
                               _ptr(g), _ptr(beta), _ptr(state), _ptr(o), stream)
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")

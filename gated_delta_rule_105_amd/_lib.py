@@ -19,6 +19,9 @@ KDA_ERR_WORKSPACE_TOO_SMALL = 3
 KDA_ERR_HIP = 4
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
+KDA_GATE_CHANNEL = 0   # g [.., H, d_k]: KDA
+KDA_GATE_HEAD = 1      # g [.., H]: Gated DeltaNet
+KDA_GATE_NONE = 2      # no g: DeltaNet
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
@@ -39,7 +42,8 @@ class ChunkDesc(ctypes.Structure):
     """Mirror of kda_chunk_desc_t."""
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("chunk", ctypes.c_int),
-                ("n_seqs", ctypes.c_int), ("dtype", ctypes.c_int), ("g_floor", ctypes.c_float)]
+                ("n_seqs", ctypes.c_int), ("dtype", ctypes.c_int), ("g_floor", ctypes.c_float),
+                ("gate", ctypes.c_int)]
 
 
 _lib = None
@@ -74,7 +78,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                                              vp, ctypes.c_int, vp, sz, vp]
     lib.kda_chunk_forward_states.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -125,7 +129,7 @@ def chunk_forward_states_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, s
                                                int(states_every), ws, ctypes.c_size_t(ws_bytes), stream))
 
 
-def decode_step_raw(N, H, d_k, d_v, dtype, g_floor, q, k, v, g, beta, state, o, stream) -> int:
+def decode_step_raw(N, H, d_k, d_v, dtype, gate, g_floor, q, k, v, g, beta, state, o, stream) -> int:
     """Call kda_decode_step with raw integer addresses; returns the status."""
-    return int(load().kda_decode_step(N, H, d_k, d_v, dtype, ctypes.c_float(g_floor), q, k, v, g,
+    return int(load().kda_decode_step(N, H, d_k, d_v, dtype, gate, ctypes.c_float(g_floor), q, k, v, g,
                                       beta, state, o, stream))

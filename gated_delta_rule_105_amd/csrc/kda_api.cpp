@@ -10,6 +10,10 @@
 
 #include "kda_launch.h"
 
+static_assert(KDA_GATE_CHANNEL == kda::kGateChannel && KDA_GATE_HEAD == kda::kGateHead &&
+                  KDA_GATE_NONE == kda::kGateNone,
+              "gate codes of the C ABI and the kernels agree");
+
 namespace {
 
 constexpr size_t kAlign = 16;
@@ -38,7 +42,8 @@ size_t elem_size(kda_dtype_t t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
 struct Sizes {
   size_t tokens;      // B * T
   size_t n_states;    // sequences
-  size_t x_bytes;     // one of q, k, v, g, o
+  size_t x_bytes;     // one of q, k, v, o (and g with channel gates)
+  size_t g_bytes;     // g for the descriptor's gate (0 without one)
   size_t beta_bytes;
   size_t state_bytes; // h0 or ht
   kda::SegPlan plan;  // segments and workspace
@@ -49,6 +54,8 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   if (d->B < 1 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1 || d->n_seqs < 0)
     return KDA_ERR_INVALID_ARGUMENT;
   if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->gate != KDA_GATE_CHANNEL && d->gate != KDA_GATE_HEAD && d->gate != KDA_GATE_NONE)
+    return KDA_ERR_INVALID_ARGUMENT;
   if (d->n_seqs > 0 && d->B != 1) return KDA_ERR_INVALID_ARGUMENT;
   if (!(d->g_floor >= -1.0f && d->g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;  // NaN fails too
   if ((double)d->chunk * -(double)d->g_floor > 16.0) return KDA_ERR_INVALID_ARGUMENT;
@@ -64,6 +71,7 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   if (!mul(s->tokens, H, &th) || !mul(th, D, &x) || !mul(x, elem_size(d->dtype), &s->x_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
   if (!mul(th, 4, &s->beta_bytes)) return KDA_ERR_INVALID_ARGUMENT;
+  s->g_bytes = d->gate == KDA_GATE_CHANNEL ? s->x_bytes : d->gate == KDA_GATE_HEAD ? th * elem_size(d->dtype) : 0;
   size_t sh, sd;
   if (!mul(s->n_states, H, &sh) || !mul(sh, D * D, &sd) || !mul(sd, 4, &s->state_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
@@ -138,13 +146,15 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
     if (!aligned(states, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
     const Range rs = range(states, states_bytes);
     const Range all[] = {range(q, s.x_bytes),     range(k, s.x_bytes),    range(v, s.x_bytes),
-                         range(g, s.x_bytes),     range(beta, s.beta_bytes), range(o, s.x_bytes),
+                         range(g, s.g_bytes),     range(beta, s.beta_bytes), range(o, s.x_bytes),
                          range(h0, s.state_bytes), range(ht, s.state_bytes), range(workspace, s.plan.ws_bytes)};
     for (const Range& r : all)
       if (overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
   }
   const bool has_tokens = s.tokens > 0;
-  if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  const bool gated = d->gate != KDA_GATE_NONE;
+  if (!gated) g = nullptr;  // not read
+  if (has_tokens && (!q || !k || !v || (gated && !g) || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
   if ((d->n_seqs > 0) != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
   for (const void* p : ptrs)
@@ -158,21 +168,21 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
   if (has_tokens) {
     const Range ro = range(o, s.x_bytes);
     const Range ins[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes),
-                         range(g, s.x_bytes), range(beta, s.beta_bytes), range(h0, s.state_bytes)};
+                         range(g, s.g_bytes), range(beta, s.beta_bytes), range(h0, s.state_bytes)};
     for (const Range& r : ins)
       if (overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
   }
   if (ht) {
     const Range rh = range(ht, s.state_bytes);
     const Range others[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes),
-                            range(g, s.x_bytes), range(beta, s.beta_bytes), range(o, s.x_bytes)};
+                            range(g, s.g_bytes), range(beta, s.beta_bytes), range(o, s.x_bytes)};
     for (const Range& r : others)
       if (overlap(rh, r)) return KDA_ERR_INVALID_ARGUMENT;
     if (h0 && h0 != ht && overlap(rh, range(h0, s.state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
   }
   if (workspace && ws_need > 0) {
     const Range rw = range(workspace, ws_need);
-    const Range all[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes), range(g, s.x_bytes),
+    const Range all[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes), range(g, s.g_bytes),
                          range(beta, s.beta_bytes), range(o, s.x_bytes), range(h0, s.state_bytes),
                          range(ht, s.state_bytes)};
     for (const Range& r : all)
@@ -181,7 +191,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
   if (!ht && s.tokens == 0 && !events) return KDA_OK;  // nothing to write (no full chunk: no states either)
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
-                                          d->g_floor, q, k, v, g, beta, h0, cu_seqlens, o, ht,
+                                          d->g_floor, (int)d->gate, q, k, v, g, beta, h0, cu_seqlens, o, ht,
                                           states_bytes > 0 ? states : nullptr, every, workspace, stream,
                                           events);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
@@ -217,30 +227,34 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d, const void* q, const voi
                        workspace_bytes, stream, nullptr);
 }
 
-int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor, const void* q,
-                    const void* k, const void* v, const void* g, const float* beta, float* state, void* o,
-                    void* stream) {
+int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate, float g_floor,
+                    const void* q, const void* k, const void* v, const void* g, const float* beta, float* state,
+                    void* o, void* stream) {
   if (N < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARGUMENT;
   if (!(g_floor >= -1.0f && g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
-  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
+  const bool gated = gate != KDA_GATE_NONE;
+  if (!gated) g = nullptr;  // not read
+  if (!q || !k || !v || (gated && !g) || !beta || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {q, k, v, g, beta, state, o};
   for (const void* p : ptrs)
-    if (!aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
+    if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
   size_t nh, x, xb, sb, bb;
   if (!mul((size_t)N, (size_t)H, &nh) || !mul(nh, (size_t)d_k, &x) || !mul(x, elem_size(dtype), &xb) ||
       !mul(x, (size_t)d_k * 4, &sb) || !mul(nh, 4, &bb))
     return KDA_ERR_INVALID_ARGUMENT;
   if (nh > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const size_t gb = gate == KDA_GATE_CHANNEL ? xb : gate == KDA_GATE_HEAD ? nh * elem_size(dtype) : 0;
   const Range rs = range(state, sb), ro = range(o, xb);
-  const Range ins[] = {range(q, xb), range(k, xb), range(v, xb), range(g, xb), range(beta, bb)};
+  const Range ins[] = {range(q, xb), range(k, xb), range(v, xb), range(g, gb), range(beta, bb)};
   for (const Range& r : ins)
     if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
   if (overlap(rs, ro)) return KDA_ERR_INVALID_ARGUMENT;
-  const int e = kda::launch_decode_step(dtype == KDA_DTYPE_BF16, d_k, N, H, g_floor, q, k, v, g, beta,
-                                        state, o, stream);
+  const int e = kda::launch_decode_step(dtype == KDA_DTYPE_BF16, d_k, N, H, g_floor, (int)gate, q, k, v, g,
+                                        beta, state, o, stream);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -41,7 +41,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(DecodeShape<D>::NTH)
 kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
            const T* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-           T* __restrict__ o, float g_floor) {
+           T* __restrict__ o, float g_floor, int gate) {
   constexpr int NTH = DecodeShape<D>::NTH;
   constexpr int CPR = D / 4;         // float4 columns per row
   constexpr int RP = NTH / CPR;      // rows per pass (row groups)
@@ -65,7 +65,8 @@ kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   for (int i = 0; i < NI; ++i) s[i] = __builtin_nontemporal_load(&S[(rg + RP * i) * CPR + cg]);
 
   if (tid < D) {
-    float gg = ldf(g + nh * D + tid);
+    // one log-decay per channel, one per head for every channel, or none
+    float gg = gate == kGateChannel ? ldf(g + nh * D + tid) : gate == kGateHead ? ldf(g + nh) : 0.f;
     gg = gg < g_floor ? g_floor : gg;  // NaN stays NaN
     sA[tid] = __expf(gg);
     sK[tid] = ldf(k + nh * D + tid);
@@ -139,23 +140,23 @@ kda_decode(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 }
 
 template <typename T, int D>
-static int launch_typed(int N, int H, float g_floor, const void* q, const void* k, const void* v,
+static int launch_typed(int N, int H, float g_floor, int gate, const void* q, const void* k, const void* v,
                         const void* g, const float* beta, float* state, void* o, hipStream_t s) {
   const size_t blocks = (size_t)N * H;
   if (blocks == 0) return 0;
-  hipLaunchKernelGGL((kda_decode<T, D>), dim3((unsigned)blocks), dim3(DecodeShape<D>::NTH), 0, s, (const T*)q, (const T*)k,
-                     (const T*)v, (const T*)g, beta, state, (T*)o, g_floor);
+  hipLaunchKernelGGL((kda_decode<T, D>), dim3((unsigned)blocks), dim3(DecodeShape<D>::NTH), 0, s, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)g, beta, state, (T*)o, g_floor, gate);
   return (int)hipGetLastError();
 }
 
-int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor, const void* q, const void* k,
+int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor, int gate, const void* q, const void* k,
                        const void* v, const void* g, const float* beta, float* state, void* o,
                        void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (is_bf16 && d == 64) return launch_typed<bf16_t, 64>(N, H, g_floor, q, k, v, g, beta, state, o, s);
-  if (is_bf16 && d == 128) return launch_typed<bf16_t, 128>(N, H, g_floor, q, k, v, g, beta, state, o, s);
-  if (!is_bf16 && d == 64) return launch_typed<float, 64>(N, H, g_floor, q, k, v, g, beta, state, o, s);
-  if (!is_bf16 && d == 128) return launch_typed<float, 128>(N, H, g_floor, q, k, v, g, beta, state, o, s);
+  if (is_bf16 && d == 64) return launch_typed<bf16_t, 64>(N, H, g_floor, gate, q, k, v, g, beta, state, o, s);
+  if (is_bf16 && d == 128) return launch_typed<bf16_t, 128>(N, H, g_floor, gate, q, k, v, g, beta, state, o, s);
+  if (!is_bf16 && d == 64) return launch_typed<float, 64>(N, H, g_floor, gate, q, k, v, g, beta, state, o, s);
+  if (!is_bf16 && d == 128) return launch_typed<float, 128>(N, H, g_floor, gate, q, k, v, g, beta, state, o, s);
   return (int)hipErrorInvalidValue;
 }
 

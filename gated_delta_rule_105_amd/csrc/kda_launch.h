@@ -9,6 +9,9 @@ namespace kda {
 
 constexpr int kChunk = 64;  // tokens per chunk
 
+// Gate layouts (the values of kda_gate_t): g per key channel, per head, none.
+constexpr int kGateChannel = 0, kGateHead = 1, kGateNone = 2;
+
 // How a chunked forward is cut for the GPU.
 //  - The state passes cut every sequence into segments of `seg_chunks`
 //    chunks.  One record per (segment, head) holds three d x d fp32 matrices:
@@ -122,19 +125,20 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
 constexpr int kLaunches = 3;  // chunk pass (with the segment maps), segment scan, output pass
 
 // Enqueue the chunked forward.  All arguments were validated by the caller.
-// n_rows: number of sequences (n_seqs, or B when cu == nullptr).  states:
+// n_rows: number of sequences (n_seqs, or B when cu == nullptr).  gate: a
+// kda_gate_t (g is null for KDA_GATE_NONE).  states:
 // null, or the state slots of kda_chunk_forward_states, one every `every`
 // chunks.  events: null, or kLaunches + 1 hipEvent_t handles (entries may be
 // null) recorded on the stream before each launch and after the last.
 // Returns a hipError_t.
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan,
-                         float g_floor, const void* q, const void* k, const void* v,
+                         float g_floor, int gate, const void* q, const void* k, const void* v,
                          const void* g, const float* beta, const float* h0,
                          const int32_t* cu, void* o, float* ht, float* states, int every,
                          void* ws, void* stream, void* const* events);
 
-// Enqueue one decode step.  Returns a hipError_t.
-int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor,
+// Enqueue one decode step (gate: a kda_gate_t).  Returns a hipError_t.
+int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor, int gate,
                        const void* q, const void* k, const void* v,
                        const void* g, const float* beta, float* state, void* o,
                        void* stream);

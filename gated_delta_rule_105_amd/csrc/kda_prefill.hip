@@ -163,6 +163,16 @@ template <typename T, int D> struct Rec {
   }
 };
 
+// one element replicated over a 16-byte piece
+__device__ __forceinline__ uint4 splat16(bf16_t x) {
+  const uint32_t u = (uint32_t)x | ((uint32_t)x << 16);
+  return (uint4){u, u, u, u};
+}
+__device__ __forceinline__ uint4 splat16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint4){u, u, u, u};
+}
+
 // ---- raw chunk inputs: global -> registers (prefetch) -> LDS -------------
 template <typename T, int D, int NT, bool WITH_Q> struct Raw {
   typedef Lds<T, D> M;
@@ -177,8 +187,10 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
   // (beta and g of such rows must be 0; their q, k and v then reach no
   // output).  The buffer is scoped to one chunk iteration.  load = load_qkg
   // (q, k, g and beta) + load_v, which may be issued at different times.
+  // gate: g per channel (16-byte pieces like q), one per (token, head)
+  // replicated over the channels, or none (zeros: no decay).
   __device__ __forceinline__ void load_qkg(const T* Q, const T* K, const T* G, const float* B, int64_t tok0,
-                                           int len, int H, int h, int tid) {
+                                           int len, int H, int h, int tid, int gate) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
@@ -187,7 +199,9 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
         const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;
         if (WITH_Q) q[j] = stream_load16(Q + off);
         k[j] = stream_load16(K + off);
-        g[j] = stream_load16(G + off);
+        g[j] = gate == kGateChannel ? stream_load16(G + off)
+               : gate == kGateHead  ? splat16(G[(size_t)(tok0 + t) * H + h])
+                                    : z;
       } else {
         if (WITH_Q) q[j] = z;
         k[j] = z;
@@ -204,8 +218,8 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
     }
   }
   __device__ __forceinline__ void load(const T* Q, const T* K, const T* V, const T* G, const float* B,
-                                       int64_t tok0, int len, int H, int h, int tid) {
-    load_qkg(Q, K, G, B, tok0, len, H, h, tid);
+                                       int64_t tok0, int len, int H, int h, int tid, int gate) {
+    load_qkg(Q, K, G, B, tok0, len, H, h, tid, gate);
     load_v(V, tok0, len, H, h, tid);
   }
 
@@ -1004,7 +1018,7 @@ template <typename T, int D, int NW, bool MAPS>
 __global__ void __launch_bounds__(64 * NW)
 kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-               int n_rows, int T_per, int H, int L, float g_floor, unsigned char* __restrict__ crec,
+               int n_rows, int T_per, int H, int L, float g_floor, int gate, unsigned char* __restrict__ crec,
                float* __restrict__ ws) {
   typedef Lds<T, D> M;
   typedef CRec<T, D> CR;
@@ -1038,7 +1052,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
 
   {
     Raw<T, D, NT, true> first;
-    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0);
+    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0, gate);
     first.store(smem, tid0);
   }
   __syncthreads();
@@ -1059,7 +1073,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     const int64_t tok_n = sg.tok0 + (int64_t)C * (j + 1);
     const int len_n = min(C, sg.len - C * (j + 1));
     if (more) {
-      raw.load_qkg(q, k, g, beta, tok_n, len_n, H, h, tid);
+      raw.load_qkg(q, k, g, beta, tok_n, len_n, H, h, tid, gate);
       if (!MAPS) raw.load_v(v, tok_n, len_n, H, h, tid);
     }
     gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
@@ -1273,8 +1287,9 @@ template <int D> struct ScanOps<bf16_t, D> {
   __device__ static __forceinline__ MRaw load_m(__amdgpu_buffer_rsrc_t r, uint32_t off, int kb) {
     typedef Rec<bf16_t, D> R;
     MRaw m;
-    m.hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)R::frag(0, kb, 0, 0), 0, 0));
-    m.lo = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)R::frag(0, kb, 1, 0), 0, 0));
+    const uint32_t oh = off + (uint32_t)R::frag(0, kb, 0, 0), ol = off + (uint32_t)R::frag(0, kb, 1, 0);
+    m.hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, oh, 0, 0));
+    m.lo = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, ol, 0, 0));
     return m;
   }
   __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) {
@@ -1291,8 +1306,8 @@ template <int D> struct ScanOps<float, D> {
   __device__ static __forceinline__ SFrag gather(const PubArea& a, int kb, int lane) { return a[kb][lane]; }
   typedef f32x4 MRaw;
   __device__ static __forceinline__ MRaw load_m(__amdgpu_buffer_rsrc_t r, uint32_t off, int kb) {
-    return __builtin_bit_cast(f32x4,
-                              __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)Rec<float, D>::frag(0, kb, 0, 0), 0, 0));
+    const uint32_t o = off + (uint32_t)Rec<float, D>::frag(0, kb, 0, 0);
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
   }
   __device__ static __forceinline__ f32x4 product(const MRaw& m, const SFrag& s, f32x4 acc) { return mma(m, s, acc); }
 };
@@ -1412,7 +1427,8 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
 }
 
 template <typename T, int D, int NW, int NW2>
-int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, const void* q, const void* k,
+int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, int gate, const void* q,
+                 const void* k,
                  const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
                  float* ht, float* states, int every, void* ws, hipStream_t stream, void* const* events) {
   constexpr int NR = D / 16;
@@ -1429,12 +1445,12 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
   if (has_segments && plan.maps_in_prep) {
     hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0,
                        stream, (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L,
-                       g_floor, crec, wsf);
+                       g_floor, gate, crec, wsf);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   } else if (has_segments) {
     hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false>), dim3((unsigned)plan.n_prep_bound, H), dim3(64 * NW), 0,
                        stream, (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H,
-                       plan.prep_chunks, g_floor, crec, wsf);
+                       plan.prep_chunks, g_floor, gate, crec, wsf);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((e = mark(1)) != hipSuccess) return (int)e;
@@ -1456,19 +1472,20 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
 }  // namespace
 
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan, float g_floor,
-                         const void* q, const void* k, const void* v, const void* g, const float* beta,
+                         int gate, const void* q, const void* k, const void* v, const void* g, const float* beta,
                          const float* h0, const int32_t* cu, void* o, float* ht, float* states, int every,
                          void* ws, void* stream, void* const* events) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, states,
-                                          every, ws, s, events);
+    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, q, k, v, g, beta, h0, cu, o, ht,
+                                          states, every, ws, s, events);
   if (is_bf16 && d == 128)
-    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0,
-                                                               cu, o, ht, states, every, ws, s, events);
+    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, gate, q, k, v, g,
+                                                               beta, h0, cu, o, ht, states, every, ws, s,
+                                                               events);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, q, k, v, g, beta, h0, cu, o, ht, states,
-                                         every, ws, s, events);
+    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, q, k, v, g, beta, h0, cu, o, ht,
+                                         states, every, ws, s, events);
   return (int)hipErrorInvalidValue;
 }
 

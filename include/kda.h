@@ -23,6 +23,16 @@
  * The pages leave the position of the gate relative to the erase open; this
  * library decays first, as in the formula above.
  *
+ * Gate variants (kda_gate_t).  KDA's channel-wise gate extends Gated
+ * DeltaNet, where one forget rate per head and token serves every key
+ * channel (akiraxclaw.com page above, same section); with no gate at all the
+ * recurrence is the plain delta rule (chenxutan.com page above, 4.2).  Both
+ * are KDA with alpha_t the same for every channel, or 1:
+ *   KDA_GATE_CHANNEL  g is [.., H, d_k]: one log-decay per key channel (KDA);
+ *   KDA_GATE_HEAD     g is [.., H]: one log-decay per (token, head), applied
+ *                     to every key channel (Gated DeltaNet);
+ *   KDA_GATE_NONE     alpha = 1, g is not read and may be NULL (DeltaNet).
+ *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
  *     16-byte aligned.  The caller owns every buffer; the library allocates
@@ -46,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 10000 /* 1.0.0 */
+#define KDA_VERSION 10100 /* 1.1.0 */
 
 typedef enum {
   KDA_OK = 0,
@@ -57,6 +67,8 @@ typedef enum {
 } kda_status_t;
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate_t;
 
 /* Shape of one chunked forward call. */
 typedef struct {
@@ -69,6 +81,7 @@ typedef struct {
   int n_seqs;       /* 0: B sequences of T tokens; > 0: packed sequences     */
   kda_dtype_t dtype;/* dtype of q, k, v, g and o                             */
   float g_floor;    /* per-step log-decay floor, in [-1, 0), |chunk*floor|<=16 */
+  kda_gate_t gate;  /* layout of g (see the gate variants above)             */
 } kda_chunk_desc_t;
 
 /* Static, human-readable name of a status code; never NULL. */
@@ -95,7 +108,9 @@ int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
  * triangular inverse, then the state is carried from chunk to chunk.  The
  * result equals the token-by-token recurrence up to rounding.
  *
- *   q, k, g : [B, T, H, d_k]  dtype
+ *   q, k    : [B, T, H, d_k]  dtype
+ *   g       : [B, T, H, d_k] (KDA_GATE_CHANNEL), [B, T, H] (KDA_GATE_HEAD)
+ *             dtype, or NULL (KDA_GATE_NONE)
  *   v       : [B, T, H, d_v]  dtype
  *   beta    : [B, T, H]       fp32, write strengths in [0, 1]
  *   h0      : [S, H, d_k, d_v] fp32 or NULL (= zero state); S = n_seqs or B
@@ -183,14 +198,16 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d,
  * (the recurrence above for a single token; decode cost and state size do
  * not depend on how many tokens came before).
  *
- *   q, k, g : [N, H, d_k] dtype      v: [N, H, d_v] dtype
+ *   q, k    : [N, H, d_k] dtype      v: [N, H, d_v] dtype
+ *   g       : [N, H, d_k] (KDA_GATE_CHANNEL), [N, H] (KDA_GATE_HEAD) dtype,
+ *             or NULL (KDA_GATE_NONE)
  *   beta    : [N, H] fp32            o: [N, H, d_v] dtype, written
  *   state   : [N, H, d_k, d_v] fp32, read and overwritten
  * d_k = d_v in {64, 128}.  state must not overlap any other argument and o
  * must not overlap any input.
  */
-int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor,
-                    const void* q, const void* k, const void* v, const void* g,
+int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate,
+                    float g_floor, const void* q, const void* k, const void* v, const void* g,
                     const float* beta, float* state, void* o, void* stream);
 
 #ifdef __cplusplus

@@ -50,7 +50,7 @@ def test_status_strings(lib):
 
 def desc(**kw):
     base = dict(B=1, T=4096, H=16, d_k=128, d_v=128, chunk=64, n_seqs=0, dtype=KDA_DTYPE_BF16,
-                g_floor=-0.125)
+                g_floor=-0.125, gate=0)
     base.update(kw)
     return ChunkDesc(**base)
 
@@ -154,10 +154,10 @@ def test_chunk_forward_rejects_bad_desc(lib):
     assert call(lib, dv, av) == KDA_ERR_INVALID_ARGUMENT                 # misaligned cu
 
 
-def dec(lib, N=256, H=32, d=128, dtype=KDA_DTYPE_BF16, g_floor=-0.125, **ptrs):
+def dec(lib, N=256, H=32, d=128, dtype=KDA_DTYPE_BF16, gate=0, g_floor=-0.125, **ptrs):
     p = {name: (i + 1) * 64 * GB for i, name in enumerate(["q", "k", "v", "g", "beta", "state", "o"])}
     p.update(ptrs)
-    return _lib.decode_step_raw(N, H, d, d, dtype, g_floor, p["q"], p["k"], p["v"], p["g"], p["beta"],
+    return _lib.decode_step_raw(N, H, d, d, dtype, gate, g_floor, p["q"], p["k"], p["v"], p["g"], p["beta"],
                                 p["state"], p["o"], None)
 
 
@@ -173,6 +173,12 @@ def test_decode_rejects(lib):
     assert dec(lib, state=64 * GB + 1024) == KDA_ERR_INVALID_ARGUMENT       # state overlaps q
     assert dec(lib, o=2 * 64 * GB) == KDA_ERR_INVALID_ARGUMENT              # o overlaps k
     assert dec(lib, N=0) == KDA_OK                                          # nothing to do
+    assert dec(lib, gate=3) == KDA_ERR_INVALID_ARGUMENT                     # no such gate
+    assert dec(lib, g=None) == KDA_ERR_INVALID_ARGUMENT                     # gated, no g
+    assert dec(lib, gate=1, g=None) == KDA_ERR_INVALID_ARGUMENT
+    assert dec(lib, gate=1, g=4 * 64 * GB + 2) == KDA_ERR_INVALID_ARGUMENT  # misaligned per-head g
+    # without a gate g is not read: a bad g is ignored, the other checks still apply
+    assert dec(lib, gate=2, g=3, state=64 * GB + 1024) == KDA_ERR_INVALID_ARGUMENT
 
 
 def test_chunk_forward_timed_needs_events(lib):
@@ -236,3 +242,19 @@ def test_chunk_forward_states_empty(lib):
     a["ht"] = None
     assert call_states(lib, d, a, None, 1) == KDA_OK
     assert call_states(lib, desc(d_k=96, d_v=96), fake_args(lib, desc()), 11 * 64 * GB, 1) == KDA_ERR_UNSUPPORTED
+
+
+def test_gate_validation(lib):
+    d = desc()
+    a = fake_args(lib, d)
+    assert call(lib, desc(gate=3), a) == KDA_ERR_INVALID_ARGUMENT         # no such gate
+    assert ws_status(lib, desc(gate=-1))[0] == KDA_ERR_INVALID_ARGUMENT
+    a2 = dict(a, g=None)
+    assert call(lib, desc(gate=1), a2) == KDA_ERR_INVALID_ARGUMENT        # per-head gate without g
+    # per-head g is [B, T, H]: 128 KiB here; o placed 64 KiB after it overlaps
+    a3 = dict(a, o=a["g"] + 64 * 1024)
+    assert call(lib, desc(gate=1), a3) == KDA_ERR_INVALID_ARGUMENT
+    # without a gate g is ignored, and the workspace does not depend on the gate
+    a4 = dict(a, g=None, ws_bytes=a["ws_bytes"] - 1)
+    assert call(lib, desc(gate=2), a4) == KDA_ERR_WORKSPACE_TOO_SMALL
+    assert ws_status(lib, desc(gate=1)) == ws_status(lib, desc(gate=2)) == ws_status(lib, desc())

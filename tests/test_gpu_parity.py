@@ -193,6 +193,69 @@ def test_resume_from_emitted_state():
     assert e_o <= TOL["bf16"] and e_h <= TOL["bf16"]
 
 
+# ------------------------------------ gate variants: GDN and DeltaNet
+# Gated DeltaNet (one log-decay per token and head) and DeltaNet (no decay)
+# are KDA with the gate broadcast over the key channels, or zero: the oracle
+# runs them that way.
+def _gate_inputs(inp, mode):
+    """(g for the GPU, g for the oracle) for a gate mode: the per-head gate is
+    channel 0 of the per-channel one."""
+    g = inp["g"]
+    if mode == "head":
+        gh = g[..., 0].contiguous()
+        return gh, gh[..., None].expand(g.shape).contiguous()
+    return None, torch.zeros_like(g)
+
+
+GATES = {
+    "head-bf16-d128-T300": (lambda: _case(1, 300, 3, 128, "bf16", wid=170), "head"),
+    "head-f32-d64-B2-T130": (lambda: _case(2, 130, 3, 64, "f32", wid=171), "head"),
+    "head-bf16-d128-varlen-sigma2": (lambda: _case(1, 0, 2, 128, "bf16", sigma_g=2.0,
+                                                   lengths=[3000, 1, 700, 0, 1777], wid=172), "head"),
+    "head-bf16-d64-T8192": (lambda: _case(1, 8192, 2, 64, "bf16", wid=173), "head"),
+    "none-bf16-d128-T1000": (lambda: _case(1, 1000, 3, 128, "bf16", wid=174), "none"),
+    "none-f32-d64-varlen": (lambda: _case(1, 0, 2, 64, "f32", lengths=[5, 0, 128, 70], wid=175), "none"),
+}
+
+
+@pytest.mark.parametrize("name", list(GATES))
+def test_chunk_forward_gates(name):
+    make, mode = GATES[name]
+    inp = make()
+    dtype = "bf16" if inp["q"].dtype == torch.bfloat16 else "f32"
+    g_gpu, g_ref = _gate_inputs(inp, mode)
+    note(f"chunk_forward gate={mode} {name} q{tuple(inp['q'].shape)}")
+    d = to_dev(dict(inp, g=g_gpu))
+    o, ht = kda.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d.get("h0"),
+                              cu_seqlens=d.get("cu_seqlens"))
+    torch.cuda.synchronize()
+    ro, rht = oracle_forward(dict(inp, g=g_ref))
+    eo, eh = rel_err(f64(o), ro), rel_err(f64(ht), rht)
+    print(f"{name}: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mode", ["head", "none"])
+@pytest.mark.parametrize("d,dtype", [(64, "f32"), (128, "bf16")])
+def test_decode_gates(mode, d, dtype):
+    N, H, steps = 5, 3, 6
+    inp = synth.decode_inputs(N, H, d, d, steps, dtype, wid=176 + d)
+    note(f"decode gate={mode} N{N} H{H} d{d} {dtype} x{steps}")
+    state = inp["state"].cuda()
+    ref_state = inp["state"].double().numpy()
+    for s in range(steps):
+        g_gpu, g_ref = _gate_inputs({"g": inp["g"][s]}, mode)
+        args = [inp[key][s].cuda() for key in ("q", "k", "v")]
+        o = kda.decode_step(*args, None if g_gpu is None else g_gpu.cuda(), inp["beta"][s].cuda(), state)
+        torch.cuda.synchronize()
+        ro, ref_state = oracle.decode_step(inp["q"][s], inp["k"][s], inp["v"][s], g_ref, inp["beta"][s], ref_state)
+        eo = rel_err(f64(o), ro)
+        assert eo <= TOL[dtype], (s, eo)
+    es = rel_err(f64(state), ref_state)
+    print(f"decode gate={mode} d{d} {dtype}: last err_o={eo:.3e} err_state={es:.3e}")
+    assert es <= TOL[dtype]
+
+
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("d,dtype", [(64, "f32"), (128, "f32"), (64, "bf16"), (128, "bf16")])
 def test_decode_small(d, dtype):
