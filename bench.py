@@ -24,7 +24,8 @@ a target).  ``other_workloads`` times the packed 8-sequence batch and the
 1,048,576-token context; ``states_workloads`` times the headline call with
 prefix-cache states (kda_chunk_forward_states) beside plain calls;
 ``gate_workloads`` times Gated DeltaNet and DeltaNet gates beside KDA on the
-prefill and decode workloads.  Other
+prefill and decode workloads; ``mx_workload`` the headline workload with q,
+k, v in MXFP8 (kda_chunk_forward_mx).  Other
 legs: ``--copy-calib MiB`` runs only a device copy of known size (for
 scaling the HBM byte counters), ``--only prefill|decode`` runs one leg,
 ``--no-cpu`` skips the oracle.
@@ -333,6 +334,54 @@ def bench_gates(calls: int, steps: int):
     return out
 
 
+def bench_mx(calls: int):
+    """MXFP8 q, k, v (kda_chunk_forward_mx) beside bf16 on the headline
+    workload: the same values (q, k, v encoded once, g bf16), buffer sets
+    rotated as in the headline leg so that every call reads from HBM."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[1]
+    base = synth.mxfp8_inputs(synth.workload_inputs(w, device="cuda"))
+    B, T, H, d = base["q"].shape
+    keys = ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale", "g", "beta", "h0")
+    set_bytes = sum(base[k_].numel() * base[k_].element_size() for k_ in keys[:-1])
+    n_sets = max(2, math.ceil(3 * LLC_BYTES / set_bytes))
+    sets = [{k_: base[k_].clone() for k_ in keys} for _ in range(n_sets)]
+    ws = torch.empty(kda.workspace_bytes(B, T, H, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty_like(base["h0"])
+    del base
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def call():
+        x = sets[it[0] % n_sets]
+        it[0] += 1
+        kda.chunk_forward_mx(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["v8"], x["v_scale"], x["g"], x["beta"],
+                             h0=x["h0"], o=o, ht=ht, workspace=ws)
+
+    for _ in range(n_sets):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    mean = sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+    log(f"mxfp8 inputs: {calls} calls over {n_sets} buffer sets, mean {mean * 1e6:.1f} us")
+    del sets, ws, o
+    torch.cuda.empty_cache()
+    th = T * H
+    in_bytes = th * (3 * d + 3 * d // 32 + 2 * d + 4)  # e4m3 q, k, v + scales + bf16 g + fp32 beta
+    return {"workload": f"{w.name} q,k,v MXFP8 (e4m3 + scale per 32 channels)", "mean_call_us": mean * 1e6,
+            "value": T / mean, "unit": "tokens/s", "input_bytes": in_bytes,
+            "hbm_frac": (in_bytes + th * 2 * d + 2 * H * STATE_BYTES) / mean / 1e9 / PEAK_HBM_GBS}
+
+
 def bench_decode(steps: int, warmup: int):
     import torch
     import gated_delta_rule_105_amd as kda
@@ -444,6 +493,7 @@ def main() -> int:
         out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3)]
         out["states_workloads"] = bench_states(50)
         out["gate_workloads"] = bench_gates(50, 100)
+        out["mx_workload"] = bench_mx(100)
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

@@ -26,8 +26,8 @@ from ._lib import (CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_GATE_CHANN
                    KDA_GATE_NONE, KDA_OK, ChunkDesc, KdaError, status_string, version)
 from . import _lib
 
-__all__ = ["chunk_forward", "chunk_forward_states", "decode_step", "workspace_bytes", "make_desc",
-           "KdaError", "status_string", "version", "CHUNK_LAUNCHES"]
+__all__ = ["chunk_forward", "chunk_forward_states", "chunk_forward_mx", "decode_step", "workspace_bytes",
+           "make_desc", "KdaError", "status_string", "version", "CHUNK_LAUNCHES"]
 
 
 def _torch():
@@ -132,14 +132,34 @@ def chunk_forward_states(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int 
                     validate_cu, stream, None, states, states_every)
 
 
-def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace, output_final_state,
-             validate_cu, stream, events, states, states_every):
+def chunk_forward_mx(q, q_scale, k, k_scale, v, v_scale, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
+                     g_floor: float = -0.125, *, o=None, ht=None, workspace=None,
+                     output_final_state: bool = True, validate_cu: bool = True,
+                     stream=None) -> Tuple[object, object]:
+    """chunk_forward with q, k, v in MXFP8 (kda_chunk_forward_mx): uint8
+    tensors [B, T, H, d] of e4m3 bytes and uint8 scale tensors [B, T, H, d/32]
+    (2^(s - 127) per block of 32 channels).  g (bf16, per channel or per
+    head, or None) and o are bf16."""
     torch = _torch()
     B, T, H, d = q.shape
-    dt = q.dtype
-    _check_dev("q", q, dt)
-    for name, t in (("k", k), ("v", v)):
-        _check_dev(name, t, dt, (B, T, H, d))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.uint8, (B, T, H, d))
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_dev(name, t, torch.uint8, (B, T, H, d // 32))
+    o, ht, _ = _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace, output_final_state,
+                        validate_cu, stream, None, None, 0, mx=(q_scale, k_scale, v_scale))
+    return o, ht
+
+
+def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace, output_final_state,
+             validate_cu, stream, events, states, states_every, mx=None):
+    torch = _torch()
+    B, T, H, d = q.shape
+    dt = torch.bfloat16 if mx is not None else q.dtype  # dtype of g, o (and q, k, v without MXFP8)
+    if mx is None:
+        _check_dev("q", q, dt)
+        for name, t in (("k", k), ("v", v)):
+            _check_dev(name, t, dt, (B, T, H, d))
     gate = _gate_of(g, 4)
     _check_dev("g", g, dt, (B, T, H, d) if gate == KDA_GATE_CHANNEL else (B, T, H))
     _check_dev("beta", beta, torch.float32, (B, T, H))
@@ -168,7 +188,11 @@ def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
     args = (desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
             _ptr(ht))
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), stream)
-    if states is not None:
+    if mx is not None:
+        st = _lib.chunk_forward_mx_raw(desc, _ptr(q), _ptr(mx[0]), _ptr(k), _ptr(mx[1]), _ptr(v), _ptr(mx[2]),
+                                       *args[4:], *tail)
+        what = "kda_chunk_forward_mx"
+    elif states is not None:
         st = _lib.chunk_forward_states_raw(*args, _ptr(states) if states.numel() else None, states_every,
                                            *tail)
         what = "kda_chunk_forward_states"

@@ -26,7 +26,7 @@ KDA_GATE_NONE = 2      # no g: DeltaNet
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
            "kda_chunk_forward", "kda_chunk_forward_timed", "kda_chunk_forward_states_count",
-           "kda_chunk_forward_states", "kda_decode_step")
+           "kda_chunk_forward_states", "kda_chunk_forward_mx", "kda_decode_step")
 
 # Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed).
 CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_scan", "kda_seg_forward")
@@ -77,6 +77,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_forward_states.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              vp, ctypes.c_int, vp, sz, vp]
     lib.kda_chunk_forward_states.restype = ctypes.c_int
+    lib.kda_chunk_forward_mx.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp]
+    lib.kda_chunk_forward_mx.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -127,6 +130,12 @@ def chunk_forward_states_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, s
     """Call kda_chunk_forward_states with raw integer addresses; returns the status."""
     return int(load().kda_chunk_forward_states(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, states,
                                                int(states_every), ws, ctypes.c_size_t(ws_bytes), stream))
+
+
+def chunk_forward_mx_raw(desc: ChunkDesc, q, qs, k, ks, v, vs, g, beta, h0, cu, o, ht, ws, ws_bytes, stream) -> int:
+    """Call kda_chunk_forward_mx with raw integer addresses; returns the status."""
+    return int(load().kda_chunk_forward_mx(ctypes.byref(desc), q, qs, k, ks, v, vs, g, beta, h0, cu, o, ht, ws,
+                                           ctypes.c_size_t(ws_bytes), stream))
 
 
 def decode_step_raw(N, H, d_k, d_v, dtype, gate, g_floor, q, k, v, g, beta, state, o, stream) -> int:

@@ -128,30 +128,31 @@ int kda_chunk_forward_states_count(const kda_chunk_desc_t* d, int states_every, 
   return KDA_OK;
 }
 
+// mx: MXFP8 q, k, v (e4m3 bytes) with their scale bytes, or NULL.
+struct MxIn {
+  const uint8_t* qs;
+  const uint8_t* ks;
+  const uint8_t* vs;
+};
+
 // states: NULL (no state emission) or the kda_chunk_forward_states buffer,
 // with every >= 1.
 static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
                          const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
-                         float* states, int every, void* workspace, size_t workspace_bytes, void* stream,
-                         void* const* events) {
+                         float* states, int every, const MxIn* mx, void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* events) {
   Sizes s;
   const int st = check_desc(d, &s);
   if (st != KDA_OK) return st;
-  size_t states_bytes = 0;
-  if (states) {
-    size_t slots, per;
-    if (!state_slots(d, every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
-    if (!mul((size_t)d->H * d->d_k, (size_t)d->d_v * 4, &per) || !mul(slots, per, &states_bytes))
-      return KDA_ERR_INVALID_ARGUMENT;
-    if (!aligned(states, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
-    const Range rs = range(states, states_bytes);
-    const Range all[] = {range(q, s.x_bytes),     range(k, s.x_bytes),    range(v, s.x_bytes),
-                         range(g, s.g_bytes),     range(beta, s.beta_bytes), range(o, s.x_bytes),
-                         range(h0, s.state_bytes), range(ht, s.state_bytes), range(workspace, s.plan.ws_bytes)};
-    for (const Range& r : all)
-      if (overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
-  }
   const bool has_tokens = s.tokens > 0;
+  // bytes of q, k, v (MXFP8: one byte per element) and of each scale tensor
+  size_t qkv_bytes = s.x_bytes, sc_bytes = 0;
+  if (mx) {
+    if (d->dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;  // MXFP8 inputs feed the bf16 path
+    qkv_bytes = s.x_bytes / 2;
+    sc_bytes = qkv_bytes / 32;
+    if (has_tokens && (!mx->qs || !mx->ks || !mx->vs)) return KDA_ERR_INVALID_ARGUMENT;
+  }
   const bool gated = d->gate != KDA_GATE_NONE;
   if (!gated) g = nullptr;  // not read
   if (has_tokens && (!q || !k || !v || (gated && !g) || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
@@ -165,33 +166,40 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
     if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   }
-  if (has_tokens) {
-    const Range ro = range(o, s.x_bytes);
-    const Range ins[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes),
-                         range(g, s.g_bytes), range(beta, s.beta_bytes), range(h0, s.state_bytes)};
-    for (const Range& r : ins)
-      if (overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
+  // every input (read only; they may overlap one another)
+  const Range ins[] = {range(q, qkv_bytes),
+                       range(k, qkv_bytes),
+                       range(v, qkv_bytes),
+                       range(g, s.g_bytes),
+                       range(beta, s.beta_bytes),
+                       range(h0, s.state_bytes),
+                       range(mx ? mx->qs : nullptr, sc_bytes),
+                       range(mx ? mx->ks : nullptr, sc_bytes),
+                       range(mx ? mx->vs : nullptr, sc_bytes)};
+  const Range ro = range(o, s.x_bytes), rh = range(ht, s.state_bytes), rw = range(workspace, ws_need);
+  size_t states_bytes = 0;
+  if (states) {
+    size_t slots, per;
+    if (!state_slots(d, every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!mul((size_t)d->H * d->d_k, (size_t)d->d_v * 4, &per) || !mul(slots, per, &states_bytes))
+      return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(states, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
   }
-  if (ht) {
-    const Range rh = range(ht, s.state_bytes);
-    const Range others[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes),
-                            range(g, s.g_bytes), range(beta, s.beta_bytes), range(o, s.x_bytes)};
-    for (const Range& r : others)
-      if (overlap(rh, r)) return KDA_ERR_INVALID_ARGUMENT;
-    if (h0 && h0 != ht && overlap(rh, range(h0, s.state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+  const Range rs = range(states, states_bytes);
+  for (const Range& r : ins) {
+    if (has_tokens && overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
+    if (&r != &ins[5] && overlap(rh, r)) return KDA_ERR_INVALID_ARGUMENT;  // ht may alias h0 exactly
+    if (overlap(rw, r) || overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
   }
-  if (workspace && ws_need > 0) {
-    const Range rw = range(workspace, ws_need);
-    const Range all[] = {range(q, s.x_bytes), range(k, s.x_bytes), range(v, s.x_bytes), range(g, s.g_bytes),
-                         range(beta, s.beta_bytes), range(o, s.x_bytes), range(h0, s.state_bytes),
-                         range(ht, s.state_bytes)};
-    for (const Range& r : all)
-      if (overlap(rw, r)) return KDA_ERR_INVALID_ARGUMENT;
-  }
+  if (h0 && h0 != ht && overlap(rh, range(h0, s.state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+  if (overlap(rh, ro) || overlap(rw, ro) || overlap(rw, rh) || overlap(rs, ro) || overlap(rs, rh) ||
+      overlap(rs, rw))
+    return KDA_ERR_INVALID_ARGUMENT;
   if (!ht && s.tokens == 0 && !events) return KDA_OK;  // nothing to write (no full chunk: no states either)
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
+  const kda::ChunkInputs in{q, k, v, g, beta, mx ? mx->qs : nullptr, mx ? mx->ks : nullptr, mx ? mx->vs : nullptr};
   const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
-                                          d->g_floor, (int)d->gate, q, k, v, g, beta, h0, cu_seqlens, o, ht,
+                                          d->g_floor, (int)d->gate, in, h0, cu_seqlens, o, ht,
                                           states_bytes > 0 ? states : nullptr, every, workspace, stream,
                                           events);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
@@ -200,8 +208,8 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
 int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
                       const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                       void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, workspace, workspace_bytes, stream,
-                       nullptr);
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr, workspace, workspace_bytes,
+                       stream, nullptr);
 }
 
 int kda_chunk_forward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
@@ -209,8 +217,8 @@ int kda_chunk_forward_timed(const kda_chunk_desc_t* d, const void* q, const void
                             void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events) {
   if (!events) return KDA_ERR_INVALID_ARGUMENT;
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, workspace, workspace_bytes, stream,
-                       events);
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr, workspace, workspace_bytes,
+                       stream, events);
 }
 
 int kda_chunk_forward_states(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
@@ -223,8 +231,17 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d, const void* q, const voi
   size_t slots;
   if (!state_slots(d, states_every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
   if (!states && slots > 0) return KDA_ERR_INVALID_ARGUMENT;
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, states, states_every, workspace,
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, states, states_every, nullptr, workspace,
                        workspace_bytes, stream, nullptr);
+}
+
+int kda_chunk_forward_mx(const kda_chunk_desc_t* d, const void* q, const uint8_t* q_scale, const void* k,
+                         const uint8_t* k_scale, const void* v, const uint8_t* v_scale, const void* g,
+                         const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const MxIn mx{q_scale, k_scale, v_scale};
+  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, &mx, workspace, workspace_bytes,
+                       stream, nullptr);
 }
 
 int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate, float g_floor,

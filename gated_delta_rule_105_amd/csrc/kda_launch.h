@@ -121,6 +121,21 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
   return true;
 }
 
+// The inputs of one chunked forward.  q, k, v are in the operand type, or
+// with MXFP8 inputs (qs != null) e4m3 bytes whose blocks of 32 channels
+// share the power-of-two scale 2^(s - 127) of the scale byte s in qs, ks, vs
+// ([.., H, d / 32]).  g: per the gate; null without one.
+struct ChunkInputs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const float* beta;
+  const uint8_t* qs;
+  const uint8_t* ks;
+  const uint8_t* vs;
+};
+
 // Launches of one chunked forward, in stream order.
 constexpr int kLaunches = 3;  // chunk pass (with the segment maps), segment scan, output pass
 
@@ -132,8 +147,7 @@ constexpr int kLaunches = 3;  // chunk pass (with the segment maps), segment sca
 // null) recorded on the stream before each launch and after the last.
 // Returns a hipError_t.
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan,
-                         float g_floor, int gate, const void* q, const void* k, const void* v,
-                         const void* g, const float* beta, const float* h0,
+                         float g_floor, int gate, const ChunkInputs& in, const float* h0,
                          const int32_t* cu, void* o, float* ht, float* states, int every,
                          void* ws, void* stream, void* const* events);
 

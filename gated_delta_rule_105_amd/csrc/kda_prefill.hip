@@ -174,13 +174,34 @@ __device__ __forceinline__ uint4 splat16(float x) {
 }
 
 // ---- raw chunk inputs: global -> registers (prefetch) -> LDS -------------
-template <typename T, int D, int NT, bool WITH_Q> struct Raw {
+// 8 e4m3 bytes (OCP, finite-only) times their block's scale 2^(s - 127),
+// as 8 bf16 (exact: e4m3 has 3 significand bits, bf16 8; the gfx950
+// conversion takes the scale as an fp32 multiplier)
+__device__ __forceinline__ uint4 mx_decode8(const uint2& w, uint32_t s) {
+  const float sc = __uint_as_float(s ? s << 23 : 0x00400000u);
+  return (uint4){__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, sc, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, sc, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, sc, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, sc, true))};
+}
+
+// With MX, q, k and v arrive as e4m3 bytes with a scale byte per 32
+// channels: each thread loads 16 bytes (16 channels of one token, inside one
+// scale block) and their scale per tensor, decoded to two 16-byte vectors
+// of bf16 when they are stored to LDS; everything after that is the bf16
+// path.
+template <typename T, int D, int NT, bool WITH_Q, bool MX = false> struct Raw {
   typedef Lds<T, D> M;
   static constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte vector
   static constexpr int VPR = D / EPV;              // vectors per token row
   static constexpr int PER = C * VPR / NT;         // vectors per thread per tensor
   static_assert(PER * NT == C * VPR, "thread count must divide the chunk");
-  uint4 q[WITH_Q ? PER : 1], k[PER], v[PER], g[PER];
+  static_assert(!MX || (sizeof(T) == 2 && D % 32 == 0), "MXFP8 inputs feed the bf16 path");
+  static constexpr int NB = MX ? 1 : PER;
+  static constexpr int TPR = D / 16;  // MX: threads per token row (16 channels each)
+  static_assert(!MX || C * TPR == NT, "MX: one 16-byte load per thread and tensor");
+  uint4 q[WITH_Q ? NB : 1], k[NB], v[NB], g[PER];  // MX: q[0], k[0], v[0] hold e4m3 bytes
+  uint32_t qs, ks, vs;                              // MX: their scale bytes
   float beta;
 
   // Rows past the chunk's end (a sequence's last chunk) are loaded as zeros
@@ -189,38 +210,70 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
   // (q, k, g and beta) + load_v, which may be issued at different times.
   // gate: g per channel (16-byte pieces like q), one per (token, head)
   // replicated over the channels, or none (zeros: no decay).
-  __device__ __forceinline__ void load_qkg(const T* Q, const T* K, const T* G, const float* B, int64_t tok0,
-                                           int len, int H, int h, int tid, int gate) {
+  __device__ __forceinline__ void load_qkg(const ChunkInputs& in, int64_t tok0, int len, int H, int h, int tid,
+                                           int gate) {
+    const T* G = (const T*)in.g;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
       const uint4 z = {0u, 0u, 0u, 0u};
       if (t < len) {
-        const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;
-        if (WITH_Q) q[j] = stream_load16(Q + off);
-        k[j] = stream_load16(K + off);
+        const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;  // element index
+        if (!MX) {
+          if (WITH_Q) q[j] = stream_load16((const T*)in.q + off);
+          k[j] = stream_load16((const T*)in.k + off);
+        }
         g[j] = gate == kGateChannel ? stream_load16(G + off)
                : gate == kGateHead  ? splat16(G[(size_t)(tok0 + t) * H + h])
                                     : z;
       } else {
-        if (WITH_Q) q[j] = z;
-        k[j] = z;
+        if (!MX) {
+          if (WITH_Q) q[j] = z;
+          k[j] = z;
+        }
         g[j] = z;
       }
     }
-    beta = (tid < len) ? B[(size_t)(tok0 + tid) * H + h] : 0.f;
+    if (MX) {
+      const int t = tid / TPR;
+      const size_t off = ((size_t)(tok0 + t) * H + h) * D + (tid % TPR) * 16;  // element (= byte) index
+      const bool in_seq = t < len;
+      if (WITH_Q) {
+        q[0] = in_seq ? stream_load16((const uint8_t*)in.q + off) : (uint4){0u, 0u, 0u, 0u};
+        qs = in_seq ? in.qs[off / 32] : 127u;
+      }
+      k[0] = in_seq ? stream_load16((const uint8_t*)in.k + off) : (uint4){0u, 0u, 0u, 0u};
+      ks = in_seq ? in.ks[off / 32] : 127u;
+    }
+    beta = (tid < len) ? in.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
   }
-  __device__ __forceinline__ void load_v(const T* V, int64_t tok0, int len, int H, int h, int tid) {
+  __device__ __forceinline__ void load_v(const ChunkInputs& in, int64_t tok0, int len, int H, int h, int tid) {
+    if (MX) {
+      const int t = tid / TPR;
+      const size_t off = ((size_t)(tok0 + t) * H + h) * D + (tid % TPR) * 16;
+      v[0] = t < len ? stream_load16((const uint8_t*)in.v + off) : (uint4){0u, 0u, 0u, 0u};
+      vs = t < len ? in.vs[off / 32] : 127u;
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
-      v[j] = t < len ? stream_load16(V + ((size_t)(tok0 + t) * H + h) * D + cv * EPV) : (uint4){0u, 0u, 0u, 0u};
+      v[j] = t < len ? stream_load16((const T*)in.v + ((size_t)(tok0 + t) * H + h) * D + cv * EPV)
+                     : (uint4){0u, 0u, 0u, 0u};
     }
   }
-  __device__ __forceinline__ void load(const T* Q, const T* K, const T* V, const T* G, const float* B,
-                                       int64_t tok0, int len, int H, int h, int tid, int gate) {
-    load_qkg(Q, K, G, B, tok0, len, H, h, tid, gate);
-    load_v(V, tok0, len, H, h, tid);
+  __device__ __forceinline__ void load(const ChunkInputs& in, int64_t tok0, int len, int H, int h, int tid,
+                                       int gate) {
+    load_qkg(in, tok0, len, H, h, tid, gate);
+    load_v(in, tok0, len, H, h, tid);
+  }
+  // MX: 16 e4m3 bytes and their scale -> channels (tid % TPR) * 16 .. + 15 of
+  // token tid / TPR, two bf16 vectors in the token-major array at `area`
+  __device__ __forceinline__ static void store_mx(unsigned char* smem, int area, int tid, const uint4& b,
+                                                  uint32_t s) {
+    unsigned char* p = smem + area + (tid / TPR) * M::LDT * 2 + (tid % TPR) * 32;
+    *(uint4*)p = mx_decode8((uint2){b.x, b.y}, s);
+    *(uint4*)(p + 16) = mx_decode8((uint2){b.z, b.w}, s);
   }
 
   // into LDS: everything but v (store_qkg), v (store_v), or both (store)
@@ -229,13 +282,23 @@ template <typename T, int D, int NT, bool WITH_Q> struct Raw {
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
       const int off = t * M::LDT * (int)sizeof(T) + cv * 16;
-      if (WITH_Q) *(uint4*)(smem + M::Q + off) = q[j];
-      *(uint4*)(smem + M::K + off) = k[j];
+      if (!MX) {
+        if (WITH_Q) *(uint4*)(smem + M::Q + off) = q[j];
+        *(uint4*)(smem + M::K + off) = k[j];
+      }
       *(uint4*)(smem + M::G + off) = g[j];
+    }
+    if (MX) {
+      if (WITH_Q) store_mx(smem, M::Q, tid, q[0], qs);
+      store_mx(smem, M::K, tid, k[0], ks);
     }
     if (tid < C) ((float*)(smem + M::BETA))[tid] = beta;
   }
   __device__ __forceinline__ void store_v(unsigned char* smem, int tid) const {
+    if (MX) {
+      store_mx(smem, M::V, tid, v[0], vs);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
@@ -1014,12 +1077,10 @@ __device__ __forceinline__ void save_map(float* sM, float* recs, const f32x4 (&X
 // (started from I, value part of U off), wave w on the column tiles it owns.
 // Without MAPS (every sequence is one segment) the group length is the chunk
 // pass's own.
-template <typename T, int D, int NW, bool MAPS>
+template <typename T, int D, int NW, bool MAPS, bool MX>
 __global__ void __launch_bounds__(64 * NW)
-kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-               const T* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-               int n_rows, int T_per, int H, int L, float g_floor, int gate, unsigned char* __restrict__ crec,
-               float* __restrict__ ws) {
+kda_chunk_prep(const ChunkInputs in, const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
+               float g_floor, int gate, unsigned char* __restrict__ crec, float* __restrict__ ws) {
   typedef Lds<T, D> M;
   typedef CRec<T, D> CR;
   constexpr int NT = 64 * NW, NR = D / 16, NV = NR / NW;
@@ -1051,8 +1112,8 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   }
 
   {
-    Raw<T, D, NT, true> first;
-    first.load(q, k, v, g, beta, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0, gate);
+    Raw<T, D, NT, true, MX> first;
+    first.load(in, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0, gate);
     first.store(smem, tid0);
   }
   __syncthreads();
@@ -1068,13 +1129,13 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     // g and beta now (into LDS once Wk is complete), v now as well, or with
     // MAPS (short of registers) once Wk is complete, the map's state step
     // covering its latency (into LDS at the end of the chunk)
-    Raw<T, D, NT, true> raw;
+    Raw<T, D, NT, true, MX> raw;
     const bool more = j + 1 < j1;
     const int64_t tok_n = sg.tok0 + (int64_t)C * (j + 1);
     const int len_n = min(C, sg.len - C * (j + 1));
     if (more) {
-      raw.load_qkg(q, k, g, beta, tok_n, len_n, H, h, tid, gate);
-      if (!MAPS) raw.load_v(v, tok_n, len_n, H, h, tid);
+      raw.load_qkg(in, tok_n, len_n, H, h, tid, gate);
+      if (!MAPS) raw.load_v(in, tok_n, len_n, H, h, tid);
     }
     gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
     unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
@@ -1109,7 +1170,7 @@ kda_chunk_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     // the next chunk's q, k, g and beta go to their areas now (v's area holds
     // Wk until the end of the chunk)
     if (more) {
-      if (MAPS) raw.load_v(v, tok_n, len_n, H, h, tid);
+      if (MAPS) raw.load_v(in, tok_n, len_n, H, h, tid);
       raw.store_qkg(smem, tid);
     }
     save_wk<T, D, M::V>(smem, cr, wave, NW, lane);
@@ -1426,31 +1487,42 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   }
 }
 
+// MXFP8 inputs are decoded into the bf16 path (the fp32 path takes none).
+template <typename T, int D> struct MxOk { static constexpr bool value = sizeof(T) == 2 && D % 32 == 0; };
+
 template <typename T, int D, int NW, int NW2>
-int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, int gate, const void* q,
-                 const void* k,
-                 const void* v, const void* g, const float* beta, const float* h0, const int32_t* cu, void* o,
-                 float* ht, float* states, int every, void* ws, hipStream_t stream, void* const* events) {
+int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, int gate, const ChunkInputs& in,
+                 const float* h0, const int32_t* cu, void* o, float* ht, float* states, int every, void* ws,
+                 hipStream_t stream, void* const* events) {
   constexpr int NR = D / 16;
   const int L = plan.seg_chunks;
   float* wsf = (float*)ws;
   unsigned char* crec = (unsigned char*)ws + plan.crec_off;
   if (plan.crec_bytes != CRec<T, D>::BYTES) return (int)hipErrorInvalidValue;
+  if (in.qs && !MxOk<T, D>::value) return (int)hipErrorInvalidValue;  // MXFP8 inputs: bf16 path only
   const bool has_segments = plan.n_seg_bound > 0;
   hipError_t e;
   auto mark = [&](int i) -> hipError_t {
     return (events && events[i]) ? hipEventRecord((hipEvent_t)events[i], stream) : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return (int)e;
-  if (has_segments && plan.maps_in_prep) {
-    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW), 0,
-                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H, L,
-                       g_floor, gate, crec, wsf);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  } else if (has_segments) {
-    hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false>), dim3((unsigned)plan.n_prep_bound, H), dim3(64 * NW), 0,
-                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)g, beta, cu, n_rows, T_per, H,
-                       plan.prep_chunks, g_floor, gate, crec, wsf);
+  if (has_segments) {
+    const bool mx = in.qs != nullptr;
+    const unsigned grid = (unsigned)(plan.maps_in_prep ? plan.n_seg_bound : plan.n_prep_bound);
+    const int gl = plan.maps_in_prep ? L : plan.prep_chunks;
+    const dim3 g3(grid, H), b3(64 * NW);
+    if (plan.maps_in_prep && mx)
+      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true, MxOk<T, D>::value>), g3, b3, 0, stream, in, cu, n_rows,
+                         T_per, H, gl, g_floor, gate, crec, wsf);
+    else if (plan.maps_in_prep)
+      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true, false>), g3, b3, 0, stream, in, cu, n_rows, T_per, H, gl,
+                         g_floor, gate, crec, wsf);
+    else if (mx)
+      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false, MxOk<T, D>::value>), g3, b3, 0, stream, in, cu, n_rows,
+                         T_per, H, gl, g_floor, gate, crec, wsf);
+    else
+      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false, false>), g3, b3, 0, stream, in, cu, n_rows, T_per, H, gl,
+                         g_floor, gate, crec, wsf);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((e = mark(1)) != hipSuccess) return (int)e;
@@ -1472,20 +1544,18 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
 }  // namespace
 
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan, float g_floor,
-                         int gate, const void* q, const void* k, const void* v, const void* g, const float* beta,
-                         const float* h0, const int32_t* cu, void* o, float* ht, float* states, int every,
-                         void* ws, void* stream, void* const* events) {
+                         int gate, const ChunkInputs& in, const float* h0, const int32_t* cu, void* o, float* ht,
+                         float* states, int every, void* ws, void* stream, void* const* events) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, q, k, v, g, beta, h0, cu, o, ht,
-                                          states, every, ws, s, events);
+    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws,
+                                          s, events);
   if (is_bf16 && d == 128)
-    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, gate, q, k, v, g,
-                                                               beta, h0, cu, o, ht, states, every, ws, s,
-                                                               events);
+    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o,
+                                                               ht, states, every, ws, s, events);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, q, k, v, g, beta, h0, cu, o, ht,
-                                         states, every, ws, s, events);
+    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws,
+                                         s, events);
   return (int)hipErrorInvalidValue;
 }
 

@@ -155,6 +155,31 @@ int kda_chunk_forward_timed(const kda_chunk_desc_t* d,
                             void* stream, void* const* events);
 
 /*
+ * kda_chunk_forward with q, k and v in MXFP8 (OCP microscaling): each element
+ * is one e4m3 byte (finite-only encoding), and every block of 32 consecutive
+ * channels of one (token, head) shares a scale byte s meaning 2^(s - 127)
+ * (e8m0; 255 is not allowed).  Element value = e4m3(byte) * 2^(s - 127).
+ * The decoded values are exact in bf16, and from there the call is the bf16
+ * path: d->dtype must be KDA_DTYPE_BF16, which is the dtype of g and o.
+ * (K3 trains with MXFP8 activations: "Kimi K3 技術報告：三個架構改動一次看懂"
+ * (akiraxclaw.com), "MoonViT-V2 與低位元訓練也不能省略"; here MXFP8 halves the
+ * bytes of q, k and v.)
+ *   q, k, v             : [B, T, H, d] e4m3 bytes, 16-byte aligned
+ *   q/k/v_scale         : [B, T, H, d / 32] scale bytes
+ * Everything else as kda_chunk_forward (same workspace size); the scale
+ * tensors count as inputs in the overlap rules.
+ */
+int kda_chunk_forward_mx(const kda_chunk_desc_t* d,
+                         const void* q, const uint8_t* q_scale,
+                         const void* k, const uint8_t* k_scale,
+                         const void* v, const uint8_t* v_scale,
+                         const void* g, const float* beta, const float* h0,
+                         const int32_t* cu_seqlens,
+                         void* o, float* ht,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * States at chunk boundaries, for prefix caching (the system side of a
  * long-context KDA model keeps KDA states and a prefix cache: "3 分钟看懂
  * Kimi K3" (landx.limxdynamics.com), section "第一条主线", the paragraph after

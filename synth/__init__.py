@@ -168,6 +168,38 @@ def decode_inputs(N: int, H: int, dk: int, dv: int, steps: int, dtype: str = "bf
             "g_floor": g_floor}
 
 
+def to_mxfp8(x: torch.Tensor):
+    """MXFP8 encoding of x along its last dimension (input preparation, no
+    KDA arithmetic): blocks of 32 consecutive elements share one power-of-two
+    scale 2^E with E = floor(log2 amax) - 8 (8 is the exponent of e4m3's
+    largest power of two), clamped to [-127, 127]; each element is x / 2^E
+    saturated to +-448 and rounded to nearest even in e4m3 (finite-only
+    encoding, OCP MX).  Returns (e4m3 bytes as uint8, scale bytes E + 127 as
+    uint8 [..., d / 32], the decoded values in fp32: exactly what the bytes
+    mean, which both sides of a parity check use)."""
+    shp = x.shape
+    xb = x.float().reshape(*shp[:-1], shp[-1] // 32, 32)
+    amax = xb.abs().amax(-1, keepdim=True)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax)), torch.full_like(amax, -127.0)) - 8
+    e = e.clamp(-127, 127)
+    scale = torch.exp2(e)
+    f8 = (xb / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    dec = f8.float() * scale
+    return (f8.view(torch.uint8).reshape(shp), (e + 127).to(torch.uint8).squeeze(-1),
+            dec.reshape(shp))
+
+
+def mxfp8_inputs(inp: dict) -> dict:
+    """The prefill inputs with q, k and v in MXFP8: adds q8/k8/v8 (bytes) and
+    q_scale/k_scale/v_scale, and replaces q, k, v by their decoded values
+    (fp32) for the oracle."""
+    out = dict(inp)
+    for name in ("q", "k", "v"):
+        b, sc, dec = to_mxfp8(inp[name])
+        out[name + "8"], out[name + "_scale"], out[name] = b, sc, dec
+    return out
+
+
 def sample_positions(wid: int, T: int, n: int) -> list:
     """n distinct token positions in [0, T), seeded."""
     gen = torch.Generator(device="cpu")

@@ -258,3 +258,22 @@ def test_gate_validation(lib):
     a4 = dict(a, g=None, ws_bytes=a["ws_bytes"] - 1)
     assert call(lib, desc(gate=2), a4) == KDA_ERR_WORKSPACE_TOO_SMALL
     assert ws_status(lib, desc(gate=1)) == ws_status(lib, desc(gate=2)) == ws_status(lib, desc())
+
+
+def call_mx(lib, d, a, qs, ks, vs):
+    return _lib.chunk_forward_mx_raw(d, a["q"], qs, a["k"], ks, a["v"], vs, a["g"], a["beta"], a["h0"], a["cu"],
+                                     a["o"], a["ht"], a["ws"], a["ws_bytes"], None)
+
+
+def test_chunk_forward_mx_rejects(lib):
+    d = desc()
+    a = fake_args(lib, d)
+    sc = [(12 + i) * 64 * GB for i in range(3)]
+    assert call_mx(lib, d, a, None, sc[1], sc[2]) == KDA_ERR_INVALID_ARGUMENT        # a scale missing
+    assert call_mx(lib, desc(dtype=KDA_DTYPE_F32, d_k=64, d_v=64), fake_args(lib, desc(dtype=KDA_DTYPE_F32, d_k=64,
+                   d_v=64)), *sc) == KDA_ERR_UNSUPPORTED                              # MXFP8 feeds the bf16 path
+    assert call_mx(lib, d, dict(a, o=sc[0] - 4096), *sc) == KDA_ERR_INVALID_ARGUMENT  # o overlaps q_scale
+    assert call_mx(lib, d, a, sc[0], a["ws"] + 4096, sc[2]) == KDA_ERR_INVALID_ARGUMENT  # scale in the workspace
+    # q is one byte per element (8 MiB here): o starting inside it overlaps
+    assert call_mx(lib, d, dict(a, o=a["q"] + 4096 * 16 * 128 - 4096), *sc) == KDA_ERR_INVALID_ARGUMENT
+    assert call_mx(lib, d, dict(a, ws_bytes=a["ws_bytes"] - 1), *sc) == KDA_ERR_WORKSPACE_TOO_SMALL

@@ -256,6 +256,48 @@ def test_decode_gates(mode, d, dtype):
     assert es <= TOL[dtype]
 
 
+# ------------------------------------------------------- MXFP8 inputs
+# q, k, v as e4m3 bytes with a power-of-two scale per 32 channels
+# (synth.mxfp8_inputs); the oracle reads the very values the bytes mean.
+MX = {
+    "mx-d128-T300": lambda: _case(1, 300, 3, 128, "bf16", wid=180),
+    "mx-d64-varlen": lambda: _case(1, 0, 2, 64, "bf16", lengths=[5, 0, 128, 70, 200], wid=181),
+    "mx-d128-varlen-long-weak": lambda: _case(1, 0, 2, 128, "bf16", g_mode="weak",
+                                              lengths=[3000, 1, 4096, 0, 777], wid=182),
+    "mx-d128-T4096-H16": lambda: synth.workload_inputs(synth.WORKLOADS[1]),
+}
+
+
+@pytest.mark.parametrize("name", list(MX))
+def test_chunk_forward_mx(name):
+    inp = synth.mxfp8_inputs(MX[name]())
+    note(f"chunk_forward_mx {name} q{tuple(inp['q'].shape)}")
+    d = to_dev(inp)
+    o, ht = kda.chunk_forward_mx(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["v8"], d["v_scale"], d["g"],
+                                 d["beta"], h0=d.get("h0"), cu_seqlens=d.get("cu_seqlens"))
+    torch.cuda.synchronize()
+    ro, rht = oracle_forward(inp)
+    eo, eh = rel_err(f64(o), ro), rel_err(f64(ht), rht)
+    print(f"{name}: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_chunk_forward_mx_per_head_gate():
+    """MXFP8 inputs with a Gated DeltaNet gate."""
+    base = _case(1, 700, 2, 128, "bf16", wid=183)
+    inp = synth.mxfp8_inputs(base)
+    g_gpu, g_ref = _gate_inputs(base, "head")
+    note("chunk_forward_mx gate=head T=700 H=2 d=128")
+    d = to_dev(inp)
+    o, ht = kda.chunk_forward_mx(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["v8"], d["v_scale"],
+                                 g_gpu.cuda(), d["beta"], h0=d.get("h0"))
+    torch.cuda.synchronize()
+    ro, rht = oracle_forward(dict(inp, g=g_ref))
+    eo, eh = rel_err(f64(o), ro), rel_err(f64(ht), rht)
+    print(f"mx gate=head: err_o={eo:.3e} err_ht={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("d,dtype", [(64, "f32"), (128, "f32"), (64, "bf16"), (128, "bf16")])
 def test_decode_small(d, dtype):
