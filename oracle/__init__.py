@@ -11,6 +11,12 @@ Contents
     The token-by-token fp64 recurrence (the oracle proper).  Pinned by the
     invariant, closed-form, brute-force and library checks in
     ``tests/test_oracle_pins.py``.
+``kda_oracle_bwd.c`` / :func:`backward`
+    Its reverse-mode derivative, token by token in fp64 (the chain rule on
+    the forward's lines, last line first).  Pinned by central finite
+    differences of the forward, by the homogeneity identities of the
+    recurrence and by the floor's one-sided derivative in
+    ``tests/test_oracle_bwd_pins.py``.
 :mod:`oracle.chunked`
     The chunk-parallel (UT/WY) rewriting of the same recurrence, in fp64
     numpy.  Used only as a cross-formulation pin of :func:`forward`.
@@ -38,6 +44,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "kda_oracle.c")
+SOURCE_BWD = os.path.join(_HERE, "kda_oracle_bwd.c")
 LIBRARY = os.path.join(_HERE, "libkda_oracle.so")
 
 # No -ffast-math and no -march: IEEE semantics, no contraction into FMA.  -O3
@@ -46,10 +53,11 @@ LIBRARY = os.path.join(_HERE, "libkda_oracle.so")
 CFLAGS = ["-O3", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-Wall"]
 
 
-def build(source: str = SOURCE, out: str = LIBRARY) -> str:
-    """Compile the C oracle with gcc; returns the path of the shared object."""
+def build(source: str = SOURCE, out: str = LIBRARY, extra=(SOURCE_BWD,)) -> str:
+    """Compile the C oracle (forward and gradient) with gcc; returns the path
+    of the shared object."""
     tmp = out + ".tmp"
-    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, *extra, "-lm"], check=True)
     os.replace(tmp, out)
     return out
 
@@ -82,6 +90,17 @@ class Oracle:
                       p, p, ctypes.c_int]
         f.restype = ctypes.c_int
         self._lib.kda_oracle_max_threads.restype = ctypes.c_int
+
+    def _bwd(self):
+        # looked up on first use: a build of the forward source alone (the
+        # mutant tests make such builds) has no gradient symbol
+        f = self._lib.kda_oracle_backward
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        f.argtypes = [i64, p, i64, i64, i64, ctypes.c_double, p, p, p, p, p, p,
+                      p, p, p, p, p, p, p, p, ctypes.c_int]
+        f.restype = ctypes.c_int
+        return f
 
     def max_threads(self) -> int:
         return int(self._lib.kda_oracle_max_threads())
@@ -140,6 +159,50 @@ class Oracle:
                              n_threads=n_threads)
         return o[0], ht
 
+    def backward(self, q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None,
+                 g_floor: float = -0.125, n_threads: int = 0):
+        """Gradients of L = <do, o> + <dht, ht> for the forward above.
+
+        q, k, g: [B, T, H, dk]; v, do: [B, T, H, dv]; beta: [B, T, H];
+        h0, dht: [S, H, dk, dv] or None (zeros).  Returns a dict of float64
+        arrays dq, dk, dv, dg, dbeta (shapes of their inputs) and dh0
+        [S, H, dk, dv].  Where g is below g_floor, dg is 0; at g == g_floor
+        the gradient passes.
+        """
+        q, k, v, g, beta = (_as_f32(x) for x in (q, k, v, g, beta))
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        assert k.shape == q.shape and g.shape == q.shape
+        assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+        if cu_seqlens is None:
+            cu = np.arange(B + 1, dtype=np.int64) * T
+        else:
+            assert B == 1, "packed sequences need B == 1"
+            cu = np.ascontiguousarray(np.asarray(
+                cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+                dtype=np.int64))
+            assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+        n_seqs = len(cu) - 1
+        doa = _as_f64(do)
+        assert doa.shape == (B, T, H, dv)
+        h0a = None if h0 is None else _as_f64(h0)
+        dhta = None if dht is None else _as_f64(dht)
+        for a in (h0a, dhta):
+            if a is not None:
+                assert a.shape == (n_seqs, H, dk, dv)
+        out = dict(dq=np.zeros((B, T, H, dk)), dk=np.zeros((B, T, H, dk)),
+                   dv=np.zeros((B, T, H, dv)), dg=np.zeros((B, T, H, dk)),
+                   dbeta=np.zeros((B, T, H)), dh0=np.zeros((n_seqs, H, dk, dv)))
+        ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+        rc = self._bwd()(
+            n_seqs, ptr(cu), H, dk, dv, float(g_floor), ptr(q), ptr(k), ptr(v),
+            ptr(g), ptr(beta), ptr(h0a), ptr(doa), ptr(dhta), ptr(out["dq"]),
+            ptr(out["dk"]), ptr(out["dv"]), ptr(out["dg"]), ptr(out["dbeta"]),
+            ptr(out["dh0"]), int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_backward failed with status {rc}")
+        return out
+
 
 _default: Optional[Oracle] = None
 
@@ -159,3 +222,8 @@ def forward(*args, **kwargs):
 def decode_step(*args, **kwargs):
     """Module-level shortcut for :meth:`Oracle.decode_step`."""
     return default().decode_step(*args, **kwargs)
+
+
+def backward(*args, **kwargs):
+    """Module-level shortcut for :meth:`Oracle.backward`."""
+    return default().backward(*args, **kwargs)
