@@ -8,6 +8,7 @@ missing library raises.
     o, ht = chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None)
     o, ht, states = chunk_forward_states(q, k, v, g, beta, states_every=16)
     o = decode_step(q, k, v, g, beta, state)          # state updated in place
+    grads = chunk_backward(q, k, v, g, beta, do, h0=None, dht=None)
 
 g selects the gate: [.., H, d] one log-decay per key channel (KDA), [.., H]
 one per head (Gated DeltaNet), None no decay (DeltaNet).
@@ -22,12 +23,13 @@ from __future__ import annotations
 
 from typing import Optional, Tuple
 
-from ._lib import (CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,
+from ._lib import (BWD_STAGES, CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,
                    KDA_GATE_NONE, KDA_OK, ChunkDesc, KdaError, status_string, version)
 from . import _lib
 
-__all__ = ["chunk_forward", "chunk_forward_states", "chunk_forward_mx", "decode_step", "workspace_bytes",
-           "make_desc", "KdaError", "status_string", "version", "CHUNK_LAUNCHES"]
+__all__ = ["chunk_forward", "chunk_forward_states", "chunk_forward_mx", "chunk_backward", "decode_step",
+           "workspace_bytes", "backward_workspace_bytes", "make_desc", "KdaError", "status_string", "version",
+           "CHUNK_LAUNCHES", "BWD_STAGES"]
 
 
 def _torch():
@@ -205,6 +207,77 @@ def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
     if st != KDA_OK:
         raise KdaError(st, what)
     return o, ht, states
+
+
+def backward_workspace_bytes(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
+                             g_floor: float = -0.125, gate: int = KDA_GATE_CHANNEL) -> int:
+    """Device workspace one chunk_backward call of this shape needs."""
+    return _lib.backward_workspace_size(make_desc(B, T, H, d, dtype, n_seqs, chunk, g_floor, gate))
+
+
+def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chunk: int = 64,
+                   g_floor: float = -0.125, *, want_dh0: bool = True, out=None, workspace=None,
+                   validate_cu: bool = True, stream=None, events=None) -> dict:
+    """Gradients of L = <do, o> + <dht, ht> for chunk_forward with the same
+    inputs (kda_chunk_backward).  do: [B, T, H, d] in the input dtype; dht:
+    fp32 [S, H, d, d] or None (zero).  Returns a dict with dq, dk, dv (input
+    dtype), dg (the layout of g, input dtype; None without a gate), dbeta
+    (fp32 [B, T, H]) and dh0 (fp32 [S, H, d, d], or None when want_dh0 is
+    False).  `out` may supply those tensors.  events: optional
+    len(BWD_STAGES) + 1 raw hipEvent_t handles (kda_chunk_backward_timed)."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    dt = q.dtype
+    _check_dev("q", q, dt)
+    for name, t in (("k", k), ("v", v), ("do", do)):
+        _check_dev(name, t, dt, (B, T, H, d))
+    gate = _gate_of(g, 4)
+    gshape = (B, T, H, d) if gate == KDA_GATE_CHANNEL else (B, T, H)
+    _check_dev("g", g, dt, gshape)
+    _check_dev("beta", beta, torch.float32, (B, T, H))
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        if validate_cu:
+            check_cu_seqlens(cu_seqlens.cpu(), T)
+    S = n_seqs if n_seqs else B
+    _check_dev("h0", h0, torch.float32, (S, H, d, d))
+    _check_dev("dht", dht, torch.float32, (S, H, d, d))
+    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor, gate)
+    ws_bytes = _lib.backward_workspace_size(desc)
+    out = dict(out or {})
+    dev = q.device
+    for name, shape, odt in (("dq", (B, T, H, d), dt), ("dk", (B, T, H, d), dt), ("dv", (B, T, H, d), dt),
+                             ("dbeta", (B, T, H), torch.float32)):
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=odt, device=dev)
+        _check_dev(name, out[name], odt, shape)
+    if gate == KDA_GATE_NONE:
+        out["dg"] = None
+    else:
+        if out.get("dg") is None:
+            out["dg"] = torch.empty(gshape, dtype=dt, device=dev)
+        _check_dev("dg", out["dg"], dt, gshape)
+    if want_dh0:
+        if out.get("dh0") is None:
+            out["dh0"] = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+        _check_dev("dh0", out["dh0"], torch.float32, (S, H, d, d))
+    else:
+        out["dh0"] = None
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = _lib.chunk_backward_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                 _ptr(cu_seqlens), _ptr(do), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]),
+                                 _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), stream, events)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_backward_timed" if events is not None else "kda_chunk_backward")
+    return out
 
 
 def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, stream=None):

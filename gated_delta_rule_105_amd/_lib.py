@@ -26,10 +26,13 @@ KDA_GATE_NONE = 2      # no g: DeltaNet
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
            "kda_chunk_forward", "kda_chunk_forward_timed", "kda_chunk_forward_states_count",
-           "kda_chunk_forward_states", "kda_chunk_forward_mx", "kda_decode_step")
+           "kda_chunk_forward_states", "kda_chunk_forward_mx", "kda_chunk_backward_workspace_size",
+           "kda_chunk_backward", "kda_chunk_backward_timed", "kda_decode_step")
 
 # Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed).
 CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_scan", "kda_seg_forward")
+# Stages of one kda_chunk_backward call, in stream order (kda_chunk_backward_timed).
+BWD_STAGES = ("forward_replay", "kda_bwd_chunk", "kda_bwd_state", "kda_bwd_local")
 
 
 class KdaError(RuntimeError):
@@ -80,6 +83,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_forward_mx.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, sz, vp]
     lib.kda_chunk_forward_mx.restype = ctypes.c_int
+    lib.kda_chunk_backward_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(sz)]
+    lib.kda_chunk_backward_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_backward.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp]
+    lib.kda_chunk_backward.restype = ctypes.c_int
+    lib.kda_chunk_backward_timed.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp,
+                                                                                      ctypes.POINTER(vp)]
+    lib.kda_chunk_backward_timed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -136,6 +146,26 @@ def chunk_forward_mx_raw(desc: ChunkDesc, q, qs, k, ks, v, vs, g, beta, h0, cu, 
     """Call kda_chunk_forward_mx with raw integer addresses; returns the status."""
     return int(load().kda_chunk_forward_mx(ctypes.byref(desc), q, qs, k, ks, v, vs, g, beta, h0, cu, o, ht, ws,
                                            ctypes.c_size_t(ws_bytes), stream))
+
+
+def backward_workspace_size(desc: ChunkDesc) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().kda_chunk_backward_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_backward_workspace_size")
+    return int(out.value)
+
+
+def chunk_backward_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws,
+                       ws_bytes, stream, events=None) -> int:
+    """Call kda_chunk_backward (or its timed twin when `events`, len(BWD_STAGES)
+    + 1 raw hipEvent_t handles, is given); returns the status."""
+    args = (ctypes.byref(desc), q, k, v, g, beta, h0, cu, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws,
+            ctypes.c_size_t(ws_bytes), stream)
+    if events is None:
+        return int(load().kda_chunk_backward(*args))
+    arr = (ctypes.c_void_p * (len(BWD_STAGES) + 1))(*events)
+    return int(load().kda_chunk_backward_timed(*args, arr))
 
 
 def decode_step_raw(N, H, d_k, d_v, dtype, gate, g_floor, q, k, v, g, beta, state, o, stream) -> int:

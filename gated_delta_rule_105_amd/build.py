@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_backward.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -244,6 +244,94 @@ int kda_chunk_forward_mx(const kda_chunk_desc_t* d, const void* q, const uint8_t
                        stream, nullptr);
 }
 
+// ---- backward ------------------------------------------------------------
+
+namespace {
+
+bool plan_bwd(const kda_chunk_desc_t* d, const Sizes& s, kda::BwdPlan* bp) {
+  size_t chunk_states;
+  if (!state_slots(d, 1, &chunk_states)) return false;
+  const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
+  return kda::plan_backward(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s.tokens,
+                            chunk_states, bp);
+}
+
+int chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+                   const float* beta, const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dht,
+                   void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* events) {
+  Sizes s;
+  const int st = check_desc(d, &s);
+  if (st != KDA_OK) return st;
+  kda::BwdPlan bp;
+  if (!plan_bwd(d, s, &bp)) return KDA_ERR_UNSUPPORTED;
+  const bool has_tokens = s.tokens > 0;
+  const bool gated = d->gate != KDA_GATE_NONE;
+  if (!gated) {
+    g = nullptr;  // neither read nor written
+    dg = nullptr;
+  }
+  if (has_tokens && (!q || !k || !v || (gated && (!g || !dg)) || !beta || !dout || !dq || !dk || !dv || !dbeta))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if ((d->n_seqs > 0) != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < bp.ws_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // inputs may overlap one another; outputs overlap nothing
+  const Range ins[] = {range(q, s.x_bytes),   range(k, s.x_bytes),    range(v, s.x_bytes),
+                       range(g, s.g_bytes),   range(beta, s.beta_bytes), range(h0, s.state_bytes),
+                       range(dout, s.x_bytes), range(dht, s.state_bytes)};
+  const Range outs[] = {range(dq, s.x_bytes),      range(dk, s.x_bytes),         range(dv, s.x_bytes),
+                        range(dg, s.g_bytes),      range(dbeta, s.beta_bytes),   range(dh0, s.state_bytes),
+                        range(workspace, bp.ws_bytes)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return KDA_ERR_INVALID_ARGUMENT;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
+  const kda::ChunkInputs in{q, k, v, g, beta, nullptr, nullptr, nullptr};
+  const int e = kda::launch_chunk_backward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, bp, d->g_floor,
+                                           (int)d->gate, in, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0,
+                                           workspace, stream, events);
+  return e == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
+  if (!bytes) return KDA_ERR_INVALID_ARGUMENT;
+  Sizes s;
+  const int st = check_desc(d, &s);
+  if (st != KDA_OK) return st;
+  kda::BwdPlan bp;
+  if (!plan_bwd(d, s, &bp)) return KDA_ERR_UNSUPPORTED;
+  *bytes = bp.ws_bytes;
+  return KDA_OK;
+}
+
+int kda_chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+                       const float* beta, const float* h0, const int32_t* cu_seqlens, const void* dout,
+                       const float* dht, void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_backward(d, q, k, v, g, beta, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+int kda_chunk_backward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                             const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                             const void* dout, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                             float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events) {
+  if (!events) return KDA_ERR_INVALID_ARGUMENT;
+  return chunk_backward(d, q, k, v, g, beta, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace,
+                        workspace_bytes, stream, events);
+}
+
 int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate, float g_floor,
                     const void* q, const void* k, const void* v, const void* g, const float* beta, float* state,
                     void* o, void* stream) {

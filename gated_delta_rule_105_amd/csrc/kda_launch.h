@@ -151,6 +151,73 @@ int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const Seg
                          const int32_t* cu, void* o, float* ht, float* states, int every,
                          void* ws, void* stream, void* const* events);
 
+// ---- backward pass ------------------------------------------------------
+// Floats of one (chunk, head) record of the backward pass at width d: seven
+// [64][d] blocks (Qt, Kt, Kh, V, dO, Wk, Wv), three [64][64] (P, T, Abar),
+// gamma [d] and beta [64]; and of one (chunk, head) scratch area of its local
+// gradient kernel: six [64][d] blocks, two [64][64] and one [d].
+constexpr size_t bwd_rec_floats(int d) {
+  return (size_t)7 * kChunk * d + (size_t)3 * kChunk * kChunk + (size_t)d + kChunk;
+}
+constexpr size_t bwd_scr_floats(int d) { return (size_t)6 * kChunk * d + (size_t)2 * kChunk * kChunk + (size_t)d; }
+
+// Workspace of one backward call (byte offsets, each 256-byte aligned): the
+// forward replay's own workspace first, then its o (discarded), its final
+// states, the state after every full chunk, one zero state, the chunk
+// records, the scratch areas and the end-state gradient of every chunk.
+struct BwdPlan {
+  SegPlan fwd;
+  int64_t n_slots;  // upper bound of chunks over all sequences
+  size_t o_off, ht_off, states_off, zero_off, rec_off, scr_off, dh_off, ws_bytes;
+  size_t rec_floats, scr_floats;
+};
+
+// n_states: sequences; chunk_states: full chunks over all sequences (an
+// upper bound for a packed batch).  Returns false on overflow.
+inline bool plan_backward(int d, int esz, int n_rows, int64_t T, int H, bool packed, size_t tokens,
+                          size_t chunk_states, BwdPlan* p) {
+  if (!plan_segments(d, esz, n_rows, T, H, packed, &p->fwd)) return false;
+  const size_t a = 256, hh = (size_t)H, dd = (size_t)d * d * sizeof(float);
+  auto up = [&](size_t x) { return (x + a - 1) / a * a; };
+  p->n_slots = p->fwd.n_slots;
+  p->rec_floats = bwd_rec_floats(d);
+  p->scr_floats = bwd_scr_floats(d);
+  const double total = (double)p->fwd.ws_bytes + (double)tokens * hh * d * esz +
+                       ((double)n_rows + (double)chunk_states + 1.0) * hh * dd +
+                       (double)p->n_slots * hh * ((p->rec_floats + p->scr_floats) * 4.0 + (double)dd);
+  if (total > 1.0e15) return false;
+  size_t off = up(p->fwd.ws_bytes);
+  p->o_off = off;
+  off = up(off + tokens * hh * (size_t)d * esz);
+  p->ht_off = off;
+  off = up(off + (size_t)n_rows * hh * dd);
+  p->states_off = off;
+  off = up(off + chunk_states * hh * dd);
+  p->zero_off = off;
+  off = up(off + dd);
+  p->rec_off = off;
+  off = up(off + (size_t)p->n_slots * hh * p->rec_floats * 4);
+  p->scr_off = off;
+  off = up(off + (size_t)p->n_slots * hh * p->scr_floats * 4);
+  p->dh_off = off;
+  off = up(off + (size_t)p->n_slots * hh * dd);
+  p->ws_bytes = off;
+  return true;
+}
+
+// Launches of one backward call, in stream order.
+constexpr int kBwdLaunches = 4;  // forward replay (3 kernels), chunk records, state gradients, local gradients
+
+// Enqueue the backward pass.  All arguments were validated by the caller;
+// dout is [.., H, d] in the operand type, dht may be null (zero), dg is null
+// without a gate, dh0 may be null (not written).  events: null, or
+// kBwdLaunches + 1 hipEvent_t handles recorded before each stage and after
+// the last.  Returns a hipError_t.
+int launch_chunk_backward(int is_bf16, int d, int n_rows, int T, int H, const BwdPlan& bp, float g_floor, int gate,
+                          const ChunkInputs& in, const float* h0, const int32_t* cu, const void* dout,
+                          const float* dht, void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
+                          void* ws, void* stream, void* const* events);
+
 // Enqueue one decode step (gate: a kda_gate_t).  Returns a hipError_t.
 int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor, int gate,
                        const void* q, const void* k, const void* v,

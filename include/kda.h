@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 10100 /* 1.1.0 */
+#define KDA_VERSION 10200 /* 1.2.0 */
 
 typedef enum {
   KDA_OK = 0,
@@ -214,6 +214,50 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d,
                              float* states, int states_every,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * Backward pass of kda_chunk_forward (training: K3's KDA layers are trained
+ * chunk-parallel up to million-token contexts, "3 分钟看懂 Kimi K3"
+ * (landx.limxdynamics.com), "第一条主线"; the pages give no gradient, so it is
+ * derived from the recurrence above by the chain rule).
+ *
+ * Given dout = dL/do and dht = dL/dht for the forward with the same
+ * descriptor and inputs, writes the gradients of L with respect to every
+ * input:
+ *   dq, dk  : [B, T, H, d_k]  dtype          dv: [B, T, H, d_v] dtype
+ *   dg      : the layout of g (dtype), or NULL with KDA_GATE_NONE (ignored)
+ *   dbeta   : [B, T, H] fp32
+ *   dh0     : [S, H, d_k, d_v] fp32, or NULL (not written)
+ * dout: [B, T, H, d_v] dtype; dht: [S, H, d_k, d_v] fp32 or NULL (= zero).
+ * The floor max(g, g_floor) passes the gradient where g >= g_floor (on the
+ * floor itself too: the derivative from above) and gives 0 where g is below.
+ * The call replays the forward internally (its outputs are not needed).
+ * The workspace (kda_chunk_backward_workspace_size, 256-byte aligned) holds
+ * the replay's states and fp32 per-chunk records: about 0.6 MiB per
+ * (chunk of 64 tokens, head) at d = 128.  Outputs must not overlap each
+ * other, the inputs or the workspace.  Other rules as kda_chunk_forward.
+ */
+int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
+int kda_chunk_backward(const kda_chunk_desc_t* d,
+                       const void* q, const void* k, const void* v, const void* g,
+                       const float* beta, const float* h0, const int32_t* cu_seqlens,
+                       const void* dout, const float* dht,
+                       void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement twin of kda_chunk_backward: events[i] (5 caller-created
+ * hipEvent_t, entries may be NULL) is recorded before stage i and events[4]
+ * after the last.  Stages: 0 forward replay (three launches), 1 chunk records,
+ * 2 state gradients (reverse over the chunks), 3 local gradients.
+ */
+int kda_chunk_backward_timed(const kda_chunk_desc_t* d,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const float* beta, const float* h0, const int32_t* cu_seqlens,
+                             const void* dout, const float* dht,
+                             void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events);
 
 /*
  * One decode step: one new token for each of N sequences, state resident

@@ -29,7 +29,7 @@ from typing import Dict, Optional
 import torch
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "g": 4, "h0": 5,
-              "lengths": 6, "positions": 7, "state": 8}
+              "lengths": 6, "positions": 7, "state": 8, "do": 9, "dht": 10}
 BLOCK_TOKENS = 65536
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -132,6 +132,29 @@ def prefill_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16"
     else:
         out["cu_seqlens"] = None
     out["g_floor"] = g_floor
+    return out
+
+
+def grad_inputs(inp: dict, wid: int, dht: bool = True, device="cpu") -> dict:
+    """Upstream gradients for a backward call on the inputs `inp` of
+    prefill_inputs: do ~ N(0, 1) in the shape and dtype of v (drawn per
+    65,536-token block like the inputs), dht ~ N(0, 1) fp32 in the shape of
+    the final state, or None."""
+    v = inp["v"]
+    B, T, H, dv = v.shape
+    dk = inp["q"].shape[-1]
+    do = torch.empty_like(v, device=device)
+    nblk = max(1, math.ceil(T / BLOCK_TOKENS))
+    for b in range(B):
+        for blk in range(nblk):
+            t0, t1 = blk * BLOCK_TOKENS, min(T, (blk + 1) * BLOCK_TOKENS)
+            if t1 > t0:
+                do[b, t0:t1] = normal((t1 - t0, H, dv), wid, "do", b * 4096 + blk, device).to(v.dtype)
+    cu = inp.get("cu_seqlens")
+    n_states = B if cu is None else cu.numel() - 1
+    out = {"do": do, "dht": None}
+    if dht:
+        out["dht"] = normal((n_states, H, dk, dv), wid, "dht", 0, device)
     return out
 
 

@@ -277,3 +277,81 @@ def test_chunk_forward_mx_rejects(lib):
     # q is one byte per element (8 MiB here): o starting inside it overlaps
     assert call_mx(lib, d, dict(a, o=a["q"] + 4096 * 16 * 128 - 4096), *sc) == KDA_ERR_INVALID_ARGUMENT
     assert call_mx(lib, d, dict(a, ws_bytes=a["ws_bytes"] - 1), *sc) == KDA_ERR_WORKSPACE_TOO_SMALL
+
+
+# ---- backward ----------------------------------------------------------------
+
+def bws_status(lib, d):
+    out = ctypes.c_size_t(0)
+    st = lib.kda_chunk_backward_workspace_size(None if d is None else ctypes.byref(d), ctypes.byref(out))
+    return st, out.value
+
+
+def test_backward_workspace_size(lib):
+    st, n = bws_status(lib, desc())
+    assert st == KDA_OK and n % 256 == 0
+    # at least the forward's workspace, the state after every chunk, and an
+    # fp32 record plus scratch plus end-state gradient per (chunk, head)
+    fwd = ws_status(lib, desc())[1]
+    chunks = 4096 // 64
+    per_chunk = (7 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 6 * 64 * 128 + 2 * 64 * 64 + 128 + 128 * 128) * 4
+    assert n >= fwd + 16 * chunks * 128 * 128 * 4 + 16 * chunks * per_chunk
+    assert bws_status(lib, desc(d_k=96, d_v=96))[0] == KDA_ERR_UNSUPPORTED
+    assert bws_status(lib, desc(dtype=KDA_DTYPE_F32))[0] == KDA_ERR_UNSUPPORTED
+    assert bws_status(lib, desc(T=0))[0] == KDA_OK
+    assert lib.kda_chunk_backward_workspace_size(ctypes.byref(desc()), None) == KDA_ERR_INVALID_ARGUMENT
+
+
+BWD_NAMES = ["q", "k", "v", "g", "beta", "h0", "cu", "do", "dht", "dq", "dk", "dv", "dg", "dbeta", "dh0", "ws"]
+
+
+def bwd_args(lib, d):
+    st, ws = bws_status(lib, d)
+    assert st == KDA_OK
+    a = {name: (i + 1) * 64 * GB for i, name in enumerate(BWD_NAMES)}
+    a["ws_bytes"] = ws
+    if d.n_seqs == 0:
+        a["cu"] = None
+    return a
+
+
+def bwd_call(d, a, events=None):
+    return _lib.chunk_backward_raw(d, *(a[n] for n in BWD_NAMES), a["ws_bytes"], None, events)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: a.update(do=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(dq=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(dg=None), KDA_ERR_INVALID_ARGUMENT),                # gated: dg needed
+    (lambda a: a.update(dbeta=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(dk=a["dk"] + 4), KDA_ERR_INVALID_ARGUMENT),         # misaligned
+    (lambda a: a.update(ws=a["ws"] + 64), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(ws=None), KDA_ERR_INVALID_ARGUMENT),
+    (lambda a: a.update(ws_bytes=a["ws_bytes"] - 1), KDA_ERR_WORKSPACE_TOO_SMALL),
+    (lambda a: a.update(dq=a["q"] + 1024), KDA_ERR_INVALID_ARGUMENT),       # output overlaps an input
+    (lambda a: a.update(dv=a["dk"] + 4096), KDA_ERR_INVALID_ARGUMENT),      # outputs overlap
+    (lambda a: a.update(dh0=a["dht"]), KDA_ERR_INVALID_ARGUMENT),           # dh0 overlaps dht
+    (lambda a: a.update(ws=a["dbeta"]), KDA_ERR_INVALID_ARGUMENT),          # workspace overlaps an output
+    (lambda a: a.update(cu=7 * 64 * GB), KDA_ERR_INVALID_ARGUMENT),         # cu without n_seqs
+])
+def test_chunk_backward_rejects(lib, mutate, code):
+    d = desc()
+    a = bwd_args(lib, d)
+    mutate(a)
+    assert bwd_call(d, a) == code
+
+
+def test_chunk_backward_rejects_bad_desc(lib):
+    a = bwd_args(lib, desc())
+    assert bwd_call(desc(d_k=96, d_v=96), a) == KDA_ERR_UNSUPPORTED
+    assert bwd_call(desc(g_floor=-0.5), a) == KDA_ERR_INVALID_ARGUMENT
+    # the timed twin needs its event array
+    d = desc()
+    st = lib.kda_chunk_backward_timed(ctypes.byref(d), *(a[n] for n in BWD_NAMES),
+                                      ctypes.c_size_t(a["ws_bytes"]), None, None)
+    assert st == KDA_ERR_INVALID_ARGUMENT
+    # without a gate, g and dg are neither read nor written: a bad dg is ignored
+    dn = desc(gate=2)
+    an = bwd_args(lib, dn)
+    an.update(g=None, dg=3, dq=an["q"] + 1024)
+    assert bwd_call(dn, an) == KDA_ERR_INVALID_ARGUMENT                   # the overlap is still caught

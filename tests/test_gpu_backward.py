@@ -1,0 +1,182 @@
+"""Backward pass (kda_chunk_backward) vs the oracle's gradient, element by
+element, on seeded inputs and seeded upstream gradients.
+
+Tolerance, per gradient (dq, dk, dv, dg, dbeta, dh0): max|x - x_ref| /
+max|x_ref| <= 1e-4 on the fp32 path and <= 1e-2 on the bf16 path, as for the
+forward outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_105_amd as kda
+import oracle
+import synth
+from gpu_util import TOL, f64, note, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _case(B, T, H, d, dtype, h0=True, lengths=None, g_mode="floored", wid=300, sigma_g=1.0, dht=True):
+    inp = synth.prefill_inputs(B, T, H, d, d, dtype, wid=wid, sigma_g=sigma_g, h0=h0, lengths=lengths)
+    if g_mode == "weak":
+        inp["g"] = torch.full_like(inp["g"], -1e-3)
+    elif g_mode == "zero":
+        inp["g"] = torch.zeros_like(inp["g"])
+    elif g_mode == "raw":  # below the floor in places: the kernel floors, the gradient is 0 there
+        x = synth.normal(tuple(inp["g"].shape), wid, "g")
+        inp["g"] = (-torch.nn.functional.softplus(x)).to(inp["g"].dtype)
+    inp.update(synth.grad_inputs(inp, wid, dht=dht))
+    return inp
+
+
+def _gpu_backward(inp, g=None, gate_mode=None):
+    d = to_dev(inp)
+    gg = d["g"] if gate_mode is None else (None if g is None else g.cuda())
+    out = kda.chunk_backward(d["q"], d["k"], d["v"], gg, d["beta"], d["do"], h0=d.get("h0"),
+                             dht=d.get("dht"), cu_seqlens=d.get("cu_seqlens"))
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_backward(inp, g=None):
+    cu = inp.get("cu_seqlens")
+    return oracle.backward(inp["q"], inp["k"], inp["v"], inp["g"] if g is None else g, inp["beta"], inp["do"],
+                           h0=inp.get("h0"), dht=inp.get("dht"),
+                           cu_seqlens=None if cu is None else cu.cpu().numpy())
+
+
+def _check(name, out, ref, dtype, skip=()):
+    errs = {}
+    for key in GRADS:
+        if key in skip or out.get(key) is None:
+            continue
+        errs[key] = rel_err(f64(out[key]), ref[key])
+    print(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, f"{name}: {bad}"
+
+
+CASES = {
+    "f32-d64-T256": lambda: _case(1, 256, 2, 64, "f32", h0=False, wid=300),
+    "f32-d64-B2-T130": lambda: _case(2, 130, 3, 64, "f32", wid=301),
+    "f32-d64-T1": lambda: _case(1, 1, 2, 64, "f32", wid=302),
+    "f32-d64-varlen": lambda: _case(1, 0, 2, 64, "f32", lengths=[5, 0, 128, 70], wid=303),
+    "f32-d64-weak-decay": lambda: _case(1, 300, 2, 64, "f32", g_mode="weak", wid=304),
+    "f32-d64-no-decay": lambda: _case(1, 256, 2, 64, "f32", g_mode="zero", wid=305),
+    "f32-d64-below-floor": lambda: _case(1, 200, 2, 64, "f32", g_mode="raw", wid=306),
+    "f32-d64-no-dht": lambda: _case(1, 190, 2, 64, "f32", dht=False, wid=307),
+    "bf16-d128-T300": lambda: _case(1, 300, 3, 128, "bf16", wid=308),
+    "bf16-d128-varlen": lambda: _case(1, 0, 2, 128, "bf16", lengths=[1, 64, 65, 0, 100, 37], wid=309),
+    "bf16-d64-B2-T129": lambda: _case(2, 129, 2, 64, "bf16", wid=310),
+    "bf16-d128-weak-decay": lambda: _case(1, 700, 2, 128, "bf16", g_mode="weak", wid=311),
+    "bf16-d128-sigma2": lambda: _case(1, 333, 2, 128, "bf16", sigma_g=2.0, wid=312),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_chunk_backward(name):
+    inp = CASES[name]()
+    dtype = "bf16" if inp["q"].dtype == torch.bfloat16 else "f32"
+    note(f"chunk_backward {name} q{tuple(inp['q'].shape)} {dtype}")
+    out = _gpu_backward(inp)
+    ref = _oracle_backward(inp)
+    _check(name, out, ref, dtype)
+
+
+GATE_CASES = {
+    "head-bf16-d128-T300": (lambda: _case(1, 300, 2, 128, "bf16", wid=320), "head"),
+    "head-f32-d64-varlen": (lambda: _case(1, 0, 2, 64, "f32", lengths=[5, 0, 128, 70], wid=321), "head"),
+    "none-bf16-d128-T200": (lambda: _case(1, 200, 2, 128, "bf16", wid=322), "none"),
+    "none-f32-d64-B2-T130": (lambda: _case(2, 130, 2, 64, "f32", wid=323), "none"),
+}
+
+
+@pytest.mark.parametrize("name", list(GATE_CASES))
+def test_chunk_backward_gates(name):
+    """Gated DeltaNet (per-head g) and DeltaNet (no g).  The oracle runs the
+    per-head gate broadcast over the channels; its per-channel dg summed over
+    the channels is the per-head dg (every channel carries the same g)."""
+    make, mode = GATE_CASES[name]
+    inp = make()
+    dtype = "bf16" if inp["q"].dtype == torch.bfloat16 else "f32"
+    if mode == "head":
+        g_gpu = inp["g"][..., 0].contiguous()
+        g_ref = g_gpu[..., None].expand(inp["g"].shape).contiguous()
+    else:
+        g_gpu, g_ref = None, torch.zeros_like(inp["g"])
+    note(f"chunk_backward gate={mode} {name} q{tuple(inp['q'].shape)}")
+    out = _gpu_backward(inp, g=g_gpu, gate_mode=mode)
+    ref = _oracle_backward(inp, g=g_ref)
+    if mode == "head":
+        ref["dg"] = ref["dg"].sum(axis=-1)
+        _check(name, out, ref, dtype)
+    else:
+        assert out["dg"] is None
+        _check(name, out, ref, dtype, skip=("dg",))
+
+
+def test_backward_full_workload_sampled_heads():
+    """B=1, H=16, T=4096, d=128 bf16 (the prefill workload), all heads on the
+    GPU: every gradient element of heads 0 and 11 against the oracle, and the
+    homogeneity identities of the recurrence over all heads:
+    <dv, v> + <dh0, h0> = <do, o> + <dht, ht> and <dq, q> = <do, o>."""
+    inp = synth.workload_inputs(synth.WORKLOADS[1])
+    inp.update(synth.grad_inputs(inp, 1))
+    note("chunk_backward workload 1 (T=4096 H=16 d=128 bf16)")
+    out = _gpu_backward(inp)
+    d = to_dev(inp)
+    o, ht = kda.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"])
+    torch.cuda.synchronize()
+    heads = [0, 11]
+    sub = {key: (val[:, :, heads].contiguous() if key in ("q", "k", "v", "g", "beta", "do") else val)
+           for key, val in inp.items()}
+    sub["h0"] = inp["h0"][:, heads].contiguous()
+    sub["dht"] = inp["dht"][:, heads].contiguous()
+    ref = _oracle_backward(sub)
+    got = {key: (out[key][:, :, heads] if key != "dh0" else out[key][:, heads]) for key in GRADS}
+    _check("workload1 heads 0, 11", got, ref, "bf16")
+    # identities over all heads, in fp64 from the GPU's own outputs
+    v, q, do = f64(d["v"]), f64(d["q"]), f64(d["do"])
+    do_o = np.sum(do * f64(o))
+    scale = np.sum(np.abs(do * f64(o)))
+    lhs = np.sum(f64(out["dv"]) * v) + np.sum(f64(out["dh0"]) * f64(d["h0"]))
+    rhs = do_o + np.sum(f64(d["dht"]) * f64(ht))
+    print(f"identities: v/h0 {lhs:.6e} vs {rhs:.6e}; q {np.sum(f64(out['dq']) * q):.6e} vs {do_o:.6e}")
+    assert abs(lhs - rhs) <= 1e-2 * scale
+    assert abs(np.sum(f64(out["dq"]) * q) - do_o) <= 1e-2 * scale
+
+
+def test_backward_split_resume():
+    """The gradient of a sequence equals that of its two halves run with the
+    state and the state gradient handed across (split at a chunk boundary
+    and inside a chunk)."""
+    inp = _case(1, 400, 2, 64, "f32", wid=330)
+    d = to_dev(inp)
+    full = kda.chunk_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], h0=d["h0"], dht=d["dht"])
+    for t1 in (128, 150):
+        note(f"chunk_backward split at {t1}")
+        sl = lambda x, a, b: x[:, a:b].contiguous()  # noqa: E731
+        _, mid = kda.chunk_forward(sl(d["q"], 0, t1), sl(d["k"], 0, t1), sl(d["v"], 0, t1), sl(d["g"], 0, t1),
+                                   sl(d["beta"], 0, t1), h0=d["h0"])
+        tail = kda.chunk_backward(*(sl(d[x], t1, 400) for x in ("q", "k", "v", "g", "beta", "do")),
+                                  h0=mid, dht=d["dht"])
+        head = kda.chunk_backward(*(sl(d[x], 0, t1) for x in ("q", "k", "v", "g", "beta", "do")),
+                                  h0=d["h0"], dht=tail["dh0"])
+        torch.cuda.synchronize()
+        for key in ("dq", "dk", "dv", "dg", "dbeta"):
+            joined = torch.cat([head[key], tail[key]], dim=1)
+            e = rel_err(f64(joined), f64(full[key]))
+            assert e <= 1e-4, (t1, key, e)
+        assert rel_err(f64(head["dh0"]), f64(full["dh0"])) <= 1e-4
+
+
+def test_backward_deterministic():
+    inp = _case(1, 300, 2, 128, "bf16", wid=331)
+    note("chunk_backward determinism")
+    a = _gpu_backward(inp)
+    b = _gpu_backward(inp)
+    for key in GRADS:
+        assert torch.equal(a[key], b[key]), key
