@@ -25,9 +25,10 @@ a target).  ``other_workloads`` times the packed 8-sequence batch and the
 prefix-cache states (kda_chunk_forward_states) beside plain calls;
 ``gate_workloads`` times Gated DeltaNet and DeltaNet gates beside KDA on the
 prefill and decode workloads; ``mx_workload`` the headline workload with q,
-k, v in MXFP8 (kda_chunk_forward_mx).  Other
+k, v in MXFP8 (kda_chunk_forward_mx); ``backward_workload`` the backward pass
+(kda_chunk_backward) on the headline workload.  Other
 legs: ``--copy-calib MiB`` runs only a device copy of known size (for
-scaling the HBM byte counters), ``--only prefill|decode`` runs one leg,
+scaling the HBM byte counters), ``--only prefill|decode|backward`` runs one leg,
 ``--no-cpu`` skips the oracle.
 """
 from __future__ import annotations
@@ -73,6 +74,21 @@ LAUNCH_WORK = {
     "kda_seg_forward": dict(bytes=2 * 128, flop=2 * (3 * 128 * 128 + 128 * 65 // 2)),
 }
 
+# Backward pass (kda_chunk_backward) per (token, head) at d = 128, C = 64.
+# Algorithmic multiply-adds beyond the forward replay (needed triangles only):
+#   chunk-local recompute   d (C - 1) / 2 + 3 d (C + 1) / 2 + (C - 1)(C - 2) / 6
+#   state products          7 d^2   (Wk S, Kh dH, Qt^T dO, Wk^T dU, dU S^T, dO S^T, U dH^T)
+#   chunk-scaled products   6 d (C + 1) / 2 (P^T dO, dP, T^T dU, T^T dWk, dP Kh, dP^T Qt)
+#                           + 4 d (C - 1) / 2 (dA: two products, dA Kh, dA^T Kt)
+# plus the replay (FLOP_PER_TOKEN_HEAD).  Compulsory bytes: bf16 q, k, v, g,
+# do read, bf16 dq, dk, dv, dg written (256 B each), fp32 beta read and dbeta
+# written, plus h0 and dht read and dh0 written per (sequence, head).
+BWD_MAC_PER_TOKEN_HEAD = (128 * 63 // 2 + 3 * 128 * 65 // 2 + 63 * 62 // 6 + 7 * 128 * 128
+                          + 6 * 128 * 65 // 2 + 4 * 128 * 63 // 2)
+BWD_FLOP_PER_TOKEN_HEAD = 2 * BWD_MAC_PER_TOKEN_HEAD + FLOP_PER_TOKEN_HEAD
+BWD_BYTES_PER_TOKEN_HEAD = 9 * 2 * 128 + 2 * 4
+PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix (the backward's products run on fp32 MFMA)
+
 PREFILL = dict(B=1, T=4096, H=16, d=128, wid=1)
 DECODE = dict(N=256, H=32, d=128, wid=4)
 CPU_SAMPLE_SECONDS = 10.0
@@ -114,7 +130,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="timed prefill calls")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000, help="timed decode steps")
-    ap.add_argument("--only", choices=("prefill", "decode", "both"), default="both")
+    ap.add_argument("--only", choices=("prefill", "decode", "backward", "both"), default="both")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the packed and long-context workloads")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
@@ -382,6 +398,74 @@ def bench_mx(calls: int):
             "hbm_frac": (in_bytes + th * 2 * d + 2 * H * STATE_BYTES) / mean / 1e9 / PEAK_HBM_GBS}
 
 
+def bench_backward(calls: int):
+    """Backward pass (kda_chunk_backward) on the prefill workload with N(0, 1)
+    upstream gradients for o and ht: mean call and per-stage durations (HIP
+    events on the launch stream, kda_chunk_backward_timed)."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[1]
+    inp = synth.workload_inputs(w, device="cuda")
+    inp.update(synth.grad_inputs(inp, w.wid, device="cuda"))
+    B, T, H, d = inp["q"].shape
+    ws = torch.empty(kda.backward_workspace_bytes(B, T, H, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def call(events=None):
+        return kda.chunk_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], h0=inp["h0"],
+                                  dht=inp["dht"], out=out, workspace=ws, events=events)
+
+    out.update(call())
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    mean = sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+    n_ev = len(kda.BWD_STAGES) + 1
+    evl = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(calls)]
+    for row in evl:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for row in evl:
+        call([e.cuda_event for e in row])
+    torch.cuda.synchronize()
+    stage = {name: sum(row[j].elapsed_time(row[j + 1]) for row in evl) / calls * 1e-3
+             for j, name in enumerate(kda.BWD_STAGES)}
+    token_heads = B * T * H
+    flop = token_heads * BWD_FLOP_PER_TOKEN_HEAD
+    byts = token_heads * BWD_BYTES_PER_TOKEN_HEAD + 3 * B * H * STATE_BYTES
+    log(f"backward {calls} calls: mean {mean * 1e6:.1f} us; per stage "
+        + ", ".join(f"{n} {t * 1e6:.1f} us" for n, t in stage.items()))
+    # the dominant stage against the fp32 matrix peak: its share of the
+    # algorithmic products (the local-gradient kernel does all but the
+    # chunk-local recompute and the three state-gradient products)
+    mac_chunk = 128 * 63 // 2 + 3 * 128 * 65 // 2 + 63 * 62 // 6
+    mac_state = 3 * 128 * 128 + 128 * 65 // 2
+    stage_flop = {"forward_replay": FLOP_PER_TOKEN_HEAD, "kda_bwd_chunk": 2 * mac_chunk,
+                  "kda_bwd_state": 2 * mac_state,
+                  "kda_bwd_local": 2 * (BWD_MAC_PER_TOKEN_HEAD - mac_chunk - mac_state)}
+    dom = max(stage, key=stage.get)
+    dom_tf = stage_flop[dom] * token_heads / stage[dom] / 1e12
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": "kda-backward-bf16-B1-H16-T4096-d128 (do, dht ~ N(0,1))", "mean_call_us": mean * 1e6,
+            "value": B * T / mean, "unit": "tokens/s",
+            "stage_us": {n: t * 1e6 for n, t in stage.items()},
+            "call_roofline": {"bound": "mfma", "achieved": flop / mean / 1e12, "peak": PEAK_F32_MFMA_TFLOPS,
+                              "unit": "TFLOP/s", "frac": flop / mean / 1e12 / PEAK_F32_MFMA_TFLOPS,
+                              "algorithmic_flop": flop, "hbm_frac": byts / mean / 1e9 / PEAK_HBM_GBS},
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tf, "peak": PEAK_F32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": dom_tf / PEAK_F32_MFMA_TFLOPS,
+                         "algorithmic_flop": stage_flop[dom] * token_heads, "mean_launch_us": stage[dom] * 1e6}}
+
+
 def bench_decode(steps: int, warmup: int):
     import torch
     import gated_delta_rule_105_amd as kda
@@ -494,6 +578,9 @@ def main() -> int:
         out["states_workloads"] = bench_states(50)
         out["gate_workloads"] = bench_gates(50, 100)
         out["mx_workload"] = bench_mx(100)
+        out["backward_workload"] = bench_backward(20)
+    if args.only == "backward":
+        out["backward_workload"] = bench_backward(args.steps)
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

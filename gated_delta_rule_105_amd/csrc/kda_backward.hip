@@ -56,35 +56,64 @@ __device__ __forceinline__ float ldx(const bf16_t* p) { return bf16_to_f32(*p); 
 __device__ __forceinline__ void stx(float* p, float x) { *p = x; }
 __device__ __forceinline__ void stx(bf16_t* p, float x) { *p = f32_to_bf16(x); }
 
-// Four consecutive-k values of one operand row: k stride `s` elements.
-__device__ __forceinline__ f32x4 ld4(const float* p, int s) {
-  if (s == 1) return *(const f32x4*)p;
-  return (f32x4){p[0], p[s], p[2 * s], p[3 * s]};
-}
-
 // One 16x16 tile: acc += sum_k A(i, k) B(k, j) over k < K (K % 16 == 0),
 // A(i, k) = A[i * ai + k * ak], B(k, j) = B[k * bk + j * bj]; A and B point
 // at the tile's first row / column.  bs: per-k scale of B, or null.  The
 // lane layout is the one of kda_device.h: lane 16 g + i supplies row i of A
-// and column i of B at k = k0 + 4 g + e in issue e, and holds D[4 g + r][i].
-__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float* A, int ai, int ak, const float* B, int bk,
-                                          int bj, const float* bs, int K, int lane) {
+// and column i of B at k = 16 kk + 4 g + e in issue e of k-block kk, and
+// holds D[4 g + r][i].  Every operand load of the tile is issued before the
+// first product (one memory latency per tile, not one per k-block); a unit
+// k-stride reads 16 bytes per lane.
+template <int K>
+__device__ __forceinline__ f32x4 tile_mma_k(f32x4 acc, const float* A, int ai, int ak, const float* B, int bk,
+                                            int bj, const float* bs, int lane) {
+  constexpr int NK = K / 16;
   const int i = lane & 15, g = lane >> 4;
   const float* pa = A + i * ai + 4 * g * ak;
   const float* pb = B + i * bj + 4 * g * bk;
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const f32x4 a = ld4(pa + k0 * ak, ak);
-    f32x4 b = ld4(pb + k0 * bk, bk);
-    if (bs) {
-      const f32x4 s = *(const f32x4*)(bs + k0 + 4 * g);
-      b = (f32x4){b[0] * s[0], b[1] * s[1], b[2] * s[2], b[3] * s[3]};
+  f32x4 a[NK], b[NK];
+  if (ak == 1) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) a[kk] = *(const f32x4*)(pa + 16 * kk);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const float* p = pa + 16 * kk * ak;
+      a[kk] = (f32x4){p[0], p[ak], p[2 * ak], p[3 * ak]};
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+  }
+  if (bk == 1) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) b[kk] = *(const f32x4*)(pb + 16 * kk);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const float* p = pb + 16 * kk * bk;
+      b[kk] = (f32x4){p[0], p[bk], p[2 * bk], p[3 * bk]};
+    }
+  }
+  if (bs) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const f32x4 sc = *(const f32x4*)(bs + 16 * kk + 4 * g);
+      b[kk] = (f32x4){b[kk][0] * sc[0], b[kk][1] * sc[1], b[kk][2] * sc[2], b[kk][3] * sc[3]};
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][0], b[kk][0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][1], b[kk][1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][2], b[kk][2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][3], b[kk][3], acc, 0, 0, 0);
   }
   return acc;
+}
+// The same for the two depths the chunk algebra has: K = 64 (the chunk) or
+// K = 128 (the key/value width); K = 64 is also the width 64.
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float* A, int ai, int ak, const float* B, int bk,
+                                          int bj, const float* bs, int K, int lane) {
+  if (K == 128) return tile_mma_k<128>(acc, A, ai, ak, B, bk, bj, bs, lane);
+  return tile_mma_k<64>(acc, A, ai, ak, B, bk, bj, bs, lane);
 }
 
 // Operand views for one product: A is M x K, B is K x N.
@@ -138,15 +167,24 @@ __device__ void gemm(float* out, int ldo, int M, int N, float alpha, bool acc_in
 }
 
 // Floats of one (chunk, head) record at key/value width D: Qt, Kt, Kh, V,
-// dO, Wk, Wv ([C][D] each, rows past the chunk's end zero), P, T, Abar
-// ([C][C]), gamma [D], beta [C] (0 past the end).
+// dO, Wk, Wv, Gamma ([C][D] each, rows past the chunk's end zero; Gamma
+// there repeats the last row), P, T, Abar ([C][C]), gamma [D], beta [C] (0
+// past the end).
 template <int D> struct Rec {
   static constexpr int QT = 0, KT = C * D, KH = 2 * C * D, VV = 3 * C * D, DO = 4 * C * D, WK = 5 * C * D,
-                       WV = 6 * C * D, PM = 7 * C * D, TM = PM + C * C, AB = TM + C * C, GAM = AB + C * C,
-                       BET = GAM + D, FLOATS = BET + C;
+                       WV = 6 * C * D, GM = 7 * C * D, PM = 8 * C * D, TM = PM + C * C, AB = TM + C * C,
+                       GAM = AB + C * C, BET = GAM + D, FLOATS = BET + C;
+};
+// Threads of the per-chunk kernels, and how they split the rows of a chunk
+// for the prefix sums over rows: NG groups of RG rows, one thread per
+// (group, channel).
+constexpr int kThreads = 512;
+template <int D> struct RowSplit {
+  static constexpr int NG = kThreads / D, RG = C / NG;
+  static_assert(NG * D == kThreads && NG * RG == C, "row groups tile the chunk");
 };
 // Floats of one (chunk, head) scratch area of kda_bwd_local: U (then Dk),
-// dU (then E = Dk + dA Kh), dWk (then dGamma), Dv, dQt, dKh ([C][D] each),
+// dU (then E = Dk + dA Kh), dWk, Dv, dQt, dKh ([C][D] each),
 // dP, dA ([C][C]), dgamma-last [D].
 template <int D> struct Scr {
   static constexpr int U = 0, DU = C * D, DWK = 2 * C * D, DV = 3 * C * D, DQT = 4 * C * D, DKH = 5 * C * D,
@@ -210,7 +248,7 @@ __device__ __forceinline__ float gate_at(const void* g, int gate, bool bf16, int
 // Chunk record: Gamma and the scaled rows, the two Gram blocks, the inverse
 // by forward substitution, Wk and Wv.
 template <typename T, int D>
-__global__ void __launch_bounds__(512) kda_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k,
+__global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const void* __restrict__ g,
                                                      const float* __restrict__ beta, const T* __restrict__ dout,
                                                      const int32_t* __restrict__ cu, int n_rows, int T_per, int H,
@@ -230,35 +268,50 @@ __global__ void __launch_bounds__(512) kda_bwd_chunk(const T* __restrict__ q, co
   const bool bf = sizeof(T) == 2;
   const int len = pos.len;
 
-  // element-wise: one thread per key channel walks the rows (prefix sum)
-  if (tid < D) {
-    const int c = tid;
-    float G = 0.f;
-    for (int r = 0; r < C; ++r) {
+  // element-wise.  Gamma: per channel, each group of RG rows takes its own
+  // prefix sums, then adds the sums of the groups before it.
+  {
+    typedef RowSplit<D> RS;
+    __shared__ float gsum[RS::NG][D];
+    const int c = tid % D, grp = tid / D, r0 = grp * RS::RG;
+    float gl[RS::RG];
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < RS::RG; ++i) {
+      const int r = r0 + i;
+      if (r < len) run += fmaxf(gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c), g_floor);
+      gl[i] = run;
+    }
+    gsum[grp][c] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int j = 0; j < grp; ++j) off += gsum[j][c];
+#pragma unroll
+    for (int i = 0; i < RS::RG; ++i) {
+      const int r = r0 + i;
       float qv = 0.f, kv = 0.f;
       if (r < len) {
         const int64_t th = (pos.tok0 + r) * H + h;
-        G += fmaxf(gate_at(g, gate, bf, th, D, c), g_floor);
         qv = ldx(q + th * D + c);
         kv = ldx(k + th * D + c);
       }
+      const float G = off + gl[i];
       const float e = __expf(G), ei = __expf(-G);
-      Rp[R::QT + r * D + c] = qv * e;
-      Rp[R::KT + r * D + c] = kv * e;
-      Rp[R::KH + r * D + c] = kv * ei;
+      const int x = r * D + c;
+      Rp[R::GM + x] = G;
+      Rp[R::QT + x] = qv * e;
+      Rp[R::KT + x] = kv * e;
+      Rp[R::KH + x] = kv * ei;
+      if (r == C - 1) Rp[R::GAM + c] = e;
     }
-    Rp[R::GAM + c] = __expf(G);
-  } else if (tid < 2 * D) {
-    const int c = tid - D;
-    for (int r = 0; r < C; ++r) {
-      const int64_t th = (pos.tok0 + r) * H + h;
-      Rp[R::VV + r * D + c] = r < len ? ldx(v + th * D + c) : 0.f;
-      Rp[R::DO + r * D + c] = r < len ? ldx(dout + th * D + c) : 0.f;
-    }
-  } else if (tid < 2 * D + C) {
-    const int r = tid - 2 * D;
-    Rp[R::BET + r] = r < len ? beta[(pos.tok0 + r) * H + h] : 0.f;
   }
+  for (int x = tid; x < C * D; x += blockDim.x) {
+    const int r = x / D, c = x % D;
+    const int64_t th = (pos.tok0 + r) * H + h;
+    Rp[R::VV + x] = r < len ? ldx(v + th * D + c) : 0.f;
+    Rp[R::DO + x] = r < len ? ldx(dout + th * D + c) : 0.f;
+  }
+  if (tid < C) Rp[R::BET + tid] = tid < len ? beta[(pos.tok0 + tid) * H + h] : 0.f;
   __syncthreads();
 
   // Abar = strict_lower(Kt Kh^T), P = lower_incl(Qt Kh^T)
@@ -268,23 +321,46 @@ __global__ void __launch_bounds__(512) kda_bwd_chunk(const T* __restrict__ q, co
        nullptr, nullptr, 0, wave, nw, lane);
   __syncthreads();
   for (int x = tid; x < C * C; x += blockDim.x) {
-    const int r = x / C, s = x % C;
-    As[r][s] = Rp[R::BET + r] * Rp[R::AB + x];
+    const int r = x / C, c = x % C;
+    As[r][c] = Rp[R::BET + r] * Rp[R::AB + x];
+    Ts[r][c] = r == c ? 1.f : 0.f;
   }
   __syncthreads();
-  // T = (I + A)^{-1}, A strictly lower: column s by forward substitution,
-  // T[r][s] = -sum_{s <= m < r} A[r][m] T[m][s] for r > s, T[s][s] = 1
+  // T = (I + A)^{-1}, A strictly lower, over 4 x 4 blocks of 16.  Diagonal
+  // blocks by forward substitution, one lane per column:
+  //   T[r][s] = -sum_{s <= m < r} A[r][m] T[m][s]   (s < r in the same block)
   if (tid < C) {
-    const int s = tid;
-    for (int r = 0; r < s; ++r) Ts[r][s] = 0.f;
-    Ts[s][s] = 1.f;
-    for (int r = s + 1; r < C; ++r) {
+    const int s = tid, end = (s | 15) + 1;
+    for (int r = s + 1; r < end; ++r) {
       float acc = 0.f;
       for (int m = s; m < r; ++m) acc += As[r][m] * Ts[m][s];
       Ts[r][s] = -acc;
     }
   }
   __syncthreads();
+  // then block row i from the rows above it, one wave per block (i, j < i):
+  //   T_ij = -T_ii sum_{j <= m < i} A_im T_mj
+  // two 16 x 16 MFMA products; the first one's accumulator is the second
+  // one's B operand as it stands (its rows run over k).
+  for (int bi = 1; bi < C / 16; ++bi) {
+    if (wave < bi) {
+      const int bj = wave, ii = lane & 15, g = lane >> 4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int bm = bj; bm < bi; ++bm)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = 16 * bm + 4 * g + e;  // issue e: lane group g supplies k = 4 g + e of the block
+          x = __builtin_amdgcn_mfma_f32_16x16x4f32(As[16 * bi + ii][kk], Ts[kk][16 * bj + ii], x, 0, 0, 0);
+        }
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(Ts[16 * bi + ii][16 * bi + 4 * g + e], x[e], y, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ts[16 * bi + 4 * g + e][16 * bj + ii] = -y[e];
+    }
+    __syncthreads();
+  }
   for (int x = tid; x < C * C; x += blockDim.x) Rp[R::TM + x] = Ts[x / C][x % C];
   __syncthreads();
   // Wk = T diag(beta) Kt, Wv = T diag(beta) V
@@ -296,21 +372,58 @@ __global__ void __launch_bounds__(512) kda_bwd_chunk(const T* __restrict__ q, co
 
 // ---------------------------------------------------------------------------
 // Reverse pass over the chunks of one sequence for 16 columns of dS.
+//
+// Fragments of one 16-row (or 16-column) panel over a full k range, loaded
+// in one go: A(i, k) = p[i * ai + k * ak] (lane row i, k = 16 kk + 4 g + e).
+template <int NK>
+__device__ __forceinline__ void load_panel(f32x4 (&f)[NK], const float* p, int ai, int ak, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const float* q = p + i * ai + 4 * g * ak;
+  if (ak == 1) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) f[kk] = *(const f32x4*)(q + 16 * kk);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const float* r = q + 16 * kk * ak;
+      f[kk] = (f32x4){r[0], r[ak], r[2 * ak], r[3 * ak]};
+    }
+  }
+}
+template <int NK>
+__device__ __forceinline__ f32x4 mma_panels(f32x4 acc, const f32x4 (&a)[NK], const f32x4 (&b)[NK]) {
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][0], b[kk][0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][1], b[kk][1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][2], b[kk][2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][3], b[kk][3], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// One workgroup per (sequence, head, 16 state columns), four waves: wave w
+// owns row tile w of dU (C / 16 = 4 tiles) and row tiles w, w + 4, .. of dS.
+// Each chunk step loads every record operand it needs (P^T, Kh, dO, Qt^T,
+// Wk^T panels) before its first barrier, so one memory latency covers the
+// step.  Workgroups are ordered so that the column blocks of a (sequence,
+// head) pair have the same block index mod 8, i.e. share one XCD's L2 (the
+// record operands are common to them).
 template <int D>
 __global__ void __launch_bounds__(256) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
                                                      const int32_t* __restrict__ cu, int n_rows, int T_per, int H,
                                                      float* __restrict__ dHs, float* __restrict__ dh0) {
   typedef Rec<D> R;
-  constexpr int NCB = D / 16;
+  constexpr int NCB = D / 16, NT = D / 64, NKC = C / 16, NKD = D / 16;
   __shared__ __align__(16) float dH[D][16];
   __shared__ __align__(16) float dU[C][16];
   __shared__ __align__(16) float gam[D];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int pair = blockIdx.x / NCB, cb = blockIdx.x % NCB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int cb = (b / 8) % NCB, pair = 8 * (b / (8 * NCB)) + b % 8;
   const int n = pair / H, h = pair % H;
   if (n >= n_rows) return;
-  const int j0 = cb * 16;
-  // this sequence's chunks and the slot of its first one
+  const int j0 = cb * 16, ii = lane & 15, g = lane >> 4;
   int64_t base = 0, nc;
   if (cu) {
     for (int m = 0; m < n; ++m) base += ((int64_t)cu[m + 1] - cu[m] + C - 1) / C;
@@ -328,6 +441,17 @@ __global__ void __launch_bounds__(256) kda_bwd_state(const float* __restrict__ r
     const int64_t slot = base + m;
     const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
     float* dHo = dHs + (slot * H + h) * (int64_t)D * D;
+    // every record operand of this step
+    f32x4 aP[NKC], aKh[NKD], bO[NKC], aQ[NT][NKC], aW[NT][NKC];
+    load_panel(aP, Rp + R::PM + 16 * wave, 1, C, lane);   // P^T rows 16 w..: P[r][16 w + i]
+    load_panel(aKh, Rp + R::KH + 16 * wave * D, D, 1, lane);
+    load_panel(bO, Rp + R::DO + j0, 1, D, lane);          // B(k = r, j) = dO[r][j0 + j]
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r0 = 16 * (wave + 4 * t);
+      load_panel(aQ[t], Rp + R::QT + r0, 1, D, lane);     // Qt^T rows r0..: Qt[r][r0 + i]
+      load_panel(aW[t], Rp + R::WK + r0, 1, D, lane);
+    }
     for (int x = tid; x < D; x += blockDim.x) gam[x] = Rp[R::GAM + x];
     __syncthreads();  // dH and gamma ready
     for (int x = tid; x < D * 16; x += blockDim.x) {
@@ -336,25 +460,38 @@ __global__ void __launch_bounds__(256) kda_bwd_state(const float* __restrict__ r
     }
     // dU = P^T dO + Kh diag(gamma) dH                          [C x 16]
     {
-      const MatA a1 = trans(Rp + R::PM, C), a2 = rows(Rp + R::KH, D);
-      const MatB b1 = krows(Rp + R::DO + j0, D), b2 = krows(&dH[0][0], 16, gam);
-      gemm(&dU[0][0], 16, C, 16, 1.f, false, kFull, nullptr, a1, b1, C, &a2, &b2, D, wave, nw, lane);
+      f32x4 bH[NKD];
+#pragma unroll
+      for (int kk = 0; kk < NKD; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 16 * kk + 4 * g + e;
+          bH[kk][e] = gam[k] * dH[k][ii];
+        }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mma_panels(acc, aP, bO);
+      acc = mma_panels(acc, aKh, bH);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dU[16 * wave + 4 * g + e][ii] = acc[e];
     }
     __syncthreads();  // dU ready; every wave is done reading dH
     // dH <- diag(gamma) dH + Qt^T dO - Wk^T dU                  [D x 16]
     {
-      const int tiles = D / 16;
-      const int i = lane & 15, g = lane >> 4;
-      for (int t = wave; t < tiles; t += nw) {
-        const int r0 = t * 16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_mma(acc, Rp + R::QT + r0, 1, D, Rp + R::DO + j0, D, 1, nullptr, C, lane);
-        f32x4 neg = {0.f, 0.f, 0.f, 0.f};
-        neg = tile_mma(neg, Rp + R::WK + r0, 1, D, &dU[0][0], 16, 1, nullptr, C, lane);
+      f32x4 bU[NKC];
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bU[kk][e] = dU[16 * kk + 4 * g + e][ii];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int r0 = 16 * (wave + 4 * t);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, neg = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_panels(acc, aQ[t], bO);
+        neg = mma_panels(neg, aW[t], bU);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = r0 + 4 * g + e;
-          dH[r][i] = gam[r] * dH[r][i] + acc[e] - neg[e];  // this lane's own element only
+          dH[r][ii] = gam[r] * dH[r][ii] + acc[e] - neg[e];  // this lane's own element only
         }
       }
     }
@@ -370,7 +507,7 @@ __global__ void __launch_bounds__(256) kda_bwd_state(const float* __restrict__ r
 // ---------------------------------------------------------------------------
 // Local gradients of one chunk.
 template <typename T, int D>
-__global__ void __launch_bounds__(512) kda_bwd_local(
+__global__ void __launch_bounds__(kThreads) kda_bwd_local(
     const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
     int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
@@ -402,11 +539,16 @@ __global__ void __launch_bounds__(512) kda_bwd_local(
     const MatB b1 = krows(Rp + R::DO, D), b2 = krows(dH, D, gam);
     gemm(Wp + W::DU, D, C, D, 1.f, false, kFull, nullptr, a1, b1, C, &a2, &b2, D, wave, nw, lane);
   }
-  // dgamma-last: sum_j dH_cj S_next_cj per channel
-  for (int c = tid; c < D; c += blockDim.x) {
+  // dgamma-last: sum_j dH_cj S_next_cj per channel; NP neighbouring lanes
+  // share a channel and combine their partial sums by shuffles
+  {
+    constexpr int NP = kThreads / D;
+    const int c = tid / NP, part = tid % NP;
     float acc = 0.f;
-    for (int j = 0; j < D; ++j) acc += dH[c * D + j] * Sn[c * D + j];
-    Wp[W::DGL + c] = acc;
+    for (int j = part; j < D; j += NP) acc += dH[c * D + j] * Sn[c * D + j];
+#pragma unroll
+    for (int m = 1; m < NP; m <<= 1) acc += __shfl_xor(acc, m);
+    if (part == 0) Wp[W::DGL + c] = acc;
   }
   __syncthreads();
   for (int x = tid; x < C * D; x += blockDim.x) Wp[W::U + x] += Rp[R::WV + x];
@@ -448,61 +590,76 @@ __global__ void __launch_bounds__(512) kda_bwd_local(
   for (int x = tid; x < C * D; x += blockDim.x) Wp[W::DU + x] += Wp[W::U + x];
   __syncthreads();
 
-  // 6: element-wise.  dbeta per row; dv; then per channel the prefix sums
-  // of the gate again (same order as the record), dq, dk, dGamma.
+  // 6: element-wise.
   const bool bf = sizeof(T) == 2;
   const int len = pos.len;
-  if (tid < C) {
-    const int r = tid;
+  // dbeta: 8 neighbouring lanes per row, combined by shuffles
+  {
+    const int r = tid / 8, part = tid % 8;
     float acc = 0.f;
-    for (int c = 0; c < D; ++c)
+    for (int c = part; c < D; c += 8)
       acc += Wp[W::U + r * D + c] * Rp[R::KT + r * D + c] + Wp[W::DV + r * D + c] * Rp[R::VV + r * D + c];
-    for (int s = 0; s < r; ++s) acc += Wp[W::DA + r * C + s] * Rp[R::AB + r * C + s];
-    if (r < len) dbeta[(pos.tok0 + r) * H + h] = acc;
+    for (int s2 = part; s2 < r; s2 += 8) acc += Wp[W::DA + r * C + s2] * Rp[R::AB + r * C + s2];
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
+    if (part == 0 && r < len) dbeta[(pos.tok0 + r) * H + h] = acc;
   }
   for (int x = tid; x < len * D; x += blockDim.x) {
     const int r = x / D, c = x % D;
     stx(dv + ((pos.tok0 + r) * H + h) * D + c, bet[r] * Wp[W::DV + x]);
   }
-  float* dG = Wp + W::DWK;  // dGamma, then the masked dg per channel
-  if (tid < D) {
-    const int c = tid;
-    float G = 0.f;
-    for (int r = 0; r < C; ++r) {
-      if (r < len) G += fmaxf(gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c), g_floor);
-      const float e = __expf(G), ei = __expf(-G);
-      const int x = r * D + c;
-      const float dqt = Wp[W::DQT + x], dkt = bet[r] * Wp[W::DU + x], dkh = Wp[W::DKH + x];
-      dG[x] = dqt * Rp[R::QT + x] + dkt * Rp[R::KT + x] - dkh * Rp[R::KH + x];
-      if (r < len) {
-        const int64_t o = ((pos.tok0 + r) * H + h) * D + c;
-        stx(dq + o, dqt * e);
-        stx(dk + o, dkt * e + dkh * ei);
-      }
+  // dq, dk and dGamma per element (Gamma from the record)
+  __shared__ float dG[C][D];
+  for (int x = tid; x < C * D; x += blockDim.x) {
+    const int r = x / D, c = x % D;
+    const float G = Rp[R::GM + x];
+    const float e = __expf(G), ei = __expf(-G);
+    const float dqt = Wp[W::DQT + x], dkt = bet[r] * Wp[W::DU + x], dkh = Wp[W::DKH + x];
+    dG[r][c] = dqt * Rp[R::QT + x] + dkt * Rp[R::KT + x] - dkh * Rp[R::KH + x];
+    if (r < len) {
+      const int64_t o = ((pos.tok0 + r) * H + h) * D + c;
+      stx(dq + o, dqt * e);
+      stx(dk + o, dkt * e + dkh * ei);
     }
-    // reverse prefix sum; the chunk-end decay belongs to the last row
+  }
+  __syncthreads();
+  // dg_r = sum_{s >= r} dGamma_s plus the chunk-end decay (it depends on
+  // every row), masked by the floor.  Per channel, each group of RG rows sums
+  // its rows, then walks them backward from the sums of the later groups.
+  {
+    typedef RowSplit<D> RS;
+    __shared__ float gsum[RS::NG][D];
+    const int c = tid % D, grp = tid / D, r0 = grp * RS::RG;
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < RS::RG; ++i) part += dG[r0 + i][c];
+    gsum[grp][c] = part;
+    __syncthreads();
     float acc = Wp[W::DGL + c];
-    for (int r = C - 1; r >= 0; --r) {
-      acc += dG[r * D + c];
+    for (int j = grp + 1; j < RS::NG; ++j) acc += gsum[j][c];
+#pragma unroll
+    for (int i = RS::RG - 1; i >= 0; --i) {
+      const int r = r0 + i;
+      acc += dG[r][c];
       float out = 0.f;
       if (r < len) {
         const float graw = gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c);
         out = graw >= g_floor ? acc : 0.f;
       }
-      dG[r * D + c] = out;
+      dG[r][c] = out;  // this thread's own element
       if (gate == kGateChannel && r < len) stx(dg + ((pos.tok0 + r) * H + h) * D + c, out);
     }
   }
   if (gate == kGateHead) {
     __syncthreads();
-    if (tid < len) {
-      const int r = tid;
-      const float graw = gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, 0);
-      float acc = 0.f;
-      // per-channel sums before the mask: the mask is the head's own
-      for (int c = 0; c < D; ++c) acc += dG[r * D + c];
-      stx(dg + (pos.tok0 + r) * H + h, graw >= g_floor ? acc : 0.f);
-    }
+    // per (token, head): the channel sum of the masked per-channel values (the
+    // mask is the head's own, the same on every channel); 8 lanes per row
+    const int r = tid / 8, part = tid % 8;
+    float acc = 0.f;
+    for (int c = part; c < D; c += 8) acc += dG[r][c];
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
+    if (part == 0 && r < len) stx(dg + (pos.tok0 + r) * H + h, acc);
   }
 }
 
@@ -532,17 +689,19 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   if ((e = mark(1)) != hipSuccess) return (int)e;
   const dim3 gc((unsigned)bp.n_slots, H);
   if (bp.n_slots > 0) {
-    hipLaunchKernelGGL((kda_bwd_chunk<T, D>), gc, dim3(512), 0, stream, (const T*)in.q, (const T*)in.k,
+    hipLaunchKernelGGL((kda_bwd_chunk<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k,
                        (const T*)in.v, in.g, in.beta, (const T*)dout, cu, n_rows, T_per, H, g_floor, gate, rec, zero);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((e = mark(2)) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)(n_rows * H * (D / 16))), dim3(256), 0, stream,
+  // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
+  const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
+  hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(256), 0, stream,
                      (const float*)rec, dht, cu, n_rows, T_per, H, dHs, dh0);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if ((e = mark(3)) != hipSuccess) return (int)e;
   if (bp.n_slots > 0) {
-    hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(512), 0, stream, (const T*)in.q, (const T*)in.k, in.g, cu,
+    hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k, in.g, cu,
                        n_rows, T_per, H, g_floor, gate, (const float*)rec, h0, (const float*)ht,
                        (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv,
                        (T*)dg, dbeta);
