@@ -38,9 +38,9 @@
 //                   dS walked backward over the chunks (column j of dS only
 //                   needs column j of dH and dO), writing every chunk's dH.
 //   kda_bwd_local : one workgroup per (chunk, head): everything else.
-// Every product runs on fp32 MFMA (v_mfma_f32_16x16x4f32); a wave owns one
-// 16x16 output tile at a time and reads its operands straight from memory
-// (records and scratch are L2-resident while a workgroup works on them).
+// Every product runs on fp32 MFMA (v_mfma_f32_16x16x4f32).  In the per-chunk
+// kernels the operands pass through LDS in k-slices (each element read once
+// per product); the state-gradient pass keeps its operands in registers.
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -55,66 +55,6 @@ __device__ __forceinline__ float ldx(const float* p) { return *p; }
 __device__ __forceinline__ float ldx(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ void stx(float* p, float x) { *p = x; }
 __device__ __forceinline__ void stx(bf16_t* p, float x) { *p = f32_to_bf16(x); }
-
-// One 16x16 tile: acc += sum_k A(i, k) B(k, j) over k < K (K % 16 == 0),
-// A(i, k) = A[i * ai + k * ak], B(k, j) = B[k * bk + j * bj]; A and B point
-// at the tile's first row / column.  bs: per-k scale of B, or null.  The
-// lane layout is the one of kda_device.h: lane 16 g + i supplies row i of A
-// and column i of B at k = 16 kk + 4 g + e in issue e of k-block kk, and
-// holds D[4 g + r][i].  Every operand load of the tile is issued before the
-// first product (one memory latency per tile, not one per k-block); a unit
-// k-stride reads 16 bytes per lane.
-template <int K>
-__device__ __forceinline__ f32x4 tile_mma_k(f32x4 acc, const float* A, int ai, int ak, const float* B, int bk,
-                                            int bj, const float* bs, int lane) {
-  constexpr int NK = K / 16;
-  const int i = lane & 15, g = lane >> 4;
-  const float* pa = A + i * ai + 4 * g * ak;
-  const float* pb = B + i * bj + 4 * g * bk;
-  f32x4 a[NK], b[NK];
-  if (ak == 1) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) a[kk] = *(const f32x4*)(pa + 16 * kk);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const float* p = pa + 16 * kk * ak;
-      a[kk] = (f32x4){p[0], p[ak], p[2 * ak], p[3 * ak]};
-    }
-  }
-  if (bk == 1) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) b[kk] = *(const f32x4*)(pb + 16 * kk);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const float* p = pb + 16 * kk * bk;
-      b[kk] = (f32x4){p[0], p[bk], p[2 * bk], p[3 * bk]};
-    }
-  }
-  if (bs) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const f32x4 sc = *(const f32x4*)(bs + 16 * kk + 4 * g);
-      b[kk] = (f32x4){b[kk][0] * sc[0], b[kk][1] * sc[1], b[kk][2] * sc[2], b[kk][3] * sc[3]};
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][0], b[kk][0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][1], b[kk][1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][2], b[kk][2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][3], b[kk][3], acc, 0, 0, 0);
-  }
-  return acc;
-}
-// The same for the two depths the chunk algebra has: K = 64 (the chunk) or
-// K = 128 (the key/value width); K = 64 is also the width 64.
-__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float* A, int ai, int ak, const float* B, int bk,
-                                          int bj, const float* bs, int K, int lane) {
-  if (K == 128) return tile_mma_k<128>(acc, A, ai, ak, B, bk, bj, bs, lane);
-  return tile_mma_k<64>(acc, A, ai, ak, B, bk, bj, bs, lane);
-}
 
 // Operand views for one product: A is M x K, B is K x N.
 struct MatA {
@@ -138,26 +78,101 @@ __device__ __forceinline__ MatB kcols(const float* p, int ld) { return MatB{p, 1
 // Mask of a stored tile element (row r, column c).
 enum Mask { kFull = 0, kLowerIncl = 1, kStrictLower = 2 };
 
+// Threads of the per-chunk kernels (eight waves).
+constexpr int kThreads = 512;
+
 // out[r][c] = alpha * (A1 B1 + A2 B2)[r][c] (+ out[r][c] when acc_in), then
-// column scale cs[c] if given, masked; M x N, tiles split over the waves.
-// A2 may be null (one product).  out rows have stride ldo.
-__device__ void gemm(float* out, int ldo, int M, int N, float alpha, bool acc_in, Mask mask, const float* cs,
-                     const MatA& A1, const MatB& B1, int K1, const MatA* A2, const MatB* B2, int K2, int wave,
-                     int nwaves, int lane) {
-  const int tn = N / 16, tiles = (M / 16) * tn;
+// column scale cs[c] if given, masked; 64 rows, N = 64 or 128 columns, K1,
+// K2 multiples of 32 (A2 null: one product).  Called by every thread of a
+// kThreads workgroup.
+//
+// The k range is walked in slices of KS = 32: the workgroup copies the
+// slice's A (64 x KS) and B (KS x N) into LDS, each element read once from
+// memory (B's per-k scale applied on the way), both stored k-contiguous so
+// that every MFMA operand fragment is one 16-byte LDS read.  The next
+// slice's loads are issued before the current slice's products.  Wave w
+// owns row tile w / 2 and N / 32 consecutive column tiles of half w % 2, so
+// one A fragment serves all of its tiles.  The lane layout is the one of
+// kda_device.h: lane 16 g + i supplies row i of A and column i of B at
+// k = 16 kk + 4 g + e in issue e, and holds D[4 g + r][i].
+constexpr int KS = 32, KSP = KS + 4, GM_ROWS = 64;
+constexpr int kGemmLds = (GM_ROWS + 128) * KSP;  // floats of LDS the products use (the caller's buffer)
+template <int N>
+__device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, Mask mask, const float* cs,
+                     const MatA& A1, const MatB& B1, int K1, const MatA* A2, const MatB* B2, int K2) {
+  constexpr int M = GM_ROWS, NA = M * KS / kThreads, NB = N * KS / kThreads, NT = N / 32;
+  static_assert(NA * kThreads == M * KS && NB * kThreads == N * KS, "slices tile the workgroup");
+  float(*sA)[KSP] = (float(*)[KSP])lds;
+  float(*sB)[KSP] = (float(*)[KSP])(lds + M * KSP);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  for (int t = wave; t < tiles; t += nwaves) {
-    const int r0 = (t / tn) * 16, c0 = (t % tn) * 16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile_mma(acc, A1.at(r0), A1.ai, A1.ak, B1.at(c0), B1.bk, B1.bj, B1.bs, K1, lane);
-    if (A2) acc = tile_mma(acc, A2->at(r0), A2->ai, A2->ak, B2->at(c0), B2->bk, B2->bj, B2->bs, K2, lane);
-    const int c = c0 + i;
+  const int r0 = 16 * (wave >> 1), c0 = (wave & 1) * (N / 2);
+  float ra[NA], rb[NB];
+  auto fetch = [&](const MatA& A, const MatB& B, int k0) {
+#pragma unroll
+    for (int e = 0; e < NA; ++e) {
+      const int x = tid + kThreads * e;
+      const int r = A.ak == 1 ? x / KS : x % M, k = A.ak == 1 ? x % KS : x / M;
+      ra[e] = A.p[r * A.ai + (k0 + k) * A.ak];
+    }
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      const int x = tid + kThreads * e;
+      const int c = B.bk == 1 ? x / KS : x % N, k = B.bk == 1 ? x % KS : x / N;
+      float val = B.p[(k0 + k) * B.bk + c * B.bj];
+      if (B.bs) val *= B.bs[k0 + k];
+      rb[e] = val;
+    }
+  };
+  auto stash = [&](const MatA& A, const MatB& B) {
+#pragma unroll
+    for (int e = 0; e < NA; ++e) {
+      const int x = tid + kThreads * e;
+      const int r = A.ak == 1 ? x / KS : x % M, k = A.ak == 1 ? x % KS : x / M;
+      sA[r][k] = ra[e];
+    }
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      const int x = tid + kThreads * e;
+      const int c = B.bk == 1 ? x / KS : x % N, k = B.bk == 1 ? x % KS : x / N;
+      sB[c][k] = rb[e];
+    }
+  };
+  f32x4 acc[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  auto run = [&](const MatA& A, const MatB& B, int K) {
+    fetch(A, B, 0);
+    for (int k0 = 0; k0 < K; k0 += KS) {
+      __syncthreads();  // every wave is done with the previous slice
+      stash(A, B);
+      __syncthreads();
+      if (k0 + KS < K) fetch(A, B, k0 + KS);
+#pragma unroll
+      for (int kk = 0; kk < KS / 16; ++kk) {
+        const f32x4 a = *(const f32x4*)&sA[r0 + i][16 * kk + 4 * g];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          const f32x4 b = *(const f32x4*)&sB[c0 + 16 * u + i][16 * kk + 4 * g];
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc[u], 0, 0, 0);
+        }
+      }
+    }
+  };
+  run(A1, B1, K1);
+  if (A2) run(*A2, *B2, K2);
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int c = c0 + 16 * u + i;
     const float sc = cs ? cs[c] : 1.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + 4 * g + e;
       float* dst = out + r * ldo + c;
-      float x = alpha * acc[e];
+      float x = alpha * acc[u][e];
       if (acc_in) x += *dst;
       x *= sc;
       const bool keep = mask == kFull || (mask == kLowerIncl ? r >= c : r > c);
@@ -175,10 +190,8 @@ template <int D> struct Rec {
                        WV = 6 * C * D, GM = 7 * C * D, PM = 8 * C * D, TM = PM + C * C, AB = TM + C * C,
                        GAM = AB + C * C, BET = GAM + D, FLOATS = BET + C;
 };
-// Threads of the per-chunk kernels, and how they split the rows of a chunk
-// for the prefix sums over rows: NG groups of RG rows, one thread per
-// (group, channel).
-constexpr int kThreads = 512;
+// How the per-chunk kernels split the rows of a chunk for the prefix sums
+// over rows: NG groups of RG rows, one thread per (group, channel).
 template <int D> struct RowSplit {
   static constexpr int NG = kThreads / D, RG = C / NG;
   static_assert(NG * D == kThreads && NG * RG == C, "row groups tile the chunk");
@@ -256,8 +269,12 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
                                                      float* __restrict__ zero_state) {
   typedef Rec<D> R;
   __shared__ ChunkPos pos;
-  __shared__ float As[C][C + 1];  // diag(beta) Abar
-  __shared__ float Ts[C][C + 1];  // T
+  // the products' slices, and later (once the Gram products are done) the
+  // inverse's operands diag(beta) Abar and T
+  constexpr int kLds = kGemmLds > 2 * C * (C + 1) ? kGemmLds : 2 * C * (C + 1);
+  __shared__ __align__(16) float lds[kLds];
+  float(*As)[C + 1] = (float(*)[C + 1])lds;
+  float(*Ts)[C + 1] = (float(*)[C + 1])(lds + C * (C + 1));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
@@ -315,10 +332,10 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   __syncthreads();
 
   // Abar = strict_lower(Kt Kh^T), P = lower_incl(Qt Kh^T)
-  gemm(Rp + R::AB, C, C, C, 1.f, false, kStrictLower, nullptr, rows(Rp + R::KT, D), kcols(Rp + R::KH, D), D,
-       nullptr, nullptr, 0, wave, nw, lane);
-  gemm(Rp + R::PM, C, C, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::QT, D), kcols(Rp + R::KH, D), D,
-       nullptr, nullptr, 0, wave, nw, lane);
+  gemm<C>(lds, Rp + R::AB, C, 1.f, false, kStrictLower, nullptr, rows(Rp + R::KT, D), kcols(Rp + R::KH, D), D,
+       nullptr, nullptr, 0);
+  gemm<C>(lds, Rp + R::PM, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::QT, D), kcols(Rp + R::KH, D), D,
+       nullptr, nullptr, 0);
   __syncthreads();
   for (int x = tid; x < C * C; x += blockDim.x) {
     const int r = x / C, c = x % C;
@@ -364,10 +381,10 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   for (int x = tid; x < C * C; x += blockDim.x) Rp[R::TM + x] = Ts[x / C][x % C];
   __syncthreads();
   // Wk = T diag(beta) Kt, Wv = T diag(beta) V
-  gemm(Rp + R::WK, D, C, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::KT, D, Rp + R::BET), C,
-       nullptr, nullptr, 0, wave, nw, lane);
-  gemm(Rp + R::WV, D, C, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::VV, D, Rp + R::BET), C,
-       nullptr, nullptr, 0, wave, nw, lane);
+  gemm<D>(lds, Rp + R::WK, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::KT, D, Rp + R::BET), C,
+       nullptr, nullptr, 0);
+  gemm<D>(lds, Rp + R::WV, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::VV, D, Rp + R::BET), C,
+       nullptr, nullptr, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -516,6 +533,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   typedef Rec<D> R;
   typedef Scr<D> W;
   __shared__ ChunkPos pos;
+  // the products' slices, and later the per-element dGamma of the chunk
+  constexpr int kLds = kGemmLds > C * D ? kGemmLds : C * D;
+  __shared__ __align__(16) float lds[kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
@@ -532,12 +552,11 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   const float* bet = Rp + R::BET;
 
   // 1: U = Wv - Wk S;  dU = P^T dO + Kh diag(gamma) dH
-  gemm(Wp + W::U, D, C, D, -1.f, false, kFull, nullptr, rows(Rp + R::WK, D), krows(S, D), D, nullptr, nullptr, 0,
-       wave, nw, lane);
+  gemm<D>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Rp + R::WK, D), krows(S, D), D, nullptr, nullptr, 0);
   {
     const MatA a1 = trans(Rp + R::PM, C), a2 = rows(Rp + R::KH, D);
     const MatB b1 = krows(Rp + R::DO, D), b2 = krows(dH, D, gam);
-    gemm(Wp + W::DU, D, C, D, 1.f, false, kFull, nullptr, a1, b1, C, &a2, &b2, D, wave, nw, lane);
+    gemm<D>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, a1, b1, C, &a2, &b2, D);
   }
   // dgamma-last: sum_j dH_cj S_next_cj per channel; NP neighbouring lanes
   // share a channel and combine their partial sums by shuffles
@@ -555,37 +574,34 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   __syncthreads();
   // 2: dP = lower_incl(dO U^T); dWk = -dU S^T; Dv = T^T dU; dQt = dO S^T;
   //    dKh = U dH^T diag(gamma)
-  gemm(Wp + W::DP, C, C, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::DO, D), kcols(Wp + W::U, D), D, nullptr,
-       nullptr, 0, wave, nw, lane);
-  gemm(Wp + W::DWK, D, C, D, -1.f, false, kFull, nullptr, rows(Wp + W::DU, D), kcols(S, D), D, nullptr, nullptr, 0,
-       wave, nw, lane);
-  gemm(Wp + W::DV, D, C, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DU, D), C, nullptr,
-       nullptr, 0, wave, nw, lane);
-  gemm(Wp + W::DQT, D, C, D, 1.f, false, kFull, nullptr, rows(Rp + R::DO, D), kcols(S, D), D, nullptr, nullptr, 0,
-       wave, nw, lane);
-  gemm(Wp + W::DKH, D, C, D, 1.f, false, kFull, gam, rows(Wp + W::U, D), kcols(dH, D), D, nullptr, nullptr, 0,
-       wave, nw, lane);
+  gemm<C>(lds, Wp + W::DP, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::DO, D), kcols(Wp + W::U, D), D, nullptr,
+       nullptr, 0);
+  gemm<D>(lds, Wp + W::DWK, D, -1.f, false, kFull, nullptr, rows(Wp + W::DU, D), kcols(S, D), D, nullptr, nullptr, 0);
+  gemm<D>(lds, Wp + W::DV, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DU, D), C, nullptr,
+       nullptr, 0);
+  gemm<D>(lds, Wp + W::DQT, D, 1.f, false, kFull, nullptr, rows(Rp + R::DO, D), kcols(S, D), D, nullptr, nullptr, 0);
+  gemm<D>(lds, Wp + W::DKH, D, 1.f, false, kFull, gam, rows(Wp + W::U, D), kcols(dH, D), D, nullptr, nullptr, 0);
   __syncthreads();
   // 3: Dk = T^T dWk (into U); dQt += dP Kh; dKh += dP^T Qt
-  gemm(Wp + W::U, D, C, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DWK, D), C, nullptr,
-       nullptr, 0, wave, nw, lane);
-  gemm(Wp + W::DQT, D, C, D, 1.f, true, kFull, nullptr, rows(Wp + W::DP, C), krows(Rp + R::KH, D), C, nullptr,
-       nullptr, 0, wave, nw, lane);
-  gemm(Wp + W::DKH, D, C, D, 1.f, true, kFull, nullptr, trans(Wp + W::DP, C), krows(Rp + R::QT, D), C, nullptr,
-       nullptr, 0, wave, nw, lane);
+  gemm<D>(lds, Wp + W::U, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DWK, D), C, nullptr,
+       nullptr, 0);
+  gemm<D>(lds, Wp + W::DQT, D, 1.f, true, kFull, nullptr, rows(Wp + W::DP, C), krows(Rp + R::KH, D), C, nullptr,
+       nullptr, 0);
+  gemm<D>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DP, C), krows(Rp + R::QT, D), C, nullptr,
+       nullptr, 0);
   __syncthreads();
   // 4: dA = strict_lower(-Dk Wk^T - Dv Wv^T)
   {
     const MatA a1 = rows(Wp + W::U, D), a2 = rows(Wp + W::DV, D);
     const MatB b1 = kcols(Rp + R::WK, D), b2 = kcols(Rp + R::WV, D);
-    gemm(Wp + W::DA, C, C, C, -1.f, false, kStrictLower, nullptr, a1, b1, D, &a2, &b2, D, wave, nw, lane);
+    gemm<C>(lds, Wp + W::DA, C, -1.f, false, kStrictLower, nullptr, a1, b1, D, &a2, &b2, D);
   }
   __syncthreads();
   // 5: E = Dk + dA Kh (into dU); dKh += dA^T diag(beta) Kt
-  gemm(Wp + W::DU, D, C, D, 1.f, false, kFull, nullptr, rows(Wp + W::DA, C), krows(Rp + R::KH, D), C, nullptr,
-       nullptr, 0, wave, nw, lane);
-  gemm(Wp + W::DKH, D, C, D, 1.f, true, kFull, nullptr, trans(Wp + W::DA, C), krows(Rp + R::KT, D, bet), C,
-       nullptr, nullptr, 0, wave, nw, lane);
+  gemm<D>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, rows(Wp + W::DA, C), krows(Rp + R::KH, D), C, nullptr,
+       nullptr, 0);
+  gemm<D>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DA, C), krows(Rp + R::KT, D, bet), C,
+       nullptr, nullptr, 0);
   __syncthreads();
   for (int x = tid; x < C * D; x += blockDim.x) Wp[W::DU + x] += Wp[W::U + x];
   __syncthreads();
@@ -609,7 +625,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     stx(dv + ((pos.tok0 + r) * H + h) * D + c, bet[r] * Wp[W::DV + x]);
   }
   // dq, dk and dGamma per element (Gamma from the record)
-  __shared__ float dG[C][D];
+  float(*dG)[D] = (float(*)[D])lds;  // the products are done with it
   for (int x = tid; x < C * D; x += blockDim.x) {
     const int r = x / D, c = x % D;
     const float G = Rp[R::GM + x];
