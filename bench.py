@@ -94,6 +94,7 @@ DECODE = dict(N=256, H=32, d=128, wid=4)
 CPU_SAMPLE_SECONDS = 10.0
 
 PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
+BWD_SOURCES = ("kda_backward.hip", "kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
 
 
 def log(msg: str) -> None:
@@ -108,20 +109,20 @@ def source_digest(names) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(name: str, digest: str):
-    """HBM bytes per call from a committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+def read_traffic(name: str, digest: str, key: str = "hbm_bytes_per_call"):
+    """HBM bytes per call (or the value of `key`) from a committed counter
+    summary, if it was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
-            key, _, val = line.partition("=")
-            vals[key.strip()] = val.strip()
-    if vals.get("source_digest") != digest or "hbm_bytes_per_call" not in vals:
+            name_, _, val = line.partition("=")
+            vals[name_.strip()] = val.strip()
+    if vals.get("source_digest") != digest or key not in vals:
         return None
-    return float(vals["hbm_bytes_per_call"])
+    return float(vals[key])
 
 
 def parse():
@@ -463,7 +464,9 @@ def bench_backward(calls: int):
                               "algorithmic_flop": flop, "hbm_frac": byts / mean / 1e9 / PEAK_HBM_GBS},
             "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tf, "peak": PEAK_F32_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": dom_tf / PEAK_F32_MFMA_TFLOPS,
-                         "algorithmic_flop": stage_flop[dom] * token_heads, "mean_launch_us": stage[dom] * 1e6}}
+                         "algorithmic_flop": stage_flop[dom] * token_heads, "mean_launch_us": stage[dom] * 1e6,
+                         "traffic": read_traffic("kda_chunk_backward_T4096_H16_traffic.txt",
+                                                 source_digest(BWD_SOURCES), f"{dom}_hbm_bytes")}}
 
 
 def bench_decode(steps: int, warmup: int):
