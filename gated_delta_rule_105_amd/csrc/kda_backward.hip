@@ -36,7 +36,8 @@
 //                   quantities above that do not involve the state), fp32.
 //   kda_bwd_state : one workgroup per (sequence, head, 16 state columns):
 //                   dS walked backward over the chunks (column j of dS only
-//                   needs column j of dH and dO), writing every chunk's dH.
+//                   needs column j of dH and dO), writing every chunk's dH;
+//                   the next chunk's operands load during the current step.
 //   kda_bwd_local : one workgroup per (chunk, head): everything else.
 // Every product runs on fp32 MFMA (v_mfma_f32_16x16x4f32).  In the per-chunk
 // kernels the operands pass through LDS in k-slices (each element read once
@@ -419,22 +420,50 @@ __device__ __forceinline__ f32x4 mma_panels(f32x4 acc, const f32x4 (&a)[NK], con
   return acc;
 }
 
-// One workgroup per (sequence, head, 16 state columns), four waves: wave w
-// owns row tile w of dU (C / 16 = 4 tiles) and row tiles w, w + 4, .. of dS.
-// Each chunk step loads every record operand it needs (P^T, Kh, dO, Qt^T,
-// Wk^T panels) before its first barrier, so one memory latency covers the
-// step.  Workgroups are ordered so that the column blocks of a (sequence,
-// head) pair have the same block index mod 8, i.e. share one XCD's L2 (the
-// record operands are common to them).
+// One workgroup per (sequence, head, 16 state columns), eight waves.  With
+// dH the gradient of a chunk's end state (these 16 columns) and
+// G = diag(gamma) dH, a step is
+//   dU = P^T dO + Kh G,   dH_in = G + Qt^T dO - Wk^T dU.
+// Row tile t (of 4) of dU is split over k: wave t takes P^T dO and the first
+// half of Kh G, wave t + 4 the second half; the two partial tiles sit in LDS
+// and are added where dU is read.  Wave w < D / 16 owns row tile w of dH.
+// Every record operand of the next chunk (the step's k-panels and the gamma
+// of the wave's own rows) is loaded while the current chunk is computed, so
+// the chain of chunks waits on memory once, not once per step.  Workgroups
+// are ordered so that the column blocks of one (sequence, head) pair have the
+// same block index mod 8, i.e. share one XCD's L2 (the record operands are
+// common to them).
+template <int D> struct StateOps {
+  static constexpr int NKC = C / 16, NKH = D / 32;
+  f32x4 aP[NKC], aKh[NKH], bO[NKC], aQ[NKC], aW[NKC];
+  float gr[4];  // gamma of rows 16 w + 4 g + e (this wave's dH tile)
+  // gamma first: a step needs the next chunk's gamma before its other operands
+  // (loads complete in issue order)
+  __device__ void load(const float* Rp, int j0, int wave, int lane) {
+    typedef Rec<D> R;
+    const int t = wave & 3, koff = wave < 4 ? 0 : D / 2;
+    if (wave < D / 16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gr[e] = Rp[R::GAM + 16 * wave + 4 * (lane >> 4) + e];
+    }
+    load_panel(bO, Rp + R::DO + j0, 1, D, lane);                           // B(k = r, j) = dO[r][j0 + j]
+    load_panel(aKh, Rp + R::KH + 16 * t * D + koff, D, 1, lane);            // Kh rows 16 t.., k from koff
+    if (wave < 4) load_panel(aP, Rp + R::PM + 16 * t, 1, C, lane);          // P^T rows 16 t..: P[r][16 t + i]
+    if (wave < D / 16) {
+      load_panel(aQ, Rp + R::QT + 16 * wave, 1, D, lane);                   // Qt^T rows 16 w..
+      load_panel(aW, Rp + R::WK + 16 * wave, 1, D, lane);
+    }
+  }
+};
+
 template <int D>
-__global__ void __launch_bounds__(256) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
+__global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
                                                      const int32_t* __restrict__ cu, int n_rows, int T_per, int H,
                                                      float* __restrict__ dHs, float* __restrict__ dh0) {
   typedef Rec<D> R;
-  constexpr int NCB = D / 16, NT = D / 64, NKC = C / 16, NKD = D / 16;
-  __shared__ __align__(16) float dH[D][16];
-  __shared__ __align__(16) float dU[C][16];
-  __shared__ __align__(16) float gam[D];
+  constexpr int NCB = D / 16, NKC = C / 16, NKH = D / 32;
+  __shared__ __align__(16) float G[D][16];
+  __shared__ __align__(16) float dU[2][C][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const int cb = (b / 8) % NCB, pair = 8 * (b / (8 * NCB)) + b % 8;
@@ -450,75 +479,80 @@ __global__ void __launch_bounds__(256) kda_bwd_state(const float* __restrict__ r
     base = (int64_t)n * nc;
   }
   const int64_t sd = ((int64_t)n * H + h) * D * D;
-  for (int x = tid; x < D * 16; x += blockDim.x) {
-    const int c = x / 16, j = x % 16;
-    dH[c][j] = dht ? dht[sd + c * D + j0 + j] : 0.f;
+  auto rec_of = [&](int64_t m) { return rec + ((base + m) * H + h) * (int64_t)R::FLOATS; };
+  auto dhs_of = [&](int64_t m) { return dHs + ((base + m) * H + h) * (int64_t)D * D; };
+  if (nc == 0) {  // no tokens: the gradient passes through unchanged
+    if (dh0)
+      for (int x = tid; x < D * 16; x += blockDim.x) {
+        const int c = x / 16, j = x % 16;
+        dh0[sd + c * D + j0 + j] = dht ? dht[sd + c * D + j0 + j] : 0.f;
+      }
+    return;
   }
-  for (int64_t m = nc - 1; m >= 0; --m) {
-    const int64_t slot = base + m;
-    const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
-    float* dHo = dHs + (slot * H + h) * (int64_t)D * D;
-    // every record operand of this step
-    f32x4 aP[NKC], aKh[NKD], bO[NKC], aQ[NT][NKC], aW[NT][NKC];
-    load_panel(aP, Rp + R::PM + 16 * wave, 1, C, lane);   // P^T rows 16 w..: P[r][16 w + i]
-    load_panel(aKh, Rp + R::KH + 16 * wave * D, D, 1, lane);
-    load_panel(bO, Rp + R::DO + j0, 1, D, lane);          // B(k = r, j) = dO[r][j0 + j]
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int r0 = 16 * (wave + 4 * t);
-      load_panel(aQ[t], Rp + R::QT + r0, 1, D, lane);     // Qt^T rows r0..: Qt[r][r0 + i]
-      load_panel(aW[t], Rp + R::WK + r0, 1, D, lane);
-    }
-    for (int x = tid; x < D; x += blockDim.x) gam[x] = Rp[R::GAM + x];
-    __syncthreads();  // dH and gamma ready
+  // the last chunk's end-state gradient is dht: store it and form G
+  {
+    const float* Rp = rec_of(nc - 1);
+    float* dHo = dhs_of(nc - 1);
     for (int x = tid; x < D * 16; x += blockDim.x) {
       const int c = x / 16, j = x % 16;
-      dHo[c * D + j0 + j] = dH[c][j];
+      const float v = dht ? dht[sd + c * D + j0 + j] : 0.f;
+      dHo[c * D + j0 + j] = v;
+      G[c][j] = Rp[R::GAM + c] * v;
     }
-    // dU = P^T dO + Kh diag(gamma) dH                          [C x 16]
+  }
+  // two operand sets used in turn: step m computes from one while the other
+  // receives chunk m - 1
+  StateOps<D> opsA, opsB;
+  const int t = wave & 3, koff = wave < 4 ? 0 : D / 2;
+  auto step = [&](StateOps<D>& cur, StateOps<D>& nxt, int64_t m) {
+    if (m > 0) nxt.load(rec_of(m - 1), j0, wave, lane);
+    __syncthreads();  // G ready
+    // dU: wave t < 4 adds P^T dO to its half of Kh G
     {
-      f32x4 bH[NKD];
+      f32x4 bG[NKH];
 #pragma unroll
-      for (int kk = 0; kk < NKD; ++kk)
+      for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k = 16 * kk + 4 * g + e;
-          bH[kk][e] = gam[k] * dH[k][ii];
-        }
+        for (int e = 0; e < 4; ++e) bG[kk][e] = G[koff + 16 * kk + 4 * g + e][ii];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma_panels(acc, aP, bO);
-      acc = mma_panels(acc, aKh, bH);
+      if (wave < 4) acc = mma_panels(acc, cur.aP, cur.bO);
+      acc = mma_panels(acc, cur.aKh, bG);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dU[16 * wave + 4 * g + e][ii] = acc[e];
+      for (int e = 0; e < 4; ++e) dU[wave >> 2][16 * t + 4 * g + e][ii] = acc[e];
     }
-    __syncthreads();  // dU ready; every wave is done reading dH
-    // dH <- diag(gamma) dH + Qt^T dO - Wk^T dU                  [D x 16]
-    {
+    __syncthreads();  // both halves of dU
+    if (wave < D / 16) {
       f32x4 bU[NKC];
 #pragma unroll
       for (int kk = 0; kk < NKC; ++kk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bU[kk][e] = dU[16 * kk + 4 * g + e][ii];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int r0 = 16 * (wave + 4 * t);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, neg = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_panels(acc, aQ[t], bO);
-        neg = mma_panels(neg, aW[t], bU);
-#pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = r0 + 4 * g + e;
-          dH[r][ii] = gam[r] * dH[r][ii] + acc[e] - neg[e];  // this lane's own element only
+          const int r = 16 * kk + 4 * g + e;
+          bU[kk][e] = dU[0][r][ii] + dU[1][r][ii];
+        }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, neg = {0.f, 0.f, 0.f, 0.f};
+      acc = mma_panels(acc, cur.aQ, cur.bO);
+      neg = mma_panels(neg, cur.aW, bU);
+      float* dHo = m > 0 ? dhs_of(m - 1) : nullptr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wave + 4 * g + e;
+        const float v = G[r][ii] + acc[e] - neg[e];  // this lane's own element of G
+        if (m > 0) {
+          dHo[r * D + j0 + ii] = v;
+          G[r][ii] = nxt.gr[e] * v;
+        } else if (dh0) {
+          dh0[sd + r * D + j0 + ii] = v;
         }
       }
     }
-    __syncthreads();
+  };
+  opsA.load(rec_of(nc - 1), j0, wave, lane);
+  for (int64_t m = nc - 1; m >= 0; m -= 2) {
+    step(opsA, opsB, m);
+    if (m == 0) break;
+    step(opsB, opsA, m - 1);
   }
-  if (dh0)
-    for (int x = tid; x < D * 16; x += blockDim.x) {
-      const int c = x / 16, j = x % 16;
-      dh0[sd + c * D + j0 + j] = dH[c][j];
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -712,7 +746,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   if ((e = mark(2)) != hipSuccess) return (int)e;
   // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
   const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
-  hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(512), 0, stream,
                      (const float*)rec, dht, cu, n_rows, T_per, H, dHs, dh0);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if ((e = mark(3)) != hipSuccess) return (int)e;
