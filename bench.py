@@ -399,7 +399,7 @@ def bench_mx(calls: int):
             "hbm_frac": (in_bytes + th * 2 * d + 2 * H * STATE_BYTES) / mean / 1e9 / PEAK_HBM_GBS}
 
 
-def bench_backward(calls: int):
+def bench_backward(calls: int, with_cpu: bool = True):
     """Backward pass (kda_chunk_backward) on the prefill workload with N(0, 1)
     upstream gradients for o and ht: mean call and per-stage durations (HIP
     events on the launch stream, kda_chunk_backward_timed)."""
@@ -454,9 +454,26 @@ def bench_backward(calls: int):
                   "kda_bwd_local": 2 * (BWD_MAC_PER_TOKEN_HEAD - mac_chunk - mac_state)}
     dom = max(stage, key=stage.get)
     dom_tf = stage_flop[dom] * token_heads / stage[dom] / 1e12
-    del inp, ws, out
+    del ws, out
     torch.cuda.empty_cache()
+    cpu = None
+    if with_cpu:
+        # the oracle's gradient on a bounded sample: heads 0 and 1 of the same
+        # inputs (token-heads per second, scaled to tokens/s of 16 heads)
+        import oracle
+        cpu_inp = {key: (val[:, :, :2].cpu() if key in ("q", "k", "v", "g", "beta", "do") else val)
+                   for key, val in inp.items()}
+        t0 = time.perf_counter()
+        oracle.backward(cpu_inp["q"], cpu_inp["k"], cpu_inp["v"], cpu_inp["g"], cpu_inp["beta"], cpu_inp["do"],
+                        h0=inp["h0"][:, :2].cpu(), dht=inp["dht"][:, :2].cpu())
+        el = time.perf_counter() - t0
+        cpu = {"value": T * 2 / el / H, "unit": "tokens/s", "cores": 2, "kind": "oracle",
+               "sample": f"fp64 token-by-token gradient of heads 0-1 of the T={T} workload, {el:.1f} s on 2 threads "
+                         "(one per head), scaled to 16 heads"}
+        log(f"cpu oracle backward: {el:.2f} s for 2 heads")
+    del inp
     return {"workload": "kda-backward-bf16-B1-H16-T4096-d128 (do, dht ~ N(0,1))", "mean_call_us": mean * 1e6,
+            "cpu_baseline": cpu,
             "value": B * T / mean, "unit": "tokens/s",
             "stage_us": {n: t * 1e6 for n, t in stage.items()},
             "call_roofline": {"bound": "mfma", "achieved": flop / mean / 1e12, "peak": PEAK_F32_MFMA_TFLOPS,
@@ -581,9 +598,9 @@ def main() -> int:
         out["states_workloads"] = bench_states(50)
         out["gate_workloads"] = bench_gates(50, 100)
         out["mx_workload"] = bench_mx(100)
-        out["backward_workload"] = bench_backward(20)
+        out["backward_workload"] = bench_backward(20, not args.no_cpu)
     if args.only == "backward":
-        out["backward_workload"] = bench_backward(args.steps)
+        out["backward_workload"] = bench_backward(args.steps, not args.no_cpu)
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

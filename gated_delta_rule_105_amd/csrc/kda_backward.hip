@@ -87,7 +87,7 @@ constexpr int kThreads = 512;
 // K2 multiples of 32 (A2 null: one product).  Called by every thread of a
 // kThreads workgroup.
 //
-// The k range is walked in slices of KS = 32: the workgroup copies the
+// The k range is walked in slices of KS = 64: the workgroup copies the
 // slice's A (64 x KS) and B (KS x N) into LDS, each element read once from
 // memory (B's per-k scale applied on the way), both stored k-contiguous so
 // that every MFMA operand fragment is one 16-byte LDS read.  The next
@@ -96,7 +96,7 @@ constexpr int kThreads = 512;
 // one A fragment serves all of its tiles.  The lane layout is the one of
 // kda_device.h: lane 16 g + i supplies row i of A and column i of B at
 // k = 16 kk + 4 g + e in issue e, and holds D[4 g + r][i].
-constexpr int KS = 32, KSP = KS + 4, GM_ROWS = 64;
+constexpr int KS = 64, KSP = KS + 4, GM_ROWS = 64;
 constexpr int kGemmLds = (GM_ROWS + 128) * KSP;  // floats of LDS the products use (the caller's buffer)
 template <int N>
 __device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, Mask mask, const float* cs,

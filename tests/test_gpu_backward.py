@@ -149,6 +149,34 @@ def test_backward_full_workload_sampled_heads():
     assert abs(np.sum(f64(out["dq"]) * q) - do_o) <= 1e-2 * scale
 
 
+def test_backward_packed_workload_sampled_heads():
+    """The packed batch (8 sequences, L ~ U[1024, 8192], H=32, d=128, bf16,
+    log-decay spread 2): every gradient element of heads 3 and 30 against the
+    oracle, and the homogeneity identities over all heads."""
+    w = synth.WORKLOADS[2]
+    inp = synth.workload_inputs(w)
+    inp.update(synth.grad_inputs(inp, w.wid))
+    note(f"chunk_backward workload 2 (packed, T={inp['q'].shape[1]} H=32 d=128 bf16)")
+    out = _gpu_backward(inp)
+    d = to_dev(inp)
+    o, ht = kda.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    sub = {key: (val[:, :, heads].contiguous() if key in ("q", "k", "v", "g", "beta", "do") else val)
+           for key, val in inp.items()}
+    sub["dht"] = inp["dht"][:, heads].contiguous()
+    ref = _oracle_backward(sub)
+    got = {key: (out[key][:, :, heads] if key != "dh0" else out[key][:, heads]) for key in GRADS}
+    _check("workload2 heads 3, 30", got, ref, "bf16")
+    v, q, do = f64(d["v"]), f64(d["q"]), f64(d["do"])
+    do_o = np.sum(do * f64(o))
+    scale = np.sum(np.abs(do * f64(o)))
+    lhs = np.sum(f64(out["dv"]) * v)  # h0 = 0 here
+    rhs = do_o + np.sum(f64(d["dht"]) * f64(ht))
+    assert abs(lhs - rhs) <= 1e-2 * scale
+    assert abs(np.sum(f64(out["dq"]) * q) - do_o) <= 1e-2 * scale
+
+
 def test_backward_split_resume():
     """The gradient of a sequence equals that of its two halves run with the
     state and the state gradient handed across (split at a chunk boundary
