@@ -52,6 +52,12 @@ namespace {
 
 constexpr int C = kChunk;
 
+// Barrier for LDS hand-offs only: the waves' LDS operations are complete,
+// global loads may still be in flight (__syncthreads() is a release fence and
+// would first wait for every outstanding load, prefetches included).  The
+// kernels keep __syncthreads() where a barrier orders global-memory data.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float ldx(const float* p) { return *p; }
 __device__ __forceinline__ float ldx(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ void stx(float* p, float x) { *p = x; }
@@ -145,9 +151,9 @@ __device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, 
   auto run = [&](const MatA& A, const MatB& B, int K) {
     fetch(A, B, 0);
     for (int k0 = 0; k0 < K; k0 += KS) {
-      __syncthreads();  // every wave is done with the previous slice
+      lds_barrier();  // every wave is done with the previous slice
       stash(A, B);
-      __syncthreads();
+      lds_barrier();
       if (k0 + KS < K) fetch(A, B, k0 + KS);
 #pragma unroll
       for (int kk = 0; kk < KS / 16; ++kk) {
@@ -506,7 +512,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   const int t = wave & 3, koff = wave < 4 ? 0 : D / 2;
   auto step = [&](StateOps<D>& cur, StateOps<D>& nxt, int64_t m) {
     if (m > 0) nxt.load(rec_of(m - 1), j0, wave, lane);
-    __syncthreads();  // G ready
+    lds_barrier();  // G ready
     // dU: wave t < 4 adds P^T dO to its half of Kh G
     {
       f32x4 bG[NKH];
@@ -520,7 +526,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 #pragma unroll
       for (int e = 0; e < 4; ++e) dU[wave >> 2][16 * t + 4 * g + e][ii] = acc[e];
     }
-    __syncthreads();  // both halves of dU
+    lds_barrier();  // both halves of dU
     if (wave < D / 16) {
       f32x4 bU[NKC];
 #pragma unroll
