@@ -201,6 +201,15 @@ def test_backward_split_resume():
         assert rel_err(f64(head["dh0"]), f64(full["dh0"])) <= 1e-4
 
 
+def test_backward_no_tokens():
+    """T = 0: nothing to differentiate through, dh0 = dht exactly."""
+    inp = _case(1, 0, 2, 64, "f32", lengths=[0, 0], wid=332)
+    note("chunk_backward T=0")
+    out = _gpu_backward(inp)
+    assert torch.equal(out["dh0"].cpu(), inp["dht"])
+    assert out["dq"].numel() == 0 and out["dbeta"].numel() == 0
+
+
 def test_backward_deterministic():
     inp = _case(1, 300, 2, 128, "bf16", wid=331)
     note("chunk_backward determinism")
