@@ -94,6 +94,7 @@ DECODE = dict(N=256, H=32, d=128, wid=4)
 CPU_SAMPLE_SECONDS = 10.0
 
 PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
+MFMA_PROFILE = "kda_mfma_util_prefill_T4096_H16_backward.txt"
 BWD_SOURCES = ("kda_backward.hip", "kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
 
 
@@ -109,9 +110,10 @@ def source_digest(names) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(name: str, digest: str, key: str = "hbm_bytes_per_call"):
+def read_traffic(name: str, digest: str, key: str = "hbm_bytes_per_call", digest_key: str = "source_digest"):
     """HBM bytes per call (or the value of `key`) from a committed counter
-    summary, if it was taken on the current kernel source (else None)."""
+    summary, if it was taken on the current kernel source, whose digest the
+    file records under `digest_key` (else None)."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -120,7 +122,7 @@ def read_traffic(name: str, digest: str, key: str = "hbm_bytes_per_call"):
         if "=" in line and not line.lstrip().startswith("#"):
             name_, _, val = line.partition("=")
             vals[name_.strip()] = val.strip()
-    if vals.get("source_digest") != digest or key not in vals:
+    if vals.get(digest_key) != digest or key not in vals:
         return None
     return float(vals[key])
 
@@ -483,7 +485,9 @@ def bench_backward(calls: int, with_cpu: bool = True):
                          "unit": "TFLOP/s", "frac": dom_tf / PEAK_F32_MFMA_TFLOPS,
                          "algorithmic_flop": stage_flop[dom] * token_heads, "mean_launch_us": stage[dom] * 1e6,
                          "traffic": read_traffic("kda_chunk_backward_T4096_H16_traffic.txt",
-                                                 source_digest(BWD_SOURCES), f"{dom}_hbm_bytes")}}
+                                                 source_digest(BWD_SOURCES), f"{dom}_hbm_bytes"),
+                         "mfma_util_counter_pct": read_traffic(MFMA_PROFILE, source_digest(BWD_SOURCES),
+                                                               f"{dom}_mfma_util_pct", "backward_source_digest")}}
 
 
 def bench_decode(steps: int, warmup: int):
@@ -581,6 +585,9 @@ def main() -> int:
                            "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": dom,
                            "algorithmic_bytes": dom_bytes, "algorithmic_flop": dom_flop,
                            "mfma_frac": dom_flop / t_dom / 1e12 / PEAK_BF16_TFLOPS,
+                           # MFMA busy cycles per SIMD from the counters (percent), when taken on this source
+                           "mfma_util_counter_pct": read_traffic(MFMA_PROFILE, source_digest(PREFILL_SOURCES),
+                                                                 f"{dom}_mfma_util_pct", "prefill_source_digest"),
                            "mean_launch_us": t_dom * 1e6,
                            "launch_us": {n: t * 1e6 for n, t in p["launch"].items()}}
         call_gbs = p["bytes_call"] / p["mean_call"] / 1e9
