@@ -73,6 +73,11 @@ CASES = {
     "bf16-d64-B2-T129": lambda: _case(2, 129, 2, 64, "bf16", wid=310),
     "bf16-d128-weak-decay": lambda: _case(1, 700, 2, 128, "bf16", g_mode="weak", wid=311),
     "bf16-d128-sigma2": lambda: _case(1, 333, 2, 128, "bf16", sigma_g=2.0, wid=312),
+    # long chains of chunks with weak or no decay: the state gradient is
+    # carried across every chunk of the sequence
+    "f32-d64-T4096-weak-decay": lambda: _case(1, 4096, 2, 64, "f32", g_mode="weak", wid=313),
+    "bf16-d128-T16384-weak-decay": lambda: _case(1, 16384, 2, 128, "bf16", g_mode="weak", wid=314),
+    "bf16-d128-T8192-no-decay": lambda: _case(1, 8192, 2, 128, "bf16", g_mode="zero", wid=315),
 }
 
 
