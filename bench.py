@@ -57,6 +57,10 @@ LLC_BYTES = 256 << 20          # MI355X last-level (infinity) cache
 #   4 d (C + 1) / 2           Wk, Wv, P, P U (lower triangles incl. diagonal)
 #   (C - 1)(C - 2) / 6        triangular inverse
 FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 128 * 63 // 2 + 4 * 128 * 65 // 2 + 63 * 62 // 6)
+# The same products as full 64 x 64 tiles (what dense MFMA tiles issue for
+# the key Gram, P, Wk, Wv and P U; the inverse not counted): per (token, head)
+#   3 d^2 + 5 d C, FLOP = 2 MAC
+ISSUED_FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 5 * 128 * 64)
 # bf16 q, k, v, g read + bf16 o written (2 B x 128 each) + fp32 beta
 BYTES_PER_TOKEN_HEAD = 5 * 2 * 128 + 4
 STATE_BYTES = 128 * 128 * 4    # one fp32 state matrix (h0 read, ht written)
@@ -595,8 +599,11 @@ def main() -> int:
                                 "frac": call_gbs / PEAK_HBM_GBS, "algorithmic_bytes": p["bytes_call"],
                                 "mean_call_us": p["mean_call"] * 1e6}
         tf = p["flop_call"] / p["mean_call"] / 1e12
+        issued = p["token_heads"] * ISSUED_FLOP_PER_TOKEN_HEAD
         out["mfma"] = {"achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                       "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop": p["flop_call"]}
+                       "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop": p["flop_call"],
+                       "issued_flop": issued,
+                       "issued_frac": issued / p["mean_call"] / 1e12 / PEAK_BF16_TFLOPS}
         out["config"]["buffer_sets"] = p["n_sets"]
     if args.only in ("prefill", "both") and not args.no_extra:
         # the packed 8-sequence batch and the million-token context, timed the

@@ -67,13 +67,11 @@ __device__ __forceinline__ void stx(bf16_t* p, float x) { *p = f32_to_bf16(x); }
 struct MatA {
   const float* p;
   int ai, ak;
-  __device__ const float* at(int i) const { return p + i * ai; }
 };
 struct MatB {
   const float* p;
   int bk, bj;
   const float* bs;
-  __device__ const float* at(int j) const { return p + j * bj; }
 };
 __device__ __forceinline__ MatA rows(const float* p, int ld) { return MatA{p, ld, 1}; }      // X, X[i][k]
 __device__ __forceinline__ MatA trans(const float* p, int ld) { return MatA{p, 1, ld}; }     // X^T, X[k][i]
