@@ -217,7 +217,13 @@ struct ChunkPos {
   int n, m, nc, len;
   int64_t tok0, st0;
 };
-__device__ bool chunk_pos(int64_t slot, const int32_t* cu, int n_rows, int T_per, ChunkPos* p) {
+// Per-sequence prefix sums of a packed batch (kda_bwd_seqs): seqs[n] = chunks
+// of sequences 0 .. n-1 (the first chunk slot of sequence n), and
+// seqs[n_rows + 1 + n] = full chunks of sequences 0 .. n-1 (the first
+// prefix-state slot of sequence n, the layout of kda_chunk_forward_states).
+// A chunk slot finds its sequence by binary search over the first array.
+__device__ bool chunk_pos(int64_t slot, const int32_t* cu, const int64_t* seqs, int n_rows, int T_per,
+                          ChunkPos* p) {
   if (!cu) {
     const int64_t per = (T_per + C - 1) / C;
     if (per == 0 || slot >= per * n_rows) return false;
@@ -229,29 +235,64 @@ __device__ bool chunk_pos(int64_t slot, const int32_t* cu, int n_rows, int T_per
     p->st0 = (int64_t)p->n * (T_per / C);
     return true;
   }
-  int64_t base = 0, st0 = 0;
-  for (int n = 0; n < n_rows; ++n) {
-    const int64_t L = (int64_t)cu[n + 1] - cu[n];
-    const int64_t nc = (L + C - 1) / C;
-    if (slot < base + nc) {
-      p->n = n;
-      p->m = (int)(slot - base);
-      p->nc = (int)nc;
-      p->tok0 = (int64_t)cu[n] + (int64_t)p->m * C;
-      p->len = (int)min((int64_t)C, L - (int64_t)p->m * C);
-      p->st0 = st0;
-      return true;
-    }
-    base += nc;
-    st0 += L / C;
+  if (n_rows == 0 || slot >= seqs[n_rows]) return false;
+  // the largest n with seqs[n] <= slot: that sequence is not empty
+  int lo = 0, hi = n_rows - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (seqs[mid] <= slot) lo = mid;
+    else hi = mid - 1;
   }
-  return false;
+  const int n = lo;
+  const int64_t L = (int64_t)cu[n + 1] - cu[n];
+  p->n = n;
+  p->m = (int)(slot - seqs[n]);
+  p->nc = (int)((L + C - 1) / C);
+  p->tok0 = (int64_t)cu[n] + (int64_t)p->m * C;
+  p->len = (int)min((int64_t)C, L - (int64_t)p->m * C);
+  p->st0 = seqs[n_rows + 1 + n];
+  return true;
+}
+
+// The prefix sums above, for n_rows sequences: one workgroup, each thread
+// summing a contiguous range of sequences, then the ranges' offsets.
+__global__ void __launch_bounds__(256) kda_bwd_seqs(const int32_t* __restrict__ cu, int n_rows,
+                                                    int64_t* __restrict__ seqs) {
+  __shared__ int64_t part[2][256];
+  const int tid = threadIdx.x, per = (n_rows + 255) / 256;
+  const int n0 = min(n_rows, tid * per), n1 = min(n_rows, n0 + per);
+  int64_t a = 0, f = 0;
+  for (int n = n0; n < n1; ++n) {
+    const int64_t L = (int64_t)cu[n + 1] - cu[n];
+    a += (L + C - 1) / C;
+    f += L / C;
+  }
+  part[0][tid] = a;
+  part[1][tid] = f;
+  __syncthreads();
+  int64_t oa = 0, of = 0;
+  for (int t = 0; t < tid; ++t) {
+    oa += part[0][t];
+    of += part[1][t];
+  }
+  for (int n = n0; n < n1; ++n) {
+    seqs[n] = oa;
+    seqs[n_rows + 1 + n] = of;
+    const int64_t L = (int64_t)cu[n + 1] - cu[n];
+    oa += (L + C - 1) / C;
+    of += L / C;
+  }
+  if (tid == 255) {
+    seqs[n_rows] = oa;  // every chunk (the last thread's range ends at n_rows)
+    seqs[2 * n_rows + 1] = of;
+  }
 }
 
 // Same position, found once per workgroup by thread 0 and shared via LDS.
-__device__ bool chunk_pos_shared(int64_t slot, const int32_t* cu, int n_rows, int T_per, ChunkPos* sh) {
+__device__ bool chunk_pos_shared(int64_t slot, const int32_t* cu, const int64_t* seqs, int n_rows, int T_per,
+                                 ChunkPos* sh) {
   __shared__ int ok;
-  if (threadIdx.x == 0) ok = chunk_pos(slot, cu, n_rows, T_per, sh) ? 1 : 0;
+  if (threadIdx.x == 0) ok = chunk_pos(slot, cu, seqs, n_rows, T_per, sh) ? 1 : 0;
   __syncthreads();
   return ok != 0;
 }
@@ -269,7 +310,8 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const void* __restrict__ g,
                                                      const float* __restrict__ beta, const T* __restrict__ dout,
-                                                     const int32_t* __restrict__ cu, int n_rows, int T_per, int H,
+                                                     const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs,
+                                                     int n_rows, int T_per, int H,
                                                      float g_floor, int gate, float* __restrict__ rec,
                                                      float* __restrict__ zero_state) {
   typedef Rec<D> R;
@@ -285,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   const int64_t slot = blockIdx.x;
   if (slot == 0 && h == 0)
     for (int x = tid; x < D * D; x += blockDim.x) zero_state[x] = 0.f;
-  if (!chunk_pos_shared(slot, cu, n_rows, T_per, &pos)) return;
+  if (!chunk_pos_shared(slot, cu, seqs, n_rows, T_per, &pos)) return;
   float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
   const bool bf = sizeof(T) == 2;
   const int len = pos.len;
@@ -462,7 +504,8 @@ template <int D> struct StateOps {
 
 template <int D>
 __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
-                                                     const int32_t* __restrict__ cu, int n_rows, int T_per, int H,
+                                                     const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs,
+                                                     int n_rows, int T_per, int H,
                                                      float* __restrict__ dHs, float* __restrict__ dh0) {
   typedef Rec<D> R;
   constexpr int NCB = D / 16, NKC = C / 16, NKH = D / 32;
@@ -476,7 +519,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   const int j0 = cb * 16, ii = lane & 15, g = lane >> 4;
   int64_t base = 0, nc;
   if (cu) {
-    for (int m = 0; m < n; ++m) base += ((int64_t)cu[m + 1] - cu[m] + C - 1) / C;
+    base = seqs[n];
     nc = ((int64_t)cu[n + 1] - cu[n] + C - 1) / C;
   } else {
     nc = (T_per + C - 1) / C;
@@ -564,7 +607,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
-    int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
+    const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta) {
@@ -577,7 +620,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
-  if (!chunk_pos_shared(slot, cu, n_rows, T_per, &pos)) return;
+  if (!chunk_pos_shared(slot, cu, seqs, n_rows, T_per, &pos)) return;
   const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
   float* Wp = scr + (slot * H + h) * (int64_t)W::FLOATS;
   const float* dH = dHs + (slot * H + h) * (int64_t)D * D;
@@ -729,6 +772,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   float* rec = (float*)(w + bp.rec_off);
   float* scr = (float*)(w + bp.scr_off);
   float* dHs = (float*)(w + bp.dh_off);
+  int64_t* seqs = (int64_t*)(w + bp.seq_off);
   if (bp.rec_floats != (size_t)Rec<D>::FLOATS || bp.scr_floats != (size_t)Scr<D>::FLOATS)
     return (int)hipErrorInvalidValue;
   hipError_t e;
@@ -736,6 +780,10 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     return (events && events[i]) ? hipEventRecord((hipEvent_t)events[i], stream) : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return (int)e;
+  if (cu && n_rows > 0) {
+    hipLaunchKernelGGL(kda_bwd_seqs, dim3(1), dim3(256), 0, stream, cu, n_rows, seqs);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
   // forward replay: ht and the state after every full chunk
   int rc = launch_chunk_forward(sizeof(T) == 2, D, n_rows, T_per, H, bp.fwd, g_floor, gate, in, h0, cu,
                                 (void*)(w + bp.o_off), ht, states, 1, ws, stream, nullptr);
@@ -744,19 +792,20 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   const dim3 gc((unsigned)bp.n_slots, H);
   if (bp.n_slots > 0) {
     hipLaunchKernelGGL((kda_bwd_chunk<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k,
-                       (const T*)in.v, in.g, in.beta, (const T*)dout, cu, n_rows, T_per, H, g_floor, gate, rec, zero);
+                       (const T*)in.v, in.g, in.beta, (const T*)dout, cu, (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, rec,
+                       zero);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((e = mark(2)) != hipSuccess) return (int)e;
   // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
   const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
   hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(512), 0, stream,
-                     (const float*)rec, dht, cu, n_rows, T_per, H, dHs, dh0);
+                     (const float*)rec, dht, cu, (const int64_t*)seqs, n_rows, T_per, H, dHs, dh0);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if ((e = mark(3)) != hipSuccess) return (int)e;
   if (bp.n_slots > 0) {
     hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k, in.g, cu,
-                       n_rows, T_per, H, g_floor, gate, (const float*)rec, h0, (const float*)ht,
+                       (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0, (const float*)ht,
                        (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv,
                        (T*)dg, dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;

@@ -164,11 +164,12 @@ constexpr size_t bwd_scr_floats(int d) { return (size_t)6 * kChunk * d + (size_t
 // Workspace of one backward call (byte offsets, each 256-byte aligned): the
 // forward replay's own workspace first, then its o (discarded), its final
 // states, the state after every full chunk, one zero state, the chunk
-// records, the scratch areas and the end-state gradient of every chunk.
+// records, the scratch areas, the end-state gradient of every chunk and the
+// per-sequence chunk and state-slot offsets of a packed batch.
 struct BwdPlan {
   SegPlan fwd;
   int64_t n_slots;  // upper bound of chunks over all sequences
-  size_t o_off, ht_off, states_off, zero_off, rec_off, scr_off, dh_off, ws_bytes;
+  size_t o_off, ht_off, states_off, zero_off, rec_off, scr_off, dh_off, seq_off, ws_bytes;
   size_t rec_floats, scr_floats;
 };
 
@@ -201,6 +202,8 @@ inline bool plan_backward(int d, int esz, int n_rows, int64_t T, int H, bool pac
   off = up(off + (size_t)p->n_slots * hh * p->scr_floats * 4);
   p->dh_off = off;
   off = up(off + (size_t)p->n_slots * hh * dd);
+  p->seq_off = off;  // per-sequence prefix sums of a packed batch: 2 (n_rows + 1) int64
+  off = up(off + (size_t)2 * ((size_t)n_rows + 1) * sizeof(int64_t));
   p->ws_bytes = off;
   return true;
 }

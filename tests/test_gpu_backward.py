@@ -64,6 +64,10 @@ CASES = {
     "f32-d64-B2-T130": lambda: _case(2, 130, 3, 64, "f32", wid=301),
     "f32-d64-T1": lambda: _case(1, 1, 2, 64, "f32", wid=302),
     "f32-d64-varlen": lambda: _case(1, 0, 2, 64, "f32", lengths=[5, 0, 128, 70], wid=303),
+    # many packed sequences (empty ones, exact multiples of the chunk and
+    # ragged ones): each chunk finds its sequence by binary search
+    "f32-d64-300-seqs": lambda: _case(1, 0, 2, 64, "f32", wid=316,
+                                      lengths=[(37 * i) % 193 if i % 7 else 64 * (i % 3) for i in range(300)]),
     "f32-d64-weak-decay": lambda: _case(1, 300, 2, 64, "f32", g_mode="weak", wid=304),
     "f32-d64-no-decay": lambda: _case(1, 256, 2, 64, "f32", g_mode="zero", wid=305),
     "f32-d64-below-floor": lambda: _case(1, 200, 2, 64, "f32", g_mode="raw", wid=306),
