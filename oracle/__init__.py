@@ -20,6 +20,9 @@ Contents
 :mod:`oracle.chunked`
     The chunk-parallel (UT/WY) rewriting of the same recurrence, in fp64
     numpy.  Used only as a cross-formulation pin of :func:`forward`.
+:mod:`oracle.chunked_bwd`
+    The gradient of that chunk-parallel form, in fp64 numpy: a
+    cross-formulation pin of :func:`backward`.
 :mod:`oracle.unrolled`
     Explicit products of the per-token transition matrices, for tiny T.
 :mod:`oracle.toy_delta`

@@ -10,7 +10,9 @@ copy of the reverse pass:
   * the floor's one-sided derivative from above where g equals the floor;
   * homogeneity: (v, h0) -> (o, ht) is linear and o is linear in q, so by
     Euler's identity <dv, v> + <dh0, h0> = <do, o> + <dht, ht> and
-    <dq, q> = <do, o>, at any size.
+    <dq, q> = <do, o>, at any size;
+  * the chunk-parallel gradient (``oracle.chunked_bwd``, the algebra of the
+    backward kernels), a second formulation that must agree to ~1e-12.
 They run against the real oracle in ``test_oracle_bwd_pins.py`` and against
 builds with planted mistakes, which must each fail at least one pin.
 """
@@ -125,3 +127,26 @@ def pin_bwd_homogeneity(orc):
 
 
 ALL_BWD_PINS = [pin_bwd_finite_differences, pin_bwd_floor_tie, pin_bwd_homogeneity]
+
+
+# the chunk-parallel gradient (the algebra of the backward kernels) against
+# the token-by-token one, for several chunk sizes, ragged and packed lengths,
+# decays above, on and below the floor
+def pin_bwd_chunked_form(orc):
+    from oracle.chunked_bwd import chunked_backward
+    from oracle_pins import rand_inputs
+    rng = np.random.default_rng(21)
+    for mode, chunk in (("floored", 64), ("raw", 16), ("weak", 4), ("zero", 1)):
+        q, k, v, g, beta, S0 = rand_inputs(rng, 1, 150, 2, 8, 6, g_mode=mode)
+        cu = np.array([0, 37, 37, 150])
+        h0 = 0.3 * rng.standard_normal((3, 2, 8, 6))
+        do = rng.standard_normal(v.shape)
+        dht = rng.standard_normal((3, 2, 8, 6))
+        ref = orc.backward(q, k, v, g, beta, do, h0=h0, dht=dht, cu_seqlens=cu, g_floor=FLOOR)
+        got = chunked_backward(q, k, v, g, beta, do, h0=h0, dht=dht, cu_seqlens=cu, g_floor=FLOOR, chunk=chunk)
+        for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+            err = np.max(np.abs(got[key] - ref[key])) / max(np.max(np.abs(ref[key])), 1e-300)
+            assert err < 1e-10, f"{mode} chunk={chunk} {key}: {err:.2e}"
+
+
+ALL_BWD_PINS.append(pin_bwd_chunked_form)
