@@ -19,7 +19,7 @@
 //   dS   = Qt^T dO + diag(gamma) dH - Wk^T dU            (to the previous chunk)
 //   dP   = lower_incl(dO U^T)
 //   dQt  = dO S^T + dP Kh
-//   Dk   = T^T (-dU S^T),   Dv = T^T dU
+//   Dk   = T^T (-dU S^T) = -Dv S^T,   Dv = T^T dU
 //   dA   = strict_lower(-Dk Wk^T - Dv Wv^T)
 //   dKt  = diag(beta)(Dk + dA Kh)
 //   dKh  = U dH^T diag(gamma) + dP^T Qt + dA^T diag(beta) Kt
@@ -86,8 +86,9 @@ enum Mask { kFull = 0, kLowerIncl = 1, kStrictLower = 2 };
 // Threads of the per-chunk kernels (eight waves).
 constexpr int kThreads = 512;
 
-// out[r][c] = alpha * (A1 B1 + A2 B2)[r][c] (+ out[r][c] when acc_in), then
-// column scale cs[c] if given, masked; 64 rows, N = 64 or 128 columns, K1,
+// out[r][c] = alpha * (A1 B1 + A2 B2)[r][c] (+ out[r][c] when acc_in, + add[r][c]
+// when add is given, add laid out like out), then column scale cs[c] if
+// given, masked; 64 rows, N = 64 or 128 columns, K1,
 // K2 multiples of 32 (A2 null: one product).  Called by every thread of a
 // kThreads workgroup.
 //
@@ -104,7 +105,8 @@ constexpr int KS = 64, KSP = KS + 4, GM_ROWS = 64;
 constexpr int kGemmLds = (GM_ROWS + 128) * KSP;  // floats of LDS the products use (the caller's buffer)
 template <int N>
 __device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, Mask mask, const float* cs,
-                     const MatA& A1, const MatB& B1, int K1, const MatA* A2, const MatB* B2, int K2) {
+                     const MatA& A1, const MatB& B1, int K1, const MatA* A2, const MatB* B2, int K2,
+                     const float* add = nullptr) {
   constexpr int M = GM_ROWS, NA = M * KS / kThreads, NB = N * KS / kThreads, NT = N / 32;
   static_assert(NA * kThreads == M * KS && NB * kThreads == N * KS, "slices tile the workgroup");
   float(*sA)[KSP] = (float(*)[KSP])lds;
@@ -179,6 +181,7 @@ __device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, 
       float* dst = out + r * ldo + c;
       float x = alpha * acc[u][e];
       if (acc_in) x += *dst;
+      if (add) x += add[r * ldo + c];
       x *= sc;
       const bool keep = mask == kFull || (mask == kLowerIncl ? r >= c : r > c);
       *dst = keep ? x : 0.f;
@@ -202,11 +205,11 @@ template <int D> struct RowSplit {
   static_assert(NG * D == kThreads && NG * RG == C, "row groups tile the chunk");
 };
 // Floats of one (chunk, head) scratch area of kda_bwd_local: U (then Dk),
-// dU (then E = Dk + dA Kh), dWk, Dv, dQt, dKh ([C][D] each),
-// dP, dA ([C][C]), dgamma-last [D].
+// dU (then E = Dk + dA Kh), Dv, dQt, dKh ([C][D] each), dP, dA ([C][C]),
+// dgamma-last [D].
 template <int D> struct Scr {
-  static constexpr int U = 0, DU = C * D, DWK = 2 * C * D, DV = 3 * C * D, DQT = 4 * C * D, DKH = 5 * C * D,
-                       DP = 6 * C * D, DA = DP + C * C, DGL = DA + C * C, FLOATS = DGL + D;
+  static constexpr int U = 0, DU = C * D, DV = 2 * C * D, DQT = 3 * C * D, DKH = 4 * C * D, DP = 5 * C * D,
+                       DA = DP + C * C, DGL = DA + C * C, FLOATS = DGL + D;
 };
 
 // Chunk `slot` of the call (slots count the chunks of all sequences in
@@ -633,7 +636,8 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   const float* bet = Rp + R::BET;
 
   // 1: U = Wv - Wk S;  dU = P^T dO + Kh diag(gamma) dH
-  gemm<D>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Rp + R::WK, D), krows(S, D), D, nullptr, nullptr, 0);
+  gemm<D>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Rp + R::WK, D), krows(S, D), D, nullptr, nullptr, 0,
+          Rp + R::WV);
   {
     const MatA a1 = trans(Rp + R::PM, C), a2 = rows(Rp + R::KH, D);
     const MatB b1 = krows(Rp + R::DO, D), b2 = krows(dH, D, gam);
@@ -651,23 +655,21 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     if (part == 0) Wp[W::DGL + c] = acc;
   }
   __syncthreads();
-  for (int x = tid; x < C * D; x += blockDim.x) Wp[W::U + x] += Rp[R::WV + x];
-  __syncthreads();
-  // 2: dP = lower_incl(dO U^T); dWk = -dU S^T; Dv = T^T dU; dQt = dO S^T;
-  //    dKh = U dH^T diag(gamma)
+  // 2: dP = lower_incl(dO U^T); Dv = T^T dU; dKh = U dH^T diag(gamma)
   gemm<C>(lds, Wp + W::DP, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::DO, D), kcols(Wp + W::U, D), D, nullptr,
        nullptr, 0);
-  gemm<D>(lds, Wp + W::DWK, D, -1.f, false, kFull, nullptr, rows(Wp + W::DU, D), kcols(S, D), D, nullptr, nullptr, 0);
   gemm<D>(lds, Wp + W::DV, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DU, D), C, nullptr,
        nullptr, 0);
-  gemm<D>(lds, Wp + W::DQT, D, 1.f, false, kFull, nullptr, rows(Rp + R::DO, D), kcols(S, D), D, nullptr, nullptr, 0);
   gemm<D>(lds, Wp + W::DKH, D, 1.f, false, kFull, gam, rows(Wp + W::U, D), kcols(dH, D), D, nullptr, nullptr, 0);
   __syncthreads();
-  // 3: Dk = T^T dWk (into U); dQt += dP Kh; dKh += dP^T Qt
-  gemm<D>(lds, Wp + W::U, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DWK, D), C, nullptr,
-       nullptr, 0);
-  gemm<D>(lds, Wp + W::DQT, D, 1.f, true, kFull, nullptr, rows(Wp + W::DP, C), krows(Rp + R::KH, D), C, nullptr,
-       nullptr, 0);
+  // 3: Dk = T^T (-dU S^T) = -Dv S^T (into U); dQt = dO S^T + dP Kh;
+  //    dKh += dP^T Qt
+  gemm<D>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Wp + W::DV, D), kcols(S, D), D, nullptr, nullptr, 0);
+  {
+    const MatA a1 = rows(Rp + R::DO, D), a2 = rows(Wp + W::DP, C);
+    const MatB b1 = kcols(S, D), b2 = krows(Rp + R::KH, D);
+    gemm<D>(lds, Wp + W::DQT, D, 1.f, false, kFull, nullptr, a1, b1, D, &a2, &b2, C);
+  }
   gemm<D>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DP, C), krows(Rp + R::QT, D), C, nullptr,
        nullptr, 0);
   __syncthreads();
@@ -680,11 +682,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   __syncthreads();
   // 5: E = Dk + dA Kh (into dU); dKh += dA^T diag(beta) Kt
   gemm<D>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, rows(Wp + W::DA, C), krows(Rp + R::KH, D), C, nullptr,
-       nullptr, 0);
+       nullptr, 0, Wp + W::U);
   gemm<D>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DA, C), krows(Rp + R::KT, D, bet), C,
        nullptr, nullptr, 0);
-  __syncthreads();
-  for (int x = tid; x < C * D; x += blockDim.x) Wp[W::DU + x] += Wp[W::U + x];
   __syncthreads();
 
   // 6: element-wise.

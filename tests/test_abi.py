@@ -291,10 +291,11 @@ def test_backward_workspace_size(lib):
     st, n = bws_status(lib, desc())
     assert st == KDA_OK and n % 256 == 0
     # at least the forward's workspace, the state after every chunk, and an
-    # fp32 record plus scratch plus end-state gradient per (chunk, head)
+    # fp32 record (eight [64][d] blocks, three [64][64], gamma, beta), scratch
+    # (five [64][d], two [64][64], one [d]) and end-state gradient per (chunk, head)
     fwd = ws_status(lib, desc())[1]
     chunks = 4096 // 64
-    per_chunk = (8 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 6 * 64 * 128 + 2 * 64 * 64 + 128 + 128 * 128) * 4
+    per_chunk = (8 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 5 * 64 * 128 + 2 * 64 * 64 + 128 + 128 * 128) * 4
     assert n >= fwd + 16 * chunks * 128 * 128 * 4 + 16 * chunks * per_chunk
     assert bws_status(lib, desc(d_k=96, d_v=96))[0] == KDA_ERR_UNSUPPORTED
     assert bws_status(lib, desc(dtype=KDA_DTYPE_F32))[0] == KDA_ERR_UNSUPPORTED
