@@ -406,9 +406,10 @@ def bench_mx(calls: int):
 
 
 def bench_backward(calls: int, with_cpu: bool = True):
-    """Backward pass (kda_chunk_backward) on the prefill workload with N(0, 1)
-    upstream gradients for o and ht: mean call and per-stage durations (HIP
-    events on the launch stream, kda_chunk_backward_timed)."""
+    """Backward pass on the prefill workload with N(0, 1) upstream gradients
+    for o and ht: mean call of kda_chunk_backward_overlapped (the value) and
+    of kda_chunk_backward, and per-stage durations (HIP events on the launch
+    stream, kda_chunk_backward_timed)."""
     import torch
     import gated_delta_rule_105_amd as kda
     import synth
@@ -421,19 +422,25 @@ def bench_backward(calls: int, with_cpu: bool = True):
     out = {}
     stream = torch.cuda.current_stream()
 
-    def call(events=None):
+    def call(events=None, overlap=False):
         return kda.chunk_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], h0=inp["h0"],
-                                  dht=inp["dht"], out=out, workspace=ws, events=events)
+                                  dht=inp["dht"], out=out, workspace=ws, events=events, overlap=overlap)
 
     out.update(call())
+    call(overlap=True)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-    for a, b in ev:
-        a.record(stream)
-        call()
-        b.record(stream)
-    torch.cuda.synchronize()
-    mean = sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+
+    def timed(overlap):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in ev:
+            a.record(stream)
+            call(overlap=overlap)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+
+    mean_seq = timed(False)
+    mean = timed(True)
     n_ev = len(kda.BWD_STAGES) + 1
     evl = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(calls)]
     for row in evl:
@@ -448,7 +455,7 @@ def bench_backward(calls: int, with_cpu: bool = True):
     token_heads = B * T * H
     flop = token_heads * BWD_FLOP_PER_TOKEN_HEAD
     byts = token_heads * BWD_BYTES_PER_TOKEN_HEAD + 3 * B * H * STATE_BYTES
-    log(f"backward {calls} calls: mean {mean * 1e6:.1f} us; per stage "
+    log(f"backward {calls} calls: mean {mean * 1e6:.1f} us overlapped, {mean_seq * 1e6:.1f} us sequential; per stage "
         + ", ".join(f"{n} {t * 1e6:.1f} us" for n, t in stage.items()))
     # the dominant stage against the fp32 matrix peak: its share of the
     # algorithmic products (the local-gradient kernel does all but the
@@ -479,6 +486,8 @@ def bench_backward(calls: int, with_cpu: bool = True):
         log(f"cpu oracle backward: {el:.2f} s for 2 heads")
     del inp
     return {"workload": "kda-backward-bf16-B1-H16-T4096-d128 (do, dht ~ N(0,1))", "mean_call_us": mean * 1e6,
+            "call": "kda_chunk_backward_overlapped (forward replay on a second stream)",
+            "sequential_call_us": mean_seq * 1e6,
             "cpu_baseline": cpu,
             "value": B * T / mean, "unit": "tokens/s",
             "stage_us": {n: t * 1e6 for n, t in stage.items()},

@@ -215,16 +215,41 @@ def backward_workspace_bytes(B: int, T: int, H: int, d: int, dtype, n_seqs: int 
     return _lib.backward_workspace_size(make_desc(B, T, H, d, dtype, n_seqs, chunk, g_floor, gate))
 
 
+_AUX = {}
+
+
+def _aux_stream(dev):
+    """Second stream and fork/join events of `dev` for overlapped backward
+    calls (created once per device; the events are recorded once so that
+    their handles exist)."""
+    torch = _torch()
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _AUX:
+        with torch.cuda.device(idx):
+            side = torch.cuda.Stream()
+            evs = [torch.cuda.Event(), torch.cuda.Event()]
+            for e in evs:
+                e.record()
+            torch.cuda.current_stream().synchronize()
+        _AUX[idx] = (side, evs)
+    side, evs = _AUX[idx]
+    return side.cuda_stream, evs[0].cuda_event, evs[1].cuda_event
+
+
 def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chunk: int = 64,
                    g_floor: float = -0.125, *, want_dh0: bool = True, out=None, workspace=None,
-                   validate_cu: bool = True, stream=None, events=None) -> dict:
+                   validate_cu: bool = True, stream=None, events=None, overlap: bool = False) -> dict:
     """Gradients of L = <do, o> + <dht, ht> for chunk_forward with the same
     inputs (kda_chunk_backward).  do: [B, T, H, d] in the input dtype; dht:
     fp32 [S, H, d, d] or None (zero).  Returns a dict with dq, dk, dv (input
     dtype), dg (the layout of g, input dtype; None without a gate), dbeta
     (fp32 [B, T, H]) and dh0 (fp32 [S, H, d, d], or None when want_dh0 is
     False).  `out` may supply those tensors.  events: optional
-    len(BWD_STAGES) + 1 raw hipEvent_t handles (kda_chunk_backward_timed)."""
+    len(BWD_STAGES) + 1 raw hipEvent_t handles (kda_chunk_backward_timed).
+    overlap: run the forward replay on a second stream of the device beside
+    the record and state-gradient stages (kda_chunk_backward_overlapped; the
+    same results).  Overlapped calls on one device share that stream and its
+    events, so they must be issued from one host thread."""
     torch = _torch()
     B, T, H, d = q.shape
     dt = q.dtype
@@ -271,12 +296,15 @@ def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chu
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    aux = _aux_stream(dev) if overlap else None
     st = _lib.chunk_backward_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                                  _ptr(cu_seqlens), _ptr(do), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]),
                                  _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(), stream, events)
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), stream, events,
+                                 aux)
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_backward_timed" if events is not None else "kda_chunk_backward")
+        raise KdaError(st, "kda_chunk_backward_timed" if events is not None else
+                       "kda_chunk_backward_overlapped" if overlap else "kda_chunk_backward")
     return out
 
 

@@ -27,7 +27,8 @@ KDA_GATE_NONE = 2      # no g: DeltaNet
 EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size",
            "kda_chunk_forward", "kda_chunk_forward_timed", "kda_chunk_forward_states_count",
            "kda_chunk_forward_states", "kda_chunk_forward_mx", "kda_chunk_backward_workspace_size",
-           "kda_chunk_backward", "kda_chunk_backward_timed", "kda_decode_step")
+           "kda_chunk_backward", "kda_chunk_backward_overlapped", "kda_chunk_backward_timed",
+           "kda_decode_step")
 
 # Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed).
 CHUNK_LAUNCHES = ("kda_chunk_prep", "kda_seg_scan", "kda_seg_forward")
@@ -87,6 +88,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_backward_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_backward.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp]
     lib.kda_chunk_backward.restype = ctypes.c_int
+    lib.kda_chunk_backward_overlapped.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp, vp, vp, vp]
+    lib.kda_chunk_backward_overlapped.restype = ctypes.c_int
     lib.kda_chunk_backward_timed.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp,
                                                                                       ctypes.POINTER(vp)]
     lib.kda_chunk_backward_timed.restype = ctypes.c_int
@@ -157,11 +160,17 @@ def backward_workspace_size(desc: ChunkDesc) -> int:
 
 
 def chunk_backward_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws,
-                       ws_bytes, stream, events=None) -> int:
-    """Call kda_chunk_backward (or its timed twin when `events`, len(BWD_STAGES)
-    + 1 raw hipEvent_t handles, is given); returns the status."""
+                       ws_bytes, stream, events=None, aux=None) -> int:
+    """Call kda_chunk_backward; its timed twin when `events` (len(BWD_STAGES)
+    + 1 raw hipEvent_t handles) is given; kda_chunk_backward_overlapped when
+    `aux` (raw second stream, fork event, join event) is given.  Returns the
+    status."""
     args = (ctypes.byref(desc), q, k, v, g, beta, h0, cu, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws,
             ctypes.c_size_t(ws_bytes), stream)
+    if aux is not None:
+        if events is not None:
+            raise ValueError("a call is either timed or overlapped")
+        return int(load().kda_chunk_backward_overlapped(*args, *aux))
     if events is None:
         return int(load().kda_chunk_backward(*args))
     arr = (ctypes.c_void_p * (len(BWD_STAGES) + 1))(*events)

@@ -259,7 +259,8 @@ bool plan_bwd(const kda_chunk_desc_t* d, const Sizes& s, kda::BwdPlan* bp) {
 int chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
                    const float* beta, const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dht,
                    void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0, void* workspace,
-                   size_t workspace_bytes, void* stream, void* const* events) {
+                   size_t workspace_bytes, void* stream, void* const* events,
+                   const kda::AuxStream* aux = nullptr) {
   Sizes s;
   const int st = check_desc(d, &s);
   if (st != KDA_OK) return st;
@@ -297,7 +298,7 @@ int chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, cons
   const kda::ChunkInputs in{q, k, v, g, beta, nullptr, nullptr, nullptr};
   const int e = kda::launch_chunk_backward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, bp, d->g_floor,
                                            (int)d->gate, in, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0,
-                                           workspace, stream, events);
+                                           workspace, stream, events, aux);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -320,6 +321,17 @@ int kda_chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, 
                        void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_backward(d, q, k, v, g, beta, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace,
                         workspace_bytes, stream, nullptr);
+}
+
+int kda_chunk_backward_overlapped(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                                  const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                  const void* dout, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                                  float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream,
+                                  void* aux_stream, void* fork_event, void* join_event) {
+  if (!fork_event || !join_event || fork_event == join_event) return KDA_ERR_INVALID_ARGUMENT;
+  const kda::AuxStream aux{aux_stream, fork_event, join_event};
+  return chunk_backward(d, q, k, v, g, beta, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace,
+                        workspace_bytes, stream, nullptr, &aux);
 }
 
 int kda_chunk_backward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,

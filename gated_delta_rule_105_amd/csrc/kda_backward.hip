@@ -764,7 +764,7 @@ template <typename T, int D>
 int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_floor, int gate,
                      const ChunkInputs& in, const float* h0, const int32_t* cu, const void* dout, const float* dht,
                      void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0, void* ws,
-                     hipStream_t stream, void* const* events) {
+                     hipStream_t stream, void* const* events, const AuxStream* aux) {
   unsigned char* w = (unsigned char*)ws;
   float* ht = (float*)(w + bp.ht_off);
   float* states = (float*)(w + bp.states_off);
@@ -784,10 +784,17 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     hipLaunchKernelGGL(kda_bwd_seqs, dim3(1), dim3(256), 0, stream, cu, n_rows, seqs);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  // forward replay: ht and the state after every full chunk
-  int rc = launch_chunk_forward(sizeof(T) == 2, D, n_rows, T_per, H, bp.fwd, g_floor, gate, in, h0, cu,
-                                (void*)(w + bp.o_off), ht, states, 1, ws, stream, nullptr);
-  if (rc != 0) return rc;
+  // forward replay: ht and the state after every full chunk.  Only the local
+  // kernel reads what it writes, and it writes nothing the record and
+  // state-gradient passes touch, so with a second stream it runs beside them.
+  auto replay = [&](hipStream_t st) {
+    return launch_chunk_forward(sizeof(T) == 2, D, n_rows, T_per, H, bp.fwd, g_floor, gate, in, h0, cu,
+                                (void*)(w + bp.o_off), ht, states, 1, ws, st, nullptr);
+  };
+  if (!aux) {
+    const int rc = replay(stream);
+    if (rc != 0) return rc;
+  }
   if ((e = mark(1)) != hipSuccess) return (int)e;
   const dim3 gc((unsigned)bp.n_slots, H);
   if (bp.n_slots > 0) {
@@ -796,6 +803,15 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
                        zero);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
+  if (aux) {
+    // forked after the record pass, so that the replay fills the CUs the
+    // state-gradient pass (one workgroup per pair and 16 columns) leaves idle
+    if ((e = hipEventRecord((hipEvent_t)aux->fork, stream)) != hipSuccess) return (int)e;
+    if ((e = hipStreamWaitEvent((hipStream_t)aux->stream, (hipEvent_t)aux->fork, 0)) != hipSuccess) return (int)e;
+    const int rc = replay((hipStream_t)aux->stream);
+    if (rc != 0) return rc;
+    if ((e = hipEventRecord((hipEvent_t)aux->join, (hipStream_t)aux->stream)) != hipSuccess) return (int)e;
+  }
   if ((e = mark(2)) != hipSuccess) return (int)e;
   // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
   const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
@@ -803,6 +819,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
                      (const float*)rec, dht, cu, (const int64_t*)seqs, n_rows, T_per, H, dHs, dh0);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if ((e = mark(3)) != hipSuccess) return (int)e;
+  if (aux && (e = hipStreamWaitEvent(stream, (hipEvent_t)aux->join, 0)) != hipSuccess) return (int)e;
   if (bp.n_slots > 0) {
     hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k, in.g, cu,
                        (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0, (const float*)ht,
@@ -827,17 +844,17 @@ static_assert(Rec<128>::FLOATS % 4 == 0 && Rec<64>::FLOATS % 4 == 0 && Scr<128>:
 int launch_chunk_backward(int is_bf16, int d, int n_rows, int T, int H, const BwdPlan& bp, float g_floor, int gate,
                           const ChunkInputs& in, const float* h0, const int32_t* cu, const void* dout,
                           const float* dht, void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
-                          void* ws, void* stream, void* const* events) {
+                          void* ws, void* stream, void* const* events, const AuxStream* aux) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
     return launch_bwd_typed<bf16_t, 64>(n_rows, T, H, bp, g_floor, gate, in, h0, cu, dout, dht, dq, dk, dv, dg,
-                                        dbeta, dh0, ws, s, events);
+                                        dbeta, dh0, ws, s, events, aux);
   if (is_bf16 && d == 128)
     return launch_bwd_typed<bf16_t, 128>(n_rows, T, H, bp, g_floor, gate, in, h0, cu, dout, dht, dq, dk, dv, dg,
-                                         dbeta, dh0, ws, s, events);
+                                         dbeta, dh0, ws, s, events, aux);
   if (!is_bf16 && d == 64)
     return launch_bwd_typed<float, 64>(n_rows, T, H, bp, g_floor, gate, in, h0, cu, dout, dht, dq, dk, dv, dg,
-                                       dbeta, dh0, ws, s, events);
+                                       dbeta, dh0, ws, s, events, aux);
   return (int)hipErrorInvalidValue;
 }
 

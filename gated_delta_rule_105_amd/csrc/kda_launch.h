@@ -211,15 +211,25 @@ inline bool plan_backward(int d, int esz, int n_rows, int64_t T, int H, bool pac
 // Launches of one backward call, in stream order.
 constexpr int kBwdLaunches = 4;  // forward replay (3 kernels), chunk records, state gradients, local gradients
 
+// A second stream for the forward replay of a backward call, with the two
+// caller-created events that fork it from the call's stream and join it back
+// (hipStream_t, hipEvent_t, hipEvent_t).
+struct AuxStream {
+  void* stream;
+  void* fork;
+  void* join;
+};
+
 // Enqueue the backward pass.  All arguments were validated by the caller;
 // dout is [.., H, d] in the operand type, dht may be null (zero), dg is null
 // without a gate, dh0 may be null (not written).  events: null, or
 // kBwdLaunches + 1 hipEvent_t handles recorded before each stage and after
-// the last.  Returns a hipError_t.
+// the last.  aux: null (every launch on `stream`), or a second stream for the
+// forward replay (then events must be null).  Returns a hipError_t.
 int launch_chunk_backward(int is_bf16, int d, int n_rows, int T, int H, const BwdPlan& bp, float g_floor, int gate,
                           const ChunkInputs& in, const float* h0, const int32_t* cu, const void* dout,
                           const float* dht, void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
-                          void* ws, void* stream, void* const* events);
+                          void* ws, void* stream, void* const* events, const AuxStream* aux = nullptr);
 
 // Enqueue one decode step (gate: a kda_gate_t).  Returns a hipError_t.
 int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor, int gate,

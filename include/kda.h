@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 10200 /* 1.2.0 */
+#define KDA_VERSION 10300 /* 1.3.0 */
 
 typedef enum {
   KDA_OK = 0,
@@ -244,6 +244,29 @@ int kda_chunk_backward(const kda_chunk_desc_t* d,
                        const void* dout, const float* dht,
                        void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_backward with its forward replay on a second stream.  Only the
+ * local-gradient stage reads what the replay writes, so the replay runs beside
+ * the chunk-record and state-gradient stages (the latter fills one CU per
+ * (sequence, head, 16 state columns) and leaves the rest idle at small batch).
+ *   aux_stream : hipStream_t (NULL = the default stream) the replay is
+ *                enqueued on; it waits for `stream` at the fork, and `stream`
+ *                waits for it before the local-gradient stage.
+ *   fork_event, join_event : two distinct caller-created hipEvent_t; both are
+ *                re-recorded by every call, so concurrent calls need their own.
+ * Results are bit-identical to kda_chunk_backward.  Every work item the call
+ * enqueues is ordered before later work on `stream`.  Arguments, workspace
+ * and errors as kda_chunk_backward; NULL or equal events are
+ * KDA_ERR_INVALID_ARGUMENT.
+ */
+int kda_chunk_backward_overlapped(const kda_chunk_desc_t* d,
+                                  const void* q, const void* k, const void* v, const void* g,
+                                  const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                  const void* dout, const float* dht,
+                                  void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* aux_stream, void* fork_event, void* join_event);
 
 /*
  * Measurement twin of kda_chunk_backward: events[i] (5 caller-created

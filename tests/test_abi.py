@@ -356,3 +356,27 @@ def test_chunk_backward_rejects_bad_desc(lib):
     an = bwd_args(lib, dn)
     an.update(g=None, dg=3, dq=an["q"] + 1024)
     assert bwd_call(dn, an) == KDA_ERR_INVALID_ARGUMENT                   # the overlap is still caught
+
+
+def test_chunk_backward_overlapped_rejects(lib):
+    """The overlapped entry point needs two distinct events, and otherwise
+    validates exactly as kda_chunk_backward (fake addresses: nothing here
+    reaches a launch)."""
+    d = desc()
+    a = bwd_args(lib, d)
+    ev1, ev2, side = 1 << 40, 2 << 40, 3 << 40   # never dereferenced
+    def ov(args, fork, join, dd=d):
+        return _lib.chunk_backward_raw(dd, *(args[n] for n in BWD_NAMES), args["ws_bytes"], None,
+                                       aux=(side, fork, join))
+    assert ov(a, None, ev2) == KDA_ERR_INVALID_ARGUMENT
+    assert ov(a, ev1, None) == KDA_ERR_INVALID_ARGUMENT
+    assert ov(a, ev1, ev1) == KDA_ERR_INVALID_ARGUMENT
+    for mutate, code in ((lambda x: x.update(ws_bytes=x["ws_bytes"] - 1), KDA_ERR_WORKSPACE_TOO_SMALL),
+                         (lambda x: x.update(dq=x["q"] + 1024), KDA_ERR_INVALID_ARGUMENT),
+                         (lambda x: x.update(do=None), KDA_ERR_INVALID_ARGUMENT)):
+        b = dict(a)
+        mutate(b)
+        assert ov(b, ev1, ev2) == code
+    assert ov(a, ev1, ev2, dd=desc(d_k=96, d_v=96)) == KDA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        _lib.chunk_backward_raw(d, *(a[n] for n in BWD_NAMES), a["ws_bytes"], None, [0] * 5, (side, ev1, ev2))

@@ -226,3 +226,50 @@ def test_backward_deterministic():
     b = _gpu_backward(inp)
     for key in GRADS:
         assert torch.equal(a[key], b[key]), key
+
+
+def _both(d, **kw):
+    """The sequential call, then two overlapped calls in a row (the second
+    one's outputs copied on the calling stream straight after it, before any
+    synchronisation: the copy must see the finished gradients)."""
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"])
+    kw = dict(h0=d.get("h0"), dht=d.get("dht"), cu_seqlens=d.get("cu_seqlens"), **kw)
+    seq = kda.chunk_backward(*args, **kw)
+    kda.chunk_backward(*args, overlap=True, **kw)
+    ov = kda.chunk_backward(*args, overlap=True, **kw)
+    copy = {key: None if ov[key] is None else ov[key].clone() for key in GRADS}
+    torch.cuda.synchronize()
+    return seq, copy
+
+
+@pytest.mark.parametrize("name", ["f32_B2_T300_d64", "bf16_packed_ragged_d128", "bf16_T0"])
+def test_backward_overlapped_matches_sequential(name):
+    """kda_chunk_backward_overlapped (forward replay on a second stream) gives
+    the sequential call's results bit for bit, and against the oracle."""
+    if name == "f32_B2_T300_d64":
+        inp = _case(2, 300, 2, 64, "f32", wid=340)
+    elif name == "bf16_packed_ragged_d128":
+        inp = _case(1, 0, 2, 128, "bf16", lengths=[130, 1, 64, 257], wid=341)
+    else:
+        inp = _case(1, 0, 2, 128, "bf16", lengths=[0, 0], wid=342)
+    note(f"chunk_backward overlapped {name}")
+    seq, ov = _both(to_dev(inp))
+    for key in GRADS:
+        assert (seq[key] is None) == (ov[key] is None), key
+        if seq[key] is not None:
+            assert torch.equal(seq[key], ov[key]), key
+    if inp["q"].shape[1] > 0:
+        _check(name + " overlapped", ov, _oracle_backward(inp), "f32" if name.startswith("f32") else "bf16")
+
+
+def test_backward_overlapped_full_workload():
+    """The overlapped call at the benchmarked size (B=1, H=16, T=4096, d=128,
+    bf16) equals the sequential call bit for bit."""
+    w = synth.WORKLOADS[1]
+    note("chunk_backward overlapped, T=4096 H=16 workload")
+    inp = synth.workload_inputs(w, device="cuda")
+    inp.update(synth.grad_inputs(inp, w.wid, device="cuda"))
+    seq, ov = _both(inp)
+    for key in GRADS:
+        if seq[key] is not None:
+            assert torch.equal(seq[key], ov[key]), key
