@@ -233,7 +233,7 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d,
  * floor itself too: the derivative from above) and gives 0 where g is below.
  * The call replays the forward internally (its outputs are not needed).
  * The workspace (kda_chunk_backward_workspace_size, 256-byte aligned) holds
- * the replay's states and fp32 per-chunk records: about 0.6 MiB per
+ * the replay's states and fp32 per-chunk records: about 0.55 MiB per
  * (chunk of 64 tokens, head) at d = 128.  Outputs must not overlap each
  * other, the inputs or the workspace.  Other rules as kda_chunk_forward.
  */
