@@ -508,7 +508,7 @@ template <int D> struct StateOps {
 template <int D>
 __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
                                                      const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs,
-                                                     int n_rows, int T_per, int H,
+                                                     int n_rows, int T_per, int H, int64_t m_lo, int64_t m_hi,
                                                      float* __restrict__ dHs, float* __restrict__ dh0) {
   typedef Rec<D> R;
   constexpr int NCB = D / 16, NKC = C / 16, NKH = D / 32;
@@ -532,21 +532,30 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   auto rec_of = [&](int64_t m) { return rec + ((base + m) * H + h) * (int64_t)R::FLOATS; };
   auto dhs_of = [&](int64_t m) { return dHs + ((base + m) * H + h) * (int64_t)D * D; };
   if (nc == 0) {  // no tokens: the gradient passes through unchanged
-    if (dh0)
+    if (dh0 && m_lo == 0)
       for (int x = tid; x < D * 16; x += blockDim.x) {
         const int c = x / 16, j = x % 16;
         dh0[sd + c * D + j0 + j] = dht ? dht[sd + c * D + j0 + j] : 0.f;
       }
     return;
   }
-  // the last chunk's end-state gradient is dht: store it and form G
+  // this launch walks chunks [m_lo, top) of the sequence
+  const int64_t top = nc < m_hi ? nc : m_hi;
+  if (top <= m_lo) return;
+  // the end-state gradient of chunk top - 1: dht for the sequence's last
+  // chunk (stored), else what the launch over the later chunks stored
   {
-    const float* Rp = rec_of(nc - 1);
-    float* dHo = dhs_of(nc - 1);
+    const float* Rp = rec_of(top - 1);
+    float* dHo = dhs_of(top - 1);
     for (int x = tid; x < D * 16; x += blockDim.x) {
       const int c = x / 16, j = x % 16;
-      const float v = dht ? dht[sd + c * D + j0 + j] : 0.f;
-      dHo[c * D + j0 + j] = v;
+      float v;
+      if (top == nc) {
+        v = dht ? dht[sd + c * D + j0 + j] : 0.f;
+        dHo[c * D + j0 + j] = v;
+      } else {
+        v = dHo[c * D + j0 + j];
+      }
       G[c][j] = Rp[R::GAM + c] * v;
     }
   }
@@ -597,33 +606,36 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       }
     }
   };
-  opsA.load(rec_of(nc - 1), j0, wave, lane);
-  for (int64_t m = nc - 1; m >= 0; m -= 2) {
+  opsA.load(rec_of(top - 1), j0, wave, lane);
+  for (int64_t m = top - 1; m >= m_lo; m -= 2) {
     step(opsA, opsB, m);
-    if (m == 0) break;
+    if (m == m_lo) break;
     step(opsB, opsA, m - 1);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Local gradients of one chunk.
+// Local gradients of one chunk, for the chunks m_lo <= m < m_hi of their
+// sequences (the other workgroups of the grid exit at once).
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
     const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
-    T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta) {
+    T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta,
+    int64_t m_lo, int64_t m_hi) {
   typedef Rec<D> R;
   typedef Scr<D> W;
   __shared__ ChunkPos pos;
   // the products' slices, and later the per-element dGamma of the chunk
   constexpr int kLds = kGemmLds > C * D ? kGemmLds : C * D;
   __shared__ __align__(16) float lds[kLds];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
   if (!chunk_pos_shared(slot, cu, seqs, n_rows, T_per, &pos)) return;
+  if (pos.m < m_lo || pos.m >= m_hi) return;  // another launch's chunks
   const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
   float* Wp = scr + (slot * H + h) * (int64_t)W::FLOATS;
   const float* dH = dHs + (slot * H + h) * (int64_t)D * D;
@@ -803,31 +815,64 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
                        zero);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  if (aux) {
-    // forked after the record pass, so that the replay fills the CUs the
-    // state-gradient pass (one workgroup per pair and 16 columns) leaves idle
-    if ((e = hipEventRecord((hipEvent_t)aux->fork, stream)) != hipSuccess) return (int)e;
-    if ((e = hipStreamWaitEvent((hipStream_t)aux->stream, (hipEvent_t)aux->fork, 0)) != hipSuccess) return (int)e;
-    const int rc = replay((hipStream_t)aux->stream);
-    if (rc != 0) return rc;
-    if ((e = hipEventRecord((hipEvent_t)aux->join, (hipStream_t)aux->stream)) != hipSuccess) return (int)e;
-  }
-  if ((e = mark(2)) != hipSuccess) return (int)e;
   // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
   const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
-  hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(512), 0, stream,
-                     (const float*)rec, dht, cu, (const int64_t*)seqs, n_rows, T_per, H, dHs, dh0);
-  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  if ((e = mark(3)) != hipSuccess) return (int)e;
-  if (aux && (e = hipStreamWaitEvent(stream, (hipEvent_t)aux->join, 0)) != hipSuccess) return (int)e;
-  if (bp.n_slots > 0) {
-    hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k, in.g, cu,
+  constexpr int64_t kAll = INT64_MAX;
+  auto state = [&](int64_t lo, int64_t hi) {
+    hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(512), 0, stream,
+                       (const float*)rec, dht, cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, dHs, dh0);
+    return hipGetLastError();
+  };
+  auto local = [&](hipStream_t st, int64_t lo, int64_t hi) {
+    if (bp.n_slots == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(kThreads), 0, st, (const T*)in.q, (const T*)in.k, in.g, cu,
                        (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0, (const float*)ht,
                        (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv,
-                       (T*)dg, dbeta);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+                       (T*)dg, dbeta, lo, hi);
+    return hipGetLastError();
+  };
+  if (!aux) {
+    if ((e = mark(2)) != hipSuccess) return (int)e;
+    if ((e = state(0, kAll)) != hipSuccess) return (int)e;
+    if ((e = mark(3)) != hipSuccess) return (int)e;
+    if ((e = local(stream, 0, kAll)) != hipSuccess) return (int)e;
+    return (int)mark(4);
   }
-  return (int)mark(4);
+  // Second stream.  The state-gradient pass runs one workgroup per (pair, 16
+  // columns) and leaves most CUs idle at small batch; the second stream fills
+  // them.  First with the replay, forked after the record pass.  Then the
+  // state gradients are walked in two launches, the later half of the
+  // (average) chunks of a sequence first; while the second launch walks the
+  // earlier half, the side stream computes the local gradients of the later
+  // half.  Those of the earlier half follow on the call's stream once the
+  // walk and the replay are done, beside whatever the side stream has left.
+  const hipStream_t side = (hipStream_t)aux->stream;
+  const hipEvent_t fork = (hipEvent_t)aux->fork, join = (hipEvent_t)aux->join;
+  if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
+  if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
+  const int rc = replay(side);
+  if (rc != 0) return rc;
+  if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;  // replay done
+  const int64_t per_seq = cu ? (T_per + (int64_t)C * n_rows - 1) / ((int64_t)C * (n_rows > 0 ? n_rows : 1))
+                             : (T_per + C - 1) / C;
+  const int64_t split = per_seq / 2;
+  if (split > 0) {
+    if ((e = state(split, kAll)) != hipSuccess) return (int)e;
+    // the event is recorded again: the replay's wait above holds its earlier state
+    if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
+    if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
+    if ((e = local(side, split, kAll)) != hipSuccess) return (int)e;
+    if ((e = state(0, split)) != hipSuccess) return (int)e;
+    if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;  // the replay
+    if ((e = local(stream, 0, split)) != hipSuccess) return (int)e;
+    // join recorded again after the side's local gradients; the wait above
+    // holds the replay's record
+    if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;
+    return (int)hipStreamWaitEvent(stream, join, 0);
+  }
+  if ((e = state(0, kAll)) != hipSuccess) return (int)e;
+  if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;
+  return (int)local(stream, 0, kAll);
 }
 
 }  // namespace

@@ -225,7 +225,8 @@ struct AuxStream {
 // without a gate, dh0 may be null (not written).  events: null, or
 // kBwdLaunches + 1 hipEvent_t handles recorded before each stage and after
 // the last.  aux: null (every launch on `stream`), or a second stream for the
-// forward replay (then events must be null).  Returns a hipError_t.
+// forward replay and the local gradients of the later half of the chunks
+// (then events must be null).  Returns a hipError_t.
 int launch_chunk_backward(int is_bf16, int d, int n_rows, int T, int H, const BwdPlan& bp, float g_floor, int gate,
                           const ChunkInputs& in, const float* h0, const int32_t* cu, const void* dout,
                           const float* dht, void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,

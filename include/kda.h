@@ -246,13 +246,17 @@ int kda_chunk_backward(const kda_chunk_desc_t* d,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * kda_chunk_backward with its forward replay on a second stream.  Only the
- * local-gradient stage reads what the replay writes, so the replay runs beside
- * the chunk-record and state-gradient stages (the latter fills one CU per
- * (sequence, head, 16 state columns) and leaves the rest idle at small batch).
- *   aux_stream : hipStream_t (NULL = the default stream) the replay is
- *                enqueued on; it waits for `stream` at the fork, and `stream`
- *                waits for it before the local-gradient stage.
+ * kda_chunk_backward with part of its work on a second stream.  Only the
+ * local-gradient stage reads what the forward replay writes, so the replay
+ * runs beside the state-gradient stage, which fills one CU per (sequence,
+ * head, 16 state columns) and leaves the rest idle at small batch.  That stage
+ * is then walked in two launches (the later half of the chunks first), and
+ * the local gradients of the later half run on the second stream beside the
+ * walk over the earlier half.
+ *   aux_stream : hipStream_t (NULL = the default stream) that work is
+ *                enqueued on; it waits for `stream` at each fork, and
+ *                `stream` waits for it before the call's last launch and
+ *                once more at the end.
  *   fork_event, join_event : two distinct caller-created hipEvent_t; both are
  *                re-recorded by every call, so concurrent calls need their own.
  * Results are bit-identical to kda_chunk_backward.  Every work item the call
