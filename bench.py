@@ -140,6 +140,8 @@ def parse():
     ap.add_argument("--only", choices=("prefill", "decode", "backward", "both"), default="both")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the packed and long-context workloads")
+    ap.add_argument("--bwd-sequential", action="store_true",
+                    help="backward leg: only kda_chunk_backward (one launch per kernel and call, for counters)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="only run device copies of this size (counter calibration)")
     return ap.parse_args()
@@ -405,7 +407,7 @@ def bench_mx(calls: int):
             "hbm_frac": (in_bytes + th * 2 * d + 2 * H * STATE_BYTES) / mean / 1e9 / PEAK_HBM_GBS}
 
 
-def bench_backward(calls: int, with_cpu: bool = True):
+def bench_backward(calls: int, with_cpu: bool = True, overlap: bool = True):
     """Backward pass on the prefill workload with N(0, 1) upstream gradients
     for o and ht: mean call of kda_chunk_backward_overlapped (the value) and
     of kda_chunk_backward, and per-stage durations (HIP events on the launch
@@ -427,7 +429,8 @@ def bench_backward(calls: int, with_cpu: bool = True):
                                   dht=inp["dht"], out=out, workspace=ws, events=events, overlap=overlap)
 
     out.update(call())
-    call(overlap=True)
+    if overlap:
+        call(overlap=True)
     torch.cuda.synchronize()
 
     def timed(overlap):
@@ -440,7 +443,7 @@ def bench_backward(calls: int, with_cpu: bool = True):
         return sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
 
     mean_seq = timed(False)
-    mean = timed(True)
+    mean = timed(True) if overlap else mean_seq
     n_ev = len(kda.BWD_STAGES) + 1
     evl = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(calls)]
     for row in evl:
@@ -486,7 +489,8 @@ def bench_backward(calls: int, with_cpu: bool = True):
         log(f"cpu oracle backward: {el:.2f} s for 2 heads")
     del inp
     return {"workload": "kda-backward-bf16-B1-H16-T4096-d128 (do, dht ~ N(0,1))", "mean_call_us": mean * 1e6,
-            "call": "kda_chunk_backward_overlapped (forward replay on a second stream)",
+            "call": ("kda_chunk_backward_overlapped (replay and the later chunks' local gradients on a second stream)"
+                     if overlap else "kda_chunk_backward"),
             "sequential_call_us": mean_seq * 1e6,
             "cpu_baseline": cpu,
             "value": B * T / mean, "unit": "tokens/s",
@@ -623,7 +627,7 @@ def main() -> int:
         out["mx_workload"] = bench_mx(100)
         out["backward_workload"] = bench_backward(20, not args.no_cpu)
     if args.only == "backward":
-        out["backward_workload"] = bench_backward(args.steps, not args.no_cpu)
+        out["backward_workload"] = bench_backward(args.steps, not args.no_cpu, not args.bwd_sequential)
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9
