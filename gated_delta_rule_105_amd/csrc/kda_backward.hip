@@ -473,35 +473,33 @@ __device__ __forceinline__ f32x4 mma_panels(f32x4 acc, const f32x4 (&a)[NK], con
 // dH the gradient of a chunk's end state (these 16 columns) and
 // G = diag(gamma) dH, a step is
 //   dU = P^T dO + Kh G,   dH_in = G + Qt^T dO - Wk^T dU.
-// Row tile t (of 4) of dU is split over k: wave t takes P^T dO and the first
-// half of Kh G, wave t + 4 the second half; the two partial tiles sit in LDS
+// Row tile t (of 4) of dU is split over k between waves t and t + 4, each
+// taking half of P^T dO and half of Kh G; the two partial tiles sit in LDS
 // and are added where dU is read.  Wave w < D / 16 owns row tile w of dH.
 // Every record operand of the next chunk (the step's k-panels and the gamma
 // of the wave's own rows) is loaded while the current chunk is computed, so
-// the chain of chunks waits on memory once, not once per step.  Workgroups
-// are ordered so that the column blocks of one (sequence, head) pair have the
-// same block index mod 8, i.e. share one XCD's L2 (the record operands are
-// common to them).
+// the chain of chunks waits on memory once, not once per step.  For that
+// every wave issues the same loads on every step (61 at d = 128: below the 63
+// that the hardware counts, so that waiting for the current operands never
+// means waiting for the next ones).  Workgroups are ordered so that the column
+// blocks of one (sequence, head) pair have the same block index mod 8, i.e.
+// share one XCD's L2 (the record operands are common to them).
 template <int D> struct StateOps {
-  static constexpr int NKC = C / 16, NKH = D / 32;
-  f32x4 aP[NKC], aKh[NKH], bO[NKC], aQ[NKC], aW[NKC];
-  float gr[4];  // gamma of rows 16 w + 4 g + e (this wave's dH tile)
+  static constexpr int NKC = C / 16, NKH = D / 32, NKP = C / 32;
+  f32x4 aP[NKP], aKh[NKH], bO[NKC], aQ[NKC], aW[NKC];
+  f32x4 gr;  // gamma of rows 16 w + 4 g + e (this wave's dH tile)
   // gamma first: a step needs the next chunk's gamma before its other operands
-  // (loads complete in issue order)
+  // (loads complete in issue order).  Waves past D / 16 (d = 64) load a
+  // copy of another wave's dH operands and do not use them.
   __device__ void load(const float* Rp, int j0, int wave, int lane) {
     typedef Rec<D> R;
-    const int t = wave & 3, koff = wave < 4 ? 0 : D / 2;
-    if (wave < D / 16) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gr[e] = Rp[R::GAM + 16 * wave + 4 * (lane >> 4) + e];
-    }
-    load_panel(bO, Rp + R::DO + j0, 1, D, lane);                           // B(k = r, j) = dO[r][j0 + j]
-    load_panel(aKh, Rp + R::KH + 16 * t * D + koff, D, 1, lane);            // Kh rows 16 t.., k from koff
-    if (wave < 4) load_panel(aP, Rp + R::PM + 16 * t, 1, C, lane);          // P^T rows 16 t..: P[r][16 t + i]
-    if (wave < D / 16) {
-      load_panel(aQ, Rp + R::QT + 16 * wave, 1, D, lane);                   // Qt^T rows 16 w..
-      load_panel(aW, Rp + R::WK + 16 * wave, 1, D, lane);
-    }
+    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16);
+    gr = *(const f32x4*)(Rp + R::GAM + 16 * w + 4 * (lane >> 4));
+    load_panel(bO, Rp + R::DO + j0, 1, D, lane);                               // B(k = r, j) = dO[r][j0 + j]
+    load_panel(aKh, Rp + R::KH + 16 * t * D + half * (D / 2), D, 1, lane);      // Kh rows 16 t.., k in this half
+    load_panel(aP, Rp + R::PM + half * (C / 2) * C + 16 * t, 1, C, lane);       // P^T rows 16 t.., k in this half
+    load_panel(aQ, Rp + R::QT + 16 * w, 1, D, lane);                            // Qt^T rows 16 w..
+    load_panel(aW, Rp + R::WK + 16 * w, 1, D, lane);                            // Wk^T rows 16 w..
   }
 };
 
@@ -562,25 +560,31 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   // two operand sets used in turn: step m computes from one while the other
   // receives chunk m - 1
   StateOps<D> opsA, opsB;
-  const int t = wave & 3, koff = wave < 4 ? 0 : D / 2;
+  const int t = wave & 3, half = wave >> 2, koff = half * (D / 2);
   auto step = [&](StateOps<D>& cur, StateOps<D>& nxt, int64_t m) {
-    if (m > 0) nxt.load(rec_of(m - 1), j0, wave, lane);
+    // cur arrived during the previous step: wait for it here, leaving at most
+    // that step's four dH stores in flight, so that no later wait for cur can
+    // take the loads issued next with it
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4) expcnt(7) lgkmcnt(15)
+    nxt.load(rec_of(m > m_lo ? m - 1 : m), j0, wave, lane);  // (the last step loads a chunk it does not use)
     lds_barrier();  // G ready
-    // dU: wave t < 4 adds P^T dO to its half of Kh G
+    // dU: this wave's halves of P^T dO and Kh G
     {
-      f32x4 bG[NKH];
+      f32x4 bG[NKH], bOh[StateOps<D>::NKP];
 #pragma unroll
       for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) bG[kk][e] = G[koff + 16 * kk + 4 * g + e][ii];
+#pragma unroll
+      for (int kk = 0; kk < StateOps<D>::NKP; ++kk) bOh[kk] = half ? cur.bO[StateOps<D>::NKP + kk] : cur.bO[kk];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (wave < 4) acc = mma_panels(acc, cur.aP, cur.bO);
+      acc = mma_panels(acc, cur.aP, bOh);
       acc = mma_panels(acc, cur.aKh, bG);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dU[wave >> 2][16 * t + 4 * g + e][ii] = acc[e];
     }
     lds_barrier();  // both halves of dU
-    if (wave < D / 16) {
+    if (D / 16 >= 8 || wave < D / 16) {
       f32x4 bU[NKC];
 #pragma unroll
       for (int kk = 0; kk < NKC; ++kk)
