@@ -1168,10 +1168,12 @@ kda_chunk_prep(const ChunkInputs in, const int32_t* __restrict__ cu, int n_rows,
     }
     __syncthreads();  // Wk complete; Tp, Qt, Kh and beta are dead
     // the next chunk's q, k, g and beta go to their areas now (v's area holds
-    // Wk until the end of the chunk)
+    // Wk until the end of the chunk).  With MAPS, v is fetched only after
+    // that store: the store's wait for q, k and g would otherwise cover the v
+    // loads too (loads complete in order), leaving no time to hide them.
     if (more) {
-      if (MAPS) raw.load_v(in, tok_n, len_n, H, h, tid);
       raw.store_qkg(smem, tid);
+      if (MAPS) raw.load_v(in, tok_n, len_n, H, h, tid);
     }
     save_wk<T, D, M::V>(smem, cr, wave, NW, lane);
 #pragma unroll
