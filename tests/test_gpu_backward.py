@@ -228,11 +228,12 @@ def test_backward_deterministic():
         assert torch.equal(a[key], b[key]), key
 
 
-def _both(d, **kw):
+def _both(d, g="same", **kw):
     """The sequential call, then two overlapped calls in a row (the second
     one's outputs copied on the calling stream straight after it, before any
-    synchronisation: the copy must see the finished gradients)."""
-    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"])
+    synchronisation: the copy must see the finished gradients).  g: the gate
+    to pass instead of d["g"] (a per-head gate, or None)."""
+    args = (d["q"], d["k"], d["v"], d["g"] if isinstance(g, str) else g, d["beta"], d["do"])
     kw = dict(h0=d.get("h0"), dht=d.get("dht"), cu_seqlens=d.get("cu_seqlens"), **kw)
     seq = kda.chunk_backward(*args, **kw)
     kda.chunk_backward(*args, overlap=True, **kw)
@@ -271,5 +272,23 @@ def test_backward_overlapped_full_workload():
     inp.update(synth.grad_inputs(inp, w.wid, device="cuda"))
     seq, ov = _both(inp)
     for key in GRADS:
+        if seq[key] is not None:
+            assert torch.equal(seq[key], ov[key]), key
+
+
+@pytest.mark.parametrize("name,mode", [("head-bf16-d64-T300", "head"), ("none-bf16-d128-varlen", "none")])
+def test_backward_overlapped_gates(name, mode):
+    """The overlapped call with a per-head gate (Gated DeltaNet) and with none
+    (DeltaNet) equals the sequential call bit for bit."""
+    if name.startswith("head"):
+        inp = _case(1, 300, 2, 64, "bf16", wid=343)
+    else:
+        inp = _case(1, 0, 2, 128, "bf16", lengths=[200, 3, 129], wid=344)
+    d = to_dev(inp)
+    g = d["g"][..., 0].contiguous() if mode == "head" else None
+    note(f"chunk_backward overlapped gate={mode} {name}")
+    seq, ov = _both(d, g=g)
+    for key in GRADS:
+        assert (seq[key] is None) == (ov[key] is None), key
         if seq[key] is not None:
             assert torch.equal(seq[key], ov[key]), key
