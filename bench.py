@@ -65,17 +65,20 @@ ISSUED_FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 5 * 128 * 64)
 BYTES_PER_TOKEN_HEAD = 5 * 2 * 128 + 4
 STATE_BYTES = 128 * 128 * 4    # one fp32 state matrix (h0 read, ht written)
 
-# The same work split over the call's launches (per token and head).  The
-# chunk pass reads every input and does the chunk-local products (key Gram,
-# P, Wk, Wv, the inverse); the output pass does the state products and P U
-# and writes o (plus h0 read / ht written per sequence and head).  The
-# segment maps (composed in the chunk pass) and the scan are extra work of
-# the segment decomposition, with no share of the algorithmic figures.
+# The same work per launch (per token and head).  The output sweep does the
+# whole algorithmic work of the call: it reads every input, recomputes the
+# chunk-local algebra, applies the state and writes o (plus ht per sequence
+# and head).  The map sweep (composes each segment's affine state map from
+# k, v, g, beta) and the segment scan are extra work of the segment
+# decomposition: the map sweep's figures are its own compulsory reads and
+# products (chunk-local key Gram, Wk, Wv, inverse; U = Wv - Wk B, Kh^T U,
+# Wk M, Kh^T (Wk M) on the map), with no share of the call's algorithmic
+# figures.
 LAUNCH_WORK = {
-    "kda_chunk_prep": dict(bytes=4 * 2 * 128 + 4,
-                           flop=2 * (128 * 63 // 2 + 3 * 128 * 65 // 2 + 63 * 62 // 6)),
+    "kda_chunk_sweep_map": dict(bytes=3 * 2 * 128 + 4,
+                                flop=2 * (128 * 63 // 2 + 2 * 128 * 65 // 2 + 63 * 62 // 6 + 4 * 128 * 128)),
     "kda_seg_scan": dict(bytes=0, flop=0),
-    "kda_seg_forward": dict(bytes=2 * 128, flop=2 * (3 * 128 * 128 + 128 * 65 // 2)),
+    "kda_chunk_sweep_out": dict(bytes=BYTES_PER_TOKEN_HEAD, flop=FLOP_PER_TOKEN_HEAD),
 }
 
 # Backward pass (kda_chunk_backward) per (token, head) at d = 128, C = 64.
@@ -593,8 +596,8 @@ def main() -> int:
         dom = max(p["launch"], key=p["launch"].get)
         t_dom = p["launch"][dom]
         work = LAUNCH_WORK[dom]
-        dom_bytes = work["bytes"] * p["token_heads"] + (2 * PREFILL["B"] * PREFILL["H"] * STATE_BYTES
-                                                         if dom == "kda_seg_forward" else 0)
+        dom_bytes = work["bytes"] * p["token_heads"] + (PREFILL["B"] * PREFILL["H"] * STATE_BYTES
+                                                         if dom == "kda_chunk_sweep_out" else 0)
         dom_flop = work["flop"] * p["token_heads"]
         gbs = dom_bytes / t_dom / 1e9
         traffic = read_traffic(f"{dom}_prefill_T4096_H16_traffic.txt", source_digest(PREFILL_SOURCES))

@@ -24,11 +24,12 @@ from __future__ import annotations
 from typing import Optional, Tuple
 
 from ._lib import (BWD_STAGES, CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_GATE_CHANNEL, KDA_GATE_HEAD,
-                   KDA_GATE_NONE, KDA_OK, ChunkDesc, KdaError, status_string, version)
+                   KDA_GATE_NONE, KDA_OK, ChunkDesc, ChunkDescEx, KdaError, status_string, version)
 from . import _lib
 
 __all__ = ["chunk_forward", "chunk_forward_states", "chunk_forward_mx", "chunk_backward", "decode_step",
-           "workspace_bytes", "backward_workspace_bytes", "make_desc", "KdaError", "status_string", "version",
+           "workspace_bytes", "backward_workspace_bytes", "make_desc", "make_desc_ex", "KdaError", "status_string",
+           "version",
            "CHUNK_LAUNCHES", "BWD_STAGES"]
 
 
@@ -64,9 +65,34 @@ def _check_dev(name, t, dtype=None, shape=None):
 
 
 def make_desc(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
-              g_floor: float = -0.125, gate: int = KDA_GATE_CHANNEL) -> ChunkDesc:
+              g_floor: float = -0.125) -> ChunkDesc:
     return ChunkDesc(B=B, T=T, H=H, d_k=d, d_v=d, chunk=chunk, n_seqs=n_seqs,
-                     dtype=_dtype_code(dtype), g_floor=g_floor, gate=gate)
+                     dtype=_dtype_code(dtype), g_floor=g_floor)
+
+
+def make_desc_ex(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
+                 g_floor: float = -0.125, gate: int = KDA_GATE_CHANNEL) -> ChunkDescEx:
+    return ChunkDescEx(shape=make_desc(B, T, H, d, dtype, n_seqs, chunk, g_floor), gate=gate)
+
+
+class _on_stream:
+    """Context in which torch allocates from the pool of the stream the
+    library enqueues on, so that a tensor freed on return (a workspace) is
+    not handed to other work while that stream still uses it."""
+
+    def __init__(self, stream, device):
+        self.ctx = None
+        if stream is not None:
+            torch = _torch()
+            self.ctx = torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device))
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
 
 
 def _gate_of(g, full_dims: int) -> int:
@@ -175,44 +201,48 @@ def _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
             check_cu_seqlens(cu_seqlens.cpu(), T)
     S = n_seqs if n_seqs else B
     _check_dev("h0", h0, torch.float32, (S, H, d, d))
-    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor, gate)
+    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor)
+    dx = ChunkDescEx(shape=desc, gate=gate)
     ws_bytes = _lib.workspace_size(desc)
-    if o is None:
-        o = torch.empty((B, T, H, d), dtype=dt, device=q.device)
+    with _on_stream(stream, q.device):
+        if o is None:
+            o = torch.empty((B, T, H, d), dtype=dt, device=q.device)
+        if ht is None and output_final_state:
+            ht = torch.empty((S, H, d, d), dtype=torch.float32, device=q.device)
+        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     _check_dev("o", o, dt, (B, T, H, d))
-    if ht is None and output_final_state:
-        ht = torch.empty((S, H, d, d), dtype=torch.float32, device=q.device)
     _check_dev("ht", ht, torch.float32, (S, H, d, d))
-    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    args = (desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
-            _ptr(ht))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o), _ptr(ht))
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), stream)
     if mx is not None:
-        st = _lib.chunk_forward_mx_raw(desc, _ptr(q), _ptr(mx[0]), _ptr(k), _ptr(mx[1]), _ptr(v), _ptr(mx[2]),
-                                       *args[4:], *tail)
+        st = _lib.chunk_forward_mx_raw(dx, _ptr(q), _ptr(mx[0]), _ptr(k), _ptr(mx[1]), _ptr(v), _ptr(mx[2]),
+                                       *ptrs[3:], *tail)
         what = "kda_chunk_forward_mx"
     elif states is not None:
-        st = _lib.chunk_forward_states_raw(*args, _ptr(states) if states.numel() else None, states_every,
+        st = _lib.chunk_forward_states_raw(dx, *ptrs, _ptr(states) if states.numel() else None, states_every,
                                            *tail)
         what = "kda_chunk_forward_states"
-    elif events is None:
-        st = _lib.chunk_forward_raw(*args, *tail)
+    elif events is not None:
+        st = _lib.chunk_forward_timed_raw(dx, *ptrs, *tail, events)
+        what = "kda_chunk_forward_timed"
+    elif gate == KDA_GATE_CHANNEL:
+        st = _lib.chunk_forward_raw(desc, *ptrs, *tail)
         what = "kda_chunk_forward"
     else:
-        st = _lib.chunk_forward_timed_raw(*args, *tail, events)
-        what = "kda_chunk_forward_timed"
+        st = _lib.chunk_forward_gated_raw(dx, *ptrs, *tail)
+        what = "kda_chunk_forward_gated"
     if st != KDA_OK:
         raise KdaError(st, what)
     return o, ht, states
 
 
 def backward_workspace_bytes(B: int, T: int, H: int, d: int, dtype, n_seqs: int = 0, chunk: int = 64,
-                             g_floor: float = -0.125, gate: int = KDA_GATE_CHANNEL) -> int:
-    """Device workspace one chunk_backward call of this shape needs."""
-    return _lib.backward_workspace_size(make_desc(B, T, H, d, dtype, n_seqs, chunk, g_floor, gate))
+                             g_floor: float = -0.125) -> int:
+    """Device workspace one chunk_backward call of this shape needs (any gate)."""
+    return _lib.backward_workspace_size(make_desc(B, T, H, d, dtype, n_seqs, chunk, g_floor))
 
 
 _AUX = {}
@@ -271,33 +301,37 @@ def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chu
     S = n_seqs if n_seqs else B
     _check_dev("h0", h0, torch.float32, (S, H, d, d))
     _check_dev("dht", dht, torch.float32, (S, H, d, d))
-    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor, gate)
+    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor)
+    dx = ChunkDescEx(shape=desc, gate=gate)
     ws_bytes = _lib.backward_workspace_size(desc)
     out = dict(out or {})
     dev = q.device
+    with _on_stream(stream, dev):
+        for name, shape, odt in (("dq", (B, T, H, d), dt), ("dk", (B, T, H, d), dt), ("dv", (B, T, H, d), dt),
+                                 ("dbeta", (B, T, H), torch.float32)):
+            if out.get(name) is None:
+                out[name] = torch.empty(shape, dtype=odt, device=dev)
+        if gate != KDA_GATE_NONE and out.get("dg") is None:
+            out["dg"] = torch.empty(gshape, dtype=dt, device=dev)
+        if want_dh0 and out.get("dh0") is None:
+            out["dh0"] = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     for name, shape, odt in (("dq", (B, T, H, d), dt), ("dk", (B, T, H, d), dt), ("dv", (B, T, H, d), dt),
                              ("dbeta", (B, T, H), torch.float32)):
-        if out.get(name) is None:
-            out[name] = torch.empty(shape, dtype=odt, device=dev)
         _check_dev(name, out[name], odt, shape)
     if gate == KDA_GATE_NONE:
         out["dg"] = None
     else:
-        if out.get("dg") is None:
-            out["dg"] = torch.empty(gshape, dtype=dt, device=dev)
         _check_dev("dg", out["dg"], dt, gshape)
     if want_dh0:
-        if out.get("dh0") is None:
-            out["dh0"] = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
         _check_dev("dh0", out["dh0"], torch.float32, (S, H, d, d))
     else:
         out["dh0"] = None
-    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     aux = _aux_stream(dev) if overlap else None
-    st = _lib.chunk_backward_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+    st = _lib.chunk_backward_raw(dx, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                                  _ptr(cu_seqlens), _ptr(do), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]),
                                  _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), stream, events,
@@ -323,12 +357,17 @@ def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, str
     _check_dev("beta", beta, torch.float32, (N, H))
     _check_dev("state", state, torch.float32, (N, H, d, d))
     if o is None:
-        o = torch.empty((N, H, d), dtype=dt, device=q.device)
+        with _on_stream(stream, q.device):
+            o = torch.empty((N, H, d), dtype=dt, device=q.device)
     _check_dev("o", o, dt, (N, H, d))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = _lib.decode_step_raw(N, H, d, d, _dtype_code(dt), gate, g_floor, _ptr(q), _ptr(k), _ptr(v),
-                              _ptr(g), _ptr(beta), _ptr(state), _ptr(o), stream)
+    if gate == KDA_GATE_CHANNEL:
+        st = _lib.decode_step_raw(N, H, d, d, _dtype_code(dt), g_floor, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(state), _ptr(o), stream)
+    else:
+        st = _lib.decode_step_gated_raw(N, H, d, d, _dtype_code(dt), gate, g_floor, _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(g), _ptr(beta), _ptr(state), _ptr(o), stream)
     if st != KDA_OK:
-        raise KdaError(st, "kda_decode_step")
+        raise KdaError(st, "kda_decode_step" if gate == KDA_GATE_CHANNEL else "kda_decode_step_gated")
     return o

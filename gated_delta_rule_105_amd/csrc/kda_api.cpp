@@ -1,8 +1,10 @@
 // C-ABI front end of the KDA library: argument validation and dispatch.
 //
-// Plain C++: nothing here touches HIP, so every argument error is reported
-// before any GPU call (and can be exercised on a machine without a GPU).
-// The entry points and their contracts are declared in include/kda.h.
+// Plain C++: every argument error is reported before any launch (and can be
+// exercised on a machine without a GPU); the only HIP call made here is the
+// compute-unit query behind the forward's cut into segments
+// (kda::device_compute_units).  The entry points and their contracts are
+// declared in include/kda.h.
 #include "kda.h"
 
 #include <math.h>
@@ -46,16 +48,18 @@ struct Sizes {
   size_t g_bytes;     // g for the descriptor's gate (0 without one)
   size_t beta_bytes;
   size_t state_bytes; // h0 or ht
+  int n_cu;           // compute units the plan was made for
   kda::SegPlan plan;  // segments and workspace
 };
 
-int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
+bool valid_gate(int gate) { return gate == KDA_GATE_CHANNEL || gate == KDA_GATE_HEAD || gate == KDA_GATE_NONE; }
+
+int check_desc(const kda_chunk_desc_t* d, int gate, Sizes* s) {
   if (!d) return KDA_ERR_INVALID_ARGUMENT;
   if (d->B < 1 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1 || d->n_seqs < 0)
     return KDA_ERR_INVALID_ARGUMENT;
   if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
-  if (d->gate != KDA_GATE_CHANNEL && d->gate != KDA_GATE_HEAD && d->gate != KDA_GATE_NONE)
-    return KDA_ERR_INVALID_ARGUMENT;
+  if (!valid_gate(gate)) return KDA_ERR_INVALID_ARGUMENT;
   if (d->n_seqs > 0 && d->B != 1) return KDA_ERR_INVALID_ARGUMENT;
   if (!(d->g_floor >= -1.0f && d->g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;  // NaN fails too
   if ((double)d->chunk * -(double)d->g_floor > 16.0) return KDA_ERR_INVALID_ARGUMENT;
@@ -71,15 +75,17 @@ int check_desc(const kda_chunk_desc_t* d, Sizes* s) {
   if (!mul(s->tokens, H, &th) || !mul(th, D, &x) || !mul(x, elem_size(d->dtype), &s->x_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
   if (!mul(th, 4, &s->beta_bytes)) return KDA_ERR_INVALID_ARGUMENT;
-  s->g_bytes = d->gate == KDA_GATE_CHANNEL ? s->x_bytes : d->gate == KDA_GATE_HEAD ? th * elem_size(d->dtype) : 0;
+  s->g_bytes = gate == KDA_GATE_CHANNEL ? s->x_bytes : gate == KDA_GATE_HEAD ? th * elem_size(d->dtype) : 0;
   size_t sh, sd;
   if (!mul(s->n_states, H, &sh) || !mul(sh, D * D, &sd) || !mul(sd, 4, &s->state_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
   if (s->tokens > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
-  if (!kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, &s->plan))
+  s->n_cu = kda::device_compute_units();
+  if (!kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s->n_cu,
+                          &s->plan))
     return KDA_ERR_UNSUPPORTED;
-  if (s->plan.n_seg_bound > (int64_t)INT32_MAX || s->plan.n_prep_bound > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (s->plan.n_seg_bound > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 
@@ -113,7 +119,7 @@ int kda_version(void) { return KDA_VERSION; }
 int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
   if (!bytes) return KDA_ERR_INVALID_ARGUMENT;
   Sizes s;
-  const int st = check_desc(d, &s);
+  const int st = check_desc(d, KDA_GATE_CHANNEL, &s);
   if (st != KDA_OK) return st;
   *bytes = s.plan.ws_bytes;
   return KDA_OK;
@@ -122,7 +128,7 @@ int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
 int kda_chunk_forward_states_count(const kda_chunk_desc_t* d, int states_every, size_t* count) {
   if (!count) return KDA_ERR_INVALID_ARGUMENT;
   Sizes s;
-  const int st = check_desc(d, &s);
+  const int st = check_desc(d, KDA_GATE_CHANNEL, &s);
   if (st != KDA_OK) return st;
   if (!state_slots(d, states_every, count)) return KDA_ERR_INVALID_ARGUMENT;
   return KDA_OK;
@@ -137,12 +143,12 @@ struct MxIn {
 
 // states: NULL (no state emission) or the kda_chunk_forward_states buffer,
 // with every >= 1.
-static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
-                         const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
-                         float* states, int every, const MxIn* mx, void* workspace, size_t workspace_bytes,
-                         void* stream, void* const* events) {
+static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, const void* k, const void* v,
+                         const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens, void* o,
+                         float* ht, float* states, int every, const MxIn* mx, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events) {
   Sizes s;
-  const int st = check_desc(d, &s);
+  const int st = check_desc(d, gate, &s);
   if (st != KDA_OK) return st;
   const bool has_tokens = s.tokens > 0;
   // bytes of q, k, v (MXFP8: one byte per element) and of each scale tensor
@@ -153,7 +159,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
     sc_bytes = qkv_bytes / 32;
     if (has_tokens && (!mx->qs || !mx->ks || !mx->vs)) return KDA_ERR_INVALID_ARGUMENT;
   }
-  const bool gated = d->gate != KDA_GATE_NONE;
+  const bool gated = gate != KDA_GATE_NONE;
   if (!gated) g = nullptr;  // not read
   if (has_tokens && (!q || !k || !v || (gated && !g) || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
   if ((d->n_seqs > 0) != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARGUMENT;
@@ -199,49 +205,60 @@ static int chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const kda::ChunkInputs in{q, k, v, g, beta, mx ? mx->qs : nullptr, mx ? mx->ks : nullptr, mx ? mx->vs : nullptr};
   const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
-                                          d->g_floor, (int)d->gate, in, h0, cu_seqlens, o, ht,
+                                          d->g_floor, gate, in, h0, cu_seqlens, o, ht,
                                           states_bytes > 0 ? states : nullptr, every, workspace, stream,
                                           events);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+// the extended descriptor: its shape, and its gate (NULL: invalid)
+static const kda_chunk_desc_t* shape_of(const kda_chunk_desc_ex_t* d) { return d ? &d->shape : nullptr; }
+static int gate_of(const kda_chunk_desc_ex_t* d) { return d ? (int)d->gate : KDA_GATE_CHANNEL; }
+
 int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
                       const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                       void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr, workspace, workspace_bytes,
-                       stream, nullptr);
+  return chunk_forward(d, KDA_GATE_CHANNEL, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr, workspace,
+                       workspace_bytes, stream, nullptr);
 }
 
-int kda_chunk_forward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+int kda_chunk_forward_gated(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v,
+                            const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                            void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_forward(shape_of(d), gate_of(d), q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr,
+                       workspace, workspace_bytes, stream, nullptr);
+}
+
+int kda_chunk_forward_timed(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v,
                             const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                             void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events) {
   if (!events) return KDA_ERR_INVALID_ARGUMENT;
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr, workspace, workspace_bytes,
-                       stream, events);
+  return chunk_forward(shape_of(d), gate_of(d), q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr,
+                       workspace, workspace_bytes, stream, events);
 }
 
-int kda_chunk_forward_states(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+int kda_chunk_forward_states(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v,
                              const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                              void* o, float* ht, float* states, int states_every, void* workspace,
                              size_t workspace_bytes, void* stream) {
   Sizes s;
-  const int st = check_desc(d, &s);  // before state_slots divides by the chunk
+  const int st = check_desc(shape_of(d), gate_of(d), &s);  // before state_slots divides by the chunk
   if (st != KDA_OK) return st;
   size_t slots;
-  if (!state_slots(d, states_every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!state_slots(shape_of(d), states_every, &slots)) return KDA_ERR_INVALID_ARGUMENT;
   if (!states && slots > 0) return KDA_ERR_INVALID_ARGUMENT;
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, states, states_every, nullptr, workspace,
-                       workspace_bytes, stream, nullptr);
+  return chunk_forward(shape_of(d), gate_of(d), q, k, v, g, beta, h0, cu_seqlens, o, ht, states, states_every,
+                       nullptr, workspace, workspace_bytes, stream, nullptr);
 }
 
-int kda_chunk_forward_mx(const kda_chunk_desc_t* d, const void* q, const uint8_t* q_scale, const void* k,
+int kda_chunk_forward_mx(const kda_chunk_desc_ex_t* d, const void* q, const uint8_t* q_scale, const void* k,
                          const uint8_t* k_scale, const void* v, const uint8_t* v_scale, const void* g,
                          const float* beta, const float* h0, const int32_t* cu_seqlens, void* o, float* ht,
                          void* workspace, size_t workspace_bytes, void* stream) {
   const MxIn mx{q_scale, k_scale, v_scale};
-  return chunk_forward(d, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, &mx, workspace, workspace_bytes,
-                       stream, nullptr);
+  return chunk_forward(shape_of(d), gate_of(d), q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, &mx,
+                       workspace, workspace_bytes, stream, nullptr);
 }
 
 // ---- backward ------------------------------------------------------------
@@ -252,22 +269,24 @@ bool plan_bwd(const kda_chunk_desc_t* d, const Sizes& s, kda::BwdPlan* bp) {
   size_t chunk_states;
   if (!state_slots(d, 1, &chunk_states)) return false;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
-  return kda::plan_backward(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s.tokens,
-                            chunk_states, bp);
+  return kda::plan_backward(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s.n_cu,
+                            s.tokens, chunk_states, bp);
 }
 
-int chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+int chunk_backward(const kda_chunk_desc_ex_t* dx, const void* q, const void* k, const void* v, const void* g,
                    const float* beta, const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dht,
                    void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0, void* workspace,
                    size_t workspace_bytes, void* stream, void* const* events,
                    const kda::AuxStream* aux = nullptr) {
+  const kda_chunk_desc_t* d = shape_of(dx);
+  const int gate = gate_of(dx);
   Sizes s;
-  const int st = check_desc(d, &s);
+  const int st = check_desc(d, gate, &s);
   if (st != KDA_OK) return st;
   kda::BwdPlan bp;
   if (!plan_bwd(d, s, &bp)) return KDA_ERR_UNSUPPORTED;
   const bool has_tokens = s.tokens > 0;
-  const bool gated = d->gate != KDA_GATE_NONE;
+  const bool gated = gate != KDA_GATE_NONE;
   if (!gated) {
     g = nullptr;  // neither read nor written
     dg = nullptr;
@@ -297,7 +316,7 @@ int chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, cons
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const kda::ChunkInputs in{q, k, v, g, beta, nullptr, nullptr, nullptr};
   const int e = kda::launch_chunk_backward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, bp, d->g_floor,
-                                           (int)d->gate, in, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0,
+                                           gate, in, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0,
                                            workspace, stream, events, aux);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }
@@ -307,7 +326,7 @@ int chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, cons
 int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) {
   if (!bytes) return KDA_ERR_INVALID_ARGUMENT;
   Sizes s;
-  const int st = check_desc(d, &s);
+  const int st = check_desc(d, KDA_GATE_CHANNEL, &s);
   if (st != KDA_OK) return st;
   kda::BwdPlan bp;
   if (!plan_bwd(d, s, &bp)) return KDA_ERR_UNSUPPORTED;
@@ -315,7 +334,7 @@ int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) 
   return KDA_OK;
 }
 
-int kda_chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+int kda_chunk_backward(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v, const void* g,
                        const float* beta, const float* h0, const int32_t* cu_seqlens, const void* dout,
                        const float* dht, void* dq, void* dk, void* dv, void* dg, float* dbeta, float* dh0,
                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -323,7 +342,7 @@ int kda_chunk_backward(const kda_chunk_desc_t* d, const void* q, const void* k, 
                         workspace_bytes, stream, nullptr);
 }
 
-int kda_chunk_backward_overlapped(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+int kda_chunk_backward_overlapped(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v,
                                   const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                                   const void* dout, const float* dht, void* dq, void* dk, void* dv, void* dg,
                                   float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream,
@@ -334,7 +353,7 @@ int kda_chunk_backward_overlapped(const kda_chunk_desc_t* d, const void* q, cons
                         workspace_bytes, stream, nullptr, &aux);
 }
 
-int kda_chunk_backward_timed(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+int kda_chunk_backward_timed(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v,
                              const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
                              const void* dout, const float* dht, void* dq, void* dk, void* dv, void* dg,
                              float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream,
@@ -344,12 +363,19 @@ int kda_chunk_backward_timed(const kda_chunk_desc_t* d, const void* q, const voi
                         workspace_bytes, stream, events);
 }
 
-int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate, float g_floor,
-                    const void* q, const void* k, const void* v, const void* g, const float* beta, float* state,
-                    void* o, void* stream) {
+int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor, const void* q,
+                    const void* k, const void* v, const void* g, const float* beta, float* state, void* o,
+                    void* stream) {
+  return kda_decode_step_gated(N, H, d_k, d_v, dtype, KDA_GATE_CHANNEL, g_floor, q, k, v, g, beta, state, o,
+                               stream);
+}
+
+int kda_decode_step_gated(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate, float g_floor,
+                          const void* q, const void* k, const void* v, const void* g, const float* beta,
+                          float* state, void* o, void* stream) {
   if (N < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
-  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARGUMENT;
+  if (!valid_gate(gate)) return KDA_ERR_INVALID_ARGUMENT;
   if (!(g_floor >= -1.0f && g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;

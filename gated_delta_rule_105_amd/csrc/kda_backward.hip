@@ -797,8 +797,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   };
   if ((e = mark(0)) != hipSuccess) return (int)e;
   if (cu && n_rows > 0) {
-    hipLaunchKernelGGL(kda_bwd_seqs, dim3(1), dim3(256), 0, stream, cu, n_rows, seqs);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    if ((e = launch_kernel(kda_bwd_seqs, dim3(1), dim3(256), stream, cu, n_rows, seqs)) != hipSuccess) return (int)e;
   }
   // forward replay: ht and the state after every full chunk.  Only the local
   // kernel reads what it writes, and it writes nothing the record and
@@ -814,26 +813,24 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   if ((e = mark(1)) != hipSuccess) return (int)e;
   const dim3 gc((unsigned)bp.n_slots, H);
   if (bp.n_slots > 0) {
-    hipLaunchKernelGGL((kda_bwd_chunk<T, D>), gc, dim3(kThreads), 0, stream, (const T*)in.q, (const T*)in.k,
-                       (const T*)in.v, in.g, in.beta, (const T*)dout, cu, (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, rec,
-                       zero);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    if ((e = launch_kernel(kda_bwd_chunk<T, D>, gc, dim3(kThreads), stream, (const T*)in.q, (const T*)in.k,
+                           (const T*)in.v, in.g, in.beta, (const T*)dout, cu, (const int64_t*)seqs, n_rows, T_per, H,
+                           g_floor, gate, rec, zero)) != hipSuccess)
+      return (int)e;
   }
   // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
   const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
   constexpr int64_t kAll = INT64_MAX;
   auto state = [&](int64_t lo, int64_t hi) {
-    hipLaunchKernelGGL((kda_bwd_state<D>), dim3((unsigned)state_blocks), dim3(512), 0, stream,
-                       (const float*)rec, dht, cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, dHs, dh0);
-    return hipGetLastError();
+    return launch_kernel(kda_bwd_state<D>, dim3((unsigned)state_blocks), dim3(512), stream, (const float*)rec, dht,
+                         cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, dHs, dh0);
   };
   auto local = [&](hipStream_t st, int64_t lo, int64_t hi) {
     if (bp.n_slots == 0) return hipSuccess;
-    hipLaunchKernelGGL((kda_bwd_local<T, D>), gc, dim3(kThreads), 0, st, (const T*)in.q, (const T*)in.k, in.g, cu,
-                       (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0, (const float*)ht,
-                       (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv,
-                       (T*)dg, dbeta, lo, hi);
-    return hipGetLastError();
+    return launch_kernel(kda_bwd_local<T, D>, gc, dim3(kThreads), st, (const T*)in.q, (const T*)in.k, in.g, cu,
+                         (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0,
+                         (const float*)ht, (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq,
+                         (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi);
   };
   if (!aux) {
     if ((e = mark(2)) != hipSuccess) return (int)e;

@@ -144,9 +144,8 @@ static int launch_typed(int N, int H, float g_floor, int gate, const void* q, co
                         const void* g, const float* beta, float* state, void* o, hipStream_t s) {
   const size_t blocks = (size_t)N * H;
   if (blocks == 0) return 0;
-  hipLaunchKernelGGL((kda_decode<T, D>), dim3((unsigned)blocks), dim3(DecodeShape<D>::NTH), 0, s, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)g, beta, state, (T*)o, g_floor, gate);
-  return (int)hipGetLastError();
+  return (int)launch_kernel(kda_decode<T, D>, dim3((unsigned)blocks), dim3(DecodeShape<D>::NTH), s, (const T*)q,
+                            (const T*)k, (const T*)v, (const T*)g, beta, state, (T*)o, g_floor, gate);
 }
 
 int launch_decode_step(int is_bf16, int d, int N, int H, float g_floor, int gate, const void* q, const void* k,

@@ -20,6 +20,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace kda {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -123,5 +127,23 @@ template <> struct Frag<bf16_t> {
     return frag_rows_f32_to_bf16(X, ld, row, k0, g);
   }
 };
+
+// ---- launches ---------------------------------------------------------------
+// Enqueue `kernel` and return the status of this launch itself: the
+// arguments are converted to the kernel's parameter types and handed to
+// hipLaunchKernel, whose return value is the launch's own (unlike
+// hipGetLastError(), which also reports errors that earlier, unrelated HIP
+// calls left on the calling thread).
+template <typename K, typename Tup, size_t... I>
+hipError_t launch_tuple(K kernel, dim3 grid, dim3 block, hipStream_t stream, Tup& vals, std::index_sequence<I...>) {
+  void* ptrs[] = {(void*)&std::get<I>(vals)...};
+  return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+}
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "one argument per kernel parameter");
+  std::tuple<std::decay_t<KArgs>...> vals(std::forward<Args>(args)...);
+  return launch_tuple(kernel, grid, block, stream, vals, std::index_sequence_for<KArgs...>{});
+}
 
 }  // namespace kda

@@ -12,45 +12,26 @@ constexpr int kChunk = 64;  // tokens per chunk
 // Gate layouts (the values of kda_gate_t): g per key channel, per head, none.
 constexpr int kGateChannel = 0, kGateHead = 1, kGateNone = 2;
 
-// How a chunked forward is cut for the GPU.
-//  - The state passes cut every sequence into segments of `seg_chunks`
-//    chunks.  One record per (segment, head) holds three d x d fp32 matrices:
-//    the segment's affine state map S_out = M S_in + B (M and B) and its
-//    incoming state S_in.
-//  - The chunk pass writes one record per (chunk, head) with the chunk's
-//    operands for the output pass.  With `maps_in_prep` its workgroups are
-//    the (segment, head) pairs and also compose the segment maps; otherwise
-//    every sequence is a single segment (no maps) and the chunk pass takes
-//    groups of `prep_chunks` consecutive chunks of a sequence, one workgroup
-//    per (group, head).
-// Workspace: the segment records, then the chunk records.
+// How a chunked forward is cut for the GPU.  Every sequence is cut into
+// segments of `seg_chunks` chunks.  A chunk maps the state entering it
+// affinely, and so does a segment: S_out = M S_in + B.
+//  - With `maps`, a map sweep composes every segment's (M, B) from a zero
+//    state, a scan chains them into each segment's incoming state S_in, and
+//    the output sweep runs every segment from its S_in.  One record per
+//    (segment, head) holds three d x d fp32 matrices: B, M and S_in.
+//  - Without, every sequence is one segment: the output sweep alone, from h0.
+// Both sweeps recompute the chunk-local algebra from the inputs; nothing per
+// chunk goes through memory.
+// Workspace: the segment records (with maps), then for a packed batch the
+// per-sequence prefix sums of segments and of prefix-cache state slots.
 struct SegPlan {
-  int prep_chunks;       // chunks per chunk-pass workgroup
-  int seg_chunks;        // chunks per segment of the state passes
-  bool maps_in_prep;     // chunk-pass groups are the segments, and it writes their maps
-  int64_t n_prep_bound;  // upper bound of chunk-pass groups over all sequences
-  int64_t n_seg_bound;   // upper bound of segments over all sequences
-  int64_t n_slots;       // upper bound of chunks over all sequences
+  int seg_chunks;        // chunks per segment (the longest sequence's chunks without maps)
+  bool maps;             // map sweep + scan before the output sweep
+  int64_t n_seg_bound;   // upper bound of segments over all sequences (grid of both sweeps)
   size_t rec_bytes;      // bytes of one (segment, head) record
-  size_t crec_bytes;     // bytes of one (chunk, head) record
-  size_t crec_off;       // byte offset of the chunk records
-  size_t ws_bytes;       // crec_off + n_slots * H * crec_bytes
+  size_t seq_off;        // byte offset of the per-sequence prefix sums (packed batches)
+  size_t ws_bytes;       // whole workspace
 };
-
-// Bytes of one chunk record for key/value width d and operand size esz.  The
-// record starts with an image of the state passes' LDS: the MFMA A-operand
-// fragments (1 KiB each, k-blocks of KB = 32 for bf16 and 16 for fp32) of
-// Qt and Wk (4 row tiles x d / KB), Kh^T (d / 16 row tiles x 64 / KB) and P
-// (4 x 64 / KB), then gamma (d fp32), padded to a multiple of 1 KiB; then
-// Wv, 64 x d in the operand type.
-inline size_t chunk_image_bytes(int d, int esz) {
-  const size_t kb = esz == 2 ? 32 : 16;
-  const size_t frags = 8 * (d / kb) + (size_t)(d / 16) * (kChunk / kb) + 4 * (kChunk / kb);
-  return (frags * 1024 + (size_t)d * 4 + 1023) / 1024 * 1024;
-}
-inline size_t chunk_record_bytes(int d, int esz) {
-  return chunk_image_bytes(d, esz) + (size_t)kChunk * d * esz;
-}
 
 // Upper bound of groups of g chunks over the sequences: n_rows rows of T
 // tokens, or (packed) n_rows sequences sharing T tokens.
@@ -61,63 +42,54 @@ inline int64_t group_bound(int64_t T, int n_rows, bool packed, int64_t g) {
   return (int64_t)n_rows * ((chunks + g - 1) / g);
 }
 
-// Chooses the cut from a cost model of the launches (one workgroup per CU
-// in the chunk and output passes; times per chunk and per scan step measured
-// on the target).  Either every sequence is one segment (the chunk pass then
-// balances its groups over the CUs on its own, and the output pass walks each
-// sequence), or segments of L chunks: one workgroup per (segment, head) in
-// both passes, the chunk pass composing the maps, and a scan of
-// (segments - 1) steps between them.  Host-only, deterministic in its
-// arguments.  `packed`: n_rows sequences share T tokens (lengths unknown on
-// the host; the mean length is used), else n_rows rows of T tokens each.
-// esz: operand bytes (2 bf16, 4 fp32).  Returns false on overflow.
-inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool packed, SegPlan* p) {
-  const double t_prep = 9.0, t_map = 1.5, t_scan = 1.4, t_fwd = 4.7;  // us
-  const int64_t n_cu = 256;
+// Compute units of the current device (0 when no device answers): the cost
+// model below cuts sequences into segments for it.
+int device_compute_units();
+
+// Per-chunk times of the two sweeps and per-step time of the scan on one CU
+// (one workgroup per CU), measured on MI355X at d = 128; the model scales
+// them by (d / 128)^2 for d = 64.
+constexpr double kMapChunkUs = 3.0, kOutChunkUs = 3.0, kScanStepUs = 1.1;
+
+// Chooses the cut from a cost model of the launches.  Either every sequence
+// is one segment (the output sweep alone; one workgroup per (sequence, head)
+// walks the sequence), or segments of L chunks (map sweep, scan of
+// segments - 1 steps, output sweep; one workgroup per (segment, head) in
+// both sweeps).  Host-only, deterministic in its arguments.  `packed`:
+// n_rows sequences share T tokens (lengths unknown on the host; the mean
+// length is used), else n_rows rows of T tokens each.  n_cu: compute units
+// of the device.  Returns false on overflow.
+inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool packed, int n_cu, SegPlan* p) {
+  (void)esz;
+  const double sc = (double)d * d / (128.0 * 128.0);
+  const double t_map = kMapChunkUs * sc, t_out = kOutChunkUs * sc, t_scan = kScanStepUs * sc;
+  const int64_t cus = n_cu > 0 ? n_cu : 256;
   const int64_t chunks_total = (T + kChunk - 1) / kChunk;
   const int rows = n_rows > 0 ? n_rows : 1;
   int64_t per_seq = packed ? (chunks_total + rows - 1) / rows : chunks_total;
   if (per_seq < 1) per_seq = 1;
   const int64_t pairs = (int64_t)n_rows * H;
-  auto rounds = [&](int64_t wg) { return (double)((wg + n_cu - 1) / n_cu); };
-  // one segment per sequence
-  const int64_t share = (pairs * per_seq + n_cu - 1) / n_cu;  // chunks per CU
-  double best = (double)share * t_prep + rounds(pairs) * (double)per_seq * t_fwd;
-  int best_l = 0;  // 0: one segment per sequence
+  auto rounds = [&](int64_t wg) { return (double)((wg + cus - 1) / cus); };
+  double best = rounds(pairs) * (double)per_seq * t_out;  // one segment per sequence
+  int best_l = 0;
   for (int64_t L = 1; L < per_seq; L *= 2) {
     const int64_t segs = (per_seq + L - 1) / L;
-    const double t = rounds(pairs * segs) * (double)L * (t_prep + t_map + t_fwd) + (double)(segs - 1) * t_scan;
+    const double t = rounds(pairs * segs) * (double)L * (t_map + t_out) + (double)(segs - 1) * t_scan;
     if (t < best) {
       best = t;
       best_l = (int)L;
     }
   }
-  p->maps_in_prep = best_l > 0;
-  if (p->maps_in_prep) {
-    p->seg_chunks = best_l;
-    p->prep_chunks = best_l;
-  } else {
-    // Whole sequences: a packed batch needs the longest sequence to fit, so
-    // the segment is the bound of all chunks.  Chunk-pass groups: long enough
-    // that the prefetch of the next chunk pays (at least 4 chunks where there
-    // is work for it), short enough that the last round of workgroups stays
-    // short: at most a quarter of one CU's share of all chunks, 64 at most.
-    p->seg_chunks = (int)(packed ? (chunks_total > 0 ? chunks_total : 1) : per_seq);
-    int64_t cap = share / 4 > 4 ? share / 4 : 4;
-    if (cap > per_seq) cap = per_seq;
-    int64_t pg = 1;
-    while (pg < 64 && 2 * pg <= cap) pg *= 2;
-    p->prep_chunks = (int)pg;
-  }
+  p->maps = best_l > 0;
+  // without maps a packed batch needs its longest sequence to fit one segment
+  p->seg_chunks = p->maps ? best_l : (int)(packed ? (chunks_total > 0 ? chunks_total : 1) : per_seq);
   p->n_seg_bound = group_bound(T, n_rows, packed, p->seg_chunks);
-  p->n_prep_bound = p->maps_in_prep ? p->n_seg_bound : group_bound(T, n_rows, packed, p->prep_chunks);
-  p->n_slots = T == 0 ? 0 : (packed ? chunks_total + n_rows : (int64_t)n_rows * chunks_total);
   p->rec_bytes = (size_t)3 * d * d * sizeof(float);
-  p->crec_bytes = chunk_record_bytes(d, esz);
   const int64_t hh = H > 0 ? H : 1;
-  if (p->n_seg_bound > ((int64_t)1 << 36) / hh || p->n_slots > ((int64_t)1 << 36) / hh) return false;
-  p->crec_off = (size_t)p->n_seg_bound * (size_t)H * p->rec_bytes;
-  p->ws_bytes = p->crec_off + (size_t)p->n_slots * (size_t)H * p->crec_bytes;
+  if (p->n_seg_bound > ((int64_t)1 << 36) / hh || chunks_total > ((int64_t)1 << 36) / hh) return false;
+  const size_t recs = p->maps ? (size_t)p->n_seg_bound * (size_t)H * p->rec_bytes : 0;
+  p->seq_off = (recs + 255) / 256 * 256;
+  p->ws_bytes = packed ? p->seq_off + (size_t)2 * ((size_t)n_rows + 1) * sizeof(int64_t) : recs;
   return true;
 }
 
@@ -137,7 +109,7 @@ struct ChunkInputs {
 };
 
 // Launches of one chunked forward, in stream order.
-constexpr int kLaunches = 3;  // chunk pass (with the segment maps), segment scan, output pass
+constexpr int kLaunches = 3;  // map sweep, segment scan, output sweep
 
 // Enqueue the chunked forward.  All arguments were validated by the caller.
 // n_rows: number of sequences (n_seqs, or B when cu == nullptr).  gate: a
@@ -175,12 +147,13 @@ struct BwdPlan {
 
 // n_states: sequences; chunk_states: full chunks over all sequences (an
 // upper bound for a packed batch).  Returns false on overflow.
-inline bool plan_backward(int d, int esz, int n_rows, int64_t T, int H, bool packed, size_t tokens,
+inline bool plan_backward(int d, int esz, int n_rows, int64_t T, int H, bool packed, int n_cu, size_t tokens,
                           size_t chunk_states, BwdPlan* p) {
-  if (!plan_segments(d, esz, n_rows, T, H, packed, &p->fwd)) return false;
+  if (!plan_segments(d, esz, n_rows, T, H, packed, n_cu, &p->fwd)) return false;
   const size_t a = 256, hh = (size_t)H, dd = (size_t)d * d * sizeof(float);
   auto up = [&](size_t x) { return (x + a - 1) / a * a; };
-  p->n_slots = p->fwd.n_slots;
+  const int64_t chunks_total = (T + kChunk - 1) / kChunk;
+  p->n_slots = T == 0 ? 0 : (packed ? chunks_total + n_rows : (int64_t)n_rows * chunks_total);
   p->rec_floats = bwd_rec_floats(d);
   p->scr_floats = bwd_scr_floats(d);
   const double total = (double)p->fwd.ws_bytes + (double)tokens * hh * d * esz +

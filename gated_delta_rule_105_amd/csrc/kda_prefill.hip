@@ -1,11 +1,12 @@
-// Chunked KDA forward for gfx950: two chunk passes around a segment scan.
+// Chunked KDA forward for gfx950: two sweeps over the inputs around a
+// segment scan.
 //
 // Chunk algebra (per sequence and head; chunk rows r = 0..63, S the state
 // entering the chunk, g floored, G = running sum of g over the chunk's rows,
 // G_L its last row, gamma = e^{G_L} per key channel):
 //   Qt = Q e^{G},  Kt = K e^{G},  Kh = K e^{-G}
-//   A  = diag(beta) strict_lower(Kt Kh^T),   T = (I + A)^{-1}
-//   Wk = T diag(beta) Kt,   Wv = T diag(beta) V,   P = lower_incl(Qt Kh^T)
+//   A  = diag(beta) strict_lower(Kt Kh^T),   (I + A) W = diag(beta) [Kt | V]
+//   Wk, Wv = the two halves of W,   P = lower_incl(Qt Kh^T)
 //   U  = Wv - Wk S,   O = Qt S + P U,   S <- diag(gamma) (S + Kh^T U)
 // which is the recurrence S_t = (I - b k k^T) diag(a) S_{t-1} + b k v^T,
 // o_t = S_t^T q_t unrolled over one chunk (K e^{G_L - G} = diag(gamma) Kh
@@ -17,133 +18,233 @@
 // Figure 3, and "Kimi K3 发布 47 页技术报告" (163.com), 01.
 //
 // One chunk maps the state affinely, S -> M_j S + B_j.  Every sequence is cut
-// into segments of L chunks; the composition of a segment's maps is again
-// affine, S_out = M S_in + B.  Three launches:
-//   1. kda_chunk_prep (one workgroup per (segment, head), all in parallel):
-//      the chunk-local part of each chunk (decay prefix sums, Gram blocks,
-//      the inverse (I + A)^{-1}, Wk and Wv) from the inputs, written to a
-//      per-chunk record: Qt, Wk, Kh^T, P and gamma as an image of the output
-//      pass's LDS, and Wv.  The same workgroup runs each chunk, while its
-//      operands are still in LDS, on the state started from 0 (giving B) and
-//      from I with the value part of U switched off (giving M), and writes the
-//      segment's map; the last segment of a sequence has none (no later
-//      segment needs it).  When every sequence is one segment there are no
-//      maps, and the chunks are grouped by a length of the pass's own.
+// into segments of L chunks; a segment's composition is again affine,
+// S_out = M S_in + B.  Up to three launches:
+//   1. map sweep (kda_chunk_sweep<MAP>, one workgroup per (segment, head)):
+//      the chunk-local algebra of each chunk from the inputs, then one state
+//      step on B (from 0) and on M (from I, value part of U off); writes the
+//      segment's (M, B).  The last segment of a sequence has none.
 //   2. kda_seg_scan (one workgroup per (sequence, head, 16 state columns)):
-//      S_0 = h0, S_{s+1} = M_s S_s + B_s, writing every segment's incoming
-//      state.  M S is done as three bf16 products of a hi/lo split of both
-//      factors (about fp32 accuracy).
-//   3. kda_seg_forward (one workgroup per (segment, head), all in parallel):
-//      the state recurrence from the segment's incoming state over its chunk
-//      records, writing o and, for the last segment, the final state.  It
-//      keeps two record images in LDS (about 57 KiB each at d = 128): the
-//      next chunk's image lands by direct global-to-LDS loads while the
-//      current one is used.
-// Within a workgroup, wave w owns 16 value columns of the state: columns of
-// U, O and S never mix, so the state products need no exchange.
+//      S_0 = h0, S_{s+1} = M_s S_s + B_s, writing every segment's S_in.
+//      M S is three bf16 products of a hi/lo split of both factors.
+//   3. output sweep (kda_chunk_sweep<OUT>, one workgroup per (segment,
+//      head)): the chunk-local algebra again, and the state step with the
+//      outputs from S_in; writes o, the final state and prefix-cache states.
+// With one segment per sequence only the output sweep runs, from h0.
+//
+// Within a chunk (one workgroup of D / 16 waves): the inputs arrive in
+// registers (fetched during the previous chunk); the element-wise stage
+// writes Qt, Kt, Kh and V token-major to LDS.  Operands whose contraction
+// runs over tokens (Kt, V, Kh^T, Wk) are read from token- or channel-major
+// arrays with the gfx950 transpose read, so no array is stored twice.  The
+// triangular system is solved by 16-row blocks: the diagonal blocks'
+// inverses by substitution, the rest by MFMA block products.  Wave w owns
+// 16 value columns: columns of W, U, O and S never mix.
 #include <type_traits>
 
 #include "kda_device.h"
 #include "kda_launch.h"
-
-#ifndef KDA_NW128
-#define KDA_NW128 8
-#endif
-#ifndef KDA_NW128_FWD
-#define KDA_NW128_FWD 4
-#endif
 
 namespace kda {
 namespace {
 
 constexpr int C = kChunk;
 
-// Streaming accesses: the chunk inputs are read once and o is written once,
-// and the chunk records are read back once per state pass; non-temporal
-// hints keep them from displacing cached data.  (The record stores stay
-// ordinary: a short workload's records are read back from cache.)
 typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2nt __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 stream_load16(const void* p) {
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4nt*)p));
-}
-__device__ __forceinline__ void stream_store16(void* p, const uint4& x) {
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4nt, x), (u32x4nt*)p);
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// ---- LDS layout of the chunk engine -------------------------------------
-template <typename T, int D> struct Lds {
-  static constexpr int PADT = 16 / (int)sizeof(T);
-  static constexpr int LDT = D + PADT;  // token-major arrays [64][LDT]
-  static constexpr int LDC = C + PADT;  // channel-major arrays [D][LDC]; P [64][LDC]
-  static constexpr int LDF = C + 4;     // fp32 [64][LDF]
-  static constexpr int ROW_T = C * LDT * (int)sizeof(T);
-  static constexpr int ROW_F = C * LDF * 4;
-  static constexpr int ROW = ((ROW_T > ROW_F ? ROW_T : ROW_F) + 15) / 16 * 16;
-  static constexpr int COL = (D * LDC * (int)sizeof(T) + 15) / 16 * 16;
-  static constexpr int PSZ = (C * LDC * (int)sizeof(T) + 15) / 16 * 16;
-  static constexpr int Q = 0;              // q, then Qt
-  static constexpr int K = ROW;            // k, then Kt, then Wk
-  static constexpr int G = 2 * ROW;        // g, then Kh, then T (fp32)
-  static constexpr int V = 3 * ROW;        // v, then A (fp32)
-  static constexpr int KT = 4 * ROW;       // Kt^T
-  static constexpr int KH = KT + COL;      // Kh^T
-  static constexpr int VT = KH + COL;      // V^T
-  static constexpr int P = VT + COL;       // P
-  static constexpr int BETA = P + PSZ;     // fp32 [64]
-  static constexpr int PART = BETA + C * 4;  // fp32 [8][D] partial sums of g
-  static constexpr int GL = PART + 8 * D * 4;  // fp32 [D] gamma
-  static constexpr int TII = GL + D * 4;       // fp32 [4][16][16] diagonal-block inverses
-  static constexpr int BYTES = TII + 4 * 16 * 16 * 4;
+// ---- LDS arrays -------------------------------------------------------------
+// A [rows][W] array is stored with rows of W + 16 elements and in units of 4
+// elements; unit u of row t sits at unit u ^ ((t >> 2) & 3).  The padding
+// puts consecutive rows 8 banks apart; the swizzle touches only the two low
+// bits of the unit, which hold the lane-dependent part of every access, so
+// each lane's addresses into an array differ by immediates only.  Both
+// access patterns used here hit distinct banks within 16 lanes: 16 rows at
+// one unit (row fragments) and 4 rows x 4 units (transpose reads).
+template <int W>
+__device__ __forceinline__ int sidx(int t, int c) {
+  return t * (W + 16) + ((((c >> 2) ^ ((t >> 2) & 3))) << 2) + (c & 3);
+}
+// Workgroup barrier that orders LDS accesses only: it waits for this wave's
+// LDS operations, not for its global loads, so that the next chunk's inputs
+// stay in flight across it (__syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, int W> struct Arr {
+  static constexpr int BYTES = C * (W + 16) * (int)sizeof(T);  // 64 rows
 };
 
-// ---- sequences and segments ---------------------------------------------
-__device__ __forceinline__ int n_segments(int len, int L) { return ((len + C - 1) / C + L - 1) / L; }
+// Row fragment (A- or B-operand whose k runs along a row): row r, elements
+// k0 + 4g .. k0 + 4g + 3 and, for bf16 (k-blocks of 32), k0 + 16 + 4g ...
+template <int W>
+__device__ __forceinline__ bf16x8 rowfrag(const bf16_t* X, int r, int k0, int g) {
+  const bf16x4 lo = *(const bf16x4*)(X + sidx<W>(r, k0 + 4 * g));
+  const bf16x4 hi = *(const bf16x4*)(X + sidx<W>(r, k0 + 16 + 4 * g));
+  return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <int W>
+__device__ __forceinline__ f32x4 rowfrag(const float* X, int r, int k0, int g) {
+  return *(const f32x4*)(X + sidx<W>(r, k0 + 4 * g));
+}
+// Column piece: lane (g, i) gets X[r0 + 4g + e][c0 + i], e = 0..3 (the
+// accumulator layout of a 16 x 16 tile, and an operand fragment whose k runs
+// down a column).  bf16: one transpose read, lane (g, L) addressing row
+// r0 + 4g + L / 4, elements c0 + 4 (L % 4) ..; fp32: four scalar reads.
+template <int W>
+__device__ __forceinline__ s16x4 colpiece(const bf16_t* X, int r0, int c0, int lane) {
+  const int g = lane >> 4, L = lane & 15;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + sidx<W>(r0 + 4 * g + (L >> 2), c0 + 4 * (L & 3))));
+}
+template <int W>
+__device__ __forceinline__ f32x4 colpiece(const float* X, int r0, int c0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  f32x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = X[sidx<W>(r0 + 4 * g + e, c0 + i)];
+  return x;
+}
+__device__ __forceinline__ f32x4 widen4(const s16x4& h) {
+  const uint2 w = __builtin_bit_cast(uint2, h);
+  return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 widen4(const f32x4& x) { return x; }
+// Column fragment over a k-block (bf16: 32 rows as two pieces; fp32: 16)
+template <int W>
+__device__ __forceinline__ bf16x8 colfrag(const bf16_t* X, int r0, int c0, int lane) {
+  const s16x4 a = colpiece<W>(X, r0, c0, lane), b = colpiece<W>(X, r0 + 16, c0, lane);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <int W>
+__device__ __forceinline__ f32x4 colfrag(const float* X, int r0, int c0, int lane) {
+  return colpiece<W>(X, r0, c0, lane);
+}
 
+// ---- LDS layout of a sweep workgroup --------------------------------------
+// Token-major [64][D]: Qt (output sweep only) and Kh in two buffer sets (a
+// chunk's state step reads them while the next chunk's element-wise stage
+// writes the other set), Kt, V.  Channel-major [D][64]: Wk^T.  Fragment images, 64 lanes x 4 elements in lane order: P
+// tiles (rt, sb), sb <= rt (output sweep); the off-diagonal blocks of -A as
+// operand fragments (i, m), m < i; the diagonal blocks' inverses T_bb (bf16:
+// a hi and a lo image).  fp32: partial sums of g [8][D], beta [64], gamma [D]
+// in two buffer sets.
+// After the last chunk the map sweep stages M [D][D + 4] fp32 from offset 0.
+template <typename T, int D, bool OUT> struct Lay {
+  static constexpr int ES = (int)sizeof(T);
+  // two buffer sets (state step overlapped with the next element-wise stage)
+  // on the bf16 path; the fp32 path, whose arrays are twice as large, runs
+  // the state step in an interval of its own with one set
+  static constexpr bool OVL = ES == 2;
+  static constexpr int NBUF = OVL ? 2 : 1;
+  static constexpr int ARR = Arr<T, D>::BYTES;       // token-major [64][D]
+  static constexpr int ARRT = D * (C + 16) * ES;     // channel-major [D][64]
+  static constexpr int IMG = 64 * 4 * ES;            // one fragment image
+  static constexpr int NTI = ES == 2 ? 2 : 1;
+  static constexpr int QT0 = 0;                      // Qt, two buffer sets (output sweep)
+  static constexpr int KH0 = QT0 + (OUT ? NBUF * ARR : 0);  // Kh, two buffer sets
+  static constexpr int KT = KH0 + NBUF * ARR;
+  static constexpr int VV = KT + ARR;
+  static constexpr int WKT = VV + ARR;
+  static constexpr int PIMG = WKT + ARRT;
+  static constexpr int AIMG = PIMG + (OUT ? 10 * IMG : 0);
+  static constexpr int TIMG = AIMG + 6 * IMG;
+  static constexpr int PART = TIMG + 4 * NTI * IMG;
+  static constexpr int BETA = PART + 8 * D * 4;
+  static constexpr int GAM0 = BETA + C * 4;          // gamma, two buffer sets
+  static constexpr int STAGE_M = D * (D + 4) * 4;
+  static constexpr int END = GAM0 + NBUF * D * 4;
+  static constexpr int BYTES = OUT || END >= STAGE_M ? END : STAGE_M;
+  __device__ static __forceinline__ int qt(int buf) { return QT0 + (OVL ? buf : 0) * ARR; }
+  __device__ static __forceinline__ int kh(int buf) { return KH0 + (OVL ? buf : 0) * ARR; }
+  __device__ static __forceinline__ int gam(int buf) { return GAM0 + (OVL ? buf : 0) * D * 4; }
+  __device__ static __forceinline__ int pimg(int rt, int sb) { return PIMG + (rt * (rt + 1) / 2 + sb) * IMG; }
+  __device__ static __forceinline__ int aimg(int i, int m) { return AIMG + (i * (i - 1) / 2 + m) * IMG; }
+  __device__ static __forceinline__ int timg(int b, int part) { return TIMG + (b * NTI + part) * IMG; }
+};
+
+// ---- sequences and segments -----------------------------------------------
 struct Seg {
-  int64_t tok0;    // first packed token of the sequence
-  int64_t chunk0;  // chunks of all earlier sequences (first chunk-record slot)
-  int len;         // tokens of the sequence
-  int n;           // sequence
-  int s;           // segment within the sequence
-  int nseg;        // segments of the sequence
+  int64_t tok0;   // first packed token of the sequence
+  int64_t slot0;  // first prefix-cache state slot of the sequence
+  int len;        // tokens of the sequence
+  int n;          // sequence
+  int s;          // segment within the sequence
+  int nseg;       // segments of the sequence
 };
+__device__ __forceinline__ int n_segments(int64_t len, int L) { return (int)(((len + C - 1) / C + L - 1) / L); }
 
-// Global segment gs -> its sequence.  false when gs is past the last one.
-__device__ __forceinline__ bool locate(const int32_t* cu, int n_rows, int T, int L, int64_t gs, Seg& r) {
+// Packed batches: seqs[n] = segments of sequences 0 .. n - 1, seqs[n_rows +
+// 1 + n] = prefix-cache state slots of sequences 0 .. n - 1 (kda_fwd_seqs).
+// Global segment gs -> its sequence (binary search); false past the last.
+__device__ __forceinline__ bool locate(const int32_t* cu, const int64_t* seqs, int n_rows, int T_per, int L,
+                                       int64_t period, int64_t gs, Seg& r) {
   if (!cu) {
-    const int per = n_segments(T, L);
+    const int per = n_segments(T_per, L);
     if (per == 0) return false;
     const int64_t n = gs / per;
     if (n >= n_rows) return false;
     r.n = (int)n;
     r.s = (int)(gs % per);
     r.nseg = per;
-    r.tok0 = n * (int64_t)T;
-    r.chunk0 = n * (int64_t)((T + C - 1) / C);
-    r.len = T;
+    r.tok0 = n * (int64_t)T_per;
+    r.len = T_per;
+    r.slot0 = period > 0 ? n * (T_per / period) : 0;
     return true;
   }
-  int64_t base = 0, chunks = 0;
-  for (int n = 0; n < n_rows; ++n) {
-    const int len = cu[n + 1] - cu[n];
-    const int ns = n_segments(len, L);
-    if (gs < base + ns) {
-      r.n = n;
-      r.s = (int)(gs - base);
-      r.nseg = ns;
-      r.tok0 = cu[n];
-      r.chunk0 = chunks;
-      r.len = len;
-      return true;
-    }
-    base += ns;
-    chunks += (len + C - 1) / C;
+  if (n_rows == 0 || gs >= seqs[n_rows]) return false;
+  int lo = 0, hi = n_rows - 1;  // the largest n with seqs[n] <= gs: not an empty sequence
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (seqs[mid] <= gs) lo = mid;
+    else hi = mid - 1;
   }
-  return false;
+  r.n = lo;
+  r.s = (int)(gs - seqs[lo]);
+  r.tok0 = cu[lo];
+  r.len = cu[lo + 1] - cu[lo];
+  r.nseg = n_segments(r.len, L);
+  r.slot0 = seqs[n_rows + 1 + lo];
+  return true;
 }
 
-// ---- workspace record of one (segment, head): three d x d blocks of fp32 size
+// The prefix sums above for n_rows packed sequences: one workgroup, each
+// thread summing a contiguous range of sequences, then the ranges' offsets.
+// period = tokens per prefix-cache state (0: none).
+__global__ void __launch_bounds__(256) kda_fwd_seqs(const int32_t* __restrict__ cu, int n_rows, int L,
+                                                    int64_t period, int64_t* __restrict__ seqs) {
+  __shared__ int64_t part[2][256];
+  const int tid = threadIdx.x, per = (n_rows + 255) / 256;
+  const int n0 = min(n_rows, tid * per), n1 = min(n_rows, n0 + per);
+  int64_t a = 0, f = 0;
+  for (int n = n0; n < n1; ++n) {
+    const int64_t len = (int64_t)cu[n + 1] - cu[n];
+    a += n_segments(len, L);
+    f += period > 0 ? len / period : 0;
+  }
+  part[0][tid] = a;
+  part[1][tid] = f;
+  __syncthreads();
+  int64_t oa = 0, of = 0;
+  for (int t = 0; t < tid; ++t) {
+    oa += part[0][t];
+    of += part[1][t];
+  }
+  for (int n = n0; n < n1; ++n) {
+    seqs[n] = oa;
+    seqs[n_rows + 1 + n] = of;
+    const int64_t len = (int64_t)cu[n + 1] - cu[n];
+    oa += n_segments(len, L);
+    of += period > 0 ? len / period : 0;
+  }
+  if (tid == 255) {
+    seqs[n_rows] = oa;
+    seqs[2 * n_rows + 1] = of;
+  }
+}
+
+// ---- segment record: three d x d blocks of fp32 size per (segment, head)
 //   B    : [d/16 row tiles][d/16 column tiles][64 lanes][4] fp32, accumulator
 //          tile order (lane 16 g + i holds rows 4 g .. 4 g + 3 of column i)
 //   M    : A-operand fragments of M for the scan, [d/16 row tiles][k-blocks]
@@ -153,895 +254,636 @@ __device__ __forceinline__ bool locate(const int32_t* cu, int n_rows, int T, int
 template <typename T, int D> struct Rec {
   static constexpr int NRT = D / 16, KB = Elem<T>::KB, NKB = D / KB;
   static constexpr size_t B = 0, M = (size_t)D * D, SIN = 2 * (size_t)D * D, FLOATS = 3 * (size_t)D * D;
-  // float offset of accumulator tile (rr, ct) in a tile-ordered block
   __device__ static __forceinline__ size_t tile(int rr, int ct, int lane) {
     return (((size_t)rr * NRT + ct) * 64 + lane) * 4;
   }
-  // byte offset of the (rr, kb) fragment (part 0 = hi, 1 = lo for bf16)
   __device__ static __forceinline__ size_t frag(int rr, int kb, int part, int lane) {
     return ((((size_t)rr * NKB + kb) * (sizeof(T) == 2 ? 2 : 1) + part) * 64 + lane) * 16;
   }
 };
 
-// one element replicated over a 16-byte piece
-__device__ __forceinline__ uint4 splat16(bf16_t x) {
-  const uint32_t u = (uint32_t)x | ((uint32_t)x << 16);
-  return (uint4){u, u, u, u};
+// ---- chunk inputs: global -> registers (fetched one chunk ahead) -----------
+// Thread (channel pair cp = tid % (D / 2), part = tid / (D / 2)) holds rows
+// 8 part .. 8 part + 7 of channels 2 cp, 2 cp + 1: one 32-bit word of a bf16
+// pair (fp32: two floats) per row and tensor, so that one wave's load covers
+// whole rows and the prefix sums over a part's rows stay in one thread.
+// Each tensor of a chunk is one buffer resource whose range ends with the
+// chunk's last row: rows past the chunk's end (a sequence's last chunk) read
+// as zeros, with no branch, and every lane's offsets are 32-bit.  gate: g
+// per channel, one per (token, head) (replicated over the channels when
+// used), or none.  MX: q, k and v arrive as e4m3 bytes (two per pair) with
+// their 32-channel block's scale byte, decoded to bf16 when used.  The output
+// sweep's loads are non-temporal (last use); the map sweep's are not (the
+// output sweep reads the same inputs again).
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
-__device__ __forceinline__ uint4 splat16(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (uint4){u, u, u, u};
-}
-
-// ---- raw chunk inputs: global -> registers (prefetch) -> LDS -------------
-// 8 e4m3 bytes (OCP, finite-only) times their block's scale 2^(s - 127),
-// as 8 bf16 (exact: e4m3 has 3 significand bits, bf16 8; the gfx950
-// conversion takes the scale as an fp32 multiplier)
-__device__ __forceinline__ uint4 mx_decode8(const uint2& w, uint32_t s) {
-  const float sc = __uint_as_float(s ? s << 23 : 0x00400000u);
-  return (uint4){__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, sc, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, sc, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, sc, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, sc, true))};
-}
-
-// With MX, q, k and v arrive as e4m3 bytes with a scale byte per 32
-// channels: each thread loads 16 bytes (16 channels of one token, inside one
-// scale block) and their scale per tensor, decoded to two 16-byte vectors
-// of bf16 when they are stored to LDS; everything after that is the bf16
-// path.
-template <typename T, int D, int NT, bool WITH_Q, bool MX = false> struct Raw {
-  typedef Lds<T, D> M;
-  static constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  static constexpr int VPR = D / EPV;              // vectors per token row
-  static constexpr int PER = C * VPR / NT;         // vectors per thread per tensor
-  static_assert(PER * NT == C * VPR, "thread count must divide the chunk");
-  static_assert(!MX || (sizeof(T) == 2 && D % 32 == 0), "MXFP8 inputs feed the bf16 path");
-  static constexpr int NB = MX ? 1 : PER;
-  static constexpr int TPR = D / 16;  // MX: threads per token row (16 channels each)
-  static_assert(!MX || C * TPR == NT, "MX: one 16-byte load per thread and tensor");
-  uint4 q[WITH_Q ? NB : 1], k[NB], v[NB], g[PER];  // MX: q[0], k[0], v[0] hold e4m3 bytes
-  uint32_t qs, ks, vs;                              // MX: their scale bytes
-  float beta;
-
-  // Rows past the chunk's end (a sequence's last chunk) are loaded as zeros
-  // (beta and g of such rows must be 0; their q, k and v then reach no
-  // output).  The buffer is scoped to one chunk iteration.  load = load_qkg
-  // (q, k, g and beta) + load_v, which may be issued at different times.
-  // gate: g per channel (16-byte pieces like q), one per (token, head)
-  // replicated over the channels, or none (zeros: no decay).
-  __device__ __forceinline__ void load_qkg(const ChunkInputs& in, int64_t tok0, int len, int H, int h, int tid,
-                                           int gate) {
-    const T* G = (const T*)in.g;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
-      const uint4 z = {0u, 0u, 0u, 0u};
-      if (t < len) {
-        const size_t off = ((size_t)(tok0 + t) * H + h) * D + cv * EPV;  // element index
-        if (!MX) {
-          if (WITH_Q) q[j] = stream_load16((const T*)in.q + off);
-          k[j] = stream_load16((const T*)in.k + off);
-        }
-        g[j] = gate == kGateChannel ? stream_load16(G + off)
-               : gate == kGateHead  ? splat16(G[(size_t)(tok0 + t) * H + h])
-                                    : z;
-      } else {
-        if (!MX) {
-          if (WITH_Q) q[j] = z;
-          k[j] = z;
-        }
-        g[j] = z;
-      }
-    }
-    if (MX) {
-      const int t = tid / TPR;
-      const size_t off = ((size_t)(tok0 + t) * H + h) * D + (tid % TPR) * 16;  // element (= byte) index
-      const bool in_seq = t < len;
-      if (WITH_Q) {
-        q[0] = in_seq ? stream_load16((const uint8_t*)in.q + off) : (uint4){0u, 0u, 0u, 0u};
-        qs = in_seq ? in.qs[off / 32] : 127u;
-      }
-      k[0] = in_seq ? stream_load16((const uint8_t*)in.k + off) : (uint4){0u, 0u, 0u, 0u};
-      ks = in_seq ? in.ks[off / 32] : 127u;
-    }
-    beta = (tid < len) ? in.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
-  }
-  __device__ __forceinline__ void load_v(const ChunkInputs& in, int64_t tok0, int len, int H, int h, int tid) {
-    if (MX) {
-      const int t = tid / TPR;
-      const size_t off = ((size_t)(tok0 + t) * H + h) * D + (tid % TPR) * 16;
-      v[0] = t < len ? stream_load16((const uint8_t*)in.v + off) : (uint4){0u, 0u, 0u, 0u};
-      vs = t < len ? in.vs[off / 32] : 127u;
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
-      v[j] = t < len ? stream_load16((const T*)in.v + ((size_t)(tok0 + t) * H + h) * D + cv * EPV)
-                     : (uint4){0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void load(const ChunkInputs& in, int64_t tok0, int len, int H, int h, int tid,
-                                       int gate) {
-    load_qkg(in, tok0, len, H, h, tid, gate);
-    load_v(in, tok0, len, H, h, tid);
-  }
-  // MX: 16 e4m3 bytes and their scale -> channels (tid % TPR) * 16 .. + 15 of
-  // token tid / TPR, two bf16 vectors in the token-major array at `area`
-  __device__ __forceinline__ static void store_mx(unsigned char* smem, int area, int tid, const uint4& b,
-                                                  uint32_t s) {
-    unsigned char* p = smem + area + (tid / TPR) * M::LDT * 2 + (tid % TPR) * 32;
-    *(uint4*)p = mx_decode8((uint2){b.x, b.y}, s);
-    *(uint4*)(p + 16) = mx_decode8((uint2){b.z, b.w}, s);
-  }
-
-  // into LDS: everything but v (store_qkg), v (store_v), or both (store)
-  __device__ __forceinline__ void store_qkg(unsigned char* smem, int tid) const {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
-      const int off = t * M::LDT * (int)sizeof(T) + cv * 16;
-      if (!MX) {
-        if (WITH_Q) *(uint4*)(smem + M::Q + off) = q[j];
-        *(uint4*)(smem + M::K + off) = k[j];
-      }
-      *(uint4*)(smem + M::G + off) = g[j];
-    }
-    if (MX) {
-      if (WITH_Q) store_mx(smem, M::Q, tid, q[0], qs);
-      store_mx(smem, M::K, tid, k[0], ks);
-    }
-    if (tid < C) ((float*)(smem + M::BETA))[tid] = beta;
-  }
-  __device__ __forceinline__ void store_v(unsigned char* smem, int tid) const {
-    if (MX) {
-      store_mx(smem, M::V, tid, v[0], vs);
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
-      *(uint4*)(smem + M::V + t * M::LDT * (int)sizeof(T) + cv * 16) = v[j];
-    }
-  }
-  __device__ __forceinline__ void store(unsigned char* smem, int tid) const {
-    store_qkg(smem, tid);
-    store_v(smem, tid);
-  }
-
-  // Chunk output [64][LDT] staged in LDS -> o rows tok0 .. tok0 + clen - 1.
-  __device__ __forceinline__ static void store_out(const unsigned char* stage, T* o, int64_t tok0, int clen, int H,
-                                                   int h, int tid) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int vi = tid + j * NT, t = vi / VPR, cv = vi % VPR;
-      if (t < clen)
-        stream_store16(o + ((size_t)(tok0 + t) * H + h) * D + cv * EPV,
-                       *(const uint4*)(stage + t * M::LDT * (int)sizeof(T) + cv * 16));
-    }
-  }
-};
-
-template <typename T>
-__device__ __forceinline__ float to_f32(T x) { return Elem<T>::to_f32(x); }
-
-// ---- element-wise stage: prefix sums of the floored log-decay and the
-// decay-scaled operands.  Thread (channel pair c, c + 1; part p) owns TPP
-// consecutive rows of its two channels; the parts exchange their sums through
-// LDS.  Rows are processed in blocks of 8 whose LDS reads are issued together.
-template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-  typedef uint32_t word;  // two bf16 channels
+template <typename T> struct PairT;
+template <> struct PairT<bf16_t> {
+  typedef uint32_t word;
   __device__ static __forceinline__ float lo(word w) { return __uint_as_float(w << 16); }
   __device__ static __forceinline__ float hi(word w) { return __uint_as_float(w & 0xffff0000u); }
   __device__ static __forceinline__ word pack(float a, float b) {
     return __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(a, b));
   }
+  __device__ static __forceinline__ word splat(word x) { return (x & 0xffffu) | (x << 16); }
+  __device__ static __forceinline__ word zero() { return 0u; }
+  template <int AUX>
+  __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+  }
+  template <int AUX>
+  __device__ static __forceinline__ word load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+  }
 };
-template <> struct Pair<float> {
+template <> struct PairT<float> {
   typedef f32x2 word;
   __device__ static __forceinline__ float lo(word w) { return w[0]; }
   __device__ static __forceinline__ float hi(word w) { return w[1]; }
   __device__ static __forceinline__ word pack(float a, float b) { return (f32x2){a, b}; }
+  __device__ static __forceinline__ word splat(word x) { return (f32x2){x[0], x[0]}; }
+  __device__ static __forceinline__ word zero() { return (f32x2){0.f, 0.f}; }
+  template <int AUX>
+  __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+  }
+  template <int AUX>
+  __device__ static __forceinline__ word load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (f32x2){__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX)), 0.f};
+  }
 };
 
-// Channel-major store of 8 consecutive rows of a channel pair, given the 8
-// token-major pair words: channel c gets the low halves, c + 1 the high ones.
-__device__ __forceinline__ void store_cols8(bf16_t* dst, int ldc, const uint32_t (&w)[8]) {
-  uint32_t a[4], b[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    a[u] = (w[2 * u] & 0xffffu) | (w[2 * u + 1] << 16);
-    b[u] = (w[2 * u] >> 16) | (w[2 * u + 1] & 0xffff0000u);
-  }
-  *(uint4*)dst = (uint4){a[0], a[1], a[2], a[3]};
-  *(uint4*)(dst + ldc) = (uint4){b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ void store_cols8(float* dst, int ldc, const f32x2 (&w)[8]) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    *(f32x4*)(dst + 4 * u) = (f32x4){w[4 * u][0], w[4 * u + 1][0], w[4 * u + 2][0], w[4 * u + 3][0]};
-    *(f32x4*)(dst + ldc + 4 * u) = (f32x4){w[4 * u][1], w[4 * u + 1][1], w[4 * u + 2][1], w[4 * u + 3][1]};
-  }
-}
-
-template <typename T, int D, int NW, bool WITH_Q>
-__device__ __forceinline__ void elementwise(unsigned char* smem, float g_floor, int tid) {
-  typedef Lds<T, D> M;
-  typedef Pair<T> PW;
+template <typename T, int D, bool WITH_Q, bool MX, bool NT> struct Raw {
+  typedef PairT<T> PW;
   typedef typename PW::word word;
-  constexpr int LDT = M::LDT, LDC = M::LDC;
-  constexpr int NT = 64 * NW, NPR = D / 2, NP = NT / NPR, TPP = C / NP;
-  static_assert(NP * NPR == NT && NP * TPP == C && NP <= 8 && TPP % 8 == 0, "thread layout");
-  word* sQ = (word*)(smem + M::Q);
-  word* sK = (word*)(smem + M::K);
-  word* sG = (word*)(smem + M::G);
-  const word* sV = (const word*)(smem + M::V);
-  T* sKT = (T*)(smem + M::KT);
-  T* sKH = (T*)(smem + M::KH);
-  T* sVT = (T*)(smem + M::VT);
-  float* sPart = (float*)(smem + M::PART);
-  float* sGL = (float*)(smem + M::GL);
-  const int cp = tid % NPR, c = 2 * cp, part = tid / NPR, t0 = TPP * part;
-  auto at = [&](int t) { return t * (LDT / 2) + cp; };  // pair index of (row t, channel c)
+  static constexpr int NPR = D / 2, ES = (int)sizeof(T);
+  static_assert(!MX || sizeof(T) == 2, "MXFP8 inputs feed the bf16 path");
+  word q[WITH_Q ? 8 : 1], k[8], v[8], g[8];  // MX: q, k, v hold two e4m3 bytes in the low half
+  uint32_t qs[MX && WITH_Q ? 8 : 1], ks[MX ? 8 : 1], vs[MX ? 8 : 1];
+  float beta;
 
-  // decays in log2 units, so that every factor is one v_exp_f32 (exp2)
+  // chunk rows tok0 .. tok0 + clen - 1 (clen >= 1) of head h
+  __device__ __forceinline__ void load(const ChunkInputs& in, int64_t tok0, int clen, int H, int h, int tid,
+                                       int gate) {
+    constexpr int aux = NT ? 2 : 0;                    // non-temporal
+    const int cp = tid % NPR, part = tid / NPR;
+    const size_t row0 = (size_t)tok0 * H + h;          // first (token, head) row of the chunk
+    const uint32_t rs = (uint32_t)H * D;               // row stride, elements
+    const uint32_t span = (uint32_t)(clen - 1) * rs + D;  // elements from row0 * D to the chunk's end
+    const uint32_t off0 = (uint32_t)(8 * part) * rs + 2 * cp;
+    if (MX) {
+      const uint32_t sspan = span / 32;
+      const __amdgpu_buffer_rsrc_t rk = rsrc((const uint8_t*)in.k + row0 * D, span);
+      const __amdgpu_buffer_rsrc_t rv = rsrc((const uint8_t*)in.v + row0 * D, span);
+      const __amdgpu_buffer_rsrc_t rks = rsrc(in.ks + row0 * D / 32, sspan);
+      const __amdgpu_buffer_rsrc_t rvs = rsrc(in.vs + row0 * D / 32, sspan);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t off = off0 + (uint32_t)s * rs;
+        k[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rk, off, 0, aux);
+        v[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, aux);
+        ks[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rks, off / 32, 0, aux);
+        vs[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rvs, off / 32, 0, aux);
+      }
+      if constexpr (WITH_Q) {
+        const __amdgpu_buffer_rsrc_t rq = rsrc((const uint8_t*)in.q + row0 * D, span);
+        const __amdgpu_buffer_rsrc_t rqs = rsrc(in.qs + row0 * D / 32, sspan);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t off = off0 + (uint32_t)s * rs;
+          q[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, off, 0, aux);
+          qs[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rqs, off / 32, 0, aux);
+        }
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rk = rsrc((const T*)in.k + row0 * D, span * ES);
+      const __amdgpu_buffer_rsrc_t rv = rsrc((const T*)in.v + row0 * D, span * ES);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        k[s] = PW::template load<aux>(rk, (off0 + (uint32_t)s * rs) * ES);
+        v[s] = PW::template load<aux>(rv, (off0 + (uint32_t)s * rs) * ES);
+      }
+      if constexpr (WITH_Q) {
+        const __amdgpu_buffer_rsrc_t rq = rsrc((const T*)in.q + row0 * D, span * ES);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) q[s] = PW::template load<aux>(rq, (off0 + (uint32_t)s * rs) * ES);
+      }
+    }
+    if (gate == kGateChannel) {
+      const __amdgpu_buffer_rsrc_t rgt = rsrc((const T*)in.g + row0 * D, span * ES);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) g[s] = PW::template load<aux>(rgt, (off0 + (uint32_t)s * rs) * ES);
+    } else if (gate == kGateHead) {
+      const __amdgpu_buffer_rsrc_t rgt = rsrc((const T*)in.g + row0, ((uint32_t)(clen - 1) * H + 1) * ES);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) g[s] = PW::template load1<aux>(rgt, (uint32_t)(8 * part + s) * H * ES);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) g[s] = PW::zero();
+    }
+    const __amdgpu_buffer_rsrc_t rb = rsrc(in.beta + row0, ((uint32_t)(clen - 1) * H + 1) * 4);
+    beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)tid * H * 4, 0, aux));
+  }
+  // the pair (2 cp, 2 cp + 1) of row s as operand words
+  __device__ static __forceinline__ word dec(word w, uint32_t s) {
+    if constexpr (MX) {
+      const float sc = __uint_as_float(s ? s << 23 : 0x00400000u);  // 2^(s - 127)
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, false));
+    } else {
+      return w;
+    }
+  }
+  __device__ __forceinline__ word qw(int s) const { return dec(q[WITH_Q ? s : 0], MX && WITH_Q ? qs[s] : 0u); }
+  __device__ __forceinline__ word kw(int s) const { return dec(k[s], MX ? ks[s] : 0u); }
+  __device__ __forceinline__ word vw(int s) const { return dec(v[s], MX ? vs[s] : 0u); }
+};
+
+// ---- element-wise stage -----------------------------------------------------
+// Floored log-decays in log2 units (every factor is one exp2); their partial
+// sums over the thread's 8 rows go to PART (estage1); after a barrier each
+// thread adds the parts before its own and forms Qt, Kt, Kh row by row, stored
+// with V, beta and gamma into the chunk's buffer set `buf` (estage2).
+template <typename T, int D, bool OUT, bool MX, bool NT>
+__device__ __forceinline__ void estage1(unsigned char* smem, const Raw<T, D, OUT, MX, NT>& raw, float g_floor,
+                                        int gate, int tid, float (&g0)[8], float (&g1)[8]) {
+  typedef Lay<T, D, OUT> Y;
+  typedef PairT<T> PW;
   constexpr float kLog2e = 1.4426950408889634f;
-  float g0[TPP], g1[TPP];
+  const int cp = tid % (D / 2), part = tid / (D / 2), c = 2 * cp;
+  typename PW::word w[8];
+  if (gate == kGateHead) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) w[s] = PW::splat(raw.g[s]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) w[s] = raw.g[s];
+  }
   float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-  for (int s = 0; s < TPP; ++s) {
-    const word w = sG[at(t0 + s)];
-    const float x0 = PW::lo(w), x1 = PW::hi(w);
+  for (int s = 0; s < 8; ++s) {
+    const float x0 = PW::lo(w[s]), x1 = PW::hi(w[s]);
     g0[s] = (x0 < g_floor ? g_floor : x0) * kLog2e;  // NaN stays NaN
     g1[s] = (x1 < g_floor ? g_floor : x1) * kLog2e;
     p0 += g0[s];
     p1 += g1[s];
   }
-  *(f32x2*)(sPart + part * D + c) = (f32x2){p0, p1};
-  __syncthreads();
+  *(f32x2*)((float*)(smem + Y::PART) + part * D + c) = (f32x2){p0, p1};
+}
+template <typename T, int D, bool OUT, bool MX, bool NT>
+__device__ __forceinline__ void estage2(unsigned char* smem, int buf, const Raw<T, D, OUT, MX, NT>& raw, int tid,
+                                        const float (&g0)[8], const float (&g1)[8]) {
+  typedef Lay<T, D, OUT> Y;
+  typedef PairT<T> PW;
+  typedef typename PW::word word;
+  const int cp = tid % (D / 2), part = tid / (D / 2), c = 2 * cp;
+  const float* sPart = (const float*)(smem + Y::PART);
   float gam0 = 0.f, gam1 = 0.f, gl0 = 0.f, gl1 = 0.f;
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
+  for (int p = 0; p < 8; ++p) {
     const f32x2 x = *(const f32x2*)(sPart + p * D + c);
     gam0 += p < part ? x[0] : 0.f;
     gam1 += p < part ? x[1] : 0.f;
     gl0 += x[0];
     gl1 += x[1];
   }
-  if (part == 0) *(f32x2*)(sGL + c) = (f32x2){__builtin_amdgcn_exp2f(gl0), __builtin_amdgcn_exp2f(gl1)};
-
+  if (part == 0)
+    *(f32x2*)((float*)(smem + Y::gam(buf)) + c) = (f32x2){__builtin_amdgcn_exp2f(gl0), __builtin_amdgcn_exp2f(gl1)};
+  T* sQ = (T*)(smem + Y::qt(buf));
+  T* sK = (T*)(smem + Y::KT);
+  T* sH = (T*)(smem + Y::kh(buf));
+  T* sV = (T*)(smem + Y::VV);
 #pragma unroll
-  for (int b0 = 0; b0 < TPP; b0 += 8) {
-    const int tb = t0 + b0;
-    word kw[8], qw[8], vw[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kw[s] = sK[at(tb + s)];
-      vw[s] = sV[at(tb + s)];
-      if (WITH_Q) qw[s] = sQ[at(tb + s)];
-    }
-    word kt[8], kh[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      gam0 += g0[b0 + s];
-      gam1 += g1[b0 + s];
-      const float e0 = __builtin_amdgcn_exp2f(gam0), e1 = __builtin_amdgcn_exp2f(gam1);
-      const float ei0 = __builtin_amdgcn_exp2f(-gam0), ei1 = __builtin_amdgcn_exp2f(-gam1);
-      const float k0 = PW::lo(kw[s]), k1 = PW::hi(kw[s]);
-      kt[s] = PW::pack(k0 * e0, k1 * e1);
-      kh[s] = PW::pack(k0 * ei0, k1 * ei1);
-      sK[at(tb + s)] = kt[s];
-      sG[at(tb + s)] = kh[s];
-      if (WITH_Q) sQ[at(tb + s)] = PW::pack(PW::lo(qw[s]) * e0, PW::hi(qw[s]) * e1);
-    }
-    store_cols8(sKT + c * LDC + tb, LDC, kt);
-    store_cols8(sKH + c * LDC + tb, LDC, kh);
-    store_cols8(sVT + c * LDC + tb, LDC, vw);
-  }
-  __syncthreads();
-}
-
-// (I + A_bb)^{-1} for diagonal block b (16 x 16, unit lower triangular) by
-// fp32 forward substitution, lane idx solving column idx; written to
-// sTii[b][16][16].  Called by the wave that has just written row tile b of A
-// (its own LDS writes are visible to its later reads).
-template <int LDF>
-__device__ __forceinline__ void diag_inverse(const float* sA, float* sTii, int b, int lane) {
-  const int idx = lane & 15, b0 = 16 * b;
-  float x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float acc = (r == idx) ? 1.f : 0.f;
-#pragma unroll
-    for (int m = 0; m < r; ++m) acc -= sA[(b0 + r) * LDF + b0 + m] * x[m];
-    x[r] = acc;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sTii[(b * 16 + r) * 16 + idx] = x[r];
-  }
-}
-
-// ---- Gram blocks: A = diag(beta) strict_lower(Kt Kh^T) (fp32) and
-// P = lower_incl(Qt Kh^T) (operand type), as 16 x 16 tiles on and below the
-// diagonal, each one MMA chain over the key channels: rows from Kt (A) or Qt
-// (P), columns from Kh.  Four waves: wave w takes row tile w of A and row
-// tile 3 - w of P (five tiles each; every Kh fragment it loads serves the A
-// and the P tile of its column).  Eight waves: waves 0-3 take the diagonal
-// tiles (b, b) of A and P, waves 4-7 three of the twelve others each, in an
-// order where consecutive tiles mostly share their column.  Of the upper P
-// tiles only (0, 1) and (2, 3) share a 32-wide k-block with needed ones; they
-// are zeroed (bf16 path).  A's upper tiles are never read.
-// Eight-wave tile lists, wave w's tile t in byte w of kGram8[t]: bit 6 set for
-// a tile (clear: the list has ended), bit 4 P (else A), bits 2-3 the row
-// tile, bits 0-1 the column tile.  Immediate operands, taken apart with
-// scalar shifts (a table in memory would be read by vector loads, which wait
-// behind the prefetch of the next chunk's inputs).
-constexpr uint64_t gram_code(int p, int r, int c) { return (uint64_t)(64 | 16 * p | 4 * r | c); }
-constexpr uint64_t gram_list(const int (&x)[8][3]) {
-  uint64_t v = 0;
-  for (int w = 0; w < 8; ++w)
-    if (x[w][0] >= 0) v |= gram_code(x[w][0], x[w][1], x[w][2]) << (8 * w);
-  return v;
-}
-constexpr int kGramT0[8][3] = {{0, 0, 0}, {0, 1, 1}, {0, 2, 2}, {0, 3, 3}, {0, 1, 0}, {1, 2, 0}, {0, 2, 1}, {1, 3, 1}};
-constexpr int kGramT1[8][3] = {{1, 0, 0}, {1, 1, 1}, {1, 2, 2}, {1, 3, 3}, {1, 1, 0}, {0, 3, 0}, {1, 2, 1}, {0, 3, 2}};
-constexpr int kGramT2[8][3] = {{-1, 0, 0}, {-1, 0, 0}, {-1, 0, 0}, {-1, 0, 0},
-                               {0, 2, 0},  {1, 3, 0},  {0, 3, 1},  {1, 3, 2}};
-constexpr uint64_t kGram8[3] = {gram_list(kGramT0), gram_list(kGramT1), gram_list(kGramT2)};
-
-template <typename T, int D>
-__device__ __forceinline__ void gram_store(unsigned char* smem, bool is_p, int r, int c, const f32x4& acc,
-                                           int lane) {
-  typedef Lds<T, D> M;
-  const int idx = lane & 15, gq = lane >> 4, s = 16 * c + idx;
-  if (!is_p) {
-    float* sA = (float*)(smem + M::V);
-    const float* sBeta = (const float*)(smem + M::BETA);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * r + 4 * gq + i;
-      sA[row * M::LDF + s] = s < row ? sBeta[row] * acc[i] : 0.f;
-    }
-  } else {
-    T* sP = (T*)(smem + M::P);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * r + 4 * gq + i;
-      sP[row * M::LDC + s] = Elem<T>::from_f32(s <= row ? acc[i] : 0.f);
+  for (int s = 0; s < 8; ++s) {
+    const int t = 8 * part + s, e = sidx<D>(t, c);
+    gam0 += g0[s];
+    gam1 += g1[s];
+    const float e0 = __builtin_amdgcn_exp2f(gam0), e1 = __builtin_amdgcn_exp2f(gam1);
+    const float ei0 = __builtin_amdgcn_exp2f(-gam0), ei1 = __builtin_amdgcn_exp2f(-gam1);
+    const word kw = raw.kw(s);
+    const float k0 = PW::lo(kw), k1 = PW::hi(kw);
+    *(word*)(sK + e) = PW::pack(k0 * e0, k1 * e1);
+    *(word*)(sH + e) = PW::pack(k0 * ei0, k1 * ei1);
+    *(word*)(sV + e) = raw.vw(s);
+    if (OUT) {
+      const word qw = raw.qw(s);
+      *(word*)(sQ + e) = PW::pack(PW::lo(qw) * e0, PW::hi(qw) * e1);
     }
   }
+  if (tid < C) ((float*)(smem + Y::BETA))[tid] = raw.beta;
 }
 
-template <typename T, int D, int NW, bool WITH_P>
-__device__ __forceinline__ void gram(unsigned char* smem, int wave, int lane) {
-  typedef Lds<T, D> M;
-  typedef typename Frag<T>::type FragT;
-  static_assert(NW == 4 || NW == 8, "Gram tiles over four or eight waves");
-  static_assert(NW == 4 || WITH_P, "the eight-wave split includes P");
-  constexpr int KB = Elem<T>::KB, NKD = D / KB, LDT = M::LDT, LDC = M::LDC, LDF = M::LDF;
-  const T* sQ = (const T*)(smem + M::Q);
-  const T* sK = (const T*)(smem + M::K);
-  const T* sG = (const T*)(smem + M::G);
-  T* sP = (T*)(smem + M::P);
-  const int idx = lane & 15, gq = lane >> 4;
-  if constexpr (NW == 8) {
-    FragT fb[NKD];
-    int cprev = -1;
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      const int code = (int)(kGram8[t] >> (8 * wave)) & 0xff;  // wave-uniform
-      if (!(code & 64)) break;
-      const bool is_p = code & 16;
-      const int r = (code >> 2) & 3, c = code & 3;
-      if (c != cprev) {
-#pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) fb[kb] = frag_rows(sG, LDT, 16 * c + idx, kb * KB, gq);
-        cprev = c;
-      }
-      const T* src = is_p ? sQ : sK;
-      FragT fr[NKD];
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) fr[kb] = frag_rows(src, LDT, 16 * r + idx, kb * KB, gq);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) acc = mma(fr[kb], fb[kb], acc);
-      gram_store<T, D>(smem, is_p, r, c, acc, lane);
-    }
-    if (KB == 32 && (wave == 0 || wave == 2)) {
-      // P tile (0, 1) from wave 0, tile (2, 3) from wave 2
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sP[(16 * wave + 4 * gq + i) * LDC + 16 * wave + 16 + idx] = Elem<T>::from_f32(0.f);
-    }
-    // the diagonal block of A just written, by the same wave
-    if (wave < 4) diag_inverse<LDF>((const float*)(smem + M::V), (float*)(smem + M::TII), wave, lane);
-  } else {
-    const int rA = wave, rP = 3 - wave;  // wave-uniform
-    FragT fa[NKD], fq[NKD];
-#pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-      fa[kb] = frag_rows(sK, LDT, 16 * rA + idx, kb * KB, gq);
-      if (WITH_P) fq[kb] = frag_rows(sQ, LDT, 16 * rP + idx, kb * KB, gq);
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const bool doA = ct <= rA, doP = WITH_P && ct <= rP;
-      if (doA || doP) {
-        FragT fb[NKD];
-#pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) fb[kb] = frag_rows(sG, LDT, 16 * ct + idx, kb * KB, gq);
-        if (doA) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < NKD; ++kb) acc = mma(fa[kb], fb[kb], acc);
-          gram_store<T, D>(smem, false, rA, ct, acc, lane);
-        }
-        if (doP) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < NKD; ++kb) acc = mma(fq[kb], fb[kb], acc);
-          gram_store<T, D>(smem, true, rP, ct, acc, lane);
-        }
-      }
-    }
-    if (WITH_P && KB == 32 && (rP == 0 || rP == 2)) {
-      // P tile (0, 1) from the wave with rP = 0, tile (2, 3) from rP = 2
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sP[(16 * rP + 4 * gq + i) * LDC + 16 * rP + 16 + idx] = Elem<T>::from_f32(0.f);
-    }
-    diag_inverse<LDF>((const float*)(smem + M::V), (float*)(smem + M::TII), rA, lane);
-  }
-  __syncthreads();
-}
-
-// ---- the inverse (I + A)^{-1} and the WY products -----------------------
-// Tp = (I + A)^{-1} diag(beta) (64 x 64, lower triangular) is formed once per
-// chunk, by 16-column blocks: wave j < 4 takes column block j,
-//   Tp_jj = T_jj diag(beta_j),   Tp_ij = -T_ii sum_{m=j}^{i-1} A_im Tp_mj  (i > j),
-// with the diagonal inverses T_ii = (I + A_ii)^{-1} from fp32 forward
-// substitution.  The 16 x 16 x 16 products take A_im and T_ii rounded to bf16
-// and Tp_mj as a hi/lo bf16 pair (fp32 path: fp32 MFMA), accumulating in
-// fp32.  Tp goes to LDS as a hi and a lo bf16 array (fp32 path: one fp32
-// array), zeros above the diagonal.  Then
-//   Wk = Tp Kt,   Wv = Tp V
-// are plain MFMA products whose right-hand operands are the chunk operands
-// themselves (exact in bf16): only Tp needs the two-term split.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// ---- fragment images and 16 x 16 x 16 block products ----------------------
 __device__ __forceinline__ s16x4 to_bf16x4(const f32x4& x) {
   const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1]));
   const uint32_t b = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3]));
   return __builtin_bit_cast(s16x4, (uint2){a, b});
 }
-__device__ __forceinline__ f32x4 from_bf16x4(const s16x4& h) {
-  const uint2 w = __builtin_bit_cast(uint2, h);
-  return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-                 __uint_as_float(w.y & 0xffff0000u)};
-}
-
-// c + a b over k = 16 for one 16 x 16 tile: a is a coefficient fragment (row
-// idx, k = 4 g .. 4 g + 3), b an accumulator tile whose rows run over k,
-// prepared once as an operand (Opnd) and used by every product it enters.
-template <typename T> struct Sub;
-template <> struct Sub<bf16_t> {
+// Blk<T>: coefficient fragments (A operand of a 16 x 16 x 16 product: lane
+// (g, i) holds row i, k = 4 g .. 4 g + 3) kept as images, and right operands
+// from accumulator tiles.  bf16: a right operand is split hi + lo, so that
+// the product keeps about fp32 accuracy in it; the diagonal inverses are
+// split too (tri: three products).  fp32: fp32 MFMA throughout.
+template <typename T> struct Blk;
+template <> struct Blk<bf16_t> {
   typedef s16x4 Coef;
-  struct Opnd { s16x4 hi, lo; };
-  __device__ static __forceinline__ Coef coef(const float* p, bool neg) {
-    const f32x4 v = *(const f32x4*)p;
-    return to_bf16x4(neg ? -v : v);
+  struct Opnd {
+    s16x4 hi, lo;
+  };
+  static constexpr int NPARTS = 2;
+  __device__ static __forceinline__ Coef load(const unsigned char* p) { return *(const s16x4*)p; }
+  __device__ static __forceinline__ void store(unsigned char* p, const f32x4& x) { *(s16x4*)p = to_bf16x4(x); }
+  __device__ static __forceinline__ void store_split(unsigned char* hi, unsigned char* lo, const f32x4& x) {
+    const s16x4 h = to_bf16x4(x);
+    *(s16x4*)hi = h;
+    *(s16x4*)lo = to_bf16x4(x - widen4(h));
   }
   __device__ static __forceinline__ Opnd opnd(const f32x4& b) {
     Opnd o;
     o.hi = to_bf16x4(b);
-    o.lo = to_bf16x4(b - from_bf16x4(o.hi));
+    o.lo = to_bf16x4(b - widen4(o.hi));
     return o;
   }
   __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) {
     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, c, 0, 0, 0);
   }
+  __device__ static __forceinline__ f32x4 tri(const Coef& th, const Coef& tl, const Opnd& r) {
+    f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(th, r.hi, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(th, r.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tl, r.hi, c, 0, 0, 0);
+  }
 };
-template <> struct Sub<float> {
+template <> struct Blk<float> {
   typedef f32x4 Coef;
   typedef f32x4 Opnd;
-  __device__ static __forceinline__ Coef coef(const float* p, bool neg) {
-    const f32x4 v = *(const f32x4*)p;
-    return neg ? -v : v;
+  static constexpr int NPARTS = 1;
+  __device__ static __forceinline__ Coef load(const unsigned char* p) { return *(const f32x4*)p; }
+  __device__ static __forceinline__ void store(unsigned char* p, const f32x4& x) { *(f32x4*)p = x; }
+  __device__ static __forceinline__ void store_split(unsigned char* hi, unsigned char*, const f32x4& x) {
+    *(f32x4*)hi = x;
   }
   __device__ static __forceinline__ Opnd opnd(const f32x4& b) { return b; }
   __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) { return mma(a, b, c); }
+  __device__ static __forceinline__ f32x4 tri(const Coef& th, const Coef&, const Opnd& r) {
+    return mma(th, r, (f32x4){0.f, 0.f, 0.f, 0.f});
+  }
 };
 
-// Tp in the K area (free after the Gram blocks): rows of LD elements; bf16
-// keeps Tp = hi + lo in two arrays.
-template <typename T, int D> struct TpArea {
-  static constexpr int LD = C + 4;
-  static constexpr int HI = Lds<T, D>::K;
-  static constexpr int LO = HI + C * LD * (int)sizeof(T);
-  static_assert((sizeof(T) == 2 ? 2 : 1) * C * LD * sizeof(T) <= (size_t)Lds<T, D>::ROW, "Tp fits the K area");
-};
-
-// tile (i, j) of Tp (accumulator layout) into the Tp area
+// ---- Gram tiles ---------------------------------------------------------------
+// lane (g, i) = sum_c XA[ra + 4 g + e][c] XB[rb + i][c]: with XA = Kh and
+// XB = Kt or Qt, element (row rb + i, k = ra + 4 g + e) of Kt Kh^T or Qt Kh^T,
+// i.e. directly the coefficient fragment of that block.
 template <typename T, int D>
-__device__ __forceinline__ void store_tp(unsigned char* smem, const f32x4& w, int i, int j, int lane) {
-  typedef TpArea<T, D> TP;
-  const int idx = lane & 15, gq = lane >> 4;
-  const int off = (16 * i + 4 * gq) * TP::LD + 16 * j + idx;
-  if constexpr (sizeof(T) == 2) {
-    const s16x4 hi = to_bf16x4(w);
-    const uint2 h = __builtin_bit_cast(uint2, hi);
-    const uint2 l = __builtin_bit_cast(uint2, to_bf16x4(w - from_bf16x4(hi)));
-    bf16_t* ph = (bf16_t*)(smem + TP::HI) + off;
-    bf16_t* pl = (bf16_t*)(smem + TP::LO) + off;
-    ph[0] = (bf16_t)(h.x & 0xffffu);
-    ph[TP::LD] = (bf16_t)(h.x >> 16);
-    ph[2 * TP::LD] = (bf16_t)(h.y & 0xffffu);
-    ph[3 * TP::LD] = (bf16_t)(h.y >> 16);
-    pl[0] = (bf16_t)(l.x & 0xffffu);
-    pl[TP::LD] = (bf16_t)(l.x >> 16);
-    pl[2 * TP::LD] = (bf16_t)(l.y & 0xffffu);
-    pl[3 * TP::LD] = (bf16_t)(l.y >> 16);
+__device__ __forceinline__ f32x4 gram_tile(const T* XA, int ra, const T* XB, int rb, int lane) {
+  constexpr int KB = Elem<T>::KB;
+  const int g = lane >> 4, i = lane & 15;
+  typename Frag<T>::type fa[D / KB], fb[D / KB];
+#pragma unroll
+  for (int kb = 0; kb < D / KB; ++kb) {
+    fa[kb] = rowfrag<D>(XA, ra + i, kb * KB, g);
+    fb[kb] = rowfrag<D>(XB, rb + i, kb * KB, g);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < D / KB; ++kb) acc = mma(fa[kb], fb[kb], acc);
+  return acc;
+}
+// Off-diagonal block (i, m), m < i, of -A = -diag(beta) Kt Kh^T, as an image.
+template <typename T, int D, bool OUT>
+__device__ __forceinline__ void a_block(unsigned char* smem, int buf, int i, int m, int lane) {
+  typedef Lay<T, D, OUT> Y;
+  const f32x4 t = gram_tile<T, D>((const T*)(smem + Y::kh(buf)), 16 * m, (const T*)(smem + Y::KT), 16 * i, lane);
+  const float nb = -((const float*)(smem + Y::BETA))[16 * i + (lane & 15)];
+  Blk<T>::store(smem + Y::aimg(i, m) + lane * 4 * Y::ES, nb * t);
+}
+// Tile (rt, sb), sb <= rt, of P = lower_incl(Qt Kh^T), as an image.
+template <typename T, int D>
+__device__ __forceinline__ void p_block(unsigned char* smem, int buf, int rt, int sb, int lane) {
+  typedef Lay<T, D, true> Y;
+  f32x4 t = gram_tile<T, D>((const T*)(smem + Y::kh(buf)), 16 * sb, (const T*)(smem + Y::qt(buf)), 16 * rt, lane);
+  if (sb == rt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * (lane >> 4) + e > (lane & 15)) t[e] = 0.f;
+  }
+  Blk<T>::store(smem + Y::pimg(rt, sb) + lane * 4 * Y::ES, t);
+}
+// Diagonal block b: T_bb = (I + A_bb)^{-1}, A_bb = diag(beta) strict_lower(
+// Kt Kh^T) (16 x 16, nilpotent).  With N = -A_bb,
+//   T_bb = (I + N)(I + N^2)(I + N^4)(I + N^8)
+// (N^16 = 0), four levels of 16 x 16 x 16 fp32 MFMA products instead of a
+// 16-step substitution.  A 16 x 16 matrix X is held in one of two layouts:
+// coef(X) (lane (g, i) has X[i][4 g + e], a left operand) and acc(X) (lane
+// (g, i) has X[4 g + e][i], a right operand and a product's result); coef(X)
+// = acc(X^T), so for Z = X Y: acc(Z) = mma(coef(X), acc(Y)) and coef(Z) =
+// mma(acc(Y), coef(X)).  The two Gram tiles give N in both layouts.  Lane
+// (g, i) ends with coef(T_bb), the coefficient fragment, stored as an image
+// (bf16: hi and lo).
+template <typename T, int D, bool OUT>
+__device__ __forceinline__ void diag_block(unsigned char* smem, int buf, int b, int lane) {
+  typedef Lay<T, D, OUT> Y;
+  const int g = lane >> 4, i = lane & 15;
+  const T* sK = (const T*)(smem + Y::KT);
+  const T* sH = (const T*)(smem + Y::kh(buf));
+  const float* sB = (const float*)(smem + Y::BETA) + 16 * b;
+  const f32x4 tc = gram_tile<T, D>(sH, 16 * b, sK, 16 * b, lane);  // (Kt Kh^T)[i][4 g + e]
+  const f32x4 ta = gram_tile<T, D>(sK, 16 * b, sH, 16 * b, lane);  // (Kt Kh^T)[4 g + e][i]
+  const float bi = sB[i];
+  const f32x4 b4 = *(const f32x4*)(sB + 4 * g);
+  f32x4 cN, aN, cT;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    cN[e] = (4 * g + e < i) ? -bi * tc[e] : 0.f;
+    aN[e] = (i < 4 * g + e) ? -b4[e] * ta[e] : 0.f;
+    cT[e] = cN[e] + (4 * g + e == i ? 1.f : 0.f);  // coef(I + N)
+  }
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 aN2 = mma(cN, aN, z), cN2 = mma(aN, cN, z);
+  const f32x4 aN4 = mma(cN2, aN2, z), cN4 = mma(aN2, cN2, z);
+  const f32x4 aN8 = mma(cN4, aN4, z);
+  cT = mma(aN2, cT, cT);  // coef(T (I + N^2)) = coef(T) + coef(T N^2)
+  cT = mma(aN4, cT, cT);
+  cT = mma(aN8, cT, cT);
+  Blk<T>::store_split(smem + Y::timg(b, 0) + lane * 4 * Y::ES, smem + Y::timg(b, Blk<T>::NPARTS - 1) + lane * 4 * Y::ES,
+                      cT);
+}
+
+// The Gram stage.  Waves 0-3 take a diagonal block each (its inverse is the
+// critical path) and, in the output sweep, the diagonal P tile; the other
+// tiles (the off-diagonal blocks of A and P) go to the other waves (all four
+// waves at d = 64, where there are only four), in an order where consecutive
+// tiles share their Kh rows.
+template <typename T, int D, bool OUT>
+__device__ __forceinline__ void gram_stage(unsigned char* smem, int buf, int wave, int lane) {
+  constexpr int NW = D / 16;
+  if (wave < 4) {
+    diag_block<T, D, OUT>(smem, buf, wave, lane);
+    if constexpr (OUT) p_block<T, D>(smem, buf, wave, wave, lane);
+  }
+  if (NW == 8 && wave < 4) return;
+  const int q = NW == 8 ? wave - 4 : wave;  // wave-uniform
+  if constexpr (OUT) {
+    // A and P of blocks (1,0) (2,0) (3,0) (2,1) (3,1) (3,2), three tiles a wave
+    switch (q) {
+      case 0: a_block<T, D, OUT>(smem, buf, 1, 0, lane); p_block<T, D>(smem, buf, 1, 0, lane); a_block<T, D, OUT>(smem, buf, 2, 0, lane); break;
+      case 1: p_block<T, D>(smem, buf, 2, 0, lane); a_block<T, D, OUT>(smem, buf, 3, 0, lane); p_block<T, D>(smem, buf, 3, 0, lane); break;
+      case 2: a_block<T, D, OUT>(smem, buf, 2, 1, lane); p_block<T, D>(smem, buf, 2, 1, lane); a_block<T, D, OUT>(smem, buf, 3, 1, lane); break;
+      default: p_block<T, D>(smem, buf, 3, 1, lane); a_block<T, D, OUT>(smem, buf, 3, 2, lane); p_block<T, D>(smem, buf, 3, 2, lane); break;
+    }
   } else {
-    float* p = (float*)(smem + TP::HI) + off;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e * TP::LD] = w[e];
+    switch (q) {
+      case 0: a_block<T, D, OUT>(smem, buf, 1, 0, lane); a_block<T, D, OUT>(smem, buf, 2, 0, lane); break;
+      case 1: a_block<T, D, OUT>(smem, buf, 3, 0, lane); a_block<T, D, OUT>(smem, buf, 2, 1, lane); break;
+      case 2: a_block<T, D, OUT>(smem, buf, 3, 1, lane); break;
+      default: a_block<T, D, OUT>(smem, buf, 3, 2, lane); break;
+    }
   }
 }
 
-// Column block j = wave (< 4) of Tp into the Tp area.  Reads A (V area) and
-// the diagonal inverses (TII area).
+// ---- the triangular system (I + A) W = diag(beta) [Kt | V] ------------------
+// By 16-row blocks, wave w on value columns 16 w .. 16 w + 15 of both halves:
+//   W_i = T_ii (beta_i X_i - sum_{m < i} A_im W_m),
+// X_i read as accumulator tiles by transpose reads.  Wk goes to LDS
+// channel-major (Wk^T, 16 contiguous tokens of a channel per lane: no
+// scatter); Wv stays in the wave's registers.
+template <typename T, int D, bool OUT>
+__device__ __forceinline__ void substitute(unsigned char* smem, int w, int lane, f32x4 (&Wv)[4]) {
+  typedef Lay<T, D, OUT> Y;
+  typedef Blk<T> Bk;
+  const T* sK = (const T*)(smem + Y::KT);
+  const T* sV = (const T*)(smem + Y::VV);
+  const float* sB = (const float*)(smem + Y::BETA);
+  const int g = lane >> 4, i = lane & 15;
+  f32x4 Wk[4];
+  typename Bk::Opnd ok[3], ov[3];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x4 b4 = *(const f32x4*)(sB + 16 * b + 4 * g);
+    f32x4 rk = b4 * widen4(colpiece<D>(sK, 16 * b, 16 * w, lane));
+    f32x4 rv = b4 * widen4(colpiece<D>(sV, 16 * b, 16 * w, lane));
+#pragma unroll
+    for (int m = 0; m < b; ++m) {
+      const typename Bk::Coef a = Bk::load(smem + Y::aimg(b, m) + lane * 4 * Y::ES);
+      rk = Bk::apply(a, ok[m], rk);
+      rv = Bk::apply(a, ov[m], rv);
+    }
+    const typename Bk::Coef th = Bk::load(smem + Y::timg(b, 0) + lane * 4 * Y::ES);
+    const typename Bk::Coef tl = Bk::load(smem + Y::timg(b, Bk::NPARTS - 1) + lane * 4 * Y::ES);
+    Wk[b] = Bk::tri(th, tl, Bk::opnd(rk));
+    Wv[b] = Bk::tri(th, tl, Bk::opnd(rv));
+    if (b < 3) {
+      ok[b] = Bk::opnd(Wk[b]);
+      ov[b] = Bk::opnd(Wv[b]);
+    }
+  }
+  T* sW = (T*)(smem + Y::WKT);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    T* p = sW + sidx<C>(16 * w + i, 16 * b + 4 * g);
+    if constexpr (sizeof(T) == 2) *(s16x4*)p = to_bf16x4(Wk[b]);
+    else *(f32x4*)p = Wk[b];
+  }
+}
+
+// ---- the state step ---------------------------------------------------------
+// Wave w owns column tile w of the state (rows = D key channels, accumulator
+// tiles S[rr]).  The same bf16 fragments of S serve as the right operand of
+// Wk S and as the left operand of S^T Qt^T; those of U as the right operand
+// of Kh^T U and the left operand of U^T P^T.  The outputs come out transposed
+// (O^T tiles: lane (g, i) holds O[token i][4 g .. 4 g + 3] of the wave's
+// columns), so each lane stores 4 contiguous elements.
 template <typename T, int D>
-__device__ __forceinline__ void inverse_cols(unsigned char* smem, int wave, int lane) {
-  typedef Lds<T, D> M;
-  typedef Sub<T> S;
-  const float* sA = (const float*)(smem + M::V);
-  const float* sTii = (const float*)(smem + M::TII);  // [4][16][16]
-  const float* sBeta = (const float*)(smem + M::BETA);
-  const int idx = lane & 15, gq = lane >> 4, j = wave;
-  typename S::Opnd wo[3];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-    if (i == j) {
-      const float b = sBeta[16 * i + idx];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = sTii[(16 * i + 4 * gq + e) * 16 + idx] * b;
-    } else if (i > j) {
-      f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < i; ++m)
-        if (m >= j) r = S::apply(S::coef(sA + (16 * i + idx) * M::LDF + 16 * m + 4 * gq, true), wo[m], r);
-      w = S::apply(S::coef(sTii + (16 * i + idx) * 16 + 4 * gq, false), S::opnd(r),
-                   (f32x4){0.f, 0.f, 0.f, 0.f});
-    }
-    if (i < 3 && i >= j) wo[i] = S::opnd(w);
-    store_tp<T, D>(smem, w, i, j, lane);
+__device__ __forceinline__ typename Frag<T>::type pfrag(const unsigned char* smem, int rt, int kb, int lane) {
+  typedef Lay<T, D, true> Y;
+  if constexpr (sizeof(T) == 2) {
+    const s16x4 a = *(const s16x4*)(smem + Y::pimg(rt, 2 * kb) + lane * 8);
+    const s16x4 b = 2 * kb + 1 <= rt ? *(const s16x4*)(smem + Y::pimg(rt, 2 * kb + 1) + lane * 8)
+                                     : (s16x4){0, 0, 0, 0};
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    return *(const f32x4*)(smem + Y::pimg(rt, kb) + lane * 16);
   }
 }
 
-// W = Tp X for NX column tiles: tile ct[t] of the channel-major X^T array
-// xt[t]; w[t][rb] is row tile rb.  Tp's zero blocks above the diagonal are
-// skipped where a whole k-block is zero.
-template <typename T, int D, int NX>
-__device__ __forceinline__ void w_products(const unsigned char* smem, const T* const (&xt)[NX], const int (&ct)[NX],
-                                           int lane, f32x4 (&w)[NX][4]) {
-  typedef Lds<T, D> M;
-  typedef TpArea<T, D> TP;
-  typedef typename Frag<T>::type FragT;
-  constexpr int KB = Elem<T>::KB, NKC = C / KB;
-  const int idx = lane & 15, gq = lane >> 4;
-  const T* tph = (const T*)(smem + TP::HI);
-  const T* tpl = (const T*)(smem + TP::LO);
-  FragT xb[NX][NKC];
-#pragma unroll
-  for (int t = 0; t < NX; ++t)
-#pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) xb[t][kb] = frag_rows(xt[t], M::LDC, 16 * ct[t] + idx, kb * KB, gq);
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-    for (int t = 0; t < NX; ++t) w[t][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      if (kb * KB > 16 * rb + 15) continue;
-      const FragT ah = frag_rows(tph, TP::LD, 16 * rb + idx, kb * KB, gq);
-#pragma unroll
-      for (int t = 0; t < NX; ++t) w[t][rb] = mma(ah, xb[t][kb], w[t][rb]);
-      if constexpr (sizeof(T) == 2) {
-        const FragT al = frag_rows(tpl, TP::LD, 16 * rb + idx, kb * KB, gq);
-#pragma unroll
-        for (int t = 0; t < NX; ++t) w[t][rb] = mma(al, xb[t][kb], w[t][rb]);
-      }
-    }
-  }
-}
-
-// Wk tile (all 64 rows, 16 channels from 16 ct) into LDS area AREA, token-major.
-template <typename T, int D, int AREA>
-__device__ __forceinline__ void store_wk(unsigned char* smem, const f32x4 (&w)[4], int ct, int lane) {
-  typedef Lds<T, D> M;
-  T* sW = (T*)(smem + AREA);
-  const int idx = lane & 15, gq = lane >> 4;
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * gq + i) * M::LDT + 16 * ct + idx] = Elem<T>::from_f32(w[rt][i]);
-}
-
-// ---- chunk record: what the chunk pass leaves for the two state passes,
-// per (chunk, head), in device memory.  It starts with an image of the state
-// passes' LDS (Img), copied linearly: the A-operand fragments of the state
-// products, each 64 lanes x 16 bytes in lane order (one 16-byte LDS read per
-// lane and fragment):
-//   WF  Wk rows       [4 row tiles][D / KB k-blocks]
-//   KF  Kh^T rows     [D / 16 row tiles][64 / KB k-blocks]
-//   GAM gamma         [D] fp32, padded to 1 KiB
-//   QF  Qt rows       [4 row tiles][D / KB k-blocks]
-//   PF  P rows        [4 row tiles][64 / KB k-blocks]
-// then
-//   WV  [D/16 column tiles][4 row tiles][64 lanes][4]  Wv in the operand type (bf16
-//       path: rounded to bf16, as U = Wv - Wk S is before every product it
-//       enters), accumulator order.
-// Chunk j of sequence n has slot (chunks of sequences 0 .. n - 1) + j.
-template <typename T, int D> struct Img {
-  static constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
-  static constexpr int WF = 0, KF = WF + 4 * NKD * 1024, GAM = KF + NR * NKC * 1024,
-                       QF = GAM + (D * 4 + 1023) / 1024 * 1024, PF = QF + 4 * NKD * 1024, BYTES = PF + 4 * NKC * 1024;
-  __device__ static __forceinline__ int q(int rt, int kb, int lane) { return QF + ((rt * NKD + kb) * 64 + lane) * 16; }
-  __device__ static __forceinline__ int w(int rt, int kb, int lane) { return WF + ((rt * NKD + kb) * 64 + lane) * 16; }
-  __device__ static __forceinline__ int k(int rr, int kb, int lane) { return KF + ((rr * NKC + kb) * 64 + lane) * 16; }
-  __device__ static __forceinline__ int p(int rt, int kb, int lane) { return PF + ((rt * NKC + kb) * 64 + lane) * 16; }
-};
-template <typename T, int D> struct CRec {
-  static constexpr size_t ES = sizeof(T);
-  static constexpr size_t WV = Img<T, D>::BYTES, BYTES = WV + (size_t)C * D * ES;
-  __device__ static __forceinline__ size_t wv(int ct, int rt, int lane) {
-    return WV + (((size_t)ct * 4 + rt) * 64 + lane) * 4 * ES;
-  }
-  typedef typename std::conditional<sizeof(T) == 2, uint2, f32x4>::type WvRaw;
-  // one lane's 4 accumulator values of a Wv tile, in the operand type
-  __device__ static __forceinline__ WvRaw pack(const f32x4& w) {
-    if constexpr (sizeof(T) == 2) {
-      return (uint2){__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[0], w[1])),
-                     __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(w[2], w[3]))};
-    } else {
-      return w;
-    }
-  }
-  __device__ static __forceinline__ void put_wv(unsigned char* p, const f32x4& w) { *(WvRaw*)p = pack(w); }
-  // loaded as raw words (a prefetch then holds them without waiting for the
-  // load) and widened only where they are used
-  __device__ static __forceinline__ WvRaw load_wv(const unsigned char* p) {
-    if constexpr (sizeof(T) == 2) return __builtin_bit_cast(WvRaw, __builtin_nontemporal_load((const u32x2nt*)p));
-    else return __builtin_bit_cast(WvRaw, __builtin_nontemporal_load((const u32x4nt*)p));
-  }
-  __device__ static __forceinline__ f32x4 widen(const WvRaw& u) {
-    if constexpr (sizeof(T) == 2) {
-      return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                     __uint_as_float(u.y & 0xffff0000u)};
-    } else {
-      return u;
-    }
-  }
-  // w rounded as the record stores it
-  __device__ static __forceinline__ f32x4 as_stored(const f32x4& w) { return widen(pack(w)); }
-};
-
-// The chunk's record from the chunk pass's LDS, in two parts:
-//   save_early: Qt (Q area), Kh^T (KH), P (P) fragments and gamma (GL), ready
-//               once the Gram blocks are done;
-//   save_wk:    Wk fragments (area WKA), ready after the W products.
-// Waves w0 .. w0 + nw - 1 take the fragments w - w0, w - w0 + nw, ...
+// Operand fragments are fetched a row block ahead of their products (two
+// register sets), so each group of MFMAs waits for loads issued a group
+// earlier rather than for the one just before it.
 template <typename T, int D>
-__device__ __forceinline__ void save_early(const unsigned char* smem, unsigned char* rec, int w, int nw, int lane) {
-  typedef Lds<T, D> M;
-  typedef Img<T, D> I;
+__device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f32x4 (&S)[D / 16],
+                                          const f32x4 (&Wv)[4], int w, int lane, T* __restrict__ o, int64_t tokc,
+                                          int clen, int H, int h) {
+  typedef Lay<T, D, true> Y;
   typedef typename Frag<T>::type FragT;
-  constexpr int KB = I::KB, NQ = 4 * I::NKD, NK = I::NR * I::NKC, NP = 4 * I::NKC, NF = NQ + NK + NP;
-  const int idx = lane & 15, gq = lane >> 4;
-  const T* sQ = (const T*)(smem + M::Q);
-  const T* sKH = (const T*)(smem + M::KH);
-  const T* sP = (const T*)(smem + M::P);
-  for (int f = w; f < NF; f += nw) {
-    FragT x;
-    int off;
-    if (f < NQ) {
-      const int rt = f / I::NKD, kb = f % I::NKD;
-      x = frag_rows(sQ, M::LDT, 16 * rt + idx, kb * KB, gq);
-      off = I::q(rt, kb, lane);
-    } else if (f < NQ + NK) {
-      const int rr = (f - NQ) / I::NKC, kb = (f - NQ) % I::NKC;
-      x = frag_rows(sKH, M::LDC, 16 * rr + idx, kb * KB, gq);
-      off = I::k(rr, kb, lane);
-    } else {
-      const int rt = (f - NQ - NK) / I::NKC, kb = (f - NQ - NK) % I::NKC;
-      x = frag_rows(sP, M::LDC, 16 * rt + idx, kb * KB, gq);
-      off = I::p(rt, kb, lane);
-    }
-    *(FragT*)(rec + off) = x;
-  }
-  if (w == 0 && lane < D / 4) *(f32x4*)(rec + I::GAM + 16 * lane) = *(const f32x4*)(smem + M::GL + 16 * lane);
-}
-template <typename T, int D, int WKA>
-__device__ __forceinline__ void save_wk(const unsigned char* smem, unsigned char* rec, int w, int nw, int lane) {
-  typedef Lds<T, D> M;
-  typedef Img<T, D> I;
-  typedef typename Frag<T>::type FragT;
-  constexpr int KB = I::KB, NQ = 4 * I::NKD;
-  const int idx = lane & 15, gq = lane >> 4;
-  const T* sW = (const T*)(smem + WKA);
-  for (int f = w; f < NQ; f += nw) {
-    const int rt = f / I::NKD, kb = f % I::NKD;
-    *(FragT*)(rec + I::w(rt, kb, lane)) = frag_rows(sW, M::LDT, 16 * rt + idx, kb * KB, gq);
-  }
-}
-
-// Record image bytes [0, NBYTES) -> LDS `dst` by direct global-to-LDS loads
-// (lane i of a wave fills bytes 16 i .. 16 i + 15 of a 1 KiB block; no
-// registers held).  Wave w takes blocks w, w + NW, ...; part k of NPARTS
-// issues the k-th slice of them, so that the issue can be spread over other
-// work.  The loads are only issued: vmcnt_wait_all() and a barrier make them
-// visible.
-constexpr int kCpolNt = 2;  // cache-policy operand of the direct loads: non-temporal
-template <int NW, int NBYTES, int NPARTS>
-__device__ __forceinline__ void issue_image(unsigned char* dst, const unsigned char* rec, int wave, int lane, int k) {
-  constexpr int NB = NBYTES / 1024;
-  static_assert(NBYTES % 1024 == 0, "whole blocks");
-  const int nbw = (NB - wave + NW - 1) / NW;  // blocks of this wave
-  const int i0 = k * nbw / NPARTS, i1 = (k + 1) * nbw / NPARTS;
-  for (int i = i0; i < i1; ++i) {
-    const int b = wave + NW * i;
-    __builtin_amdgcn_global_load_lds((const void*)(rec + 1024 * b + 16 * lane),
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16, 0,
-                                     kCpolNt);
-  }
-}
-__device__ __forceinline__ void vmcnt_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
-// Workgroup barrier that orders LDS reads and writes only: it waits for this
-// wave's LDS operations but not for its global loads, so direct-to-LDS loads
-// into the other image buffer stay in flight (__syncthreads() would wait for
-// them as pending LDS writes).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Where a state step reads its A operands (each one 16-byte LDS read per
-// lane): a record image (ImgSrc, the state passes), or the chunk pass's own
-// arrays (LdsSrc: Qt, Kh^T, P, gamma and Wk in area WKA), from which the
-// image fragments are cut, so both give the same values.
-template <typename T, int D> struct ImgSrc {
-  typedef Img<T, D> I;
-  typedef typename Frag<T>::type FragT;
-  const unsigned char* img;
-  int lane;
-  __device__ __forceinline__ FragT at(int off) const { return *(const FragT*)(img + off); }
-  __device__ __forceinline__ FragT w(int rt, int kb) const { return at(I::w(rt, kb, lane)); }
-  __device__ __forceinline__ FragT q(int rt, int kb) const { return at(I::q(rt, kb, lane)); }
-  __device__ __forceinline__ FragT p(int rt, int kb) const { return at(I::p(rt, kb, lane)); }
-  __device__ __forceinline__ FragT k(int rr, int kb) const { return at(I::k(rr, kb, lane)); }
-  __device__ __forceinline__ f32x4 gam(int rr) const {
-    return *(const f32x4*)(img + I::GAM + 4 * (16 * rr + 4 * (lane >> 4)));
-  }
-};
-template <typename T, int D, int WKA> struct LdsSrc {
-  typedef Lds<T, D> M;
-  typedef typename Frag<T>::type FragT;
-  static constexpr int KB = Elem<T>::KB;
-  const unsigned char* smem;
-  int lane;
-  __device__ __forceinline__ FragT rows(int area, int ld, int r, int kb) const {
-    return frag_rows((const T*)(smem + area), ld, r + (lane & 15), kb * KB, lane >> 4);
-  }
-  __device__ __forceinline__ FragT w(int rt, int kb) const { return rows(WKA, M::LDT, 16 * rt, kb); }
-  __device__ __forceinline__ FragT q(int rt, int kb) const { return rows(M::Q, M::LDT, 16 * rt, kb); }
-  __device__ __forceinline__ FragT p(int rt, int kb) const { return rows(M::P, M::LDC, 16 * rt, kb); }
-  __device__ __forceinline__ FragT k(int rr, int kb) const { return rows(M::KH, M::LDC, 16 * rr, kb); }
-  __device__ __forceinline__ f32x4 gam(int rr) const {
-    return *(const f32x4*)(smem + M::GL + 4 * (16 * rr + 4 * (lane >> 4)));
-  }
-};
-
-// CT column tiles of the state (rows = D key channels) through one chunk:
-// U = Wv - Wk S; S <- diag(gamma) (S + Kh^T U).  With WITH_O also
-// O = Qt S + P U.  `wv` holds Wv's tiles for these columns.  The A operands
-// come from `src` (ImgSrc or LdsSrc), each loaded once per phase and fed to
-// the CT tiles.  hook(k), k = 0 .. 4 + D / 16 - 1, is called between the row
-// blocks (the callers spread the next image's loads there).
-template <typename T, int D, int CT, bool WITH_O, typename Src, typename Hook>
-__device__ __forceinline__ void state_step(const Src& src, f32x4 (&S)[CT][D / 16], const f32x4 (&wv)[CT][4],
-                                           f32x4 (&O)[CT][4], int lane, Hook&& hook) {
-  typedef Img<T, D> I;
-  typedef typename Frag<T>::type FragT;
-  constexpr int KB = I::KB, NKD = I::NKD, NKC = I::NKC, NR = I::NR;
-
-  FragT SB[CT][NKD];
+  constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
+  const T* sQ = (const T*)(smem + Y::qt(buf));
+  const T* sH = (const T*)(smem + Y::kh(buf));
+  const T* sW = (const T*)(smem + Y::WKT);
+  const float* sG = (const float*)(smem + Y::gam(buf));
+  const int g = lane >> 4, i = lane & 15;
+  FragT SB[NKD];
 #pragma unroll
-  for (int c = 0; c < CT; ++c)
+  for (int kb = 0; kb < NKD; ++kb) SB[kb] = Frag<T>::from_acc(S, kb);
+  // U = Wv - Wk S
+  f32x4 U[4];
+  {
+    FragT a[2][NKD];
 #pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) SB[c][kb] = Frag<T>::from_acc(S[c], kb);
-  // U and Qt S
-  f32x4 U[CT][4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    FragT aw[NKD], aq[NKD];
-#pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-      aw[kb] = src.w(rt, kb);
-      if (WITH_O) aq[kb] = src.q(rt, kb);
-    }
-    f32x4 ws[CT], qs[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) ws[c] = qs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKD; ++kb)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        ws[c] = mma(aw[kb], SB[c][kb], ws[c]);
-        if (WITH_O) qs[c] = mma(aq[kb], SB[c][kb], qs[c]);
-      }
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U[c][rt][i] = wv[c][rt][i] - ws[c][i];
-      O[c][rt] = qs[c];
-    }
-    hook(rt);
-  }
-  FragT UB[CT][NKC];
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) UB[c][kb] = Frag<T>::from_acc(U[c], kb);
-  if (WITH_O) {
+    for (int kb = 0; kb < NKD; ++kb) a[0][kb] = colfrag<C>(sW, kb * KB, 0, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      FragT ap[NKC];
+      if (rt + 1 < 4) {
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb)
-        if (kb * KB <= 16 * rt + 15) ap[kb] = src.p(rt, kb);
+        for (int kb = 0; kb < NKD; ++kb) a[(rt + 1) & 1][kb] = colfrag<C>(sW, kb * KB, 16 * (rt + 1), lane);
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb)
-        if (kb * KB <= 16 * rt + 15) {
-#pragma unroll
-          for (int c = 0; c < CT; ++c) O[c][rt] = mma(ap[kb], UB[c][kb], O[c][rt]);
-        }
+      for (int kb = 0; kb < NKD; ++kb) acc = mma(a[rt & 1][kb], SB[kb], acc);
+      U[rt] = Wv[rt] - acc;
     }
   }
+  FragT UB[NKC];
 #pragma unroll
-  for (int rr = 0; rr < NR; ++rr) {
-    FragT ak[NKC];
+  for (int kb = 0; kb < NKC; ++kb) UB[kb] = Frag<T>::from_acc(U, kb);
+  // O^T = S^T Qt^T + U^T P^T, one token tile at a time
+  {
+    FragT q[2][NKD], pf[2][NKC];
+    auto fetch = [&](int rt, FragT (&qq)[NKD], FragT (&pp)[NKC]) {
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) ak[kb] = src.k(rr, kb);
-    const f32x4 gm = src.gam(rr);
+      for (int kb = 0; kb < NKD; ++kb) qq[kb] = rowfrag<D>(sQ, 16 * rt + i, kb * KB, g);
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb)
+      for (int kb = 0; kb < NKC; ++kb)
+        if (kb * KB <= 16 * rt + 15) pp[kb] = pfrag<T, D>(smem, rt, kb, lane);
+    };
+    fetch(0, q[0], pf[0]);
 #pragma unroll
-      for (int c = 0; c < CT; ++c) S[c][rr] = mma(ak[kb], UB[c][kb], S[c][rr]);
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt + 1 < 4) fetch(rt + 1, q[(rt + 1) & 1], pf[(rt + 1) & 1]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+      for (int kb = 0; kb < NKD; ++kb) acc = mma(SB[kb], q[rt & 1][kb], acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[c][rr][i] *= gm[i];
-    hook(4 + rr);
+      for (int kb = 0; kb < NKC; ++kb)
+        if (kb * KB <= 16 * rt + 15) acc = mma(UB[kb], pf[rt & 1][kb], acc);
+      if (16 * rt + i < clen) {
+        T* dst = o + ((size_t)(tokc + 16 * rt + i) * H + h) * D + 16 * w + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          const uint2 p = __builtin_bit_cast(uint2, to_bf16x4(acc));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x2nt, p), (u32x2nt*)dst);
+        } else {
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4nt, acc), (u32x4nt*)dst);
+        }
+      }
+    }
+  }
+  // S <- diag(gamma) (S + Kh^T U), two row tiles at a time
+  {
+    FragT a[2][2][NKC];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) a[0][r][kb] = colfrag<D>(sH, kb * KB, 16 * r, lane);
+#pragma unroll
+    for (int rp = 0; rp < NR / 2; ++rp) {
+      if (rp + 1 < NR / 2) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int kb = 0; kb < NKC; ++kb)
+            a[(rp + 1) & 1][r][kb] = colfrag<D>(sH, kb * KB, 16 * (2 * rp + 2 + r), lane);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int rr = 2 * rp + r;
+#pragma unroll
+        for (int kb = 0; kb < NKC; ++kb) S[rr] = mma(a[rp & 1][r][kb], UB[kb], S[rr]);
+        S[rr] = S[rr] * *(const f32x4*)(sG + 16 * rr + 4 * g);
+      }
+    }
   }
 }
 
-// The segment map in the segment record (Rec): B from each wave's accumulator
-// tiles, M through LDS (sM, [D][D + 4] fp32) into the scan's A-operand
-// fragments.  wave owns the column tiles cols[x] of B (XB[x]) and of M (XM[x]).
-template <typename T, int D, int NW, int NC>
-__device__ __forceinline__ void save_map(float* sM, float* recs, const f32x4 (&XB)[NC][D / 16],
-                                         const f32x4 (&XM)[NC][D / 16], const int (&cols)[NC], int wave,
-                                         int lane) {
-  typedef Rec<T, D> R;
-  constexpr int NR = D / 16, LDM = D + 4;
-  const int idx = lane & 15, gq = lane >> 4;
+// The map sweep's step: B (from 0) and M (from I, value part of U off).
+template <typename T, int D>
+__device__ __forceinline__ void state_map(const unsigned char* smem, int buf, f32x4 (&B)[D / 16],
+                                          f32x4 (&M)[D / 16], const f32x4 (&Wv)[4], int lane) {
+  typedef Lay<T, D, false> Y;
+  typedef typename Frag<T>::type FragT;
+  constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
+  const T* sH = (const T*)(smem + Y::kh(buf));
+  const T* sW = (const T*)(smem + Y::WKT);
+  const float* sG = (const float*)(smem + Y::gam(buf));
+  const int g = lane >> 4;
+  FragT BB[NKD], MB[NKD];
 #pragma unroll
-  for (int x = 0; x < NC; ++x)
+  for (int kb = 0; kb < NKD; ++kb) {
+    BB[kb] = Frag<T>::from_acc(B, kb);
+    MB[kb] = Frag<T>::from_acc(M, kb);
+  }
+  f32x4 UBt[4], UMt[4];
+  {
+    FragT a[2][NKD];
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) a[0][kb] = colfrag<C>(sW, kb * KB, 0, lane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt + 1 < 4) {
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) a[(rt + 1) & 1][kb] = colfrag<C>(sW, kb * KB, 16 * (rt + 1), lane);
+      }
+      f32x4 ab = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKD; ++kb) {
+        ab = mma(a[rt & 1][kb], BB[kb], ab);
+        am = mma(a[rt & 1][kb], MB[kb], am);
+      }
+      UBt[rt] = Wv[rt] - ab;
+      UMt[rt] = -am;
+    }
+  }
+  FragT UB[NKC], UM[NKC];
+#pragma unroll
+  for (int kb = 0; kb < NKC; ++kb) {
+    UB[kb] = Frag<T>::from_acc(UBt, kb);
+    UM[kb] = Frag<T>::from_acc(UMt, kb);
+  }
+  {
+    FragT a[2][NKC];
+#pragma unroll
+    for (int kb = 0; kb < NKC; ++kb) a[0][kb] = colfrag<D>(sH, kb * KB, 0, lane);
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
-      *(f32x4*)(recs + R::B + R::tile(rr, cols[x], lane)) = XB[x][rr];
+      if (rr + 1 < NR) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sM[(16 * rr + 4 * gq + i) * LDM + 16 * cols[x] + idx] = XM[x][rr][i];
+        for (int kb = 0; kb < NKC; ++kb) a[(rr + 1) & 1][kb] = colfrag<D>(sH, kb * KB, 16 * (rr + 1), lane);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) {
+        B[rr] = mma(a[rr & 1][kb], UB[kb], B[rr]);
+        M[rr] = mma(a[rr & 1][kb], UM[kb], M[rr]);
+      }
+      const f32x4 gm = *(const f32x4*)(sG + 16 * rr + 4 * g);
+      B[rr] = B[rr] * gm;
+      M[rr] = M[rr] * gm;
     }
+  }
+}
+
+// The segment map to its record: B from each wave's accumulator tiles, M
+// through LDS (sM, [D][D + 4] fp32) into the scan's A-operand fragments.
+template <typename T, int D>
+__device__ __forceinline__ void save_map(float* sM, float* recs, const f32x4 (&XB)[D / 16], const f32x4 (&XM)[D / 16],
+                                         int wave, int lane) {
+  typedef Rec<T, D> R;
+  constexpr int NR = D / 16, NW = D / 16, LDM = D + 4;
+  const int idx = lane & 15, gq = lane >> 4;
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    *(f32x4*)(recs + R::B + R::tile(rr, wave, lane)) = XB[rr];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sM[(16 * rr + 4 * gq + e) * LDM + 16 * wave + idx] = XM[rr][e];
+  }
   __syncthreads();
   unsigned char* mf = (unsigned char*)(recs + R::M);
   for (int f = wave; f < NR * R::NKB; f += NW) {
@@ -1064,271 +906,118 @@ __device__ __forceinline__ void save_map(float* sM, float* recs, const f32x4 (&X
   }
 }
 
-// ---- pass 1: the chunk-local part of every chunk -> its record -----------
-// One workgroup per (group of L consecutive chunks of a sequence, head)
-// walks its chunks; the inputs of the next chunk are fetched while the
-// current one is finished.  Wave w forms Wk and Wv for the value-column tiles
-// w + NW x.
-// With MAPS the groups are the segments of the state passes, and the
-// workgroup also composes its segment's affine map S_out = M S_in + B (not
-// for the last segment of a sequence: no later segment needs it): after each
-// chunk's W products it takes the chunk's Wk, Kh^T, gamma and Wv, still in
-// LDS and registers, through a state step on B (started from 0) and on M
-// (started from I, value part of U off), wave w on the column tiles it owns.
-// Without MAPS (every sequence is one segment) the group length is the chunk
-// pass's own.
-template <typename T, int D, int NW, bool MAPS, bool MX>
-__global__ void __launch_bounds__(64 * NW)
-kda_chunk_prep(const ChunkInputs in, const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
-               float g_floor, int gate, unsigned char* __restrict__ crec, float* __restrict__ ws) {
-  typedef Lds<T, D> M;
-  typedef CRec<T, D> CR;
-  constexpr int NT = 64 * NW, NR = D / 16, NV = NR / NW;
-  static_assert(NV >= 1 && NV * NW == NR, "waves must split the value columns");
-  static_assert(D * (D + 4) * 4 <= M::BYTES, "M staging fits the chunk pass's LDS");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[M::BYTES];
+// ---- the sweeps -------------------------------------------------------------
+// One workgroup per (segment, head); wave w owns value-column tile w.  The
+// output sweep (OUT) starts from the segment's S_in (with maps) or h0, writes
+// o, the final state (last segment) and, with `states`, the state after
+// every `every`-th full chunk of a sequence to its slot (the prefix-cache
+// states of kda_chunk_forward_states).  The map sweep starts B from 0 and M
+// from I and writes the segment's record; the last segment of a sequence has
+// no map and exits.
+template <typename T, int D, bool OUT, bool MX>
+__global__ void __launch_bounds__(64 * (D / 16))
+kda_chunk_sweep(const ChunkInputs in, const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs, int n_rows,
+                int T_per, int H, int L, int maps, float g_floor, int gate, float* __restrict__ ws, const float* h0,
+                T* __restrict__ o, float* ht, float* __restrict__ states, int every) {
+  typedef Lay<T, D, OUT> Y;
+  typedef Rec<T, D> R;
+  constexpr int NW = D / 16, NR = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Y::BYTES];
+  const int64_t period = (OUT && states) ? (int64_t)C * every : 0;
   Seg sg;
-  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
+  if (!locate(cu, seqs, n_rows, T_per, L, period, blockIdx.x, sg)) return;
+  if (!OUT && sg.s == sg.nseg - 1) return;
   const int h = blockIdx.y, tid0 = threadIdx.x, lane0 = tid0 & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // uniform: scalar control flow
-  const int idx = lane0 & 15, gq = lane0 >> 4;
+  const int g = lane0 >> 4, i = lane0 & 15;
   const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
-  const bool maps = MAPS && sg.s < sg.nseg - 1;
-  int cts[NV];
+  float* rec = ws + ((size_t)blockIdx.x * H + h) * R::FLOATS;
+  // OUT: X[0] = S.  Map sweep: X[0] = B, X[1] = M.
+  f32x4 X[OUT ? 1 : 2][NR];
+  if (OUT) {
+    const float* h0p = h0 ? h0 + ((size_t)sg.n * H + h) * D * D : nullptr;
 #pragma unroll
-  for (int x = 0; x < NV; ++x) cts[x] = wave + NW * x;
-  // the segment map's column tiles cts[x]: B in X[x], M in X[NV + x]
-  f32x4 X[MAPS ? 2 * NV : 1][NR];
-  if (MAPS) {
+    for (int rr = 0; rr < NR; ++rr) {
+      if (maps) {
+        X[0][rr] = *(const f32x4*)(rec + R::SIN + R::tile(rr, wave, lane0));
+      } else {
 #pragma unroll
-    for (int x = 0; x < NV; ++x)
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          X[x][rr][i] = 0.f;
-          X[NV + x][rr][i] = (16 * rr + 4 * gq + i == 16 * cts[x] + idx) ? 1.f : 0.f;
-        }
-  }
-
-  {
-    Raw<T, D, NT, true, MX> first;
-    first.load(in, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0, gate);
-    first.store(smem, tid0);
-  }
-  __syncthreads();
-  for (int j = j0; j < j1; ++j) {
-    // With MAPS (the map's state tiles take 64 registers), thread and lane
-    // index as opaque per-chunk values: the addresses derived from them are
-    // formed inside the loop, not hoisted and held across it, which would
-    // overflow the registers.
-    int tid = tid0, lane = lane0;
-    if (MAPS) asm volatile("" : "+v"(tid), "+v"(lane));
-    elementwise<T, D, NW, true>(smem, g_floor, tid);
-    // the next chunk's inputs are fetched while this one is worked on: q, k,
-    // g and beta now (into LDS once Wk is complete), v now as well, or with
-    // MAPS (short of registers) once Wk is complete, the map's state step
-    // covering its latency (into LDS at the end of the chunk)
-    Raw<T, D, NT, true, MX> raw;
-    const bool more = j + 1 < j1;
-    const int64_t tok_n = sg.tok0 + (int64_t)C * (j + 1);
-    const int len_n = min(C, sg.len - C * (j + 1));
-    if (more) {
-      raw.load_qkg(in, tok_n, len_n, H, h, tid, gate);
-      if (!MAPS) raw.load_v(in, tok_n, len_n, H, h, tid);
-    }
-    gram<T, D, NW, true>(smem, wave, lane);  // also the diagonal-block inverses
-    unsigned char* cr = crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES;
-    // waves 0-3 form Tp; with eight waves the other four meanwhile write the
-    // record parts that are already final
-    if (wave < 4) inverse_cols<T, D>(smem, wave, lane);
-    if (NW > 4 && wave >= 4) save_early<T, D>(smem, cr, wave - 4, NW - 4, lane);
-    if (NW <= 4) save_early<T, D>(smem, cr, wave, NW, lane);
-    __syncthreads();  // Tp complete; A and the diagonal inverses are dead
-    // Wk and Wv in one pass over Tp: operands x < NV are Kt^T column tiles,
-    // the others V^T tiles
-    const T* xo[2 * NV];
-    int co[2 * NV];
-#pragma unroll
-    for (int x = 0; x < NV; ++x) {
-      xo[x] = (const T*)(smem + M::KT);
-      xo[NV + x] = (const T*)(smem + M::VT);
-      co[x] = co[NV + x] = cts[x];
-    }
-    f32x4 wvt[NV][4];
-    {
-      f32x4 w[2 * NV][4];
-      w_products<T, D, 2 * NV>(smem, xo, co, lane, w);
-#pragma unroll
-      for (int x = 0; x < NV; ++x) {
-        store_wk<T, D, M::V>(smem, w[x], cts[x], lane);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wvt[x][rt] = w[NV + x][rt];
+        for (int e = 0; e < 4; ++e) X[0][rr][e] = h0p ? h0p[(16 * rr + 4 * g + e) * D + 16 * wave + i] : 0.f;
       }
     }
-    __syncthreads();  // Wk complete; Tp, Qt, Kh and beta are dead
-    // the next chunk's q, k, g and beta go to their areas now (v's area holds
-    // Wk until the end of the chunk).  With MAPS, v is fetched only after
-    // that store: the store's wait for q, k and g would otherwise cover the v
-    // loads too (loads complete in order), leaving no time to hide them.
-    if (more) {
-      raw.store_qkg(smem, tid);
-      if (MAPS) raw.load_v(in, tok_n, len_n, H, h, tid);
-    }
-    save_wk<T, D, M::V>(smem, cr, wave, NW, lane);
+  } else {
 #pragma unroll
-    for (int x = 0; x < NV; ++x)
+    for (int rr = 0; rr < NR; ++rr)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) CR::put_wv(cr + CR::wv(cts[x], rt, lane), wvt[x][rt]);
-    if (maps) {
-      // Wv as the record holds it, so that the map and the output pass see
-      // the same chunk
-      f32x4 wvx[MAPS ? 2 * NV : 1][4], unused[MAPS ? 2 * NV : 1][4];
-#pragma unroll
-      for (int x = 0; x < NV; ++x)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          wvx[x][rt] = CR::as_stored(wvt[x][rt]);
-          wvx[NV + x][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
-      state_step<T, D, MAPS ? 2 * NV : 1, false>(LdsSrc<T, D, M::V>{smem, lane}, X, wvx, unused, lane,
-                                                  [](int) {});
-    }
-    __syncthreads();  // done with this chunk's LDS
-    if (more) {
-      raw.store_v(smem, tid);
-      __syncthreads();
-    }
-  }
-  if (maps) {
-    f32x4 XB[NV][NR], XM[NV][NR];
-#pragma unroll
-    for (int x = 0; x < NV; ++x)
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr) {
-        XB[x][rr] = X[x][rr];
-        XM[x][rr] = X[MAPS ? NV + x : 0][rr];
+      for (int e = 0; e < 4; ++e) {
+        X[0][rr][e] = 0.f;
+        X[OUT ? 0 : 1][rr][e] = (16 * rr + 4 * g + e == 16 * wave + i) ? 1.f : 0.f;
       }
-    save_map<T, D, NW, NV>((float*)smem, ws + ((size_t)blockIdx.x * H + h) * Rec<T, D>::FLOATS, XB, XM, cts,
-                           wave, lane0);
   }
-}
-
-// ---- pass 3: outputs from every segment's incoming state -----------------
-// Reads the chunk records into two LDS image buffers; wave w owns the
-// value-column tiles w + NW x, x < CT.  O is staged at the start of the
-// current image (Wk and Kh^T fragments, dead after the products) so that the
-// global stores are whole 16-byte pieces of rows.  The next chunk's image is
-// issued piecewise between the row blocks of the state step.  With `states`,
-// the state after every `every`-th full chunk of a sequence goes to its slot
-// (the prefix-cache states of kda_chunk_forward_states).
-template <typename T, int D, int NW, int CT>
-__global__ void __launch_bounds__(64 * NW)
-kda_seg_forward(const int32_t* __restrict__ cu, int n_rows, int T_per, int H, int L,
-                const float* __restrict__ ws, const unsigned char* __restrict__ crec, T* __restrict__ o,
-                float* ht, float* __restrict__ states, int every) {
-  typedef Lds<T, D> M;
-  typedef CRec<T, D> CR;
-  typedef Img<T, D> I;
-  constexpr int NT = 64 * NW, NR = D / 16;
-  static_assert(NW * CT == NR, "waves must split the value columns");
-  static_assert(M::ROW_T <= I::GAM, "O staging fits the Wk and Kh^T fragments");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * I::BYTES];
-  Seg sg;
-  if (!locate(cu, n_rows, T_per, L, blockIdx.x, sg)) return;
-  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control flow
-  const int idx = lane & 15, gq = lane >> 4;
-  const int nch = (sg.len + C - 1) / C, j0 = sg.s * L, j1 = min(j0 + L, nch);
-  auto rec = [&](int j) -> const unsigned char* { return crec + ((size_t)(sg.chunk0 + j) * H + h) * CR::BYTES; };
-  typedef typename CR::WvRaw WvRaw;
-  auto load_wv = [&](int j, WvRaw (&w)[CT][4]) {
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) w[c][rt] = CR::load_wv(rec(j) + CR::wv(wave + NW * c, rt, lane));
-  };
-
-  constexpr int NP = 4 + NR;  // hook points of a state step
-  for (int k = 0; k < NP; ++k) issue_image<NW, I::BYTES, NP>(smem, rec(j0), wave, lane, k);
-  WvRaw wv[CT][4];
-  load_wv(j0, wv);
-  typedef Rec<T, D> R;
-  const float* sin = ws + ((size_t)(blockIdx.x) * H + h) * R::FLOATS + R::SIN;
-  f32x4 S[CT][NR];
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int rr = 0; rr < NR; ++rr) S[c][rr] = *(const f32x4*)(sin + R::tile(rr, wave + NW * c, lane));
-  // this wave's columns of S, row-major [D][D] at dst (ht and the states)
   auto put_state = [&](float* dst) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+    for (int rr = 0; rr < NR; ++rr)
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * rr + 4 * gq + i) * D + 16 * (wave + NW * c) + idx] = S[c][rr][i];
+      for (int e = 0; e < 4; ++e) dst[(16 * rr + 4 * g + e) * D + 16 * wave + i] = X[0][rr][e];
   };
-  // first state slot of this sequence: full state periods of the earlier ones
-  const int64_t period = (int64_t)C * every;
-  int64_t slot0 = 0;
-  if (states) {
-    if (cu) {
-      for (int m = 0; m < sg.n; ++m) slot0 += (cu[m + 1] - cu[m]) / period;
-    } else {
-      slot0 = (int64_t)sg.n * (T_per / period);
-    }
-  }
 
-  for (int j = j0; j < j1; ++j) {
-    const int clen = min(C, sg.len - C * j);
-    const int64_t tokc = sg.tok0 + (int64_t)C * j;
-    unsigned char* cur = smem + ((j - j0) & 1) * I::BYTES;
-    unsigned char* nxt = smem + ((j + 1 - j0) & 1) * I::BYTES;
-    vmcnt_wait_all();
-    __syncthreads();  // image j in LDS; every wave is done with the other buffer
-    WvRaw wvn[CT][4];
-    const bool more = j + 1 < j1;
-    if (more) load_wv(j + 1, wvn);
-    f32x4 wvf[CT][4];
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) wvf[c][rt] = CR::widen(wv[c][rt]);
-    f32x4 O[CT][4];
-    state_step<T, D, CT, true>(ImgSrc<T, D>{cur, lane}, S, wvf, O, lane, [&](int k) {
-      if (more) issue_image<NW, I::BYTES, NP>(nxt, rec(j + 1), wave, lane, k);
-    });
-    lds_barrier();  // every wave is done with the Wk and Kh^T fragments
-    T* sO = (T*)cur;
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sO[(16 * rt + 4 * gq + i) * M::LDT + 16 * (wave + NW * c) + idx] = Elem<T>::from_f32(O[c][rt][i]);
-    lds_barrier();
-    Raw<T, D, NT, true>::store_out(cur, o, tokc, clen, H, h, tid);
-    if (states && (j + 1) % every == 0 && (int64_t)(j + 1) * C <= sg.len)
-      put_state(states + ((size_t)(slot0 + (j + 1) / every - 1) * H + h) * D * D);
-    if (j + 1 < j1) {
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wv[c][rt] = wvn[c][rt];
+  Raw<T, D, OUT, MX, OUT> raw;
+  raw.load(in, sg.tok0 + (int64_t)C * j0, min(C, sg.len - C * j0), H, h, tid0, gate);
+  // The state step of chunk j - 1 runs in the same barrier interval as the
+  // element-wise stage of chunk j (which writes the other buffer set): waves
+  // 0-3 take the element-wise stage first, waves 4-7 the state step, so that
+  // the two waves sharing a SIMD feed its VALU and its matrix core at once.
+  f32x4 Wv[4];
+  auto state = [&](int jj, int lane) {
+    const int buf = (jj - j0) & 1;
+    if constexpr (OUT) {
+      state_out<T, D>(smem, buf, X[0], Wv, wave, lane, o, sg.tok0 + (int64_t)C * jj, min(C, sg.len - C * jj), H, h);
+      if (states && (jj + 1) % every == 0 && (int64_t)(jj + 1) * C <= sg.len)
+        put_state(states + ((size_t)(sg.slot0 + (jj + 1) / every - 1) * H + h) * D * D);
+    } else {
+      state_map<T, D>(smem, buf, X[0], X[OUT ? 0 : 1], Wv, lane);
     }
+  };
+  for (int j = j0; j < j1; ++j) {
+    const int64_t tokc = sg.tok0 + (int64_t)C * j;
+    const int buf = (j - j0) & 1;
+    // thread and lane index as opaque per-chunk values: the LDS addresses
+    // derived from them are formed inside the loop, not hoisted and held
+    // across it, which would overflow the registers
+    int tid = tid0, lane = lane0;
+    asm volatile("" : "+v"(tid), "+v"(lane));
+    float g0[8], g1[8];
+    estage1<T, D, OUT, MX, OUT>(smem, raw, g_floor, gate, tid, g0, g1);
+    lds_barrier();  // partial sums visible; the previous chunk's local stages are done
+    const bool prev = Y::OVL && j > j0;
+    if (prev && wave >= 4) state(j - 1, lane);
+    estage2<T, D, OUT, MX, OUT>(smem, buf, raw, tid, g0, g1);
+    if (j + 1 < j1) raw.load(in, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid, gate);
+    if (prev && wave < 4) state(j - 1, lane);
+    lds_barrier();
+    gram_stage<T, D, OUT>(smem, buf, wave, lane);
+    lds_barrier();
+    substitute<T, D, OUT>(smem, wave, lane, Wv);
+    lds_barrier();
+    if (!Y::OVL) state(j, lane);
   }
-  if (ht && sg.s == sg.nseg - 1) put_state(ht + ((size_t)sg.n * H + h) * D * D);
+  if (Y::OVL && j1 > j0) state(j1 - 1, lane0);
+  if constexpr (OUT) {
+    if (ht && sg.s == sg.nseg - 1) put_state(ht + ((size_t)sg.n * H + h) * D * D);
+  } else {
+    __syncthreads();  // every wave is done with the last chunk's LDS
+    save_map<T, D>((float*)smem, rec, X[0], X[1], wave, lane0);
+  }
 }
 
-// ---- pass 2: segment scan S_{s+1} = M_s S_s + B_s ------------------------
+// ---- segment scan S_{s+1} = M_s S_s + B_s -------------------------------------
 // Workgroup = (sequence, head, 16 state columns), one wave per 16-row tile of
 // S.  Each step a wave publishes its rows as halves of B-operand fragments
 // through a double-buffered LDS area and forms the same rows of the next state
 // from all k-blocks, so one barrier per step orders the exchange.  M_s and
 // B_s do not depend on the state: each wave fetches its rows of them three
-// steps ahead.
+// steps ahead.  Without maps (one segment per sequence) the launch only gives
+// empty sequences their final state (h0, or zero).
 template <typename T, int D> struct ScanOps;
 template <int D> struct ScanOps<bf16_t, D> {
   static constexpr int KB = 32, NKB = D / KB;
@@ -1338,13 +1027,17 @@ template <int D> struct ScanOps<bf16_t, D> {
   __device__ static __forceinline__ void publish(PubArea& a, int t, int lane, const f32x4& x) {
     const s16x4 h = to_bf16x4(x);
     *((uint2*)&a[0][t >> 1][lane] + (t & 1)) = __builtin_bit_cast(uint2, h);
-    *((uint2*)&a[1][t >> 1][lane] + (t & 1)) = __builtin_bit_cast(uint2, to_bf16x4(x - from_bf16x4(h)));
+    *((uint2*)&a[1][t >> 1][lane] + (t & 1)) = __builtin_bit_cast(uint2, to_bf16x4(x - widen4(h)));
   }
-  struct SFrag { bf16x8 hi, lo; };
+  struct SFrag {
+    bf16x8 hi, lo;
+  };
   __device__ static __forceinline__ SFrag gather(const PubArea& a, int kb, int lane) {
     return SFrag{__builtin_bit_cast(bf16x8, a[0][kb][lane]), __builtin_bit_cast(bf16x8, a[1][kb][lane])};
   }
-  struct MRaw { bf16x8 hi, lo; };
+  struct MRaw {
+    bf16x8 hi, lo;
+  };
   // k-block kb of this lane's M rows; off: byte offset of its (kb = 0, hi)
   // fragment in the segment record
   __device__ static __forceinline__ MRaw load_m(__amdgpu_buffer_rsrc_t r, uint32_t off, int kb) {
@@ -1377,10 +1070,10 @@ template <int D> struct ScanOps<float, D> {
 
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * (D / 16))
-kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* __restrict__ cu, int n_rows,
-             int T_per, int H, int L) {
+kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* __restrict__ cu,
+             const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, int L, int maps) {
   typedef ScanOps<T, D> Ops;
-  constexpr int NKB = Ops::NKB, NWS = D / 16, WPP = D / 16;
+  constexpr int NKB = Ops::NKB, WPP = D / 16;
   __shared__ typename Ops::PubArea sS[2];  // published state, double-buffered
   const int n_pairs = n_rows * H;
   // XCD-aware order: the WPP workgroups of one (sequence, head) get ids with
@@ -1393,10 +1086,10 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   const int lane = threadIdx.x & 63, idx = lane & 15, gq = lane >> 4;
   const int col = 16 * ct + idx;
 
-  int64_t base = 0;
+  int64_t base;
   int len;
   if (cu) {
-    for (int m = 0; m < n; ++m) base += n_segments(cu[m + 1] - cu[m], L);
+    base = seqs[n];
     len = cu[n + 1] - cu[n];
   } else {
     base = (int64_t)n * n_segments(T_per, L);
@@ -1406,18 +1099,19 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
 
   f32x4 Sk;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) Sk[i] = h0 ? h0[((size_t)p * D + 16 * wave + 4 * gq + i) * D + col] : 0.f;
-  typedef Rec<T, D> R;
-  auto rec = [&](int s) -> float* { return ws + ((size_t)(base + s) * H + h) * R::FLOATS; };
-  auto put = [&](float* dst) { *(f32x4*)(dst + R::tile(wave, ct, lane)) = Sk; };  // accumulator tile order
+  for (int e = 0; e < 4; ++e) Sk[e] = h0 ? h0[((size_t)p * D + 16 * wave + 4 * gq + e) * D + col] : 0.f;
   if (nseg == 0) {
     if (ht) {
       float* dst = ht + (size_t)p * D * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * wave + 4 * gq + i) * D + col] = Sk[i];
+      for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * gq + e) * D + col] = Sk[e];
     }
     return;
   }
+  if (!maps) return;
+  typedef Rec<T, D> R;
+  auto rec = [&](int s) -> float* { return ws + ((size_t)(base + s) * H + h) * R::FLOATS; };
+  auto put = [&](float* dst) { *(f32x4*)(dst + R::tile(wave, ct, lane)) = Sk; };  // accumulator tile order
   put(rec(0) + R::SIN);
   struct Stage {
     typename Ops::MRaw m[NKB];
@@ -1425,8 +1119,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   };
   // Buffer loads: a step's record is one scalar resource, the lanes' byte
   // offsets into it fixed registers, so the fetches take no per-lane address
-  // registers (64-bit address temporaries were placed over registers still
-  // being loaded, which made every fetch wait for the ones in flight).
+  // registers.
   const uint32_t m_off = (uint32_t)(R::M * 4 + R::frag(wave, 0, 0, lane));
   const uint32_t b_off = (uint32_t)((R::B + R::tile(wave, ct, lane)) * 4);
   constexpr int kRecBytes = (int)(R::FLOATS * 4), kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
@@ -1435,9 +1128,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) st.m[kb] = Ops::load_m(r, m_off, kb);
     st.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, b_off, 0, 0));
-    // issued here, before the step's own temporaries are allocated (moved
-    // below them, a load's target registers were handed out as temporaries,
-    // whose writes then wait for the load)
+    // issued here, before the step's own temporaries are allocated
     __builtin_amdgcn_sched_barrier(0);
   };
   auto step = [&](int s, const Stage& st) {
@@ -1457,14 +1148,9 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   const int nsteps = nseg - 1;
   if (nsteps == 0) return;
   // Fetches past the last step re-read the last step's record (in bounds,
-  // unused): unconditional loads keep the wait counts exact, so a step waits
-  // only for its own stage and never for the fetches issued after it.  A ring
-  // of three register stages (the loop unrolled by three, so that the stages
-  // never move between registers).
+  // unused): unconditional loads keep the wait counts exact.  A ring of three
+  // register stages, unrolled by six.
   auto clamp = [&](int s) { return s < nsteps ? s : nsteps - 1; };
-  // Unrolled by six (two turns of the ring), so that the conservative wait
-  // after the loop head (where the pending loads of the two incoming paths are
-  // merged) falls on one step in six.
   Stage b0, b1, b2;
   fetch(0, b0);
   fetch(clamp(1), b1);
@@ -1489,75 +1175,78 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   }
 }
 
-// MXFP8 inputs are decoded into the bf16 path (the fp32 path takes none).
-template <typename T, int D> struct MxOk { static constexpr bool value = sizeof(T) == 2 && D % 32 == 0; };
-
-template <typename T, int D, int NW, int NW2>
+// ---- launch ---------------------------------------------------------------------
+template <typename T, int D>
 int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floor, int gate, const ChunkInputs& in,
                  const float* h0, const int32_t* cu, void* o, float* ht, float* states, int every, void* ws,
                  hipStream_t stream, void* const* events) {
-  constexpr int NR = D / 16;
-  const int L = plan.seg_chunks;
+  constexpr int NT = 64 * (D / 16);
+  const int L = plan.seg_chunks, maps = plan.maps ? 1 : 0;
   float* wsf = (float*)ws;
-  unsigned char* crec = (unsigned char*)ws + plan.crec_off;
-  if (plan.crec_bytes != CRec<T, D>::BYTES) return (int)hipErrorInvalidValue;
-  if (in.qs && !MxOk<T, D>::value) return (int)hipErrorInvalidValue;  // MXFP8 inputs: bf16 path only
-  const bool has_segments = plan.n_seg_bound > 0;
+  int64_t* seqs = cu ? (int64_t*)((unsigned char*)ws + plan.seq_off) : nullptr;
+  const int64_t period = states ? (int64_t)C * every : 0;
+  const bool mx = in.qs != nullptr;
+  if (plan.rec_bytes != Rec<T, D>::FLOATS * sizeof(float)) return (int)hipErrorInvalidValue;
+  if (mx && sizeof(T) != 2) return (int)hipErrorInvalidValue;  // MXFP8 inputs: bf16 path only
   hipError_t e;
   auto mark = [&](int i) -> hipError_t {
     return (events && events[i]) ? hipEventRecord((hipEvent_t)events[i], stream) : hipSuccess;
   };
+  const dim3 sweep_grid((unsigned)plan.n_seg_bound, H), sweep_block(NT);
   if ((e = mark(0)) != hipSuccess) return (int)e;
-  if (has_segments) {
-    const bool mx = in.qs != nullptr;
-    const unsigned grid = (unsigned)(plan.maps_in_prep ? plan.n_seg_bound : plan.n_prep_bound);
-    const int gl = plan.maps_in_prep ? L : plan.prep_chunks;
-    const dim3 g3(grid, H), b3(64 * NW);
-    if (plan.maps_in_prep && mx)
-      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true, MxOk<T, D>::value>), g3, b3, 0, stream, in, cu, n_rows,
-                         T_per, H, gl, g_floor, gate, crec, wsf);
-    else if (plan.maps_in_prep)
-      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, true, false>), g3, b3, 0, stream, in, cu, n_rows, T_per, H, gl,
-                         g_floor, gate, crec, wsf);
-    else if (mx)
-      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false, MxOk<T, D>::value>), g3, b3, 0, stream, in, cu, n_rows,
-                         T_per, H, gl, g_floor, gate, crec, wsf);
-    else
-      hipLaunchKernelGGL((kda_chunk_prep<T, D, NW, false, false>), g3, b3, 0, stream, in, cu, n_rows, T_per, H, gl,
-                         g_floor, gate, crec, wsf);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if (cu && n_rows > 0 && (e = launch_kernel(kda_fwd_seqs, dim3(1), dim3(256), stream, cu, n_rows, L, period, seqs)) != hipSuccess)
+    return (int)e;
+  if (maps && plan.n_seg_bound > 0) {
+    e = mx ? launch_kernel(kda_chunk_sweep<T, D, false, sizeof(T) == 2>, sweep_grid, sweep_block, stream, in, cu,
+                           (const int64_t*)seqs, n_rows, T_per, H, L, maps, g_floor, gate, wsf, h0, (T*)o, ht, states,
+                           every)
+           : launch_kernel(kda_chunk_sweep<T, D, false, false>, sweep_grid, sweep_block, stream, in, cu,
+                           (const int64_t*)seqs, n_rows, T_per, H, L, maps, g_floor, gate, wsf, h0, (T*)o, ht, states,
+                           every);
+    if (e != hipSuccess) return (int)e;
   }
   if ((e = mark(1)) != hipSuccess) return (int)e;
-  const int64_t pairs = (int64_t)n_rows * H;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * NR;
-  hipLaunchKernelGGL((kda_seg_scan<T, D>), dim3((unsigned)blocks), dim3(64 * (D / 16)), 0, stream,
-                     h0, ht, wsf, cu, n_rows, T_per, H, L);
-  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if (maps || cu || T_per == 0) {
+    const int64_t blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
+    if ((e = launch_kernel(kda_seg_scan<T, D>, dim3((unsigned)blocks), dim3(NT), stream, h0, ht, wsf, cu,
+                           (const int64_t*)seqs, n_rows, T_per, H, L, maps)) != hipSuccess)
+      return (int)e;
+  }
   if ((e = mark(2)) != hipSuccess) return (int)e;
-  if (has_segments) {
-    hipLaunchKernelGGL((kda_seg_forward<T, D, NW2, NR / NW2>), dim3((unsigned)plan.n_seg_bound, H), dim3(64 * NW2),
-                       0, stream, cu, n_rows, T_per, H, L, (const float*)wsf, (const unsigned char*)crec, (T*)o, ht,
-                       states, every);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if (plan.n_seg_bound > 0) {
+    e = mx ? launch_kernel(kda_chunk_sweep<T, D, true, sizeof(T) == 2>, sweep_grid, sweep_block, stream, in, cu,
+                           (const int64_t*)seqs, n_rows, T_per, H, L, maps, g_floor, gate, wsf, h0, (T*)o, ht, states,
+                           every)
+           : launch_kernel(kda_chunk_sweep<T, D, true, false>, sweep_grid, sweep_block, stream, in, cu,
+                           (const int64_t*)seqs, n_rows, T_per, H, L, maps, g_floor, gate, wsf, h0, (T*)o, ht, states,
+                           every);
+    if (e != hipSuccess) return (int)e;
   }
   return (int)mark(3);
 }
 
 }  // namespace
 
+int device_compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const SegPlan& plan, float g_floor,
                          int gate, const ChunkInputs& in, const float* h0, const int32_t* cu, void* o, float* ht,
                          float* states, int every, void* ws, void* stream, void* const* events) {
   hipStream_t s = (hipStream_t)stream;
   if (is_bf16 && d == 64)
-    return launch_typed<bf16_t, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws,
-                                          s, events);
+    return launch_typed<bf16_t, 64>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws, s,
+                                    events);
   if (is_bf16 && d == 128)
-    return launch_typed<bf16_t, 128, KDA_NW128, KDA_NW128_FWD>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o,
-                                                               ht, states, every, ws, s, events);
+    return launch_typed<bf16_t, 128>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws, s,
+                                     events);
   if (!is_bf16 && d == 64)
-    return launch_typed<float, 64, 4, 4>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws,
-                                         s, events);
+    return launch_typed<float, 64>(n_rows, T, H, plan, g_floor, gate, in, h0, cu, o, ht, states, every, ws, s,
+                                   events);
   return (int)hipErrorInvalidValue;
 }
 

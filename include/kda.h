@@ -37,11 +37,17 @@
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
  *     16-byte aligned.  The caller owns every buffer; the library allocates
  *     nothing, never synchronises, keeps no global state and is reentrant.
- *   - Arguments are validated on the host before any HIP call, so argument
- *     errors come back as status codes even on a machine without a GPU.
+ *   - Arguments are validated on the host before any launch, so argument
+ *     errors come back as status codes even on a machine without a GPU.  The
+ *     only HIP calls before the launches are one device-attribute query
+ *     (the current device's compute units, which the chunked forward's cut
+ *     into segments depends on; 256 when no device answers) and nothing else.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and is asynchronous: results are valid once the caller synchronises.
- *   - A failed launch returns KDA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - A failed launch returns KDA_ERR_HIP: each launch's own status is
+ *     checked (an error that earlier, unrelated HIP calls left on the calling
+ *     thread is neither reported nor cleared).  No C++ exception crosses the
+ *     ABI.
  *   - Log-decays g must be <= 0 (alpha in (0, 1]); the library applies
  *     max(g, g_floor) itself, which is a no-op on inputs already floored.
  *   - NaN or Inf inputs propagate into the outputs; they never fault or hang.
@@ -56,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 10300 /* 1.3.0 */
+#define KDA_VERSION 20000 /* 2.0.0 */
 
 typedef enum {
   KDA_OK = 0,
@@ -70,7 +76,7 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
 
 typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate_t;
 
-/* Shape of one chunked forward call. */
+/* Shape of one chunked forward call (the KDA gate: g per key channel). */
 typedef struct {
   int B;            /* batch; must be 1 when n_seqs > 0                      */
   int T;            /* tokens per batch row (packed total when n_seqs > 0)   */
@@ -81,8 +87,16 @@ typedef struct {
   int n_seqs;       /* 0: B sequences of T tokens; > 0: packed sequences     */
   kda_dtype_t dtype;/* dtype of q, k, v, g and o                             */
   float g_floor;    /* per-step log-decay floor, in [-1, 0), |chunk*floor|<=16 */
-  kda_gate_t gate;  /* layout of g (see the gate variants above)             */
 } kda_chunk_desc_t;
+
+/* The shape and the layout of g, for the entry points that take every gate
+ * variant (kda_chunk_forward_gated and the measurement, prefix-cache, MXFP8
+ * and backward entry points).  gate = KDA_GATE_CHANNEL is kda_chunk_forward's
+ * case exactly. */
+typedef struct {
+  kda_chunk_desc_t shape;
+  kda_gate_t gate;
+} kda_chunk_desc_ex_t;
 
 /* Static, human-readable name of a status code; never NULL. */
 const char* kda_status_string(int status);
@@ -91,9 +105,14 @@ const char* kda_status_string(int status);
 int kda_version(void);
 
 /*
- * Bytes of device workspace that kda_chunk_forward needs for `d`
- * (host-only query, no HIP call).  Returns KDA_OK or KDA_ERR_* for an
- * invalid or unsupported descriptor.
+ * Bytes of device workspace that kda_chunk_forward (and every forward entry
+ * point with the same shape) needs for `d`, on the current device.  No
+ * launch; see the conventions above.  Returns KDA_OK or KDA_ERR_* for an
+ * invalid or unsupported descriptor.  The workspace holds three d_k x d_v
+ * fp32 matrices per (segment, head) when sequences are cut into segments
+ * (192 KiB at d = 128; the cut keeps segments to about one per compute unit
+ * and head, so 48 MiB at H = 16 for T = 4,096 as for T = 1,048,576), and 16
+ * bytes per packed sequence.
  */
 int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
 
@@ -105,12 +124,11 @@ int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
  * and the final state to ht.  Internally the sequence is cut into chunks of
  * `chunk` tokens (restarting at every sequence start; the last chunk may be
  * short): the chunk-local work is dense bf16/fp32 matrix products and a
- * triangular inverse, then the state is carried from chunk to chunk.  The
+ * triangular solve, then the state is carried from chunk to chunk.  The
  * result equals the token-by-token recurrence up to rounding.
  *
  *   q, k    : [B, T, H, d_k]  dtype
- *   g       : [B, T, H, d_k] (KDA_GATE_CHANNEL), [B, T, H] (KDA_GATE_HEAD)
- *             dtype, or NULL (KDA_GATE_NONE)
+ *   g       : [B, T, H, d_k]  dtype, log-decays (natural log) per key channel
  *   v       : [B, T, H, d_v]  dtype
  *   beta    : [B, T, H]       fp32, write strengths in [0, 1]
  *   h0      : [S, H, d_k, d_v] fp32 or NULL (= zero state); S = n_seqs or B
@@ -132,21 +150,36 @@ int kda_chunk_forward(const kda_chunk_desc_t* d,
                       void* stream);
 
 /*
- * Measurement twin of kda_chunk_forward: the same call, and in addition
- * hipEventRecord(events[i], stream) before each of the call's launches and
- * events[3] after the last one.  The launches, in stream order, are
- *   0: chunk pass      (chunk-local operands of every chunk, to the workspace,
- *                       and each segment's affine state map)
- *   1: segment scan    (every segment's incoming state)
- *   2: output pass     (o and the final state)
- * so hipEventElapsedTime(events[i], events[i + 1]) is launch i's time.  A
- * launch with nothing to do (no tokens) is skipped, its events still
- * recorded.  events: 4 hipEvent_t handles created by the caller (any entry
- * may be NULL: not recorded); the array itself must not be NULL.  No
- * synchronisation.  Returns what kda_chunk_forward returns, or
- * KDA_ERR_HIP if recording an event fails.
+ * kda_chunk_forward for every gate variant: d->gate selects the layout of g,
+ *   g : [B, T, H, d_k] (KDA_GATE_CHANNEL), [B, T, H] (KDA_GATE_HEAD) dtype,
+ *       or NULL (KDA_GATE_NONE: not read).
+ * Workspace: kda_chunk_forward_workspace_size(&d->shape).  Everything else
+ * as kda_chunk_forward; with KDA_GATE_CHANNEL the two calls are identical.
  */
-int kda_chunk_forward_timed(const kda_chunk_desc_t* d,
+int kda_chunk_forward_gated(const kda_chunk_desc_ex_t* d,
+                            const void* q, const void* k, const void* v, const void* g,
+                            const float* beta, const float* h0,
+                            const int32_t* cu_seqlens,
+                            void* o, float* ht,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Measurement twin of kda_chunk_forward_gated: the same call, and in
+ * addition hipEventRecord(events[i], stream) before each of the call's
+ * launches and events[3] after the last one.  The launches, in stream order:
+ *   0: map sweep       (each segment's affine state map, from the inputs)
+ *   1: segment scan    (every segment's incoming state)
+ *   2: output sweep    (o, the final state, prefix-cache states)
+ * so hipEventElapsedTime(events[i], events[i + 1]) is launch i's time.  A
+ * launch with nothing to do (no tokens, or one segment per sequence: no maps
+ * to build or chain) is skipped, its events still recorded.  events: 4
+ * hipEvent_t handles created by the caller (any entry may be NULL: not
+ * recorded); the array itself must not be NULL.  No synchronisation.
+ * Returns what kda_chunk_forward_gated returns, or KDA_ERR_HIP if recording
+ * an event fails.
+ */
+int kda_chunk_forward_timed(const kda_chunk_desc_ex_t* d,
                             const void* q, const void* k, const void* v, const void* g,
                             const float* beta, const float* h0,
                             const int32_t* cu_seqlens,
@@ -155,21 +188,21 @@ int kda_chunk_forward_timed(const kda_chunk_desc_t* d,
                             void* stream, void* const* events);
 
 /*
- * kda_chunk_forward with q, k and v in MXFP8 (OCP microscaling): each element
- * is one e4m3 byte (finite-only encoding), and every block of 32 consecutive
- * channels of one (token, head) shares a scale byte s meaning 2^(s - 127)
- * (e8m0; 255 is not allowed).  Element value = e4m3(byte) * 2^(s - 127).
- * The decoded values are exact in bf16, and from there the call is the bf16
- * path: d->dtype must be KDA_DTYPE_BF16, which is the dtype of g and o.
- * (K3 trains with MXFP8 activations: "Kimi K3 技術報告：三個架構改動一次看懂"
- * (akiraxclaw.com), "MoonViT-V2 與低位元訓練也不能省略"; here MXFP8 halves the
- * bytes of q, k and v.)
+ * kda_chunk_forward_gated with q, k and v in MXFP8 (OCP microscaling): each
+ * element is one e4m3 byte (finite-only encoding), and every block of 32
+ * consecutive channels of one (token, head) shares a scale byte s meaning
+ * 2^(s - 127) (e8m0; 255 is not allowed).  Element value = e4m3(byte) *
+ * 2^(s - 127).  The decoded values are exact in bf16, and from there the call
+ * is the bf16 path: d->shape.dtype must be KDA_DTYPE_BF16, which is the dtype
+ * of g and o.  (K3 trains with MXFP8 activations: "Kimi K3 技術報告：三個架構改動
+ * 一次看懂" (akiraxclaw.com), "MoonViT-V2 與低位元訓練也不能省略"; here MXFP8
+ * halves the bytes of q, k and v.)
  *   q, k, v             : [B, T, H, d] e4m3 bytes, 16-byte aligned
  *   q/k/v_scale         : [B, T, H, d / 32] scale bytes
- * Everything else as kda_chunk_forward (same workspace size); the scale
+ * Everything else as kda_chunk_forward_gated (same workspace size); the scale
  * tensors count as inputs in the overlap rules.
  */
-int kda_chunk_forward_mx(const kda_chunk_desc_t* d,
+int kda_chunk_forward_mx(const kda_chunk_desc_ex_t* d,
                          const void* q, const uint8_t* q_scale,
                          const void* k, const uint8_t* k_scale,
                          const void* v, const uint8_t* v_scale,
@@ -191,9 +224,9 @@ int kda_chunk_forward_mx(const kda_chunk_desc_t* d,
  * a fixed-length batch, floor(T / (states_every * chunk)) for a packed one
  * (an upper bound there: the lengths live on the device).
  *
- * kda_chunk_forward_states: kda_chunk_forward, and in addition, for every
- * sequence n in order and every m >= 1 with m * states_every * chunk <=
- * len_n, the state after the first m * states_every * chunk tokens of the
+ * kda_chunk_forward_states: kda_chunk_forward_gated, and in addition, for
+ * every sequence n in order and every m >= 1 with m * states_every * chunk
+ * <= len_n, the state after the first m * states_every * chunk tokens of the
  * sequence (what ht would be for that prefix, so a later call can resume
  * from it as h0) is written to
  *   states[slot]  : [H, d_k, d_v] fp32, row-major like ht,
@@ -202,11 +235,11 @@ int kda_chunk_forward_mx(const kda_chunk_desc_t* d,
  * consecutive; slots past the last one written are left untouched.
  * states: device buffer of at least count * H * d_k * d_v floats, 16-byte
  * aligned, overlapping no other buffer; it may be NULL only when count is 0.
- * Returns what kda_chunk_forward returns, and KDA_ERR_INVALID_ARGUMENT for
- * states_every < 1 or a states buffer that breaks the rules above.
+ * Returns what kda_chunk_forward_gated returns, and KDA_ERR_INVALID_ARGUMENT
+ * for states_every < 1 or a states buffer that breaks the rules above.
  */
 int kda_chunk_forward_states_count(const kda_chunk_desc_t* d, int states_every, size_t* count);
-int kda_chunk_forward_states(const kda_chunk_desc_t* d,
+int kda_chunk_forward_states(const kda_chunk_desc_ex_t* d,
                              const void* q, const void* k, const void* v, const void* g,
                              const float* beta, const float* h0,
                              const int32_t* cu_seqlens,
@@ -216,8 +249,8 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d,
                              void* stream);
 
 /*
- * Backward pass of kda_chunk_forward (training: K3's KDA layers are trained
- * chunk-parallel up to million-token contexts, "3 分钟看懂 Kimi K3"
+ * Backward pass of kda_chunk_forward_gated (training: K3's KDA layers are
+ * trained chunk-parallel up to million-token contexts, "3 分钟看懂 Kimi K3"
  * (landx.limxdynamics.com), "第一条主线"; the pages give no gradient, so it is
  * derived from the recurrence above by the chain rule).
  *
@@ -238,7 +271,7 @@ int kda_chunk_forward_states(const kda_chunk_desc_t* d,
  * other, the inputs or the workspace.  Other rules as kda_chunk_forward.
  */
 int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
-int kda_chunk_backward(const kda_chunk_desc_t* d,
+int kda_chunk_backward(const kda_chunk_desc_ex_t* d,
                        const void* q, const void* k, const void* v, const void* g,
                        const float* beta, const float* h0, const int32_t* cu_seqlens,
                        const void* dout, const float* dht,
@@ -264,7 +297,7 @@ int kda_chunk_backward(const kda_chunk_desc_t* d,
  * and errors as kda_chunk_backward; NULL or equal events are
  * KDA_ERR_INVALID_ARGUMENT.
  */
-int kda_chunk_backward_overlapped(const kda_chunk_desc_t* d,
+int kda_chunk_backward_overlapped(const kda_chunk_desc_ex_t* d,
                                   const void* q, const void* k, const void* v, const void* g,
                                   const float* beta, const float* h0, const int32_t* cu_seqlens,
                                   const void* dout, const float* dht,
@@ -275,10 +308,10 @@ int kda_chunk_backward_overlapped(const kda_chunk_desc_t* d,
 /*
  * Measurement twin of kda_chunk_backward: events[i] (5 caller-created
  * hipEvent_t, entries may be NULL) is recorded before stage i and events[4]
- * after the last.  Stages: 0 forward replay (three launches), 1 chunk records,
+ * after the last.  Stages: 0 forward replay (its launches), 1 chunk records,
  * 2 state gradients (reverse over the chunks), 3 local gradients.
  */
-int kda_chunk_backward_timed(const kda_chunk_desc_t* d,
+int kda_chunk_backward_timed(const kda_chunk_desc_ex_t* d,
                              const void* q, const void* k, const void* v, const void* g,
                              const float* beta, const float* h0, const int32_t* cu_seqlens,
                              const void* dout, const float* dht,
@@ -294,17 +327,25 @@ int kda_chunk_backward_timed(const kda_chunk_desc_t* d,
  * (the recurrence above for a single token; decode cost and state size do
  * not depend on how many tokens came before).
  *
- *   q, k    : [N, H, d_k] dtype      v: [N, H, d_v] dtype
- *   g       : [N, H, d_k] (KDA_GATE_CHANNEL), [N, H] (KDA_GATE_HEAD) dtype,
- *             or NULL (KDA_GATE_NONE)
+ *   q, k, g : [N, H, d_k] dtype (g: log-decays per key channel)
+ *   v       : [N, H, d_v] dtype
  *   beta    : [N, H] fp32            o: [N, H, d_v] dtype, written
  *   state   : [N, H, d_k, d_v] fp32, read and overwritten
  * d_k = d_v in {64, 128}.  state must not overlap any other argument and o
  * must not overlap any input.
  */
-int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate,
-                    float g_floor, const void* q, const void* k, const void* v, const void* g,
+int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_floor,
+                    const void* q, const void* k, const void* v, const void* g,
                     const float* beta, float* state, void* o, void* stream);
+
+/*
+ * kda_decode_step for every gate variant: g is [N, H, d_k]
+ * (KDA_GATE_CHANNEL), [N, H] (KDA_GATE_HEAD) dtype, or NULL (KDA_GATE_NONE:
+ * not read).  With KDA_GATE_CHANNEL identical to kda_decode_step.
+ */
+int kda_decode_step_gated(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate,
+                          float g_floor, const void* q, const void* k, const void* v, const void* g,
+                          const float* beta, float* state, void* o, void* stream);
 
 #ifdef __cplusplus
 }

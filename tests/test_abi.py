@@ -12,7 +12,7 @@ import pytest
 from gated_delta_rule_105_amd import _lib
 from gated_delta_rule_105_amd._lib import (KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_ERR_INVALID_ARGUMENT,
                                            KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_OK,
-                                           ChunkDesc)
+                                           ChunkDesc, ChunkDescEx)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kda.h")
 GB = 1 << 30
@@ -50,9 +50,37 @@ def test_status_strings(lib):
 
 def desc(**kw):
     base = dict(B=1, T=4096, H=16, d_k=128, d_v=128, chunk=64, n_seqs=0, dtype=KDA_DTYPE_BF16,
-                g_floor=-0.125, gate=0)
+                g_floor=-0.125)
     base.update(kw)
     return ChunkDesc(**base)
+
+
+def descx(gate=0, **kw):
+    """The extended descriptor (shape + gate) of the gated and extension entry points."""
+    return ChunkDescEx(shape=desc(**kw), gate=gate)
+
+
+def test_boundary_matches_the_scope_table():
+    """kda_chunk_desc_t, kda_chunk_forward and kda_decode_step keep exactly the
+    fields and parameters of the interface the hot path was specified with;
+    the gate variants live in separate entry points."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} kda_chunk_desc_t;", src, re.S).group(1)
+    fields = re.findall(r"(\w+)\s*;", body)
+    assert fields == ["B", "T", "H", "d_k", "d_v", "chunk", "n_seqs", "dtype", "g_floor"]
+    assert [f[0] for f in ChunkDesc._fields_] == fields
+    def params(name):
+        m = re.search(r"\bint " + name + r"\((.*?)\);", src, re.S)
+        return [re.sub(r"\s+", " ", x.strip()) for x in m.group(1).split(",")]
+    assert params("kda_decode_step") == [
+        "int N", "int H", "int d_k", "int d_v", "kda_dtype_t dtype", "float g_floor", "const void* q",
+        "const void* k", "const void* v", "const void* g", "const float* beta", "float* state", "void* o",
+        "void* stream"]
+    assert params("kda_chunk_forward") == [
+        "const kda_chunk_desc_t* d", "const void* q", "const void* k", "const void* v", "const void* g",
+        "const float* beta", "const float* h0", "const int32_t* cu_seqlens", "void* o", "float* ht",
+        "void* workspace", "size_t workspace_bytes", "void* stream"]
+    assert params("kda_chunk_forward_workspace_size") == ["const kda_chunk_desc_t* d", "size_t* bytes"]
 
 
 def ws_status(lib, d):
@@ -62,19 +90,22 @@ def ws_status(lib, d):
 
 
 def test_workspace_size_valid(lib):
+    # one record of three d x d fp32 matrices (B, M, S_in) per (segment, head)
+    # when the sequences are cut into segments; nothing per chunk
     st, n = ws_status(lib, desc())
-    assert st == KDA_OK and n > 0 and n % 256 == 0
-    st2, n2 = ws_status(lib, desc(T=8192))
-    assert st2 == KDA_OK and n2 >= n and n2 % 256 == 0
-    # at least one record of chunk operands per (chunk, head): Qt, Wk, Kh^T, Wv
-    # (64 x 128 bf16 each), P (64 x 64 bf16), gamma (128 fp32)
-    d2 = desc(T=8192)
-    per_chunk = 4 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4
-    assert n2 >= d2.B * d2.H * (8192 // 64) * per_chunk
+    rec = 3 * 128 * 128 * 4
+    assert st == KDA_OK and n > 0 and n % rec == 0
+    assert n <= 16 * (4096 // 64) * rec
+    # the number of segments follows the compute units, not the length
+    st2, n2 = ws_status(lib, desc(T=1 << 20))
+    assert st2 == KDA_OK and 0 < n2 <= 64 << 20 and n2 % rec == 0
     st3, n3 = ws_status(lib, desc(T=0))
     assert st3 == KDA_OK and n3 == 0
     st4, _ = ws_status(lib, desc(d_k=64, d_v=64, dtype=KDA_DTYPE_F32))
     assert st4 == KDA_OK
+    # a packed batch adds two int64 prefix sums per sequence (+1)
+    st5, n5 = ws_status(lib, desc(T=4096, n_seqs=7))
+    assert st5 == KDA_OK and n5 >= 2 * 8 * 8
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -157,8 +188,23 @@ def test_chunk_forward_rejects_bad_desc(lib):
 def dec(lib, N=256, H=32, d=128, dtype=KDA_DTYPE_BF16, gate=0, g_floor=-0.125, **ptrs):
     p = {name: (i + 1) * 64 * GB for i, name in enumerate(["q", "k", "v", "g", "beta", "state", "o"])}
     p.update(ptrs)
-    return _lib.decode_step_raw(N, H, d, d, dtype, gate, g_floor, p["q"], p["k"], p["v"], p["g"], p["beta"],
-                                p["state"], p["o"], None)
+    return _lib.decode_step_gated_raw(N, H, d, d, dtype, gate, g_floor, p["q"], p["k"], p["v"], p["g"],
+                                      p["beta"], p["state"], p["o"], None)
+
+
+def test_decode_step_plain_signature(lib):
+    """kda_decode_step takes (N, H, d_k, d_v, dtype, g_floor, q, k, v, g, beta,
+    state, o, stream) and validates like the gated entry point with the KDA gate."""
+    p = {name: (i + 1) * 64 * GB for i, name in enumerate(["q", "k", "v", "g", "beta", "state", "o"])}
+    f = lib.kda_decode_step
+    assert f(256, 32, 128, 128, KDA_DTYPE_BF16, ctypes.c_float(0.5), p["q"], p["k"], p["v"], p["g"], p["beta"],
+             p["state"], p["o"], None) == KDA_ERR_INVALID_ARGUMENT           # floor out of range
+    assert f(256, 32, 128, 128, KDA_DTYPE_BF16, ctypes.c_float(-0.125), p["q"], p["k"], p["v"], None, p["beta"],
+             p["state"], p["o"], None) == KDA_ERR_INVALID_ARGUMENT           # the KDA gate needs g
+    assert f(256, 32, 128, 128, KDA_DTYPE_BF16, ctypes.c_float(-0.125), p["q"], p["k"], p["v"], p["g"], p["beta"],
+             p["q"] + 1024, p["o"], None) == KDA_ERR_INVALID_ARGUMENT        # state overlaps q
+    assert f(0, 32, 128, 128, KDA_DTYPE_BF16, ctypes.c_float(-0.125), p["q"], p["k"], p["v"], p["g"], p["beta"],
+             p["state"], p["o"], None) == KDA_OK                             # nothing to do
 
 
 def test_decode_rejects(lib):
@@ -184,13 +230,13 @@ def test_decode_rejects(lib):
 def test_chunk_forward_timed_needs_events(lib):
     # the measurement twin validates like kda_chunk_forward and also needs the
     # event array (checked before any HIP call)
-    d = desc()
-    a = fake_args(lib, d)
+    d = descx()
+    a = fake_args(lib, d.shape)
     st = lib.kda_chunk_forward_timed(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
                                      a["cu"], a["o"], a["ht"], a["ws"], ctypes.c_size_t(a["ws_bytes"]), None,
                                      None)
     assert st == KDA_ERR_INVALID_ARGUMENT
-    assert _lib.chunk_forward_timed_raw(desc(d_k=96, d_v=96), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+    assert _lib.chunk_forward_timed_raw(descx(d_k=96, d_v=96), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
                                         a["cu"], a["o"], a["ht"], a["ws"], a["ws_bytes"], None,
                                         [None] * (len(_lib.CHUNK_LAUNCHES) + 1)) == KDA_ERR_UNSUPPORTED
 
@@ -214,7 +260,7 @@ def test_states_count(lib):
 
 
 def call_states(lib, d, a, states, every):
-    return _lib.chunk_forward_states_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["o"],
+    return _lib.chunk_forward_states_raw(ChunkDescEx(shape=d, gate=0), a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["o"],
                                          a["ht"], states, every, a["ws"], a["ws_bytes"], None)
 
 
@@ -244,24 +290,38 @@ def test_chunk_forward_states_empty(lib):
     assert call_states(lib, desc(d_k=96, d_v=96), fake_args(lib, desc()), 11 * 64 * GB, 1) == KDA_ERR_UNSUPPORTED
 
 
+def gated(lib, dx, a):
+    return _lib.chunk_forward_gated_raw(dx, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["o"],
+                                        a["ht"], a["ws"], a["ws_bytes"], None)
+
+
 def test_gate_validation(lib):
     d = desc()
     a = fake_args(lib, d)
-    assert call(lib, desc(gate=3), a) == KDA_ERR_INVALID_ARGUMENT         # no such gate
-    assert ws_status(lib, desc(gate=-1))[0] == KDA_ERR_INVALID_ARGUMENT
+    assert gated(lib, descx(gate=3), a) == KDA_ERR_INVALID_ARGUMENT        # no such gate
+    assert gated(lib, descx(gate=-1), a) == KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_chunk_forward_gated(None, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["o"],
+                                       a["ht"], a["ws"], ctypes.c_size_t(a["ws_bytes"]), None) == \
+        KDA_ERR_INVALID_ARGUMENT
     a2 = dict(a, g=None)
-    assert call(lib, desc(gate=1), a2) == KDA_ERR_INVALID_ARGUMENT        # per-head gate without g
+    assert gated(lib, descx(gate=1), a2) == KDA_ERR_INVALID_ARGUMENT       # per-head gate without g
+    assert call(lib, d, a2) == KDA_ERR_INVALID_ARGUMENT                    # kda_chunk_forward: the KDA gate
     # per-head g is [B, T, H]: 128 KiB here; o placed 64 KiB after it overlaps
     a3 = dict(a, o=a["g"] + 64 * 1024)
-    assert call(lib, desc(gate=1), a3) == KDA_ERR_INVALID_ARGUMENT
-    # without a gate g is ignored, and the workspace does not depend on the gate
+    assert gated(lib, descx(gate=1), a3) == KDA_ERR_INVALID_ARGUMENT
+    # without a gate g is ignored; the workspace is kda_chunk_forward's
     a4 = dict(a, g=None, ws_bytes=a["ws_bytes"] - 1)
-    assert call(lib, desc(gate=2), a4) == KDA_ERR_WORKSPACE_TOO_SMALL
-    assert ws_status(lib, desc(gate=1)) == ws_status(lib, desc(gate=2)) == ws_status(lib, desc())
+    assert gated(lib, descx(gate=2), a4) == KDA_ERR_WORKSPACE_TOO_SMALL
+    # with the KDA gate the gated entry point validates as kda_chunk_forward
+    for mutate in (lambda x: x.update(q=None), lambda x: x.update(o=x["q"] + 1024),
+                   lambda x: x.update(ws_bytes=x["ws_bytes"] - 1)):
+        b = dict(a)
+        mutate(b)
+        assert gated(lib, descx(gate=0), b) == call(lib, d, b) != KDA_OK
 
 
 def call_mx(lib, d, a, qs, ks, vs):
-    return _lib.chunk_forward_mx_raw(d, a["q"], qs, a["k"], ks, a["v"], vs, a["g"], a["beta"], a["h0"], a["cu"],
+    return _lib.chunk_forward_mx_raw(ChunkDescEx(shape=d, gate=0), a["q"], qs, a["k"], ks, a["v"], vs, a["g"], a["beta"], a["h0"], a["cu"],
                                      a["o"], a["ht"], a["ws"], a["ws_bytes"], None)
 
 
@@ -316,8 +376,9 @@ def bwd_args(lib, d):
     return a
 
 
-def bwd_call(d, a, events=None):
-    return _lib.chunk_backward_raw(d, *(a[n] for n in BWD_NAMES), a["ws_bytes"], None, events)
+def bwd_call(d, a, events=None, gate=0):
+    return _lib.chunk_backward_raw(ChunkDescEx(shape=d, gate=gate), *(a[n] for n in BWD_NAMES), a["ws_bytes"],
+                                   None, events)
 
 
 @pytest.mark.parametrize("mutate,code", [
@@ -347,15 +408,16 @@ def test_chunk_backward_rejects_bad_desc(lib):
     assert bwd_call(desc(d_k=96, d_v=96), a) == KDA_ERR_UNSUPPORTED
     assert bwd_call(desc(g_floor=-0.5), a) == KDA_ERR_INVALID_ARGUMENT
     # the timed twin needs its event array
-    d = desc()
+    d = descx()
     st = lib.kda_chunk_backward_timed(ctypes.byref(d), *(a[n] for n in BWD_NAMES),
                                       ctypes.c_size_t(a["ws_bytes"]), None, None)
     assert st == KDA_ERR_INVALID_ARGUMENT
     # without a gate, g and dg are neither read nor written: a bad dg is ignored
-    dn = desc(gate=2)
+    dn = desc()
     an = bwd_args(lib, dn)
     an.update(g=None, dg=3, dq=an["q"] + 1024)
-    assert bwd_call(dn, an) == KDA_ERR_INVALID_ARGUMENT                   # the overlap is still caught
+    assert bwd_call(dn, an, gate=2) == KDA_ERR_INVALID_ARGUMENT           # the overlap is still caught
+    assert bwd_call(dn, dict(an, dq=an["dq"]), gate=3) == KDA_ERR_INVALID_ARGUMENT  # no such gate
 
 
 def test_chunk_backward_overlapped_rejects(lib):
@@ -366,8 +428,8 @@ def test_chunk_backward_overlapped_rejects(lib):
     a = bwd_args(lib, d)
     ev1, ev2, side = 1 << 40, 2 << 40, 3 << 40   # never dereferenced
     def ov(args, fork, join, dd=d):
-        return _lib.chunk_backward_raw(dd, *(args[n] for n in BWD_NAMES), args["ws_bytes"], None,
-                                       aux=(side, fork, join))
+        return _lib.chunk_backward_raw(ChunkDescEx(shape=dd, gate=0), *(args[n] for n in BWD_NAMES),
+                                       args["ws_bytes"], None, aux=(side, fork, join))
     assert ov(a, None, ev2) == KDA_ERR_INVALID_ARGUMENT
     assert ov(a, ev1, None) == KDA_ERR_INVALID_ARGUMENT
     assert ov(a, ev1, ev1) == KDA_ERR_INVALID_ARGUMENT
@@ -379,4 +441,5 @@ def test_chunk_backward_overlapped_rejects(lib):
         assert ov(b, ev1, ev2) == code
     assert ov(a, ev1, ev2, dd=desc(d_k=96, d_v=96)) == KDA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
-        _lib.chunk_backward_raw(d, *(a[n] for n in BWD_NAMES), a["ws_bytes"], None, [0] * 5, (side, ev1, ev2))
+        _lib.chunk_backward_raw(ChunkDescEx(shape=d, gate=0), *(a[n] for n in BWD_NAMES), a["ws_bytes"], None,
+                                [0] * 5, (side, ev1, ev2))
