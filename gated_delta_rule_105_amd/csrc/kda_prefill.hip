@@ -76,33 +76,57 @@ template <typename T, int W> struct Arr {
   static constexpr int BYTES = C * (W + 16) * (int)sizeof(T);  // 64 rows
 };
 
-// Row fragment (A- or B-operand whose k runs along a row): row r, elements
-// k0 + 4g .. k0 + 4g + 3 and, for bf16 (k-blocks of 32), k0 + 16 + 4g ...
+// Lane-dependent part of an array access, in elements.  For a tile whose
+// first row r0 and first column c0 (or k-block start k0) are multiples of 16,
+// the swizzle's XOR acts on lane bits only, so an access is this part plus
+// r0 (W + 16) + c0: one register per array width and access pattern, the
+// rest immediates.
+//   row: row fragment, lane (g, i) at row r0 + i, elements k0 + 4 g ...
+//   col: column piece (bf16: lane (g, L) addressing row r0 + 4 g + L / 4 at
+//        elements c0 + 4 (L % 4) ..; fp32: row r0 + 4 g, element c0 + i)
+template <typename T, int W> struct LaneOff {
+  int row, col;
+  __device__ __forceinline__ explicit LaneOff(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    row = i * (W + 16) + ((g ^ ((i >> 2) & 3)) << 2);
+    if constexpr (sizeof(T) == 2) col = (4 * g + (i >> 2)) * (W + 16) + (((i & 3) ^ g) << 2);
+    else col = 4 * g * (W + 16) + (((i >> 2) ^ g) << 2) + (i & 3);
+  }
+};
+
+// A lane's index and its offsets into the [64][D] and [D][64] arrays.
+template <typename T, int D> struct Lanes {
+  int lane;
+  LaneOff<T, D> d;
+  LaneOff<T, kChunk> c;
+  __device__ __forceinline__ explicit Lanes(int l) : lane(l), d(l), c(l) {}
+};
+
+// Row fragment (A- or B-operand whose k runs along a row): row r0 + i,
+// elements k0 + 4g .. k0 + 4g + 3 and, for bf16 (k-blocks of 32), k0 + 16 + 4g ...
 template <int W>
-__device__ __forceinline__ bf16x8 rowfrag(const bf16_t* X, int r, int k0, int g) {
-  const bf16x4 lo = *(const bf16x4*)(X + sidx<W>(r, k0 + 4 * g));
-  const bf16x4 hi = *(const bf16x4*)(X + sidx<W>(r, k0 + 16 + 4 * g));
+__device__ __forceinline__ bf16x8 rowfrag(const bf16_t* X, const LaneOff<bf16_t, W>& lo_, int r0, int k0) {
+  const bf16_t* p = X + lo_.row + r0 * (W + 16) + k0;
+  const bf16x4 lo = *(const bf16x4*)p;
+  const bf16x4 hi = *(const bf16x4*)(p + 16);
   return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 template <int W>
-__device__ __forceinline__ f32x4 rowfrag(const float* X, int r, int k0, int g) {
-  return *(const f32x4*)(X + sidx<W>(r, k0 + 4 * g));
+__device__ __forceinline__ f32x4 rowfrag(const float* X, const LaneOff<float, W>& lo_, int r0, int k0) {
+  return *(const f32x4*)(X + lo_.row + r0 * (W + 16) + k0);
 }
 // Column piece: lane (g, i) gets X[r0 + 4g + e][c0 + i], e = 0..3 (the
 // accumulator layout of a 16 x 16 tile, and an operand fragment whose k runs
-// down a column).  bf16: one transpose read, lane (g, L) addressing row
-// r0 + 4g + L / 4, elements c0 + 4 (L % 4) ..; fp32: four scalar reads.
+// down a column).  bf16: one transpose read; fp32: four scalar reads.
 template <int W>
-__device__ __forceinline__ s16x4 colpiece(const bf16_t* X, int r0, int c0, int lane) {
-  const int g = lane >> 4, L = lane & 15;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + sidx<W>(r0 + 4 * g + (L >> 2), c0 + 4 * (L & 3))));
+__device__ __forceinline__ s16x4 colpiece(const bf16_t* X, const LaneOff<bf16_t, W>& lo_, int r0, int c0) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + lo_.col + r0 * (W + 16) + c0));
 }
 template <int W>
-__device__ __forceinline__ f32x4 colpiece(const float* X, int r0, int c0, int lane) {
-  const int g = lane >> 4, i = lane & 15;
+__device__ __forceinline__ f32x4 colpiece(const float* X, const LaneOff<float, W>& lo_, int r0, int c0) {
   f32x4 x;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] = X[sidx<W>(r0 + 4 * g + e, c0 + i)];
+  for (int e = 0; e < 4; ++e) x[e] = X[lo_.col + (r0 + e) * (W + 16) + c0];
   return x;
 }
 __device__ __forceinline__ f32x4 widen4(const s16x4& h) {
@@ -113,23 +137,24 @@ __device__ __forceinline__ f32x4 widen4(const s16x4& h) {
 __device__ __forceinline__ f32x4 widen4(const f32x4& x) { return x; }
 // Column fragment over a k-block (bf16: 32 rows as two pieces; fp32: 16)
 template <int W>
-__device__ __forceinline__ bf16x8 colfrag(const bf16_t* X, int r0, int c0, int lane) {
-  const s16x4 a = colpiece<W>(X, r0, c0, lane), b = colpiece<W>(X, r0 + 16, c0, lane);
+__device__ __forceinline__ bf16x8 colfrag(const bf16_t* X, const LaneOff<bf16_t, W>& lo_, int r0, int c0) {
+  const s16x4 a = colpiece<W>(X, lo_, r0, c0), b = colpiece<W>(X, lo_, r0 + 16, c0);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 template <int W>
-__device__ __forceinline__ f32x4 colfrag(const float* X, int r0, int c0, int lane) {
-  return colpiece<W>(X, r0, c0, lane);
+__device__ __forceinline__ f32x4 colfrag(const float* X, const LaneOff<float, W>& lo_, int r0, int c0) {
+  return colpiece<W>(X, lo_, r0, c0);
 }
 
 // ---- LDS layout of a sweep workgroup --------------------------------------
 // Token-major [64][D]: Qt (output sweep only) and Kh in two buffer sets (a
 // chunk's state step reads them while the next chunk's element-wise stage
-// writes the other set), Kt, V.  Channel-major [D][64]: Wk^T.  Fragment images, 64 lanes x 4 elements in lane order: P
-// tiles (rt, sb), sb <= rt (output sweep); the off-diagonal blocks of -A as
-// operand fragments (i, m), m < i; the diagonal blocks' inverses T_bb (bf16:
-// a hi and a lo image).  fp32: partial sums of g [8][D], beta [64], gamma [D]
-// in two buffer sets.
+// writes the other set), Kt, V.  Channel-major [D][64]: Wk^T.  Fragment
+// images in lane order: P tiles (rt, sb), sb <= rt (output sweep), 4
+// elements a lane; coefficient images of 16 bytes a lane (Blk): the
+// off-diagonal blocks of -A (i, m), m < i, and the diagonal blocks' inverses
+// T_bb.  fp32: partial sums of g [8][D], beta [64], gamma [D] in two buffer
+// sets.
 // After the last chunk the map sweep stages M [D][D + 4] fp32 from offset 0.
 template <typename T, int D, bool OUT> struct Lay {
   static constexpr int ES = (int)sizeof(T);
@@ -140,8 +165,8 @@ template <typename T, int D, bool OUT> struct Lay {
   static constexpr int NBUF = OVL ? 2 : 1;
   static constexpr int ARR = Arr<T, D>::BYTES;       // token-major [64][D]
   static constexpr int ARRT = D * (C + 16) * ES;     // channel-major [D][64]
-  static constexpr int IMG = 64 * 4 * ES;            // one fragment image
-  static constexpr int NTI = ES == 2 ? 2 : 1;
+  static constexpr int IMG = 64 * 4 * ES;            // one fragment image (P tiles)
+  static constexpr int CIMG = 64 * 16;               // one coefficient image (16 bytes a lane)
   static constexpr int QT0 = 0;                      // Qt, two buffer sets (output sweep)
   static constexpr int KH0 = QT0 + (OUT ? NBUF * ARR : 0);  // Kh, two buffer sets
   static constexpr int KT = KH0 + NBUF * ARR;
@@ -149,8 +174,8 @@ template <typename T, int D, bool OUT> struct Lay {
   static constexpr int WKT = VV + ARR;
   static constexpr int PIMG = WKT + ARRT;
   static constexpr int AIMG = PIMG + (OUT ? 10 * IMG : 0);
-  static constexpr int TIMG = AIMG + 6 * IMG;
-  static constexpr int PART = TIMG + 4 * NTI * IMG;
+  static constexpr int TIMG = AIMG + 6 * CIMG;
+  static constexpr int PART = TIMG + 4 * (ES == 2 ? 2 : 1) * CIMG;
   static constexpr int BETA = PART + 8 * D * 4;
   static constexpr int GAM0 = BETA + C * 4;          // gamma, two buffer sets
   static constexpr int STAGE_M = D * (D + 4) * 4;
@@ -160,8 +185,8 @@ template <typename T, int D, bool OUT> struct Lay {
   __device__ static __forceinline__ int kh(int buf) { return KH0 + (OVL ? buf : 0) * ARR; }
   __device__ static __forceinline__ int gam(int buf) { return GAM0 + (OVL ? buf : 0) * D * 4; }
   __device__ static __forceinline__ int pimg(int rt, int sb) { return PIMG + (rt * (rt + 1) / 2 + sb) * IMG; }
-  __device__ static __forceinline__ int aimg(int i, int m) { return AIMG + (i * (i - 1) / 2 + m) * IMG; }
-  __device__ static __forceinline__ int timg(int b, int part) { return TIMG + (b * NTI + part) * IMG; }
+  __device__ static __forceinline__ int aimg(int i, int m) { return AIMG + (i * (i - 1) / 2 + m) * CIMG; }
+  __device__ static __forceinline__ int timg(int b) { return TIMG + b * (ES == 2 ? 2 : 1) * CIMG; }
 };
 
 // ---- sequences and segments -----------------------------------------------
@@ -290,8 +315,8 @@ template <> struct PairT<bf16_t> {
   __device__ static __forceinline__ word splat(word x) { return (x & 0xffffu) | (x << 16); }
   __device__ static __forceinline__ word zero() { return 0u; }
   template <int AUX>
-  __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+  __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, AUX);
   }
   template <int AUX>
   __device__ static __forceinline__ word load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -306,8 +331,8 @@ template <> struct PairT<float> {
   __device__ static __forceinline__ word splat(word x) { return (f32x2){x[0], x[0]}; }
   __device__ static __forceinline__ word zero() { return (f32x2){0.f, 0.f}; }
   template <int AUX>
-  __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+  __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, AUX));
   }
   template <int AUX>
   __device__ static __forceinline__ word load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -360,21 +385,22 @@ template <typename T, int D, bool WITH_Q, bool MX, bool NT> struct Raw {
     } else {
       const __amdgpu_buffer_rsrc_t rk = rsrc((const T*)in.k + row0 * D, span * ES);
       const __amdgpu_buffer_rsrc_t rv = rsrc((const T*)in.v + row0 * D, span * ES);
+      // per-row steps as the uniform offset
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        k[s] = PW::template load<aux>(rk, (off0 + (uint32_t)s * rs) * ES);
-        v[s] = PW::template load<aux>(rv, (off0 + (uint32_t)s * rs) * ES);
+        k[s] = PW::template load<aux>(rk, off0 * ES, s * rs * ES);
+        v[s] = PW::template load<aux>(rv, off0 * ES, s * rs * ES);
       }
       if constexpr (WITH_Q) {
         const __amdgpu_buffer_rsrc_t rq = rsrc((const T*)in.q + row0 * D, span * ES);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) q[s] = PW::template load<aux>(rq, (off0 + (uint32_t)s * rs) * ES);
+        for (int s = 0; s < 8; ++s) q[s] = PW::template load<aux>(rq, off0 * ES, s * rs * ES);
       }
     }
     if (gate == kGateChannel) {
       const __amdgpu_buffer_rsrc_t rgt = rsrc((const T*)in.g + row0 * D, span * ES);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) g[s] = PW::template load<aux>(rgt, (off0 + (uint32_t)s * rs) * ES);
+      for (int s = 0; s < 8; ++s) g[s] = PW::template load<aux>(rgt, off0 * ES, s * rs * ES);
     } else if (gate == kGateHead) {
       const __amdgpu_buffer_rsrc_t rgt = rsrc((const T*)in.g + row0, ((uint32_t)(clen - 1) * H + 1) * ES);
 #pragma unroll
@@ -424,8 +450,8 @@ __device__ __forceinline__ void estage1(unsigned char* smem, const Raw<T, D, OUT
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const float x0 = PW::lo(w[s]), x1 = PW::hi(w[s]);
-    g0[s] = (x0 < g_floor ? g_floor : x0) * kLog2e;  // NaN stays NaN
-    g1[s] = (x1 < g_floor ? g_floor : x1) * kLog2e;
+    g0[s] = __builtin_elementwise_maximum(x0, g_floor) * kLog2e;  // NaN-propagating: NaN stays NaN
+    g1[s] = __builtin_elementwise_maximum(x1, g_floor) * kLog2e;
     p0 += g0[s];
     p1 += g1[s];
   }
@@ -438,6 +464,9 @@ __device__ __forceinline__ void estage2(unsigned char* smem, int buf, const Raw<
   typedef PairT<T> PW;
   typedef typename PW::word word;
   const int cp = tid % (D / 2), part = tid / (D / 2), c = 2 * cp;
+  // element of row 8 part + s, channel c in the swizzled arrays: the row's
+  // swizzle flips unit bit 0 from s = 4 on (the rest is the thread's)
+  const int eb0 = 8 * part * (D + 16) + (((cp >> 1) ^ (2 * (part & 1))) << 2) + 2 * (cp & 1), eb1 = eb0 ^ 4;
   const float* sPart = (const float*)(smem + Y::PART);
   float gam0 = 0.f, gam1 = 0.f, gl0 = 0.f, gl1 = 0.f;
 #pragma unroll
@@ -456,7 +485,7 @@ __device__ __forceinline__ void estage2(unsigned char* smem, int buf, const Raw<
   T* sV = (T*)(smem + Y::VV);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int t = 8 * part + s, e = sidx<D>(t, c);
+    const int e = (s < 4 ? eb0 : eb1) + s * (D + 16);
     gam0 += g0[s];
     gam1 += g1[s];
     const float e0 = __builtin_amdgcn_exp2f(gam0), e1 = __builtin_amdgcn_exp2f(gam1);
@@ -480,54 +509,63 @@ __device__ __forceinline__ s16x4 to_bf16x4(const f32x4& x) {
   const uint32_t b = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3]));
   return __builtin_bit_cast(s16x4, (uint2){a, b});
 }
-// Blk<T>: coefficient fragments (A operand of a 16 x 16 x 16 product: lane
-// (g, i) holds row i, k = 4 g .. 4 g + 3) kept as images, and right operands
-// from accumulator tiles.  bf16: a right operand is split hi + lo, so that
-// the product keeps about fp32 accuracy in it; the diagonal inverses are
-// split too (tri: three products).  fp32: fp32 MFMA throughout.
+// Blk<T>: 16 x 16 x 16 block products of the triangular solve.  Coefficient
+// fragments (A operand: lane (g, i) holds row i, k = 4 g .. 4 g + 3) are kept
+// as images of 16 bytes per lane; right operands come from accumulator
+// tiles.  bf16: a right operand is split hi + lo so that the product keeps
+// about fp32 accuracy in it, and the two halves go down the k dimension of
+// one 16 x 16 x 32 product against a coefficient image stored twice,
+// [a | a]: a (hi + lo) in one instruction.  The diagonal inverses are split
+// too, stored as two images [lo | hi] and [hi | 0]: tri forms lo r_hi + hi
+// r_lo, then hi r_hi, in two 16 x 16 x 32 products.  (Every accumulation
+// chain stays on one MFMA shape: a 16 x 16 x 16 product reading a 16 x 16 x
+// 32 product's result as its accumulator, issued back to back, gave wrong
+// sums.)  fp32: fp32 MFMA throughout.
+__device__ __forceinline__ bf16x8 cat4(const s16x4& x, const s16x4& y) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 template <typename T> struct Blk;
 template <> struct Blk<bf16_t> {
-  typedef s16x4 Coef;
-  struct Opnd {
-    s16x4 hi, lo;
-  };
-  static constexpr int NPARTS = 2;
-  __device__ static __forceinline__ Coef load(const unsigned char* p) { return *(const s16x4*)p; }
+  typedef bf16x8 Coef;  // [a | a], or [lo | hi] and [hi | 0]
+  typedef bf16x8 Opnd;  // [hi | lo]
+  __device__ static __forceinline__ Coef load(const unsigned char* p) { return *(const bf16x8*)p; }
+  // a plain 4-element image (P tiles)
   __device__ static __forceinline__ void store(unsigned char* p, const f32x4& x) { *(s16x4*)p = to_bf16x4(x); }
-  __device__ static __forceinline__ void store_split(unsigned char* hi, unsigned char* lo, const f32x4& x) {
+  __device__ static __forceinline__ void store_coef(unsigned char* p, const f32x4& x) {
     const s16x4 h = to_bf16x4(x);
-    *(s16x4*)hi = h;
-    *(s16x4*)lo = to_bf16x4(x - widen4(h));
+    *(bf16x8*)p = cat4(h, h);
+  }
+  // the two images of a diagonal inverse, p and p + TRI2
+  static constexpr int TRI2 = 64 * 16;
+  __device__ static __forceinline__ void store_tri(unsigned char* p, const f32x4& x) {
+    const s16x4 h = to_bf16x4(x);
+    *(bf16x8*)p = cat4(to_bf16x4(x - widen4(h)), h);
+    *(bf16x8*)(p + TRI2) = cat4(h, (s16x4){0, 0, 0, 0});
   }
   __device__ static __forceinline__ Opnd opnd(const f32x4& b) {
-    Opnd o;
-    o.hi = to_bf16x4(b);
-    o.lo = to_bf16x4(b - widen4(o.hi));
-    return o;
+    const s16x4 h = to_bf16x4(b);
+    return cat4(h, to_bf16x4(b - widen4(h)));
   }
   __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static __forceinline__ f32x4 tri(const Coef& th, const Coef& tl, const Opnd& r) {
-    f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(th, r.hi, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(th, r.lo, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tl, r.hi, c, 0, 0, 0);
+  __device__ static __forceinline__ f32x4 tri(const Coef& t1, const Coef& t2, const Opnd& r) {
+    const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, r, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(t2, r, c, 0, 0, 0);
   }
 };
 template <> struct Blk<float> {
   typedef f32x4 Coef;
   typedef f32x4 Opnd;
-  static constexpr int NPARTS = 1;
   __device__ static __forceinline__ Coef load(const unsigned char* p) { return *(const f32x4*)p; }
   __device__ static __forceinline__ void store(unsigned char* p, const f32x4& x) { *(f32x4*)p = x; }
-  __device__ static __forceinline__ void store_split(unsigned char* hi, unsigned char*, const f32x4& x) {
-    *(f32x4*)hi = x;
-  }
+  __device__ static __forceinline__ void store_coef(unsigned char* p, const f32x4& x) { *(f32x4*)p = x; }
+  static constexpr int TRI2 = 0;  // one image
+  __device__ static __forceinline__ void store_tri(unsigned char* p, const f32x4& x) { *(f32x4*)p = x; }
   __device__ static __forceinline__ Opnd opnd(const f32x4& b) { return b; }
   __device__ static __forceinline__ f32x4 apply(const Coef& a, const Opnd& b, f32x4 c) { return mma(a, b, c); }
-  __device__ static __forceinline__ f32x4 tri(const Coef& th, const Coef&, const Opnd& r) {
-    return mma(th, r, (f32x4){0.f, 0.f, 0.f, 0.f});
+  __device__ static __forceinline__ f32x4 tri(const Coef& t, const Coef&, const Opnd& r) {
+    return mma(t, r, (f32x4){0.f, 0.f, 0.f, 0.f});
   }
 };
 
@@ -536,14 +574,13 @@ template <> struct Blk<float> {
 // XB = Kt or Qt, element (row rb + i, k = ra + 4 g + e) of Kt Kh^T or Qt Kh^T,
 // i.e. directly the coefficient fragment of that block.
 template <typename T, int D>
-__device__ __forceinline__ f32x4 gram_tile(const T* XA, int ra, const T* XB, int rb, int lane) {
+__device__ __forceinline__ f32x4 gram_tile(const T* XA, int ra, const T* XB, int rb, const Lanes<T, D>& ln) {
   constexpr int KB = Elem<T>::KB;
-  const int g = lane >> 4, i = lane & 15;
   typename Frag<T>::type fa[D / KB], fb[D / KB];
 #pragma unroll
   for (int kb = 0; kb < D / KB; ++kb) {
-    fa[kb] = rowfrag<D>(XA, ra + i, kb * KB, g);
-    fb[kb] = rowfrag<D>(XB, rb + i, kb * KB, g);
+    fa[kb] = rowfrag<D>(XA, ln.d, ra, kb * KB);
+    fb[kb] = rowfrag<D>(XB, ln.d, rb, kb * KB);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -552,17 +589,18 @@ __device__ __forceinline__ f32x4 gram_tile(const T* XA, int ra, const T* XB, int
 }
 // Off-diagonal block (i, m), m < i, of -A = -diag(beta) Kt Kh^T, as an image.
 template <typename T, int D, bool OUT>
-__device__ __forceinline__ void a_block(unsigned char* smem, int buf, int i, int m, int lane) {
+__device__ __forceinline__ void a_block(unsigned char* smem, int buf, int i, int m, const Lanes<T, D>& ln) {
   typedef Lay<T, D, OUT> Y;
-  const f32x4 t = gram_tile<T, D>((const T*)(smem + Y::kh(buf)), 16 * m, (const T*)(smem + Y::KT), 16 * i, lane);
-  const float nb = -((const float*)(smem + Y::BETA))[16 * i + (lane & 15)];
-  Blk<T>::store(smem + Y::aimg(i, m) + lane * 4 * Y::ES, nb * t);
+  const f32x4 t = gram_tile<T, D>((const T*)(smem + Y::kh(buf)), 16 * m, (const T*)(smem + Y::KT), 16 * i, ln);
+  const float nb = -((const float*)(smem + Y::BETA))[16 * i + (ln.lane & 15)];
+  Blk<T>::store_coef(smem + Y::aimg(i, m) + ln.lane * 16, nb * t);
 }
 // Tile (rt, sb), sb <= rt, of P = lower_incl(Qt Kh^T), as an image.
 template <typename T, int D>
-__device__ __forceinline__ void p_block(unsigned char* smem, int buf, int rt, int sb, int lane) {
+__device__ __forceinline__ void p_block(unsigned char* smem, int buf, int rt, int sb, const Lanes<T, D>& ln) {
   typedef Lay<T, D, true> Y;
-  f32x4 t = gram_tile<T, D>((const T*)(smem + Y::kh(buf)), 16 * sb, (const T*)(smem + Y::qt(buf)), 16 * rt, lane);
+  const int lane = ln.lane;
+  f32x4 t = gram_tile<T, D>((const T*)(smem + Y::kh(buf)), 16 * sb, (const T*)(smem + Y::qt(buf)), 16 * rt, ln);
   if (sb == rt) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -582,14 +620,14 @@ __device__ __forceinline__ void p_block(unsigned char* smem, int buf, int rt, in
 // (g, i) ends with coef(T_bb), the coefficient fragment, stored as an image
 // (bf16: hi and lo).
 template <typename T, int D, bool OUT>
-__device__ __forceinline__ void diag_block(unsigned char* smem, int buf, int b, int lane) {
+__device__ __forceinline__ void diag_block(unsigned char* smem, int buf, int b, const Lanes<T, D>& ln) {
   typedef Lay<T, D, OUT> Y;
-  const int g = lane >> 4, i = lane & 15;
+  const int lane = ln.lane, g = lane >> 4, i = lane & 15;
   const T* sK = (const T*)(smem + Y::KT);
   const T* sH = (const T*)(smem + Y::kh(buf));
   const float* sB = (const float*)(smem + Y::BETA) + 16 * b;
-  const f32x4 tc = gram_tile<T, D>(sH, 16 * b, sK, 16 * b, lane);  // (Kt Kh^T)[i][4 g + e]
-  const f32x4 ta = gram_tile<T, D>(sK, 16 * b, sH, 16 * b, lane);  // (Kt Kh^T)[4 g + e][i]
+  const f32x4 tc = gram_tile<T, D>(sH, 16 * b, sK, 16 * b, ln);  // (Kt Kh^T)[i][4 g + e]
+  const f32x4 ta = gram_tile<T, D>(sK, 16 * b, sH, 16 * b, ln);  // (Kt Kh^T)[4 g + e][i]
   const float bi = sB[i];
   const f32x4 b4 = *(const f32x4*)(sB + 4 * g);
   f32x4 cN, aN, cT;
@@ -606,8 +644,7 @@ __device__ __forceinline__ void diag_block(unsigned char* smem, int buf, int b, 
   cT = mma(aN2, cT, cT);  // coef(T (I + N^2)) = coef(T) + coef(T N^2)
   cT = mma(aN4, cT, cT);
   cT = mma(aN8, cT, cT);
-  Blk<T>::store_split(smem + Y::timg(b, 0) + lane * 4 * Y::ES, smem + Y::timg(b, Blk<T>::NPARTS - 1) + lane * 4 * Y::ES,
-                      cT);
+  Blk<T>::store_tri(smem + Y::timg(b) + lane * 16, cT);
 }
 
 // The Gram stage.  Waves 0-3 take a diagonal block each (its inverse is the
@@ -616,7 +653,7 @@ __device__ __forceinline__ void diag_block(unsigned char* smem, int buf, int b, 
 // waves at d = 64, where there are only four), in an order where consecutive
 // tiles share their Kh rows.
 template <typename T, int D, bool OUT>
-__device__ __forceinline__ void gram_stage(unsigned char* smem, int buf, int wave, int lane) {
+__device__ __forceinline__ void gram_stage(unsigned char* smem, int buf, int wave, const Lanes<T, D>& lane) {
   constexpr int NW = D / 16;
   if (wave < 4) {
     diag_block<T, D, OUT>(smem, buf, wave, lane);
@@ -649,30 +686,30 @@ __device__ __forceinline__ void gram_stage(unsigned char* smem, int buf, int wav
 // channel-major (Wk^T, 16 contiguous tokens of a channel per lane: no
 // scatter); Wv stays in the wave's registers.
 template <typename T, int D, bool OUT>
-__device__ __forceinline__ void substitute(unsigned char* smem, int w, int lane, f32x4 (&Wv)[4]) {
+__device__ __forceinline__ void substitute(unsigned char* smem, int w, const Lanes<T, D>& ln, f32x4 (&Wv)[4]) {
   typedef Lay<T, D, OUT> Y;
   typedef Blk<T> Bk;
   const T* sK = (const T*)(smem + Y::KT);
   const T* sV = (const T*)(smem + Y::VV);
   const float* sB = (const float*)(smem + Y::BETA);
-  const int g = lane >> 4, i = lane & 15;
+  const int lane = ln.lane, g = lane >> 4;
   f32x4 Wk[4];
   typename Bk::Opnd ok[3], ov[3];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const f32x4 b4 = *(const f32x4*)(sB + 16 * b + 4 * g);
-    f32x4 rk = b4 * widen4(colpiece<D>(sK, 16 * b, 16 * w, lane));
-    f32x4 rv = b4 * widen4(colpiece<D>(sV, 16 * b, 16 * w, lane));
+    f32x4 rk = b4 * widen4(colpiece<D>(sK, ln.d, 16 * b, 16 * w));
+    f32x4 rv = b4 * widen4(colpiece<D>(sV, ln.d, 16 * b, 16 * w));
 #pragma unroll
     for (int m = 0; m < b; ++m) {
-      const typename Bk::Coef a = Bk::load(smem + Y::aimg(b, m) + lane * 4 * Y::ES);
+      const typename Bk::Coef a = Bk::load(smem + Y::aimg(b, m) + lane * 16);
       rk = Bk::apply(a, ok[m], rk);
       rv = Bk::apply(a, ov[m], rv);
     }
-    const typename Bk::Coef th = Bk::load(smem + Y::timg(b, 0) + lane * 4 * Y::ES);
-    const typename Bk::Coef tl = Bk::load(smem + Y::timg(b, Bk::NPARTS - 1) + lane * 4 * Y::ES);
-    Wk[b] = Bk::tri(th, tl, Bk::opnd(rk));
-    Wv[b] = Bk::tri(th, tl, Bk::opnd(rv));
+    const typename Bk::Coef t1 = Bk::load(smem + Y::timg(b) + lane * 16);
+    const typename Bk::Coef t2 = Bk::TRI2 ? Bk::load(smem + Y::timg(b) + Bk::TRI2 + lane * 16) : t1;
+    Wk[b] = Bk::tri(t1, t2, Bk::opnd(rk));
+    Wv[b] = Bk::tri(t1, t2, Bk::opnd(rv));
     if (b < 3) {
       ok[b] = Bk::opnd(Wk[b]);
       ov[b] = Bk::opnd(Wv[b]);
@@ -681,7 +718,7 @@ __device__ __forceinline__ void substitute(unsigned char* smem, int w, int lane,
   T* sW = (T*)(smem + Y::WKT);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    T* p = sW + sidx<C>(16 * w + i, 16 * b + 4 * g);
+    T* p = sW + ln.c.row + 16 * w * (C + 16) + 16 * b;
     if constexpr (sizeof(T) == 2) *(s16x4*)p = to_bf16x4(Wk[b]);
     else *(f32x4*)p = Wk[b];
   }
@@ -712,8 +749,8 @@ __device__ __forceinline__ typename Frag<T>::type pfrag(const unsigned char* sme
 // earlier rather than for the one just before it.
 template <typename T, int D>
 __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f32x4 (&S)[D / 16],
-                                          const f32x4 (&Wv)[4], int w, int lane, T* __restrict__ o, int64_t tokc,
-                                          int clen, int H, int h) {
+                                          const f32x4 (&Wv)[4], int w, const Lanes<T, D>& ln,
+                                          __amdgpu_buffer_rsrc_t ro, int H) {
   typedef Lay<T, D, true> Y;
   typedef typename Frag<T>::type FragT;
   constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
@@ -721,7 +758,7 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
   const T* sH = (const T*)(smem + Y::kh(buf));
   const T* sW = (const T*)(smem + Y::WKT);
   const float* sG = (const float*)(smem + Y::gam(buf));
-  const int g = lane >> 4, i = lane & 15;
+  const int lane = ln.lane, g = lane >> 4, i = lane & 15;
   FragT SB[NKD];
 #pragma unroll
   for (int kb = 0; kb < NKD; ++kb) SB[kb] = Frag<T>::from_acc(S, kb);
@@ -730,12 +767,12 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
   {
     FragT a[2][NKD];
 #pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) a[0][kb] = colfrag<C>(sW, kb * KB, 0, lane);
+    for (int kb = 0; kb < NKD; ++kb) a[0][kb] = colfrag<C>(sW, ln.c, kb * KB, 0);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       if (rt + 1 < 4) {
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) a[(rt + 1) & 1][kb] = colfrag<C>(sW, kb * KB, 16 * (rt + 1), lane);
+        for (int kb = 0; kb < NKD; ++kb) a[(rt + 1) & 1][kb] = colfrag<C>(sW, ln.c, kb * KB, 16 * (rt + 1));
       }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -751,7 +788,7 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
     FragT q[2][NKD], pf[2][NKC];
     auto fetch = [&](int rt, FragT (&qq)[NKD], FragT (&pp)[NKC]) {
 #pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) qq[kb] = rowfrag<D>(sQ, 16 * rt + i, kb * KB, g);
+      for (int kb = 0; kb < NKD; ++kb) qq[kb] = rowfrag<D>(sQ, ln.d, 16 * rt, kb * KB);
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
         if (kb * KB <= 16 * rt + 15) pp[kb] = pfrag<T, D>(smem, rt, kb, lane);
@@ -766,14 +803,14 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
         if (kb * KB <= 16 * rt + 15) acc = mma(UB[kb], pf[rt & 1][kb], acc);
-      if (16 * rt + i < clen) {
-        T* dst = o + ((size_t)(tokc + 16 * rt + i) * H + h) * D + 16 * w + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          const uint2 p = __builtin_bit_cast(uint2, to_bf16x4(acc));
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x2nt, p), (u32x2nt*)dst);
-        } else {
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4nt, acc), (u32x4nt*)dst);
-        }
+      // rows past the chunk's end fall outside the resource: not written
+      const uint32_t voff = (uint32_t)((i * H * D + 16 * w + 4 * g) * (int)sizeof(T));
+      const int soff = 16 * rt * H * D * (int)sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        const uint2 p = __builtin_bit_cast(uint2, to_bf16x4(acc));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2nt, p), ro, voff, soff, 2);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4nt, acc), ro, voff, soff, 2);
       }
     }
   }
@@ -783,7 +820,7 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb) a[0][r][kb] = colfrag<D>(sH, kb * KB, 16 * r, lane);
+      for (int kb = 0; kb < NKC; ++kb) a[0][r][kb] = colfrag<D>(sH, ln.d, kb * KB, 16 * r);
 #pragma unroll
     for (int rp = 0; rp < NR / 2; ++rp) {
       if (rp + 1 < NR / 2) {
@@ -791,7 +828,7 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
         for (int r = 0; r < 2; ++r)
 #pragma unroll
           for (int kb = 0; kb < NKC; ++kb)
-            a[(rp + 1) & 1][r][kb] = colfrag<D>(sH, kb * KB, 16 * (2 * rp + 2 + r), lane);
+            a[(rp + 1) & 1][r][kb] = colfrag<D>(sH, ln.d, kb * KB, 16 * (2 * rp + 2 + r));
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
@@ -807,14 +844,14 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
 // The map sweep's step: B (from 0) and M (from I, value part of U off).
 template <typename T, int D>
 __device__ __forceinline__ void state_map(const unsigned char* smem, int buf, f32x4 (&B)[D / 16],
-                                          f32x4 (&M)[D / 16], const f32x4 (&Wv)[4], int lane) {
+                                          f32x4 (&M)[D / 16], const f32x4 (&Wv)[4], const Lanes<T, D>& ln) {
   typedef Lay<T, D, false> Y;
   typedef typename Frag<T>::type FragT;
   constexpr int KB = Elem<T>::KB, NKD = D / KB, NKC = C / KB, NR = D / 16;
   const T* sH = (const T*)(smem + Y::kh(buf));
   const T* sW = (const T*)(smem + Y::WKT);
   const float* sG = (const float*)(smem + Y::gam(buf));
-  const int g = lane >> 4;
+  const int g = ln.lane >> 4;
   FragT BB[NKD], MB[NKD];
 #pragma unroll
   for (int kb = 0; kb < NKD; ++kb) {
@@ -825,12 +862,12 @@ __device__ __forceinline__ void state_map(const unsigned char* smem, int buf, f3
   {
     FragT a[2][NKD];
 #pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) a[0][kb] = colfrag<C>(sW, kb * KB, 0, lane);
+    for (int kb = 0; kb < NKD; ++kb) a[0][kb] = colfrag<C>(sW, ln.c, kb * KB, 0);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       if (rt + 1 < 4) {
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) a[(rt + 1) & 1][kb] = colfrag<C>(sW, kb * KB, 16 * (rt + 1), lane);
+        for (int kb = 0; kb < NKD; ++kb) a[(rt + 1) & 1][kb] = colfrag<C>(sW, ln.c, kb * KB, 16 * (rt + 1));
       }
       f32x4 ab = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -851,12 +888,12 @@ __device__ __forceinline__ void state_map(const unsigned char* smem, int buf, f3
   {
     FragT a[2][NKC];
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) a[0][kb] = colfrag<D>(sH, kb * KB, 0, lane);
+    for (int kb = 0; kb < NKC; ++kb) a[0][kb] = colfrag<D>(sH, ln.d, kb * KB, 0);
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
       if (rr + 1 < NR) {
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) a[(rr + 1) & 1][kb] = colfrag<D>(sH, kb * KB, 16 * (rr + 1), lane);
+        for (int kb = 0; kb < NKC; ++kb) a[(rr + 1) & 1][kb] = colfrag<D>(sH, ln.d, kb * KB, 16 * (rr + 1));
       }
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb) {
@@ -968,14 +1005,18 @@ kda_chunk_sweep(const ChunkInputs in, const int32_t* __restrict__ cu, const int6
   // 0-3 take the element-wise stage first, waves 4-7 the state step, so that
   // the two waves sharing a SIMD feed its VALU and its matrix core at once.
   f32x4 Wv[4];
-  auto state = [&](int jj, int lane) {
+  auto state = [&](int jj, const Lanes<T, D>& ln) {
     const int buf = (jj - j0) & 1;
     if constexpr (OUT) {
-      state_out<T, D>(smem, buf, X[0], Wv, wave, lane, o, sg.tok0 + (int64_t)C * jj, min(C, sg.len - C * jj), H, h);
+      // o rows of the chunk as one buffer resource (rows past its end are not written)
+      const int cl = min(C, sg.len - C * jj);
+      const __amdgpu_buffer_rsrc_t ro =
+          rsrc(o + ((size_t)(sg.tok0 + (int64_t)C * jj) * H + h) * D, ((uint32_t)(cl - 1) * H * D + D) * sizeof(T));
+      state_out<T, D>(smem, buf, X[0], Wv, wave, ln, ro, H);
       if (states && (jj + 1) % every == 0 && (int64_t)(jj + 1) * C <= sg.len)
         put_state(states + ((size_t)(sg.slot0 + (jj + 1) / every - 1) * H + h) * D * D);
     } else {
-      state_map<T, D>(smem, buf, X[0], X[OUT ? 0 : 1], Wv, lane);
+      state_map<T, D>(smem, buf, X[0], X[OUT ? 0 : 1], Wv, ln);
     }
   };
   for (int j = j0; j < j1; ++j) {
@@ -986,22 +1027,23 @@ kda_chunk_sweep(const ChunkInputs in, const int32_t* __restrict__ cu, const int6
     // across it, which would overflow the registers
     int tid = tid0, lane = lane0;
     asm volatile("" : "+v"(tid), "+v"(lane));
+    const Lanes<T, D> ln(lane);
     float g0[8], g1[8];
     estage1<T, D, OUT, MX, OUT>(smem, raw, g_floor, gate, tid, g0, g1);
     lds_barrier();  // partial sums visible; the previous chunk's local stages are done
     const bool prev = Y::OVL && j > j0;
-    if (prev && wave >= 4) state(j - 1, lane);
+    if (prev && wave >= 4) state(j - 1, ln);
     estage2<T, D, OUT, MX, OUT>(smem, buf, raw, tid, g0, g1);
     if (j + 1 < j1) raw.load(in, tokc + C, min(C, sg.len - C * (j + 1)), H, h, tid, gate);
-    if (prev && wave < 4) state(j - 1, lane);
+    if (prev && wave < 4) state(j - 1, ln);
     lds_barrier();
-    gram_stage<T, D, OUT>(smem, buf, wave, lane);
+    gram_stage<T, D, OUT>(smem, buf, wave, ln);
     lds_barrier();
-    substitute<T, D, OUT>(smem, wave, lane, Wv);
+    substitute<T, D, OUT>(smem, wave, ln, Wv);
     lds_barrier();
-    if (!Y::OVL) state(j, lane);
+    if (!Y::OVL) state(j, ln);
   }
-  if (Y::OVL && j1 > j0) state(j1 - 1, lane0);
+  if (Y::OVL && j1 > j0) state(j1 - 1, Lanes<T, D>(lane0));
   if constexpr (OUT) {
     if (ht && sg.s == sg.nseg - 1) put_state(ht + ((size_t)sg.n * H + h) * D * D);
   } else {
