@@ -292,3 +292,36 @@ def test_backward_overlapped_gates(name, mode):
         assert (seq[key] is None) == (ov[key] is None), key
         if seq[key] is not None:
             assert torch.equal(seq[key], ov[key]), key
+
+
+@pytest.mark.parametrize("name", ["f32_B2_T300_d64", "bf16_T4096_H16"])
+def test_backward_timed_matches_sequential(name):
+    """kda_chunk_backward_timed (HIP events recorded on the launch stream
+    before each stage and after the last) returns the plain call's gradients
+    bit for bit, and the stage times it brackets are non-negative and add up
+    to the whole."""
+    if name.startswith("f32"):
+        d = to_dev(_case(2, 300, 2, 64, "f32", wid=350))
+    else:
+        w = synth.WORKLOADS[1]
+        d = synth.workload_inputs(w, device="cuda")
+        d.update(synth.grad_inputs(d, w.wid, device="cuda"))
+    note(f"chunk_backward timed {name}")
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"])
+    kw = dict(h0=d.get("h0"), dht=d.get("dht"), cu_seqlens=d.get("cu_seqlens"))
+    seq = kda.chunk_backward(*args, **kw)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(kda.BWD_STAGES) + 1)]
+    for e in ev:
+        e.record()  # creates the event
+    torch.cuda.synchronize()
+    timed = kda.chunk_backward(*args, events=[e.cuda_event for e in ev], **kw)
+    torch.cuda.synchronize()
+    for key in GRADS:
+        assert (seq[key] is None) == (timed[key] is None), key
+        if seq[key] is not None:
+            assert torch.equal(seq[key], timed[key]), key
+    parts = [ev[j].elapsed_time(ev[j + 1]) for j in range(len(kda.BWD_STAGES))]
+    total = ev[0].elapsed_time(ev[-1])
+    print(f"{name}: stages " + " ".join(f"{s}={t * 1e3:.1f}us" for s, t in zip(kda.BWD_STAGES, parts)))
+    assert all(t >= 0 for t in parts) and total > 0
+    assert abs(sum(parts) - total) <= 1e-3 + 1e-3 * total
