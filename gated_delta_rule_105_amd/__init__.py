@@ -27,7 +27,7 @@ from ._lib import (BWD_STAGES, CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KD
                    KDA_GATE_NONE, KDA_OK, ChunkDesc, ChunkDescEx, KdaError, status_string, version)
 from . import _lib
 
-__all__ = ["chunk_forward", "chunk_forward_states", "chunk_forward_mx", "chunk_backward", "decode_step",
+__all__ = ["chunk_forward", "chunk_forward_noalloc", "chunk_forward_states", "chunk_forward_mx", "chunk_backward", "decode_step",
            "workspace_bytes", "backward_workspace_bytes", "make_desc", "make_desc_ex", "KdaError", "status_string",
            "version",
            "CHUNK_LAUNCHES", "BWD_STAGES"]
@@ -136,6 +136,43 @@ def chunk_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
     o, ht, _ = _forward(q, k, v, g, beta, h0, cu_seqlens, chunk, g_floor, o, ht, workspace,
                         output_final_state, validate_cu, stream, events, None, 0)
     return o, ht
+
+
+def chunk_forward_noalloc(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,
+                          g_floor: float = -0.125, *, o, ht=None, validate_cu: bool = True,
+                          stream=None) -> None:
+    """chunk_forward through kda_chunk_forward_noalloc, for callers that
+    cannot allocate: no workspace (the library's fixed per-device scratch
+    serves), and the outputs are the caller's: o [B, T, H, d] in q's dtype,
+    ht fp32 [S, H, d, d] or None (final state not written).  KDA gate (g per
+    key channel) only.  Calls on one device must not overlap (they share the
+    scratch); calls ordered on one stream are safe."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    dt = q.dtype
+    _check_dev("q", q, dt)
+    for name, t in (("k", k), ("v", v), ("g", g)):
+        _check_dev(name, t, dt, (B, T, H, d))
+    _check_dev("beta", beta, torch.float32, (B, T, H))
+    n_seqs = 0
+    if cu_seqlens is not None:
+        _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+        n_seqs = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        if validate_cu:
+            check_cu_seqlens(cu_seqlens.cpu(), T)
+    S = n_seqs if n_seqs else B
+    _check_dev("h0", h0, torch.float32, (S, H, d, d))
+    _check_dev("o", o, dt, (B, T, H, d))
+    _check_dev("ht", ht, torch.float32, (S, H, d, d))
+    desc = make_desc(B, T, H, d, dt, n_seqs, chunk, g_floor)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.chunk_forward_noalloc_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                        _ptr(cu_seqlens), _ptr(o), _ptr(ht), stream)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_forward_noalloc")
 
 
 def chunk_forward_states(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 64,

@@ -28,7 +28,8 @@ EXPORTS = ("kda_status_string", "kda_version", "kda_chunk_forward_workspace_size
            "kda_chunk_forward", "kda_chunk_forward_gated", "kda_chunk_forward_timed",
            "kda_chunk_forward_states_count", "kda_chunk_forward_states", "kda_chunk_forward_mx",
            "kda_chunk_backward_workspace_size", "kda_chunk_backward", "kda_chunk_backward_overlapped",
-           "kda_chunk_backward_timed", "kda_decode_step", "kda_decode_step_gated")
+           "kda_chunk_backward_timed", "kda_decode_step", "kda_decode_step_gated",
+           "kda_chunk_forward_noalloc")
 
 # Launches of one kda_chunk_forward call, in stream order (kda_chunk_forward_timed):
 # the map sweep and the output sweep are the two instances of kda_chunk_sweep.
@@ -81,6 +82,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_forward_gated.argtypes = [ctypes.POINTER(ChunkDescEx), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp]
     lib.kda_chunk_forward_gated.restype = ctypes.c_int
+    lib.kda_chunk_forward_noalloc.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 10
+    lib.kda_chunk_forward_noalloc.restype = ctypes.c_int
     lib.kda_chunk_forward_timed.argtypes = [ctypes.POINTER(ChunkDescEx), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp, ctypes.POINTER(vp)]
     lib.kda_chunk_forward_timed.restype = ctypes.c_int
@@ -138,6 +141,11 @@ def chunk_forward_gated_raw(dx: ChunkDescEx, q, k, v, g, beta, h0, cu, o, ht, ws
     """Call kda_chunk_forward_gated with raw integer addresses; returns the status."""
     return int(load().kda_chunk_forward_gated(ctypes.byref(dx), q, k, v, g, beta, h0, cu, o, ht, ws,
                                               ctypes.c_size_t(ws_bytes), stream))
+
+
+def chunk_forward_noalloc_raw(desc: ChunkDesc, q, k, v, g, beta, h0, cu, o, ht, stream) -> int:
+    """Call kda_chunk_forward_noalloc with raw integer addresses; returns the status."""
+    return int(load().kda_chunk_forward_noalloc(ctypes.byref(desc), q, k, v, g, beta, h0, cu, o, ht, stream))
 
 
 def chunk_forward_timed_raw(dx: ChunkDescEx, q, k, v, g, beta, h0, cu, o, ht, ws, ws_bytes, stream,

@@ -1,9 +1,11 @@
 // C-ABI front end of the KDA library: argument validation and dispatch.
 //
 // Plain C++: every argument error is reported before any launch (and can be
-// exercised on a machine without a GPU); the only HIP call made here is the
+// exercised on a machine without a GPU); the only HIP calls made here are the
 // compute-unit query behind the forward's cut into segments
-// (kda::device_compute_units).  The entry points and their contracts are
+// (kda::device_compute_units) and, for kda_chunk_forward_noalloc, the lookup
+// of the device scratch's address (kda::scratch_buffer), after every
+// argument check.  The entry points and their contracts are
 // declared in include/kda.h.
 #include "kda.h"
 
@@ -11,6 +13,8 @@
 #include <stdint.h>
 
 #include "kda_launch.h"
+
+static_assert(KDA_NOALLOC_SCRATCH_BYTES == kda::kScratchBytes, "scratch size of the header and the library agree");
 
 static_assert(KDA_GATE_CHANNEL == kda::kGateChannel && KDA_GATE_HEAD == kda::kGateHead &&
                   KDA_GATE_NONE == kda::kGateNone,
@@ -54,7 +58,8 @@ struct Sizes {
 
 bool valid_gate(int gate) { return gate == KDA_GATE_CHANNEL || gate == KDA_GATE_HEAD || gate == KDA_GATE_NONE; }
 
-int check_desc(const kda_chunk_desc_t* d, int gate, Sizes* s) {
+// max_ws: the largest workspace the call can have (the plan keeps to it).
+int check_desc(const kda_chunk_desc_t* d, int gate, Sizes* s, size_t max_ws = SIZE_MAX) {
   if (!d) return KDA_ERR_INVALID_ARGUMENT;
   if (d->B < 1 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1 || d->n_seqs < 0)
     return KDA_ERR_INVALID_ARGUMENT;
@@ -83,8 +88,14 @@ int check_desc(const kda_chunk_desc_t* d, int gate, Sizes* s) {
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   s->n_cu = kda::device_compute_units();
   if (!kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s->n_cu,
-                          &s->plan))
-    return KDA_ERR_UNSUPPORTED;
+                          &s->plan, max_ws)) {
+    // no cut fits max_ws (but one exists), or the sizes overflow
+    kda::SegPlan any;
+    const bool fits_unbounded = max_ws != SIZE_MAX &&
+                                kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H,
+                                                   d->n_seqs > 0, s->n_cu, &any);
+    return fits_unbounded ? KDA_ERR_WORKSPACE_TOO_SMALL : KDA_ERR_UNSUPPORTED;
+  }
   if (s->plan.n_seg_bound > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
@@ -142,13 +153,14 @@ struct MxIn {
 };
 
 // states: NULL (no state emission) or the kda_chunk_forward_states buffer,
-// with every >= 1.
+// with every >= 1.  scratch_ws: the workspace is the library's fixed device
+// scratch (workspace must be NULL), taken after every argument check.
 static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, const void* k, const void* v,
                          const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens, void* o,
                          float* ht, float* states, int every, const MxIn* mx, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* events) {
+                         size_t workspace_bytes, void* stream, void* const* events, bool scratch_ws = false) {
   Sizes s;
-  const int st = check_desc(d, gate, &s);
+  const int st = check_desc(d, gate, &s, scratch_ws ? kda::kScratchBytes : SIZE_MAX);
   if (st != KDA_OK) return st;
   const bool has_tokens = s.tokens > 0;
   // bytes of q, k, v (MXFP8: one byte per element) and of each scale tensor
@@ -168,7 +180,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, con
     if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
   const size_t ws_need = s.plan.ws_bytes;
-  if (ws_need > 0) {
+  if (!scratch_ws && ws_need > 0) {
     if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   }
@@ -202,6 +214,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, con
       overlap(rs, rw))
     return KDA_ERR_INVALID_ARGUMENT;
   if (!ht && s.tokens == 0 && !events) return KDA_OK;  // nothing to write (no full chunk: no states either)
+  if (scratch_ws && ws_need > 0 && kda::scratch_buffer(&workspace) != 0) return KDA_ERR_HIP;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const kda::ChunkInputs in{q, k, v, g, beta, mx ? mx->qs : nullptr, mx ? mx->ks : nullptr, mx ? mx->vs : nullptr};
   const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
@@ -227,6 +240,13 @@ int kda_chunk_forward_gated(const kda_chunk_desc_ex_t* d, const void* q, const v
                             void* o, float* ht, void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_forward(shape_of(d), gate_of(d), q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr,
                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int kda_chunk_forward_noalloc(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                              const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                              void* o, float* ht, void* stream) {
+  return chunk_forward(d, KDA_GATE_CHANNEL, q, k, v, g, beta, h0, cu_seqlens, o, ht, nullptr, 0, nullptr, nullptr,
+                       0, stream, nullptr, true);
 }
 
 int kda_chunk_forward_timed(const kda_chunk_desc_ex_t* d, const void* q, const void* k, const void* v,

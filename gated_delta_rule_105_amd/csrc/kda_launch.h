@@ -2,6 +2,7 @@
 // and the HIP translation units that hold the kernels.
 #pragma once
 
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -58,8 +59,10 @@ constexpr double kMapChunkUs = 3.0, kOutChunkUs = 3.0, kScanStepUs = 1.1;
 // both sweeps).  Host-only, deterministic in its arguments.  `packed`:
 // n_rows sequences share T tokens (lengths unknown on the host; the mean
 // length is used), else n_rows rows of T tokens each.  n_cu: compute units
-// of the device.  Returns false on overflow.
-inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool packed, int n_cu, SegPlan* p) {
+// of the device.  max_ws: cuts whose workspace exceeds it are not taken.
+// Returns false on overflow, or when no cut fits max_ws.
+inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool packed, int n_cu, SegPlan* p,
+                          size_t max_ws = SIZE_MAX) {
   (void)esz;
   const double sc = (double)d * d / (128.0 * 128.0);
   const double t_map = kMapChunkUs * sc, t_out = kOutChunkUs * sc, t_scan = kScanStepUs * sc;
@@ -70,12 +73,20 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
   if (per_seq < 1) per_seq = 1;
   const int64_t pairs = (int64_t)n_rows * H;
   auto rounds = [&](int64_t wg) { return (double)((wg + cus - 1) / cus); };
+  const size_t rec_bytes = (size_t)3 * d * d * sizeof(float);
+  const size_t seq_bytes = packed ? (size_t)2 * ((size_t)n_rows + 1) * sizeof(int64_t) : 0;
+  // workspace of a cut into segments of L chunks (0: one segment per sequence)
+  auto ws_of = [&](int64_t L) -> double {
+    const double recs = L > 0 ? (double)group_bound(T, n_rows, packed, L) * (double)H * (double)rec_bytes : 0.0;
+    return ceil(recs / 256.0) * 256.0 + (double)seq_bytes;
+  };
+  if (ws_of(0) > (double)max_ws) return false;
   double best = rounds(pairs) * (double)per_seq * t_out;  // one segment per sequence
   int best_l = 0;
   for (int64_t L = 1; L < per_seq; L *= 2) {
     const int64_t segs = (per_seq + L - 1) / L;
     const double t = rounds(pairs * segs) * (double)L * (t_map + t_out) + (double)(segs - 1) * t_scan;
-    if (t < best) {
+    if (t < best && ws_of(L) <= (double)max_ws) {
       best = t;
       best_l = (int)L;
     }
@@ -84,14 +95,23 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
   // without maps a packed batch needs its longest sequence to fit one segment
   p->seg_chunks = p->maps ? best_l : (int)(packed ? (chunks_total > 0 ? chunks_total : 1) : per_seq);
   p->n_seg_bound = group_bound(T, n_rows, packed, p->seg_chunks);
-  p->rec_bytes = (size_t)3 * d * d * sizeof(float);
+  p->rec_bytes = rec_bytes;
   const int64_t hh = H > 0 ? H : 1;
   if (p->n_seg_bound > ((int64_t)1 << 36) / hh || chunks_total > ((int64_t)1 << 36) / hh) return false;
   const size_t recs = p->maps ? (size_t)p->n_seg_bound * (size_t)H * p->rec_bytes : 0;
   p->seq_off = (recs + 255) / 256 * 256;
-  p->ws_bytes = packed ? p->seq_off + (size_t)2 * ((size_t)n_rows + 1) * sizeof(int64_t) : recs;
-  return true;
+  p->ws_bytes = packed ? p->seq_off + seq_bytes : recs;
+  return p->ws_bytes <= max_ws;
 }
+
+// Fixed device scratch of the allocation-free forward
+// (kda_chunk_forward_noalloc): one array per device, in the library's code
+// object, that every such call on the device shares.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+
+// Device address of the current device's scratch array (looked up once per
+// device, then kept).  Returns a hipError_t.
+int scratch_buffer(void** ptr);
 
 // The inputs of one chunked forward.  q, k, v are in the operand type, or
 // with MXFP8 inputs (qs != null) e4m3 bytes whose blocks of 32 channels

@@ -40,10 +40,19 @@
 // triangular system is solved by 16-row blocks: the diagonal blocks'
 // inverses by substitution, the rest by MFMA block products.  Wave w owns
 // 16 value columns: columns of W, U, O and S never mix.
+#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
 #include "kda_launch.h"
+
+// Scratch of the allocation-free forward: segment records and packed prefix
+// sums of kda_chunk_forward_noalloc, one copy per device, held from the
+// library's load until the process ends.  Host code never uses this name as
+// an address (on the host it is a stand-in, not device memory): the device
+// address comes from kda::scratch_buffer.  Every word a call reads is
+// written earlier in the same call, so nothing is cleared between calls.
+static __device__ __align__(256) unsigned char scratch[kda::kScratchBytes];
 
 namespace kda {
 namespace {
@@ -1268,6 +1277,26 @@ int launch_typed(int n_rows, int T_per, int H, const SegPlan& plan, float g_floo
 }
 
 }  // namespace
+
+int scratch_buffer(void** ptr) {
+  constexpr int kMaxDevices = 256;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current: its copy
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return (int)hipSuccess;
+}
 
 int device_compute_units() {
   int dev = 0, n = 0;

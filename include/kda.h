@@ -36,12 +36,14 @@
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
  *     16-byte aligned.  The caller owns every buffer; the library allocates
- *     nothing, never synchronises, keeps no global state and is reentrant.
+ *     nothing, never synchronises and is reentrant.  Its one piece of global
+ *     state is the fixed device scratch of kda_chunk_forward_noalloc.
  *   - Arguments are validated on the host before any launch, so argument
  *     errors come back as status codes even on a machine without a GPU.  The
  *     only HIP calls before the launches are one device-attribute query
  *     (the current device's compute units, which the chunked forward's cut
- *     into segments depends on; 256 when no device answers) and nothing else.
+ *     into segments depends on; 256 when no device answers) and, in
+ *     kda_chunk_forward_noalloc, the device address of its scratch.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and is asynchronous: results are valid once the caller synchronises.
  *   - A failed launch returns KDA_ERR_HIP: each launch's own status is
@@ -163,6 +165,31 @@ int kda_chunk_forward_gated(const kda_chunk_desc_ex_t* d,
                             void* o, float* ht,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * kda_chunk_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call with no workspace argument.  Its workspace is a
+ * fixed scratch array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) in the library's
+ * device code, one per device, held from the library's load on that device
+ * until the process ends; the call itself allocates nothing.  The cut into
+ * segments keeps to that size (at H = 16 the best cut needs 48 MiB, and
+ * shapes whose best cut needs more take the best one that fits); a call
+ * whose smallest cut does not fit (more than about 4 million packed
+ * sequences) returns KDA_ERR_WORKSPACE_TOO_SMALL before any launch.  Calls
+ * on one device share its scratch: two calls in flight at once on one
+ * device (on different streams, or from different threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * Nothing in the scratch needs clearing between calls.  Everything else as
+ * kda_chunk_forward; on the same plan the results are bit-identical to it.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_chunk_forward_noalloc(const kda_chunk_desc_t* d,
+                              const void* q, const void* k, const void* v, const void* g,
+                              const float* beta, const float* h0,
+                              const int32_t* cu_seqlens,
+                              void* o, float* ht,
+                              void* stream);
 
 /*
  * Measurement twin of kda_chunk_forward_gated: the same call, and in

@@ -443,3 +443,25 @@ def test_chunk_backward_overlapped_rejects(lib):
     with pytest.raises(ValueError):
         _lib.chunk_backward_raw(ChunkDescEx(shape=d, gate=0), *(a[n] for n in BWD_NAMES), a["ws_bytes"], None,
                                 [0] * 5, (side, ev1, ev2))
+
+
+def test_chunk_forward_noalloc_rejects(lib):
+    """The allocation-free forward checks its arguments like kda_chunk_forward
+    (before its scratch lookup), and refuses a call whose smallest cut needs
+    more than its fixed scratch."""
+    d = desc()
+    a = fake_args(lib, d)
+
+    def noalloc(dd, **over):
+        p = dict(a, **over)
+        return _lib.chunk_forward_noalloc_raw(dd, p["q"], p["k"], p["v"], p["g"], p["beta"], p["h0"], p["cu"],
+                                              p["o"], p["ht"], None)
+
+    assert _lib.load().kda_chunk_forward_noalloc(None, *([None] * 10)) == KDA_ERR_INVALID_ARGUMENT
+    assert noalloc(d, o=None) == KDA_ERR_INVALID_ARGUMENT
+    assert noalloc(d, q=a["q"] + 8) == KDA_ERR_INVALID_ARGUMENT                 # misaligned
+    assert noalloc(d, o=a["q"] + 1024) == KDA_ERR_INVALID_ARGUMENT              # o overlaps q
+    assert noalloc(desc(d_k=96, d_v=96)) == KDA_ERR_UNSUPPORTED
+    # 5,000,000 packed sequences: their prefix sums alone exceed the 64 MiB scratch
+    many = desc(T=5_000_000, n_seqs=5_000_000, H=1)
+    assert noalloc(many, cu=7 * 64 * GB) == KDA_ERR_WORKSPACE_TOO_SMALL
