@@ -20,8 +20,9 @@ recorded on the launch stream between the call's launches): its share of the
 algorithmic bytes (``LAUNCH_WORK``) divided by its mean duration, against HBM;
 ``call_roofline`` and ``mfma`` do the same for the whole call.
 ``cpu_baseline`` times the fp64 CPU oracle on the host cores (a baseline, not
-a target).  ``other_workloads`` times the packed 8-sequence batch and the
-1,048,576-token context; ``states_workloads`` times the headline call with
+a target).  ``other_workloads`` times the packed 8-sequence batch, the
+1,048,576-token context and a serving-like batch (512 packed sequences of
+64-512 tokens, H=32); ``states_workloads`` times the headline call with
 prefix-cache states (kda_chunk_forward_states) beside plain calls;
 ``gate_workloads`` times Gated DeltaNet and DeltaNet gates beside KDA on the
 prefill and decode workloads; ``mx_workload`` the headline workload with q,
@@ -540,9 +541,40 @@ def bench_decode(steps: int, warmup: int):
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
     mean_step = sum(durs) / len(durs)
     log(f"decode {steps} steps: wall {wall * 1e3:.3f} ms, mean step {mean_step * 1e6:.2f} us")
+    # the same steps captured once in a HIP graph (no launch gaps between the
+    # steps), replayed; one event pair around each replay
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                call(warmup + i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    reps = 3
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in gev:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    graph_step = min(a.elapsed_time(b) for a, b in gev) * 1e-3 / steps
+    log(f"decode {steps} steps as one graph: best of {reps} replays, {graph_step * 1e6:.2f} us per step")
+    del graph
     state_b = N * H * d * d * 4
     bytes_step = 2 * state_b + N * H * (5 * d * 2 + 4)
-    return dict(wall=wall, mean_step=mean_step, steps=steps, bytes_step=bytes_step)
+    return dict(wall=wall, mean_step=mean_step, steps=steps, bytes_step=bytes_step, graph_step=graph_step)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline():
@@ -562,6 +594,7 @@ def cpu_baseline():
             break
     log(f"cpu oracle: {reps} full passes in {el:.2f} s on {threads} threads")
     return {"value": reps * B * T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{reps} full passes of the prefill workload (B=1, H=16, T=4096, d=128), fp64 "
                       f"token-by-token recurrence, OpenMP over the 16 heads, {el:.1f} s"}
 
@@ -622,9 +655,9 @@ def main() -> int:
                        "issued_frac": issued / p["mean_call"] / 1e12 / PEAK_BF16_TFLOPS}
         out["config"]["buffer_sets"] = p["n_sets"]
     if args.only in ("prefill", "both") and not args.no_extra:
-        # the packed 8-sequence batch and the million-token context, timed the
+        # the packed 8-sequence batch, the million-token context and the serving batch, timed the
         # same way (secondary lines: the headline value is the workload above)
-        out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3)]
+        out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3), bench_workload(5, 20)]
         out["states_workloads"] = bench_states(50)
         out["gate_workloads"] = bench_gates(50, 100)
         out["mx_workload"] = bench_mx(100)
@@ -637,6 +670,8 @@ def main() -> int:
         out["decode"] = {"workload": "kda-decode-bf16-N256-H32-d128-fp32-state-in-place",
                          "value": dd["steps"] / dd["wall"], "unit": "steps/s",
                          "mean_step_us": dd["mean_step"] * 1e6,
+                         "graph_step_us": dd["graph_step"] * 1e6,
+                         "graph_hbm_frac": dd["bytes_step"] / dd["graph_step"] / 1e9 / PEAK_HBM_GBS,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": gbs / PEAK_HBM_GBS, "kernel": "kda_decode",
                                       "algorithmic_bytes": dd["bytes_step"],

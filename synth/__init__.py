@@ -69,6 +69,10 @@ WORKLOADS = {
                 dk=128, dv=128, dtype="bf16", B=1, T=1 << 20, h0=True),
     4: Workload(4, "kda-decode-bf16-N256-H32-d128-1000steps", "decode", H=32,
                 dk=128, dv=128, dtype="bf16", N=256, steps=1000, h0=True),
+    # a serving-like batch: many short requests packed into one call
+    5: Workload(5, "kda-prefill-serving-bf16-512seq-L64..512-H32-d128", "prefill",
+                H=32, dk=128, dv=128, dtype="bf16", n_seqs=512,
+                len_range=(64, 512), h0=True),
 }
 
 

@@ -432,6 +432,39 @@ def test_decode_config4_1000_steps():
     print(f"workload4 (8192 pairs x 1000 steps): worst err_o={worst_o:.3e} worst err_state={worst_s:.3e}")
 
 
+def test_decode_graph_replays_match_eager():
+    """Five decode steps captured in one HIP graph and replayed three times
+    from the same starting state, with eager work between the replays: every
+    replay's outputs and final state equal the eager steps' bit for bit."""
+    N, H, d, steps = 8, 4, 128, 5
+    inp = synth.decode_inputs(N, H, d, d, steps, "bf16", wid=230, device="cuda")
+    note(f"decode graph N{N} H{H} d{d} x{steps}")
+    eager_state = inp["state"].clone()
+    eager_o = [kda.decode_step(*(inp[key][s] for key in ("q", "k", "v", "g", "beta")), eager_state).clone()
+               for s in range(steps)]
+    state = inp["state"].clone()
+    outs = torch.empty((steps, N, H, d), dtype=torch.bfloat16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for s in range(steps):
+                kda.decode_step(*(inp[key][s] for key in ("q", "k", "v", "g", "beta")), state, o=outs[s])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        state.copy_(inp["state"])
+        outs.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs[s], eager_o[s]), (r, s)
+        assert torch.equal(state, eager_state), r
+        torch.cuda.synchronize()
+        _ = (eager_state * 2).sum().item()  # eager work between the replays
+
+
 def test_chunk_forward_in_place_state():
     """ht may alias h0: the final state overwrites the initial one, with the
     sequence spread over many segments."""
