@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(HERE, "libkda.so")
+# KDA_LIBRARY selects another build of the same library (the host-sanitizer
+# build of the C front end, for instance); default: the in-tree build.
+LIBRARY = os.environ.get("KDA_LIBRARY") or os.path.join(HERE, "libkda.so")
 
 KDA_OK = 0
 KDA_ERR_INVALID_ARGUMENT = 1

@@ -11,6 +11,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "kda_launch.h"
 
@@ -43,7 +44,19 @@ bool mul(size_t a, size_t b, size_t* out) {
   return true;
 }
 
-size_t elem_size(kda_dtype_t t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
+// Enum-typed arguments as their int representation: a C caller may store any
+// int in them, and loading a value outside the enumerators through the enum
+// type is undefined in C++, so they are only ever read this way.
+template <typename E>
+int as_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+int dtype_of(const kda_chunk_desc_t* d) { return as_int(d->dtype); }
+
+size_t elem_size(int t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
 
 struct Sizes {
   size_t tokens;      // B * T
@@ -63,7 +76,7 @@ int check_desc(const kda_chunk_desc_t* d, int gate, Sizes* s, size_t max_ws = SI
   if (!d) return KDA_ERR_INVALID_ARGUMENT;
   if (d->B < 1 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1 || d->n_seqs < 0)
     return KDA_ERR_INVALID_ARGUMENT;
-  if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (dtype_of(d) != KDA_DTYPE_F32 && dtype_of(d) != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
   if (!valid_gate(gate)) return KDA_ERR_INVALID_ARGUMENT;
   if (d->n_seqs > 0 && d->B != 1) return KDA_ERR_INVALID_ARGUMENT;
   if (!(d->g_floor >= -1.0f && d->g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;  // NaN fails too
@@ -71,28 +84,28 @@ int check_desc(const kda_chunk_desc_t* d, int gate, Sizes* s, size_t max_ws = SI
   if (d->d_k != d->d_v) return KDA_ERR_UNSUPPORTED;
   if (d->d_k != 64 && d->d_k != 128) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
-  if (d->dtype == KDA_DTYPE_F32 && d->d_k != 64) return KDA_ERR_UNSUPPORTED;  // fp32 tiles fit LDS at d = 64
+  if (dtype_of(d) == KDA_DTYPE_F32 && d->d_k != 64) return KDA_ERR_UNSUPPORTED;  // fp32 tiles fit LDS at d = 64
 
   const size_t B = (size_t)d->B, T = (size_t)d->T, H = (size_t)d->H, D = (size_t)d->d_k;
   s->n_states = d->n_seqs > 0 ? (size_t)d->n_seqs : B;
   if (!mul(B, T, &s->tokens)) return KDA_ERR_INVALID_ARGUMENT;
   size_t th, x;
-  if (!mul(s->tokens, H, &th) || !mul(th, D, &x) || !mul(x, elem_size(d->dtype), &s->x_bytes))
+  if (!mul(s->tokens, H, &th) || !mul(th, D, &x) || !mul(x, elem_size(dtype_of(d)), &s->x_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
   if (!mul(th, 4, &s->beta_bytes)) return KDA_ERR_INVALID_ARGUMENT;
-  s->g_bytes = gate == KDA_GATE_CHANNEL ? s->x_bytes : gate == KDA_GATE_HEAD ? th * elem_size(d->dtype) : 0;
+  s->g_bytes = gate == KDA_GATE_CHANNEL ? s->x_bytes : gate == KDA_GATE_HEAD ? th * elem_size(dtype_of(d)) : 0;
   size_t sh, sd;
   if (!mul(s->n_states, H, &sh) || !mul(sh, D * D, &sd) || !mul(sd, 4, &s->state_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
   if (s->tokens > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   s->n_cu = kda::device_compute_units();
-  if (!kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s->n_cu,
+  if (!kda::plan_segments(d->d_k, (int)elem_size(dtype_of(d)), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s->n_cu,
                           &s->plan, max_ws)) {
     // no cut fits max_ws (but one exists), or the sizes overflow
     kda::SegPlan any;
     const bool fits_unbounded = max_ws != SIZE_MAX &&
-                                kda::plan_segments(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H,
+                                kda::plan_segments(d->d_k, (int)elem_size(dtype_of(d)), rows, (int64_t)d->T, d->H,
                                                    d->n_seqs > 0, s->n_cu, &any);
     return fits_unbounded ? KDA_ERR_WORKSPACE_TOO_SMALL : KDA_ERR_UNSUPPORTED;
   }
@@ -166,7 +179,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, con
   // bytes of q, k, v (MXFP8: one byte per element) and of each scale tensor
   size_t qkv_bytes = s.x_bytes, sc_bytes = 0;
   if (mx) {
-    if (d->dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;  // MXFP8 inputs feed the bf16 path
+    if (dtype_of(d) != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;  // MXFP8 inputs feed the bf16 path
     qkv_bytes = s.x_bytes / 2;
     sc_bytes = qkv_bytes / 32;
     if (has_tokens && (!mx->qs || !mx->ks || !mx->vs)) return KDA_ERR_INVALID_ARGUMENT;
@@ -217,7 +230,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, con
   if (scratch_ws && ws_need > 0 && kda::scratch_buffer(&workspace) != 0) return KDA_ERR_HIP;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const kda::ChunkInputs in{q, k, v, g, beta, mx ? mx->qs : nullptr, mx ? mx->ks : nullptr, mx ? mx->vs : nullptr};
-  const int e = kda::launch_chunk_forward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
+  const int e = kda::launch_chunk_forward(dtype_of(d) == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, s.plan,
                                           d->g_floor, gate, in, h0, cu_seqlens, o, ht,
                                           states_bytes > 0 ? states : nullptr, every, workspace, stream,
                                           events);
@@ -226,7 +239,7 @@ static int chunk_forward(const kda_chunk_desc_t* d, int gate, const void* q, con
 
 // the extended descriptor: its shape, and its gate (NULL: invalid)
 static const kda_chunk_desc_t* shape_of(const kda_chunk_desc_ex_t* d) { return d ? &d->shape : nullptr; }
-static int gate_of(const kda_chunk_desc_ex_t* d) { return d ? (int)d->gate : KDA_GATE_CHANNEL; }
+static int gate_of(const kda_chunk_desc_ex_t* d) { return d ? as_int(d->gate) : KDA_GATE_CHANNEL; }
 
 int kda_chunk_forward(const kda_chunk_desc_t* d, const void* q, const void* k, const void* v,
                       const void* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
@@ -289,7 +302,7 @@ bool plan_bwd(const kda_chunk_desc_t* d, const Sizes& s, kda::BwdPlan* bp) {
   size_t chunk_states;
   if (!state_slots(d, 1, &chunk_states)) return false;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
-  return kda::plan_backward(d->d_k, (int)elem_size(d->dtype), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s.n_cu,
+  return kda::plan_backward(d->d_k, (int)elem_size(dtype_of(d)), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s.n_cu,
                             s.tokens, chunk_states, bp);
 }
 
@@ -335,7 +348,7 @@ int chunk_backward(const kda_chunk_desc_ex_t* dx, const void* q, const void* k, 
   }
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   const kda::ChunkInputs in{q, k, v, g, beta, nullptr, nullptr, nullptr};
-  const int e = kda::launch_chunk_backward(d->dtype == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, bp, d->g_floor,
+  const int e = kda::launch_chunk_backward(dtype_of(d) == KDA_DTYPE_BF16, d->d_k, rows, d->T, d->H, bp, d->g_floor,
                                            gate, in, h0, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta, dh0,
                                            workspace, stream, events, aux);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
@@ -393,30 +406,31 @@ int kda_decode_step(int N, int H, int d_k, int d_v, kda_dtype_t dtype, float g_f
 int kda_decode_step_gated(int N, int H, int d_k, int d_v, kda_dtype_t dtype, kda_gate_t gate, float g_floor,
                           const void* q, const void* k, const void* v, const void* g, const float* beta,
                           float* state, void* o, void* stream) {
+  const int dt = as_int(dtype), gt = as_int(gate);
   if (N < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
-  if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
-  if (!valid_gate(gate)) return KDA_ERR_INVALID_ARGUMENT;
+  if (dt != KDA_DTYPE_F32 && dt != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (!valid_gate(gt)) return KDA_ERR_INVALID_ARGUMENT;
   if (!(g_floor >= -1.0f && g_floor < 0.0f)) return KDA_ERR_INVALID_ARGUMENT;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
-  const bool gated = gate != KDA_GATE_NONE;
+  const bool gated = gt != KDA_GATE_NONE;
   if (!gated) g = nullptr;  // not read
   if (!q || !k || !v || (gated && !g) || !beta || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {q, k, v, g, beta, state, o};
   for (const void* p : ptrs)
     if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
   size_t nh, x, xb, sb, bb;
-  if (!mul((size_t)N, (size_t)H, &nh) || !mul(nh, (size_t)d_k, &x) || !mul(x, elem_size(dtype), &xb) ||
+  if (!mul((size_t)N, (size_t)H, &nh) || !mul(nh, (size_t)d_k, &x) || !mul(x, elem_size(dt), &xb) ||
       !mul(x, (size_t)d_k * 4, &sb) || !mul(nh, 4, &bb))
     return KDA_ERR_INVALID_ARGUMENT;
   if (nh > (size_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  const size_t gb = gate == KDA_GATE_CHANNEL ? xb : gate == KDA_GATE_HEAD ? nh * elem_size(dtype) : 0;
+  const size_t gb = gt == KDA_GATE_CHANNEL ? xb : gt == KDA_GATE_HEAD ? nh * elem_size(dt) : 0;
   const Range rs = range(state, sb), ro = range(o, xb);
   const Range ins[] = {range(q, xb), range(k, xb), range(v, xb), range(g, gb), range(beta, bb)};
   for (const Range& r : ins)
     if (overlap(rs, r) || overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
   if (overlap(rs, ro)) return KDA_ERR_INVALID_ARGUMENT;
-  const int e = kda::launch_decode_step(dtype == KDA_DTYPE_BF16, d_k, N, H, g_floor, (int)gate, q, k, v, g,
+  const int e = kda::launch_decode_step(dt == KDA_DTYPE_BF16, d_k, N, H, g_floor, gt, q, k, v, g,
                                         beta, state, o, stream);
   return e == 0 ? KDA_OK : KDA_ERR_HIP;
 }

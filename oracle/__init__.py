@@ -48,7 +48,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "kda_oracle.c")
 SOURCE_BWD = os.path.join(_HERE, "kda_oracle_bwd.c")
-LIBRARY = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIBRARY selects another build of the oracle (a sanitizer build);
+# default: the in-tree build, compiled on first use.
+LIBRARY = os.environ.get("KDA_ORACLE_LIBRARY") or os.path.join(_HERE, "libkda_oracle.so")
 
 # No -ffast-math and no -march: IEEE semantics, no contraction into FMA.  -O3
 # vectorises only the loops over the value index, whose sums are independent,

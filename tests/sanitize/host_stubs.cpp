@@ -1,0 +1,33 @@
+// Host-only stand-ins for the kernel launchers and device queries that the C
+// front end (kda_api.cpp) calls, so that it can be built with g++ under the
+// host sanitizers and driven by tests/test_abi.py on a machine without a GPU.
+// A launch does nothing and succeeds; there is no device, so the device
+// queries report none.  Not part of the library.
+#include "kda_launch.h"
+
+namespace kda {
+
+int device_compute_units() { return 0; }
+
+int scratch_buffer(void** ptr) {
+  *ptr = nullptr;
+  return 100;  // hipErrorNoDevice
+}
+
+int launch_chunk_forward(int, int, int, int, int, const SegPlan&, float, int, const ChunkInputs&, const float*,
+                         const int32_t*, void*, float*, float*, int, void*, void*, void* const*) {
+  return 0;
+}
+
+int launch_chunk_backward(int, int, int, int, int, const BwdPlan&, float, int, const ChunkInputs&, const float*,
+                          const int32_t*, const void*, const float*, void*, void*, void*, void*, float*, float*, void*,
+                          void*, void* const*, const AuxStream*) {
+  return 0;
+}
+
+int launch_decode_step(int, int, int, int, float, int, const void*, const void*, const void*, const void*,
+                       const float*, float*, void*, void*) {
+  return 0;
+}
+
+}  // namespace kda
