@@ -1184,7 +1184,7 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   };
   auto step = [&](int s, const Stage& st) {
     Ops::publish(sS[s & 1], wave, lane, Sk);
-    __syncthreads();
+    lds_barrier();  // LDS only: the records fetched ahead stay in flight
     // two accumulators (even and odd k-blocks) keep the MFMA chains short
     f32x4 acc0 = st.b, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

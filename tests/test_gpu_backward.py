@@ -158,6 +158,26 @@ def test_backward_full_workload_sampled_heads():
     assert abs(np.sum(f64(out["dq"]) * q) - do_o) <= 1e-2 * scale
 
 
+def test_backward_long_context_two_heads():
+    """B=1, H=16, T=65,536, d=128 bf16 (the prefill recipe at 16x the
+    length, weak decay so the state gradient crosses many chunks): every
+    gradient element of heads 2 and 13 against the oracle."""
+    T, H, wid = 65536, 16, 360
+    inp = synth.prefill_inputs(1, T, H, 128, 128, "bf16", wid=wid, h0=True)
+    inp["g"] = torch.full_like(inp["g"], -1e-3)
+    inp.update(synth.grad_inputs(inp, wid))
+    note(f"chunk_backward T={T} H={H} d=128 bf16, weak decay")
+    out = _gpu_backward(inp)
+    heads = [2, 13]
+    sub = {key: (val[:, :, heads].contiguous() if key in ("q", "k", "v", "g", "beta", "do") else val)
+           for key, val in inp.items()}
+    sub["h0"] = inp["h0"][:, heads].contiguous()
+    sub["dht"] = inp["dht"][:, heads].contiguous()
+    ref = _oracle_backward(sub)
+    got = {key: (out[key][:, :, heads] if key != "dh0" else out[key][:, heads]) for key in GRADS}
+    _check(f"T={T} heads 2, 13", got, ref, "bf16")
+
+
 def test_backward_packed_workload_sampled_heads():
     """The packed batch (8 sequences, L ~ U[1024, 8192], H=32, d=128, bf16,
     log-decay spread 2): every gradient element of heads 3 and 30 against the
