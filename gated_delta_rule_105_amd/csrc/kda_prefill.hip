@@ -981,15 +981,20 @@ kda_chunk_sweep(const ChunkInputs in, const int32_t* __restrict__ cu, const int6
   // OUT: X[0] = S.  Map sweep: X[0] = B, X[1] = M.
   f32x4 X[OUT ? 1 : 2][NR];
   if (OUT) {
-    const float* h0p = h0 ? h0 + ((size_t)sg.n * H + h) * D * D : nullptr;
+    // uniform branches, so that every load below is unconditional and they
+    // all go out before the first wait
+    if (maps) {
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr) {
-      if (maps) {
-        X[0][rr] = *(const f32x4*)(rec + R::SIN + R::tile(rr, wave, lane0));
-      } else {
+      for (int rr = 0; rr < NR; ++rr) X[0][rr] = *(const f32x4*)(rec + R::SIN + R::tile(rr, wave, lane0));
+    } else if (h0) {
+      const float* h0p = h0 + ((size_t)sg.n * H + h) * D * D + 4 * g * D + 16 * wave + i;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[0][rr][e] = h0p ? h0p[(16 * rr + 4 * g + e) * D + 16 * wave + i] : 0.f;
-      }
+      for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[0][rr][e] = h0p[(16 * rr + e) * D];
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) X[0][rr] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   } else {
 #pragma unroll
