@@ -190,17 +190,17 @@ def bench_prefill(steps: int, warmup: int):
     for i in range(warmup):
         call(sets[i % n_sets])
     torch.cuda.synchronize()
-    # timed region 1: plain calls, an event pair around each (throughput)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # timed region 1: plain calls back to back (throughput), one event pair
+    # around the whole loop (no instrumentation between the calls)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         call(sets[i % n_sets])
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
-    mean_call = sum(durs) / len(durs)
+    mean_call = e0.elapsed_time(e1) * 1e-3 / steps
     # timed region 2: the same calls through kda_chunk_forward_timed, which
     # records HIP events on the launch stream before each launch and after
     # the last (per-launch durations; the events add a little to each)
@@ -216,12 +216,12 @@ def bench_prefill(steps: int, warmup: int):
     torch.cuda.synchronize()
     launch = {name: sum(row[j].elapsed_time(row[j + 1]) for row in evl) / steps * 1e-3
               for j, name in enumerate(kda.CHUNK_LAUNCHES)}
-    log(f"prefill {steps} calls: wall {wall * 1e3:.3f} ms, mean call {mean_call * 1e6:.2f} us; per launch "
+    log(f"prefill {steps} calls: wall {wall * 1e3:.3f} ms, GPU time per call {mean_call * 1e6:.2f} us; per launch "
         + ", ".join(f"{n} {t * 1e6:.2f} us" for n, t in launch.items()))
     token_heads = B * T * H
     bytes_call = token_heads * BYTES_PER_TOKEN_HEAD + 2 * B * H * STATE_BYTES
     flop_call = token_heads * FLOP_PER_TOKEN_HEAD
-    return dict(wall=wall, mean_call=mean_call, min_call=min(durs), tokens=B * T, token_heads=token_heads,
+    return dict(wall=wall, mean_call=mean_call, tokens=B * T, token_heads=token_heads,
                 bytes_call=bytes_call, flop_call=flop_call, n_sets=n_sets, launch=launch)
 
 
@@ -530,17 +530,17 @@ def bench_decode(steps: int, warmup: int):
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # consecutive steps, one event pair around the loop
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         call(warmup + i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
-    mean_step = sum(durs) / len(durs)
-    log(f"decode {steps} steps: wall {wall * 1e3:.3f} ms, mean step {mean_step * 1e6:.2f} us")
+    mean_step = e0.elapsed_time(e1) * 1e-3 / steps
+    log(f"decode {steps} steps: wall {wall * 1e3:.3f} ms, GPU time per step {mean_step * 1e6:.2f} us")
     # the same steps captured once in a HIP graph (no launch gaps between the
     # steps), replayed; one event pair around each replay
     graph = torch.cuda.CUDAGraph()
