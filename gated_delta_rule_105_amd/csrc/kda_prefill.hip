@@ -72,6 +72,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // each lane's addresses into an array differ by immediates only.  Both
 // access patterns used here hit distinct banks within 16 lanes: 16 rows at
 // one unit (row fragments) and 4 rows x 4 units (transpose reads).
+// sidx is the layout's definition (element (t, c) of a [rows][W] array); the
+// accessors (LaneOff, the element-wise stage) form the same offsets as a
+// lane register plus immediates.
 template <int W>
 __device__ __forceinline__ int sidx(int t, int c) {
   return t * (W + 16) + ((((c >> 2) ^ ((t >> 2) & 3))) << 2) + (c & 3);
@@ -1178,9 +1181,9 @@ kda_seg_scan(const float* h0, float* ht, float* __restrict__ ws, const int32_t* 
   // registers.
   const uint32_t m_off = (uint32_t)(R::M * 4 + R::frag(wave, 0, 0, lane));
   const uint32_t b_off = (uint32_t)((R::B + R::tile(wave, ct, lane)) * 4);
-  constexpr int kRecBytes = (int)(R::FLOATS * 4), kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+  constexpr uint32_t kRecBytes = (uint32_t)(R::FLOATS * 4);
   auto fetch = [&](int s, Stage& st) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(rec(s), (short)0, kRecBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t r = rsrc(rec(s), kRecBytes);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) st.m[kb] = Ops::load_m(r, m_off, kb);
     st.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, b_off, 0, 0));

@@ -112,9 +112,9 @@ int kda_version(void);
  * launch; see the conventions above.  Returns KDA_OK or KDA_ERR_* for an
  * invalid or unsupported descriptor.  The workspace holds three d_k x d_v
  * fp32 matrices per (segment, head) when sequences are cut into segments
- * (192 KiB at d = 128; the cut keeps segments to about one per compute unit
- * and head, so 48 MiB at H = 16 for T = 4,096 as for T = 1,048,576), and 16
- * bytes per packed sequence.
+ * (192 KiB at d = 128; the cut aims at about one workgroup per compute unit
+ * over all (segment, head) pairs, so 48 MiB at H = 16 for T = 4,096 as for
+ * T = 1,048,576), and 16 bytes per packed sequence.
  */
 int kda_chunk_forward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
 
