@@ -432,6 +432,32 @@ def test_decode_config4_1000_steps():
     print(f"workload4 (8192 pairs x 1000 steps): worst err_o={worst_o:.3e} worst err_state={worst_s:.3e}")
 
 
+@pytest.mark.parametrize("where", ["k", "g", "state"])
+def test_decode_nan_stays_in_its_pair(where):
+    """A NaN in one (sequence, head) pair's k, log-decay or state reaches that
+    pair's output and state; every other pair is bit-identical to a clean
+    step."""
+    N, H, d = 6, 4, 128
+    inp = synth.decode_inputs(N, H, d, d, 1, "bf16", wid=240, device="cuda")
+    note(f"decode NaN in {where} N{N} H{H} d{d}")
+    args = {key: inp[key][0].clone() for key in ("q", "k", "v", "g", "beta")}
+    clean_state = inp["state"].clone()
+    clean_o = kda.decode_step(*(args[key] for key in ("q", "k", "v", "g", "beta")), clean_state)
+    n, h = 3, 1
+    state = inp["state"].clone()
+    if where == "state":
+        state[n, h, 7, 9] = float("nan")
+    else:
+        args[where][n, h, 5] = float("nan")
+    o = kda.decode_step(*(args[key] for key in ("q", "k", "v", "g", "beta")), state)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[n, h]).any() and torch.isnan(state[n, h]).any()
+    keep = torch.ones((N, H), dtype=torch.bool, device="cuda")
+    keep[n, h] = False
+    assert torch.equal(o[keep], clean_o[keep])
+    assert torch.equal(state[keep], clean_state[keep])
+
+
 def test_decode_graph_replays_match_eager():
     """Five decode steps captured in one HIP graph and replayed three times
     from the same starting state, with eager work between the replays: every

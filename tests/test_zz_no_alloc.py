@@ -1,7 +1,8 @@
 """kda_chunk_forward_noalloc (the forward with the library's fixed device
 scratch as its workspace) against kda_chunk_forward with a caller-allocated
 workspace: two calls in a row, the second on a smaller input (the scratch
-then holds the first call's data), and a third on the fp32 path.  Both entry
+then holds the first call's data), then the fp32 path and 300 packed
+sequences.  Both entry
 points take the same cut into segments on these shapes (the best cut fits
 the scratch), so their results are bit-identical."""
 import pytest
@@ -36,3 +37,6 @@ def test_noalloc_matches_forward_two_calls():
     _compare("bf16 packed [300, 1, 0, 1000, 64] H4 d128", small)
     f32 = synth.prefill_inputs(2, 200, 3, 64, 64, "f32", wid=221, h0=True, device="cuda")
     _compare("f32 B2 T200 H3 d64", f32)
+    many = synth.prefill_inputs(1, 0, 2, 128, 128, "bf16", wid=222, h0=True,
+                                lengths=synth.packed_lengths(222, 300, 0, 200), device="cuda")
+    _compare("bf16 300 packed sequences H2 d128", many)
