@@ -317,7 +317,10 @@ def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chu
     half of the chunks, on a second stream of the device beside the
     state-gradient walk (it forks after the record stage;
     kda_chunk_backward_overlapped, the same results).  Overlapped calls on one device share that stream and its
-    events, so they must be issued from one host thread."""
+    events, so they must be issued from one host thread.  workspace: a uint8
+    device tensor used as it is; the call fits its windows of chunks to its
+    size (smaller than backward_workspace_bytes(...) means narrower windows,
+    too small raises KdaError).  None allocates the default size."""
     torch = _torch()
     B, T, H, d = q.shape
     dt = q.dtype
@@ -353,7 +356,7 @@ def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chu
             out["dg"] = torch.empty(gshape, dtype=dt, device=dev)
         if want_dh0 and out.get("dh0") is None:
             out["dh0"] = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
-        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     for name, shape, odt in (("dq", (B, T, H, d), dt), ("dk", (B, T, H, d), dt), ("dv", (B, T, H, d), dt),
                              ("dbeta", (B, T, H), torch.float32)):

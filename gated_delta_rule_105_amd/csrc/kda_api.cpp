@@ -298,12 +298,14 @@ int kda_chunk_forward_mx(const kda_chunk_desc_ex_t* d, const void* q, const uint
 
 namespace {
 
-bool plan_bwd(const kda_chunk_desc_t* d, const Sizes& s, kda::BwdPlan* bp) {
+// budget: SIZE_MAX for the default plan (the size query), else the
+// workspace the caller gave (the widest window that fits).
+bool plan_bwd(const kda_chunk_desc_t* d, const Sizes& s, size_t budget, kda::BwdPlan* bp) {
   size_t chunk_states;
   if (!state_slots(d, 1, &chunk_states)) return false;
   const int rows = d->n_seqs > 0 ? d->n_seqs : d->B;
   return kda::plan_backward(d->d_k, (int)elem_size(dtype_of(d)), rows, (int64_t)d->T, d->H, d->n_seqs > 0, s.n_cu,
-                            s.tokens, chunk_states, bp);
+                            s.tokens, chunk_states, budget, bp);
 }
 
 int chunk_backward(const kda_chunk_desc_ex_t* dx, const void* q, const void* k, const void* v, const void* g,
@@ -317,7 +319,7 @@ int chunk_backward(const kda_chunk_desc_ex_t* dx, const void* q, const void* k, 
   const int st = check_desc(d, gate, &s);
   if (st != KDA_OK) return st;
   kda::BwdPlan bp;
-  if (!plan_bwd(d, s, &bp)) return KDA_ERR_UNSUPPORTED;
+  if (!plan_bwd(d, s, SIZE_MAX, &bp)) return KDA_ERR_UNSUPPORTED;
   const bool has_tokens = s.tokens > 0;
   const bool gated = gate != KDA_GATE_NONE;
   if (!gated) {
@@ -332,7 +334,7 @@ int chunk_backward(const kda_chunk_desc_ex_t* dx, const void* q, const void* k, 
     if (p && !aligned(p, kAlign)) return KDA_ERR_INVALID_ARGUMENT;
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
   if (!workspace || !aligned(workspace, kWsAlign)) return KDA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < bp.ws_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (!plan_bwd(d, s, workspace_bytes, &bp)) return KDA_ERR_WORKSPACE_TOO_SMALL;
   // inputs may overlap one another; outputs overlap nothing
   const Range ins[] = {range(q, s.x_bytes),   range(k, s.x_bytes),    range(v, s.x_bytes),
                        range(g, s.g_bytes),   range(beta, s.beta_bytes), range(h0, s.state_bytes),
@@ -362,7 +364,7 @@ int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes) 
   const int st = check_desc(d, KDA_GATE_CHANNEL, &s);
   if (st != KDA_OK) return st;
   kda::BwdPlan bp;
-  if (!plan_bwd(d, s, &bp)) return KDA_ERR_UNSUPPORTED;
+  if (!plan_bwd(d, s, SIZE_MAX, &bp)) return KDA_ERR_UNSUPPORTED;
   *bytes = bp.ws_bytes;
   return KDA_OK;
 }

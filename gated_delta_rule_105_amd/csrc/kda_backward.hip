@@ -291,11 +291,50 @@ __global__ void __launch_bounds__(256) kda_bwd_seqs(const int32_t* __restrict__ 
   }
 }
 
+// The window a launch works in: chunk indices [lo, hi) of every sequence,
+// chunk m of sequence n at area slot n width + (m - lo).  width = 0: one
+// window (lo = 0, hi unbounded), the area slot is the chunk's slot of the
+// call.  The per-chunk records, scratch and end-state gradients are indexed
+// by area slot.
+struct Win {
+  int64_t lo, hi, width;
+};
+__device__ __forceinline__ int64_t area_slot(const Win& w, int64_t n, int64_t base, int64_t m) {
+  return w.width ? n * w.width + (m - w.lo) : base + m;
+}
+
+// The chunk at area slot a of window w; false for a slot no chunk has.
+__device__ bool chunk_pos_win(int64_t a, const Win& w, const int32_t* cu, const int64_t* seqs, int n_rows, int T_per,
+                              ChunkPos* p) {
+  if (w.width == 0) return chunk_pos(a, cu, seqs, n_rows, T_per, p);
+  const int64_t n = a / w.width, m = w.lo + a % w.width;
+  if (n >= n_rows || m >= w.hi) return false;
+  int64_t L, tok, st0;
+  if (cu) {
+    L = (int64_t)cu[n + 1] - cu[n];
+    tok = cu[n];
+    st0 = seqs[n_rows + 1 + n];
+  } else {
+    L = T_per;
+    tok = n * T_per;
+    st0 = n * (T_per / C);
+  }
+  const int64_t nc = (L + C - 1) / C;
+  if (m >= nc) return false;
+  p->n = (int)n;
+  p->m = (int)m;
+  p->nc = (int)nc;
+  p->tok0 = tok + m * C;
+  p->len = (int)min((int64_t)C, L - m * C);
+  p->st0 = st0;
+  return true;
+}
+
 // Same position, found once per workgroup by thread 0 and shared via LDS.
-__device__ bool chunk_pos_shared(int64_t slot, const int32_t* cu, const int64_t* seqs, int n_rows, int T_per,
-                                 ChunkPos* sh) {
+__device__ bool chunk_pos_shared(int64_t a, const Win& w, const int32_t* cu, const int64_t* seqs, int n_rows,
+                                 int T_per, ChunkPos* sh) {
   __shared__ int ok;
-  if (threadIdx.x == 0) ok = chunk_pos(slot, cu, seqs, n_rows, T_per, sh) ? 1 : 0;
+  if (threadIdx.x == 0) ok = chunk_pos_win(a, w, cu, seqs, n_rows, T_per, sh) ? 1 : 0;
   __syncthreads();
   return ok != 0;
 }
@@ -316,7 +355,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
                                                      const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs,
                                                      int n_rows, int T_per, int H,
                                                      float g_floor, int gate, float* __restrict__ rec,
-                                                     float* __restrict__ zero_state) {
+                                                     float* __restrict__ zero_state, Win win) {
   typedef Rec<D> R;
   __shared__ ChunkPos pos;
   // the products' slices, and later (once the Gram products are done) the
@@ -328,9 +367,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
-  if (slot == 0 && h == 0)
+  if (slot == 0 && h == 0 && win.lo == 0)
     for (int x = tid; x < D * D; x += blockDim.x) zero_state[x] = 0.f;
-  if (!chunk_pos_shared(slot, cu, seqs, n_rows, T_per, &pos)) return;
+  if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;
   float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
   const bool bf = sizeof(T) == 2;
   const int len = pos.len;
@@ -507,7 +546,8 @@ template <int D>
 __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
                                                      const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs,
                                                      int n_rows, int T_per, int H, int64_t m_lo, int64_t m_hi,
-                                                     float* __restrict__ dHs, float* __restrict__ dh0) {
+                                                     Win win, float* __restrict__ dHs, float* __restrict__ dh0,
+                                                     const float* __restrict__ carry_in, float* carry_out) {
   typedef Rec<D> R;
   constexpr int NCB = D / 16, NKC = C / 16, NKH = D / 32;
   __shared__ __align__(16) float G[D][16];
@@ -527,8 +567,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
     base = (int64_t)n * nc;
   }
   const int64_t sd = ((int64_t)n * H + h) * D * D;
-  auto rec_of = [&](int64_t m) { return rec + ((base + m) * H + h) * (int64_t)R::FLOATS; };
-  auto dhs_of = [&](int64_t m) { return dHs + ((base + m) * H + h) * (int64_t)D * D; };
+  auto rec_of = [&](int64_t m) { return rec + (area_slot(win, n, base, m) * H + h) * (int64_t)R::FLOATS; };
+  auto dhs_of = [&](int64_t m) { return dHs + (area_slot(win, n, base, m) * H + h) * (int64_t)D * D; };
   if (nc == 0) {  // no tokens: the gradient passes through unchanged
     if (dh0 && m_lo == 0)
       for (int x = tid; x < D * 16; x += blockDim.x) {
@@ -537,23 +577,24 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       }
     return;
   }
-  // this launch walks chunks [m_lo, top) of the sequence
+  // this launch walks chunks [m_lo, top) of the sequence (m_hi <= win.hi)
   const int64_t top = nc < m_hi ? nc : m_hi;
   if (top <= m_lo) return;
   // the end-state gradient of chunk top - 1: dht for the sequence's last
-  // chunk (stored), else what the launch over the later chunks stored
+  // chunk, the carry of the later window at this window's top, else what the
+  // launch over the later chunks of this window stored; the first two are
+  // stored for the local gradients
   {
     const float* Rp = rec_of(top - 1);
     float* dHo = dhs_of(top - 1);
+    const bool from_dht = top == nc, from_carry = !from_dht && top == win.hi;
     for (int x = tid; x < D * 16; x += blockDim.x) {
       const int c = x / 16, j = x % 16;
       float v;
-      if (top == nc) {
-        v = dht ? dht[sd + c * D + j0 + j] : 0.f;
-        dHo[c * D + j0 + j] = v;
-      } else {
-        v = dHo[c * D + j0 + j];
-      }
+      if (from_dht) v = dht ? dht[sd + c * D + j0 + j] : 0.f;
+      else if (from_carry) v = carry_in[sd + c * D + j0 + j];
+      else v = dHo[c * D + j0 + j];
+      if (from_dht || from_carry) dHo[c * D + j0 + j] = v;
       G[c][j] = Rp[R::GAM + c] * v;
     }
   }
@@ -596,7 +637,9 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       f32x4 acc = {0.f, 0.f, 0.f, 0.f}, neg = {0.f, 0.f, 0.f, 0.f};
       acc = mma_panels(acc, cur.aQ, cur.bO);
       neg = mma_panels(neg, cur.aW, bU);
-      float* dHo = m > 0 ? dhs_of(m - 1) : nullptr;
+      // chunk m - 1's end-state gradient: to the carry when that chunk is in
+      // the earlier window
+      float* dHo = m > 0 ? (m == win.lo ? carry_out + sd : dhs_of(m - 1)) : nullptr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * wave + 4 * g + e;
@@ -628,7 +671,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta,
-    int64_t m_lo, int64_t m_hi) {
+    int64_t m_lo, int64_t m_hi, Win win) {
   typedef Rec<D> R;
   typedef Scr<D> W;
   __shared__ ChunkPos pos;
@@ -638,7 +681,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
-  if (!chunk_pos_shared(slot, cu, seqs, n_rows, T_per, &pos)) return;
+  if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;
   if (pos.m < m_lo || pos.m >= m_hi) return;  // another launch's chunks
   const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
   float* Wp = scr + (slot * H + h) * (int64_t)W::FLOATS;
@@ -789,6 +832,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   float* scr = (float*)(w + bp.scr_off);
   float* dHs = (float*)(w + bp.dh_off);
   int64_t* seqs = (int64_t*)(w + bp.seq_off);
+  float* carry = bp.width > 0 ? (float*)(w + bp.carry_off) : nullptr;
   if (bp.rec_floats != (size_t)Rec<D>::FLOATS || bp.scr_floats != (size_t)Scr<D>::FLOATS)
     return (int)hipErrorInvalidValue;
   hipError_t e;
@@ -806,74 +850,108 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     return launch_chunk_forward(sizeof(T) == 2, D, n_rows, T_per, H, bp.fwd, g_floor, gate, in, h0, cu,
                                 (void*)(w + bp.o_off), ht, states, 1, ws, st, nullptr);
   };
-  if (!aux) {
-    const int rc = replay(stream);
-    if (rc != 0) return rc;
-  }
-  if ((e = mark(1)) != hipSuccess) return (int)e;
-  const dim3 gc((unsigned)bp.n_slots, H);
-  if (bp.n_slots > 0) {
-    if ((e = launch_kernel(kda_bwd_chunk<T, D>, gc, dim3(kThreads), stream, (const T*)in.q, (const T*)in.k,
-                           (const T*)in.v, in.g, in.beta, (const T*)dout, cu, (const int64_t*)seqs, n_rows, T_per, H,
-                           g_floor, gate, rec, zero)) != hipSuccess)
-      return (int)e;
-  }
+  constexpr int64_t kAll = INT64_MAX;
+  const int64_t nw = bp.windows();
+  auto window = [&](int64_t wi) {
+    return bp.width > 0 ? Win{wi * bp.width, (wi + 1) * bp.width, bp.width} : Win{0, kAll, 0};
+  };
+  const dim3 gc((unsigned)bp.n_area, H);
+  auto record = [&](const Win& wn) {
+    if (bp.n_area == 0) return hipSuccess;
+    return launch_kernel(kda_bwd_chunk<T, D>, gc, dim3(kThreads), stream, (const T*)in.q, (const T*)in.k,
+                         (const T*)in.v, in.g, in.beta, (const T*)dout, cu, (const int64_t*)seqs, n_rows, T_per, H,
+                         g_floor, gate, rec, zero, wn);
+  };
   // groups of 8 (sequence, head) pairs x D / 16 column blocks (see kda_bwd_state)
   const int64_t state_blocks = ((int64_t)n_rows * H + 7) / 8 * 8 * (D / 16);
-  constexpr int64_t kAll = INT64_MAX;
-  auto state = [&](int64_t lo, int64_t hi) {
+  const size_t carry_floats = (size_t)n_rows * H * D * D;
+  // window wi reads the carry that window wi + 1 wrote and writes the other one
+  auto state = [&](const Win& wn, int64_t wi, int64_t lo, int64_t hi) {
+    const float* cin = carry ? carry + (size_t)((wi + 1) & 1) * carry_floats : nullptr;
+    float* cout = carry ? carry + (size_t)(wi & 1) * carry_floats : nullptr;
     return launch_kernel(kda_bwd_state<D>, dim3((unsigned)state_blocks), dim3(512), stream, (const float*)rec, dht,
-                         cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, dHs, dh0);
+                         cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, wn, dHs, dh0, cin, cout);
   };
-  auto local = [&](hipStream_t st, int64_t lo, int64_t hi) {
-    if (bp.n_slots == 0) return hipSuccess;
+  auto local = [&](hipStream_t st, const Win& wn, int64_t lo, int64_t hi) {
+    if (bp.n_area == 0) return hipSuccess;
     return launch_kernel(kda_bwd_local<T, D>, gc, dim3(kThreads), st, (const T*)in.q, (const T*)in.k, in.g, cu,
                          (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0,
                          (const float*)ht, (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq,
-                         (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi);
+                         (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi, wn);
   };
   if (!aux) {
-    if ((e = mark(2)) != hipSuccess) return (int)e;
-    if ((e = state(0, kAll)) != hipSuccess) return (int)e;
-    if ((e = mark(3)) != hipSuccess) return (int)e;
-    if ((e = local(stream, 0, kAll)) != hipSuccess) return (int)e;
+    const int rc = replay(stream);
+    if (rc != 0) return rc;
+    // windows from the last chunks to the first; with several windows the
+    // stage events bracket the first window's passes
+    for (int64_t wi = nw - 1; wi >= 0; --wi) {
+      const Win wn = window(wi);
+      const bool first = wi == nw - 1;
+      if (first && (e = mark(1)) != hipSuccess) return (int)e;
+      if ((e = record(wn)) != hipSuccess) return (int)e;
+      if (first && (e = mark(2)) != hipSuccess) return (int)e;
+      if ((e = state(wn, wi, wn.lo, wn.hi)) != hipSuccess) return (int)e;
+      if (first && (e = mark(3)) != hipSuccess) return (int)e;
+      if ((e = local(stream, wn, wn.lo, wn.hi)) != hipSuccess) return (int)e;
+    }
     return (int)mark(4);
   }
   // Second stream.  The state-gradient pass runs one workgroup per (pair, 16
   // columns) and leaves most CUs idle at small batch; the second stream fills
-  // them.  First with the replay, forked after the record pass.  Then the
-  // state gradients are walked in two launches, the later half of the
-  // (average) chunks of a sequence first; while the second launch walks the
-  // earlier half, the side stream computes the local gradients of the later
-  // half.  Those of the earlier half follow on the call's stream once the
-  // walk and the replay are done, beside whatever the side stream has left.
+  // them.  First with the replay, forked after the first record pass (the
+  // replay is off the critical path).  Then the state gradients of a window
+  // are walked in two launches, the later half of its chunks first; while the
+  // second launch walks the earlier half, the side stream computes the local
+  // gradients of the later half.  Those of the earlier half follow on the
+  // call's stream once the walk and the replay are done.
   const hipStream_t side = (hipStream_t)aux->stream;
   const hipEvent_t fork = (hipEvent_t)aux->fork, join = (hipEvent_t)aux->join;
+  if ((e = record(window(nw - 1))) != hipSuccess) return (int)e;
   if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
   if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
   const int rc = replay(side);
   if (rc != 0) return rc;
   if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;  // replay done
+  if (nw > 1) {
+    // Several windows share one area: a window's record pass waits until the
+    // side stream's local gradients of the window before are done with it.
+    for (int64_t wi = nw - 1; wi >= 0; --wi) {
+      const Win wn = window(wi);
+      const int64_t top = wn.hi < bp.span ? wn.hi : bp.span, mid = wn.lo + (top - wn.lo) / 2;
+      if (wi < nw - 1 && (e = record(wn)) != hipSuccess) return (int)e;
+      if ((e = state(wn, wi, mid, wn.hi)) != hipSuccess) return (int)e;
+      // events are recorded again: a wait holds the state of the record it saw
+      if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
+      if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
+      if ((e = local(side, wn, mid, wn.hi)) != hipSuccess) return (int)e;
+      if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;
+      if (mid > wn.lo && (e = state(wn, wi, wn.lo, mid)) != hipSuccess) return (int)e;
+      if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;  // replay, side's local gradients
+      if (mid > wn.lo && (e = local(stream, wn, wn.lo, mid)) != hipSuccess) return (int)e;
+    }
+    return (int)hipSuccess;
+  }
+  const Win all = window(0);
   const int64_t per_seq = cu ? (T_per + (int64_t)C * n_rows - 1) / ((int64_t)C * (n_rows > 0 ? n_rows : 1))
                              : (T_per + C - 1) / C;
   const int64_t split = per_seq / 2;
   if (split > 0) {
-    if ((e = state(split, kAll)) != hipSuccess) return (int)e;
+    if ((e = state(all, 0, split, kAll)) != hipSuccess) return (int)e;
     // the event is recorded again: the replay's wait above holds its earlier state
     if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
     if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
-    if ((e = local(side, split, kAll)) != hipSuccess) return (int)e;
-    if ((e = state(0, split)) != hipSuccess) return (int)e;
+    if ((e = local(side, all, split, kAll)) != hipSuccess) return (int)e;
+    if ((e = state(all, 0, 0, split)) != hipSuccess) return (int)e;
     if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;  // the replay
-    if ((e = local(stream, 0, split)) != hipSuccess) return (int)e;
+    if ((e = local(stream, all, 0, split)) != hipSuccess) return (int)e;
     // join recorded again after the side's local gradients; the wait above
     // holds the replay's record
     if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;
     return (int)hipStreamWaitEvent(stream, join, 0);
   }
-  if ((e = state(0, kAll)) != hipSuccess) return (int)e;
+  if ((e = state(all, 0, 0, kAll)) != hipSuccess) return (int)e;
   if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;
-  return (int)local(stream, 0, kAll);
+  return (int)local(stream, all, 0, kAll);
 }
 
 }  // namespace

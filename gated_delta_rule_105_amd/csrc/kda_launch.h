@@ -155,49 +155,103 @@ constexpr size_t bwd_scr_floats(int d) { return (size_t)5 * kChunk * d + (size_t
 
 // Workspace of one backward call (byte offsets, each 256-byte aligned): the
 // forward replay's own workspace first, then its o (discarded), its final
-// states, the state after every full chunk, one zero state, the chunk
-// records, the scratch areas, the end-state gradient of every chunk and the
-// per-sequence chunk and state-slot offsets of a packed batch.
+// states, the state after every full chunk, one zero state; then the area
+// of the chunk records, the scratch areas and the end-state gradient of every
+// chunk in flight, the per-sequence chunk and state-slot offsets of a packed
+// batch, and with windows two carry states per (sequence, head).
+//
+// Windows: with width W > 0 the chunks are processed in windows of W chunk
+// indices, [w W, (w + 1) W) of every sequence, from the last window to the
+// first; chunk m of sequence n has area slot n W + (m - w W), so the area
+// holds n_rows W slots, reused by every window.  The state gradient at a
+// window's lower edge passes to the next window through a carry state.  With
+// W = 0 the area has a slot for every chunk of the call (slots count the
+// chunks of all sequences in order) and there is one window.
 struct BwdPlan {
   SegPlan fwd;
   int64_t n_slots;  // upper bound of chunks over all sequences
-  size_t o_off, ht_off, states_off, zero_off, rec_off, scr_off, dh_off, seq_off, ws_bytes;
+  int64_t width;    // chunks per window, 0: one window
+  int64_t span;     // upper bound of the chunks of one sequence
+  int64_t n_area;   // slots of the record, scratch and gradient areas
+  size_t o_off, ht_off, states_off, zero_off, rec_off, scr_off, dh_off, seq_off, carry_off, ws_bytes;
   size_t rec_floats, scr_floats;
+  int64_t windows() const { return width > 0 ? (span + width - 1) / width : 1; }
 };
 
+// Chunk-heads of the area above which the default plan cuts sequences into
+// windows: about 4.4 GiB of records, scratch and gradients at d = 128.
+constexpr int64_t kBwdAreaChunkHeads = 8192;
+// Narrowest window of the default plan.
+constexpr int64_t kBwdMinWindow = 64;
+
 // n_states: sequences; chunk_states: full chunks over all sequences (an
-// upper bound for a packed batch).  Returns false on overflow.
+// upper bound for a packed batch).  budget: the workspace bytes available;
+// SIZE_MAX gives the default plan (one window unless the area would pass
+// kBwdAreaChunkHeads), otherwise the widest window that fits (one window
+// when the whole area fits).  Returns false on overflow or when not even
+// one-chunk windows fit the budget.
 inline bool plan_backward(int d, int esz, int n_rows, int64_t T, int H, bool packed, int n_cu, size_t tokens,
-                          size_t chunk_states, BwdPlan* p) {
+                          size_t chunk_states, size_t budget, BwdPlan* p) {
   if (!plan_segments(d, esz, n_rows, T, H, packed, n_cu, &p->fwd)) return false;
   const size_t a = 256, hh = (size_t)H, dd = (size_t)d * d * sizeof(float);
   auto up = [&](size_t x) { return (x + a - 1) / a * a; };
   const int64_t chunks_total = (T + kChunk - 1) / kChunk;
   p->n_slots = T == 0 ? 0 : (packed ? chunks_total + n_rows : (int64_t)n_rows * chunks_total);
+  p->span = chunks_total;  // a sequence of a packed batch has at most all of them
   p->rec_floats = bwd_rec_floats(d);
   p->scr_floats = bwd_scr_floats(d);
+  const double per_slot = hh * ((p->rec_floats + p->scr_floats) * 4.0 + (double)dd);
   const double total = (double)p->fwd.ws_bytes + (double)tokens * hh * d * esz +
-                       ((double)n_rows + (double)chunk_states + 1.0) * hh * dd +
-                       (double)p->n_slots * hh * ((p->rec_floats + p->scr_floats) * 4.0 + (double)dd);
+                       ((double)n_rows + (double)chunk_states + 1.0) * hh * dd + (double)p->n_slots * per_slot +
+                       2.0 * (double)n_rows * hh * dd;
   if (total > 1.0e15) return false;
-  size_t off = up(p->fwd.ws_bytes);
-  p->o_off = off;
-  off = up(off + tokens * hh * (size_t)d * esz);
-  p->ht_off = off;
-  off = up(off + (size_t)n_rows * hh * dd);
-  p->states_off = off;
-  off = up(off + chunk_states * hh * dd);
-  p->zero_off = off;
-  off = up(off + dd);
-  p->rec_off = off;
-  off = up(off + (size_t)p->n_slots * hh * p->rec_floats * 4);
-  p->scr_off = off;
-  off = up(off + (size_t)p->n_slots * hh * p->scr_floats * 4);
-  p->dh_off = off;
-  off = up(off + (size_t)p->n_slots * hh * dd);
-  p->seq_off = off;  // per-sequence prefix sums of a packed batch: 2 (n_rows + 1) int64
-  off = up(off + (size_t)2 * ((size_t)n_rows + 1) * sizeof(int64_t));
-  p->ws_bytes = off;
+  auto layout = [&](int64_t width) {
+    p->width = width;
+    p->n_area = width > 0 ? (int64_t)n_rows * width : p->n_slots;
+    size_t off = up(p->fwd.ws_bytes);
+    p->o_off = off;
+    off = up(off + tokens * hh * (size_t)d * esz);
+    p->ht_off = off;
+    off = up(off + (size_t)n_rows * hh * dd);
+    p->states_off = off;
+    off = up(off + chunk_states * hh * dd);
+    p->zero_off = off;
+    off = up(off + dd);
+    p->rec_off = off;
+    off = up(off + (size_t)p->n_area * hh * p->rec_floats * 4);
+    p->scr_off = off;
+    off = up(off + (size_t)p->n_area * hh * p->scr_floats * 4);
+    p->dh_off = off;
+    off = up(off + (size_t)p->n_area * hh * dd);
+    p->seq_off = off;  // per-sequence prefix sums of a packed batch: 2 (n_rows + 1) int64
+    off = up(off + (size_t)2 * ((size_t)n_rows + 1) * sizeof(int64_t));
+    p->carry_off = off;
+    if (width > 0) off = up(off + (size_t)2 * n_rows * hh * dd);
+    p->ws_bytes = off;
+    return off;
+  };
+  // windows narrower than a sequence whose area is smaller than one slot per chunk
+  auto useful = [&](int64_t width) { return width >= 1 && width < p->span && (int64_t)n_rows * width < p->n_slots; };
+  if (budget == SIZE_MAX) {
+    int64_t width = 0;
+    if (p->n_slots * (int64_t)H > kBwdAreaChunkHeads && n_rows > 0) {
+      const int64_t w = kBwdAreaChunkHeads / ((int64_t)H * n_rows);
+      width = w > kBwdMinWindow ? w : kBwdMinWindow;
+      if (!useful(width) || 2 * (int64_t)n_rows * width > p->n_slots) width = 0;
+    }
+    layout(width);
+    return true;
+  }
+  if (layout(0) <= budget) return true;
+  if (n_rows == 0 || p->span < 2) return false;
+  // the largest width that fits: the size grows with the width, so estimate
+  // it, then step down past the alignment slack
+  const size_t fixed = layout(1) - (size_t)n_rows * (size_t)per_slot;
+  if (fixed >= budget) return false;
+  int64_t width = (int64_t)((budget - fixed) / ((size_t)n_rows * (size_t)per_slot));
+  if (width >= p->span) width = p->span - 1;
+  while (width >= 1 && layout(width) > budget) --width;
+  if (!useful(width)) return false;
   return true;
 }
 

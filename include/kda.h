@@ -292,10 +292,19 @@ int kda_chunk_forward_states(const kda_chunk_desc_ex_t* d,
  * The floor max(g, g_floor) passes the gradient where g >= g_floor (on the
  * floor itself too: the derivative from above) and gives 0 where g is below.
  * The call replays the forward internally (its outputs are not needed).
- * The workspace (kda_chunk_backward_workspace_size, 256-byte aligned) holds
- * the replay's states and fp32 per-chunk records: about 0.55 MiB per
- * (chunk of 64 tokens, head) at d = 128.  Outputs must not overlap each
- * other, the inputs or the workspace.  Other rules as kda_chunk_forward.
+ * The workspace (256-byte aligned) holds the replay's state after every
+ * chunk (64 KiB per (chunk of 64 tokens, head) at d = 128) and, for the
+ * chunks in flight, fp32 records, scratch and state gradients (about
+ * 0.49 MiB per (chunk, head) at d = 128).  Chunks are processed in windows
+ * of W chunk indices of every sequence, from the last window to the first;
+ * the call takes the widest window that fits workspace_bytes (one window
+ * for the whole sequence when everything fits), and the results do not
+ * depend on it.  kda_chunk_backward_workspace_size gives the default: one
+ * window unless the in-flight areas of the whole call would pass 8192
+ * (chunk, head) pairs, else windows of max(64, 8192 / (H rows)) chunks.
+ * A workspace too small for windows of one chunk is
+ * KDA_ERR_WORKSPACE_TOO_SMALL.  Outputs must not overlap each other, the
+ * inputs or the workspace.  Other rules as kda_chunk_forward.
  */
 int kda_chunk_backward_workspace_size(const kda_chunk_desc_t* d, size_t* bytes);
 int kda_chunk_backward(const kda_chunk_desc_ex_t* d,

@@ -357,6 +357,15 @@ def test_backward_workspace_size(lib):
     chunks = 4096 // 64
     per_chunk = (8 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 5 * 64 * 128 + 2 * 64 * 64 + 128 + 128 * 128) * 4
     assert n >= fwd + 16 * chunks * 128 * 128 * 4 + 16 * chunks * per_chunk
+    # T = 1M: the default cuts the sequence into windows of chunks, so the
+    # workspace is the state after every chunk, the replay's o and one window
+    big = bws_status(lib, desc(T=1 << 20))
+    assert big[0] == KDA_OK
+    chunk_heads = 16 * (1 << 20) // 64
+    state, o_bytes = 128 * 128 * 4, 64 * 128 * 2
+    assert big[1] >= chunk_heads * (state + o_bytes)
+    assert big[1] / chunk_heads <= 0.15 * 2 ** 20                 # MiB per (chunk, head)
+    assert big[1] <= chunk_heads * (state + o_bytes) + 512 * 16 * per_chunk + (64 << 20)
     assert bws_status(lib, desc(d_k=96, d_v=96))[0] == KDA_ERR_UNSUPPORTED
     assert bws_status(lib, desc(dtype=KDA_DTYPE_F32))[0] == KDA_ERR_UNSUPPORTED
     assert bws_status(lib, desc(T=0))[0] == KDA_OK
@@ -389,7 +398,7 @@ def bwd_call(d, a, events=None, gate=0):
     (lambda a: a.update(dk=a["dk"] + 4), KDA_ERR_INVALID_ARGUMENT),         # misaligned
     (lambda a: a.update(ws=a["ws"] + 64), KDA_ERR_INVALID_ARGUMENT),
     (lambda a: a.update(ws=None), KDA_ERR_INVALID_ARGUMENT),
-    (lambda a: a.update(ws_bytes=a["ws_bytes"] - 1), KDA_ERR_WORKSPACE_TOO_SMALL),
+    (lambda a: a.update(ws_bytes=a["ws_bytes"] // 2000), KDA_ERR_WORKSPACE_TOO_SMALL),  # not one-chunk windows
     (lambda a: a.update(dq=a["q"] + 1024), KDA_ERR_INVALID_ARGUMENT),       # output overlaps an input
     (lambda a: a.update(dv=a["dk"] + 4096), KDA_ERR_INVALID_ARGUMENT),      # outputs overlap
     (lambda a: a.update(dh0=a["dht"]), KDA_ERR_INVALID_ARGUMENT),           # dh0 overlaps dht
@@ -433,7 +442,7 @@ def test_chunk_backward_overlapped_rejects(lib):
     assert ov(a, None, ev2) == KDA_ERR_INVALID_ARGUMENT
     assert ov(a, ev1, None) == KDA_ERR_INVALID_ARGUMENT
     assert ov(a, ev1, ev1) == KDA_ERR_INVALID_ARGUMENT
-    for mutate, code in ((lambda x: x.update(ws_bytes=x["ws_bytes"] - 1), KDA_ERR_WORKSPACE_TOO_SMALL),
+    for mutate, code in ((lambda x: x.update(ws_bytes=x["ws_bytes"] // 2000), KDA_ERR_WORKSPACE_TOO_SMALL),
                          (lambda x: x.update(dq=x["q"] + 1024), KDA_ERR_INVALID_ARGUMENT),
                          (lambda x: x.update(do=None), KDA_ERR_INVALID_ARGUMENT)):
         b = dict(a)

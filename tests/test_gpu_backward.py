@@ -345,3 +345,45 @@ def test_backward_timed_matches_sequential(name):
     print(f"{name}: stages " + " ".join(f"{s}={t * 1e3:.1f}us" for s, t in zip(kda.BWD_STAGES, parts)))
     assert all(t >= 0 for t in parts) and total > 0
     assert abs(sum(parts) - total) <= 1e-3 + 1e-3 * total
+
+
+def _window_budget(inp, W):
+    """Workspace bytes for windows of about W chunks: the default size less
+    the per-chunk areas (fp32 record, scratch and end-state gradient) of the
+    chunks beyond n_rows W slots, plus the two carry states per (sequence,
+    head) that windows add."""
+    B, T, H, d = inp["q"].shape
+    cu = inp.get("cu_seqlens")
+    rows = B if cu is None else cu.numel() - 1
+    chunks = (T + 63) // 64
+    n_slots = rows * chunks if cu is None else chunks + rows
+    per_slot = H * ((8 * 64 * d + 3 * 64 * 64 + d + 64 + 5 * 64 * d + 2 * 64 * 64 + d) * 4 + d * d * 4)
+    full = kda.backward_workspace_bytes(B, T, H, d, inp["q"].dtype, n_seqs=0 if cu is None else rows)
+    return full - (n_slots - rows * W) * per_slot + 2 * rows * H * d * d * 4 + 4 * 256
+
+
+@pytest.mark.parametrize("name", ["f32_B2_T1000_d64", "bf16_packed_d128"])
+def test_backward_windows_match(name):
+    """A workspace smaller than the default makes the call process the chunks
+    in windows (the last window first, the state gradient carried across
+    window edges): the gradients equal the one-window call's bit for bit,
+    sequential and overlapped, and the oracle's."""
+    if name.startswith("f32"):
+        inp, widths, dt = _case(2, 1000, 2, 64, "f32", wid=370), (5, 1), "f32"
+    else:
+        inp, widths, dt = _case(1, 0, 2, 128, "bf16", lengths=[700, 0, 64, 1000, 130], wid=371), (6, 3), "bf16"
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"])
+    kw = dict(h0=d.get("h0"), dht=d.get("dht"), cu_seqlens=d.get("cu_seqlens"))
+    note(f"chunk_backward windows {name}: one window")
+    one = kda.chunk_backward(*args, **kw)
+    torch.cuda.synchronize()
+    _check(name + " one window", one, _oracle_backward(inp), dt)
+    for W in widths:
+        ws = torch.empty(_window_budget(inp, W), dtype=torch.uint8, device="cuda")
+        for overlap in (False, True):
+            note(f"chunk_backward windows {name}: about {W} chunks, overlap={overlap}")
+            got = kda.chunk_backward(*args, workspace=ws, overlap=overlap, **kw)
+            torch.cuda.synchronize()
+            for key in GRADS:
+                assert torch.equal(one[key], got[key]), (W, overlap, key)
