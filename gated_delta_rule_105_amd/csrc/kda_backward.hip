@@ -364,7 +364,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   __shared__ __align__(16) float lds[kLds];
   float(*As)[C + 1] = (float(*)[C + 1])lds;
   float(*Ts)[C + 1] = (float(*)[C + 1])(lds + C * (C + 1));
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
   if (slot == 0 && h == 0 && win.lo == 0)
@@ -678,7 +678,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   // the products' slices, and later the per-element dGamma of the chunk
   constexpr int kLds = kGemmLds > C * D ? kGemmLds : C * D;
   __shared__ __align__(16) float lds[kLds];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int h = blockIdx.y;
   const int64_t slot = blockIdx.x;
   if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;

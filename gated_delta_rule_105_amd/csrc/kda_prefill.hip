@@ -325,7 +325,6 @@ template <> struct PairT<bf16_t> {
     return __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(a, b));
   }
   __device__ static __forceinline__ word splat(word x) { return (x & 0xffffu) | (x << 16); }
-  __device__ static __forceinline__ word zero() { return 0u; }
   template <int AUX>
   __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, AUX);
@@ -341,7 +340,6 @@ template <> struct PairT<float> {
   __device__ static __forceinline__ float hi(word w) { return w[1]; }
   __device__ static __forceinline__ word pack(float a, float b) { return (f32x2){a, b}; }
   __device__ static __forceinline__ word splat(word x) { return (f32x2){x[0], x[0]}; }
-  __device__ static __forceinline__ word zero() { return (f32x2){0.f, 0.f}; }
   template <int AUX>
   __device__ static __forceinline__ word load(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
     return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, AUX));
@@ -370,6 +368,10 @@ template <typename T, int D, bool WITH_Q, bool MX, bool NT> struct Raw {
     const uint32_t rs = (uint32_t)H * D;               // row stride, elements
     const uint32_t span = (uint32_t)(clen - 1) * rs + D;  // elements from row0 * D to the chunk's end
     const uint32_t off0 = (uint32_t)(8 * part) * rs + 2 * cp;
+    // beta first: loads complete in issue order, so once the chunk's other
+    // inputs have arrived beta has too, and its use needs no wait of its own
+    const __amdgpu_buffer_rsrc_t rb = rsrc(in.beta + row0, ((uint32_t)(clen - 1) * H + 1) * 4);
+    beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)tid * H * 4, 0, aux));
     if (MX) {
       const uint32_t sspan = span / 32;
       const __amdgpu_buffer_rsrc_t rk = rsrc((const uint8_t*)in.k + row0 * D, span);
@@ -409,20 +411,19 @@ template <typename T, int D, bool WITH_Q, bool MX, bool NT> struct Raw {
         for (int s = 0; s < 8; ++s) q[s] = PW::template load<aux>(rq, off0 * ES, s * rs * ES);
       }
     }
-    if (gate == kGateChannel) {
-      const __amdgpu_buffer_rsrc_t rgt = rsrc((const T*)in.g + row0 * D, span * ES);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) g[s] = PW::template load<aux>(rgt, off0 * ES, s * rs * ES);
-    } else if (gate == kGateHead) {
+    // g is filled by loads in every mode, without a gate from an empty range
+    // (zeros): a plain register write there would make the compiler wait for
+    // every load in flight (the next chunk's inputs included) before it
+    if (gate == kGateHead) {
       const __amdgpu_buffer_rsrc_t rgt = rsrc((const T*)in.g + row0, ((uint32_t)(clen - 1) * H + 1) * ES);
 #pragma unroll
       for (int s = 0; s < 8; ++s) g[s] = PW::template load1<aux>(rgt, (uint32_t)(8 * part + s) * H * ES);
     } else {
+      const bool ch = gate == kGateChannel;
+      const __amdgpu_buffer_rsrc_t rgt = rsrc(ch ? (const void*)((const T*)in.g + row0 * D) : in.k, ch ? span * ES : 0u);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) g[s] = PW::zero();
+      for (int s = 0; s < 8; ++s) g[s] = PW::template load<aux>(rgt, off0 * ES, s * rs * ES);
     }
-    const __amdgpu_buffer_rsrc_t rb = rsrc(in.beta + row0, ((uint32_t)(clen - 1) * H + 1) * 4);
-    beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)tid * H * 4, 0, aux));
   }
   // the pair (2 cp, 2 cp + 1) of row s as operand words
   __device__ static __forceinline__ word dec(word w, uint32_t s) {
@@ -970,7 +971,7 @@ kda_chunk_sweep(const ChunkInputs in, const int32_t* __restrict__ cu, const int6
                 T* __restrict__ o, float* ht, float* __restrict__ states, int every) {
   typedef Lay<T, D, OUT> Y;
   typedef Rec<T, D> R;
-  constexpr int NW = D / 16, NR = D / 16;
+  constexpr int NR = D / 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Y::BYTES];
   const int64_t period = (OUT && states) ? (int64_t)C * every : 0;
   Seg sg;
