@@ -59,8 +59,8 @@ namespace {
 
 constexpr int C = kChunk;
 
-typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2nt __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -816,14 +816,18 @@ __device__ __forceinline__ void state_out(const unsigned char* smem, int buf, f3
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb)
         if (kb * KB <= 16 * rt + 15) acc = mma(UB[kb], pf[rt & 1][kb], acc);
-      // rows past the chunk's end fall outside the resource: not written
+      // rows past the chunk's end fall outside the resource: not written.
+      // Write-back stores: a lane writes 4 channels of one token, so the
+      // eight waves' pieces of a token's row meet in L2 before it goes to
+      // HBM (non-temporal stores sent the 32-byte pieces on their own, 1.65x
+      // the bytes of o)
       const uint32_t voff = (uint32_t)((i * H * D + 16 * w + 4 * g) * (int)sizeof(T));
       const int soff = 16 * rt * H * D * (int)sizeof(T);
       if constexpr (sizeof(T) == 2) {
         const uint2 p = __builtin_bit_cast(uint2, to_bf16x4(acc));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2nt, p), ro, voff, soff, 2);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, p), ro, voff, soff, 0);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4nt, acc), ro, voff, soff, 2);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, voff, soff, 0);
       }
     }
   }
