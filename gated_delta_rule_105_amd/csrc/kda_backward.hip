@@ -51,6 +51,8 @@ namespace kda {
 namespace {
 
 constexpr int C = kChunk;
+// Launches of the state-gradient walk in the overlapped call (one window).
+constexpr int kBwdParts = 4;
 
 // Barrier for LDS hand-offs only: the waves' LDS operations are complete,
 // global loads may still be in flight (__syncthreads() is a release fence and
@@ -663,7 +665,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 
 // ---------------------------------------------------------------------------
 // Local gradients of one chunk, for the chunks m_lo <= m < m_hi of their
-// sequences (the other workgroups of the grid exit at once).
+// sequences (the other workgroups of the grid exit at once).  Workgroup x
+// takes area slot a0 + x.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
@@ -671,7 +674,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta,
-    int64_t m_lo, int64_t m_hi, Win win) {
+    int64_t m_lo, int64_t m_hi, Win win, int64_t a0) {
   typedef Rec<D> R;
   typedef Scr<D> W;
   __shared__ ChunkPos pos;
@@ -680,7 +683,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   __shared__ __align__(16) float lds[kLds];
   const int tid = threadIdx.x;
   const int h = blockIdx.y;
-  const int64_t slot = blockIdx.x;
+  const int64_t slot = a0 + blockIdx.x;
   if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;
   if (pos.m < m_lo || pos.m >= m_hi) return;  // another launch's chunks
   const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
@@ -872,12 +875,21 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     return launch_kernel(kda_bwd_state<D>, dim3((unsigned)state_blocks), dim3(512), stream, (const float*)rec, dht,
                          cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, wn, dHs, dh0, cin, cout);
   };
+  // A single fixed-length sequence has its chunks [lo, hi) at consecutive
+  // area slots, so the grid covers just those; otherwise the whole area.
   auto local = [&](hipStream_t st, const Win& wn, int64_t lo, int64_t hi) {
     if (bp.n_area == 0) return hipSuccess;
-    return launch_kernel(kda_bwd_local<T, D>, gc, dim3(kThreads), st, (const T*)in.q, (const T*)in.k, in.g, cu,
-                         (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate, (const float*)rec, h0,
-                         (const float*)ht, (const float*)states, (const float*)zero, (const float*)dHs, scr, (T*)dq,
-                         (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi, wn);
+    int64_t a0 = 0, count = bp.n_area;
+    if (!cu && n_rows == 1) {
+      const int64_t nc = (T_per + C - 1) / C, top = hi < nc ? hi : nc;
+      if (top <= lo) return hipSuccess;
+      a0 = lo - wn.lo;
+      count = top - lo;
+    }
+    return launch_kernel(kda_bwd_local<T, D>, dim3((unsigned)count, H), dim3(kThreads), st, (const T*)in.q,
+                         (const T*)in.k, in.g, cu, (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate,
+                         (const float*)rec, h0, (const float*)ht, (const float*)states, (const float*)zero,
+                         (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi, wn, a0);
   };
   if (!aux) {
     const int rc = replay(stream);
@@ -934,16 +946,22 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   const Win all = window(0);
   const int64_t per_seq = cu ? (T_per + (int64_t)C * n_rows - 1) / ((int64_t)C * (n_rows > 0 ? n_rows : 1))
                              : (T_per + C - 1) / C;
-  const int64_t split = per_seq / 2;
-  if (split > 0) {
-    if ((e = state(all, 0, split, kAll)) != hipSuccess) return (int)e;
-    // the event is recorded again: the replay's wait above holds its earlier state
-    if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
-    if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
-    if ((e = local(side, all, split, kAll)) != hipSuccess) return (int)e;
-    if ((e = state(all, 0, 0, split)) != hipSuccess) return (int)e;
+  // the walk in kBwdParts launches over chunk ranges [b_i, b_{i+1}) of the
+  // (average) sequence, the last one open-ended; the local gradients of each
+  // part but the first go to the side stream once its walk is done
+  const int parts = per_seq < kBwdParts ? (int)per_seq : kBwdParts;
+  if (parts >= 2) {
+    auto bound = [&](int i) { return i >= parts ? kAll : per_seq * i / parts; };
+    if ((e = state(all, 0, bound(parts - 1), kAll)) != hipSuccess) return (int)e;
+    for (int i = parts - 1; i >= 1; --i) {
+      // the event is recorded again: the replay's wait above holds its earlier state
+      if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
+      if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
+      if ((e = local(side, all, bound(i), bound(i + 1))) != hipSuccess) return (int)e;
+      if ((e = state(all, 0, bound(i - 1), bound(i))) != hipSuccess) return (int)e;
+    }
     if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;  // the replay
-    if ((e = local(stream, all, 0, split)) != hipSuccess) return (int)e;
+    if ((e = local(stream, all, 0, bound(1))) != hipSuccess) return (int)e;
     // join recorded again after the side's local gradients; the wait above
     // holds the replay's record
     if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;
