@@ -313,8 +313,8 @@ def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chu
     (fp32 [B, T, H]) and dh0 (fp32 [S, H, d, d], or None when want_dh0 is
     False).  `out` may supply those tensors.  events: optional
     len(BWD_STAGES) + 1 raw hipEvent_t handles (kda_chunk_backward_timed).
-    overlap: run the forward replay, and the local gradients of the later
-    half of the chunks, on a second stream of the device beside the
+    overlap: run the forward replay, and the local gradients of all but the
+    first range of chunks, on a second stream of the device beside the
     state-gradient walk (it forks after the record stage;
     kda_chunk_backward_overlapped, the same results).  Overlapped calls on one device share that stream and its
     events, so they must be issued from one host thread.  workspace: a uint8
