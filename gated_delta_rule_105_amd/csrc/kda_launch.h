@@ -47,10 +47,14 @@ inline int64_t group_bound(int64_t T, int n_rows, bool packed, int64_t g) {
 // model below cuts sequences into segments for it.
 int device_compute_units();
 
-// Per-chunk times of the two sweeps and per-step time of the scan on one CU
-// (one workgroup per CU), measured on MI355X at d = 128; the model scales
-// them by (d / 128)^2 for d = 64.
-constexpr double kMapChunkUs = 3.0, kOutChunkUs = 3.0, kScanStepUs = 1.1;
+// Costs measured on MI355X at d = 128 (per-workgroup timestamps of the
+// sweeps, B = 1, H = 16, T = 4096 and 65,536): per chunk of a sweep
+// workgroup (one per CU; the map sweep 5.8 to 7.1 us, the output sweep 6.9
+// to 8.4 us, inputs from cache or from HBM), per scan step, per launch
+// (dispatch and drain beyond the workgroups' span) and per sweep workgroup
+// outside its chunk loop.  The chunk and step times are scaled by
+// (d / 128)^2 for d = 64.
+constexpr double kMapChunkUs = 6.4, kOutChunkUs = 7.6, kScanStepUs = 1.13, kLaunchUs = 4.0, kSweepWgUs = 3.0;
 
 // Chooses the cut from a cost model of the launches.  Either every sequence
 // is one segment (the output sweep alone; one workgroup per (sequence, head)
@@ -81,11 +85,13 @@ inline bool plan_segments(int d, int esz, int n_rows, int64_t T, int H, bool pac
     return ceil(recs / 256.0) * 256.0 + (double)seq_bytes;
   };
   if (ws_of(0) > (double)max_ws) return false;
-  double best = rounds(pairs) * (double)per_seq * t_out;  // one segment per sequence
+  // one segment per sequence: the output sweep alone
+  double best = rounds(pairs) * ((double)per_seq * t_out + kSweepWgUs) + kLaunchUs;
   int best_l = 0;
   for (int64_t L = 1; L < per_seq; L *= 2) {
     const int64_t segs = (per_seq + L - 1) / L;
-    const double t = rounds(pairs * segs) * (double)L * (t_map + t_out) + (double)(segs - 1) * t_scan;
+    const double t = rounds(pairs * segs) * ((double)L * (t_map + t_out) + 2.0 * kSweepWgUs) +
+                     (double)(segs - 1) * t_scan + 3.0 * kLaunchUs;
     if (t < best && ws_of(L) <= (double)max_ws) {
       best = t;
       best_l = (int)L;
