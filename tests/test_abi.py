@@ -96,6 +96,9 @@ def test_workspace_size_valid(lib):
     rec = 3 * 128 * 128 * 4
     assert st == KDA_OK and n > 0 and n % rec == 0
     assert n <= 16 * (4096 // 64) * rec
+    # on 256 compute units the cost model cuts the 64 chunks into 16
+    # segments of 4: one workgroup per CU and (segment, head)
+    assert n == 16 * 16 * rec
     # the number of segments follows the compute units, not the length
     st2, n2 = ws_status(lib, desc(T=1 << 20))
     assert st2 == KDA_OK and 0 < n2 <= 64 << 20 and n2 % rec == 0
