@@ -27,7 +27,11 @@ prefix-cache states (kda_chunk_forward_states) beside plain calls;
 ``gate_workloads`` times Gated DeltaNet and DeltaNet gates beside KDA on the
 prefill and decode workloads; ``mx_workload`` the headline workload with q,
 k, v in MXFP8 (kda_chunk_forward_mx); ``backward_workload`` the backward pass
-(kda_chunk_backward) on the headline workload.  Other
+(kda_chunk_backward) on the headline workload; ``cold`` the headline, packed
+and million-token workloads as the median of calls each preceded by a 1 GiB
+write that flushes L2 and the last-level cache; ``gpu_clock`` the graphics
+clock under load; ``roofline_fraction`` the larger of the call's HBM and
+MFMA fractions.  Other
 legs: ``--copy-calib MiB`` runs only a device copy of known size (for
 scaling the HBM byte counters), ``--only prefill|decode|backward`` runs one leg,
 ``--no-cpu`` skips the oracle.
@@ -262,6 +266,92 @@ def bench_workload(wid: int, calls: int):
     return {"workload": w.name, "tokens": T, "heads": w.H, "mean_call_us": mean * 1e6,
             "value": T / mean, "unit": "tokens/s", "hbm_frac": bytes_call / mean / 1e9 / PEAK_HBM_GBS,
             "mfma_frac": token_heads * FLOP_PER_TOKEN_HEAD / mean / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def bench_cold(wid: int, reps: int, warm: int = 3):
+    """One workload the cold way: `warm` untimed calls, then `reps` calls,
+    each after a 1 GiB device write that evicts the inputs from L2 and the
+    last-level cache, each bracketed by its own HIP event pair; the median."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[wid]
+    log(f"cold {w.name}: {warm} warm-up calls, then {reps} calls each after a 1 GiB flush")
+    inp = synth.workload_inputs(w, device="cuda")
+    T = inp["q"].shape[1]
+    n_seqs = 0 if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    ws = torch.empty(kda.workspace_bytes(1, T, w.H, w.dk, torch.bfloat16, n_seqs), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["q"])
+    ht = torch.empty((n_seqs or 1, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def call():
+        kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"],
+                          cu_seqlens=inp["cu_seqlens"], o=o, ht=ht, workspace=ws, validate_cu=False)
+
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    times.sort()
+    med = times[len(times) // 2] if len(times) % 2 else 0.5 * (times[len(times) // 2 - 1] + times[len(times) // 2])
+    token_heads = T * w.H
+    bytes_call = token_heads * BYTES_PER_TOKEN_HEAD + (1 + (1 if inp["h0"] is not None else 0)) * (n_seqs or 1) \
+        * w.H * STATE_BYTES
+    hbm = bytes_call / med / 1e9 / PEAK_HBM_GBS
+    mfma = token_heads * FLOP_PER_TOKEN_HEAD / med / 1e12 / PEAK_BF16_TFLOPS
+    log(f"cold {w.name}: median {med * 1e6:.1f} us (min {times[0] * 1e6:.1f}, max {times[-1] * 1e6:.1f})")
+    del inp, o, ws, flush
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "reps": reps, "median_call_us": med * 1e6, "min_call_us": times[0] * 1e6,
+            "max_call_us": times[-1] * 1e6, "value": T / med, "unit": "tokens/s", "hbm_frac": hbm,
+            "mfma_frac": mfma, "roofline_fraction": max(hbm, mfma)}
+
+
+def gpu_clock():
+    """The graphics clock while a long call runs: the current level of the
+    device's sysfs clock table (MHz), and the counter-derived clock of the
+    output sweep (GRBM_GUI_ACTIVE cycles over its duration) from the
+    committed counter summary when it was taken on the current source."""
+    import glob
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[3]
+    inp = synth.workload_inputs(w, device="cuda")
+    T = inp["q"].shape[1]
+    ws = torch.empty(kda.workspace_bytes(1, T, w.H, w.dk, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"], workspace=ws)
+    sysfs = None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if "*" in line:
+                    val = line.split(":", 1)[1].replace("*", "").strip().lower()
+                    sysfs = float(val.replace("mhz", "").strip())
+                    break
+        except (OSError, ValueError):
+            continue
+        if sysfs is not None:
+            break
+    torch.cuda.synchronize()
+    del inp, ws
+    torch.cuda.empty_cache()
+    return {"sysfs_sclk_mhz": sysfs,
+            "counter_mhz_output_sweep": read_traffic(MFMA_PROFILE, source_digest(PREFILL_SOURCES),
+                                                     "kda_chunk_sweep_out_clock_mhz", "prefill_source_digest"),
+            "nominal_mhz": 2400.0}
 
 
 def bench_states(calls: int):
@@ -653,11 +743,17 @@ def main() -> int:
                        "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop": p["flop_call"],
                        "issued_flop": issued,
                        "issued_frac": issued / p["mean_call"] / 1e12 / PEAK_BF16_TFLOPS}
+        # the whole call's roofline fraction: the larger of its HBM and its
+        # (algorithmic) MFMA fractions
+        out["roofline_fraction"] = max(out["call_roofline"]["frac"], out["mfma"]["frac"])
         out["config"]["buffer_sets"] = p["n_sets"]
     if args.only in ("prefill", "both") and not args.no_extra:
         # the packed 8-sequence batch, the million-token context and the serving batch, timed the
         # same way (secondary lines: the headline value is the workload above)
         out["other_workloads"] = [bench_workload(2, 10), bench_workload(3, 3), bench_workload(5, 20)]
+        # the cold protocol: a median over calls each after a cache flush
+        out["cold"] = [bench_cold(1, 20), bench_cold(2, 20), bench_cold(3, 5)]
+        out["gpu_clock"] = gpu_clock()
         out["states_workloads"] = bench_states(50)
         out["gate_workloads"] = bench_gates(50, 100)
         out["mx_workload"] = bench_mx(100)
