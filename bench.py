@@ -320,9 +320,7 @@ def bench_cold(wid: int, reps: int, warm: int = 3):
 
 def gpu_clock():
     """The graphics clock while a long call runs: the current level of the
-    device's sysfs clock table (MHz), and the counter-derived clock of the
-    output sweep (GRBM_GUI_ACTIVE cycles over its duration) from the
-    committed counter summary when it was taken on the current source."""
+    device's sysfs clock table (MHz), beside the nominal peak clock."""
     import glob
     import torch
     import gated_delta_rule_105_amd as kda
@@ -348,10 +346,7 @@ def gpu_clock():
     torch.cuda.synchronize()
     del inp, ws
     torch.cuda.empty_cache()
-    return {"sysfs_sclk_mhz": sysfs,
-            "counter_mhz_output_sweep": read_traffic(MFMA_PROFILE, source_digest(PREFILL_SOURCES),
-                                                     "kda_chunk_sweep_out_clock_mhz", "prefill_source_digest"),
-            "nominal_mhz": 2400.0}
+    return {"sysfs_sclk_mhz": sysfs, "nominal_mhz": 2400.0}
 
 
 def bench_states(calls: int):
