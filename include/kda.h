@@ -346,7 +346,10 @@ int kda_chunk_backward_overlapped(const kda_chunk_desc_ex_t* d,
  * Measurement twin of kda_chunk_backward: events[i] (5 caller-created
  * hipEvent_t, entries may be NULL) is recorded before stage i and events[4]
  * after the last.  Stages: 0 forward replay (its launches), 1 chunk records,
- * 2 state gradients (reverse over the chunks), 3 local gradients.
+ * 2 state gradients (reverse over the chunks), 3 local gradients.  With
+ * several windows of chunks (a workspace smaller than one window needs),
+ * stages 1 to 3 are those of the first window processed (the last chunks)
+ * and the interval from events[3] to events[4] also holds the later windows.
  */
 int kda_chunk_backward_timed(const kda_chunk_desc_ex_t* d,
                              const void* q, const void* k, const void* v, const void* g,
