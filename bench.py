@@ -27,7 +27,8 @@ prefix-cache states (kda_chunk_forward_states) beside plain calls;
 ``gate_workloads`` times Gated DeltaNet and DeltaNet gates beside KDA on the
 prefill and decode workloads; ``mx_workload`` the headline workload with q,
 k, v in MXFP8 (kda_chunk_forward_mx); ``backward_workload`` the backward pass
-(kda_chunk_backward) on the headline workload; ``cold`` the headline, packed
+(kda_chunk_backward) on the headline workload, ``backward_long_workload``
+at T = 65,536 with its default (windowed) workspace; ``cold`` the headline, packed
 and million-token workloads as the median of calls each preceded by a 1 GiB
 write that flushes L2 and the last-level cache; ``gpu_clock`` the graphics
 clock under load; ``roofline_fraction`` the larger of the call's HBM and
@@ -596,6 +597,50 @@ def bench_backward(calls: int, with_cpu: bool = True, overlap: bool = True):
                                                                f"{dom}_mfma_util_pct", "backward_source_digest")}}
 
 
+def bench_backward_long(calls: int, T: int = 65536):
+    """Backward pass at a long context (B=1, H=16, the prefill recipe at T
+    tokens) with the default workspace, which processes the chunks in windows:
+    mean overlapped and sequential calls, and the workspace per (chunk, head)."""
+    import torch
+    import gated_delta_rule_105_amd as kda
+    import synth
+
+    H, d, wid = 16, 128, 360
+    log(f"backward T={T} H={H}: inputs generated on the GPU")
+    inp = synth.prefill_inputs(1, T, H, d, d, "bf16", wid=wid, h0=True, device="cuda")
+    inp.update(synth.grad_inputs(inp, wid, device="cuda"))
+    nbytes = kda.backward_workspace_bytes(1, T, H, d, torch.bfloat16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def call(overlap):
+        return kda.chunk_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], h0=inp["h0"],
+                                  dht=inp["dht"], out=out, workspace=ws, overlap=overlap)
+
+    out.update(call(False))
+    call(True)
+    torch.cuda.synchronize()
+    res = {}
+    for overlap in (False, True):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in ev:
+            a.record(stream)
+            call(overlap)
+            b.record(stream)
+        torch.cuda.synchronize()
+        res[overlap] = sum(a.elapsed_time(b) for a, b in ev) / calls * 1e-3
+    chunk_heads = (T + 63) // 64 * H
+    log(f"backward T={T}: {res[True] * 1e3:.2f} ms overlapped, {res[False] * 1e3:.2f} ms sequential, "
+        f"workspace {nbytes / 2 ** 20:.0f} MiB")
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": f"kda-backward-bf16-B1-H16-T{T}-d128 (default workspace: windows of chunks)",
+            "mean_call_us": res[True] * 1e6, "sequential_call_us": res[False] * 1e6,
+            "value": T / res[True], "unit": "tokens/s", "workspace_bytes": nbytes,
+            "workspace_mib_per_chunk_head": nbytes / 2 ** 20 / chunk_heads}
+
+
 def bench_decode(steps: int, warmup: int):
     import torch
     import gated_delta_rule_105_amd as kda
@@ -753,6 +798,7 @@ def main() -> int:
         out["gate_workloads"] = bench_gates(50, 100)
         out["mx_workload"] = bench_mx(100)
         out["backward_workload"] = bench_backward(20, not args.no_cpu)
+        out["backward_long_workload"] = bench_backward_long(3)
     if args.only == "backward":
         out["backward_workload"] = bench_backward(args.steps, not args.no_cpu, not args.bwd_sequential)
     if args.only in ("decode", "both"):
