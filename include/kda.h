@@ -83,7 +83,7 @@ typedef struct {
   int B;            /* batch; must be 1 when n_seqs > 0                      */
   int T;            /* tokens per batch row (packed total when n_seqs > 0)   */
   int H;            /* heads                                                 */
-  int d_k;          /* key/query channels: 64 or 128                         */
+  int d_k;          /* key/query channels: 64 or 128 (fp32 chunked: 64)     */
   int d_v;          /* value channels: must equal d_k                        */
   int chunk;        /* tokens per chunk: 64                                  */
   int n_seqs;       /* 0: B sequences of T tokens; > 0: packed sequences     */
