@@ -910,12 +910,8 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   }
   // Second stream.  The state-gradient pass runs one workgroup per (pair, 16
   // columns) and leaves most CUs idle at small batch; the second stream fills
-  // them.  First with the replay, forked after the first record pass (the
-  // replay is off the critical path).  Then the state gradients of a window
-  // are walked in two launches, the later half of its chunks first; while the
-  // second launch walks the earlier half, the side stream computes the local
-  // gradients of the later half.  Those of the earlier half follow on the
-  // call's stream once the walk and the replay are done.
+  // them: first with the replay, forked after the first record pass (the
+  // replay is off the critical path), then with local gradients.
   const hipStream_t side = (hipStream_t)aux->stream;
   const hipEvent_t fork = (hipEvent_t)aux->fork, join = (hipEvent_t)aux->join;
   if ((e = record(window(nw - 1))) != hipSuccess) return (int)e;
@@ -924,52 +920,43 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   const int rc = replay(side);
   if (rc != 0) return rc;
   if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;  // replay done
-  if (nw > 1) {
-    // Several windows share one area: a window's record pass waits until the
-    // side stream's local gradients of the window before are done with it.
-    for (int64_t wi = nw - 1; wi >= 0; --wi) {
-      const Win wn = window(wi);
-      const int64_t top = wn.hi < bp.span ? wn.hi : bp.span, mid = wn.lo + (top - wn.lo) / 2;
-      if (wi < nw - 1 && (e = record(wn)) != hipSuccess) return (int)e;
-      if ((e = state(wn, wi, mid, wn.hi)) != hipSuccess) return (int)e;
-      // events are recorded again: a wait holds the state of the record it saw
-      if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
-      if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
-      if ((e = local(side, wn, mid, wn.hi)) != hipSuccess) return (int)e;
-      if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;
-      if (mid > wn.lo && (e = state(wn, wi, wn.lo, mid)) != hipSuccess) return (int)e;
-      if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;  // replay, side's local gradients
-      if (mid > wn.lo && (e = local(stream, wn, wn.lo, mid)) != hipSuccess) return (int)e;
-    }
-    return (int)hipSuccess;
-  }
-  const Win all = window(0);
+  // Every window the same way: the walk in up to kBwdParts launches over
+  // ranges [b_i, b_{i+1}) of the window's chunks (of the average sequence
+  // with one window), the last one open-ended; the local gradients of each
+  // range but the first go to the side stream once its walk is done, those
+  // of the first follow on the call's stream.  Windows share one area, so a
+  // window ends with the call's stream waiting for the side stream's local
+  // gradients before the next window's record pass overwrites it.
   const int64_t per_seq = cu ? (T_per + (int64_t)C * n_rows - 1) / ((int64_t)C * (n_rows > 0 ? n_rows : 1))
                              : (T_per + C - 1) / C;
-  // the walk in kBwdParts launches over chunk ranges [b_i, b_{i+1}) of the
-  // (average) sequence, the last one open-ended; the local gradients of each
-  // part but the first go to the side stream once its walk is done
-  const int parts = per_seq < kBwdParts ? (int)per_seq : kBwdParts;
-  if (parts >= 2) {
-    auto bound = [&](int i) { return i >= parts ? kAll : per_seq * i / parts; };
-    if ((e = state(all, 0, bound(parts - 1), kAll)) != hipSuccess) return (int)e;
-    for (int i = parts - 1; i >= 1; --i) {
-      // the event is recorded again: the replay's wait above holds its earlier state
-      if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
-      if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
-      if ((e = local(side, all, bound(i), bound(i + 1))) != hipSuccess) return (int)e;
-      if ((e = state(all, 0, bound(i - 1), bound(i))) != hipSuccess) return (int)e;
+  for (int64_t wi = nw - 1; wi >= 0; --wi) {
+    const Win wn = window(wi);
+    if (wi < nw - 1 && (e = record(wn)) != hipSuccess) return (int)e;
+    const int64_t span = bp.width > 0 ? (wn.hi < bp.span ? wn.hi : bp.span) - wn.lo : per_seq;
+    const int parts = span < kBwdParts ? (int)span : kBwdParts;
+    auto bound = [&](int i) { return i >= parts ? wn.hi : wn.lo + span * i / parts; };
+    if (parts >= 2) {
+      if ((e = state(wn, wi, bound(parts - 1), wn.hi)) != hipSuccess) return (int)e;
+      for (int i = parts - 1; i >= 1; --i) {
+        // the event is recorded again: a wait holds the state of the record it saw
+        if ((e = hipEventRecord(fork, stream)) != hipSuccess) return (int)e;
+        if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return (int)e;
+        if ((e = local(side, wn, bound(i), bound(i + 1))) != hipSuccess) return (int)e;
+        if ((e = state(wn, wi, bound(i - 1), bound(i))) != hipSuccess) return (int)e;
+      }
+    } else if ((e = state(wn, wi, wn.lo, wn.hi)) != hipSuccess) {
+      return (int)e;
     }
-    if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;  // the replay
-    if ((e = local(stream, all, 0, bound(1))) != hipSuccess) return (int)e;
-    // join recorded again after the side's local gradients; the wait above
-    // holds the replay's record
-    if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;
-    return (int)hipStreamWaitEvent(stream, join, 0);
+    // join was last recorded after the replay (first window) or waited for
+    // already (later windows)
+    if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;
+    if ((e = local(stream, wn, wn.lo, parts >= 2 ? bound(1) : wn.hi)) != hipSuccess) return (int)e;
+    if (parts >= 2) {
+      if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;  // the side's local gradients
+      if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;
+    }
   }
-  if ((e = state(all, 0, 0, kAll)) != hipSuccess) return (int)e;
-  if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return (int)e;
-  return (int)local(stream, all, 0, kAll);
+  return (int)hipSuccess;
 }
 
 }  // namespace
