@@ -320,9 +320,9 @@ int kda_chunk_backward(const kda_chunk_desc_ex_t* d,
  * runs beside the state-gradient stage, which fills one CU per (sequence,
  * head, 16 state columns) and leaves the rest idle at small batch.  That stage
  * is then walked in several launches over ranges of the chunks, the last
- * chunks first (four quarters; halves of each window when the workspace
- * makes windows), and the local gradients of each range but the first run on
- * the second stream beside the walk over the ranges before it.
+ * chunks first (four quarters of the chunks, or of each window when the
+ * workspace makes windows), and the local gradients of each range but the
+ * first run on the second stream beside the walk over the ranges before it.
  *   aux_stream : hipStream_t (NULL = the default stream) that work is
  *                enqueued on; it waits for `stream` at each fork, and
  *                `stream` waits for it before the call's last launch and
