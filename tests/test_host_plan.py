@@ -1,0 +1,132 @@
+"""The backward's host plan against the workspace a call is given, on the CPU.
+
+The C front end (kda_api.cpp) is built with g++ against the stand-in
+launchers of tests/sanitize/host_stubs.cpp, which do nothing but keep the
+plan of the last backward call; so the window of chunks a call chooses can
+be read back without a GPU.  The call must take the widest window whose
+layout fits the workspace: one window when everything fits, else W chunks of
+every sequence with n_rows W area slots, never more bytes than given, and
+KDA_ERR_WORKSPACE_TOO_SMALL when not even one-chunk windows fit.
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from gated_delta_rule_105_amd._lib import (KDA_DTYPE_BF16, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_OK, ChunkDesc,
+                                           ChunkDescEx)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GB = 1 << 30
+NAMES = ["q", "k", "v", "g", "beta", "h0", "cu", "do", "dht", "dq", "dk", "dv", "dg", "dbeta", "dh0", "ws"]
+
+
+@pytest.fixture(scope="module")
+def stub(tmp_path_factory):
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    out = tmp_path_factory.mktemp("stub") / "libkda_stub.so"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-fPIC", "-shared", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "gated_delta_rule_105_amd", "csrc"), "-o", str(out),
+                    os.path.join(ROOT, "gated_delta_rule_105_amd", "csrc", "kda_api.cpp"),
+                    os.path.join(ROOT, "tests", "sanitize", "host_stubs.cpp")], check=True, timeout=600)
+    lib = ctypes.CDLL(str(out))
+    lib.kda_chunk_backward_workspace_size.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_backward.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 16 + [ctypes.c_size_t, ctypes.c_void_p]
+    lib.kda_stub_last_backward_plan.argtypes = [ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_longlong),
+                                                ctypes.POINTER(ctypes.c_ulonglong)]
+    return lib
+
+
+def desc(**kw):
+    base = dict(B=1, T=1 << 20, H=16, d_k=128, d_v=128, chunk=64, n_seqs=0, dtype=KDA_DTYPE_BF16, g_floor=-0.125)
+    base.update(kw)
+    return ChunkDesc(**base)
+
+
+def default_bytes(lib, d):
+    out = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_workspace_size(ctypes.byref(d), ctypes.byref(out)) == KDA_OK
+    return out.value
+
+
+def call(lib, d, budget):
+    """A backward call with fake, aligned, non-overlapping device addresses
+    (the stand-in launchers never touch them); returns the status and the
+    plan the call chose (window width, area slots, workspace bytes)."""
+    a = {name: (i + 1) * 64 * GB for i, name in enumerate(NAMES)}
+    if d.n_seqs == 0:
+        a["cu"] = None
+    dx = ChunkDescEx(shape=d, gate=0)
+    st = lib.kda_chunk_backward(ctypes.byref(dx), *(a[n] for n in NAMES), budget, None)
+    w, n, b = ctypes.c_longlong(-1), ctypes.c_longlong(-1), ctypes.c_ulonglong(0)
+    lib.kda_stub_last_backward_plan(ctypes.byref(w), ctypes.byref(n), ctypes.byref(b))
+    return st, w.value, n.value, b.value
+
+
+def per_slot_bytes(H, d, C=64):
+    # fp32 record (eight [C][d], three [C][C], gamma [d], beta [C]), scratch
+    # (five [C][d], two [C][C], one [d]) and end-state gradient [d][d] per
+    # (chunk, head)
+    return H * ((8 * C * d + 3 * C * C + d + C + 5 * C * d + 2 * C * C + d) * 4 + d * d * 4)
+
+
+def test_default_is_the_documented_window(stub):
+    d = desc()
+    size = default_bytes(stub, d)
+    st, width, n_area, used = call(stub, d, size)
+    assert st == KDA_OK
+    # max(64, 8192 / (H rows)) chunks: 512 at H = 16, one sequence
+    assert width == 512 and n_area == 512 and used <= size
+    # a workspace of the one-window size or more runs one window
+    st, width, n_area, single = call(stub, d, 1 << 50)
+    assert st == KDA_OK and width == 0 and n_area == (1 << 20) // 64
+    assert call(stub, d, single)[1:3] == (0, n_area)
+
+
+def test_widest_window_that_fits(stub):
+    d = desc(T=1 << 18)
+    single = call(stub, d, 1 << 50)[3]
+    step = per_slot_bytes(16, 128)
+    prev_width = 0
+    # budgets from just below one window down to a few chunks
+    for budget in sorted((single - 1, single // 2, single // 4, single // 8, single // 16), reverse=True):
+        st, width, n_area, used = call(stub, d, budget)
+        if st == KDA_ERR_WORKSPACE_TOO_SMALL:
+            break
+        assert st == KDA_OK
+        assert 1 <= width < (1 << 18) // 64 and n_area == width and used <= budget
+        # one chunk wider would need at least one more slot's bytes
+        assert used + step > budget
+        # narrower budgets never give wider windows
+        assert prev_width == 0 or width <= prev_width
+        prev_width = width
+    assert prev_width > 0
+
+
+def test_too_small_for_one_chunk_windows(stub):
+    d = desc(T=1 << 16)
+    single = call(stub, d, 1 << 50)[3]
+    st, width, _, used = call(stub, d, single // 4)
+    assert st == KDA_OK and width >= 1
+    # the state after every chunk alone is 64 KiB per (chunk, head)
+    assert call(stub, d, (1 << 16) // 64 * 16 * 128 * 128 * 4 // 2)[0] == KDA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_packed_batch_windows(stub):
+    d = desc(T=40000, H=32, n_seqs=8)
+    size = default_bytes(stub, d)
+    st, width, n_area, used = call(stub, d, size)
+    # the default keeps one window here (8 W slots would not save enough)
+    assert st == KDA_OK and width == 0 and used <= size
+    st, width, n_area, used = call(stub, d, size // 3)
+    assert st == KDA_OK and width >= 1 and n_area == 8 * width and used <= size // 3
+
+
+def test_short_call_keeps_one_window(stub):
+    d = desc(T=4096)
+    size = default_bytes(stub, d)
+    st, width, n_area, used = call(stub, d, size)
+    assert st == KDA_OK and width == 0 and n_area == 64 and used == size
