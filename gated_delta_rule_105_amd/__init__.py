@@ -28,6 +28,7 @@ from ._lib import (BWD_STAGES, CHUNK_LAUNCHES, KDA_DTYPE_BF16, KDA_DTYPE_F32, KD
 from . import _lib
 
 __all__ = ["chunk_forward", "chunk_forward_noalloc", "chunk_forward_states", "chunk_forward_mx", "chunk_backward", "decode_step",
+           "kda_chunk",
            "workspace_bytes", "backward_workspace_bytes", "make_desc", "make_desc_ex", "KdaError", "status_string",
            "version",
            "CHUNK_LAUNCHES", "BWD_STAGES"]
@@ -381,6 +382,44 @@ def chunk_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, chu
         raise KdaError(st, "kda_chunk_backward_timed" if events is not None else
                        "kda_chunk_backward_overlapped" if overlap else "kda_chunk_backward")
     return out
+
+
+_KDA_FUNCTION = None
+
+
+def _kda_function():
+    """torch.autograd.Function over chunk_forward and chunk_backward (built
+    on first use, so that importing the package does not import torch)."""
+    global _KDA_FUNCTION
+    if _KDA_FUNCTION is None:
+        torch = _torch()
+
+        class KDAChunk(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, g, beta, h0, cu_seqlens, g_floor):
+                o, ht = chunk_forward(q, k, v, g, beta, h0=h0, cu_seqlens=cu_seqlens, g_floor=g_floor)
+                ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens)
+                ctx.g_floor = g_floor
+                return o, ht
+
+            @staticmethod
+            def backward(ctx, do, dht):
+                q, k, v, g, beta, h0, cu_seqlens = ctx.saved_tensors
+                out = chunk_backward(q, k, v, g, beta, do.contiguous(), h0=h0,
+                                     dht=None if dht is None else dht.contiguous(), cu_seqlens=cu_seqlens,
+                                     g_floor=ctx.g_floor, want_dh0=h0 is not None, validate_cu=False)
+                return out["dq"], out["dk"], out["dv"], out["dg"], out["dbeta"], out["dh0"], None, None
+
+        _KDA_FUNCTION = KDAChunk
+    return _KDA_FUNCTION
+
+
+def kda_chunk(q, k, v, g, beta, h0=None, cu_seqlens=None, g_floor: float = -0.125):
+    """The chunked forward as a differentiable PyTorch operation: returns
+    (o, ht) like chunk_forward, and its backward is chunk_backward (the
+    gradients of q, k, v, g, beta and h0; o's gradient in o's dtype, ht's in
+    fp32).  Arguments as chunk_forward."""
+    return _kda_function().apply(q, k, v, g, beta, h0, cu_seqlens, g_floor)
 
 
 def decode_step(q, k, v, g, beta, state, g_floor: float = -0.125, *, o=None, stream=None):

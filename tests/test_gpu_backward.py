@@ -387,3 +387,34 @@ def test_backward_windows_match(name):
             torch.cuda.synchronize()
             for key in GRADS:
                 assert torch.equal(one[key], got[key]), (W, overlap, key)
+
+
+@pytest.mark.parametrize("name", ["f32_B2_T300_d64", "bf16_packed_d128", "bf16_deltanet_d128"])
+def test_autograd_matches_chunk_backward(name):
+    """kda_chunk under torch.autograd gives chunk_backward's gradients bit for
+    bit, for a loss whose gradients with respect to o and ht are seeded
+    tensors (o's cast to o's dtype, as autograd passes it)."""
+    if name.startswith("f32"):
+        inp = _case(2, 300, 2, 64, "f32", wid=380)
+    else:
+        inp = _case(1, 0, 2, 128, "bf16", lengths=[130, 1, 64, 257], wid=381)
+    d = to_dev(inp)
+    g = None if name.endswith("deltanet_d128") else d["g"]
+    note(f"kda_chunk autograd {name}")
+    leaves = {key: d[key].clone().requires_grad_(True) for key in ("q", "k", "v", "beta", "h0") if d.get(key) is not None}
+    gl = None if g is None else g.clone().requires_grad_(True)
+    o, ht = kda.kda_chunk(leaves["q"], leaves["k"], leaves["v"], gl, leaves["beta"], h0=leaves.get("h0"),
+                          cu_seqlens=d.get("cu_seqlens"))
+    r_o = torch.randn(o.shape, generator=torch.Generator().manual_seed(382)).cuda()
+    r_h = torch.randn(ht.shape, generator=torch.Generator().manual_seed(383)).cuda()
+    ((o.float() * r_o).sum() + (ht * r_h).sum()).backward()
+    ref = kda.chunk_backward(d["q"], d["k"], d["v"], g, d["beta"], r_o.to(o.dtype), h0=d.get("h0"), dht=r_h,
+                             cu_seqlens=d.get("cu_seqlens"))
+    torch.cuda.synchronize()
+    pairs = [("dq", leaves["q"]), ("dk", leaves["k"]), ("dv", leaves["v"]), ("dbeta", leaves["beta"])]
+    if gl is not None:
+        pairs.append(("dg", gl))
+    if "h0" in leaves:
+        pairs.append(("dh0", leaves["h0"]))
+    for key, leaf in pairs:
+        assert leaf.grad is not None and torch.equal(leaf.grad, ref[key]), key
