@@ -39,9 +39,11 @@
 //                   needs column j of dH and dO), writing every chunk's dH;
 //                   the next chunk's operands load during the current step.
 //   kda_bwd_local : one workgroup per (chunk, head): everything else.
-// Every product runs on fp32 MFMA (v_mfma_f32_16x16x4f32).  In the per-chunk
-// kernels the operands pass through LDS in k-slices (each element read once
-// per product); the state-gradient pass keeps its operands in registers.
+// Products run on fp32 MFMA (v_mfma_f32_16x16x4f32), except the record
+// pass's on the bf16 path, which take hi/lo bf16 MFMA (see gemm).  In the
+// per-chunk kernels the operands pass through LDS in k-slices (each element
+// read once per product); the state-gradient pass keeps its operands in
+// registers.
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -91,7 +93,7 @@ constexpr int kThreads = 512;
 // out[r][c] = alpha * (A1 B1 + A2 B2)[r][c] (+ out[r][c] when acc_in, + add[r][c]
 // when add is given, add laid out like out), then column scale cs[c] if
 // given, masked; 64 rows, N = 64 or 128 columns, K1,
-// K2 multiples of 32 (A2 null: one product).  Called by every thread of a
+// K2 multiples of 64 (A2 null: one product).  Called by every thread of a
 // kThreads workgroup.
 //
 // The k range is walked in slices of KS = 64: the workgroup copies the
@@ -103,76 +105,192 @@ constexpr int kThreads = 512;
 // one A fragment serves all of its tiles.  The lane layout is the one of
 // kda_device.h: lane 16 g + i supplies row i of A and column i of B at
 // k = 16 kk + 4 g + e in issue e, and holds D[4 g + r][i].
-constexpr int KS = 64, KSP = KS + 4, GM_ROWS = 64;
-constexpr int kGemmLds = (GM_ROWS + 128) * KSP;  // floats of LDS the products use (the caller's buffer)
-template <int N>
+//
+// HL (the bf16 path): each fp32 operand x is split into bf16 hi = rn(x) and
+// lo = rn(x - hi) on its way into LDS, and a 32-wide k-block of the product
+// is three bf16 MFMAs, A_hi B_hi + A_hi B_lo + A_lo B_hi (the dropped
+// A_lo B_lo and the rounding of lo leave a relative error of about 2^-16
+// per term, against the 2^-8 of a plain bf16 product).  The bf16 matrix
+// rate is 16 times the fp32 one, so the three products take about a fifth
+// of the time of fp32 MFMA.  In LDS, the element k of a 32-wide block sits
+// at 8 (k / 4 % 4) + 4 (k / 16) + k % 4, so that the 8 elements a lane
+// supplies (k = 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3) are 16
+// contiguous bytes; rows are KSH = KS + 8 elements (36 dwords, so 8
+// consecutive rows' 16-byte reads cover the 32 banks once).
+constexpr int KS = 64, KSP = KS + 4, GM_ROWS = 64, KSH = KS + 8;
+constexpr int kGemmLdsF32 = (GM_ROWS + 128) * KSP;      // floats, fp32 operands
+constexpr int kGemmLdsHL = (GM_ROWS + 128) * KSH;       // floats: hi and lo bf16 planes
+constexpr int kGemmLds = kGemmLdsF32 > kGemmLdsHL ? kGemmLdsF32 : kGemmLdsHL;  // the caller's buffer
+// position of k (0 .. KS - 1) in an HL row
+__device__ __forceinline__ int hl_pos(int k) { return (k & ~31) + 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3); }
+template <int N, bool HL>
 __device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, Mask mask, const float* cs,
                      const MatA& A1, const MatB& B1, int K1, const MatA* A2, const MatB* B2, int K2,
                      const float* add = nullptr) {
   constexpr int M = GM_ROWS, NA = M * KS / kThreads, NB = N * KS / kThreads, NT = N / 32;
   static_assert(NA * kThreads == M * KS && NB * kThreads == N * KS, "slices tile the workgroup");
-  float(*sA)[KSP] = (float(*)[KSP])lds;
-  float(*sB)[KSP] = (float(*)[KSP])(lds + M * KSP);
+  static_assert(NA % 2 == 0 && NB % 2 == 0, "pairs of k");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int r0 = 16 * (wave >> 1), c0 = (wave & 1) * (N / 2);
   float ra[NA], rb[NB];
-  auto fetch = [&](const MatA& A, const MatB& B, int k0) {
-#pragma unroll
-    for (int e = 0; e < NA; ++e) {
-      const int x = tid + kThreads * e;
-      const int r = A.ak == 1 ? x / KS : x % M, k = A.ak == 1 ? x % KS : x / M;
-      ra[e] = A.p[r * A.ai + (k0 + k) * A.ak];
-    }
-#pragma unroll
-    for (int e = 0; e < NB; ++e) {
-      const int x = tid + kThreads * e;
-      const int c = B.bk == 1 ? x / KS : x % N, k = B.bk == 1 ? x % KS : x / N;
-      float val = B.p[(k0 + k) * B.bk + c * B.bj];
-      if (B.bs) val *= B.bs[k0 + k];
-      rb[e] = val;
-    }
-  };
-  auto stash = [&](const MatA& A, const MatB& B) {
-#pragma unroll
-    for (int e = 0; e < NA; ++e) {
-      const int x = tid + kThreads * e;
-      const int r = A.ak == 1 ? x / KS : x % M, k = A.ak == 1 ? x % KS : x / M;
-      sA[r][k] = ra[e];
-    }
-#pragma unroll
-    for (int e = 0; e < NB; ++e) {
-      const int x = tid + kThreads * e;
-      const int c = B.bk == 1 ? x / KS : x % N, k = B.bk == 1 ? x % KS : x / N;
-      sB[c][k] = rb[e];
-    }
-  };
   f32x4 acc[NT];
 #pragma unroll
   for (int u = 0; u < NT; ++u) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  auto run = [&](const MatA& A, const MatB& B, int K) {
-    fetch(A, B, 0);
-    for (int k0 = 0; k0 < K; k0 += KS) {
-      lds_barrier();  // every wave is done with the previous slice
-      stash(A, B);
-      lds_barrier();
-      if (k0 + KS < K) fetch(A, B, k0 + KS);
+  if constexpr (!HL) {
+    float(*sA)[KSP] = (float(*)[KSP])lds;
+    float(*sB)[KSP] = (float(*)[KSP])(lds + M * KSP);
+    auto fetch = [&](const MatA& A, const MatB& B, int k0) {
 #pragma unroll
-      for (int kk = 0; kk < KS / 16; ++kk) {
-        const f32x4 a = *(const f32x4*)&sA[r0 + i][16 * kk + 4 * g];
+      for (int e = 0; e < NA; ++e) {
+        const int x = tid + kThreads * e;
+        const int r = A.ak == 1 ? x / KS : x % M, k = A.ak == 1 ? x % KS : x / M;
+        ra[e] = A.p[r * A.ai + (k0 + k) * A.ak];
+      }
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          const f32x4 b = *(const f32x4*)&sB[c0 + 16 * u + i][16 * kk + 4 * g];
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc[u], 0, 0, 0);
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc[u], 0, 0, 0);
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc[u], 0, 0, 0);
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc[u], 0, 0, 0);
+      for (int e = 0; e < NB; ++e) {
+        const int x = tid + kThreads * e;
+        const int c = B.bk == 1 ? x / KS : x % N, k = B.bk == 1 ? x % KS : x / N;
+        float val = B.p[(k0 + k) * B.bk + c * B.bj];
+        if (B.bs) val *= B.bs[k0 + k];
+        rb[e] = val;
+      }
+    };
+    auto stash = [&](const MatA& A, const MatB& B) {
+#pragma unroll
+      for (int e = 0; e < NA; ++e) {
+        const int x = tid + kThreads * e;
+        const int r = A.ak == 1 ? x / KS : x % M, k = A.ak == 1 ? x % KS : x / M;
+        sA[r][k] = ra[e];
+      }
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const int x = tid + kThreads * e;
+        const int c = B.bk == 1 ? x / KS : x % N, k = B.bk == 1 ? x % KS : x / N;
+        sB[c][k] = rb[e];
+      }
+    };
+    auto run = [&](const MatA& A, const MatB& B, int K) {
+      fetch(A, B, 0);
+      for (int k0 = 0; k0 < K; k0 += KS) {
+        lds_barrier();  // every wave is done with the previous slice
+        stash(A, B);
+        lds_barrier();
+        if (k0 + KS < K) fetch(A, B, k0 + KS);
+#pragma unroll
+        for (int kk = 0; kk < KS / 16; ++kk) {
+          const f32x4 a = *(const f32x4*)&sA[r0 + i][16 * kk + 4 * g];
+#pragma unroll
+          for (int u = 0; u < NT; ++u) {
+            const f32x4 b = *(const f32x4*)&sB[c0 + 16 * u + i][16 * kk + 4 * g];
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc[u], 0, 0, 0);
+          }
         }
       }
-    }
-  };
-  run(A1, B1, K1);
-  if (A2) run(*A2, *B2, K2);
+    };
+    run(A1, B1, K1);
+    if (A2) run(*A2, *B2, K2);
+  } else {
+    // planes: A hi, A lo ([M][KSH] each), B hi, B lo ([N][KSH] each), bf16
+    bf16_t* sAh = (bf16_t*)lds;
+    bf16_t* sAl = sAh + M * KSH;
+    bf16_t* sBh = sAl + M * KSH;
+    bf16_t* sBl = sBh + N * KSH;
+    // thread pair p holds two consecutive k of one row (A) or column (B):
+    // elements 2 p and 2 p + 1 of ra / rb
+    auto fetch = [&](const MatA& A, const MatB& B, int k0) {
+#pragma unroll
+      for (int e = 0; e < NA / 2; ++e) {
+        const int x = tid + kThreads * e;
+        if (A.ak == 1) {  // k contiguous: one 8-byte load
+          const int r = x / (KS / 2), k = 2 * (x % (KS / 2));
+          const float2 v2 = *(const float2*)&A.p[r * A.ai + k0 + k];
+          ra[2 * e] = v2.x;
+          ra[2 * e + 1] = v2.y;
+        } else {  // rows contiguous across the threads
+          const int r = x % M, k = 2 * (x / M);
+          ra[2 * e] = A.p[r * A.ai + (k0 + k) * A.ak];
+          ra[2 * e + 1] = A.p[r * A.ai + (k0 + k + 1) * A.ak];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NB / 2; ++e) {
+        const int x = tid + kThreads * e;
+        int k;
+        if (B.bk == 1) {
+          const int c = x / (KS / 2);
+          k = 2 * (x % (KS / 2));
+          const float2 v2 = *(const float2*)&B.p[k0 + k + c * B.bj];
+          rb[2 * e] = v2.x;
+          rb[2 * e + 1] = v2.y;
+        } else {
+          const int c = x % N;
+          k = 2 * (x / N);
+          rb[2 * e] = B.p[(k0 + k) * B.bk + c * B.bj];
+          rb[2 * e + 1] = B.p[(k0 + k + 1) * B.bk + c * B.bj];
+        }
+        if (B.bs) {
+          rb[2 * e] *= B.bs[k0 + k];
+          rb[2 * e + 1] *= B.bs[k0 + k + 1];
+        }
+      }
+    };
+    // hi and lo of a pair as two packed bf16 words
+    auto split = [](float x0, float x1, uint32_t& hi, uint32_t& lo) {
+      hi = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x0, x1));
+      lo = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x0 - __uint_as_float(hi << 16),
+                                                        x1 - __uint_as_float(hi & 0xffff0000u)));
+    };
+    auto stash = [&](const MatA& A, const MatB& B) {
+#pragma unroll
+      for (int e = 0; e < NA / 2; ++e) {
+        const int x = tid + kThreads * e;
+        const int r = A.ak == 1 ? x / (KS / 2) : x % M, k = A.ak == 1 ? 2 * (x % (KS / 2)) : 2 * (x / M);
+        uint32_t hi, lo;
+        split(ra[2 * e], ra[2 * e + 1], hi, lo);
+        const int o = r * KSH + hl_pos(k);  // even: the pair is one 32-bit word
+        *(uint32_t*)&sAh[o] = hi;
+        *(uint32_t*)&sAl[o] = lo;
+      }
+#pragma unroll
+      for (int e = 0; e < NB / 2; ++e) {
+        const int x = tid + kThreads * e;
+        const int c = B.bk == 1 ? x / (KS / 2) : x % N, k = B.bk == 1 ? 2 * (x % (KS / 2)) : 2 * (x / N);
+        uint32_t hi, lo;
+        split(rb[2 * e], rb[2 * e + 1], hi, lo);
+        const int o = c * KSH + hl_pos(k);
+        *(uint32_t*)&sBh[o] = hi;
+        *(uint32_t*)&sBl[o] = lo;
+      }
+    };
+    auto run = [&](const MatA& A, const MatB& B, int K) {
+      fetch(A, B, 0);
+      for (int k0 = 0; k0 < K; k0 += KS) {
+        lds_barrier();  // every wave is done with the previous slice
+        stash(A, B);
+        lds_barrier();
+        if (k0 + KS < K) fetch(A, B, k0 + KS);
+#pragma unroll
+        for (int kb = 0; kb < KS / 32; ++kb) {
+          const int oa = (r0 + i) * KSH + 32 * kb + 8 * g;
+          const bf16x8 ah = *(const bf16x8*)&sAh[oa], al = *(const bf16x8*)&sAl[oa];
+#pragma unroll
+          for (int u = 0; u < NT; ++u) {
+            const int ob = (c0 + 16 * u + i) * KSH + 32 * kb + 8 * g;
+            const bf16x8 bh = *(const bf16x8*)&sBh[ob], bl = *(const bf16x8*)&sBl[ob];
+            acc[u] = mma(ah, bh, acc[u]);
+            acc[u] = mma(ah, bl, acc[u]);
+            acc[u] = mma(al, bh, acc[u]);
+          }
+        }
+      }
+    };
+    run(A1, B1, K1);
+    if (A2) run(*A2, *B2, K2);
+  }
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int c = c0 + 16 * u + i;
@@ -359,6 +477,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
                                                      float g_floor, int gate, float* __restrict__ rec,
                                                      float* __restrict__ zero_state, Win win) {
   typedef Rec<D> R;
+  constexpr bool HL = sizeof(T) == 2;  // bf16 path: products on hi/lo bf16 MFMA
   __shared__ ChunkPos pos;
   // the products' slices, and later (once the Gram products are done) the
   // inverse's operands diag(beta) Abar and T
@@ -423,9 +542,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   __syncthreads();
 
   // Abar = strict_lower(Kt Kh^T), P = lower_incl(Qt Kh^T)
-  gemm<C>(lds, Rp + R::AB, C, 1.f, false, kStrictLower, nullptr, rows(Rp + R::KT, D), kcols(Rp + R::KH, D), D,
+  gemm<C, HL>(lds, Rp + R::AB, C, 1.f, false, kStrictLower, nullptr, rows(Rp + R::KT, D), kcols(Rp + R::KH, D), D,
        nullptr, nullptr, 0);
-  gemm<C>(lds, Rp + R::PM, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::QT, D), kcols(Rp + R::KH, D), D,
+  gemm<C, HL>(lds, Rp + R::PM, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::QT, D), kcols(Rp + R::KH, D), D,
        nullptr, nullptr, 0);
   __syncthreads();
   for (int x = tid; x < C * C; x += blockDim.x) {
@@ -472,9 +591,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
   for (int x = tid; x < C * C; x += blockDim.x) Rp[R::TM + x] = Ts[x / C][x % C];
   __syncthreads();
   // Wk = T diag(beta) Kt, Wv = T diag(beta) V
-  gemm<D>(lds, Rp + R::WK, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::KT, D, Rp + R::BET), C,
+  gemm<D, HL>(lds, Rp + R::WK, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::KT, D, Rp + R::BET), C,
        nullptr, nullptr, 0);
-  gemm<D>(lds, Rp + R::WV, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::VV, D, Rp + R::BET), C,
+  gemm<D, HL>(lds, Rp + R::WV, D, 1.f, false, kFull, nullptr, rows(Rp + R::TM, C), krows(Rp + R::VV, D, Rp + R::BET), C,
        nullptr, nullptr, 0);
 }
 
@@ -677,6 +796,11 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
     int64_t m_lo, int64_t m_hi, Win win, int64_t a0) {
   typedef Rec<D> R;
   typedef Scr<D> W;
+  // fp32 MFMA on both paths here: with hi/lo bf16 products this kernel ran
+  // slower (550 against 491 us at T = 4096, H = 16), since its time goes to
+  // the scratch round trips between products, not to the matrix cores, and
+  // the splits cost registers (a 48-byte spill) and VALU work
+  constexpr bool HL = false;
   __shared__ ChunkPos pos;
   // the products' slices, and later the per-element dGamma of the chunk
   constexpr int kLds = kGemmLds > C * D ? kGemmLds : C * D;
@@ -698,12 +822,12 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   const float* bet = Rp + R::BET;
 
   // 1: U = Wv - Wk S;  dU = P^T dO + Kh diag(gamma) dH
-  gemm<D>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Rp + R::WK, D), krows(S, D), D, nullptr, nullptr, 0,
+  gemm<D, HL>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Rp + R::WK, D), krows(S, D), D, nullptr, nullptr, 0,
           Rp + R::WV);
   {
     const MatA a1 = trans(Rp + R::PM, C), a2 = rows(Rp + R::KH, D);
     const MatB b1 = krows(Rp + R::DO, D), b2 = krows(dH, D, gam);
-    gemm<D>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, a1, b1, C, &a2, &b2, D);
+    gemm<D, HL>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, a1, b1, C, &a2, &b2, D);
   }
   // dgamma-last: sum_j dH_cj S_next_cj per channel; NP neighbouring lanes
   // share a channel and combine their partial sums by shuffles
@@ -718,34 +842,34 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   }
   __syncthreads();
   // 2: dP = lower_incl(dO U^T); Dv = T^T dU; dKh = U dH^T diag(gamma)
-  gemm<C>(lds, Wp + W::DP, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::DO, D), kcols(Wp + W::U, D), D, nullptr,
+  gemm<C, HL>(lds, Wp + W::DP, C, 1.f, false, kLowerIncl, nullptr, rows(Rp + R::DO, D), kcols(Wp + W::U, D), D, nullptr,
        nullptr, 0);
-  gemm<D>(lds, Wp + W::DV, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DU, D), C, nullptr,
+  gemm<D, HL>(lds, Wp + W::DV, D, 1.f, false, kFull, nullptr, trans(Rp + R::TM, C), krows(Wp + W::DU, D), C, nullptr,
        nullptr, 0);
-  gemm<D>(lds, Wp + W::DKH, D, 1.f, false, kFull, gam, rows(Wp + W::U, D), kcols(dH, D), D, nullptr, nullptr, 0);
+  gemm<D, HL>(lds, Wp + W::DKH, D, 1.f, false, kFull, gam, rows(Wp + W::U, D), kcols(dH, D), D, nullptr, nullptr, 0);
   __syncthreads();
   // 3: Dk = T^T (-dU S^T) = -Dv S^T (into U); dQt = dO S^T + dP Kh;
   //    dKh += dP^T Qt
-  gemm<D>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Wp + W::DV, D), kcols(S, D), D, nullptr, nullptr, 0);
+  gemm<D, HL>(lds, Wp + W::U, D, -1.f, false, kFull, nullptr, rows(Wp + W::DV, D), kcols(S, D), D, nullptr, nullptr, 0);
   {
     const MatA a1 = rows(Rp + R::DO, D), a2 = rows(Wp + W::DP, C);
     const MatB b1 = kcols(S, D), b2 = krows(Rp + R::KH, D);
-    gemm<D>(lds, Wp + W::DQT, D, 1.f, false, kFull, nullptr, a1, b1, D, &a2, &b2, C);
+    gemm<D, HL>(lds, Wp + W::DQT, D, 1.f, false, kFull, nullptr, a1, b1, D, &a2, &b2, C);
   }
-  gemm<D>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DP, C), krows(Rp + R::QT, D), C, nullptr,
+  gemm<D, HL>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DP, C), krows(Rp + R::QT, D), C, nullptr,
        nullptr, 0);
   __syncthreads();
   // 4: dA = strict_lower(-Dk Wk^T - Dv Wv^T)
   {
     const MatA a1 = rows(Wp + W::U, D), a2 = rows(Wp + W::DV, D);
     const MatB b1 = kcols(Rp + R::WK, D), b2 = kcols(Rp + R::WV, D);
-    gemm<C>(lds, Wp + W::DA, C, -1.f, false, kStrictLower, nullptr, a1, b1, D, &a2, &b2, D);
+    gemm<C, HL>(lds, Wp + W::DA, C, -1.f, false, kStrictLower, nullptr, a1, b1, D, &a2, &b2, D);
   }
   __syncthreads();
   // 5: E = Dk + dA Kh (into dU); dKh += dA^T diag(beta) Kt
-  gemm<D>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, rows(Wp + W::DA, C), krows(Rp + R::KH, D), C, nullptr,
+  gemm<D, HL>(lds, Wp + W::DU, D, 1.f, false, kFull, nullptr, rows(Wp + W::DA, C), krows(Rp + R::KH, D), C, nullptr,
        nullptr, 0, Wp + W::U);
-  gemm<D>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DA, C), krows(Rp + R::KT, D, bet), C,
+  gemm<D, HL>(lds, Wp + W::DKH, D, 1.f, true, kFull, nullptr, trans(Wp + W::DA, C), krows(Rp + R::KT, D, bet), C,
        nullptr, nullptr, 0);
   __syncthreads();
 
