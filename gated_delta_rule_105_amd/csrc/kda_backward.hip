@@ -66,6 +66,12 @@ __device__ __forceinline__ float ldx(const float* p) { return *p; }
 __device__ __forceinline__ float ldx(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ void stx(float* p, float x) { *p = x; }
 __device__ __forceinline__ void stx(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+// four consecutive elements (p 8-byte aligned for bf16, 16-byte for fp32)
+__device__ __forceinline__ void st4(float* p, const f32x4& x) { *(f32x4*)p = x; }
+__device__ __forceinline__ void st4(bf16_t* p, const f32x4& x) {
+  *(uint2*)p = make_uint2(__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1])),
+                          __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3])));
+}
 
 // Operand views for one product: A is M x K, B is K x N.
 struct MatA {
@@ -946,6 +952,341 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Local gradients of one chunk at D = 128, fused: the same products and
+// element-wise stage as kda_bwd_local, with every intermediate kept on chip
+// instead of passing through the scratch area.  Wave w owns column tile w
+// (16 columns): of the value side (U, dU, Dv) first, then of the key side
+// (Dk, dQt, dKh, E), so its own products stay in registers.  Operands every
+// wave reads whole go to LDS, each copied once: Wk, Kh, P, T and dO from the
+// record, then U, Dv, dP, Dk and dA as the waves produce them.  The other
+// operands are the wave's own columns, read straight from the record, the
+// states and dH.  So each record element is read about once per chunk (the
+// scratch version reads about 1.9 MB per (chunk, head) in all).
+//   phase 1 (value column tile w): U = Wv - Wk S, dU = P^T dO + Kh G
+//            (G = diag(gamma) dH), Dv = T^T dU, dv = diag(beta) Dv
+//   phase 2: dP = lower_incl(dO U^T) (tiles shared among the waves), then
+//            (key column tile w) Dk = -Dv S^T, dQt = dO S^T + dP Kh,
+//            dKh = U dH^T diag(gamma) + dP^T Qt
+//   phase 3: dA = strict_lower(-Dk Wk^T - Dv Wv^T) (tiles shared)
+//   phase 4: E = Dk + dA Kh, dKh += dA^T diag(beta) Kt, then the
+//            element-wise stage on the wave's key columns
+// Only the lower-triangular blocks of P, T, dP and dA enter the products.
+// fp32 operand fragment of a 16 x 16 x 4 product taken down a column:
+// X[k0 + 4 g + e][c] in issue e (frag_rows takes it along a row).
+__device__ __forceinline__ f32x4 frag_cols(const float* X, int ld, int c, int k0, int g) {
+  const float* p = X + (k0 + 4 * g) * ld + c;
+  return (f32x4){p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+// the lower-triangular 16 x 16 tiles (a, b), b <= a, of a 64 x 64 matrix
+__device__ __forceinline__ void low_tile(int t, int& a, int& b) {
+  a = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+  b = t - a * (a + 1) / 2;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
+    const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
+    const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
+    const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
+    const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
+    T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta,
+    int64_t m_lo, int64_t m_hi, Win win, int64_t a0) {
+  static_assert(D == 16 * (kThreads / 64), "one 16-column tile per wave");
+  typedef Rec<D> R;
+  // LDS rows of 4 extra floats: 16-byte aligned, and the 16-byte reads of
+  // 8 consecutive rows fall on distinct banks
+  constexpr int LX = D + 4, LC = C + 4, AX = C * LX, AC = C * LC;
+  __shared__ ChunkPos pos;
+  __shared__ __align__(16) float lds[3 * AX + 2 * AC];
+  float* const R0 = lds;            // Wk, then U, then Dk
+  float* const R1 = lds + AX;       // Kh, then Dv
+  float* const R3 = lds + 2 * AX;   // dO
+  float* const R2a = lds + 3 * AX;  // P, then dP
+  float* const R2b = R2a + AC;      // T, then dA
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, i = lane & 15;
+  const int h = blockIdx.y;
+  const int64_t slot = a0 + blockIdx.x;
+  if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;
+  if (pos.m < m_lo || pos.m >= m_hi) return;  // another launch's chunks
+  const float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
+  const float* dH = dHs + (slot * H + h) * (int64_t)D * D;
+  const int64_t dd = (int64_t)D * D;
+  const float* S = pos.m == 0 ? (h0 ? h0 + ((int64_t)pos.n * H + h) * dd : zero_state)
+                              : states + ((pos.st0 + pos.m - 1) * H + h) * dd;
+  const float* Sn = pos.m == pos.nc - 1 ? ht + ((int64_t)pos.n * H + h) * dd
+                                        : states + ((pos.st0 + pos.m) * H + h) * dd;
+  const float* gam = Rp + R::GAM;
+  const float* bet = Rp + R::BET;
+  const int len = pos.len;
+  const int cw = 16 * w;  // this wave's column tile
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+  // phase 1's own columns of S and G = diag(gamma) dH (k down the key
+  // channels), loaded first so that they are in flight during the staging
+  f32x4 fs[D / 16], fg[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    fs[kb] = frag_cols(S, D, cw + i, 16 * kb, gq);
+    fg[kb] = frag_cols(dH, D, cw + i, 16 * kb, gq) * *(const f32x4*)(gam + 16 * kb + 4 * gq);
+  }
+  for (int x = tid; x < C * D / 4; x += kThreads) {
+    const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
+    *(f32x4*)&R0[r * LX + c4] = *(const f32x4*)&Rp[R::WK + r * D + c4];
+    *(f32x4*)&R1[r * LX + c4] = *(const f32x4*)&Rp[R::KH + r * D + c4];
+    *(f32x4*)&R3[r * LX + c4] = *(const f32x4*)&Rp[R::DO + r * D + c4];
+  }
+  for (int x = tid; x < C * C / 4; x += kThreads) {
+    const int r = x / (C / 4), c4 = 4 * (x % (C / 4));
+    *(f32x4*)&R2a[r * LC + c4] = *(const f32x4*)&Rp[R::PM + r * C + c4];
+    *(f32x4*)&R2b[r * LC + c4] = *(const f32x4*)&Rp[R::TM + r * C + c4];
+  }
+  __syncthreads();
+
+  // ---- phase 1: value columns cw .. cw + 15
+  f32x4 U[4], dU[4], Dv[4];
+  {
+    f32x4 a[4] = {z4, z4, z4, z4}, b[4] = {z4, z4, z4, z4};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        a[rt] = mma(frag_rows(R0, LX, 16 * rt + i, 16 * kb, gq), fs[kb], a[rt]);  // Wk S
+        b[rt] = mma(frag_rows(R1, LX, 16 * rt + i, 16 * kb, gq), fg[kb], b[rt]);  // Kh G
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < C / 16; ++kb) {
+      const f32x4 fo = frag_cols(R3, LX, cw + i, 16 * kb, gq);  // dO[token][value]
+#pragma unroll
+      for (int rt = 0; rt <= kb; ++rt) b[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fo, b[rt]);  // P^T
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) U[rt][e] = Rp[R::WV + (16 * rt + 4 * gq + e) * D + cw + i] - a[rt][e];
+      dU[rt] = b[rt];
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    Dv[rt] = z4;
+#pragma unroll
+    for (int kb = rt; kb < C / 16; ++kb) Dv[rt] = mma(frag_cols(R2b, LC, 16 * rt + i, 16 * kb, gq), dU[kb], Dv[rt]);
+  }
+  lds_barrier();  // every wave is done with Wk, Kh, P and T
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      R0[(16 * rt + 4 * gq + e) * LX + cw + i] = U[rt][e];
+      R1[(16 * rt + 4 * gq + e) * LX + cw + i] = Dv[rt][e];
+    }
+  lds_barrier();
+
+  // ---- phase 2: dP = lower_incl(dO U^T), its 10 lower tiles over the waves
+  for (int t = w; t < 10; t += kThreads / 64) {
+    int ta, tb;
+    low_tile(t, ta, tb);
+    f32x4 acc = z4;
+#pragma unroll 4
+    for (int kb = 0; kb < D / 16; ++kb)
+      acc = mma(frag_rows(R3, LX, 16 * ta + i, 16 * kb, gq), frag_rows(R0, LX, 16 * tb + i, 16 * kb, gq), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      R2a[(16 * ta + 4 * gq + e) * LC + 16 * tb + i] = (ta > tb || 4 * gq + e >= i) ? acc[e] : 0.f;
+  }
+  // key columns cw .. cw + 15: Dk = -Dv S^T, dQt = dO S^T, dKh = U dH^T
+  // diag(gamma) (the products with dP wait for its tiles)
+  // With them, this lane's part of dgamma-last of key channel cw + i,
+  // sum_j dH_cj S_next_cj over the j its fragments hold.
+  f32x4 Dk[4] = {z4, z4, z4, z4}, dQt[4] = {z4, z4, z4, z4}, dKh[4] = {z4, z4, z4, z4};
+  float dgl = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    const f32x4 fs = frag_rows(S, D, cw + i, 16 * kb, gq);   // S^T[value][key] = S[key][value]
+    const f32x4 fh = frag_rows(dH, D, cw + i, 16 * kb, gq);  // dH[key][value]
+    const f32x4 fn = frag_rows(Sn, D, cw + i, 16 * kb, gq);
+    dgl += fh[0] * fn[0] + fh[1] * fn[1] + fh[2] * fn[2] + fh[3] * fn[3];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Dk[rt] = mma(frag_rows(R1, LX, 16 * rt + i, 16 * kb, gq), fs, Dk[rt]);
+      dQt[rt] = mma(frag_rows(R3, LX, 16 * rt + i, 16 * kb, gq), fs, dQt[rt]);
+      dKh[rt] = mma(frag_rows(R0, LX, 16 * rt + i, 16 * kb, gq), fh, dKh[rt]);
+    }
+  }
+  {
+    const float gc = gam[cw + i];  // the column's scale
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Dk[rt] = -Dk[rt];
+      dKh[rt] = dKh[rt] * gc;
+    }
+  }
+  // this wave's columns of Kh and Qt, k running over tokens (kept for phase 4
+  // and the element-wise stage, whose rows are these)
+  f32x4 fk[4], fq[4];
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb) {
+    fk[kb] = frag_cols(Rp + R::KH, D, cw + i, 16 * kb, gq);
+    fq[kb] = frag_cols(Rp + R::QT, D, cw + i, 16 * kb, gq);
+  }
+  lds_barrier();  // dP complete; U no longer read
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) R0[(16 * rt + 4 * gq + e) * LX + cw + i] = Dk[rt][e];
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (kb <= rt) dQt[rt] = mma(frag_rows(R2a, LC, 16 * rt + i, 16 * kb, gq), fk[kb], dQt[rt]);  // dP Kh
+      if (kb >= rt) dKh[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fq[kb], dKh[rt]);  // dP^T Qt
+    }
+  lds_barrier();  // Dk complete
+
+  // ---- phase 3: dA = strict_lower(-Dk Wk^T - Dv Wv^T), lower tiles over the waves
+  float dbr;  // dbeta of row tid / 8 (in lanes tid % 8 == 0)
+  for (int t = w; t < 10; t += kThreads / 64) {
+    int ta, tb;
+    low_tile(t, ta, tb);
+    f32x4 acc = z4;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      acc = mma(frag_rows(R0, LX, 16 * ta + i, 16 * kb, gq), frag_rows(Rp + R::WK, D, 16 * tb + i, 16 * kb, gq), acc);
+      acc = mma(frag_rows(R1, LX, 16 * ta + i, 16 * kb, gq), frag_rows(Rp + R::WV, D, 16 * tb + i, 16 * kb, gq), acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      R2b[(16 * ta + 4 * gq + e) * LC + 16 * tb + i] = (ta > tb || 4 * gq + e > i) ? -acc[e] : 0.f;
+  }
+  lds_barrier();
+  // dbeta_r = <Dk_r, Kt_r> + <Dv_r, V_r> + sum_{s < r} dA_rs Abar_rs (Dk in R0,
+  // Dv in R1, dA in R2b), 8 neighbouring lanes per row.  Loads go out before
+  // any of this kernel's stores from here on: loads and stores share one
+  // in-order completion counter, so a load issued after stores also waits
+  // for them.
+  {
+    const int r = tid / 8, part = tid % 8;
+    float acc = 0.f;
+    for (int c2 = part; c2 < D; c2 += 8)
+      acc += R0[r * LX + c2] * Rp[R::KT + r * D + c2] + R1[r * LX + c2] * Rp[R::VV + r * D + c2];
+    for (int s2 = part; s2 < r; s2 += 8) acc += R2b[r * LC + s2] * Rp[R::AB + r * C + s2];
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
+    dbr = acc;
+  }
+
+  // ---- phase 4: E = Dk + dA Kh, dKh += dA^T diag(beta) Kt (key columns)
+  f32x4 E[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) E[rt] = Dk[rt];
+  f32x4 fkt[4];  // this wave's columns of Kt
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb) {
+    fkt[kb] = frag_cols(Rp + R::KT, D, cw + i, 16 * kb, gq);
+    const f32x4 ft = fkt[kb] * *(const f32x4*)(bet + 16 * kb + 4 * gq);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (kb <= rt) E[rt] = mma(frag_rows(R2b, LC, 16 * rt + i, 16 * kb, gq), fk[kb], E[rt]);
+      if (kb >= rt) dKh[rt] = mma(frag_cols(R2b, LC, 16 * rt + i, 16 * kb, gq), ft, dKh[rt]);
+    }
+  }
+
+  // ---- element-wise, key column c of this lane, rows 16 rt + 4 gq + e
+  const bool bf = sizeof(T) == 2;
+  const int c = cw + i;
+  // Qt, Kt and Kh at this lane's elements are fq, fkt and fk (row 16 rt +
+  // 4 gq + e is element e of fragment rt); Gamma, and which rows pass the
+  // floor (bit 4 rt + e), are loaded here, before any store
+  f32x4 gm[4];
+  uint32_t keep = 0;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * gq + e;
+      gm[rt][e] = Rp[R::GM + r * D + c];
+      if (r < len && gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c) >= g_floor) keep |= 1u << (4 * rt + e);
+    }
+  dgl += __shfl_xor(dgl, 16);  // dgamma-last: the four lane groups' parts
+  dgl += __shfl_xor(dgl, 32);
+  // beta of the rows this thread writes out below (r = tid / 32 + 16 j)
+  float bv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bv[j] = bet[tid / (D / 4) + 16 * j];
+  // dq, dk and dg go out as whole rows: staged in R0 (Dk is no longer read),
+  // Q2 over R2a and R2b (dA neither) and R3
+  float* const Q2 = R2a;
+  static_assert(2 * AC >= AX, "a [C][LX] array fits R2a and R2b");
+  lds_barrier();  // every wave is past the dbeta pass and phase 4
+  f32x4 dG[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * gq + e;
+      const float G = gm[rt][e];
+      const float ep = __expf(G), ei = __expf(-G);
+      const float dqt = dQt[rt][e], dkt = bet[r] * E[rt][e], dkh = dKh[rt][e];
+      dG[rt][e] = dqt * fq[rt][e] + dkt * fkt[rt][e] - dkh * fk[rt][e];
+      R0[r * LX + c] = dqt * ep;
+      Q2[r * LX + c] = dkt * ep + dkh * ei;
+    }
+  // dg_r = sum_{s >= r} dGamma_s + dgamma-last, masked by the floor.  A lane
+  // holds rows 4 gq .. 4 gq + 3 of each row tile: the sums of the later row
+  // tiles, of the later lane groups in the same tile, then its own rows.
+  // The masked values go to R3 (dO is no longer read): dg itself with the
+  // per-channel gate, the terms of the channel sums below with the per-head one.
+  {
+    float tot[4], after[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float s = dG[rt][0] + dG[rt][1] + dG[rt][2] + dG[rt][3];
+      const float v0 = __shfl(s, i), v1 = __shfl(s, 16 + i), v2 = __shfl(s, 32 + i), v3 = __shfl(s, 48 + i);
+      tot[rt] = v0 + v1 + v2 + v3;
+      after[rt] = (gq < 1 ? v1 : 0.f) + (gq < 2 ? v2 : 0.f) + (gq < 3 ? v3 : 0.f);
+    }
+    float later = dgl;
+#pragma unroll
+    for (int rt = 3; rt >= 0; --rt) {
+      float run = later + after[rt];
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const int r = 16 * rt + 4 * gq + e;
+        run += dG[rt][e];
+        R3[r * LX + c] = (keep >> (4 * rt + e)) & 1u ? run : 0.f;
+      }
+      later += tot[rt];
+    }
+  }
+  lds_barrier();  // the staged rows are complete
+  // whole rows out, four channels a thread and step: dq, dk, dv = diag(beta)
+  // Dv (R1) and the per-channel dg
+  for (int j = 0; j < 4; ++j) {
+    const int x = tid + kThreads * j, r = x / (D / 4), c4 = 4 * (x % (D / 4));
+    if (r < len) {
+      const int64_t o = ((pos.tok0 + r) * H + h) * D + c4;
+      st4(dq + o, *(const f32x4*)&R0[r * LX + c4]);
+      st4(dk + o, *(const f32x4*)&Q2[r * LX + c4]);
+      st4(dv + o, bv[j] * *(const f32x4*)&R1[r * LX + c4]);
+      if (gate == kGateChannel) st4(dg + o, *(const f32x4*)&R3[r * LX + c4]);
+    }
+  }
+  {
+    const int r = tid / 8, part = tid % 8;
+    if (gate == kGateHead) {
+      // per-head dg_r: the channel sum of R3's row
+      float hg = 0.f;
+      for (int c2 = part; c2 < D; c2 += 8) hg += R3[r * LX + c2];
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) hg += __shfl_xor(hg, m);
+      if (part == 0 && r < len) stx(dg + (pos.tok0 + r) * H + h, hg);
+    }
+    if (part == 0 && r < len) dbeta[(pos.tok0 + r) * H + h] = dbr;
+  }
+}
+
 template <typename T, int D>
 int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_floor, int gate,
                      const ChunkInputs& in, const float* h0, const int32_t* cu, const void* dout, const float* dht,
@@ -960,8 +1301,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   float* dHs = (float*)(w + bp.dh_off);
   int64_t* seqs = (int64_t*)(w + bp.seq_off);
   float* carry = bp.width > 0 ? (float*)(w + bp.carry_off) : nullptr;
-  if (bp.rec_floats != (size_t)Rec<D>::FLOATS || bp.scr_floats != (size_t)Scr<D>::FLOATS)
-    return (int)hipErrorInvalidValue;
+  if (bp.rec_floats != (size_t)Rec<D>::FLOATS || bp.scr_floats != bwd_scr_floats(D)) return (int)hipErrorInvalidValue;
   hipError_t e;
   auto mark = [&](int i) -> hipError_t {
     return (events && events[i]) ? hipEventRecord((hipEvent_t)events[i], stream) : hipSuccess;
@@ -999,6 +1339,12 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     return launch_kernel(kda_bwd_state<D>, dim3((unsigned)state_blocks), dim3(512), stream, (const float*)rec, dht,
                          cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, wn, dHs, dh0, cin, cout);
   };
+  // the fused local kernel at D = 128 (one column tile per wave), the
+  // scratch version otherwise
+  auto const local_kernel = [] {
+    if constexpr (D == 16 * (kThreads / 64)) return &kda_bwd_local_fused<T, D>;
+    else return &kda_bwd_local<T, D>;
+  }();
   // A single fixed-length sequence has its chunks [lo, hi) at consecutive
   // area slots, so the grid covers just those; otherwise the whole area.
   auto local = [&](hipStream_t st, const Win& wn, int64_t lo, int64_t hi) {
@@ -1010,7 +1356,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
       a0 = lo - wn.lo;
       count = top - lo;
     }
-    return launch_kernel(kda_bwd_local<T, D>, dim3((unsigned)count, H), dim3(kThreads), st, (const T*)in.q,
+    return launch_kernel(local_kernel, dim3((unsigned)count, H), dim3(kThreads), st, (const T*)in.q,
                          (const T*)in.k, in.g, cu, (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate,
                          (const float*)rec, h0, (const float*)ht, (const float*)states, (const float*)zero,
                          (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi, wn, a0);
@@ -1087,8 +1433,8 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
 
 static_assert(bwd_rec_floats(64) == (size_t)Rec<64>::FLOATS && bwd_rec_floats(128) == (size_t)Rec<128>::FLOATS,
               "record layout agrees with the host plan");
-static_assert(bwd_scr_floats(64) == (size_t)Scr<64>::FLOATS && bwd_scr_floats(128) == (size_t)Scr<128>::FLOATS,
-              "scratch layout agrees with the host plan");
+static_assert(bwd_scr_floats(64) == (size_t)Scr<64>::FLOATS && bwd_scr_floats(128) == 0,
+              "scratch layout agrees with the host plan (none for the fused kernel at D = 128)");
 static_assert(Rec<128>::FLOATS % 4 == 0 && Rec<64>::FLOATS % 4 == 0 && Scr<128>::FLOATS % 4 == 0 &&
                   Scr<64>::FLOATS % 4 == 0 && Rec<128>::GAM % 4 == 0 && Rec<128>::BET % 4 == 0 &&
                   Rec<64>::GAM % 4 == 0 && Rec<64>::BET % 4 == 0,

@@ -349,7 +349,7 @@ def test_backward_timed_matches_sequential(name):
 
 def _window_budget(inp, W):
     """Workspace bytes for windows of about W chunks: the default size less
-    the per-chunk areas (fp32 record, scratch and end-state gradient) of the
+    the per-chunk areas (fp32 record, scratch at d = 64, end-state gradient) of the
     chunks beyond n_rows W slots, plus the two carry states per (sequence,
     head) that windows add."""
     B, T, H, d = inp["q"].shape
@@ -357,7 +357,8 @@ def _window_budget(inp, W):
     rows = B if cu is None else cu.numel() - 1
     chunks = (T + 63) // 64
     n_slots = rows * chunks if cu is None else chunks + rows
-    per_slot = H * ((8 * 64 * d + 3 * 64 * 64 + d + 64 + 5 * 64 * d + 2 * 64 * 64 + d) * 4 + d * d * 4)
+    scr = 0 if d == 128 else 5 * 64 * d + 2 * 64 * 64 + d  # the d = 128 kernel keeps it on chip
+    per_slot = H * ((8 * 64 * d + 3 * 64 * 64 + d + 64 + scr) * 4 + d * d * 4)
     full = kda.backward_workspace_bytes(B, T, H, d, inp["q"].dtype, n_seqs=0 if cu is None else rows)
     return full - (n_slots - rows * W) * per_slot + 2 * rows * H * d * d * 4 + 4 * 256
 
