@@ -38,7 +38,9 @@
 //                   dS walked backward over the chunks (column j of dS only
 //                   needs column j of dH and dO), writing every chunk's dH;
 //                   the next chunk's operands load during the current step.
-//   kda_bwd_local : one workgroup per (chunk, head): everything else.
+//   kda_bwd_local : one workgroup per (chunk, head): everything else
+//                   (kda_bwd_local_fused at D = 128, with every intermediate
+//                   on chip; through a scratch area at D = 64).
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4f32), except the record
 // pass's on the bf16 path, which take hi/lo bf16 MFMA (see gemm).  In the
 // per-chunk kernels the operands pass through LDS in k-slices (each element
