@@ -55,8 +55,11 @@ namespace kda {
 namespace {
 
 constexpr int C = kChunk;
-// Launches of the state-gradient walk in the overlapped call (one window).
-constexpr int kBwdParts = 4;
+// Launches of the state-gradient walk in the overlapped call (one window):
+// four, or two when a window spans at most kBwdShortSpan chunks of a
+// sequence (at T = 4096, H = 16: 722 against 733 us; at T = 65,536 four
+// parts take 10.9 against 11.1 ms).
+constexpr int kBwdParts = 4, kBwdShortSpan = 64;
 
 // Barrier for LDS hand-offs only: the waves' LDS operations are complete,
 // global loads may still be in flight (__syncthreads() is a release fence and
@@ -1392,7 +1395,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   const int rc = replay(side);
   if (rc != 0) return rc;
   if ((e = hipEventRecord(join, side)) != hipSuccess) return (int)e;  // replay done
-  // Every window the same way: the walk in up to kBwdParts launches over
+  // Every window the same way: the walk in up to `most` launches over
   // ranges [b_i, b_{i+1}) of the window's chunks (of the average sequence
   // with one window), the last one open-ended; the local gradients of each
   // range but the first go to the side stream once its walk is done, those
@@ -1405,7 +1408,8 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     const Win wn = window(wi);
     if (wi < nw - 1 && (e = record(wn)) != hipSuccess) return (int)e;
     const int64_t span = bp.width > 0 ? (wn.hi < bp.span ? wn.hi : bp.span) - wn.lo : per_seq;
-    const int parts = span < kBwdParts ? (int)span : kBwdParts;
+    const int most = span <= kBwdShortSpan ? 2 : kBwdParts;
+    const int parts = span < most ? (int)span : most;
     auto bound = [&](int i) { return i >= parts ? wn.hi : wn.lo + span * i / parts; };
     if (parts >= 2) {
       if ((e = state(wn, wi, bound(parts - 1), wn.hi)) != hipSuccess) return (int)e;

@@ -320,8 +320,9 @@ int kda_chunk_backward(const kda_chunk_desc_ex_t* d,
  * runs beside the state-gradient stage, which fills one CU per (sequence,
  * head, 16 state columns) and leaves the rest idle at small batch.  That stage
  * is then walked in several launches over ranges of the chunks, the last
- * chunks first (four quarters of the chunks, or of each window when the
- * workspace makes windows), and the local gradients of each range but the
+ * chunks first (four ranges of the chunks, or of each window when the
+ * workspace makes windows; two when that span is 64 chunks or fewer), and
+ * the local gradients of each range but the
  * first run on the second stream beside the walk over the ranges before it.
  *   aux_stream : hipStream_t (NULL = the default stream) that work is
  *                enqueued on; it waits for `stream` at each fork, and
