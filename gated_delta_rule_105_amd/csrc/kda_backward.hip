@@ -41,8 +41,9 @@
 //   kda_bwd_local : one workgroup per (chunk, head): everything else
 //                   (kda_bwd_local_fused at D = 128, with every intermediate
 //                   on chip; through a scratch area at D = 64).
-// Products run on fp32 MFMA (v_mfma_f32_16x16x4f32), except the record
-// pass's on the bf16 path, which take hi/lo bf16 MFMA (see gemm).  In the
+// Products run on fp32 MFMA (v_mfma_f32_16x16x4f32), except, on the bf16
+// path, the record pass's and most of kda_bwd_local_fused's, which take hi/lo
+// bf16 MFMA (see gemm and kda_bwd_local_fused).  In the
 // per-chunk kernels the operands pass through LDS in k-slices (each element
 // read once per product); the state-gradient pass keeps its operands in
 // registers.
@@ -977,11 +978,72 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
 //   phase 4: E = Dk + dA Kh, dKh += dA^T diag(beta) Kt, then the
 //            element-wise stage on the wave's key columns
 // Only the lower-triangular blocks of P, T, dP and dA enter the products.
+// The products whose operands run along rows (Wk S, Kh G, dP, Dk, dQt,
+// U dH^T, dA: about two thirds of the matrix work) take hi/lo bf16 MFMA, with
+// Wk, Kh, dO, U, Dv and Dk kept in LDS as hi and lo planes; those with the
+// [64][64] matrices P, T, dP and dA, read down columns, stay on fp32 MFMA,
+// each on its own accumulator (no accumulation chain mixes MFMA shapes).
 // fp32 operand fragment of a 16 x 16 x 4 product taken down a column:
 // X[k0 + 4 g + e][c] in issue e (frag_rows takes it along a row).
 __device__ __forceinline__ f32x4 frag_cols(const float* X, int ld, int c, int k0, int g) {
   const float* p = X + (k0 + 4 * g) * ld + c;
   return (f32x4){p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+// hi/lo bf16 operands of the 16 x 16 x 32 products on the bf16 path: x ~ hi
+// + lo to about 2^-16, a 32-wide k-block as A_hi B_hi + A_hi B_lo + A_lo
+// B_hi (three bf16 MFMAs against eight fp32 16 x 16 x 4 for the same k).
+struct HL8 {
+  bf16x8 h, l;
+};
+__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1]));
+  const uint32_t b = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3]));
+  hi = make_uint2(a, b);
+  lo = make_uint2(__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0] - __uint_as_float(a << 16),
+                                                               x[1] - __uint_as_float(a & 0xffff0000u))),
+                  __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2] - __uint_as_float(b << 16),
+                                                               x[3] - __uint_as_float(b & 0xffff0000u))));
+}
+// the fragment of a lane from its k = 4 g .. 4 g + 3 (x0) and 16 + 4 g ..
+// 16 + 4 g + 3 (x1) of a 32-wide k-block
+__device__ __forceinline__ HL8 hl_of(const f32x4& x0, const f32x4& x1) {
+  uint2 h0, l0, h1, l1;
+  split4(x0, h0, l0);
+  split4(x1, h1, l1);
+  return HL8{__builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y)),
+             __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y))};
+}
+__device__ __forceinline__ f32x4 mma3(const HL8& a, const HL8& b, f32x4 c) {
+  c = mma(a.h, b.h, c);
+  c = mma(a.h, b.l, c);
+  return mma(a.l, b.h, c);
+}
+// An LDS operand as hi and lo planes of [64][LH] bf16, element (r, k) at
+// r * LH + hl_pos(k) (a lane's fragment is 16 contiguous bytes of each
+// plane); rows of 68 dwords, so 8 consecutive rows' 16-byte reads fall on
+// distinct banks.
+constexpr int LH = 128 + 8, PLANE = C * LH;
+__device__ __forceinline__ HL8 hl_lds(const bf16_t* P, int r, int kb, int g) {
+  const int o = r * LH + 32 * kb + 8 * g;
+  return HL8{*(const bf16x8*)(P + o), *(const bf16x8*)(P + PLANE + o)};
+}
+__device__ __forceinline__ void hl_put(bf16_t* P, int r, int k, float x) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x, 0.f));
+  const int o = r * LH + hl_pos(k);
+  P[o] = (bf16_t)a;
+  P[PLANE + o] = (bf16_t)__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x - __uint_as_float(a << 16), 0.f));
+}
+__device__ __forceinline__ float hl_get(const bf16_t* P, int r, int k) {
+  const int o = r * LH + hl_pos(k);
+  return bf16_to_f32(P[o]) + bf16_to_f32(P[PLANE + o]);
+}
+// four consecutive k (k % 4 == 0) of row r
+__device__ __forceinline__ void hl_put4(bf16_t* P, int r, int k, const f32x4& x) {
+  uint2 hi, lo;
+  split4(x, hi, lo);
+  const int o = r * LH + hl_pos(k);
+  *(uint2*)(P + o) = hi;
+  *(uint2*)(P + PLANE + o) = lo;
 }
 // the lower-triangular 16 x 16 tiles (a, b), b <= a, of a 64 x 64 matrix
 __device__ __forceinline__ void low_tile(int t, int& a, int& b) {
@@ -999,16 +1061,22 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     int64_t m_lo, int64_t m_hi, Win win, int64_t a0) {
   static_assert(D == 16 * (kThreads / 64), "one 16-column tile per wave");
   typedef Rec<D> R;
-  // LDS rows of 4 extra floats: 16-byte aligned, and the 16-byte reads of
-  // 8 consecutive rows fall on distinct banks
-  constexpr int LX = D + 4, LC = C + 4, AX = C * LX, AC = C * LC;
+  static_assert(D == 128, "hi/lo planes of 128 columns");
+  // R0, R1, R3: hi/lo planes of [64][128] operands (2 PLANE bf16 each);
+  // R2a, R2b: fp32 [64][64] with rows of 4 extra floats (16-byte aligned,
+  // and the 16-byte reads of 8 consecutive rows fall on distinct banks).
+  // At the end R0, R3 and R2a..R2b hold fp32 [64][LX] output rows.
+  constexpr int LX = D + 4, LC = C + 4, AC = C * LC, AP = PLANE;  // AP: floats of a plane pair
+  static_assert(AP >= C * LX && 2 * AC >= C * LX, "fp32 rows fit the regions");
   __shared__ ChunkPos pos;
-  __shared__ __align__(16) float lds[3 * AX + 2 * AC];
-  float* const R0 = lds;            // Wk, then U, then Dk
-  float* const R1 = lds + AX;       // Kh, then Dv
-  float* const R3 = lds + 2 * AX;   // dO
-  float* const R2a = lds + 3 * AX;  // P, then dP
-  float* const R2b = R2a + AC;      // T, then dA
+  __shared__ __align__(16) float lds[3 * AP + 2 * AC];
+  bf16_t* const H0 = (bf16_t*)lds;             // Wk, then U, then Dk (hi/lo)
+  bf16_t* const H1 = (bf16_t*)(lds + AP);      // Kh, then Dv (hi/lo)
+  bf16_t* const H3 = (bf16_t*)(lds + 2 * AP);  // dO (hi/lo)
+  float* const R0 = lds;                       // fp32 output rows at the end
+  float* const R3 = lds + 2 * AP;
+  float* const R2a = lds + 3 * AP;             // P, then dP
+  float* const R2b = R2a + AC;                 // T, then dA
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, i = lane & 15;
   const int h = blockIdx.y;
   const int64_t slot = a0 + blockIdx.x;
@@ -1037,9 +1105,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   }
   for (int x = tid; x < C * D / 4; x += kThreads) {
     const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
-    *(f32x4*)&R0[r * LX + c4] = *(const f32x4*)&Rp[R::WK + r * D + c4];
-    *(f32x4*)&R1[r * LX + c4] = *(const f32x4*)&Rp[R::KH + r * D + c4];
-    *(f32x4*)&R3[r * LX + c4] = *(const f32x4*)&Rp[R::DO + r * D + c4];
+    hl_put4(H0, r, c4, *(const f32x4*)&Rp[R::WK + r * D + c4]);
+    hl_put4(H1, r, c4, *(const f32x4*)&Rp[R::KH + r * D + c4]);
+    hl_put4(H3, r, c4, *(const f32x4*)&Rp[R::DO + r * D + c4]);
   }
   for (int x = tid; x < C * C / 4; x += kThreads) {
     const int r = x / (C / 4), c4 = 4 * (x % (C / 4));
@@ -1051,26 +1119,27 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // ---- phase 1: value columns cw .. cw + 15
   f32x4 U[4], dU[4], Dv[4];
   {
-    f32x4 a[4] = {z4, z4, z4, z4}, b[4] = {z4, z4, z4, z4};
+    f32x4 a[4] = {z4, z4, z4, z4}, b[4] = {z4, z4, z4, z4}, bp[4] = {z4, z4, z4, z4};
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
+    for (int kb = 0; kb < D / 32; ++kb) {
+      const HL8 bs = hl_of(fs[2 * kb], fs[2 * kb + 1]), bg = hl_of(fg[2 * kb], fg[2 * kb + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        a[rt] = mma(frag_rows(R0, LX, 16 * rt + i, 16 * kb, gq), fs[kb], a[rt]);  // Wk S
-        b[rt] = mma(frag_rows(R1, LX, 16 * rt + i, 16 * kb, gq), fg[kb], b[rt]);  // Kh G
+        a[rt] = mma3(hl_lds(H0, 16 * rt + i, kb, gq), bs, a[rt]);  // Wk S
+        b[rt] = mma3(hl_lds(H1, 16 * rt + i, kb, gq), bg, b[rt]);  // Kh G
       }
     }
 #pragma unroll
     for (int kb = 0; kb < C / 16; ++kb) {
-      const f32x4 fo = frag_cols(R3, LX, cw + i, 16 * kb, gq);  // dO[token][value]
+      const f32x4 fo = frag_cols(Rp + R::DO, D, cw + i, 16 * kb, gq);  // dO[token][value]
 #pragma unroll
-      for (int rt = 0; rt <= kb; ++rt) b[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fo, b[rt]);  // P^T
+      for (int rt = 0; rt <= kb; ++rt) bp[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fo, bp[rt]);  // P^T
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) U[rt][e] = Rp[R::WV + (16 * rt + 4 * gq + e) * D + cw + i] - a[rt][e];
-      dU[rt] = b[rt];
+      dU[rt] = b[rt] + bp[rt];
     }
   }
 #pragma unroll
@@ -1084,8 +1153,8 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      R0[(16 * rt + 4 * gq + e) * LX + cw + i] = U[rt][e];
-      R1[(16 * rt + 4 * gq + e) * LX + cw + i] = Dv[rt][e];
+      hl_put(H0, 16 * rt + 4 * gq + e, cw + i, U[rt][e]);
+      hl_put(H1, 16 * rt + 4 * gq + e, cw + i, Dv[rt][e]);
     }
   lds_barrier();
 
@@ -1094,9 +1163,8 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     int ta, tb;
     low_tile(t, ta, tb);
     f32x4 acc = z4;
-#pragma unroll 4
-    for (int kb = 0; kb < D / 16; ++kb)
-      acc = mma(frag_rows(R3, LX, 16 * ta + i, 16 * kb, gq), frag_rows(R0, LX, 16 * tb + i, 16 * kb, gq), acc);
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) acc = mma3(hl_lds(H3, 16 * ta + i, kb, gq), hl_lds(H0, 16 * tb + i, kb, gq), acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       R2a[(16 * ta + 4 * gq + e) * LC + 16 * tb + i] = (ta > tb || 4 * gq + e >= i) ? acc[e] : 0.f;
@@ -1107,17 +1175,20 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // sum_j dH_cj S_next_cj over the j its fragments hold.
   f32x4 Dk[4] = {z4, z4, z4, z4}, dQt[4] = {z4, z4, z4, z4}, dKh[4] = {z4, z4, z4, z4};
   float dgl = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) {
-    const f32x4 fs = frag_rows(S, D, cw + i, 16 * kb, gq);   // S^T[value][key] = S[key][value]
-    const f32x4 fh = frag_rows(dH, D, cw + i, 16 * kb, gq);  // dH[key][value]
-    const f32x4 fn = frag_rows(Sn, D, cw + i, 16 * kb, gq);
-    dgl += fh[0] * fn[0] + fh[1] * fn[1] + fh[2] * fn[2] + fh[3] * fn[3];
+#pragma unroll 2
+  for (int kb = 0; kb < D / 32; ++kb) {
+    // S^T[value][key] = S[key][value], dH[key][value] (and S_next) along rows
+    const f32x4 s0 = frag_rows(S, D, cw + i, 32 * kb, gq), s1 = frag_rows(S, D, cw + i, 32 * kb + 16, gq);
+    const f32x4 h0v = frag_rows(dH, D, cw + i, 32 * kb, gq), h1v = frag_rows(dH, D, cw + i, 32 * kb + 16, gq);
+    const f32x4 n0 = frag_rows(Sn, D, cw + i, 32 * kb, gq), n1 = frag_rows(Sn, D, cw + i, 32 * kb + 16, gq);
+    dgl += h0v[0] * n0[0] + h0v[1] * n0[1] + h0v[2] * n0[2] + h0v[3] * n0[3] + h1v[0] * n1[0] + h1v[1] * n1[1] +
+           h1v[2] * n1[2] + h1v[3] * n1[3];
+    const HL8 bs = hl_of(s0, s1), bh = hl_of(h0v, h1v);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      Dk[rt] = mma(frag_rows(R1, LX, 16 * rt + i, 16 * kb, gq), fs, Dk[rt]);
-      dQt[rt] = mma(frag_rows(R3, LX, 16 * rt + i, 16 * kb, gq), fs, dQt[rt]);
-      dKh[rt] = mma(frag_rows(R0, LX, 16 * rt + i, 16 * kb, gq), fh, dKh[rt]);
+      Dk[rt] = mma3(hl_lds(H1, 16 * rt + i, kb, gq), bs, Dk[rt]);
+      dQt[rt] = mma3(hl_lds(H3, 16 * rt + i, kb, gq), bs, dQt[rt]);
+      dKh[rt] = mma3(hl_lds(H0, 16 * rt + i, kb, gq), bh, dKh[rt]);
     }
   }
   {
@@ -1140,13 +1211,16 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) R0[(16 * rt + 4 * gq + e) * LX + cw + i] = Dk[rt][e];
+    for (int e = 0; e < 4; ++e) hl_put(H0, 16 * rt + 4 * gq + e, cw + i, Dk[rt][e]);
+  // the fp32 products on their own accumulators (no accumulation chain mixes
+  // MFMA shapes), added below
+  f32x4 dQt2[4] = {z4, z4, z4, z4}, dKh2[4] = {z4, z4, z4, z4};
 #pragma unroll
   for (int kb = 0; kb < C / 16; ++kb)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      if (kb <= rt) dQt[rt] = mma(frag_rows(R2a, LC, 16 * rt + i, 16 * kb, gq), fk[kb], dQt[rt]);  // dP Kh
-      if (kb >= rt) dKh[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fq[kb], dKh[rt]);  // dP^T Qt
+      if (kb <= rt) dQt2[rt] = mma(frag_rows(R2a, LC, 16 * rt + i, 16 * kb, gq), fk[kb], dQt2[rt]);  // dP Kh
+      if (kb >= rt) dKh2[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fq[kb], dKh2[rt]);  // dP^T Qt
     }
   lds_barrier();  // Dk complete
 
@@ -1157,9 +1231,13 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     low_tile(t, ta, tb);
     f32x4 acc = z4;
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      acc = mma(frag_rows(R0, LX, 16 * ta + i, 16 * kb, gq), frag_rows(Rp + R::WK, D, 16 * tb + i, 16 * kb, gq), acc);
-      acc = mma(frag_rows(R1, LX, 16 * ta + i, 16 * kb, gq), frag_rows(Rp + R::WV, D, 16 * tb + i, 16 * kb, gq), acc);
+    for (int kb = 0; kb < D / 32; ++kb) {
+      const HL8 wk = hl_of(frag_rows(Rp + R::WK, D, 16 * tb + i, 32 * kb, gq),
+                           frag_rows(Rp + R::WK, D, 16 * tb + i, 32 * kb + 16, gq));
+      const HL8 wv = hl_of(frag_rows(Rp + R::WV, D, 16 * tb + i, 32 * kb, gq),
+                           frag_rows(Rp + R::WV, D, 16 * tb + i, 32 * kb + 16, gq));
+      acc = mma3(hl_lds(H0, 16 * ta + i, kb, gq), wk, acc);
+      acc = mma3(hl_lds(H1, 16 * ta + i, kb, gq), wv, acc);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -1175,7 +1253,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     const int r = tid / 8, part = tid % 8;
     float acc = 0.f;
     for (int c2 = part; c2 < D; c2 += 8)
-      acc += R0[r * LX + c2] * Rp[R::KT + r * D + c2] + R1[r * LX + c2] * Rp[R::VV + r * D + c2];
+      acc += hl_get(H0, r, c2) * Rp[R::KT + r * D + c2] + hl_get(H1, r, c2) * Rp[R::VV + r * D + c2];
     for (int s2 = part; s2 < r; s2 += 8) acc += R2b[r * LC + s2] * Rp[R::AB + r * C + s2];
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
@@ -1194,10 +1272,15 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       if (kb <= rt) E[rt] = mma(frag_rows(R2b, LC, 16 * rt + i, 16 * kb, gq), fk[kb], E[rt]);
-      if (kb >= rt) dKh[rt] = mma(frag_cols(R2b, LC, 16 * rt + i, 16 * kb, gq), ft, dKh[rt]);
+      if (kb >= rt) dKh2[rt] = mma(frag_cols(R2b, LC, 16 * rt + i, 16 * kb, gq), ft, dKh2[rt]);
     }
   }
 
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    dQt[rt] += dQt2[rt];
+    dKh[rt] += dKh2[rt];
+  }
   // ---- element-wise, key column c of this lane, rows 16 rt + 4 gq + e
   const bool bf = sizeof(T) == 2;
   const int c = cw + i;
@@ -1223,7 +1306,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // dq, dk and dg go out as whole rows: staged in R0 (Dk is no longer read),
   // Q2 over R2a and R2b (dA neither) and R3
   float* const Q2 = R2a;
-  static_assert(2 * AC >= AX, "a [C][LX] array fits R2a and R2b");
+  static_assert(2 * AC >= C * LX, "a [C][LX] array fits R2a and R2b");
   lds_barrier();  // every wave is past the dbeta pass and phase 4
   f32x4 dG[4];
 #pragma unroll
@@ -1274,7 +1357,13 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
       const int64_t o = ((pos.tok0 + r) * H + h) * D + c4;
       st4(dq + o, *(const f32x4*)&R0[r * LX + c4]);
       st4(dk + o, *(const f32x4*)&Q2[r * LX + c4]);
-      st4(dv + o, bv[j] * *(const f32x4*)&R1[r * LX + c4]);
+      const int po = r * LH + hl_pos(c4);  // Dv's four elements from its planes
+      const uint2 vh = *(const uint2*)(H1 + po), vl = *(const uint2*)(H1 + PLANE + po);
+      const f32x4 dvr = {__uint_as_float(vh.x << 16) + __uint_as_float(vl.x << 16),
+                         __uint_as_float(vh.x & 0xffff0000u) + __uint_as_float(vl.x & 0xffff0000u),
+                         __uint_as_float(vh.y << 16) + __uint_as_float(vl.y << 16),
+                         __uint_as_float(vh.y & 0xffff0000u) + __uint_as_float(vl.y & 0xffff0000u)};
+      st4(dv + o, bv[j] * dvr);
       if (gate == kGateChannel) st4(dg + o, *(const f32x4*)&R3[r * LX + c4]);
     }
   }
