@@ -31,11 +31,12 @@ k, v in MXFP8 (kda_chunk_forward_mx); ``backward_workload`` the backward pass
 at T = 65,536 with its default (windowed) workspace; ``cold`` the headline, packed
 and million-token workloads as the median of calls each preceded by a 1 GiB
 write that flushes L2 and the last-level cache; ``gpu_clock`` the graphics
-clock under load; ``roofline_fraction`` the larger of the call's HBM and
-MFMA fractions.  Other
-legs: ``--copy-calib MiB`` runs only a device copy of known size (for
-scaling the HBM byte counters), ``--only prefill|decode|backward`` runs one leg,
-``--no-cpu`` skips the oracle.
+clock under load; ``device_peaks`` the device's own measured peaks (dense
+bf16 and fp32 MFMA loops, an HBM read sweep, a device copy) beside the
+nominal ones; ``roofline_fraction`` the larger of the call's HBM and MFMA
+fractions.  Other legs: ``--copy-calib MiB`` runs only a device copy of known
+size (for scaling the HBM byte counters), ``--only
+prefill|decode|backward|peaks`` runs one leg, ``--no-cpu`` skips the oracle.
 """
 from __future__ import annotations
 
@@ -44,6 +45,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -148,7 +150,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="timed prefill calls")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000, help="timed decode steps")
-    ap.add_argument("--only", choices=("prefill", "decode", "backward", "both"), default="both")
+    ap.add_argument("--only", choices=("prefill", "decode", "backward", "peaks", "both"), default="both")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the packed and long-context workloads")
     ap.add_argument("--bwd-sequential", action="store_true",
@@ -319,6 +321,91 @@ def bench_cold(wid: int, reps: int, warm: int = 3):
     return {"workload": w.name, "reps": reps, "median_call_us": med * 1e6, "min_call_us": times[0] * 1e6,
             "max_call_us": times[-1] * 1e6, "value": T / med, "unit": "tokens/s", "hbm_frac": hbm,
             "mfma_frac": mfma, "roofline_fraction": max(hbm, mfma)}
+
+
+def device_peaks():
+    """The device's own peaks, measured beside the nominal ones the rooflines
+    use: dense bf16 and fp32 MFMA throughput (libkda_peaks.so: eight
+    independent accumulation chains per wave on register operands, four
+    workgroups of four waves per CU), HBM read bandwidth (a 4 GiB sum with
+    16-byte non-temporal loads), a 2 GiB device copy (bytes read + written),
+    and the sysfs graphics clock while an MFMA loop runs."""
+    import ctypes
+    import glob
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "gated_delta_rule_105_amd",
+                                   "libkda_peaks.so"))
+    lib.kda_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_peak_flop_per_mfma.restype = ctypes.c_longlong
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return statistics.median(ts)
+
+    def sclk():
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                for line in open(path):
+                    if "*" in line:
+                        return float(line.split(":", 1)[1].replace("*", "").strip().lower().replace("mhz", ""))
+            except (OSError, ValueError):
+                continue
+        return None
+
+    n_wg = 4 * n_cu
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    res = {"compute_units": n_cu}
+    for kind, name, iters in ((0, "bf16_mfma_tflops", 20000), (1, "fp32_mfma_tflops", 10000)):
+        def run(it=iters, k=kind):
+            st = lib.kda_peak_mfma(k, n_wg, it, ctypes.c_void_p(out.data_ptr()), sp)
+            if st != 0:
+                raise RuntimeError(f"kda_peak_mfma: HIP error {st}")
+        run(100)
+        torch.cuda.synchronize()
+        t = timed(run, 5)
+        flop = n_wg * 4 * iters * lib.kda_peak_chains() * lib.kda_peak_flop_per_mfma(kind)
+        res[name] = flop / t / 1e12
+    # the clock while a longer bf16 loop runs
+    lib.kda_peak_mfma(0, n_wg, 200000, ctypes.c_void_p(out.data_ptr()), sp)
+    time.sleep(0.01)
+    res["sysfs_sclk_mhz_under_mfma"] = sclk()
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB
+    src.fill_(1.0)
+    rn_wg = 8 * n_cu
+    rout = torch.empty(rn_wg * 256, dtype=torch.float32, device="cuda")
+
+    def read():
+        st = lib.kda_peak_read(ctypes.c_void_p(src.data_ptr()), src.numel() // 4, rn_wg, ctypes.c_void_p(rout.data_ptr()), sp)
+        if st != 0:
+            raise RuntimeError(f"kda_peak_read: HIP error {st}")
+    read()
+    res["hbm_read_gbs"] = src.numel() * 4 / timed(read, 5) / 1e9
+    del src
+    a = torch.empty(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    res["copy_gbs"] = 2 * a.numel() * 4 / timed(lambda: b.copy_(a), 5) / 1e9
+    del a, b, out, rout
+    torch.cuda.empty_cache()
+    res["nominal"] = {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "fp32_mfma_tflops": PEAK_F32_MFMA_TFLOPS,
+                      "hbm_gbs": PEAK_HBM_GBS, "sclk_mhz": 2400.0}
+    log("device peaks: " + ", ".join(f"{k} {v:.1f}" if isinstance(v, float) else f"{k} {v}"
+                                     for k, v in res.items() if k != "nominal"))
+    return res
 
 
 def gpu_clock():
@@ -797,6 +884,7 @@ def main() -> int:
         # the cold protocol: a median over calls each after a cache flush
         out["cold"] = [bench_cold(1, 20), bench_cold(2, 20), bench_cold(3, 5)]
         out["gpu_clock"] = gpu_clock()
+        out["device_peaks"] = device_peaks()
         out["states_workloads"] = bench_states(50)
         out["gate_workloads"] = bench_gates(50, 100)
         out["mx_workload"] = bench_mx(100)
@@ -804,6 +892,8 @@ def main() -> int:
         out["backward_long_workload"] = bench_backward_long(3)
     if args.only == "backward":
         out["backward_workload"] = bench_backward(args.steps, not args.no_cpu, not args.bwd_sequential)
+    if args.only == "peaks":
+        out["device_peaks"] = device_peaks()
     if args.only in ("decode", "both"):
         dd = bench_decode(args.decode_steps, max(1, args.warmup))
         gbs = dd["bytes_step"] / dd["mean_step"] / 1e9

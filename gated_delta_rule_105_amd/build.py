@@ -1,7 +1,9 @@
 """Build the HIP library ``libkda.so`` in-tree for gfx950.
 
-``python -m gated_delta_rule_105_amd.build`` compiles every source under
-``csrc/`` with hipcc into ``gated_delta_rule_105_amd/libkda.so``.
+``python -m gated_delta_rule_105_amd.build`` compiles the KDA sources under
+``csrc/`` with hipcc into ``gated_delta_rule_105_amd/libkda.so``, and the
+device-peak microbenchmarks (``csrc/kda_peaks.hip``, a measurement aid for
+bench.py) into ``libkda_peaks.so``.
 """
 from __future__ import annotations
 
@@ -16,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_backward.hip"]
+PEAKS_SOURCES = ["kda_peaks.hip"]
+PEAKS_LIBRARY = os.path.join(HERE, "libkda_peaks.so")
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -37,8 +41,14 @@ def flags() -> list:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIBRARY + ".tmp"
+    _compile(SOURCES, LIBRARY, verbose)
+    _compile(PEAKS_SOURCES, PEAKS_LIBRARY, verbose)
+    return LIBRARY
+
+
+def _compile(sources, library: str, verbose: bool) -> None:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = library + ".tmp"
     cmd = [hipcc(), *flags(), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,8 +60,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, library)
 
 
 if __name__ == "__main__":
