@@ -651,27 +651,40 @@ __device__ __forceinline__ f32x4 mma_panels(f32x4 acc, const f32x4 (&a)[NK], con
 // Every record operand of the next chunk (the step's k-panels and the gamma
 // of the wave's own rows) is loaded while the current chunk is computed, so
 // the chain of chunks waits on memory once, not once per step.  For that
-// every wave issues the same loads on every step (61 at d = 128: below the 63
-// that the hardware counts, so that waiting for the current operands never
-// means waiting for the next ones).  Workgroups are ordered so that the column
+// every wave issues the same loads on every step (46 at d = 128 on waves 0-3,
+// which also load the dO columns for all, 45 on the others: below the 63 that
+// the hardware counts, so that waiting for the current operands never means
+// waiting for the next ones).  Workgroups are ordered so that the column
 // blocks of one (sequence, head) pair have the same block index mod 8, i.e.
 // share one XCD's L2 (the record operands are common to them).
 template <int D> struct StateOps {
   static constexpr int NKC = C / 16, NKH = D / 32, NKP = C / 32;
-  f32x4 aP[NKP], aKh[NKH], bO[NKC], aQ[NKC], aW[NKC];
-  f32x4 gr;  // gamma of rows 16 w + 4 g + e (this wave's dH tile)
+  f32x4 aP[NKP], aKh[NKH], aQ[NKC], aW[NKC];
+  f32x4 bOr;  // waves 0-3: dO[tid / 4][j0 + 4 (tid % 4) ..], shared through LDS
+  f32x4 gr;   // gamma of rows 16 w + 4 g + e (this wave's dH tile)
   // gamma first: a step needs the next chunk's gamma before its other operands
   // (loads complete in issue order).  Waves past D / 16 (d = 64) load a
-  // copy of another wave's dH operands and do not use them.
+  // copy of another wave's dH operands and do not use them.  The dO columns
+  // every wave needs whole are loaded once, a 16-byte row piece per thread
+  // of waves 0-3 (put): sixteen fewer load instructions per wave and step
+  // on an address unit that sets the step time.
   __device__ void load(const float* Rp, int j0, int wave, int lane) {
     typedef Rec<D> R;
-    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16);
+    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16), tid = 64 * wave + lane;
     gr = *(const f32x4*)(Rp + R::GAM + 16 * w + 4 * (lane >> 4));
-    load_panel(bO, Rp + R::DO + j0, 1, D, lane);                               // B(k = r, j) = dO[r][j0 + j]
+    if (wave < 4) bOr = *(const f32x4*)(Rp + R::DO + (tid >> 2) * D + j0 + 4 * (tid & 3));
     load_panel(aKh, Rp + R::KH + 16 * t * D + half * (D / 2), D, 1, lane);      // Kh rows 16 t.., k in this half
     load_panel(aP, Rp + R::PM + half * (C / 2) * C + 16 * t, 1, C, lane);       // P^T rows 16 t.., k in this half
     load_panel(aQ, Rp + R::QT + 16 * w, 1, D, lane);                            // Qt^T rows 16 w..
     load_panel(aW, Rp + R::WK + 16 * w, 1, D, lane);                            // Wk^T rows 16 w..
+  }
+  // waves 0-3: the loaded dO piece into the fragment image o[kk][lane][e] =
+  // B(k = 16 kk + 4 g + e, j = i) = dO[16 kk + 4 g + e][j0 + i] (lane 16 g + i)
+  __device__ void put(float (*o)[64][4], int wave, int lane) const {
+    if (wave >= 4) return;
+    const int tid = 64 * wave + lane, r = tid >> 2, c0 = 4 * (tid & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[r >> 4][16 * ((r & 15) >> 2) + c0 + j][r & 3] = bOr[j];
   }
 };
 
@@ -685,6 +698,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   constexpr int NCB = D / 16, NKC = C / 16, NKH = D / 32;
   __shared__ __align__(16) float G[D][16];
   __shared__ __align__(16) float dU[2][C][16];
+  __shared__ __align__(16) float bOs[2][C / 16][64][4];  // dO fragment images, by step parity
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const int cb = (b / 8) % NCB, pair = 8 * (b / (8 * NCB)) + b % 8;
@@ -740,8 +754,12 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
     // that step's four dH stores in flight, so that no later wait for cur can
     // take the loads issued next with it
     __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4) expcnt(7) lgkmcnt(15)
+    // this chunk's dO fragments to LDS (the buffer of this step's parity: the
+    // other one may still be read by a wave finishing the previous step)
+    float(*const bo)[64][4] = bOs[m & 1];
+    cur.put(bo, wave, lane);
     nxt.load(rec_of(m > m_lo ? m - 1 : m), j0, wave, lane);  // (the last step loads a chunk it does not use)
-    lds_barrier();  // G ready
+    lds_barrier();  // G and the dO fragments ready
     // dU: this wave's halves of P^T dO and Kh G
     {
       f32x4 bG[NKH], bOh[StateOps<D>::NKP];
@@ -750,7 +768,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 #pragma unroll
         for (int e = 0; e < 4; ++e) bG[kk][e] = G[koff + 16 * kk + 4 * g + e][ii];
 #pragma unroll
-      for (int kk = 0; kk < StateOps<D>::NKP; ++kk) bOh[kk] = half ? cur.bO[StateOps<D>::NKP + kk] : cur.bO[kk];
+      for (int kk = 0; kk < StateOps<D>::NKP; ++kk) bOh[kk] = *(const f32x4*)bo[half * StateOps<D>::NKP + kk][lane];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mma_panels(acc, cur.aP, bOh);
       acc = mma_panels(acc, cur.aKh, bG);
@@ -768,7 +786,10 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
           bU[kk][e] = dU[0][r][ii] + dU[1][r][ii];
         }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f}, neg = {0.f, 0.f, 0.f, 0.f};
-      acc = mma_panels(acc, cur.aQ, cur.bO);
+      f32x4 bO[NKC];
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) bO[kk] = *(const f32x4*)bo[kk][lane];
+      acc = mma_panels(acc, cur.aQ, bO);
       neg = mma_panels(neg, cur.aW, bU);
       // chunk m - 1's end-state gradient: to the carry when that chunk is in
       // the earlier window
