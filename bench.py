@@ -328,10 +328,9 @@ def device_peaks():
     use: dense bf16 and fp32 MFMA throughput (libkda_peaks.so: eight
     independent accumulation chains per wave on register operands, four
     workgroups of four waves per CU), HBM read bandwidth (a 4 GiB sum with
-    16-byte non-temporal loads), a 2 GiB device copy (bytes read + written),
-    and the sysfs graphics clock while an MFMA loop runs."""
+    16-byte non-temporal loads) and a 2 GiB device copy (bytes read +
+    written)."""
     import ctypes
-    import glob
     import torch
 
     lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "gated_delta_rule_105_amd",
@@ -354,16 +353,6 @@ def device_peaks():
             ts.append(a.elapsed_time(b) * 1e-3)
         return statistics.median(ts)
 
-    def sclk():
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-            try:
-                for line in open(path):
-                    if "*" in line:
-                        return float(line.split(":", 1)[1].replace("*", "").strip().lower().replace("mhz", ""))
-            except (OSError, ValueError):
-                continue
-        return None
-
     n_wg = 4 * n_cu
     out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
     res = {"compute_units": n_cu}
@@ -377,11 +366,6 @@ def device_peaks():
         t = timed(run, 5)
         flop = n_wg * 4 * iters * lib.kda_peak_chains() * lib.kda_peak_flop_per_mfma(kind)
         res[name] = flop / t / 1e12
-    # the clock while a longer bf16 loop runs
-    lib.kda_peak_mfma(0, n_wg, 200000, ctypes.c_void_p(out.data_ptr()), sp)
-    time.sleep(0.01)
-    res["sysfs_sclk_mhz_under_mfma"] = sclk()
-    torch.cuda.synchronize()
     src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB
     src.fill_(1.0)
     rn_wg = 8 * n_cu

@@ -28,9 +28,11 @@ __global__ void __launch_bounds__(256) peak_bf16(float* __restrict__ out, int it
     a[e] = (__bf16)(t + 0.25f * e);
     b[e] = (__bf16)(0.5f - t + 0.125f * e);
   }
+  // distinct starting values: identical chains would let the compiler merge
+  // them, and it then shifted their accumulators against one another
   f32x4 acc[kChains];
 #pragma unroll
-  for (int j = 0; j < kChains; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kChains; ++j) acc[j] = (f32x4){t + j, t - j, 2.f * t + j, (float)j};
   for (int it = 0; it < iters; ++it)
 #pragma unroll
     for (int j = 0; j < kChains; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
@@ -44,7 +46,7 @@ __global__ void __launch_bounds__(256) peak_f32(float* __restrict__ out, int ite
   const float a = (float)(threadIdx.x & 63) * 1e-3f, b = 0.5f - a;
   f32x4 acc[kChains];
 #pragma unroll
-  for (int j = 0; j < kChains; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kChains; ++j) acc[j] = (f32x4){a + j, a - j, 2.f * a + j, (float)j};
   for (int it = 0; it < iters; ++it)
 #pragma unroll
     for (int j = 0; j < kChains; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
