@@ -830,9 +830,10 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
   typedef Rec<D> R;
   typedef Scr<D> W;
   // fp32 MFMA on both paths here: with hi/lo bf16 products this kernel ran
-  // slower (550 against 491 us at T = 4096, H = 16), since its time goes to
-  // the scratch round trips between products, not to the matrix cores, and
-  // the splits cost registers (a 48-byte spill) and VALU work
+  // slower (measured when it also served D = 128: 550 against 491 us at
+  // T = 4096, H = 16), since its time goes to the scratch round trips
+  // between products, not to the matrix cores, and the splits cost
+  // registers (a 48-byte spill) and VALU work
   constexpr bool HL = false;
   __shared__ ChunkPos pos;
   // the products' slices, and later the per-element dGamma of the chunk

@@ -295,11 +295,11 @@ int kda_chunk_forward_states(const kda_chunk_desc_ex_t* d,
  * The workspace (256-byte aligned) holds the replay's state after every
  * chunk (64 KiB per (chunk of 64 tokens, head) at d = 128) and, for the
  * chunks in flight, fp32 records and state gradients (about 0.36 MiB per
- * (chunk, head) at d = 128; at d = 64 also a scratch area).  Chunks are processed in windows
- * of W chunk indices of every sequence, from the last window to the first;
- * the call takes the widest window that fits workspace_bytes (one window
- * for the whole sequence when everything fits), and the results do not
- * depend on it.  kda_chunk_backward_workspace_size gives the default: one
+ * (chunk, head) at d = 128; at d = 64 also a scratch area).  Chunks are
+ * processed in windows of W chunk indices of every sequence, from the last
+ * window to the first; the call takes the widest window that fits
+ * workspace_bytes (one window for the whole sequence when everything fits),
+ * and the results do not depend on it.  kda_chunk_backward_workspace_size gives the default: one
  * window unless the in-flight areas of the whole call would pass 8192
  * (chunk, head) pairs, else windows of max(64, 8192 / (H rows)) chunks.
  * A workspace too small for windows of one chunk is
