@@ -33,7 +33,9 @@
 // Launches (after a forward replay that keeps the state at every full chunk
 // boundary):
 //   kda_bwd_chunk : one workgroup per (chunk, head): the chunk record (the
-//                   quantities above that do not involve the state), fp32.
+//                   quantities above that do not involve the state), fp32
+//                   (kda_bwd_chunk_fused at D = 128, which leaves v, dO and
+//                   Gamma to be read from the inputs by the later passes).
 //   kda_bwd_state : one workgroup per (sequence, head, 16 state columns):
 //                   dS walked backward over the chunks (column j of dS only
 //                   needs column j of dH and dO), writing every chunk's dH;
@@ -42,7 +44,7 @@
 //                   (kda_bwd_local_fused at D = 128, with every intermediate
 //                   on chip; through a scratch area at D = 64).
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4f32), except, on the bf16
-// path, the record pass's and most of kda_bwd_local_fused's, which take hi/lo
+// path, kda_bwd_chunk's and most of kda_bwd_local_fused's, which take hi/lo
 // bf16 MFMA (see gemm and kda_bwd_local_fused).  In the
 // per-chunk kernels the operands pass through LDS in k-slices (each element
 // read once per product); the state-gradient pass keeps its operands in
@@ -70,6 +72,14 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ float ldx(const float* p) { return *p; }
 __device__ __forceinline__ float ldx(const bf16_t* p) { return bf16_to_f32(*p); }
+// four bf16 (first in the low half of u.x) to fp32
+__device__ __forceinline__ f32x4 bf4_to_f32(const uint2& u) {
+  return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+// four consecutive elements (p 8-byte aligned for bf16, 16-byte for fp32)
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const bf16_t* p) { return bf4_to_f32(*(const uint2*)p); }
 __device__ __forceinline__ void stx(float* p, float x) { *p = x; }
 __device__ __forceinline__ void stx(bf16_t* p, float x) { *p = f32_to_bf16(x); }
 // four consecutive elements (p 8-byte aligned for bf16, 16-byte for fp32)
@@ -325,10 +335,19 @@ __device__ void gemm(float* lds, float* out, int ldo, float alpha, bool acc_in, 
 // dO, Wk, Wv, Gamma ([C][D] each, rows past the chunk's end zero; Gamma
 // there repeats the last row), P, T, Abar ([C][C]), gamma [D], beta [C] (0
 // past the end).
-template <int D> struct Rec {
-  static constexpr int QT = 0, KT = C * D, KH = 2 * C * D, VV = 3 * C * D, DO = 4 * C * D, WK = 5 * C * D,
-                       WV = 6 * C * D, GM = 7 * C * D, PM = 8 * C * D, TM = PM + C * C, AB = TM + C * C,
-                       GAM = AB + C * C, BET = GAM + D, FLOATS = BET + C;
+template <int D> struct RecBase {
+  static constexpr int QT = 0, KT = C * D, KH = 2 * C * D, WK = 3 * C * D, WV = 4 * C * D, PM = 5 * C * D,
+                       TM = PM + C * C, AB = TM + C * C, GAM = AB + C * C, BET = GAM + D, END = BET + C;
+};
+// At D = 64 the record also holds copies of v and dO and Gamma for the
+// products of kda_bwd_local.  At D = 128 it does not: the record pass is
+// bound by its writes, and the walk and kda_bwd_local_fused read v and dO
+// from the inputs and sum Gamma from the gate themselves.
+template <int D> struct Rec : RecBase<D> {
+  static constexpr int VV = RecBase<D>::END, DO = VV + C * D, GM = DO + C * D, FLOATS = GM + C * D;
+};
+template <> struct Rec<128> : RecBase<128> {
+  static constexpr int FLOATS = END;
 };
 // How the per-chunk kernels split the rows of a chunk for the prefix sums
 // over rows: NG groups of RG rows, one thread per (group, channel).
@@ -609,6 +628,199 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk(const T* __restrict__ 
        nullptr, nullptr, 0);
 }
 
+// fp32 operand fragment of a 16 x 16 x 4 product taken down a column:
+// X[k0 + 4 g + e][c] in issue e (frag_rows takes it along a row).
+__device__ __forceinline__ f32x4 frag_cols(const float* X, int ld, int c, int k0, int g) {
+  const float* p = X + (k0 + 4 * g) * ld + c;
+  return (f32x4){p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+// the lower-triangular 16 x 16 tiles (a, b), b <= a, of a 64 x 64 matrix
+__device__ __forceinline__ void low_tile(int t, int& a, int& b) {
+  a = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+  b = t - a * (a + 1) / 2;
+}
+
+// Chunk record at D = 128 in one pass with the operands on chip: q, k, v
+// and the gate are read once, Qt, Kt and Kh built in LDS, and the Gram
+// blocks, the inverse, Wk and Wv computed from there, on fp32 MFMA.  The
+// pass is bound by its writes, so the record gets only what the later passes
+// cannot take from the inputs (no copies of v and dO, no Gamma).  LDS: three
+// [64][D + 4] fp32 arrays (Qt, Kt, Kh; the first one holds diag(beta) V once
+// the Gram products are done) and [64][65] diag(beta) Abar, T and P.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) kda_bwd_chunk_fused(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ v, const void* __restrict__ g,
+                                                           const float* __restrict__ beta,
+                                                           const T* __restrict__ /* dout: not copied */,
+                                                           const int32_t* __restrict__ cu,
+                                                           const int64_t* __restrict__ seqs, int n_rows, int T_per,
+                                                           int H, float g_floor, int gate, float* __restrict__ rec,
+                                                           float* __restrict__ zero_state, Win win) {
+  typedef Rec<D> R;
+  typedef RowSplit<D> RS;
+  constexpr int LX = D + 4, AX = C * LX;
+  __shared__ ChunkPos pos;
+  __shared__ __align__(16) float lds[3 * AX];
+  __shared__ float As[C][C + 1], Ts[C][C + 1], Ps[C][C + 1];
+  __shared__ float gsum[RS::NG][D];
+  __shared__ float sb[C];
+  float* const LQ = lds;
+  float* const LK = lds + AX;
+  float* const LH = lds + 2 * AX;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, i = lane & 15;
+  const int h = blockIdx.y;
+  const int64_t slot = blockIdx.x;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  if (slot == 0 && h == 0 && win.lo == 0)
+    for (int x = tid; x < D * D; x += blockDim.x) zero_state[x] = 0.f;
+  if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;
+  float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
+  const bool bf = sizeof(T) == 2;
+  const int len = pos.len;
+  // element-wise, thread (group, channel c) over rows r0 .. r0 + RG - 1.
+  // Gamma: each group takes its own prefix sums of the floored log-decays,
+  // then adds the totals of the groups before it (kda_bwd_local_fused sums
+  // them in the same order).
+  const int c = tid % D, grp = tid / D, r0 = grp * RS::RG;
+  float gl[RS::RG], vr[RS::RG];
+  {
+    float qr[RS::RG], kr[RS::RG];
+    if (tid < C) sb[tid] = tid < len ? beta[(pos.tok0 + tid) * H + h] : 0.f;
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < RS::RG; ++j) {
+      const int r = r0 + j;
+      qr[j] = kr[j] = vr[j] = 0.f;
+      if (r < len) {
+        const int64_t th = ((pos.tok0 + r) * H + h) * D + c;
+        run += fmaxf(gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c), g_floor);
+        qr[j] = ldx(q + th);
+        kr[j] = ldx(k + th);
+        vr[j] = ldx(v + th);
+      }
+      gl[j] = run;
+    }
+    gsum[grp][c] = run;
+    for (int x = tid; x < C * C; x += kThreads) {
+      const int r = x / C, s2 = x % C;
+      Ts[r][s2] = r == s2 ? 1.f : 0.f;
+    }
+    __syncthreads();
+    float off = 0.f;
+    for (int j = 0; j < grp; ++j) off += gsum[j][c];
+#pragma unroll
+    for (int j = 0; j < RS::RG; ++j) {
+      const int r = r0 + j;
+      const float G = off + gl[j];
+      const float e = __expf(G), ei = __expf(-G);
+      LQ[r * LX + c] = qr[j] * e;
+      LK[r * LX + c] = kr[j] * e;
+      LH[r * LX + c] = kr[j] * ei;
+      if (r == C - 1) Rp[R::GAM + c] = e;
+    }
+  }
+  if (tid < C) Rp[R::BET + tid] = sb[tid];
+  __syncthreads();
+  // Abar = strict_lower(Kt Kh^T), P = lower_incl(Qt Kh^T): the 10 tiles of
+  // the lower triangle of each, one wave per tile
+  for (int t = w; t < 20; t += kThreads / 64) {
+    const bool isP = t < 10;
+    int ta, tb;
+    low_tile(isP ? t : t - 10, ta, tb);
+    const float* XA = isP ? LQ : LK;
+    f32x4 acc = z4;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+      acc = mma(frag_rows(XA, LX, 16 * ta + i, 16 * kb, gq), frag_rows(LH, LX, 16 * tb + i, 16 * kb, gq), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ta + 4 * gq + e, s2 = 16 * tb + i;
+      if (isP) {
+        Ps[r][s2] = (ta > tb || 4 * gq + e >= i) ? acc[e] : 0.f;
+      } else {
+        const float a = (ta > tb || 4 * gq + e > i) ? acc[e] : 0.f;
+        Rp[R::AB + r * C + s2] = a;
+        As[r][s2] = sb[r] * a;
+      }
+    }
+  }
+  __syncthreads();
+  // Qt, Kt, Kh out as rows; P and the upper tiles of Abar (zero)
+  for (int x = tid; x < C * D / 4; x += kThreads) {
+    const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
+    *(f32x4*)&Rp[R::QT + r * D + c4] = *(const f32x4*)&LQ[r * LX + c4];
+    *(f32x4*)&Rp[R::KT + r * D + c4] = *(const f32x4*)&LK[r * LX + c4];
+    *(f32x4*)&Rp[R::KH + r * D + c4] = *(const f32x4*)&LH[r * LX + c4];
+  }
+  for (int x = tid; x < C * C; x += kThreads) {
+    const int r = x / C, s2 = x % C;
+    const bool up = (s2 >> 4) > (r >> 4);
+    Rp[R::PM + x] = up ? 0.f : Ps[r][s2];
+    if (up) Rp[R::AB + x] = 0.f;
+  }
+  // T = (I + A)^{-1} (A = diag(beta) Abar strictly lower) over 4 x 4 blocks
+  // of 16, as in kda_bwd_chunk: diagonal blocks by forward substitution, one
+  // lane per column, then the blocks below them one block row at a time
+  if (tid < C) {
+    const int s2 = tid, end = (s2 | 15) + 1;
+    for (int r = s2 + 1; r < end; ++r) {
+      float acc = 0.f;
+      for (int m = s2; m < r; ++m) acc += As[r][m] * Ts[m][s2];
+      Ts[r][s2] = -acc;
+    }
+  }
+  __syncthreads();
+  // diag(beta) V over Qt (every thread is past the row stores)
+#pragma unroll
+  for (int j = 0; j < RS::RG; ++j) LQ[(r0 + j) * LX + c] = sb[r0 + j] * vr[j];
+  for (int bi = 1; bi < C / 16; ++bi) {
+    if (w < bi) {
+      const int bj = w;
+      f32x4 x = z4;
+      for (int bm = bj; bm < bi; ++bm)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = 16 * bm + 4 * gq + e;
+          x = __builtin_amdgcn_mfma_f32_16x16x4f32(As[16 * bi + i][kk], Ts[kk][16 * bj + i], x, 0, 0, 0);
+        }
+      f32x4 y = z4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(Ts[16 * bi + i][16 * bi + 4 * gq + e], x[e], y, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ts[16 * bi + 4 * gq + e][16 * bj + i] = -y[e];
+    }
+    __syncthreads();
+  }
+  for (int x = tid; x < C * C; x += kThreads) Rp[R::TM + x] = Ts[x / C][x % C];
+  // Wk = T diag(beta) Kt, Wv = T diag(beta) V: wave w takes columns 16 w ..
+  // 16 w + 15 of both, every row tile (T is lower triangular: row tile rt
+  // needs k-blocks kb <= rt only)
+  const int cw = 16 * w;
+  f32x4 wk[4] = {z4, z4, z4, z4}, wv[4] = {z4, z4, z4, z4};
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb) {
+    const int k0 = 16 * kb + 4 * gq;
+    const f32x4 bk = frag_cols(LK, LX, cw + i, 16 * kb, gq) * (f32x4){sb[k0], sb[k0 + 1], sb[k0 + 2], sb[k0 + 3]};
+    const f32x4 bv = frag_cols(LQ, LX, cw + i, 16 * kb, gq);
+#pragma unroll
+    for (int rt = kb; rt < 4; ++rt) {
+      const int r = 16 * rt + i;
+      const f32x4 a = {Ts[r][k0], Ts[r][k0 + 1], Ts[r][k0 + 2], Ts[r][k0 + 3]};
+      wk[rt] = mma(a, bk, wk[rt]);
+      wv[rt] = mma(a, bv, wv[rt]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = (16 * rt + 4 * gq + e) * D + cw + i;
+      Rp[R::WK + x] = wk[rt][e];
+      Rp[R::WV + x] = wv[rt][e];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Reverse pass over the chunks of one sequence for 16 columns of dS.
 //
@@ -665,14 +877,15 @@ template <int D> struct StateOps {
   // gamma first: a step needs the next chunk's gamma before its other operands
   // (loads complete in issue order).  Waves past D / 16 (d = 64) load a
   // copy of another wave's dH operands and do not use them.  The dO columns
-  // every wave needs whole are loaded once, a 16-byte row piece per thread
-  // of waves 0-3 (put): sixteen fewer load instructions per wave and step
-  // on an address unit that sets the step time.
-  __device__ void load(const float* Rp, int j0, int wave, int lane) {
+  // every wave needs whole are loaded once, from the input, a row piece of
+  // four elements per thread of waves 0-3 (put; `dp` null past the end of
+  // the sequence): sixteen fewer load instructions per wave and step on an
+  // address unit that sets the step time.
+  template <typename T> __device__ void load(const float* Rp, const T* dp, int wave, int lane) {
     typedef Rec<D> R;
-    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16), tid = 64 * wave + lane;
+    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16);
     gr = *(const f32x4*)(Rp + R::GAM + 16 * w + 4 * (lane >> 4));
-    if (wave < 4) bOr = *(const f32x4*)(Rp + R::DO + (tid >> 2) * D + j0 + 4 * (tid & 3));
+    if (wave < 4) bOr = dp ? ld4(dp) : (f32x4){0.f, 0.f, 0.f, 0.f};
     load_panel(aKh, Rp + R::KH + 16 * t * D + half * (D / 2), D, 1, lane);      // Kh rows 16 t.., k in this half
     load_panel(aP, Rp + R::PM + half * (C / 2) * C + 16 * t, 1, C, lane);       // P^T rows 16 t.., k in this half
     load_panel(aQ, Rp + R::QT + 16 * w, 1, D, lane);                            // Qt^T rows 16 w..
@@ -688,8 +901,9 @@ template <int D> struct StateOps {
   }
 };
 
-template <int D>
-__global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ rec, const float* __restrict__ dht,
+template <typename T, int D>
+__global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ rec, const T* __restrict__ dout,
+                                                     const float* __restrict__ dht,
                                                      const int32_t* __restrict__ cu, const int64_t* __restrict__ seqs,
                                                      int n_rows, int T_per, int H, int64_t m_lo, int64_t m_hi,
                                                      Win win, float* __restrict__ dHs, float* __restrict__ dh0,
@@ -705,17 +919,27 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   const int n = pair / H, h = pair % H;
   if (n >= n_rows) return;
   const int j0 = cb * 16, ii = lane & 15, g = lane >> 4;
-  int64_t base = 0, nc;
+  int64_t base = 0, nc, tok_n, len_n;  // first area slot, chunks; first token, tokens
   if (cu) {
     base = seqs[n];
-    nc = ((int64_t)cu[n + 1] - cu[n] + C - 1) / C;
+    tok_n = cu[n];
+    len_n = (int64_t)cu[n + 1] - cu[n];
+    nc = (len_n + C - 1) / C;
   } else {
     nc = (T_per + C - 1) / C;
     base = (int64_t)n * nc;
+    tok_n = (int64_t)n * T_per;
+    len_n = T_per;
   }
   const int64_t sd = ((int64_t)n * H + h) * D * D;
   auto rec_of = [&](int64_t m) { return rec + (area_slot(win, n, base, m) * H + h) * (int64_t)R::FLOATS; };
   auto dhs_of = [&](int64_t m) { return dHs + (area_slot(win, n, base, m) * H + h) * (int64_t)D * D; };
+  // this thread's piece of chunk m's dO (waves 0-3: row tid / 4, columns
+  // j0 + 4 (tid % 4) ..), null for the rows past the sequence's end
+  auto do_of = [&](int64_t m) -> const T* {
+    const int64_t r = (int64_t)C * m + (tid >> 2);
+    return wave < 4 && r < len_n ? dout + ((tok_n + r) * H + h) * D + j0 + 4 * (tid & 3) : nullptr;
+  };
   if (nc == 0) {  // no tokens: the gradient passes through unchanged
     if (dh0 && m_lo == 0)
       for (int x = tid; x < D * 16; x += blockDim.x) {
@@ -758,7 +982,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
     // other one may still be read by a wave finishing the previous step)
     float(*const bo)[64][4] = bOs[m & 1];
     cur.put(bo, wave, lane);
-    nxt.load(rec_of(m > m_lo ? m - 1 : m), j0, wave, lane);  // (the last step loads a chunk it does not use)
+    const int64_t mn = m > m_lo ? m - 1 : m;  // (the last step loads a chunk it does not use)
+    nxt.load(rec_of(mn), do_of(mn), wave, lane);
     lds_barrier();  // G and the dO fragments ready
     // dU: this wave's halves of P^T dO and Kh G
     {
@@ -807,7 +1032,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       }
     }
   };
-  opsA.load(rec_of(top - 1), j0, wave, lane);
+  opsA.load(rec_of(top - 1), do_of(top - 1), wave, lane);
   for (int64_t m = top - 1; m >= m_lo; m -= 2) {
     step(opsA, opsB, m);
     if (m == m_lo) break;
@@ -821,7 +1046,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 // takes area slot a0 + x.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) kda_bwd_local(
-    const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ /* v: its copy in the record */,
+    const T* __restrict__ /* dout: its copy in the record */, const void* __restrict__ g, const int32_t* __restrict__ cu,
     const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
@@ -1005,12 +1231,6 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
 // Wk, Kh, dO, U, Dv and Dk kept in LDS as hi and lo planes; those with the
 // [64][64] matrices P, T, dP and dA, read down columns, stay on fp32 MFMA,
 // each on its own accumulator (no accumulation chain mixes MFMA shapes).
-// fp32 operand fragment of a 16 x 16 x 4 product taken down a column:
-// X[k0 + 4 g + e][c] in issue e (frag_rows takes it along a row).
-__device__ __forceinline__ f32x4 frag_cols(const float* X, int ld, int c, int k0, int g) {
-  const float* p = X + (k0 + 4 * g) * ld + c;
-  return (f32x4){p[0], p[ld], p[2 * ld], p[3 * ld]};
-}
 // hi/lo bf16 operands of the 16 x 16 x 32 products on the bf16 path: x ~ hi
 // + lo to about 2^-16, a 32-wide k-block as A_hi B_hi + A_hi B_lo + A_lo
 // B_hi (three bf16 MFMAs against eight fp32 16 x 16 x 4 for the same k).
@@ -1059,6 +1279,11 @@ __device__ __forceinline__ float hl_get(const bf16_t* P, int r, int k) {
   const int o = r * LH + hl_pos(k);
   return bf16_to_f32(P[o]) + bf16_to_f32(P[PLANE + o]);
 }
+// four consecutive k (k % 4 == 0, contiguous in each plane) of row r
+__device__ __forceinline__ f32x4 hl_get4(const bf16_t* P, int r, int k) {
+  const int o = r * LH + hl_pos(k);
+  return bf4_to_f32(*(const uint2*)(P + o)) + bf4_to_f32(*(const uint2*)(P + PLANE + o));
+}
 // four consecutive k (k % 4 == 0) of row r
 __device__ __forceinline__ void hl_put4(bf16_t* P, int r, int k, const f32x4& x) {
   uint2 hi, lo;
@@ -1067,15 +1292,11 @@ __device__ __forceinline__ void hl_put4(bf16_t* P, int r, int k, const f32x4& x)
   *(uint2*)(P + o) = hi;
   *(uint2*)(P + PLANE + o) = lo;
 }
-// the lower-triangular 16 x 16 tiles (a, b), b <= a, of a 64 x 64 matrix
-__device__ __forceinline__ void low_tile(int t, int& a, int& b) {
-  a = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-  b = t - a * (a + 1) / 2;
-}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
-    const T* __restrict__ q, const T* __restrict__ k, const void* __restrict__ g, const int32_t* __restrict__ cu,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    const void* __restrict__ g, const int32_t* __restrict__ cu,
     const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
     const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
@@ -1084,6 +1305,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   static_assert(D == 16 * (kThreads / 64), "one 16-column tile per wave");
   typedef Rec<D> R;
   static_assert(D == 128, "hi/lo planes of 128 columns");
+  static_assert(sizeof(T) == 2, "the bf16 path: dO's hi/lo planes hold it exactly");
   // R0, R1, R3: hi/lo planes of [64][128] operands (2 PLANE bf16 each);
   // R2a, R2b: fp32 [64][64] with rows of 4 extra floats (16-byte aligned,
   // and the 16-byte reads of 8 consecutive rows fall on distinct banks).
@@ -1125,11 +1347,13 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     fs[kb] = frag_cols(S, D, cw + i, 16 * kb, gq);
     fg[kb] = frag_cols(dH, D, cw + i, 16 * kb, gq) * *(const f32x4*)(gam + 16 * kb + 4 * gq);
   }
+  // this head's row r of an input (r < len)
+  auto in_row = [&](const T* x, int r) { return x + ((pos.tok0 + r) * H + h) * D; };
   for (int x = tid; x < C * D / 4; x += kThreads) {
     const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
     hl_put4(H0, r, c4, *(const f32x4*)&Rp[R::WK + r * D + c4]);
     hl_put4(H1, r, c4, *(const f32x4*)&Rp[R::KH + r * D + c4]);
-    hl_put4(H3, r, c4, *(const f32x4*)&Rp[R::DO + r * D + c4]);
+    hl_put4(H3, r, c4, r < len ? ld4(in_row(dout, r) + c4) : z4);
   }
   for (int x = tid; x < C * C / 4; x += kThreads) {
     const int r = x / (C / 4), c4 = 4 * (x % (C / 4));
@@ -1153,7 +1377,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     }
 #pragma unroll
     for (int kb = 0; kb < C / 16; ++kb) {
-      const f32x4 fo = frag_cols(Rp + R::DO, D, cw + i, 16 * kb, gq);  // dO[token][value]
+      f32x4 fo;  // dO[token][value], from its planes (a bf16 value is hi + 0 there: exact)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fo[e] = hl_get(H3, 16 * kb + 4 * gq + e, cw + i);
 #pragma unroll
       for (int rt = 0; rt <= kb; ++rt) bp[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fo, bp[rt]);  // P^T
     }
@@ -1273,9 +1499,15 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // for them.
   {
     const int r = tid / 8, part = tid % 8;
-    float acc = 0.f;
-    for (int c2 = part; c2 < D; c2 += 8)
-      acc += hl_get(H0, r, c2) * Rp[R::KT + r * D + c2] + hl_get(H1, r, c2) * Rp[R::VV + r * D + c2];
+    const T* vr = in_row(v, r < len ? r : 0);
+    f32x4 a4 = z4;  // columns 16 part .. 16 part + 15, four at a time
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c4 = 16 * part + 4 * j;
+      const f32x4 vv = r < len ? ld4(vr + c4) : z4;
+      a4 += hl_get4(H0, r, c4) * *(const f32x4*)&Rp[R::KT + r * D + c4] + hl_get4(H1, r, c4) * vv;
+    }
+    float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
     for (int s2 = part; s2 < r; s2 += 8) acc += R2b[r * LC + s2] * Rp[R::AB + r * C + s2];
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
@@ -1307,8 +1539,11 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   const bool bf = sizeof(T) == 2;
   const int c = cw + i;
   // Qt, Kt and Kh at this lane's elements are fq, fkt and fk (row 16 rt +
-  // 4 gq + e is element e of fragment rt); Gamma, and which rows pass the
-  // floor (bit 4 rt + e), are loaded here, before any store
+  // 4 gq + e is element e of fragment rt).  The log-decays are loaded here,
+  // before any store: which rows pass the floor (bit 4 rt + e), and Gamma,
+  // summed in the order of the record pass (so the two agree to the bit):
+  // within each 16-row tile the rows in order, a running sum handed from
+  // lane group gq to gq + 1, then the tiles' totals in order
   f32x4 gm[4];
   uint32_t keep = 0;
 #pragma unroll
@@ -1316,9 +1551,43 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rt + 4 * gq + e;
-      gm[rt][e] = Rp[R::GM + r * D + c];
-      if (r < len && gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c) >= g_floor) keep |= 1u << (4 * rt + e);
+      float x = 0.f;
+      if (r < len) {
+        const float gv = gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c);
+        x = fmaxf(gv, g_floor);
+        if (gv >= g_floor) keep |= 1u << (4 * rt + e);
+      }
+      gm[rt][e] = x;
     }
+  {
+    float run[4], prev[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sum[4];
+    // round s settles lane group s (its predecessor settled in round s - 1)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        run[rt] = prev[rt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          run[rt] += gm[rt][e];
+          sum[rt][e] = run[rt];
+        }
+      }
+      if (s2 < 3)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const float up = __shfl_up(run[rt], 16);
+          prev[rt] = gq == 0 ? 0.f : up;
+        }
+    }
+    float off = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      gm[rt] = off + sum[rt];
+      off += __shfl(run[rt], 48 + i);  // the tile's total, from lane group 3
+    }
+  }
   dgl += __shfl_xor(dgl, 16);  // dgamma-last: the four lane groups' parts
   dgl += __shfl_xor(dgl, 32);
   // beta of the rows this thread writes out below (r = tid / 32 + 16 j)
@@ -1439,9 +1708,14 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
     return bp.width > 0 ? Win{wi * bp.width, (wi + 1) * bp.width, bp.width} : Win{0, kAll, 0};
   };
   const dim3 gc((unsigned)bp.n_area, H);
+  // at D = 128 the fused record pass (no copies of the inputs in the record)
+  auto const record_kernel = [] {
+    if constexpr (D == 128) return &kda_bwd_chunk_fused<T, D>;
+    else return &kda_bwd_chunk<T, D>;
+  }();
   auto record = [&](const Win& wn) {
     if (bp.n_area == 0) return hipSuccess;
-    return launch_kernel(kda_bwd_chunk<T, D>, gc, dim3(kThreads), stream, (const T*)in.q, (const T*)in.k,
+    return launch_kernel(record_kernel, gc, dim3(kThreads), stream, (const T*)in.q, (const T*)in.k,
                          (const T*)in.v, in.g, in.beta, (const T*)dout, cu, (const int64_t*)seqs, n_rows, T_per, H,
                          g_floor, gate, rec, zero, wn);
   };
@@ -1452,13 +1726,14 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
   auto state = [&](const Win& wn, int64_t wi, int64_t lo, int64_t hi) {
     const float* cin = carry ? carry + (size_t)((wi + 1) & 1) * carry_floats : nullptr;
     float* cout = carry ? carry + (size_t)(wi & 1) * carry_floats : nullptr;
-    return launch_kernel(kda_bwd_state<D>, dim3((unsigned)state_blocks), dim3(512), stream, (const float*)rec, dht,
-                         cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, wn, dHs, dh0, cin, cout);
+    return launch_kernel(kda_bwd_state<T, D>, dim3((unsigned)state_blocks), dim3(512), stream, (const float*)rec,
+                         (const T*)dout, dht, cu, (const int64_t*)seqs, n_rows, T_per, H, lo, hi, wn, dHs, dh0, cin,
+                         cout);
   };
   // the fused local kernel at D = 128 (one column tile per wave), the
   // scratch version otherwise
   auto const local_kernel = [] {
-    if constexpr (D == 16 * (kThreads / 64)) return &kda_bwd_local_fused<T, D>;
+    if constexpr (D == 128) return &kda_bwd_local_fused<T, D>;
     else return &kda_bwd_local<T, D>;
   }();
   // A single fixed-length sequence has its chunks [lo, hi) at consecutive
@@ -1473,7 +1748,7 @@ int launch_bwd_typed(int n_rows, int T_per, int H, const BwdPlan& bp, float g_fl
       count = top - lo;
     }
     return launch_kernel(local_kernel, dim3((unsigned)count, H), dim3(kThreads), st, (const T*)in.q,
-                         (const T*)in.k, in.g, cu, (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate,
+                         (const T*)in.k, (const T*)in.v, (const T*)dout, in.g, cu, (const int64_t*)seqs, n_rows, T_per, H, g_floor, gate,
                          (const float*)rec, h0, (const float*)ht, (const float*)states, (const float*)zero,
                          (const float*)dHs, scr, (T*)dq, (T*)dk, (T*)dv, (T*)dg, dbeta, lo, hi, wn, a0);
   };

@@ -150,13 +150,14 @@ int launch_chunk_forward(int is_bf16, int d, int n_rows, int T, int H, const Seg
                          void* ws, void* stream, void* const* events);
 
 // ---- backward pass ------------------------------------------------------
-// Floats of one (chunk, head) record of the backward pass at width d: eight
-// [64][d] blocks (Qt, Kt, Kh, V, dO, Wk, Wv, Gamma), three [64][64] (P, T, Abar),
-// gamma [d] and beta [64]; and of one (chunk, head) scratch area of its local
-// gradient kernel: five [64][d] blocks, two [64][64] and one [d] at d = 64,
-// none at d = 128 (that kernel keeps its intermediates on chip).
+// Floats of one (chunk, head) record of the backward pass at width d: five
+// [64][d] blocks (Qt, Kt, Kh, Wk, Wv), three [64][64] (P, T, Abar), gamma [d]
+// and beta [64], and at d = 64 three more [64][d] (copies of V and dO, and
+// Gamma); and of one (chunk, head) scratch area of its local gradient
+// kernel: five [64][d] blocks, two [64][64] and one [d] at d = 64, none at
+// d = 128 (that kernel keeps its intermediates on chip).
 constexpr size_t bwd_rec_floats(int d) {
-  return (size_t)8 * kChunk * d + (size_t)3 * kChunk * kChunk + (size_t)d + kChunk;
+  return (size_t)(d == 128 ? 5 : 8) * kChunk * d + (size_t)3 * kChunk * kChunk + (size_t)d + kChunk;
 }
 constexpr size_t bwd_scr_floats(int d) {
   return d == 128 ? 0 : (size_t)5 * kChunk * d + (size_t)2 * kChunk * kChunk + (size_t)d;
@@ -188,7 +189,7 @@ struct BwdPlan {
 };
 
 // Chunk-heads of the area above which the default plan cuts sequences into
-// windows: about 2.9 GiB of records and gradients at d = 128.
+// windows: about 2.1 GiB of records and gradients at d = 128.
 constexpr int64_t kBwdAreaChunkHeads = 8192;
 // Narrowest window of the default plan.
 constexpr int64_t kBwdMinWindow = 64;

@@ -294,7 +294,7 @@ int kda_chunk_forward_states(const kda_chunk_desc_ex_t* d,
  * The call replays the forward internally (its outputs are not needed).
  * The workspace (256-byte aligned) holds the replay's state after every
  * chunk (64 KiB per (chunk of 64 tokens, head) at d = 128) and, for the
- * chunks in flight, fp32 records and state gradients (about 0.36 MiB per
+ * chunks in flight, fp32 records and state gradients (about 0.27 MiB per
  * (chunk, head) at d = 128; at d = 64 also a scratch area).  Chunks are
  * processed in windows of W chunk indices of every sequence, from the last
  * window to the first; the call takes the widest window that fits

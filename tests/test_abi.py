@@ -354,13 +354,14 @@ def test_backward_workspace_size(lib):
     st, n = bws_status(lib, desc())
     assert st == KDA_OK and n % 256 == 0
     # at least the forward's workspace, the state after every chunk, and an
-    # fp32 record (eight [64][d] blocks, three [64][64], gamma, beta) and
+    # fp32 record (five [64][d] blocks, three [64][64], gamma, beta; at
+    # d = 64 three more [64][d], copies of v and dO and Gamma) and
     # end-state gradient per (chunk, head); the local-gradient kernel at
     # d = 128 needs no scratch area, at d = 64 one of five [64][d], two
     # [64][64] and one [d]
     fwd = ws_status(lib, desc())[1]
     chunks = 4096 // 64
-    per_chunk = (8 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 128 * 128) * 4
+    per_chunk = (5 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 128 * 128) * 4
     assert n >= fwd + 16 * chunks * 128 * 128 * 4 + 16 * chunks * per_chunk
     assert n < fwd + 16 * chunks * 128 * 128 * 4 + 16 * chunks * (per_chunk + 5 * 64 * 128 * 4)
     d64 = bws_status(lib, desc(d_k=64, d_v=64))[1]

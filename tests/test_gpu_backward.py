@@ -357,8 +357,10 @@ def _window_budget(inp, W):
     rows = B if cu is None else cu.numel() - 1
     chunks = (T + 63) // 64
     n_slots = rows * chunks if cu is None else chunks + rows
-    scr = 0 if d == 128 else 5 * 64 * d + 2 * 64 * 64 + d  # the d = 128 kernel keeps it on chip
-    per_slot = H * ((8 * 64 * d + 3 * 64 * 64 + d + 64 + scr) * 4 + d * d * 4)
+    # at d = 128 no copies of v, dO and Gamma in the record, and no scratch
+    # (the local-gradient kernel keeps it on chip)
+    blocks, scr = (5, 0) if d == 128 else (8, 5 * 64 * d + 2 * 64 * 64 + d)
+    per_slot = H * ((blocks * 64 * d + 3 * 64 * 64 + d + 64 + scr) * 4 + d * d * 4)
     full = kda.backward_workspace_bytes(B, T, H, d, inp["q"].dtype, n_seqs=0 if cu is None else rows)
     return full - (n_slots - rows * W) * per_slot + 2 * rows * H * d * d * 4 + 4 * 256
 

@@ -67,12 +67,12 @@ def call(lib, d, budget):
 
 
 def per_slot_bytes(H, d, C=64):
-    # fp32 record (eight [C][d], three [C][C], gamma [d], beta [C]), scratch
-    # (five [C][d], two [C][C], one [d]; none at d = 128, whose local-gradient
-    # kernel keeps its intermediates on chip) and end-state gradient [d][d]
-    # per (chunk, head)
-    scr = 0 if d == 128 else 5 * C * d + 2 * C * C + d
-    return H * ((8 * C * d + 3 * C * C + d + C + scr) * 4 + d * d * 4)
+    # fp32 record (five [C][d], three [C][C], gamma [d], beta [C]; at d = 64
+    # three more [C][d], copies of v and dO and Gamma), scratch (five [C][d],
+    # two [C][C], one [d]; none at d = 128, whose local-gradient kernel keeps
+    # its intermediates on chip) and end-state gradient [d][d] per (chunk, head)
+    blocks, scr = (5, 0) if d == 128 else (8, 5 * C * d + 2 * C * C + d)
+    return H * ((blocks * C * d + 3 * C * C + d + C + scr) * 4 + d * d * 4)
 
 
 def test_default_is_the_documented_window(stub):
