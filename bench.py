@@ -108,11 +108,11 @@ PREFILL = dict(B=1, T=4096, H=16, d=128, wid=1)
 DECODE = dict(N=256, H=32, d=128, wid=4)
 CPU_SAMPLE_SECONDS = 10.0
 
-PREFILL_SOURCES = ("kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
+PREFILL_SOURCES = ("kda_prefill.hip", "kda_rows.h", "kda_device.h", "kda_api.cpp", "kda_launch.h")
 MFMA_PROFILE = "kda_mfma_util_prefill_T4096_H16_backward.txt"
-BWD_SOURCES = ("kda_backward.hip", "kda_prefill.hip", "kda_device.h", "kda_api.cpp", "kda_launch.h")
+BWD_SOURCES = ("kda_backward.hip", "kda_prefill.hip", "kda_rows.h", "kda_device.h", "kda_api.cpp", "kda_launch.h")
 # the kernel of a backward stage where it is not the stage's own name (d = 128)
-BWD_STAGE_KERNEL = {"kda_bwd_local": "kda_bwd_local_fused"}
+BWD_STAGE_KERNEL = {"kda_bwd_chunk": "kda_bwd_chunk_fused", "kda_bwd_local": "kda_bwd_local_fused"}
 
 
 def log(msg: str) -> None:

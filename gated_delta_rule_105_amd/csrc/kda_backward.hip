@@ -53,6 +53,7 @@
 
 #include "kda_device.h"
 #include "kda_launch.h"
+#include "kda_rows.h"
 
 namespace kda {
 namespace {
@@ -656,13 +657,17 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk_fused(const T* __restr
                                                            const int64_t* __restrict__ seqs, int n_rows, int T_per,
                                                            int H, float g_floor, int gate, float* __restrict__ rec,
                                                            float* __restrict__ zero_state, Win win) {
+  static_assert(sizeof(T) == 2, "the bf16 path (inputs read as pairs)");
   typedef Rec<D> R;
-  typedef RowSplit<D> RS;
+  // element-wise mapping of the forward's input rows (Raw): thread (part, cp)
+  // takes channels 2 cp, 2 cp + 1 of rows RP part .. RP part + RP - 1
+  constexpr int NPR = D / 2, NPART = kThreads / NPR, RP = C / NPART;
+  static_assert(NPART * NPR == kThreads && RP == 8, "the row groups of Raw");
   constexpr int LX = D + 4, AX = C * LX;
   __shared__ ChunkPos pos;
   __shared__ __align__(16) float lds[3 * AX];
   __shared__ float As[C][C + 1], Ts[C][C + 1], Ps[C][C + 1];
-  __shared__ float gsum[RS::NG][D];
+  __shared__ float2 gsum[NPART][NPR];
   __shared__ float sb[C];
   float* const LQ = lds;
   float* const LK = lds + AX;
@@ -675,48 +680,53 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk_fused(const T* __restr
     for (int x = tid; x < D * D; x += blockDim.x) zero_state[x] = 0.f;
   if (!chunk_pos_shared(slot, win, cu, seqs, n_rows, T_per, &pos)) return;
   float* Rp = rec + (slot * H + h) * (int64_t)R::FLOATS;
-  const bool bf = sizeof(T) == 2;
   const int len = pos.len;
-  // element-wise, thread (group, channel c) over rows r0 .. r0 + RG - 1.
-  // Gamma: each group takes its own prefix sums of the floored log-decays,
-  // then adds the totals of the groups before it (kda_bwd_local_fused sums
-  // them in the same order).
-  const int c = tid % D, grp = tid / D, r0 = grp * RS::RG;
-  float gl[RS::RG], vr[RS::RG];
+  const int cp = tid % NPR, part = tid / NPR, c0 = 2 * cp, r0 = RP * part;
+  // Gamma: each row group takes its own prefix sums of the floored
+  // log-decays, then adds the totals of the groups before it
+  // (kda_bwd_local_fused sums them in the same order)
+  typedef PairT<T> PW;
+  // the inputs: branch-free buffer loads, all issued before the first use
+  // (rows past the chunk's end read as zeros)
+  Raw<T, D, true, false, false> raw;
+  raw.load(ChunkInputs{q, k, v, g, beta, nullptr, nullptr, nullptr}, pos.tok0, len, H, h, tid, gate);
+  float2 gl[RP];
   {
-    float qr[RS::RG], kr[RS::RG];
-    if (tid < C) sb[tid] = tid < len ? beta[(pos.tok0 + tid) * H + h] : 0.f;
-    float run = 0.f;
+    if (tid < C) sb[tid] = raw.beta;
+    const bool gh = gate == kGateHead;  // one log-decay per row, for both channels
+    float2 run = {0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < RS::RG; ++j) {
-      const int r = r0 + j;
-      qr[j] = kr[j] = vr[j] = 0.f;
-      if (r < len) {
-        const int64_t th = ((pos.tok0 + r) * H + h) * D + c;
-        run += fmaxf(gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c), g_floor);
-        qr[j] = ldx(q + th);
-        kr[j] = ldx(k + th);
-        vr[j] = ldx(v + th);
+    for (int j = 0; j < RP; ++j) {
+      if (r0 + j < len) {
+        const float x = PW::lo(raw.g[j]);
+        run.x += fmaxf(x, g_floor);
+        run.y += fmaxf(gh ? x : PW::hi(raw.g[j]), g_floor);
       }
       gl[j] = run;
     }
-    gsum[grp][c] = run;
+    gsum[part][cp] = run;
     for (int x = tid; x < C * C; x += kThreads) {
       const int r = x / C, s2 = x % C;
       Ts[r][s2] = r == s2 ? 1.f : 0.f;
     }
     __syncthreads();
-    float off = 0.f;
-    for (int j = 0; j < grp; ++j) off += gsum[j][c];
+    float2 off = {0.f, 0.f};
+    for (int j = 0; j < part; ++j) {
+      off.x += gsum[j][cp].x;
+      off.y += gsum[j][cp].y;
+    }
 #pragma unroll
-    for (int j = 0; j < RS::RG; ++j) {
+    for (int j = 0; j < RP; ++j) {
       const int r = r0 + j;
-      const float G = off + gl[j];
-      const float e = __expf(G), ei = __expf(-G);
-      LQ[r * LX + c] = qr[j] * e;
-      LK[r * LX + c] = kr[j] * e;
-      LH[r * LX + c] = kr[j] * ei;
-      if (r == C - 1) Rp[R::GAM + c] = e;
+      const float G0 = off.x + gl[j].x, G1 = off.y + gl[j].y;
+      const float e0 = __expf(G0), e1 = __expf(G1);
+      const float i0 = __expf(-G0), i1 = __expf(-G1);
+      const float q0 = PW::lo(raw.qw(j)), q1 = PW::hi(raw.qw(j));
+      const float k0 = PW::lo(raw.kw(j)), k1 = PW::hi(raw.kw(j));
+      *(float2*)&LQ[r * LX + c0] = make_float2(q0 * e0, q1 * e1);
+      *(float2*)&LK[r * LX + c0] = make_float2(k0 * e0, k1 * e1);
+      *(float2*)&LH[r * LX + c0] = make_float2(k0 * i0, k1 * i1);
+      if (r == C - 1) *(float2*)&Rp[R::GAM + c0] = make_float2(e0, e1);
     }
   }
   if (tid < C) Rp[R::BET + tid] = sb[tid];
@@ -745,34 +755,49 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk_fused(const T* __restr
     }
   }
   __syncthreads();
-  // Qt, Kt, Kh out as rows; P and the upper tiles of Abar (zero)
-  for (int x = tid; x < C * D / 4; x += kThreads) {
-    const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
-    *(f32x4*)&Rp[R::QT + r * D + c4] = *(const f32x4*)&LQ[r * LX + c4];
-    *(f32x4*)&Rp[R::KT + r * D + c4] = *(const f32x4*)&LK[r * LX + c4];
-    *(f32x4*)&Rp[R::KH + r * D + c4] = *(const f32x4*)&LH[r * LX + c4];
-  }
-  for (int x = tid; x < C * C; x += kThreads) {
-    const int r = x / C, s2 = x % C;
-    const bool up = (s2 >> 4) > (r >> 4);
-    Rp[R::PM + x] = up ? 0.f : Ps[r][s2];
-    if (up) Rp[R::AB + x] = 0.f;
-  }
   // T = (I + A)^{-1} (A = diag(beta) Abar strictly lower) over 4 x 4 blocks
   // of 16, as in kda_bwd_chunk: diagonal blocks by forward substitution, one
-  // lane per column, then the blocks below them one block row at a time
-  if (tid < C) {
-    const int s2 = tid, end = (s2 | 15) + 1;
-    for (int r = s2 + 1; r < end; ++r) {
+  // lane of wave 0 per column, then the blocks below them one block row at a
+  // time.  Lane s keeps column s of its diagonal block in registers (zero
+  // above the diagonal: the sums start at the same term as the plain
+  // substitution), so that a step waits on no LDS round trip; meanwhile the
+  // other waves write Qt, Kt, Kh as rows, P, and the upper tiles of Abar (zero).
+  if (w == 0) {
+    const int o = 16 * (tid >> 4), j = tid & 15;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = r == j ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
       float acc = 0.f;
-      for (int m = s2; m < r; ++m) acc += As[r][m] * Ts[m][s2];
-      Ts[r][s2] = -acc;
+#pragma unroll
+      for (int m = 0; m < r; ++m) acc += As[o + r][o + m] * t[m];
+      if (r > j) t[r] = -acc;
+    }
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+      if (r > j) Ts[o + r][o + j] = t[r];
+  } else {
+    constexpr int NT = kThreads - 64;
+    for (int x = tid - 64; x < C * D / 4; x += NT) {
+      const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
+      *(f32x4*)&Rp[R::QT + r * D + c4] = *(const f32x4*)&LQ[r * LX + c4];
+      *(f32x4*)&Rp[R::KT + r * D + c4] = *(const f32x4*)&LK[r * LX + c4];
+      *(f32x4*)&Rp[R::KH + r * D + c4] = *(const f32x4*)&LH[r * LX + c4];
+    }
+    for (int x = tid - 64; x < C * C; x += NT) {
+      const int r = x / C, s2 = x % C;
+      const bool up = (s2 >> 4) > (r >> 4);
+      Rp[R::PM + x] = up ? 0.f : Ps[r][s2];
+      if (up) Rp[R::AB + x] = 0.f;
     }
   }
   __syncthreads();
   // diag(beta) V over Qt (every thread is past the row stores)
 #pragma unroll
-  for (int j = 0; j < RS::RG; ++j) LQ[(r0 + j) * LX + c] = sb[r0 + j] * vr[j];
+  for (int j = 0; j < RP; ++j)
+    *(float2*)&LQ[(r0 + j) * LX + c0] =
+        make_float2(sb[r0 + j] * PW::lo(raw.vw(j)), sb[r0 + j] * PW::hi(raw.vw(j)));
   for (int bi = 1; bi < C / 16; ++bi) {
     if (w < bi) {
       const int bj = w;
@@ -1542,8 +1567,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // 4 gq + e is element e of fragment rt).  The log-decays are loaded here,
   // before any store: which rows pass the floor (bit 4 rt + e), and Gamma,
   // summed in the order of the record pass (so the two agree to the bit):
-  // within each 16-row tile the rows in order, a running sum handed from
-  // lane group gq to gq + 1, then the tiles' totals in order
+  // within each group of 8 rows (lane groups gq = 2 p', 2 p' + 1 of a
+  // tile) the rows in order, a running sum handed from the even lane group
+  // to the odd one, then the groups' totals in order
   f32x4 gm[4];
   uint32_t keep = 0;
 #pragma unroll
@@ -1562,9 +1588,9 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   {
     float run[4], prev[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 sum[4];
-    // round s settles lane group s (its predecessor settled in round s - 1)
+    // round 0 settles the even lane groups, round 1 the odd ones
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         run[rt] = prev[rt];
@@ -1574,18 +1600,21 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
           sum[rt][e] = run[rt];
         }
       }
-      if (s2 < 3)
+      if (s2 == 0)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const float up = __shfl_up(run[rt], 16);
-          prev[rt] = gq == 0 ? 0.f : up;
+          prev[rt] = (gq & 1) ? up : 0.f;
         }
     }
+    // the groups' totals come from lane groups 1 and 3
     float off = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      gm[rt] = off + sum[rt];
-      off += __shfl(run[rt], 48 + i);  // the tile's total, from lane group 3
+      const float t0 = __shfl(run[rt], 16 + i), t1 = __shfl(run[rt], 48 + i);
+      const float off1 = off + t0;
+      gm[rt] = (gq < 2 ? off : off1) + sum[rt];
+      off = off1 + t1;
     }
   }
   dgl += __shfl_xor(dgl, 16);  // dgamma-last: the four lane groups' parts
