@@ -1372,18 +1372,40 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     fs[kb] = frag_cols(S, D, cw + i, 16 * kb, gq);
     fg[kb] = frag_cols(dH, D, cw + i, 16 * kb, gq) * *(const f32x4*)(gam + 16 * kb + 4 * gq);
   }
-  // this head's row r of an input (r < len)
-  auto in_row = [&](const T* x, int r) { return x + ((pos.tok0 + r) * H + h) * D; };
-  for (int x = tid; x < C * D / 4; x += kThreads) {
-    const int r = x / (D / 4), c4 = 4 * (x % (D / 4));
-    hl_put4(H0, r, c4, *(const f32x4*)&Rp[R::WK + r * D + c4]);
-    hl_put4(H1, r, c4, *(const f32x4*)&Rp[R::KH + r * D + c4]);
-    hl_put4(H3, r, c4, r < len ? ld4(in_row(dout, r) + c4) : z4);
-  }
-  for (int x = tid; x < C * C / 4; x += kThreads) {
-    const int r = x / (C / 4), c4 = 4 * (x % (C / 4));
-    *(f32x4*)&R2a[r * LC + c4] = *(const f32x4*)&Rp[R::PM + r * C + c4];
-    *(f32x4*)&R2b[r * LC + c4] = *(const f32x4*)&Rp[R::TM + r * C + c4];
+  // this chunk's rows of v and dO as buffer resources (ChunkRows): rows past
+  // the chunk's end read as zeros, with no branch; a masked load would wait
+  // for every load before it
+  const ChunkRows<T> vrows(v, pos.tok0, len, H, h, D), orows(dout, pos.tok0, len, H, h, D);
+  {
+    // every staging load before the first LDS store
+    constexpr int NS = C * D / 4 / kThreads, NP = C * C / 4 / kThreads;
+    f32x4 sw[NS], sk[NS], so[NS], sp[NP], st[NP];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int x = tid + j * kThreads, r = x / (D / 4), c4 = 4 * (x % (D / 4));
+      sw[j] = *(const f32x4*)&Rp[R::WK + r * D + c4];
+      sk[j] = *(const f32x4*)&Rp[R::KH + r * D + c4];
+      so[j] = orows.ld4(r, c4);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int x = tid + j * kThreads, r = x / (C / 4), c4 = 4 * (x % (C / 4));
+      sp[j] = *(const f32x4*)&Rp[R::PM + r * C + c4];
+      st[j] = *(const f32x4*)&Rp[R::TM + r * C + c4];
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int x = tid + j * kThreads, r = x / (D / 4), c4 = 4 * (x % (D / 4));
+      hl_put4(H0, r, c4, sw[j]);
+      hl_put4(H1, r, c4, sk[j]);
+      hl_put4(H3, r, c4, so[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int x = tid + j * kThreads, r = x / (C / 4), c4 = 4 * (x % (C / 4));
+      *(f32x4*)&R2a[r * LC + c4] = sp[j];
+      *(f32x4*)&R2b[r * LC + c4] = st[j];
+    }
   }
   __syncthreads();
 
@@ -1524,13 +1546,18 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // for them.
   {
     const int r = tid / 8, part = tid % 8;
-    const T* vr = in_row(v, r < len ? r : 0);
     f32x4 a4 = z4;  // columns 16 part .. 16 part + 15, four at a time
+    f32x4 vv[4], kt[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c4 = 16 * part + 4 * j;
-      const f32x4 vv = r < len ? ld4(vr + c4) : z4;
-      a4 += hl_get4(H0, r, c4) * *(const f32x4*)&Rp[R::KT + r * D + c4] + hl_get4(H1, r, c4) * vv;
+      vv[j] = vrows.ld4(r, c4);
+      kt[j] = *(const f32x4*)&Rp[R::KT + r * D + c4];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c4 = 16 * part + 4 * j;
+      a4 += hl_get4(H0, r, c4) * kt[j] + hl_get4(H1, r, c4) * vv[j];
     }
     float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
     for (int s2 = part; s2 < r; s2 += 8) acc += R2b[r * LC + s2] * Rp[R::AB + r * C + s2];
@@ -1572,19 +1599,22 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // to the odd one, then the groups' totals in order
   f32x4 gm[4];
   uint32_t keep = 0;
+  {
+    const GateRows<T> grows(g, gate, pos.tok0, len, H, h, D);
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + 4 * gq + e;
-      float x = 0.f;
-      if (r < len) {
-        const float gv = gate_at(g, gate, bf, (pos.tok0 + r) * H + h, D, c);
-        x = fmaxf(gv, g_floor);
-        if (gv >= g_floor) keep |= 1u << (4 * rt + e);
+      for (int e = 0; e < 4; ++e) gm[rt][e] = grows.ld(16 * rt + 4 * gq + e, c);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * gq + e;
+        const float gv = gm[rt][e];
+        if (r < len && gv >= g_floor) keep |= 1u << (4 * rt + e);
+        gm[rt][e] = r < len ? fmaxf(gv, g_floor) : 0.f;
       }
-      gm[rt][e] = x;
-    }
+  }
   {
     float run[4], prev[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 sum[4];

@@ -150,4 +150,55 @@ template <typename T, int D, bool WITH_Q, bool MX, bool NT> struct Raw {
   __device__ __forceinline__ word vw(int s) const { return dec(v[s], MX ? vs[s] : 0u); }
 };
 
+
+// ---- one chunk's rows of an input, read by any element ----------------------
+// Rows tok0 .. tok0 + len - 1 (len >= 1) of head h of a [tokens, H, D]
+// tensor as one buffer resource: element (r, c) at byte offset
+// (r H D + c) sizeof(T), and a read past the last row returns zeros, with no
+// branch.
+template <typename T> struct ChunkRows {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t rs;  // row stride, bytes
+  __device__ __forceinline__ ChunkRows(const T* x, int64_t tok0, int len, int H, int h, int D)
+      : r(rsrc(x + (tok0 * H + h) * D, ((uint32_t)(len - 1) * H * D + D) * sizeof(T))),
+        rs((uint32_t)H * D * sizeof(T)) {}
+  // elements c .. c + 3 of row row (c % 4 == 0)
+  __device__ __forceinline__ f32x4 ld4(int row, int c) const {
+    const uint32_t off = (uint32_t)row * rs + (uint32_t)c * sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+      return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+  }
+};
+// The log-decays of one chunk: per channel ([tokens, H, D]), one per
+// (token, head) ([tokens, H], the same for every channel), or none (zeros:
+// an empty range).
+template <typename T> struct GateRows {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t rs, cs;  // row and channel strides, bytes
+  __device__ __forceinline__ GateRows(const void* g, int gate, int64_t tok0, int len, int H, int h, int D) {
+    const T* x = (const T*)g;
+    if (gate == kGateChannel) {
+      r = rsrc(x + (tok0 * H + h) * D, ((uint32_t)(len - 1) * H * D + D) * sizeof(T));
+      rs = (uint32_t)H * D * sizeof(T);
+      cs = sizeof(T);
+    } else {
+      r = gate == kGateHead ? rsrc(x + tok0 * H + h, ((uint32_t)(len - 1) * H + 1) * sizeof(T)) : rsrc(g, 0u);
+      rs = (uint32_t)H * sizeof(T);
+      cs = 0;
+    }
+  }
+  __device__ __forceinline__ float ld(int row, int c) const {
+    const uint32_t off = (uint32_t)row * rs + (uint32_t)c * cs;
+    if constexpr (sizeof(T) == 2)
+      return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
+    else
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+};
+
 }  // namespace kda
