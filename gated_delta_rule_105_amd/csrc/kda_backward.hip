@@ -1323,7 +1323,8 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const void* __restrict__ g, const int32_t* __restrict__ cu,
     const int64_t* __restrict__ seqs, int n_rows, int T_per, int H, float g_floor, int gate, const float* __restrict__ rec,
-    const float* __restrict__ h0, const float* __restrict__ ht, const float* __restrict__ states,
+    const float* __restrict__ h0, const float* __restrict__ /* ht: S_next not read */,
+    const float* __restrict__ states,
     const float* __restrict__ zero_state, const float* __restrict__ dHs, float* __restrict__ scr,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dg, float* __restrict__ dbeta,
     int64_t m_lo, int64_t m_hi, Win win, int64_t a0) {
@@ -1356,8 +1357,6 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   const int64_t dd = (int64_t)D * D;
   const float* S = pos.m == 0 ? (h0 ? h0 + ((int64_t)pos.n * H + h) * dd : zero_state)
                               : states + ((pos.st0 + pos.m - 1) * H + h) * dd;
-  const float* Sn = pos.m == pos.nc - 1 ? ht + ((int64_t)pos.n * H + h) * dd
-                                        : states + ((pos.st0 + pos.m) * H + h) * dd;
   const float* gam = Rp + R::GAM;
   const float* bet = Rp + R::BET;
   const int len = pos.len;
@@ -1454,6 +1453,10 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   lds_barrier();
 
   // ---- phase 2: dP = lower_incl(dO U^T), its 10 lower tiles over the waves
+  // (the first k-block's rows of S and dH for the products after it go out
+  // first, to arrive meanwhile)
+  f32x4 s0 = frag_rows(S, D, cw + i, 0, gq), s1 = frag_rows(S, D, cw + i, 16, gq);
+  f32x4 h0v = frag_rows(dH, D, cw + i, 0, gq), h1v = frag_rows(dH, D, cw + i, 16, gq);
   for (int t = w; t < 10; t += kThreads / 64) {
     int ta, tb;
     low_tile(t, ta, tb);
@@ -1465,20 +1468,26 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
       R2a[(16 * ta + 4 * gq + e) * LC + 16 * tb + i] = (ta > tb || 4 * gq + e >= i) ? acc[e] : 0.f;
   }
   // key columns cw .. cw + 15: Dk = -Dv S^T, dQt = dO S^T, dKh = U dH^T
-  // diag(gamma) (the products with dP wait for its tiles)
-  // With them, this lane's part of dgamma-last of key channel cw + i,
-  // sum_j dH_cj S_next_cj over the j its fragments hold.
+  // diag(gamma) (the products with dP wait for its tiles).
+  // dgamma-last of key channel c = cw + i is sum_j dH_cj S_next_cj, with
+  // S_next = diag(gamma)(S + Kh^T U):
+  //   gamma_c <dH_c, S_c> + sum_r Kh_rc (U dH^T diag(gamma))_rc,
+  // the first sum over the j of this lane's row fragments here, the second
+  // over its rows once Kh's columns are in (phase 4), without reading S_next.
   f32x4 Dk[4] = {z4, z4, z4, z4}, dQt[4] = {z4, z4, z4, z4}, dKh[4] = {z4, z4, z4, z4};
   float dgl = 0.f;
 #pragma unroll 2
   for (int kb = 0; kb < D / 32; ++kb) {
-    // S^T[value][key] = S[key][value], dH[key][value] (and S_next) along rows
-    const f32x4 s0 = frag_rows(S, D, cw + i, 32 * kb, gq), s1 = frag_rows(S, D, cw + i, 32 * kb + 16, gq);
-    const f32x4 h0v = frag_rows(dH, D, cw + i, 32 * kb, gq), h1v = frag_rows(dH, D, cw + i, 32 * kb + 16, gq);
-    const f32x4 n0 = frag_rows(Sn, D, cw + i, 32 * kb, gq), n1 = frag_rows(Sn, D, cw + i, 32 * kb + 16, gq);
-    dgl += h0v[0] * n0[0] + h0v[1] * n0[1] + h0v[2] * n0[2] + h0v[3] * n0[3] + h1v[0] * n1[0] + h1v[1] * n1[1] +
-           h1v[2] * n1[2] + h1v[3] * n1[3];
+    // S^T[value][key] = S[key][value] and dH[key][value] along rows
+    dgl += h0v[0] * s0[0] + h0v[1] * s0[1] + h0v[2] * s0[2] + h0v[3] * s0[3] + h1v[0] * s1[0] + h1v[1] * s1[1] +
+           h1v[2] * s1[2] + h1v[3] * s1[3];
     const HL8 bs = hl_of(s0, s1), bh = hl_of(h0v, h1v);
+    if (kb + 1 < D / 32) {  // the next k-block's rows, in flight during this one's products
+      s0 = frag_rows(S, D, cw + i, 32 * kb + 32, gq);
+      s1 = frag_rows(S, D, cw + i, 32 * kb + 48, gq);
+      h0v = frag_rows(dH, D, cw + i, 32 * kb + 32, gq);
+      h1v = frag_rows(dH, D, cw + i, 32 * kb + 48, gq);
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       Dk[rt] = mma3(hl_lds(H1, 16 * rt + i, kb, gq), bs, Dk[rt]);
@@ -1488,6 +1497,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   }
   {
     const float gc = gam[cw + i];  // the column's scale
+    dgl *= gc;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       Dk[rt] = -Dk[rt];
@@ -1584,11 +1594,11 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
+    dgl += fk[rt][0] * dKh[rt][0] + fk[rt][1] * dKh[rt][1] + fk[rt][2] * dKh[rt][2] + fk[rt][3] * dKh[rt][3];
     dQt[rt] += dQt2[rt];
     dKh[rt] += dKh2[rt];
   }
   // ---- element-wise, key column c of this lane, rows 16 rt + 4 gq + e
-  const bool bf = sizeof(T) == 2;
   const int c = cw + i;
   // Qt, Kt and Kh at this lane's elements are fq, fkt and fk (row 16 rt +
   // 4 gq + e is element e of fragment rt).  The log-decays are loaded here,
