@@ -1251,11 +1251,10 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
 //   phase 4: E = Dk + dA Kh, dKh += dA^T diag(beta) Kt, then the
 //            element-wise stage on the wave's key columns
 // Only the lower-triangular blocks of P, T, dP and dA enter the products.
-// The products whose operands run along rows (Wk S, Kh G, dP, Dk, dQt,
-// U dH^T, dA: about two thirds of the matrix work) take hi/lo bf16 MFMA, with
-// Wk, Kh, dO, U, Dv and Dk kept in LDS as hi and lo planes; those with the
-// [64][64] matrices P, T, dP and dA, read down columns, stay on fp32 MFMA,
-// each on its own accumulator (no accumulation chain mixes MFMA shapes).
+// Every product takes hi/lo bf16 MFMA, with Wk, Kh, dO, U, Dv and Dk kept in
+// LDS as hi and lo planes, and the [64][64] matrices P, T, dP and dA (fp32 in
+// LDS) and the register operands split as they are read: one MFMA shape
+// throughout, so that no accumulation chain mixes shapes.
 // hi/lo bf16 operands of the 16 x 16 x 32 products on the bf16 path: x ~ hi
 // + lo to about 2^-16, a 32-wide k-block as A_hi B_hi + A_hi B_lo + A_lo
 // B_hi (three bf16 MFMAs against eight fp32 16 x 16 x 4 for the same k).
@@ -1332,21 +1331,23 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   typedef Rec<D> R;
   static_assert(D == 128, "hi/lo planes of 128 columns");
   static_assert(sizeof(T) == 2, "the bf16 path: dO's hi/lo planes hold it exactly");
-  // R0, R1, R3: hi/lo planes of [64][128] operands (2 PLANE bf16 each);
-  // R2a, R2b: fp32 [64][64] with rows of 4 extra floats (16-byte aligned,
-  // and the 16-byte reads of 8 consecutive rows fall on distinct banks).
-  // At the end R0, R3 and R2a..R2b hold fp32 [64][LX] output rows.
+  // H0, H1, H3, H4: hi/lo planes of [64][128] operands (2 PLANE bf16 each);
+  // R2a (over H4's start), R2b: fp32 [64][64] with rows of 4 extra floats
+  // (16-byte aligned, and the 16-byte reads of 8 consecutive rows fall on
+  // distinct banks).  At the end R0, R3 and Q2 (over H4) hold fp32 [64][LX]
+  // output rows.
   constexpr int LX = D + 4, LC = C + 4, AC = C * LC, AP = PLANE;  // AP: floats of a plane pair
-  static_assert(AP >= C * LX && 2 * AC >= C * LX, "fp32 rows fit the regions");
+  static_assert(AP >= C * LX && AP >= AC, "fp32 rows and [64][64] arrays fit a plane pair's region");
   __shared__ ChunkPos pos;
-  __shared__ __align__(16) float lds[3 * AP + 2 * AC];
+  __shared__ __align__(16) float lds[4 * AP + AC];
   bf16_t* const H0 = (bf16_t*)lds;             // Wk, then U, then Dk (hi/lo)
   bf16_t* const H1 = (bf16_t*)(lds + AP);      // Kh, then Dv (hi/lo)
-  bf16_t* const H3 = (bf16_t*)(lds + 2 * AP);  // dO (hi/lo)
+  bf16_t* const H3 = (bf16_t*)(lds + 2 * AP);  // dO, then Wk (hi/lo)
+  bf16_t* const H4 = (bf16_t*)(lds + 3 * AP);  // Wv in phase 3 (hi/lo)
   float* const R0 = lds;                       // fp32 output rows at the end
   float* const R3 = lds + 2 * AP;
   float* const R2a = lds + 3 * AP;             // P, then dP
-  float* const R2b = R2a + AC;                 // T, then dA
+  float* const R2b = lds + 4 * AP;             // T, then dA
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, i = lane & 15;
   const int h = blockIdx.y;
   const int64_t slot = a0 + blockIdx.x;
@@ -1409,38 +1410,55 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   __syncthreads();
 
   // ---- phase 1: value columns cw .. cw + 15
-  f32x4 U[4], dU[4], Dv[4];
+  // A 32-wide k-block kb of a product with a lower-triangular [64][64]
+  // factor is nonzero for row tile rt when kb <= rt / 2 (the factor's rows
+  // along k) or kb >= rt / 2 (its columns along k); the zero tiles a block
+  // takes in are zeros in LDS.
+  f32x4 U[4], dU[4] = {z4, z4, z4, z4}, Dv[4] = {z4, z4, z4, z4};
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)  // Wv's columns, U = Wv - Wk S once the products are done
+#pragma unroll
+    for (int e = 0; e < 4; ++e) U[rt][e] = Rp[R::WV + (16 * rt + 4 * gq + e) * D + cw + i];
   {
-    f32x4 a[4] = {z4, z4, z4, z4}, b[4] = {z4, z4, z4, z4}, bp[4] = {z4, z4, z4, z4};
+    f32x4 a[4] = {z4, z4, z4, z4};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
       const HL8 bs = hl_of(fs[2 * kb], fs[2 * kb + 1]), bg = hl_of(fg[2 * kb], fg[2 * kb + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        a[rt] = mma3(hl_lds(H0, 16 * rt + i, kb, gq), bs, a[rt]);  // Wk S
-        b[rt] = mma3(hl_lds(H1, 16 * rt + i, kb, gq), bg, b[rt]);  // Kh G
+        a[rt] = mma3(hl_lds(H0, 16 * rt + i, kb, gq), bs, a[rt]);    // Wk S
+        dU[rt] = mma3(hl_lds(H1, 16 * rt + i, kb, gq), bg, dU[rt]);  // Kh G
       }
     }
+    // dU += P^T dO: dO's column fragments from its planes (bf16 values are
+    // hi + 0 there: exact)
 #pragma unroll
-    for (int kb = 0; kb < C / 16; ++kb) {
-      f32x4 fo;  // dO[token][value], from its planes (a bf16 value is hi + 0 there: exact)
+    for (int kb = 0; kb < C / 32; ++kb) {
+      f32x4 o0, o1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) fo[e] = hl_get(H3, 16 * kb + 4 * gq + e, cw + i);
+      for (int e = 0; e < 4; ++e) {
+        o0[e] = hl_get(H3, 32 * kb + 4 * gq + e, cw + i);
+        o1[e] = hl_get(H3, 32 * kb + 16 + 4 * gq + e, cw + i);
+      }
+      const HL8 bo = hl_of(o0, o1);
 #pragma unroll
-      for (int rt = 0; rt <= kb; ++rt) bp[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fo, bp[rt]);  // P^T
+      for (int rt = 0; rt < 4; ++rt)
+        if (kb >= rt / 2)
+          dU[rt] = mma3(hl_of(frag_cols(R2a, LC, 16 * rt + i, 32 * kb, gq),
+                              frag_cols(R2a, LC, 16 * rt + i, 32 * kb + 16, gq)), bo, dU[rt]);
     }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) U[rt][e] = Rp[R::WV + (16 * rt + 4 * gq + e) * D + cw + i] - a[rt][e];
-      dU[rt] = b[rt] + bp[rt];
-    }
+    for (int rt = 0; rt < 4; ++rt) U[rt] -= a[rt];
   }
+  // Dv = T^T dU
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    Dv[rt] = z4;
+  for (int kb = 0; kb < C / 32; ++kb) {
+    const HL8 bu = hl_of(dU[2 * kb], dU[2 * kb + 1]);
 #pragma unroll
-    for (int kb = rt; kb < C / 16; ++kb) Dv[rt] = mma(frag_cols(R2b, LC, 16 * rt + i, 16 * kb, gq), dU[kb], Dv[rt]);
+    for (int rt = 0; rt < 4; ++rt)
+      if (kb >= rt / 2)
+        Dv[rt] = mma3(hl_of(frag_cols(R2b, LC, 16 * rt + i, 32 * kb, gq),
+                            frag_cols(R2b, LC, 16 * rt + i, 32 * kb + 16, gq)), bu, Dv[rt]);
   }
   lds_barrier();  // every wave is done with Wk, Kh, P and T
 #pragma unroll
@@ -1457,6 +1475,14 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // first, to arrive meanwhile)
   f32x4 s0 = frag_rows(S, D, cw + i, 0, gq), s1 = frag_rows(S, D, cw + i, 16, gq);
   f32x4 h0v = frag_rows(dH, D, cw + i, 0, gq), h1v = frag_rows(dH, D, cw + i, 16, gq);
+  // this wave's columns of Kh and Qt, k running over tokens (for the products
+  // with dP and dA, and the element-wise stage, whose rows are these)
+  f32x4 fk[4], fq[4];
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb) {
+    fk[kb] = frag_cols(Rp + R::KH, D, cw + i, 16 * kb, gq);
+    fq[kb] = frag_cols(Rp + R::QT, D, cw + i, 16 * kb, gq);
+  }
   for (int t = w; t < 10; t += kThreads / 64) {
     int ta, tb;
     low_tile(t, ta, tb);
@@ -1504,45 +1530,60 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
       dKh[rt] = dKh[rt] * gc;
     }
   }
-  // this wave's columns of Kh and Qt, k running over tokens (kept for phase 4
-  // and the element-wise stage, whose rows are these)
-  f32x4 fk[4], fq[4];
-#pragma unroll
-  for (int kb = 0; kb < C / 16; ++kb) {
-    fk[kb] = frag_cols(Rp + R::KH, D, cw + i, 16 * kb, gq);
-    fq[kb] = frag_cols(Rp + R::QT, D, cw + i, 16 * kb, gq);
-  }
   lds_barrier();  // dP complete; U no longer read
+  // Wk and Wv as rows, for phase 3's planes (in flight during the products below)
+  constexpr int NW = C * D / 4 / kThreads;
+  f32x4 wkr[NW], wvr[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int x = tid + j * kThreads, r = x / (D / 4), c4 = 4 * (x % (D / 4));
+    wkr[j] = *(const f32x4*)&Rp[R::WK + r * D + c4];
+    wvr[j] = *(const f32x4*)&Rp[R::WV + r * D + c4];
+  }
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) hl_put(H0, 16 * rt + 4 * gq + e, cw + i, Dk[rt][e]);
-  // the fp32 products on their own accumulators (no accumulation chain mixes
-  // MFMA shapes), added below
-  f32x4 dQt2[4] = {z4, z4, z4, z4}, dKh2[4] = {z4, z4, z4, z4};
+  // dgamma-last's second sum, while dKh is still U dH^T diag(gamma)
 #pragma unroll
-  for (int kb = 0; kb < C / 16; ++kb)
+  for (int rt = 0; rt < 4; ++rt)
+    dgl += fk[rt][0] * dKh[rt][0] + fk[rt][1] * dKh[rt][1] + fk[rt][2] * dKh[rt][2] + fk[rt][3] * dKh[rt][3];
+  // dQt += dP Kh, dKh += dP^T Qt
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb) {
+    const HL8 bk = hl_of(fk[2 * kb], fk[2 * kb + 1]), bq = hl_of(fq[2 * kb], fq[2 * kb + 1]);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      if (kb <= rt) dQt2[rt] = mma(frag_rows(R2a, LC, 16 * rt + i, 16 * kb, gq), fk[kb], dQt2[rt]);  // dP Kh
-      if (kb >= rt) dKh2[rt] = mma(frag_cols(R2a, LC, 16 * rt + i, 16 * kb, gq), fq[kb], dKh2[rt]);  // dP^T Qt
+      if (kb <= rt / 2)
+        dQt[rt] = mma3(hl_of(frag_rows(R2a, LC, 16 * rt + i, 32 * kb, gq),
+                             frag_rows(R2a, LC, 16 * rt + i, 32 * kb + 16, gq)), bk, dQt[rt]);
+      if (kb >= rt / 2)
+        dKh[rt] = mma3(hl_of(frag_cols(R2a, LC, 16 * rt + i, 32 * kb, gq),
+                             frag_cols(R2a, LC, 16 * rt + i, 32 * kb + 16, gq)), bq, dKh[rt]);
     }
-  lds_barrier();  // Dk complete
+  }
+  lds_barrier();  // Dk complete; dO and dP no longer read
 
   // ---- phase 3: dA = strict_lower(-Dk Wk^T - Dv Wv^T), lower tiles over the waves
   float dbr;  // dbeta of row tid / 8 (in lanes tid % 8 == 0)
+  f32x4 fkt[4];  // this wave's columns of Kt, for phase 4 and the element-wise stage
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb) fkt[kb] = frag_cols(Rp + R::KT, D, cw + i, 16 * kb, gq);
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int x = tid + j * kThreads, r = x / (D / 4), c4 = 4 * (x % (D / 4));
+    hl_put4(H3, r, c4, wkr[j]);
+    hl_put4(H4, r, c4, wvr[j]);
+  }
+  lds_barrier();  // Wk and Wv planes complete
   for (int t = w; t < 10; t += kThreads / 64) {
     int ta, tb;
     low_tile(t, ta, tb);
     f32x4 acc = z4;
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
-      const HL8 wk = hl_of(frag_rows(Rp + R::WK, D, 16 * tb + i, 32 * kb, gq),
-                           frag_rows(Rp + R::WK, D, 16 * tb + i, 32 * kb + 16, gq));
-      const HL8 wv = hl_of(frag_rows(Rp + R::WV, D, 16 * tb + i, 32 * kb, gq),
-                           frag_rows(Rp + R::WV, D, 16 * tb + i, 32 * kb + 16, gq));
-      acc = mma3(hl_lds(H0, 16 * ta + i, kb, gq), wk, acc);
-      acc = mma3(hl_lds(H1, 16 * ta + i, kb, gq), wv, acc);
+      acc = mma3(hl_lds(H0, 16 * ta + i, kb, gq), hl_lds(H3, 16 * tb + i, kb, gq), acc);
+      acc = mma3(hl_lds(H1, 16 * ta + i, kb, gq), hl_lds(H4, 16 * tb + i, kb, gq), acc);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -1580,23 +1621,20 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   f32x4 E[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) E[rt] = Dk[rt];
-  f32x4 fkt[4];  // this wave's columns of Kt
 #pragma unroll
-  for (int kb = 0; kb < C / 16; ++kb) {
-    fkt[kb] = frag_cols(Rp + R::KT, D, cw + i, 16 * kb, gq);
-    const f32x4 ft = fkt[kb] * *(const f32x4*)(bet + 16 * kb + 4 * gq);
+  for (int kb = 0; kb < C / 32; ++kb) {
+    const HL8 bk = hl_of(fk[2 * kb], fk[2 * kb + 1]);
+    const HL8 bt = hl_of(fkt[2 * kb] * *(const f32x4*)(bet + 32 * kb + 4 * gq),
+                         fkt[2 * kb + 1] * *(const f32x4*)(bet + 32 * kb + 16 + 4 * gq));
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      if (kb <= rt) E[rt] = mma(frag_rows(R2b, LC, 16 * rt + i, 16 * kb, gq), fk[kb], E[rt]);
-      if (kb >= rt) dKh2[rt] = mma(frag_cols(R2b, LC, 16 * rt + i, 16 * kb, gq), ft, dKh2[rt]);
+      if (kb <= rt / 2)
+        E[rt] = mma3(hl_of(frag_rows(R2b, LC, 16 * rt + i, 32 * kb, gq),
+                           frag_rows(R2b, LC, 16 * rt + i, 32 * kb + 16, gq)), bk, E[rt]);
+      if (kb >= rt / 2)
+        dKh[rt] = mma3(hl_of(frag_cols(R2b, LC, 16 * rt + i, 32 * kb, gq),
+                             frag_cols(R2b, LC, 16 * rt + i, 32 * kb + 16, gq)), bt, dKh[rt]);
     }
-  }
-
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    dgl += fk[rt][0] * dKh[rt][0] + fk[rt][1] * dKh[rt][1] + fk[rt][2] * dKh[rt][2] + fk[rt][3] * dKh[rt][3];
-    dQt[rt] += dQt2[rt];
-    dKh[rt] += dKh2[rt];
   }
   // ---- element-wise, key column c of this lane, rows 16 rt + 4 gq + e
   const int c = cw + i;
@@ -1664,9 +1702,8 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
 #pragma unroll
   for (int j = 0; j < 4; ++j) bv[j] = bet[tid / (D / 4) + 16 * j];
   // dq, dk and dg go out as whole rows: staged in R0 (Dk is no longer read),
-  // Q2 over R2a and R2b (dA neither) and R3
+  // Q2 over H4 (Wv's planes neither) and R3
   float* const Q2 = R2a;
-  static_assert(2 * AC >= C * LX, "a [C][LX] array fits R2a and R2b");
   lds_barrier();  // every wave is past the dbeta pass and phase 4
   f32x4 dG[4];
 #pragma unroll
