@@ -635,6 +635,35 @@ __device__ __forceinline__ f32x4 frag_cols(const float* X, int ld, int c, int k0
   const float* p = X + (k0 + 4 * g) * ld + c;
   return (f32x4){p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
+// hi/lo bf16 operands of the 16 x 16 x 32 products on the bf16 path: x ~ hi
+// + lo to about 2^-16, a 32-wide k-block as A_hi B_hi + A_hi B_lo + A_lo
+// B_hi (three bf16 MFMAs against eight fp32 16 x 16 x 4 for the same k).
+struct HL8 {
+  bf16x8 h, l;
+};
+__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1]));
+  const uint32_t b = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3]));
+  hi = make_uint2(a, b);
+  lo = make_uint2(__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0] - __uint_as_float(a << 16),
+                                                               x[1] - __uint_as_float(a & 0xffff0000u))),
+                  __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2] - __uint_as_float(b << 16),
+                                                               x[3] - __uint_as_float(b & 0xffff0000u))));
+}
+// the fragment of a lane from its k = 4 g .. 4 g + 3 (x0) and 16 + 4 g ..
+// 16 + 4 g + 3 (x1) of a 32-wide k-block
+__device__ __forceinline__ HL8 hl_of(const f32x4& x0, const f32x4& x1) {
+  uint2 h0, l0, h1, l1;
+  split4(x0, h0, l0);
+  split4(x1, h1, l1);
+  return HL8{__builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y)),
+             __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y))};
+}
+__device__ __forceinline__ f32x4 mma3(const HL8& a, const HL8& b, f32x4 c) {
+  c = mma(a.h, b.h, c);
+  c = mma(a.h, b.l, c);
+  return mma(a.l, b.h, c);
+}
 // the lower-triangular 16 x 16 tiles (a, b), b <= a, of a 64 x 64 matrix
 __device__ __forceinline__ void low_tile(int t, int& a, int& b) {
   a = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
@@ -866,14 +895,22 @@ __device__ __forceinline__ void load_panel(f32x4 (&f)[NK], const float* p, int a
     }
   }
 }
-template <int NK>
+// HL: on hi/lo bf16 MFMA, the panels split as they are used (k-blocks of
+// 32: fragments 2 kb and 2 kb + 1), else on fp32 MFMA
+template <bool HL, int NK>
 __device__ __forceinline__ f32x4 mma_panels(f32x4 acc, const f32x4 (&a)[NK], const f32x4 (&b)[NK]) {
+  if constexpr (HL) {
+    static_assert(NK % 2 == 0, "whole 32-wide k-blocks");
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][0], b[kk][0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][1], b[kk][1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][2], b[kk][2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][3], b[kk][3], acc, 0, 0, 0);
+    for (int kb = 0; kb < NK / 2; ++kb) acc = mma3(hl_of(a[2 * kb], a[2 * kb + 1]), hl_of(b[2 * kb], b[2 * kb + 1]), acc);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][0], b[kk][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][1], b[kk][1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][2], b[kk][2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk][3], b[kk][3], acc, 0, 0, 0);
+    }
   }
   return acc;
 }
@@ -935,6 +972,9 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
                                                      const float* __restrict__ carry_in, float* carry_out) {
   typedef Rec<D> R;
   constexpr int NCB = D / 16, NKC = C / 16, NKH = D / 32;
+  // the bf16 path's products on hi/lo bf16 MFMA (about 2^-16 relative per
+  // product, against fp32 MFMA on the fp32 path)
+  constexpr bool HL = sizeof(T) == 2;
   __shared__ __align__(16) float G[D][16];
   __shared__ __align__(16) float dU[2][C][16];
   __shared__ __align__(16) float bOs[2][C / 16][64][4];  // dO fragment images, by step parity
@@ -1020,8 +1060,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 #pragma unroll
       for (int kk = 0; kk < StateOps<D>::NKP; ++kk) bOh[kk] = *(const f32x4*)bo[half * StateOps<D>::NKP + kk][lane];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma_panels(acc, cur.aP, bOh);
-      acc = mma_panels(acc, cur.aKh, bG);
+      acc = mma_panels<HL>(acc, cur.aP, bOh);
+      acc = mma_panels<HL>(acc, cur.aKh, bG);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dU[wave >> 2][16 * t + 4 * g + e][ii] = acc[e];
     }
@@ -1039,8 +1079,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       f32x4 bO[NKC];
 #pragma unroll
       for (int kk = 0; kk < NKC; ++kk) bO[kk] = *(const f32x4*)bo[kk][lane];
-      acc = mma_panels(acc, cur.aQ, bO);
-      neg = mma_panels(neg, cur.aW, bU);
+      acc = mma_panels<HL>(acc, cur.aQ, bO);
+      neg = mma_panels<HL>(neg, cur.aW, bU);
       // chunk m - 1's end-state gradient: to the carry when that chunk is in
       // the earlier window
       float* dHo = m > 0 ? (m == win.lo ? carry_out + sd : dhs_of(m - 1)) : nullptr;
@@ -1255,35 +1295,6 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local(
 // LDS as hi and lo planes, and the [64][64] matrices P, T, dP and dA (fp32 in
 // LDS) and the register operands split as they are read: one MFMA shape
 // throughout, so that no accumulation chain mixes shapes.
-// hi/lo bf16 operands of the 16 x 16 x 32 products on the bf16 path: x ~ hi
-// + lo to about 2^-16, a 32-wide k-block as A_hi B_hi + A_hi B_lo + A_lo
-// B_hi (three bf16 MFMAs against eight fp32 16 x 16 x 4 for the same k).
-struct HL8 {
-  bf16x8 h, l;
-};
-__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
-  const uint32_t a = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0], x[1]));
-  const uint32_t b = __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2], x[3]));
-  hi = make_uint2(a, b);
-  lo = make_uint2(__builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[0] - __uint_as_float(a << 16),
-                                                               x[1] - __uint_as_float(a & 0xffff0000u))),
-                  __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(x[2] - __uint_as_float(b << 16),
-                                                               x[3] - __uint_as_float(b & 0xffff0000u))));
-}
-// the fragment of a lane from its k = 4 g .. 4 g + 3 (x0) and 16 + 4 g ..
-// 16 + 4 g + 3 (x1) of a 32-wide k-block
-__device__ __forceinline__ HL8 hl_of(const f32x4& x0, const f32x4& x1) {
-  uint2 h0, l0, h1, l1;
-  split4(x0, h0, l0);
-  split4(x1, h1, l1);
-  return HL8{__builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y)),
-             __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y))};
-}
-__device__ __forceinline__ f32x4 mma3(const HL8& a, const HL8& b, f32x4 c) {
-  c = mma(a.h, b.h, c);
-  c = mma(a.h, b.l, c);
-  return mma(a.l, b.h, c);
-}
 // An LDS operand as hi and lo planes of [64][LH] bf16, element (r, k) at
 // r * LH + hl_pos(k) (a lane's fragment is 16 contiguous bytes of each
 // plane); rows of 68 dwords, so 8 consecutive rows' 16-byte reads fall on
