@@ -43,9 +43,10 @@
 //   kda_bwd_local : one workgroup per (chunk, head): everything else
 //                   (kda_bwd_local_fused at D = 128, with every intermediate
 //                   on chip; through a scratch area at D = 64).
-// Products run on fp32 MFMA (v_mfma_f32_16x16x4f32), except, on the bf16
-// path, kda_bwd_chunk's and most of kda_bwd_local_fused's, which take hi/lo
-// bf16 MFMA (see gemm and kda_bwd_local_fused).  In the
+// Products run on fp32 MFMA (v_mfma_f32_16x16x4f32) on the fp32 path; on the
+// bf16 path the record pass's, the walk's and the local gradients' take
+// hi/lo bf16 MFMA (x = hi + lo to about 2^-16: see HL8), the inverse's
+// small block products excepted.  In the
 // per-chunk kernels the operands pass through LDS in k-slices (each element
 // read once per product); the state-gradient pass keeps its operands in
 // registers.
@@ -672,7 +673,8 @@ __device__ __forceinline__ void low_tile(int t, int& a, int& b) {
 
 // Chunk record at D = 128 in one pass with the operands on chip: q, k, v
 // and the gate are read once, Qt, Kt and Kh built in LDS, and the Gram
-// blocks, the inverse, Wk and Wv computed from there, on fp32 MFMA.  The
+// blocks, the inverse, Wk and Wv computed from there (the Gram blocks, Wk
+// and Wv on hi/lo bf16 MFMA, the inverse's block rows on fp32 MFMA).  The
 // pass is bound by its writes, so the record gets only what the later passes
 // cannot take from the inputs (no copies of v and dO, no Gamma).  LDS: three
 // [64][D + 4] fp32 arrays (Qt, Kt, Kh; the first one holds diag(beta) V once
@@ -769,8 +771,10 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk_fused(const T* __restr
     const float* XA = isP ? LQ : LK;
     f32x4 acc = z4;
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb)
-      acc = mma(frag_rows(XA, LX, 16 * ta + i, 16 * kb, gq), frag_rows(LH, LX, 16 * tb + i, 16 * kb, gq), acc);
+    for (int kb = 0; kb < D / 32; ++kb)
+      acc = mma3(hl_of(frag_rows(XA, LX, 16 * ta + i, 32 * kb, gq), frag_rows(XA, LX, 16 * ta + i, 32 * kb + 16, gq)),
+                 hl_of(frag_rows(LH, LX, 16 * tb + i, 32 * kb, gq), frag_rows(LH, LX, 16 * tb + i, 32 * kb + 16, gq)),
+                 acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * ta + 4 * gq + e, s2 = 16 * tb + i;
@@ -849,20 +853,24 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_chunk_fused(const T* __restr
   for (int x = tid; x < C * C; x += kThreads) Rp[R::TM + x] = Ts[x / C][x % C];
   // Wk = T diag(beta) Kt, Wv = T diag(beta) V: wave w takes columns 16 w ..
   // 16 w + 15 of both, every row tile (T is lower triangular: row tile rt
-  // needs k-blocks kb <= rt only)
+  // needs the 32-wide k-blocks kb <= rt / 2 only, whose tiles above the
+  // diagonal are zeros in Ts)
   const int cw = 16 * w;
   f32x4 wk[4] = {z4, z4, z4, z4}, wv[4] = {z4, z4, z4, z4};
+  auto sb4 = [&](int k0) { return (f32x4){sb[k0], sb[k0 + 1], sb[k0 + 2], sb[k0 + 3]}; };
 #pragma unroll
-  for (int kb = 0; kb < C / 16; ++kb) {
-    const int k0 = 16 * kb + 4 * gq;
-    const f32x4 bk = frag_cols(LK, LX, cw + i, 16 * kb, gq) * (f32x4){sb[k0], sb[k0 + 1], sb[k0 + 2], sb[k0 + 3]};
-    const f32x4 bv = frag_cols(LQ, LX, cw + i, 16 * kb, gq);
+  for (int kb = 0; kb < C / 32; ++kb) {
+    const int k0 = 32 * kb + 4 * gq, k1 = k0 + 16;
+    const HL8 bk = hl_of(frag_cols(LK, LX, cw + i, 32 * kb, gq) * sb4(k0),
+                         frag_cols(LK, LX, cw + i, 32 * kb + 16, gq) * sb4(k1));
+    const HL8 bv = hl_of(frag_cols(LQ, LX, cw + i, 32 * kb, gq), frag_cols(LQ, LX, cw + i, 32 * kb + 16, gq));
 #pragma unroll
-    for (int rt = kb; rt < 4; ++rt) {
+    for (int rt = 2 * kb; rt < 4; ++rt) {
       const int r = 16 * rt + i;
-      const f32x4 a = {Ts[r][k0], Ts[r][k0 + 1], Ts[r][k0 + 2], Ts[r][k0 + 3]};
-      wk[rt] = mma(a, bk, wk[rt]);
-      wv[rt] = mma(a, bv, wv[rt]);
+      const HL8 a = hl_of((f32x4){Ts[r][k0], Ts[r][k0 + 1], Ts[r][k0 + 2], Ts[r][k0 + 3]},
+                          (f32x4){Ts[r][k1], Ts[r][k1 + 1], Ts[r][k1 + 2], Ts[r][k1 + 3]});
+      wk[rt] = mma3(a, bk, wk[rt]);
+      wv[rt] = mma3(a, bv, wv[rt]);
     }
   }
 #pragma unroll
