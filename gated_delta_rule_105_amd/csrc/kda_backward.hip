@@ -958,6 +958,12 @@ template <int D> struct StateOps {
     if (wave < 4) bOr = dp ? ld4(dp) : (f32x4){0.f, 0.f, 0.f, 0.f};
     load_panel(aKh, Rp + R::KH + 16 * t * D + half * (D / 2), D, 1, lane);      // Kh rows 16 t.., k in this half
     load_panel(aP, Rp + R::PM + half * (C / 2) * C + 16 * t, 1, C, lane);       // P^T rows 16 t.., k in this half
+  }
+  // the dH products' panels, issued later in the step than the others so
+  // that the address unit works through them while the waves compute
+  __device__ void load2(const float* Rp, int wave, int lane) {
+    typedef Rec<D> R;
+    const int w = wave % (D / 16);
     load_panel(aQ, Rp + R::QT + 16 * w, 1, D, lane);                            // Qt^T rows 16 w..
     load_panel(aW, Rp + R::WK + 16 * w, 1, D, lane);                            // Wk^T rows 16 w..
   }
@@ -1073,6 +1079,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 #pragma unroll
       for (int e = 0; e < 4; ++e) dU[wave >> 2][16 * t + 4 * g + e][ii] = acc[e];
     }
+    nxt.load2(rec_of(mn), wave, lane);
     lds_barrier();  // both halves of dU
     if (D / 16 >= 8 || wave < D / 16) {
       f32x4 bU[NKC];
@@ -1106,6 +1113,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
     }
   };
   opsA.load(rec_of(top - 1), do_of(top - 1), wave, lane);
+  opsA.load2(rec_of(top - 1), wave, lane);
   for (int64_t m = top - 1; m >= m_lo; m -= 2) {
     step(opsA, opsB, m);
     if (m == m_lo) break;
