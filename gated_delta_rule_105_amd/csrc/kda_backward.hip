@@ -1062,8 +1062,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
     float(*const bo)[64][4] = bOs[m & 1];
     cur.put(bo, wave, lane);
     const int64_t mn = m > m_lo ? m - 1 : m;  // (the last step loads a chunk it does not use)
-    nxt.load(rec_of(mn), do_of(mn), wave, lane);
     lds_barrier();  // G and the dO fragments ready
+    nxt.load(rec_of(mn), do_of(mn), wave, lane);
     // dU: this wave's halves of P^T dO and Kh G
     {
       f32x4 bG[NKH], bOh[StateOps<D>::NKP];
