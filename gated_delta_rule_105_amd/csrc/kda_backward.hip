@@ -1626,6 +1626,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     const int r = tid / 8, part = tid % 8;
     f32x4 a4 = z4;  // columns 16 part .. 16 part + 15, four at a time
     f32x4 vv[4], kt[4];
+    float ab[C / 8];  // Abar_rs, s = part + 8 j (the whole row: every load in bounds, issued at once)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c4 = 16 * part + 4 * j;
@@ -1633,26 +1634,32 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
       kt[j] = *(const f32x4*)&Rp[R::KT + r * D + c4];
     }
 #pragma unroll
+    for (int j = 0; j < C / 8; ++j) ab[j] = Rp[R::AB + r * C + part + 8 * j];
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c4 = 16 * part + 4 * j;
       a4 += hl_get4(H0, r, c4) * kt[j] + hl_get4(H1, r, c4) * vv[j];
     }
     float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-    for (int s2 = part; s2 < r; s2 += 8) acc += R2b[r * LC + s2] * Rp[R::AB + r * C + s2];
+#pragma unroll
+    for (int j = 0; j < C / 8; ++j)
+      if (part + 8 * j < r) acc += R2b[r * LC + part + 8 * j] * ab[j];
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
     dbr = acc;
   }
 
   // ---- phase 4: E = Dk + dA Kh, dKh += dA^T diag(beta) Kt (key columns)
-  f32x4 E[4];
+  f32x4 E[4], brow[4];  // brow: beta of rows 16 rt + 4 gq + e (phase 4 and the element-wise stage)
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) E[rt] = Dk[rt];
+  for (int rt = 0; rt < 4; ++rt) {
+    E[rt] = Dk[rt];
+    brow[rt] = *(const f32x4*)(bet + 16 * rt + 4 * gq);
+  }
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb) {
     const HL8 bk = hl_of(fk[2 * kb], fk[2 * kb + 1]);
-    const HL8 bt = hl_of(fkt[2 * kb] * *(const f32x4*)(bet + 32 * kb + 4 * gq),
-                         fkt[2 * kb + 1] * *(const f32x4*)(bet + 32 * kb + 16 + 4 * gq));
+    const HL8 bt = hl_of(fkt[2 * kb] * brow[2 * kb], fkt[2 * kb + 1] * brow[2 * kb + 1]);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       if (kb <= rt / 2)
@@ -1740,7 +1747,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
       const int r = 16 * rt + 4 * gq + e;
       const float G = gm[rt][e];
       const float ep = __expf(G), ei = __expf(-G);
-      const float dqt = dQt[rt][e], dkt = bet[r] * E[rt][e], dkh = dKh[rt][e];
+      const float dqt = dQt[rt][e], dkt = brow[rt][e] * E[rt][e], dkh = dKh[rt][e];
       dG[rt][e] = dqt * fq[rt][e] + dkt * fkt[rt][e] - dkh * fk[rt][e];
       R0[r * LX + c] = dqt * ep;
       Q2[r * LX + c] = dkt * ep + dkh * ei;
