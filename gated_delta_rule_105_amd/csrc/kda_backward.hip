@@ -942,20 +942,27 @@ __device__ __forceinline__ f32x4 mma_panels(f32x4 acc, const f32x4 (&a)[NK], con
 template <int D> struct StateOps {
   static constexpr int NKC = C / 16, NKH = D / 32, NKP = C / 32;
   f32x4 aP[NKP], aKh[NKH], aQ[NKC], aW[NKC];
-  f32x4 bOr;  // waves 0-3: dO[tid / 4][j0 + 4 (tid % 4) ..], shared through LDS
+  uint4 bOw;  // waves 0-3: dO[tid / 4][j0 + 4 (tid % 4) ..] as loaded, shared through LDS
+  // the dH values this set's step stored, held until the next step's dU
+  // products are issued: a store's data registers cannot be reused before
+  // it completes, so reusing them at once would make the next step wait
+  // for the stores
+  float keep[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4 gr;   // gamma of rows 16 w + 4 g + e (this wave's dH tile)
   // gamma first: a step needs the next chunk's gamma before its other operands
   // (loads complete in issue order).  Waves past D / 16 (d = 64) load a
   // copy of another wave's dH operands and do not use them.  The dO columns
   // every wave needs whole are loaded once, from the input, a row piece of
-  // four elements per thread of waves 0-3 (put; `dp` null past the end of
-  // the sequence): sixteen fewer load instructions per wave and step on an
-  // address unit that sets the step time.
-  template <typename T> __device__ void load(const float* Rp, const T* dp, int wave, int lane) {
+  // four elements per thread of waves 0-3 (put; rows past the end of the
+  // sequence read as zeros, with no branch: a masked load would make the
+  // wave wait for every load in flight): sixteen fewer load instructions
+  // per wave and step on an address unit that sets the step time.
+  template <typename T>
+  __device__ void load(const float* Rp, const ChunkRows<T>& dO, int j0, int wave, int lane) {
     typedef Rec<D> R;
-    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16);
+    const int t = wave & 3, half = wave >> 2, w = wave % (D / 16), tid = 64 * wave + lane;
     gr = *(const f32x4*)(Rp + R::GAM + 16 * w + 4 * (lane >> 4));
-    if (wave < 4) bOr = dp ? ld4(dp) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (wave < 4) bOw = dO.raw4(tid >> 2, j0 + 4 * (tid & 3));
     load_panel(aKh, Rp + R::KH + 16 * t * D + half * (D / 2), D, 1, lane);      // Kh rows 16 t.., k in this half
     load_panel(aP, Rp + R::PM + half * (C / 2) * C + 16 * t, 1, C, lane);       // P^T rows 16 t.., k in this half
   }
@@ -969,11 +976,12 @@ template <int D> struct StateOps {
   }
   // waves 0-3: the loaded dO piece into the fragment image o[kk][lane][e] =
   // B(k = 16 kk + 4 g + e, j = i) = dO[16 kk + 4 g + e][j0 + i] (lane 16 g + i)
-  __device__ void put(float (*o)[64][4], int wave, int lane) const {
+  template <typename T> __device__ void put(float (*o)[64][4], int wave, int lane) const {
     if (wave >= 4) return;
     const int tid = 64 * wave + lane, r = tid >> 2, c0 = 4 * (tid & 3);
+    const f32x4 v = ChunkRows<T>::to_f32x4(bOw);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[r >> 4][16 * ((r & 15) >> 2) + c0 + j][r & 3] = bOr[j];
+    for (int j = 0; j < 4; ++j) o[r >> 4][16 * ((r & 15) >> 2) + c0 + j][r & 3] = v[j];
   }
 };
 
@@ -992,7 +1000,8 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   __shared__ __align__(16) float G[D][16];
   __shared__ __align__(16) float dU[2][C][16];
   __shared__ __align__(16) float bOs[2][C / 16][64][4];  // dO fragment images, by step parity
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches stay scalar
   const int b = blockIdx.x;
   const int cb = (b / 8) % NCB, pair = 8 * (b / (8 * NCB)) + b % 8;
   const int n = pair / H, h = pair % H;
@@ -1013,11 +1022,10 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
   const int64_t sd = ((int64_t)n * H + h) * D * D;
   auto rec_of = [&](int64_t m) { return rec + (area_slot(win, n, base, m) * H + h) * (int64_t)R::FLOATS; };
   auto dhs_of = [&](int64_t m) { return dHs + (area_slot(win, n, base, m) * H + h) * (int64_t)D * D; };
-  // this thread's piece of chunk m's dO (waves 0-3: row tid / 4, columns
-  // j0 + 4 (tid % 4) ..), null for the rows past the sequence's end
-  auto do_of = [&](int64_t m) -> const T* {
-    const int64_t r = (int64_t)C * m + (tid >> 2);
-    return wave < 4 && r < len_n ? dout + ((tok_n + r) * H + h) * D + j0 + 4 * (tid & 3) : nullptr;
+  // chunk m's rows of dO (m < nc)
+  auto do_of = [&](int64_t m) {
+    const int64_t rest = len_n - (int64_t)C * m;
+    return ChunkRows<T>(dout, tok_n + (int64_t)C * m, rest < C ? (int)rest : C, H, h, D);
   };
   if (nc == 0) {  // no tokens: the gradient passes through unchanged
     if (dh0 && m_lo == 0)
@@ -1060,10 +1068,10 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
     // this chunk's dO fragments to LDS (the buffer of this step's parity: the
     // other one may still be read by a wave finishing the previous step)
     float(*const bo)[64][4] = bOs[m & 1];
-    cur.put(bo, wave, lane);
+    cur.template put<T>(bo, wave, lane);
     const int64_t mn = m > m_lo ? m - 1 : m;  // (the last step loads a chunk it does not use)
     lds_barrier();  // G and the dO fragments ready
-    nxt.load(rec_of(mn), do_of(mn), wave, lane);
+    nxt.load(rec_of(mn), do_of(mn), j0, wave, lane);
     // dU: this wave's halves of P^T dO and Kh G
     {
       f32x4 bG[NKH], bOh[StateOps<D>::NKP];
@@ -1079,6 +1087,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
 #pragma unroll
       for (int e = 0; e < 4; ++e) dU[wave >> 2][16 * t + 4 * g + e][ii] = acc[e];
     }
+    asm volatile("" ::"v"(nxt.keep[0]), "v"(nxt.keep[1]), "v"(nxt.keep[2]), "v"(nxt.keep[3]));
     nxt.load2(rec_of(mn), wave, lane);
     lds_barrier();  // both halves of dU
     if (D / 16 >= 8 || wave < D / 16) {
@@ -1098,13 +1107,18 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       neg = mma_panels<HL>(neg, cur.aW, bU);
       // chunk m - 1's end-state gradient: to the carry when that chunk is in
       // the earlier window
+      // (a buffer store: its per-lane offset is the same on every step, so
+      // no address register is overwritten while the stores are in flight)
       float* dHo = m > 0 ? (m == win.lo ? carry_out + sd : dhs_of(m - 1)) : nullptr;
+      const __amdgpu_buffer_rsrc_t rh = rsrc(dHo, m > 0 ? (uint32_t)(D * D * sizeof(float)) : 0u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * wave + 4 * g + e;
         const float v = G[r][ii] + acc[e] - neg[e];  // this lane's own element of G
+        cur.keep[e] = v;
         if (m > 0) {
-          dHo[r * D + j0 + ii] = v;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur.keep[e]), rh,
+                                                (uint32_t)((r * D + j0 + ii) * sizeof(float)), 0, 0);
           G[r][ii] = nxt.gr[e] * v;
         } else if (dh0) {
           dh0[sd + r * D + j0 + ii] = v;
@@ -1112,7 +1126,7 @@ __global__ void __launch_bounds__(512) kda_bwd_state(const float* __restrict__ r
       }
     }
   };
-  opsA.load(rec_of(top - 1), do_of(top - 1), wave, lane);
+  opsA.load(rec_of(top - 1), do_of(top - 1), j0, wave, lane);
   opsA.load2(rec_of(top - 1), wave, lane);
   for (int64_t m = top - 1; m >= m_lo; m -= 2) {
     step(opsA, opsB, m);

@@ -162,6 +162,24 @@ template <typename T> struct ChunkRows {
   __device__ __forceinline__ ChunkRows(const T* x, int64_t tok0, int len, int H, int h, int D)
       : r(rsrc(x + (tok0 * H + h) * D, ((uint32_t)(len - 1) * H * D + D) * sizeof(T))),
         rs((uint32_t)H * D * sizeof(T)) {}
+  // the bits of elements c .. c + 3 of row row (c % 4 == 0; bf16: the low
+  // two words), to be widened by to_f32x4 where they are used
+  __device__ __forceinline__ uint4 raw4(int row, int c) const {
+    const uint32_t off = (uint32_t)row * rs + (uint32_t)c * sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      return make_uint4(u.x, u.y, 0u, 0u);
+    } else {
+      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+  }
+  __device__ static __forceinline__ f32x4 to_f32x4(const uint4& u) {
+    if constexpr (sizeof(T) == 2)
+      return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u)};
+    else
+      return __builtin_bit_cast(f32x4, u);
+  }
   // elements c .. c + 3 of row row (c % 4 == 0)
   __device__ __forceinline__ f32x4 ld4(int row, int c) const {
     const uint32_t off = (uint32_t)row * rs + (uint32_t)c * sizeof(T);
