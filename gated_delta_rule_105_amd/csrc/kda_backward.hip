@@ -1408,6 +1408,7 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
   // phase 1's own columns of S and G = diag(gamma) dH (k down the key
   // channels), loaded first so that they are in flight during the staging
   f32x4 fs[D / 16], fg[D / 16];
+  const float gc = gam[cw + i];  // gamma of this lane's key column (phase 2)
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) {
     fs[kb] = frag_cols(S, D, cw + i, 16 * kb, gq);
@@ -1563,7 +1564,6 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
     }
   }
   {
-    const float gc = gam[cw + i];  // the column's scale
     dgl *= gc;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -1655,9 +1655,12 @@ __global__ void __launch_bounds__(kThreads) kda_bwd_local_fused(
       a4 += hl_get4(H0, r, c4) * kt[j] + hl_get4(H1, r, c4) * vv[j];
     }
     float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    // (a select, not a branch: loads under a branch would wait one by one)
 #pragma unroll
-    for (int j = 0; j < C / 8; ++j)
-      if (part + 8 * j < r) acc += R2b[r * LC + part + 8 * j] * ab[j];
+    for (int j = 0; j < C / 8; ++j) {
+      const float x = R2b[r * LC + part + 8 * j] * ab[j];
+      acc += part + 8 * j < r ? x : 0.f;
+    }
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);
     dbr = acc;
